@@ -1,0 +1,103 @@
+/*
+ * hikv_ref -- CPU oracle for the importance-aware KV decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, plain definition the
+ * GPU library is checked against.  Only the test suite, the package smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * Everything here works on host memory, one (batch, KV head) unit at a time,
+ * in the order the pages state the method:
+ *   append -> attention (per q-head) -> importance accumulation -> eviction.
+ * Arithmetic is fp64; stored state (importance) keeps the cache's fp32 type.
+ *
+ * Sources (pages are cited by title and section):
+ *  - HiKV: Hierarchical Importance-Aware KV Cache with Hardware Acceleration,
+ *    Sec. II-A (P = softmax(QK^T), PV), Sec. III-B (importance score),
+ *    Sec. III-C (Stage II: top-B_II channels of Q by magnitude), Algorithm 1.
+ *  - KV Cache Compression and Dynamic Pruning in Production Serving,
+ *    Sec. 3 "StreamingLLM" (sink + window set), Sec. 3 "H2O" (cumulative
+ *    attention score, protected sinks/window, keep the top of the rest),
+ *    Sec. 5 (GQA pooled importance).
+ *  - Kelle (papercache summary), Sec. 2.2 (order of [k,v] pairs does not
+ *    matter), Sec. 4.1 (per-head eviction by accumulated attention; prefill
+ *    importance as attention column sums; initial and recent tokens kept).
+ *  - Not All Heads Matter (HeadKV), Sec. 3.2 (per-head budgets).
+ */
+#ifndef HIKV_REF_H
+#define HIKV_REF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HIKV_REF_F32 0
+#define HIKV_REF_BF16 1
+
+#define HIKV_REF_OK 0
+#define HIKV_REF_EINVAL (-1)
+#define HIKV_REF_ECAPACITY (-4)
+#define HIKV_REF_EBUDGET (-5)
+
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim, capacity;
+  int32_t kv_dtype; /* HIKV_REF_F32 | HIKV_REF_BF16 (q, k_new, v_new too) */
+  float scale;      /* <= 0 -> 1/sqrt(head_dim) */
+} hikv_ref_shape;
+
+typedef struct {
+  void *k, *v;      /* [B][Hkv][cap][D] */
+  int32_t *pos;     /* [B][Hkv][cap] absolute position per slot */
+  float *imp;       /* [B][Hkv][cap] cumulative importance */
+  int32_t *len;     /* [B][Hkv] live slots are [0, len) */
+} hikv_ref_cache;
+
+typedef struct {
+  const int32_t *budget; /* [B][Hkv] or NULL -> budget_all */
+  int32_t budget_all, n_sink, n_recent;
+  int32_t stage2_channels; /* r; 0 = Stage II off */
+  int32_t stage2_tokens;   /* tokens kept for the exact softmax (k_T) */
+} hikv_ref_policy;
+
+/* Optional per-step debug outputs; any pointer may be NULL. */
+typedef struct {
+  int32_t *sel_channels; /* [B][Hq][r]  chosen channels, ascending */
+  int32_t *sel_tokens;   /* [B][Hq][k_T] positions of the exact-softmax set, ascending, -1 padded */
+  int32_t *sel_count;    /* [B][Hq]     size of that set */
+  double *approx_logits; /* [B][Hq][cap] Stage II approximate logit per pre-eviction slot */
+  float *imp_pre_evict;  /* [B][Hkv][cap] importance after accumulation, pre-eviction slot order */
+  uint8_t *kept;         /* [B][Hkv][cap] 1 if that pre-eviction slot survives eviction */
+  double *prob_sum;      /* [B][Hkv] total importance added this step */
+} hikv_ref_debug;
+
+/* One decode step for every (b, j).  Returns 0, or the first unit error
+ * (ECAPACITY / EBUDGET; that unit is left unchanged and its output rows are
+ * zero), or EINVAL for a bad shape/policy (nothing is touched). */
+int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_cache *cache,
+                         const hikv_ref_policy *policy, const void *q, const void *k_new,
+                         const void *v_new, const int32_t *new_pos, float *out,
+                         hikv_ref_debug *dbg);
+
+/* Compress every unit to its budget using the current importance;
+ * newest_pos[b] anchors the recent window. */
+int hikv_ref_evict(const hikv_ref_shape *shape, const hikv_ref_cache *cache,
+                   const hikv_ref_policy *policy, const int32_t *newest_pos,
+                   hikv_ref_debug *dbg);
+
+/* Add prompt-side importance: for every observation query i (position
+ * q_pos[b][i]) and q-head of the group, the causal softmax row over the
+ * cached tokens (those with pos <= q_pos) is added to those tokens'
+ * importance.  window == 0: every such entry counts (column sums);
+ * window > 0: an entry counts only when 0 <= q_pos - pos < window. */
+int hikv_ref_prefill_scores(const hikv_ref_shape *shape, const hikv_ref_cache *cache,
+                            const void *q_obs /* [B][Hq][n_obs][D] */,
+                            const int32_t *q_pos /* [B][n_obs] */, int32_t n_obs,
+                            int32_t window);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

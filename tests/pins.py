@@ -1,0 +1,454 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each check raises AssertionError on a violation.  They are run against the
+real oracle (test_oracle_pins.py) and against deliberately broken copies of
+it (test_oracle_mutants.py), which every one of a set of plausible mistakes
+must trip.
+
+What pins what:
+  attention_matches_library   -- output = torch's scaled_dot_product_attention
+      (a library routine) when nothing is evicted, including the appended
+      token attending to itself and the GQA head grouping; the importance a
+      step adds = the library's attention weights (obtained as SDPA with
+      V = identity), summed over the group.
+  rows_sum_to_group           -- softmax rows sum to one: a step adds exactly
+      G to a unit's importance.
+  streaming_closed_form       -- budget = S + W keeps exactly the first S and
+      last W positions, whatever the scores (StreamingLLM set formula).
+  eviction_brute_force        -- on tiny caches, the kept set is the unique
+      subset (containing the protected tokens) in which every kept candidate
+      outranks every evicted one; it also maximises the kept importance.
+  golden_cases                -- hand-worked cases in tests/golden.
+  permutation_invariance      -- permuting cache slots leaves the output and
+      the kept position set unchanged (Kelle: order of [k, v] pairs).
+  channel_permutation         -- one channel permutation applied to q and K,
+      another to V, permutes the output the same way.
+  conservation                -- over a run with eviction, live + evicted
+      importance = G * steps.
+  stage2_reduces_to_stage1    -- r = D and k_T >= len gives Stage I exactly.
+  stage2_selection            -- chosen channels = brute-force top-r of |q|
+      (ties: lower index); approximate importance = library attention
+      weights of the masked query; output = library attention over the
+      chosen tokens.
+  equal_keys_closed_form      -- all keys equal: uniform softmax, output =
+      mean of the values, each token gains G/L; Stage II's exact set is the
+      k_T lowest positions (tie rule).
+  prefill_column_sums         -- window 0 with every prompt query = column
+      sums of the library's causal attention matrix; window W = its banded
+      sums; one query = its softmax row.
+  errors_leave_unit_unchanged -- capacity and budget errors.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from importance_aware_kv_amd import workloads as W
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def widen(a, dtype):
+    if dtype == W.BF16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def sdpa(q, k, v, scale, mask=None):
+    """Library attention in float64: q [Hq, n, D], k [Hk, L, D], v [Hk, L, Dv]."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None]
+    m = None if mask is None else torch.from_numpy(mask)[None]
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, scale=scale,
+                                       enable_gqa=True)
+    return o[0].numpy()
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(np.abs(b).max(), 1e-300)
+    return float(np.abs(a - b).max() / den)
+
+
+def _unit_rows(state, b, j, dtype):
+    n = int(state["len"][b, j])
+    return (widen(state["k"][b, j, :n], dtype), widen(state["v"][b, j, :n], dtype),
+            state["pos"][b, j, :n].copy(), state["imp"][b, j, :n].astype(np.float64))
+
+
+def attention_matches_library(seed=1, dtype=W.BF16):
+    B, Hkv, G, D, cap = 2, 3, 3, 16, 40
+    Hq = Hkv * G
+    lens = np.array([[0, 7, 23], [1, 38, 12]], dtype=np.int32)
+    st = W.random_cache(seed, B, Hq, Hkv, D, dtype, cap, lens)
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, dtype, st["newest"])
+    before = ref.copy_state(st)
+    scale = 1.0 / math.sqrt(D)
+    code, out, dbg = ref.decode_step(st, Hq, step["q"], step["k_new"], step["v_new"],
+                                     step["new_pos"], budget_all=cap, n_sink=2, n_recent=3)
+    assert code == 0
+    for b in range(B):
+        for j in range(Hkv):
+            k, v, pos, imp = _unit_rows(before, b, j, dtype)
+            k = np.concatenate([k, widen(step["k_new"][b, j], dtype)[None]])
+            v = np.concatenate([v, widen(step["v_new"][b, j], dtype)[None]])
+            q = widen(step["q"][b, j * G:(j + 1) * G], dtype)[:, None, :]
+            want = sdpa(q, k[None], v[None], scale)[:, 0, :]
+            got = out[b, j * G:(j + 1) * G]
+            assert rel_err(got, want) < 2e-7, ("output", b, j, rel_err(got, want))
+            L = k.shape[0]
+            P = sdpa(q, k[None], np.eye(L)[None], scale)[:, 0, :]   # [G, L] weights
+            added = dbg["imp_pre_evict"][b, j, :L].astype(np.float64) - np.append(imp, 0.0)
+            assert np.abs(added - P.sum(0)).max() < 1e-6 * max(1.0, np.abs(imp).max(initial=0.0)), \
+                ("importance increment", b, j)
+            # nothing evicted: every position is still there
+            assert sorted(ref.live_positions(st, b, j)) == sorted(np.append(pos, st["newest"]))
+
+
+def rows_sum_to_group(seed=3):
+    B, Hkv, G, D, cap = 2, 2, 4, 32, 64
+    Hq = Hkv * G
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.BF16, cap, [[10, 40], [63 - 1, 3]])
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.BF16, st["newest"])
+    code, _, dbg = ref.decode_step(st, Hq, step["q"], step["k_new"], step["v_new"],
+                                   step["new_pos"], budget_all=20, n_sink=4, n_recent=4)
+    assert code == 0
+    assert np.abs(dbg["prob_sum"] - G).max() < 1e-12
+
+
+def streaming_closed_form(seed=5, steps=12):
+    w = W.workload("tiny", ctx=48, steps=steps)
+    d = W.generate(w)
+    st = ref.copy_state(d)
+    S, R = 3, 5
+    for t in range(steps):
+        code, _, _ = ref.decode_step(st, w.n_q_heads, d["q"][t], d["k_new"][t], d["v_new"][t],
+                                     d["new_pos"][t], budget_all=S + R, n_sink=S, n_recent=R)
+        assert code == 0
+        newest = int(d["new_pos"][t, 0])
+        want = sorted(set(range(S)) | set(range(newest - R + 1, newest + 1)))
+        assert list(ref.live_positions(st, 0, 0)) == want, (t, list(ref.live_positions(st, 0, 0)))
+
+
+def _brute_kept(pos, imp, beta, S, R, newest):
+    L = len(pos)
+    if L <= beta:
+        return set(pos.tolist())
+    Wp = min(R, beta - S)
+    prot = [i for i in range(L) if pos[i] < S or pos[i] > newest - Wp]
+    cand = [i for i in range(L) if i not in prot]
+    need = beta - len(prot)
+
+    def outranks(a, b):
+        return imp[a] > imp[b] or (imp[a] == imp[b] and pos[a] < pos[b])
+
+    valid = []
+    best = -1.0
+    best_sets = []
+    for sub in itertools.combinations(cand, need):
+        s = set(sub)
+        rest = [c for c in cand if c not in s]
+        if all(outranks(a, b) for a in sub for b in rest):
+            valid.append(s)
+        tot = sum(float(imp[i]) for i in sub)
+        if tot > best + 1e-12:
+            best, best_sets = tot, [s]
+        elif abs(tot - best) <= 1e-12:
+            best_sets.append(s)
+    assert len(valid) == 1, "brute force: a strict total order has exactly one valid split"
+    assert valid[0] in best_sets, "brute force: the valid split maximises kept importance"
+    return set(int(pos[i]) for i in prot) | set(int(pos[i]) for i in valid[0])
+
+
+def eviction_brute_force(seed=7, trials=150):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for t in range(trials):
+        L = int(rng.integers(1, 13))
+        beta = int(rng.integers(0, 8))
+        S = int(rng.integers(0, 3))
+        R = int(rng.integers(0, 4))
+        if beta < S:
+            beta = S
+        cap = 16
+        newest = L + int(rng.integers(0, 3))
+        pos = rng.permutation(np.arange(newest + 1))[:L].astype(np.int32)
+        pos[rng.integers(0, L)] = newest  # the newest token is live
+        pos = np.unique(pos)
+        rng.shuffle(pos)
+        L = len(pos)
+        imp = (rng.integers(0, 4, size=L) / 4.0).astype(np.float32)  # many ties
+        st = dict(k=np.zeros((1, 1, cap, 4), np.float32), v=np.zeros((1, 1, cap, 4), np.float32),
+                  pos=np.full((1, 1, cap), -1, np.int32), imp=np.zeros((1, 1, cap), np.float32),
+                  len=np.array([[L]], np.int32))
+        st["pos"][0, 0, :L] = pos
+        st["imp"][0, 0, :L] = imp
+        st["k"][0, 0, :L, 0] = pos  # payload follows its token
+        code, dbg = ref.evict(st, 1, [newest], budget_all=beta, n_sink=S, n_recent=R)
+        assert code == 0
+        want = _brute_kept(pos, imp.astype(np.float64), beta, S, R, newest)
+        got = set(ref.live_positions(st, 0, 0).tolist())
+        assert got == want, (t, sorted(got), sorted(want), beta, S, R)
+        n = int(st["len"][0, 0])
+        assert n == min(L, beta)
+        assert np.all(st["k"][0, 0, :n, 0] == st["pos"][0, 0, :n])
+        kept_slots = set(np.nonzero(dbg["kept"][0, 0, :L])[0].tolist())
+        assert set(int(pos[i]) for i in kept_slots) == want
+
+
+def read_golden(name="evict_cases.txt"):
+    cases = []
+    cur = None
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, rest = line.partition(" ")
+        if key == "case":
+            cur = dict(name=rest)
+            cases.append(cur)
+        elif key == "tokens":
+            pairs = [tok.split(":") for tok in rest.split()]
+            cur["pos"] = np.array([int(p) for p, _ in pairs], np.int32)
+            cur["imp"] = np.array([float(v) for _, v in pairs], np.float32)
+        elif key == "kept":
+            cur["kept"] = sorted(int(x) for x in rest.split())
+        else:
+            cur[key] = int(rest)
+    return cases
+
+
+def golden_cases():
+    for c in read_golden():
+        L = len(c["pos"])
+        cap = max(L, c["budget"]) + 1
+        st = dict(k=np.zeros((1, 1, cap, 4), np.float32), v=np.zeros((1, 1, cap, 4), np.float32),
+                  pos=np.full((1, 1, cap), -1, np.int32), imp=np.zeros((1, 1, cap), np.float32),
+                  len=np.array([[L]], np.int32))
+        st["pos"][0, 0, :L] = c["pos"]
+        st["imp"][0, 0, :L] = c["imp"]
+        code, _ = ref.evict(st, 1, [c["newest"]], budget_all=c["budget"], n_sink=c["sink"],
+                            n_recent=c["recent"])
+        assert code == 0, c["name"]
+        got = list(ref.live_positions(st, 0, 0))
+        assert got == c["kept"], (c["name"], got, c["kept"])
+
+
+def permutation_invariance(seed=11):
+    B, Hkv, G, D, cap = 1, 2, 2, 16, 32
+    Hq = Hkv * G
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.F32, cap, [[25, 30]], shuffle_pos=False)
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.F32, st["newest"])
+    a = ref.copy_state(st)
+    b_ = ref.copy_state(st)
+    rng = np.random.Generator(np.random.PCG64(seed + 2))
+    for j in range(Hkv):
+        n = int(st["len"][0, j])
+        perm = rng.permutation(n)
+        for f in ("k", "v", "pos", "imp"):
+            b_[f][0, j, :n] = st[f][0, j, :n][perm]
+    kw = dict(budget_all=20, n_sink=2, n_recent=3)
+    _, oa, _ = ref.decode_step(a, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"], **kw)
+    _, ob, _ = ref.decode_step(b_, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"], **kw)
+    assert rel_err(oa, ob) < 1e-6
+    for j in range(Hkv):
+        ra, rb = ref.live_rows(a, 0, j), ref.live_rows(b_, 0, j)
+        assert set(ra) == set(rb)
+        for p in ra:
+            assert ra[p][0] == rb[p][0] and ra[p][1] == rb[p][1]
+            assert abs(ra[p][2] - rb[p][2]) <= 1e-6 * max(1.0, abs(ra[p][2]))
+
+
+def channel_permutation(seed=13):
+    B, Hkv, G, D, cap = 1, 1, 3, 16, 24
+    Hq = Hkv * G
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.F32, cap, [[20]])
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.F32, st["newest"])
+    rng = np.random.Generator(np.random.PCG64(seed + 2))
+    pk, pv = rng.permutation(D), rng.permutation(D)
+    a = ref.copy_state(st)
+    b_ = ref.copy_state(st)
+    b_["k"] = np.ascontiguousarray(b_["k"][..., pk])
+    b_["v"] = np.ascontiguousarray(b_["v"][..., pv])
+    kw = dict(budget_all=cap, n_sink=0, n_recent=0)
+    _, oa, _ = ref.decode_step(a, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"], **kw)
+    _, ob, _ = ref.decode_step(b_, Hq, np.ascontiguousarray(step["q"][..., pk]),
+                               np.ascontiguousarray(step["k_new"][..., pk]),
+                               np.ascontiguousarray(step["v_new"][..., pv]), step["new_pos"], **kw)
+    assert rel_err(ob, oa[..., pv]) < 1e-6
+
+
+def conservation(seed=17, steps=40):
+    w = W.workload("llama8b", ctx=96, steps=steps, batch=1)
+    w.n_q_heads, w.n_kv_heads = 4, 2
+    d = W.generate(w)
+    st = ref.copy_state(d)
+    G = w.group
+    evicted = np.zeros((w.batch, w.n_kv_heads))
+    for t in range(steps):
+        code, _, dbg = ref.decode_step(st, w.n_q_heads, d["q"][t], d["k_new"][t], d["v_new"][t],
+                                       d["new_pos"][t], budget_all=40, n_sink=4, n_recent=8)
+        assert code == 0
+        gone = (dbg["kept"] == 0) & ~np.isnan(dbg["imp_pre_evict"])
+        evicted += np.where(gone, dbg["imp_pre_evict"], 0.0).sum(-1)
+    live = np.array([[st["imp"][b, j, :st["len"][b, j]].astype(np.float64).sum()
+                      for j in range(w.n_kv_heads)] for b in range(w.batch)])
+    assert np.abs(live + evicted - G * steps).max() < 1e-4 * G * steps
+    assert np.all(st["len"] == 40)
+
+
+def stage2_reduces_to_stage1(seed=19):
+    B, Hkv, G, D, cap = 2, 2, 2, 16, 40
+    Hq = Hkv * G
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.BF16, cap, [[30, 12], [5, 33]])
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.BF16, st["newest"])
+    a, b_ = ref.copy_state(st), ref.copy_state(st)
+    kw = dict(budget_all=16, n_sink=2, n_recent=4)
+    _, oa, _ = ref.decode_step(a, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"], **kw)
+    _, ob, _ = ref.decode_step(b_, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"],
+                               stage2_channels=D, stage2_tokens=cap, **kw)
+    assert rel_err(ob, oa) < 1e-6
+    for b in range(B):
+        for j in range(Hkv):
+            assert list(ref.live_positions(a, b, j)) == list(ref.live_positions(b_, b, j))
+
+
+def stage2_selection(seed=23):
+    B, Hkv, G, D, cap = 1, 2, 2, 32, 48
+    Hq = Hkv * G
+    r, kT = 8, 10
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.BF16, cap, [[40, 6]])
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.BF16, st["newest"])
+    # force ties in |q|: quantise to a coarse grid (the stored bf16 stays exact)
+    qf = np.round(W.bf16_bits_to_f32(step["q"]) * 2.0) / 2.0
+    step["q"] = W.bf16_bits(qf.astype(np.float32))
+    before = ref.copy_state(st)
+    scale = 1.0 / math.sqrt(D)
+    code, out, dbg = ref.decode_step(st, Hq, step["q"], step["k_new"], step["v_new"],
+                                     step["new_pos"], budget_all=cap, stage2_channels=r,
+                                     stage2_tokens=kT)
+    assert code == 0
+    for j in range(Hkv):
+        k, v, pos, imp = _unit_rows(before, 0, j, W.BF16)
+        k = np.concatenate([k, widen(step["k_new"][0, j], W.BF16)[None]])
+        v = np.concatenate([v, widen(step["v_new"][0, j], W.BF16)[None]])
+        pos = np.append(pos, st["newest"])
+        L = k.shape[0]
+        add = np.zeros(L)
+        for g in range(G):
+            h = j * G + g
+            q = widen(step["q"][0, h], W.BF16)
+            order = np.lexsort((np.arange(D), -np.abs(q)))   # |q| desc, index asc
+            E = np.sort(order[:r])
+            assert list(dbg["sel_channels"][0, h]) == list(E), ("channels", h)
+            qm = np.where(np.isin(np.arange(D), E), q, 0.0)
+            Pt = sdpa(qm[None, None], k[None], np.eye(L)[None], scale)[0, 0]
+            add += Pt
+            tord = np.lexsort((pos, -Pt))                    # approx score desc, pos asc
+            T = tord[:min(kT, L)]
+            assert list(dbg["sel_tokens"][0, h, :len(T)]) == sorted(pos[T].tolist()), ("tokens", h)
+            want = sdpa(q[None, None], k[T][None], v[T][None], scale)[0, 0]
+            assert rel_err(out[0, h], want) < 2e-7, ("output", h)
+        got = dbg["imp_pre_evict"][0, j, :L].astype(np.float64) - np.append(imp, 0.0)
+        assert np.abs(got - add).max() < 1e-6 * max(1.0, np.abs(imp).max(initial=0.0))
+
+
+def equal_keys_closed_form(seed=37):
+    """All keys equal -> uniform softmax: output = mean of the values attended,
+    each token gains G/L; Stage II's exact set = the k_T lowest positions."""
+    B, Hkv, G, D, cap = 1, 1, 2, 16, 32
+    Hq = Hkv * G
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.F32, cap, [[20]])
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.F32, st["newest"])
+    st["k"][0, 0, :] = step["k_new"][0, 0]
+    for stage2 in (False, True):
+        a = ref.copy_state(st)
+        before = ref.copy_state(st)
+        kT = 7
+        kw = dict(stage2_channels=5, stage2_tokens=kT) if stage2 else {}
+        code, out, dbg = ref.decode_step(a, Hq, step["q"], step["k_new"], step["v_new"],
+                                         step["new_pos"], budget_all=cap, **kw)
+        assert code == 0
+        L = 21
+        pos = np.append(before["pos"][0, 0, :20], st["newest"])
+        v = np.concatenate([before["v"][0, 0, :20], step["v_new"][0, 0][None]]).astype(np.float64)
+        rows = np.argsort(pos)[:kT] if stage2 else np.arange(L)
+        want = v[rows].mean(0)
+        for g in range(G):
+            assert rel_err(out[0, g], want) < 1e-6, (stage2, g)
+        added = dbg["imp_pre_evict"][0, 0, :L].astype(np.float64) - np.append(before["imp"][0, 0, :20], 0)
+        assert np.abs(added - G / L).max() < 1e-6
+        if stage2:
+            for g in range(G):
+                assert list(dbg["sel_tokens"][0, g, :kT]) == sorted(pos)[:kT]
+
+
+def prefill_column_sums(seed=29):
+    B, Hkv, G, D = 1, 2, 2, 16
+    Hq = Hkv * G
+    L = 24
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    qo = rng.standard_normal((B, Hq, L, D)).astype(np.float32)
+    scale = 1.0 / math.sqrt(D)
+    mask = np.tril(np.ones((L, L), dtype=bool))
+    P = np.stack([sdpa(qo[0, h][None], k[0, h // G][None], np.eye(L)[None], scale, mask)[0]
+                  for h in range(Hq)])                       # [Hq, query, token]
+    perm = rng.permutation(L)                                # slots in shuffled order
+    for window, n_obs_sel in ((0, slice(None)), (5, slice(None)), (0, slice(L - 1, L))):
+        st = dict(k=np.ascontiguousarray(k[:, :, perm]), v=np.zeros_like(k),
+                  pos=np.ascontiguousarray(np.broadcast_to(perm.astype(np.int32), (B, Hkv, L))),
+                  imp=np.zeros((B, Hkv, L), np.float32), len=np.full((B, Hkv), L, np.int32))
+        qsel = np.ascontiguousarray(qo[:, :, n_obs_sel])
+        qpos = np.arange(L, dtype=np.int32)[n_obs_sel][None].copy()
+        code = ref.prefill_scores(st, Hq, qsel, qpos, window=window)
+        assert code == 0
+        qi = np.arange(L)[n_obs_sel]
+        for j in range(Hkv):
+            want = np.zeros(L)
+            for g in range(G):
+                Pq = P[j * G + g][qi]                         # [n_obs, token]
+                if window > 0:
+                    band = (qi[:, None] - np.arange(L)[None, :] < window)
+                    Pq = Pq * band
+                want += Pq.sum(0)
+            got = np.zeros(L)
+            got[st["pos"][0, j]] = st["imp"][0, j]
+            assert np.abs(got - want).max() < 1e-5, (window, j)
+
+
+def errors_leave_unit_unchanged(seed=31):
+    B, Hkv, G, D, cap = 1, 2, 1, 8, 10
+    st = W.random_cache(seed, B, G * Hkv, Hkv, D, W.F32, cap, [[10, 4]])
+    step = W.random_step(seed + 1, B, G * Hkv, Hkv, D, W.F32, st["newest"])
+    before = ref.copy_state(st)
+    code, out, _ = ref.decode_step(st, G * Hkv, step["q"], step["k_new"], step["v_new"],
+                                   step["new_pos"], budget_all=8, n_sink=2, n_recent=2)
+    assert code == -4                       # unit 0 is full
+    for f in ("k", "v", "pos", "imp"):
+        assert np.array_equal(st[f][0, 0], before[f][0, 0])
+    assert st["len"][0, 0] == 10 and st["len"][0, 1] == 5
+    assert np.all(out[0, 0] == 0)
+    st2 = ref.copy_state(before)
+    code, _, _ = ref.decode_step(st2, G * Hkv, step["q"], step["k_new"], step["v_new"],
+                                 step["new_pos"], budget=np.array([[8, 1]]), n_sink=2, n_recent=0)
+    assert code == -4  # first error wins (unit 0 capacity); unit 1 budget < sinks
+    assert st2["len"][0, 1] == 4
+    bad = ref.Shape(1, 3, 2, 8, 10, 0, 0.0)  # Hq not a multiple of Hkv
+    cache = ref.cache_of(st2)
+    pol, _ = ref.policy_of(None, 8, 0, 0)
+    import ctypes as C
+    assert ref.lib().hikv_ref_decode_step(C.byref(bad), C.byref(cache), C.byref(pol), None, None,
+                                          None, None, None, None) == -1
+
+
+ALL = [attention_matches_library, rows_sum_to_group, streaming_closed_form, eviction_brute_force,
+       golden_cases, permutation_invariance, channel_permutation, conservation,
+       stage2_reduces_to_stage1, stage2_selection, equal_keys_closed_form, prefill_column_sums,
+       errors_leave_unit_unchanged]

@@ -1,0 +1,74 @@
+"""Plant plausible mistakes in copies of the oracle; the pins must catch each.
+
+Every mutant is one exact text substitution in oracle/hikv_ref.cpp, compiled
+into a temporary library.  The real oracle source is never modified.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import pins
+from oracle import ref
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+MUTANTS = [
+    ("drop_logit_scale", "            s[n] = d.scale * acc;", "            s[n] = acc;"),
+    ("new_token_not_attended", "      *x.len = slot + 1;\n      const int L = *x.len;",
+     "      *x.len = slot + 1;\n      const int L = *x.len - 1;"),
+    ("tie_keeps_newer", "      return x.pos[a] < x.pos[b];\n    });",
+     "      return x.pos[a] > x.pos[b];\n    });"),
+    ("window_off_by_one", "(x.pos[n] > newest - W)", "(x.pos[n] >= newest - W)"),
+    ("importance_from_logits", "            added[n] += p[n];", "            added[n] += s[n];"),
+    ("gqa_group_strided", "        const int h = j * d.G + g;\n        std::vector<double> qh",
+     "        const int h = g * d.Hkv + j;\n        std::vector<double> qh"),
+    ("stage2_smallest_channels", "if (fa != fb) return fa > fb;", "if (fa != fb) return fa < fb;"),
+    ("prefill_window_in_softmax", "if ((int64_t)qp - x.pos[n] >= 0) vis.push_back(n);",
+     "if ((int64_t)qp - x.pos[n] >= 0 && (window == 0 || (int64_t)qp - x.pos[n] < window)) "
+     "vis.push_back(n);"),
+    ("evict_highest", "if (x.imp[a] != x.imp[b]) return x.imp[a] > x.imp[b];",
+     "if (x.imp[a] != x.imp[b]) return x.imp[a] < x.imp[b];"),
+    ("compaction_forgets_importance", "        x.imp[w] = x.imp[n];\n", "\n"),
+    ("sinks_by_slot", "prot[n] = (x.pos[n] < S)", "prot[n] = (n < S)"),
+    ("stage2_approx_probs_for_output", "o[c] += p[i] * val_elem(d, x, T[i], c);",
+     "o[c] += pt[T[i]] * val_elem(d, x, T[i], c);"),
+    ("budget_off_by_one", "int keep_n = std::max(0, beta - n_prot);",
+     "int keep_n = std::max(0, beta - n_prot - 1);"),
+    ("value_rows_from_keys", "  return elem(x.v, d.dtype, (size_t)n * d.D + c);",
+     "  return elem(x.k, d.dtype, (size_t)n * d.D + c);"),
+    ("stage2_tokens_tie_by_higher_pos", "            return x.pos[a] < x.pos[bb];",
+     "            return x.pos[a] > x.pos[bb];"),
+]
+
+
+def _build(tmp, name, old, new):
+    src = open(os.path.join(SRC, "hikv_ref.cpp")).read()
+    assert src.count(old) >= 1, f"mutant {name}: pattern not found"
+    src = src.replace(old, new, 1)
+    path = os.path.join(tmp, name + ".cpp")
+    with open(path, "w") as f:
+        f.write(src)
+    so = os.path.join(tmp, name + ".so")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-fPIC", "-shared", "-I", SRC, path, "-o", so],
+                   check=True)
+    return so
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new):
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build(tmp, name, old, new)
+        prev = ref.use_library(so)
+        caught = None
+        try:
+            for check in pins.ALL:
+                try:
+                    check()
+                except (AssertionError, ValueError, IndexError) as e:  # noqa: PERF203
+                    caught = (check.__name__, repr(e)[:200])
+                    break
+        finally:
+            ref.use_library(prev)
+        assert caught is not None, f"no pin caught mutant {name}"
