@@ -1,0 +1,213 @@
+"""Benchmark: steady-state decode steps/s of the fused importance-aware KV step.
+
+Workload ``headkv32k``: batch 4, 32 q / 8 KV heads, D = 128, bf16, a
+32768-token prefilled cache per (batch, KV head), per-KV-head budgets from one
+Dirichlet(0.5) draw (total about 8 * 2048, clamped to [64, 8192]), 4 sinks,
+128 recent.  Every layer copy first takes the compression step (32769 -> its
+budget); the timed region is K steady decode steps (attend over budget + 1
+tokens, accumulate, evict one, compact), captured in one HIP graph.
+
+Cold measurement: the steps cycle over L independent layer copies (like
+successive layers of a model), so the ~34 MB a step touches is not resident
+in the 256 MB Infinity Cache when the step starts.
+
+Prints one JSON line (stdout).  Diagnostics go to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--workload", default="headkv32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no "
+              "multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from importance_aware_kv_amd import bytes_model as BM
+    from importance_aware_kv_amd import hikv as H
+    from importance_aware_kv_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    H.lib()  # raises when the HIP library is missing: no fallback
+    dev_name = torch.cuda.get_device_name(0)
+
+    n_inputs = 256
+    w = W.workload(args.workload, steps=n_inputs)
+    per_layer_steps = 1 + (args.warmup + args.steps + args.layers - 1) // args.layers
+    w.capacity = w.ctx + per_layer_steps + 1
+    t0 = time.time()
+    d = W.generate(w)
+    log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f}s on {dev_name}")
+    B, Hq, Hkv, D, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    budget = w.budget_array()
+
+    layers = [H.DeviceCache(d, Hq)]
+    for _ in range(1, args.layers):
+        c = H.DeviceCache.__new__(H.DeviceCache)
+        c.torch = torch
+        c.dtype, c.shape = layers[0].dtype, layers[0].shape
+        for f in ("k", "v", "pos", "imp", "len"):
+            setattr(c, f, getattr(layers[0], f).clone())
+        c.cache = H.hikv_cache(c.k.data_ptr(), c.v.data_ptr(), c.pos.data_ptr(), c.imp.data_ptr(),
+                               c.len.data_ptr())
+        layers.append(c)
+    budget_t = torch.from_numpy(budget).cuda()
+    pol = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
+    ws = H.workspace(layers[0].shape, pol)
+    q_all = H.to_device(d["q"])
+    kn_all = H.to_device(d["k_new"])
+    vn_all = H.to_device(d["v_new"])
+    pos_all = torch.from_numpy(
+        (w.ctx + np.arange(per_layer_steps + 1, dtype=np.int32))[:, None].repeat(B, 1).copy()).cuda()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    layer_step = [0] * args.layers
+
+    def step(li):
+        c = layers[li]
+        n = layer_step[li]
+        layer_step[li] += 1
+        code = H.hikv_decode_step(c.shape, c.cache, pol, q_all[n % n_inputs], kn_all[n % n_inputs],
+                                  vn_all[n % n_inputs], pos_all[n], out, ws)
+        if code != 0:
+            raise RuntimeError(f"hikv_decode_step: {H.status_string(code)}")
+
+    stream = torch.cuda.current_stream()
+    # Compression step of every layer copy (32769 tokens -> budget).
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for li in range(args.layers):
+        step(li)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    comp_ms = e0.elapsed_time(e1) / args.layers
+    H.check(H.hikv_device_status(ws), "device status after compression")
+    live_after = np.minimum(w.ctx + 1, budget)
+    assert np.array_equal(layers[0].len.cpu().numpy(), live_after), "compression did not reach the budgets"
+    comp_bytes = BM.decode_step_bytes(B, Hq, Hkv, D, w.el, np.full((B, Hkv), w.ctx + 1),
+                                      int(np.minimum(budget, w.ctx + 1).sum()))
+    log(f"[bench] compression step: {comp_ms * 1e3:.1f} us/layer "
+        f"({comp_bytes / comp_ms / 1e6:.0f} GB/s algorithmic)")
+
+    # Warm-up steady steps, eager.
+    for i in range(args.warmup):
+        step(i % args.layers)
+    torch.cuda.synchronize()
+    H.check(H.hikv_device_status(ws), "device status after warm-up")
+
+    # Timed steady steps: one HIP graph, replayed once.
+    base = args.warmup
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(args.steps):
+            step((base + i) % args.layers)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    g.replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    H.check(H.hikv_device_status(ws), "device status after timed steps")
+    ms_step = ms_total / args.steps
+    steps_per_s = 1e3 / ms_step
+    live_steady = budget + 1
+    step_bytes = BM.decode_step_bytes(B, Hq, Hkv, D, w.el, live_steady, B * Hkv)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"[bench] steady step: {ms_step * 1e3:.2f} us, {steps_per_s:.0f} steps/s, "
+        f"{step_bytes / 1e6:.2f} MB/step algorithmic -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, d, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    line = {
+        "metric": "decode steps/s and achieved KV HBM GB/s (fraction of 8 TB/s) per budget",
+        "value": round(steps_per_s, 1),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "headkv32k steady state: batch 4, 32 q / 8 KV heads, D 128, bf16 KV, "
+                        "32768-token prefill, per-KV-head budgets " + ",".join(map(str, budget[0])),
+            "global_batch": B,
+            "seq_len": w.ctx,
+            "layers_cycled": args.layers,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "whole decode step (all kernels of one step, graph-replayed)",
+            "bytes_per_launch": step_bytes,
+        },
+        "compression_step_us": round(comp_ms * 1e3, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, d, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    its own compression step, then steady steps until `seconds` have passed."""
+    import numpy as np
+
+    from oracle import ref
+    st = ref.copy_state(d)
+    budget = w.budget_array()
+    kw = dict(budget=budget, n_sink=w.n_sink, n_recent=w.n_recent, debug=False)
+    ref.decode_step(st, w.n_q_heads, d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], **kw)
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and n + 1 < d["q"].shape[0]:
+        t = n + 1
+        ref.decode_step(st, w.n_q_heads, d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t], **kw)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 2), "unit": "decode steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} steady decode steps of the same workload after the oracle's own "
+                      f"compression step, single-threaded fp64 C++ ({dt:.1f}s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+// api.hip -- the C ABI (include/hikv.h): argument checks, workspace carving
+// and the launch sequence of each entry point.  All launches go to the
+// caller's stream; nothing here allocates, synchronises or memsets (except
+// hikv_device_status, which is documented to synchronise).
+
+#include <math.h>
+#include <string.h>
+
+#include "hikv_launch.h"
+
+using namespace hikv;
+
+namespace {
+
+// gfx950 check, once per device.
+int arch_ok() {
+  static int cache[64];  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HIKV_EDEVICE;
+  if (dev < 0 || dev >= 64) return HIKV_EUNSUPPORTED;
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return HIKV_EDEVICE;
+    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return cache[dev] == 1 ? HIKV_OK : HIKV_EUNSUPPORTED;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const hikv_shape *s) {
+  if (!s) return HIKV_EINVAL;
+  if (s->batch < 0 || s->n_kv_heads < 1 || s->n_q_heads < 1 || s->capacity < 1) return HIKV_EINVAL;
+  if (s->n_q_heads % s->n_kv_heads) return HIKV_EINVAL;
+  if (s->kv_dtype != HIKV_F32 && s->kv_dtype != HIKV_BF16) return HIKV_EINVAL;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HIKV_EUNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return HIKV_EUNSUPPORTED;
+  if ((long long)s->batch * s->n_kv_heads > kMaxUnits) return HIKV_EUNSUPPORTED;
+  return HIKV_OK;
+}
+
+int check_policy(const hikv_shape *s, const hikv_policy *p) {
+  if (!p) return HIKV_EINVAL;
+  if (p->n_sink < 0 || p->n_recent < 0) return HIKV_EINVAL;
+  if (p->stage2_channels < 0 || p->stage2_channels > s->head_dim) return HIKV_EINVAL;
+  if (p->stage2_channels > 0 && p->stage2_tokens < 1) return HIKV_EINVAL;
+  return HIKV_OK;
+}
+
+int check_cache(const hikv_cache *c) {
+  if (!c || !c->k || !c->v || !c->pos || !c->imp || !c->len) return HIKV_EINVAL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return HIKV_EINVAL;
+  return HIKV_OK;
+}
+
+WsSizes sizes_for(const hikv_shape *s, const hikv_policy *p) {
+  const int kT = (p && p->stage2_channels > 0) ? p->stage2_tokens : 1;
+  return ws_sizes(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->capacity, kT);
+}
+
+StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *p, const Ws &ws) {
+  StepArgs a;
+  memset(&a, 0, sizeof a);
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.D = s->head_dim;
+  a.cap = s->capacity;
+  a.G = s->n_q_heads / s->n_kv_heads;
+  a.n_units = s->batch * s->n_kv_heads;
+  const double scale = s->scale > 0.f ? (double)s->scale : 1.0 / sqrt((double)s->head_dim);
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  a.k_cache = c->k;
+  a.v_cache = c->v;
+  a.k_w = c->k;
+  a.v_w = c->v;
+  a.pos = c->pos;
+  a.imp = c->imp;
+  a.len = c->len;
+  a.budget = p->budget;
+  a.budget_all = p->budget_all;
+  a.n_sink = p->n_sink;
+  a.n_recent = p->n_recent;
+  a.r = p->stage2_channels;
+  a.kT = p->stage2_channels > 0 ? p->stage2_tokens : 0;
+  a.ws = ws;
+  return a;
+}
+
+inline int dev_err(hipError_t e) { return e == hipSuccess ? HIKV_OK : HIKV_EDEVICE; }
+
+}  // namespace
+
+extern "C" size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy) {
+  if (check_shape(shape) != HIKV_OK) return 0;
+  if (policy && check_policy(shape, policy) != HIKV_OK) return 0;
+  return sizes_for(shape, policy).total;
+}
+
+extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache,
+                                const hikv_policy *policy, const void *q, const void *k_new,
+                                const void *v_new, const int32_t *new_pos, float *out, void *ws,
+                                size_t ws_bytes, const hikv_debug *debug, void *stream) {
+  int st = check_shape(shape);
+  if (st != HIKV_OK) return st;
+  if ((st = check_policy(shape, policy)) != HIKV_OK) return st;
+  if (shape->batch == 0) return HIKV_OK;
+  if ((st = check_cache(cache)) != HIKV_OK) return st;
+  if (!q || !k_new || !v_new || !new_pos || !out || !ws) return HIKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ws)) return HIKV_EINVAL;
+  const WsSizes sz = sizes_for(shape, policy);
+  if (ws_bytes < sz.total) return HIKV_EINVAL;
+  if ((st = arch_ok()) != HIKV_OK) return st;
+
+  StepArgs a = make_args(shape, cache, policy, ws_carve(ws, sz));
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_pos = new_pos;
+  a.out = out;
+  if (debug) {
+    a.dbg_channels = debug->sel_channels;
+    a.dbg_tokens = debug->sel_tokens;
+    a.dbg_count = debug->sel_count;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = shape->kv_dtype;
+  hipError_t e;
+  if (a.r == 0) {
+    if ((e = launch_attn_tiles(a, dt, true, false, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
+  } else {
+    if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_attn_tiles(a, dt, false, true, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);
+  }
+  if ((e = launch_accumulate(a, dt, s)) != hipSuccess) return dev_err(e);
+  if ((e = launch_bulk_evict(a, dt, new_pos, true, s)) != hipSuccess) return dev_err(e);
+  return HIKV_OK;
+}
+
+extern "C" int hikv_evict(const hikv_shape *shape, const hikv_cache *cache,
+                          const hikv_policy *policy, const int32_t *newest_pos, void *ws,
+                          size_t ws_bytes, void *stream) {
+  int st = check_shape(shape);
+  if (st != HIKV_OK) return st;
+  if ((st = check_policy(shape, policy)) != HIKV_OK) return st;
+  if (shape->batch == 0) return HIKV_OK;
+  if ((st = check_cache(cache)) != HIKV_OK) return st;
+  if (!newest_pos || !ws || !aligned16(ws)) return HIKV_EINVAL;
+  const WsSizes sz = sizes_for(shape, policy);
+  if (ws_bytes < sz.total) return HIKV_EINVAL;
+  if ((st = arch_ok()) != HIKV_OK) return st;
+  StepArgs a = make_args(shape, cache, policy, ws_carve(ws, sz));
+  return dev_err(launch_bulk_evict(a, shape->kv_dtype, newest_pos, false,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+extern "C" size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t n_obs) {
+  if (check_shape(shape) != HIKV_OK || n_obs < 0) return 0;
+  const size_t U = (size_t)shape->batch * shape->n_kv_heads;
+  const size_t G = (size_t)(shape->n_q_heads / shape->n_kv_heads);
+  return 256 + align256(sizeof(float) * U * G * (size_t)(n_obs > 0 ? n_obs : 1) * 2);
+}
+
+extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *cache,
+                                   const void *q_obs, const int32_t *q_pos, int32_t n_obs,
+                                   int32_t window, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_shape(shape);
+  if (st != HIKV_OK) return st;
+  if (n_obs < 0 || window < 0) return HIKV_EINVAL;
+  if (shape->batch == 0 || n_obs == 0) return HIKV_OK;
+  if ((st = check_cache(cache)) != HIKV_OK) return st;
+  if (!q_obs || !q_pos || !ws || !aligned16(q_obs) || !aligned16(ws)) return HIKV_EINVAL;
+  if (ws_bytes < hikv_prefill_workspace_bytes(shape, n_obs)) return HIKV_EINVAL;
+  if ((st = arch_ok()) != HIKV_OK) return st;
+  PrefillArgs p;
+  memset(&p, 0, sizeof p);
+  p.B = shape->batch;
+  p.Hq = shape->n_q_heads;
+  p.Hkv = shape->n_kv_heads;
+  p.D = shape->head_dim;
+  p.cap = shape->capacity;
+  p.G = p.Hq / p.Hkv;
+  p.n_units = p.B * p.Hkv;
+  p.n_obs = n_obs;
+  p.window = window;
+  const double scale = shape->scale > 0.f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  p.k_cache = cache->k;
+  p.pos = cache->pos;
+  p.imp = cache->imp;
+  p.len = cache->len;
+  p.q_obs = q_obs;
+  p.q_pos = q_pos;
+  p.status = static_cast<int32_t *>(ws);
+  p.stats = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
+  return dev_err(launch_prefill(p, shape->kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int hikv_device_status(void *ws, int clear, void *stream) {
+  if (!ws) return HIKV_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return HIKV_EDEVICE;
+  int32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return HIKV_EDEVICE;
+  if (clear && v != 0) {
+    const int32_t z = 0;
+    if (hipMemcpy(ws, &z, sizeof z, hipMemcpyHostToDevice) != hipSuccess) return HIKV_EDEVICE;
+  }
+  return v;
+}
+
+extern "C" const char *hikv_status_string(int status) {
+  switch (status) {
+    case HIKV_OK: return "ok";
+    case HIKV_EINVAL: return "invalid argument";
+    case HIKV_EUNSUPPORTED: return "unsupported shape or device";
+    case HIKV_EDEVICE: return "HIP runtime or launch failure";
+    case HIKV_ECAPACITY: return "cache capacity exceeded";
+    case HIKV_EBUDGET: return "budget below sink count or above capacity";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,116 @@
+// hikv_block.h -- workgroup-wide scan / reduction / radix-select helpers.
+#pragma once
+
+#include "hikv_common.h"
+
+namespace hikv {
+
+template <int NT>
+__device__ int block_excl_scan(int v, int *sc, int *total) {
+  const int t = threadIdx.x;
+  sc[t] = v;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int x = (t >= off) ? sc[t - off] : 0;
+    __syncthreads();
+    sc[t] += x;
+    __syncthreads();
+  }
+  const int incl = sc[t];
+  *total = sc[NT - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+template <int NT>
+__device__ long long block_sum_ll(long long v, long long *sc) {
+  const int t = threadIdx.x;
+  sc[t] = v;
+  __syncthreads();
+  for (int off = NT / 2; off > 0; off >>= 1) {
+    if (t < off) sc[t] += sc[t + off];
+    __syncthreads();
+  }
+  const long long r = sc[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_up(v, off);
+    if (lane >= off) v += x;
+  }
+  return v;
+}
+
+struct RadixState {
+  uint64_t prefix;
+  int shift, krem, done;
+};
+
+// Radix select over 64-bit keys, 8-bit digits from the most significant one.
+// Among the items n in [0, n_items) for which key_of(n, key) is true, finds
+// (prefix, shift) such that exactly k of them satisfy
+// (key >> shift) <= (prefix >> shift).  Keys must be distinct and
+// 1 <= k <= number of participating items.  The search stops at the first
+// digit whose bucket is taken whole.  Every thread of the block must call it;
+// the result is in *st when it returns.
+template <int NT, typename F>
+__device__ void radix_select_smallest(int n_items, int k, F key_of, uint32_t *hist,
+                                      RadixState *st) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    st->prefix = 0;
+    st->shift = 64;
+    st->krem = k;
+    st->done = 0;
+  }
+  __syncthreads();
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    const uint64_t prefix = st->prefix;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int n = tid; n < n_items; n += NT) {
+      uint64_t key;
+      if (!key_of(n, key)) continue;
+      if (pass > 0 && (key >> (shift + 8)) != (prefix >> (shift + 8))) continue;
+      atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // Find the digit whose bucket holds the krem-th smallest key: each lane
+      // owns 4 bins, one wave scan gives the crossing lane.
+      const uint32_t krem = (uint32_t)st->krem;
+      const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
+                     h3 = hist[4 * tid + 3];
+      const uint32_t s = h0 + h1 + h2 + h3;
+      const uint32_t incl = wave_incl_scan_u32(s);
+      const uint32_t excl = incl - s;
+      if (excl < krem && incl >= krem) {
+        const uint32_t hh[4] = {h0, h1, h2, h3};
+        uint32_t cum = excl;
+        int d = 3;
+        for (int i = 0; i < 4; ++i) {
+          if (cum + hh[i] >= krem) {
+            d = i;
+            break;
+          }
+          cum += hh[i];
+        }
+        const uint32_t rem = krem - cum;
+        st->prefix = prefix | ((uint64_t)(4 * tid + d) << shift);
+        st->shift = shift;
+        st->krem = (int)rem;
+        st->done = (hh[d] == rem) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (st->done) break;
+  }
+}
+
+}  // namespace hikv

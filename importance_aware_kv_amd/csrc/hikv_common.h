@@ -1,0 +1,180 @@
+// hikv_common.h -- device helpers and the workspace layout shared by the HIP
+// kernels of the importance-aware KV decode library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hikv.h"
+
+namespace hikv {
+
+constexpr int kWave = 64;
+constexpr int kMaxUnits = 4096;     // (batch, KV head) units per call
+constexpr int kTileMin = 64;        // smallest split-K tile, tokens
+constexpr int kTilesTarget = 512;   // split-K tiles aimed for per step (2 per CU)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Workspace layout.  Offsets are 256-byte aligned; everything is derived from
+// the shape and policy alone, so the host can size it without the device.
+// ---------------------------------------------------------------------------
+struct Ws {
+  int32_t *status;      // [1] sticky first device-side error
+  uint32_t *ticket;     // [n_units] last-tile-arrives counters (self-resetting)
+  int32_t *plan;        // [n_units + 4]: tile base per unit (exclusive prefix), then
+                        //   [n_units] = total tiles, [+1] = tile size T
+  float *stats;         // [n_units][G][2] softmax max (log2 domain) and sum per q-head
+  float *part_ml;       // [max_tiles][G][2] per-tile partial max / sum
+  float *part_acc;      // [max_tiles][G][D] per-tile partial P.V (unnormalised)
+  float *logits;        // [n_units][cap][G] log2-domain logits of this step
+  uint64_t *tile_key;   // [max_tiles] lowest eviction key per tile
+  int32_t *tile_slot;   // [max_tiles] its slot
+  int32_t *holes;       // [n_units][cap] bulk compaction: evicted slots below budget
+  int32_t *movers;      // [n_units][cap] bulk compaction: survivors at/above budget
+  uint32_t *chmask;     // [B*Hq][D/32] Stage II channel mask
+  int32_t *tsel;        // [B*Hq][k_T] Stage II exact-softmax slots
+  int32_t *tcount;      // [B*Hq]
+};
+
+struct WsSizes {
+  size_t off[14];
+  size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int max_tiles_for(int n_units) { return kTilesTarget + n_units + 8; }
+
+inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
+  const size_t U = (size_t)B * Hkv, G = (size_t)(Hq / Hkv), MT = (size_t)max_tiles_for((int)U);
+  const size_t sz[14] = {
+      sizeof(int32_t) * 64,            // status (+ spare)
+      sizeof(uint32_t) * U,            // ticket
+      sizeof(int32_t) * (U + 4),       // plan
+      sizeof(float) * U * G * 2,       // stats
+      sizeof(float) * MT * G * 2,      // part_ml
+      sizeof(float) * MT * G * D,      // part_acc
+      sizeof(float) * U * cap * G,     // logits
+      sizeof(uint64_t) * MT,           // tile_key
+      sizeof(int32_t) * MT,            // tile_slot
+      sizeof(int32_t) * U * cap,       // holes
+      sizeof(int32_t) * U * cap,       // movers
+      sizeof(uint32_t) * B * Hq * ((D + 31) / 32),  // chmask
+      sizeof(int32_t) * B * Hq * (size_t)(kT > 0 ? kT : 1),  // tsel
+      sizeof(int32_t) * B * Hq,        // tcount
+  };
+  WsSizes w;
+  size_t o = 0;
+  for (int i = 0; i < 14; ++i) {
+    w.off[i] = o;
+    o += align256(sz[i]);
+  }
+  w.total = o;
+  return w;
+}
+
+inline Ws ws_carve(void *base, const WsSizes &s) {
+  char *b = static_cast<char *>(base);
+  Ws w;
+  w.status = reinterpret_cast<int32_t *>(b + s.off[0]);
+  w.ticket = reinterpret_cast<uint32_t *>(b + s.off[1]);
+  w.plan = reinterpret_cast<int32_t *>(b + s.off[2]);
+  w.stats = reinterpret_cast<float *>(b + s.off[3]);
+  w.part_ml = reinterpret_cast<float *>(b + s.off[4]);
+  w.part_acc = reinterpret_cast<float *>(b + s.off[5]);
+  w.logits = reinterpret_cast<float *>(b + s.off[6]);
+  w.tile_key = reinterpret_cast<uint64_t *>(b + s.off[7]);
+  w.tile_slot = reinterpret_cast<int32_t *>(b + s.off[8]);
+  w.holes = reinterpret_cast<int32_t *>(b + s.off[9]);
+  w.movers = reinterpret_cast<int32_t *>(b + s.off[10]);
+  w.chmask = reinterpret_cast<uint32_t *>(b + s.off[11]);
+  w.tsel = reinterpret_cast<int32_t *>(b + s.off[12]);
+  w.tcount = reinterpret_cast<int32_t *>(b + s.off[13]);
+  return w;
+}
+
+// Everything a decode-step kernel needs, passed by value.
+struct StepArgs {
+  int B, Hq, Hkv, D, cap, G, n_units;
+  float scale_log2;          // logit scale * log2(e): logits live in the log2 domain
+  const void *k_cache;       // K [U][cap][D]
+  const void *v_cache;
+  void *k_w, *v_w;           // same pointers, writable
+  int32_t *pos;
+  float *imp;
+  int32_t *len;
+  const int32_t *budget;     // may be null
+  int32_t budget_all, n_sink, n_recent;
+  int32_t r, kT;             // Stage II
+  const void *q, *k_new, *v_new;
+  const int32_t *new_pos;
+  float *out;
+  int32_t *dbg_channels, *dbg_tokens, *dbg_count;
+  Ws ws;
+};
+
+// ---------------------------------------------------------------------------
+// Small device helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
+  atomicCAS(status, 0, code);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+
+// All-reduce across the LPR consecutive lanes that hold one token row.
+// quad_perm xor1 / xor2, then half-row and row mirrors (DPP, full rate), then
+// cross-row swizzles for rows wider than 16 lanes.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  if constexpr (LPR >= 2) v += dpp<0xB1>(v);
+  if constexpr (LPR >= 4) v += dpp<0x4E>(v);
+  if constexpr (LPR >= 8) v += dpp<0x141>(v);
+  if constexpr (LPR >= 16) v += dpp<0x140>(v);
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 pair (one uint32) -> two floats.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Monotone map float -> uint32 (total order of the float values).
+__device__ __forceinline__ uint32_t ord_f32(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Eviction key: smaller = evicted first.  Lower importance first; among
+// equal importance the higher position first (so the lower one is kept).
+__device__ __forceinline__ uint64_t evict_key(float imp, int32_t pos) {
+  return ((uint64_t)ord_f32(imp) << 32) | (uint64_t)(~(uint32_t)pos);
+}
+
+__device__ __forceinline__ int unit_budget(const StepArgs &a, int u) {
+  return a.budget ? a.budget[u] : a.budget_all;
+}
+
+// Budget / capacity validity of a unit before a decode step.
+__device__ __forceinline__ int32_t unit_error(const StepArgs &a, int u, int len_now, int add) {
+  const int beta = unit_budget(a, u);
+  if (len_now + add > a.cap || len_now < 0) return HIKV_ECAPACITY;
+  if (beta < a.n_sink || beta > a.cap) return HIKV_EBUDGET;
+  return 0;
+}
+
+}  // namespace hikv

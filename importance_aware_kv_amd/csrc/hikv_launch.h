@@ -1,0 +1,43 @@
+// hikv_launch.h -- host-side launchers of the HIP kernels (internal).
+#pragma once
+
+#include "hikv_common.h"
+
+namespace hikv {
+
+// Split-K decode attention over the live slots of every unit (append
+// included).  with_v=false: logits + softmax statistics only (Stage II's
+// reduced-channel pass).
+hipError_t launch_attn_tiles(const StepArgs &a, int dtype, bool with_v, bool masked,
+                             hipStream_t s);
+// Per (unit, q-head): merge tile partials; write out (when with_v) and stats.
+hipError_t launch_combine(const StepArgs &a, bool with_v, hipStream_t s);
+// Per tile: importance += probabilities; steady-state single eviction.
+hipError_t launch_accumulate(const StepArgs &a, int dtype, hipStream_t s);
+// Per unit: radix-select eviction of every token over budget + compaction.
+// newest = new_pos (decode) or newest_pos (hikv_evict); from_decode selects
+// which units are eligible (those the decode step processed).
+hipError_t launch_bulk_evict(const StepArgs &a, int dtype, const int32_t *newest,
+                             bool from_decode, hipStream_t s);
+
+// Stage II.
+hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s);
+hipError_t launch_stage2_tokens(const StepArgs &a, hipStream_t s);
+hipError_t launch_stage2_exact(const StepArgs &a, int dtype, hipStream_t s);
+
+// Prefill scores.
+struct PrefillArgs {
+  int B, Hq, Hkv, D, cap, G, n_units, n_obs, window;
+  float scale_log2;
+  const void *k_cache;
+  const int32_t *pos;
+  float *imp;
+  const int32_t *len;
+  const void *q_obs;
+  const int32_t *q_pos;
+  float *stats;       // [U][G][n_obs][2]
+  int32_t *status;
+};
+hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s);
+
+}  // namespace hikv

@@ -1,0 +1,288 @@
+// stage2.hip -- HiKV-style Stage II: reduced-channel logits and an exact
+// softmax over the best tokens.
+//
+// "HiKV: Hierarchical Importance-Aware KV Cache", Sec. III-C and Algorithm 1:
+// the B_II = d_h / r_II channels of the query with the largest magnitude
+// select which K elements are loaded for QK^T.  Here, per q-head:
+//   E    = the r channels of largest |q_d| (ties: lower channel)    [kernel S1]
+//   s~   = scale * sum_{d in E} q_d k_d over every live token        [attention
+//          kernel with the query masked to E, K-only]
+//   p~   = softmax(s~) feeds the importance (accumulation kernel)
+//   T    = the k_T tokens of largest s~ (ties: lower position)       [kernel S2]
+//   out  = exact full-D softmax over T only, times V                 [kernel S3]
+// The page's V side selects rows per chunk of P with no renormalisation; the
+// workload definition used here renormalises over a global top-k_T instead.
+
+#include "hikv_block.h"
+#include "hikv_launch.h"
+
+namespace hikv {
+
+__device__ __forceinline__ float load_abs(const void *q, size_t idx, int el) {
+  if (el == 2) {
+    const uint32_t w = (uint32_t) static_cast<const uint16_t *>(q)[idx] << 16;
+    return fabsf(__uint_as_float(w));
+  }
+  return fabsf(static_cast<const float *>(q)[idx]);
+}
+
+__device__ __forceinline__ bool unit_has_tiles(const StepArgs &a, int u) {
+  const int U = a.n_units;
+  const int nt = ((u + 1 < U) ? a.ws.plan[u + 1] : a.ws.plan[U]) - a.ws.plan[u];
+  return nt > 0;
+}
+
+// S1: one wave per (b, q-head): rank every channel by (|q| desc, index asc).
+__global__ __launch_bounds__(64) void k_stage2_channels(StepArgs a, int el) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const int D = a.D;
+  __shared__ float aq[128];
+  for (int d = lane; d < D; d += 64) aq[d] = load_abs(a.q, (size_t)bh * D + d, el);
+  __syncthreads();
+  bool sel[2] = {false, false};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int d = lane + 64 * t;
+    if (d >= D) continue;
+    const float x = aq[d];
+    int rank = 0;
+    for (int e = 0; e < D; ++e) {
+      const float y = aq[e];
+      rank += (y > x) || (y == x && e < d);
+    }
+    sel[t] = rank < a.r;
+  }
+  const uint64_t b0 = __ballot(sel[0]);
+  const uint64_t b1 = __ballot(sel[1]);
+  if (lane == 0) {
+    uint32_t *mw = a.ws.chmask + (size_t)bh * (D / 32);
+    mw[0] = (uint32_t)b0;
+    mw[1] = (uint32_t)(b0 >> 32);
+    if (D > 64) {
+      mw[2] = (uint32_t)b1;
+      mw[3] = (uint32_t)(b1 >> 32);
+    }
+  }
+  if (a.dbg_channels) {
+    const int n0 = __popcll(b0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int d = lane + 64 * t;
+      if (d < D && sel[t]) {
+        const uint64_t below = (lane == 0) ? 0ull : ((t == 0 ? b0 : b1) & ((1ull << lane) - 1ull));
+        const int idx = (t == 0 ? 0 : n0) + __popcll(below);
+        a.dbg_channels[(size_t)bh * a.r + idx] = d;
+      }
+    }
+  }
+}
+
+// S2: per (b, q-head), the k_T live tokens with the largest reduced logit
+// (ties: lower position), gathered in slot order.
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void k_stage2_tokens(StepArgs a) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int b = bh / a.Hq, h = bh - b * a.Hq, j = h / a.G, g = h - j * a.G;
+  const int u = b * a.Hkv + j;
+  int32_t *tsel = a.ws.tsel + (size_t)bh * a.kT;
+  if (!unit_has_tiles(a, u)) {
+    if (tid == 0) a.ws.tcount[bh] = 0;
+    if (a.dbg_count && tid == 0) a.dbg_count[bh] = 0;
+    if (a.dbg_tokens)
+      for (int i = tid; i < a.kT; i += kSelThreads) a.dbg_tokens[(size_t)bh * a.kT + i] = -1;
+    return;
+  }
+  const int L = a.len[u] + 1;
+  const int k = min(a.kT, L);
+  const float *lg = a.ws.logits + (size_t)u * a.cap * a.G;
+  const int32_t *pos = a.pos + (size_t)u * a.cap;
+  __shared__ uint32_t hist[256];
+  __shared__ int sc[kSelThreads];
+  __shared__ RadixState rs;
+  // Smaller key = better token: larger logit, then lower position.
+  auto key_of = [&](int n, uint64_t &key) -> bool {
+    key = ((uint64_t)(~ord_f32(lg[(size_t)n * a.G + g])) << 32) | (uint32_t)pos[n];
+    return true;
+  };
+  radix_select_smallest<kSelThreads>(L, k, key_of, hist, &rs);
+  const uint64_t prefix = rs.prefix;
+  const int shift = rs.shift;
+  const int per = (L + kSelThreads - 1) / kSelThreads;
+  const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
+  int cnt = 0;
+  for (int n = n0; n < n1; ++n) {
+    uint64_t key;
+    key_of(n, key);
+    cnt += (key >> shift) <= (prefix >> shift);
+  }
+  int total;
+  int o = block_excl_scan<kSelThreads>(cnt, sc, &total);
+  for (int n = n0; n < n1; ++n) {
+    uint64_t key;
+    key_of(n, key);
+    if ((key >> shift) <= (prefix >> shift)) {
+      if (o < a.kT) tsel[o] = n;  // exactly k with distinct positions; bound anyway
+      ++o;
+    }
+  }
+  if (total > a.kT) total = a.kT;
+  if (tid == 0) a.ws.tcount[bh] = total;
+  __syncthreads();
+  if (a.dbg_count && tid == 0) a.dbg_count[bh] = total;
+  if (a.dbg_tokens) {
+    int32_t *dt = a.dbg_tokens + (size_t)bh * a.kT;
+    for (int i = tid; i < a.kT; i += kSelThreads) {
+      if (i >= total) {
+        dt[i] = -1;
+        continue;
+      }
+      const int p = pos[tsel[i]];
+      int rank = 0;
+      for (int e = 0; e < total; ++e) rank += pos[tsel[e]] < p;
+      if (rank < a.kT) dt[rank] = p;
+    }
+  }
+}
+
+// S3: per (b, q-head), exact logits over the selected tokens, softmax over
+// them only, P.V.  Same lane layout as the attention kernel: LPR lanes per
+// row, one online softmax per row, rows and waves merged at the end.
+template <int EL, int D>
+__global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
+  constexpr int CH = 16 / EL, LPR = D / CH, TPW = kWave / LPR;
+  constexpr int U = (16 / TPW) > 0 ? 16 / TPW : 1;
+  constexpr int RB = D * EL;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = bh / a.Hq, h = bh - b * a.Hq, j = h / a.G;
+  const int u = b * a.Hkv + j;
+  const int r = lane / LPR, c = lane - r * LPR;
+  float *outp = a.out + (size_t)bh * D;
+  const int nt = a.ws.tcount[bh];
+  if (nt == 0) {
+    for (int d = tid; d < D; d += 256) outp[d] = 0.f;
+    return;
+  }
+  const int32_t *tsel = a.ws.tsel + (size_t)bh * a.kT;
+  const char *kc = static_cast<const char *>(a.k_cache) + (size_t)u * a.cap * RB;
+  const char *vc = static_cast<const char *>(a.v_cache) + (size_t)u * a.cap * RB;
+  const uint4 qf = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
+                                                    ((size_t)bh * D + c * CH) * EL);
+  float m = -INFINITY, l = 0.f, acc[CH];
+#pragma unroll
+  for (int e = 0; e < CH; ++e) acc[e] = 0.f;
+  for (int base = wave * TPW * U; base < nt; base += 4 * TPW * U) {
+    uint4 kf[U], vf[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int t = base + i * TPW + r;
+      const bool ok = t < nt;
+      const int n = ok ? tsel[t] : 0;
+      kf[i] = ok ? *reinterpret_cast<const uint4 *>(kc + (size_t)n * RB + c * 16) : make_uint4(0, 0, 0, 0);
+      vf[i] = ok ? *reinterpret_cast<const uint4 *>(vc + (size_t)n * RB + c * 16) : make_uint4(0, 0, 0, 0);
+    }
+    float s[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float d;
+      if constexpr (EL == 2) {
+        d = dot2_bf16(qf.x, kf[i].x, 0.f);
+        d = dot2_bf16(qf.y, kf[i].y, d);
+        d = dot2_bf16(qf.z, kf[i].z, d);
+        d = dot2_bf16(qf.w, kf[i].w, d);
+      } else {
+        d = __uint_as_float(qf.x) * __uint_as_float(kf[i].x);
+        d = fmaf(__uint_as_float(qf.y), __uint_as_float(kf[i].y), d);
+        d = fmaf(__uint_as_float(qf.z), __uint_as_float(kf[i].z), d);
+        d = fmaf(__uint_as_float(qf.w), __uint_as_float(kf[i].w), d);
+      }
+      d = row_sum<LPR>(d) * a.scale_log2;
+      s[i] = (base + i * TPW + r < nt) ? d : -INFINITY;
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < U; ++i) mx = fmaxf(mx, s[i]);
+    const float mxs = (mx == -INFINITY) ? 0.f : mx;
+    const float corr = fast_exp2(m - mxs);
+    l *= corr;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const float p = fast_exp2(s[i] - mxs);
+      l += p;
+      if constexpr (EL == 2) {
+        const uint32_t *vw = reinterpret_cast<const uint32_t *>(&vf[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(p, bf_lo(vw[e]), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(p, bf_hi(vw[e]), acc[2 * e + 1]);
+        }
+      } else {
+        const float *vv = reinterpret_cast<const float *>(&vf[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(p, vv[e], acc[e]);
+      }
+    }
+    m = mx;
+  }
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    const float mo = __shfl_xor(m, off), lo = __shfl_xor(l, off);
+    const float mx = fmaxf(m, mo);
+    const float mxs = (mx == -INFINITY) ? 0.f : mx;
+    const float ea = fast_exp2(m - mxs), eb = fast_exp2(mo - mxs);
+    l = l * ea + lo * eb;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[e] = acc[e] * ea + __shfl_xor(acc[e], off) * eb;
+    m = mx;
+  }
+  __shared__ float sm_ml[4][2];
+  __shared__ float sm_acc[4][D];
+  if (r == 0) {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) sm_acc[wave][c * CH + e] = acc[e];
+    if (c == 0) {
+      sm_ml[wave][0] = m;
+      sm_ml[wave][1] = l;
+    }
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += 256) {
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[w][0]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float av = 0.f, lv = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float e = fast_exp2(sm_ml[w][0] - Ms);
+      av += sm_acc[w][d] * e;
+      lv += sm_ml[w][1] * e;
+    }
+    outp[d] = av / lv;
+  }
+}
+
+hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s) {
+  hipLaunchKernelGGL(k_stage2_channels, dim3(a.B * a.Hq), dim3(64), 0, s, a,
+                     dtype == HIKV_BF16 ? 2 : 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage2_tokens(const StepArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_stage2_tokens, dim3(a.B * a.Hq), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage2_exact(const StepArgs &a, int dtype, hipStream_t s) {
+  const dim3 grid(a.B * a.Hq), block(256);
+  if (dtype == HIKV_BF16) {
+    if (a.D == 128) hipLaunchKernelGGL((k_stage2_exact<2, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_stage2_exact<2, 64>), grid, block, 0, s, a);
+  } else {
+    if (a.D == 128) hipLaunchKernelGGL((k_stage2_exact<4, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_stage2_exact<4, 64>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hikv

@@ -1,0 +1,204 @@
+"""ctypes binding of libhikv.so (include/hikv.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libhikv.so.  There is no fallback; if the library is not built the
+import of this module's functions raises.  torch provides device memory and
+the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhikv.so")
+
+HIKV_F32, HIKV_BF16 = 0, 1
+HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
+
+EXPORTS = ("hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_prefill_workspace_bytes",
+           "hikv_prefill_scores", "hikv_device_status", "hikv_status_string")
+
+
+class hikv_shape(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("capacity", C.c_int32), ("kv_dtype", C.c_int32),
+                ("scale", C.c_float)]
+
+
+class hikv_cache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("pos", C.c_void_p), ("imp", C.c_void_p),
+                ("len", C.c_void_p)]
+
+
+class hikv_policy(C.Structure):
+    _fields_ = [("budget", C.c_void_p), ("budget_all", C.c_int32), ("n_sink", C.c_int32),
+                ("n_recent", C.c_int32), ("stage2_channels", C.c_int32),
+                ("stage2_tokens", C.c_int32)]
+
+
+class hikv_debug(C.Structure):
+    _fields_ = [("sel_channels", C.c_void_p), ("sel_tokens", C.c_void_p), ("sel_count", C.c_void_p)]
+
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libhikv.so (built in-tree).  Raises if it is missing: no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(f"{LIB_PATH} is not built; run `python -m importance_aware_kv_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P = C.POINTER
+        vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        L.hikv_workspace_bytes.argtypes = [P(hikv_shape), P(hikv_policy)]
+        L.hikv_workspace_bytes.restype = sz
+        L.hikv_decode_step.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, vp, vp,
+                                       vp, vp, sz, P(hikv_debug), vp]
+        L.hikv_decode_step.restype = C.c_int
+        L.hikv_evict.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, sz, vp]
+        L.hikv_evict.restype = C.c_int
+        L.hikv_prefill_workspace_bytes.argtypes = [P(hikv_shape), i32]
+        L.hikv_prefill_workspace_bytes.restype = sz
+        L.hikv_prefill_scores.argtypes = [P(hikv_shape), P(hikv_cache), vp, vp, i32, i32, vp, sz, vp]
+        L.hikv_prefill_scores.restype = C.c_int
+        L.hikv_device_status.argtypes = [vp, C.c_int, vp]
+        L.hikv_device_status.restype = C.c_int
+        L.hikv_status_string.argtypes = [C.c_int]
+        L.hikv_status_string.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, capacity, kv_dtype, scale=0.0) -> hikv_shape:
+    return hikv_shape(batch, n_q_heads, n_kv_heads, head_dim, capacity, kv_dtype, scale)
+
+
+def make_policy(budget=None, budget_all=0, n_sink=0, n_recent=0, stage2_channels=0,
+                stage2_tokens=0) -> hikv_policy:
+    return hikv_policy(None if budget is None else budget.data_ptr(), budget_all, n_sink, n_recent,
+                       stage2_channels, stage2_tokens)
+
+
+def status_string(code: int) -> str:
+    return lib().hikv_status_string(code).decode()
+
+
+def check(code: int, what: str = "hikv call"):
+    if code != HIKV_OK:
+        raise RuntimeError(f"{what} failed: {code} ({status_string(code)})")
+
+
+def hikv_workspace_bytes(shape: hikv_shape, policy: Optional[hikv_policy]) -> int:
+    return lib().hikv_workspace_bytes(C.byref(shape), C.byref(policy) if policy is not None else None)
+
+
+def hikv_prefill_workspace_bytes(shape: hikv_shape, n_obs: int) -> int:
+    return lib().hikv_prefill_workspace_bytes(C.byref(shape), n_obs)
+
+
+def hikv_decode_step(shape, cache, policy, q, k_new, v_new, new_pos, out, ws, debug=None,
+                     stream=None) -> int:
+    return lib().hikv_decode_step(C.byref(shape), C.byref(cache), C.byref(policy), _p(q), _p(k_new),
+                                  _p(v_new), _p(new_pos), _p(out), _p(ws), ws.numel() * ws.element_size(),
+                                  C.byref(debug) if debug is not None else None, _stream(stream))
+
+
+def hikv_evict(shape, cache, policy, newest_pos, ws, stream=None) -> int:
+    return lib().hikv_evict(C.byref(shape), C.byref(cache), C.byref(policy), _p(newest_pos), _p(ws),
+                            ws.numel() * ws.element_size(), _stream(stream))
+
+
+def hikv_prefill_scores(shape, cache, q_obs, q_pos, n_obs, window, ws, stream=None) -> int:
+    return lib().hikv_prefill_scores(C.byref(shape), C.byref(cache), _p(q_obs), _p(q_pos), n_obs,
+                                     window, _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+
+
+def hikv_device_status(ws, clear=True, stream=None) -> int:
+    return lib().hikv_device_status(_p(ws), 1 if clear else 0, _stream(stream))
+
+
+# ---------------------------------------------------------------------------
+# Device-side state (torch owns the memory) built from the seeded workloads.
+# ---------------------------------------------------------------------------
+class DeviceCache:
+    """The cache of one layer on the GPU plus the descriptors the ABI wants."""
+
+    def __init__(self, state: dict, n_q_heads: int, device="cuda", scale: float = 0.0):
+        import torch
+        self.torch = torch
+        k = state["k"]
+        B, Hkv, cap, D = k.shape
+        self.dtype = HIKV_F32 if k.dtype == np.float32 else HIKV_BF16
+        self.shape = make_shape(B, n_q_heads, Hkv, D, cap, self.dtype, scale)
+        self.k = self._to(state["k"], device)
+        self.v = self._to(state["v"], device)
+        self.pos = torch.from_numpy(np.ascontiguousarray(state["pos"])).to(device)
+        self.imp = torch.from_numpy(np.ascontiguousarray(state["imp"])).to(device)
+        self.len = torch.from_numpy(np.ascontiguousarray(state["len"])).to(device)
+        self.cache = hikv_cache(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(),
+                                self.imp.data_ptr(), self.len.data_ptr())
+
+    def _to(self, a, device):
+        t = self.torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            t = t.view(self.torch.int16)
+        return t.to(device)
+
+    def to_numpy(self) -> dict:
+        k = self.k.cpu().numpy()
+        v = self.v.cpu().numpy()
+        if self.dtype == HIKV_BF16:
+            k = k.view(np.uint16)
+            v = v.view(np.uint16)
+        return dict(k=k, v=v, pos=self.pos.cpu().numpy(), imp=self.imp.cpu().numpy(),
+                    len=self.len.cpu().numpy())
+
+    def load(self, state: dict):
+        """Overwrite the device state with a host state of the same shape."""
+        for name in ("k", "v"):
+            src = self.torch.from_numpy(np.ascontiguousarray(state[name]))
+            if state[name].dtype == np.uint16:
+                src = src.view(self.torch.int16)
+            getattr(self, name).copy_(src)
+        for name in ("pos", "imp", "len"):
+            getattr(self, name).copy_(self.torch.from_numpy(np.ascontiguousarray(state[name])))
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.int16)
+    return t.to(device)
+
+
+def workspace(shape: hikv_shape, policy: hikv_policy, device="cuda"):
+    import torch
+    n = hikv_workspace_bytes(shape, policy)
+    if n == 0:
+        raise RuntimeError("invalid shape/policy for workspace sizing")
+    return torch.zeros(n, dtype=torch.uint8, device=device)

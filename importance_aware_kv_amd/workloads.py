@@ -48,11 +48,19 @@ BF16 = 1
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
-    out[nan] = 0x7FC0
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_x = x.reshape(-1)
+    flat_o = out.reshape(-1)
+    step = 1 << 22
+    for i in range(0, flat_x.size, step):         # chunked: bounded temporaries
+        u = flat_x[i:i + step].view(np.uint32)
+        r = (u >> 16) & 1
+        r += 0x7FFF
+        r += u                                     # wraps only for NaN patterns, fixed below
+        r >>= 16
+        o = r.astype(np.uint16)
+        o[np.isnan(flat_x[i:i + step])] = 0x7FC0
+        flat_o[i:i + step] = o
     return out
 
 

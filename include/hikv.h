@@ -1,0 +1,162 @@
+/*
+ * hikv.h -- C ABI of the importance-aware KV decode library (AMD MI355X, gfx950).
+ *
+ * One decode step of single-query attention over a budgeted, slot-indexed KV
+ * cache, fused with importance-based eviction:
+ *
+ *   append the new (k, v) -> logits q.k for the G q-heads sharing each KV
+ *   head -> softmax -> P.V -> add each cached token's attention probability
+ *   (summed over the group) to its importance -> if the cache is over budget,
+ *   evict the lowest-importance tokens, never the sinks or the recent window,
+ *   and compact the survivors in place.
+ *
+ * Sources (pages are cited by title and section):
+ *   [HiKV]  "HiKV: Hierarchical Importance-Aware KV Cache with Hardware
+ *           Acceleration for LLM Decoding": Sec. II-A (decode GeMVs QK^T and
+ *           PV, P = softmax(QK^T)), Sec. III-B (importance score from
+ *           accumulated P; budget), Sec. III-C (Stage II: top-B_II channels of
+ *           Q by magnitude guide the K loads), Algorithm 1.
+ *   [Blog]  "KV Cache Compression and Dynamic Pruning in Production Serving":
+ *           Sec. 3 StreamingLLM (sinks + rolling window), Sec. 3 H2O
+ *           (cumulative attention score; evict the lowest while keeping sinks
+ *           and the local window), Sec. 5 (GQA: pool importance over the
+ *           q-heads of a KV group; ragged per-head lengths; compaction).
+ *   [Kelle] "Kelle: Co-design KV Caching and eDRAM" summary: Sec. 2.2 (the
+ *           order of [k, v] pairs does not change the output, so a slot cache
+ *           needs no order), Sec. 4.1 (per-head eviction by accumulated
+ *           attention; prefill importance as column sums of the prompt's
+ *           attention; initial and recent tokens are kept).
+ *   [HeadKV] "Not All Heads Matter": Sec. 3.2 (a budget per head).
+ *
+ * Conventions
+ *   - Every data pointer is a DEVICE pointer owned by the caller, except the
+ *     three descriptor structs, which live in host memory and are read during
+ *     the call only.  The library keeps no pointer after a call returns.
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream).  No call allocates device memory,
+ *     synchronises or issues a memset, so a sequence of calls can be captured
+ *     into a HIP graph.  Exception: hikv_device_status() synchronises.
+ *   - Calls that share a cache or a workspace must be ordered on one stream.
+ *   - Layouts are row-major; q-head h belongs to KV head h / G (G = Hq/Hkv).
+ *   - Host-detectable errors are returned synchronously and enqueue nothing.
+ *     Per-unit errors found on the device leave that (batch, KV head) unit
+ *     unchanged, zero its output rows, and set a sticky status word in the
+ *     workspace that hikv_device_status() reports.
+ */
+#ifndef HIKV_H
+#define HIKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of K, V, q, k_new, v_new, q_obs. */
+#define HIKV_F32 0
+#define HIKV_BF16 1
+
+/* Status codes. */
+#define HIKV_OK 0
+#define HIKV_EINVAL (-1)       /* null pointer, bad shape/policy, workspace too small */
+#define HIKV_EUNSUPPORTED (-2) /* head_dim not 64/128, group size not 1/2/4/8, too many units, no gfx950 */
+#define HIKV_EDEVICE (-3)      /* a HIP runtime call or kernel launch failed */
+#define HIKV_ECAPACITY (-4)    /* device: len + 1 > capacity for some unit */
+#define HIKV_EBUDGET (-5)      /* device: budget < n_sink or budget > capacity for some unit */
+
+typedef struct hikv_shape {
+  int32_t batch;       /* B >= 0 (0: every call is a no-op) */
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t capacity;    /* slots per (batch, KV head) */
+  int32_t kv_dtype;    /* HIKV_F32 or HIKV_BF16; q, k_new, v_new, q_obs use it too */
+  float scale;         /* logit scale; <= 0 -> 1/sqrt(head_dim) */
+} hikv_shape;
+
+/* The cache.  One "unit" is a (batch b, KV head j) pair, u = b*Hkv + j.
+ * Slots [0, len[u]) of a unit are live, in no particular order ([Kelle]
+ * Sec. 2.2); pos holds each slot's absolute token position. */
+typedef struct hikv_cache {
+  void *k;        /* [B][Hkv][capacity][D] kv_dtype */
+  void *v;        /* [B][Hkv][capacity][D] kv_dtype */
+  int32_t *pos;   /* [B][Hkv][capacity] */
+  float *imp;     /* [B][Hkv][capacity] cumulative importance ([Blog] Sec. 3 H2O) */
+  int32_t *len;   /* [B][Hkv] */
+} hikv_cache;
+
+typedef struct hikv_policy {
+  const int32_t *budget;   /* [B][Hkv] device per-unit budgets ([HeadKV] Sec. 3.2), or NULL */
+  int32_t budget_all;      /* budget of every unit when `budget` is NULL */
+  int32_t n_sink;          /* S: positions 0..S-1 are never evicted */
+  int32_t n_recent;        /* W: the W' = min(W, budget - S) newest positions are never evicted */
+  int32_t stage2_channels; /* r: 0 = Stage II off; else 1..D channels per q-head ([HiKV] Sec. III-C) */
+  int32_t stage2_tokens;   /* k_T >= 1: tokens in Stage II's exact softmax (used when r > 0) */
+} hikv_policy;
+
+/* Optional Stage II selections written by hikv_decode_step (device pointers,
+ * each may be NULL).  For tests and inspection. */
+typedef struct hikv_debug {
+  int32_t *sel_channels;   /* [B][Hq][r] chosen channels, ascending */
+  int32_t *sel_tokens;     /* [B][Hq][k_T] positions of the exact-softmax tokens, ascending, -1 padded */
+  int32_t *sel_count;      /* [B][Hq] number of exact-softmax tokens, min(k_T, len + 1) */
+} hikv_debug;
+
+/* Bytes of device workspace the decode step and hikv_evict need for this
+ * shape and policy.  The workspace must be zero-filled before its first use;
+ * the library leaves it ready for the next call.  0 on a bad shape. */
+size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
+
+/* One decode step for every unit ([HiKV] Algorithm 1 with [Blog] Sec. 3 H2O
+ * eviction; cfg. [Kelle] Sec. 4.1):
+ *   1. append: slot len[u] <- (k_new[b][j], v_new[b][j]), pos = new_pos[b],
+ *      importance 0; len[u] += 1;
+ *   2. for every q-head h of KV head j: out[b][h] = softmax(scale * q.K^T) V
+ *      over the live slots (the new token attends to itself);
+ *      Stage II (r > 0): the logits use only the r channels of largest |q_d|
+ *      (ties: lower channel); out = exact full-D softmax restricted to the
+ *      k_T tokens with the largest reduced logit (ties: lower position);
+ *   3. imp[slot] += sum over the group's q-heads of the slot's probability
+ *      (Stage II: the reduced-logit softmax);
+ *   4. if len[u] > budget: keep the protected tokens (pos < S or
+ *      pos > new_pos[b] - W') and the budget - |protected| other tokens with
+ *      the highest (importance, then lower position); compact them into
+ *      slots [0, budget); len[u] = budget.
+ * q: [B][Hq][D]; k_new, v_new: [B][Hkv][D]; new_pos: [B] int32;
+ * out: [B][Hq][D] float32.  `debug` may be NULL. */
+int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                     const void *q, const void *k_new, const void *v_new,
+                     const int32_t *new_pos, float *out, void *ws, size_t ws_bytes,
+                     const hikv_debug *debug, void *stream);
+
+/* Compress every unit over its budget to exactly its budget with step 4 of
+ * hikv_decode_step, using the current importance; newest_pos[b] anchors the
+ * recent window ([Blog] Sec. 3 H2O; [Kelle] Sec. 4.1, prefill eviction). */
+int hikv_evict(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+               const int32_t *newest_pos, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes hikv_prefill_scores needs for n_obs observation queries. */
+size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t n_obs);
+
+/* Add prompt-side importance ([Kelle] Sec. 4.1 prefill: column sums of the
+ * prompt's attention; [HiKV] Sec. III-B/III-D: the windowed sum).  For every
+ * observation query i at position q_pos[b][i] and every q-head of a KV group,
+ * the causal softmax row over the unit's live tokens with pos <= q_pos is
+ * formed; a token's share is added to its importance when window == 0, or
+ * when 0 <= q_pos - pos < window.  q_obs: [B][Hq][n_obs][D]; q_pos: [B][n_obs]. */
+int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *cache, const void *q_obs,
+                        const int32_t *q_pos, int32_t n_obs, int32_t window, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* Synchronise `stream`, return the first device-side error recorded in `ws`
+ * since it was last cleared (HIKV_OK if none), and clear it when `clear`. */
+int hikv_device_status(void *ws, int clear, void *stream);
+
+/* Static description of a status code. */
+const char *hikv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,88 @@
+"""The C-ABI library loads and exports every entry point include/hikv.h
+declares; host-side argument checks return their codes without touching a
+GPU (no compute calls here)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from importance_aware_kv_amd import hikv as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hikv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hikv_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("hikv_decode_step", "hikv_evict", "hikv_prefill_scores", "hikv_workspace_bytes",
+                 "hikv_device_status", "hikv_status_string"):
+        assert want in names
+    assert set(names) == set(H.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = H.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", H.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hikv_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def _shape(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, capacity=64, kv_dtype=H.HIKV_BF16,
+             scale=0.0)
+    d.update(kw)
+    return H.make_shape(**d)
+
+
+def test_workspace_sizing_and_bad_shapes():
+    pol = H.make_policy(budget_all=32, n_sink=4, n_recent=8)
+    assert H.hikv_workspace_bytes(_shape(), pol) > 0
+    assert H.hikv_workspace_bytes(_shape(n_q_heads=6, n_kv_heads=4), pol) == 0   # Hq % Hkv
+    assert H.hikv_workspace_bytes(_shape(head_dim=96), pol) == 0                  # D
+    assert H.hikv_workspace_bytes(_shape(n_q_heads=32, n_kv_heads=2), pol) == 0   # G = 16
+    assert H.hikv_workspace_bytes(_shape(kv_dtype=7), pol) == 0
+    bad_pol = H.make_policy(budget_all=32, n_sink=-1)
+    assert H.hikv_workspace_bytes(_shape(), bad_pol) == 0
+    s2 = H.make_policy(budget_all=32, stage2_channels=32, stage2_tokens=256)
+    assert H.hikv_workspace_bytes(_shape(), s2) > H.hikv_workspace_bytes(_shape(), pol)
+    assert H.hikv_workspace_bytes(_shape(), H.make_policy(stage2_channels=200, stage2_tokens=1)) == 0
+
+
+def test_decode_step_host_checks():
+    L = H.lib()
+    pol = H.make_policy(budget_all=32, n_sink=4, n_recent=8)
+    fake = C.c_void_p(0x1000)
+    cache = H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+
+    def call(shape, cache=cache, pol=pol, q=fake, ws=fake, ws_bytes=1 << 30):
+        return L.hikv_decode_step(C.byref(shape), C.byref(cache), C.byref(pol), q, fake, fake, fake,
+                                  fake, ws, ws_bytes, None, None)
+
+    assert call(_shape(n_q_heads=6, n_kv_heads=4)) == H.HIKV_EINVAL
+    assert call(_shape(head_dim=96)) == H.HIKV_EUNSUPPORTED
+    assert call(_shape(n_q_heads=48, n_kv_heads=3)) == H.HIKV_EUNSUPPORTED          # G = 16
+    assert call(_shape(batch=4096, n_kv_heads=2, n_q_heads=2)) == H.HIKV_EUNSUPPORTED  # units
+    assert call(_shape(), cache=H.hikv_cache(0, 0x1000, 0x1000, 0x1000, 0x1000)) == H.HIKV_EINVAL
+    assert call(_shape(), q=None) == H.HIKV_EINVAL
+    assert call(_shape(), q=C.c_void_p(0x1008)) == H.HIKV_EINVAL                    # alignment
+    assert call(_shape(), ws_bytes=16) == H.HIKV_EINVAL                             # workspace
+    assert call(_shape(), pol=H.make_policy(budget_all=8, n_recent=-2)) == H.HIKV_EINVAL
+    assert call(_shape(batch=0)) == H.HIKV_OK                                       # empty batch
+    assert L.hikv_evict(C.byref(_shape()), C.byref(cache), C.byref(pol), None, fake, 1 << 30,
+                        None) == H.HIKV_EINVAL
+    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, -1, 0, fake,
+                                 1 << 30, None) == H.HIKV_EINVAL
+    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, 0, 0, fake,
+                                 1 << 30, None) == H.HIKV_OK
+    assert H.status_string(H.HIKV_ECAPACITY) == "cache capacity exceeded"
