@@ -4,6 +4,7 @@
 // hikv_device_status, which is documented to synchronise).
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "hikv_launch.h"
@@ -90,6 +91,13 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
 
 inline int dev_err(hipError_t e) { return e == hipSuccess ? HIKV_OK : HIKV_EDEVICE; }
 
+// HIKV_MULTI_KERNEL=1 selects the four-launch Stage I path (for comparison
+// and tests); the two-launch step is the default.  Read on every call.
+bool multi_kernel_path() {
+  const char *e = getenv("HIKV_MULTI_KERNEL");
+  return e && e[0] == '1';
+}
+
 }  // namespace
 
 extern "C" size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy) {
@@ -128,6 +136,7 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   const int dt = shape->kv_dtype;
   hipError_t e;
   if (a.r == 0) {
+    if (!multi_kernel_path()) return dev_err(launch_step(a, dt, s));
     if ((e = launch_attn_tiles(a, dt, true, false, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
   } else {

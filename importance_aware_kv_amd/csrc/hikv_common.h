@@ -13,6 +13,7 @@ constexpr int kWave = 64;
 constexpr int kMaxUnits = 4096;     // (batch, KV head) units per call
 constexpr int kTileMin = 64;        // smallest split-K tile, tokens
 constexpr int kTilesTarget = 512;   // split-K tiles aimed for per step (2 per CU)
+constexpr int kMaxGrid = 2048;      // upper bound on resident workgroups (256 CUs x 8)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -21,6 +22,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---------------------------------------------------------------------------
 struct Ws {
   int32_t *status;      // [1] sticky first device-side error
+  int32_t *tinfo;       // [max_tiles][4] per-tile record from the attention launch
+  float *fz_newimp;     // [n_units] the new token's importance this step
   uint32_t *ticket;     // [n_units] last-tile-arrives counters (self-resetting)
   int32_t *plan;        // [n_units + 4]: tile base per unit (exclusive prefix), then
                         //   [n_units] = total tiles, [+1] = tile size T
@@ -37,19 +40,22 @@ struct Ws {
   int32_t *tcount;      // [B*Hq]
 };
 
+constexpr int kWsParts = 16;
 struct WsSizes {
-  size_t off[14];
+  size_t off[kWsParts];
   size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline int max_tiles_for(int n_units) { return kTilesTarget + n_units + 8; }
+inline int max_tiles_for(int n_units) { return kMaxGrid + n_units + 8; }
 
 inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
   const size_t U = (size_t)B * Hkv, G = (size_t)(Hq / Hkv), MT = (size_t)max_tiles_for((int)U);
-  const size_t sz[14] = {
-      sizeof(int32_t) * 64,            // status (+ spare)
+  const size_t sz[kWsParts] = {
+      512,                             // status (+ spare)
+      sizeof(int32_t) * 4 * MT,        // tinfo
+      sizeof(float) * U,               // fz_newimp
       sizeof(uint32_t) * U,            // ticket
       sizeof(int32_t) * (U + 4),       // plan
       sizeof(float) * U * G * 2,       // stats
@@ -66,7 +72,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
   };
   WsSizes w;
   size_t o = 0;
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < kWsParts; ++i) {
     w.off[i] = o;
     o += align256(sz[i]);
   }
@@ -78,19 +84,21 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   char *b = static_cast<char *>(base);
   Ws w;
   w.status = reinterpret_cast<int32_t *>(b + s.off[0]);
-  w.ticket = reinterpret_cast<uint32_t *>(b + s.off[1]);
-  w.plan = reinterpret_cast<int32_t *>(b + s.off[2]);
-  w.stats = reinterpret_cast<float *>(b + s.off[3]);
-  w.part_ml = reinterpret_cast<float *>(b + s.off[4]);
-  w.part_acc = reinterpret_cast<float *>(b + s.off[5]);
-  w.logits = reinterpret_cast<float *>(b + s.off[6]);
-  w.tile_key = reinterpret_cast<uint64_t *>(b + s.off[7]);
-  w.tile_slot = reinterpret_cast<int32_t *>(b + s.off[8]);
-  w.holes = reinterpret_cast<int32_t *>(b + s.off[9]);
-  w.movers = reinterpret_cast<int32_t *>(b + s.off[10]);
-  w.chmask = reinterpret_cast<uint32_t *>(b + s.off[11]);
-  w.tsel = reinterpret_cast<int32_t *>(b + s.off[12]);
-  w.tcount = reinterpret_cast<int32_t *>(b + s.off[13]);
+  w.tinfo = reinterpret_cast<int32_t *>(b + s.off[1]);
+  w.fz_newimp = reinterpret_cast<float *>(b + s.off[2]);
+  w.ticket = reinterpret_cast<uint32_t *>(b + s.off[3]);
+  w.plan = reinterpret_cast<int32_t *>(b + s.off[4]);
+  w.stats = reinterpret_cast<float *>(b + s.off[5]);
+  w.part_ml = reinterpret_cast<float *>(b + s.off[6]);
+  w.part_acc = reinterpret_cast<float *>(b + s.off[7]);
+  w.logits = reinterpret_cast<float *>(b + s.off[8]);
+  w.tile_key = reinterpret_cast<uint64_t *>(b + s.off[9]);
+  w.tile_slot = reinterpret_cast<int32_t *>(b + s.off[10]);
+  w.holes = reinterpret_cast<int32_t *>(b + s.off[11]);
+  w.movers = reinterpret_cast<int32_t *>(b + s.off[12]);
+  w.chmask = reinterpret_cast<uint32_t *>(b + s.off[13]);
+  w.tsel = reinterpret_cast<int32_t *>(b + s.off[14]);
+  w.tcount = reinterpret_cast<int32_t *>(b + s.off[15]);
   return w;
 }
 

@@ -20,6 +20,10 @@ hipError_t launch_accumulate(const StepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_bulk_evict(const StepArgs &a, int dtype, const int32_t *newest,
                              bool from_decode, hipStream_t s);
 
+// The Stage I step in two launches (attention tiles, then statistics,
+// output, importance and eviction).
+hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s);
+
 // Stage II.
 hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_stage2_tokens(const StepArgs &a, hipStream_t s);

@@ -52,6 +52,32 @@ def test_tiny_free_running_matches_oracle():
         assert list(ref.live_positions(g, 0, 0)) == list(ref.live_positions(st, 0, 0)), t
 
 
+@pytest.fixture
+def multi_kernel_path(monkeypatch):
+    """Route Stage I through the multi-kernel path instead of the single launch."""
+    monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
+    yield
+
+
+def test_multi_kernel_path_lockstep(multi_kernel_path):
+    w = W.workload("llama8b", ctx=900, steps=3, batch=2)
+    w.budget_all, w.n_recent = 200, 16
+    d = W.generate(w)
+    lockstep(_run(w, d), d, w.steps, tag="multi-kernel")
+    wt = W.workload("tiny", steps=6)
+    dt = W.generate(wt)
+    lockstep(_run(wt, dt), dt, wt.steps, tag="multi-kernel tiny")
+
+
+def test_many_units_use_multi_kernel_path():
+    """More units than one resident grid handles: the library switches paths."""
+    B, Hkv, G, D, cap = 40, 8, 2, 64, 96
+    lens = np.random.Generator(np.random.PCG64(3)).integers(0, 95, size=(B, Hkv))
+    st = W.random_cache(41, B, G * Hkv, Hkv, D, W.BF16, cap, lens)
+    data = {k: v[None] for k, v in W.random_step(42, B, G * Hkv, Hkv, D, W.BF16, st["newest"]).items()}
+    lockstep(GpuRun(st, G * Hkv, budget_all=48, n_sink=2, n_recent=8), data, 1, tag="320 units")
+
+
 def test_llama8b_reduced_lockstep():
     w = W.workload("llama8b", ctx=1000, steps=3, batch=2)
     w.budget_all, w.n_recent = 256, 32
@@ -136,16 +162,21 @@ def test_edge_cases_streaming_zero_budget_errors():
     run2 = GpuRun(ref.copy_state(st2), G * Hkv, budget=np.array([[8, 2, 8, 8]]), n_sink=4, n_recent=2)
     run2.step(d2["q"], d2["k_new"], d2["v_new"], d2["new_pos"], expect=H.HIKV_EBUDGET)
     assert run2.dev.to_numpy()["len"].tolist() == [[6, 20, 8, 8]]
-    # StreamingLLM: budget = S + W keeps exactly sinks + window, and matches the oracle
-    st3 = W.random_cache(13, B, G * Hkv, Hkv, D, W.BF16, cap, [[10, 20, 30, 35]], shuffle_pos=True)
-    d3 = {k: v[None] for k, v in W.random_step(14, B, G * Hkv, Hkv, D, W.BF16, st3["newest"]).items()}
+    # StreamingLLM: with contiguous history, budget = S + W keeps exactly the
+    # sinks and the window, and matches the oracle
+    lens3 = [35, 35, 35, 35]
+    st3 = W.random_cache(13, B, G * Hkv, Hkv, D, W.BF16, cap, [lens3])
+    rng = np.random.Generator(np.random.PCG64(17))
+    for j, n in enumerate(lens3):
+        st3["pos"][0, j, :n] = rng.permutation(n).astype(np.int32)  # shuffled slots
+    st3["newest"] = 35
+    d3 = {k: v[None] for k, v in W.random_step(14, B, G * Hkv, Hkv, D, W.BF16, 35).items()}
     run3 = GpuRun(ref.copy_state(st3), G * Hkv, budget_all=7, n_sink=3, n_recent=4)
     lockstep(run3, d3, 1, tag="streaming")
     post3 = run3.dev.to_numpy()
-    newest = int(st3["newest"])
     for j in range(Hkv):
         live = sorted(ref.live_positions(post3, 0, j).tolist())
-        assert live == [0, 1, 2] + list(range(newest - 3, newest + 1)), (j, live)
+        assert live == [0, 1, 2, 32, 33, 34, 35], (j, live)
 
 
 def test_evict_standalone_matches_oracle():
