@@ -42,6 +42,7 @@ def main():
     ap.add_argument("--workload", default="headkv32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-hint", action="store_true", help="do not pass host lengths")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no "
@@ -82,6 +83,10 @@ def main():
     budget_t = torch.from_numpy(budget).cuda()
     pol = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
     ws = H.workspace(layers[0].shape, pol)
+    # The caller's host copy of every layer's lengths (a serving loop tracks
+    # them anyway); passed as the length hint so the tile plan is made on the
+    # host.  --no-hint measures the device-derived plan instead.
+    host_len = [np.full((B, Hkv), w.ctx, dtype=np.int32) for _ in range(args.layers)]
     q_all = H.to_device(d["q"])
     kn_all = H.to_device(d["k_new"])
     vn_all = H.to_device(d["v_new"])
@@ -94,10 +99,15 @@ def main():
         c = layers[li]
         n = layer_step[li]
         layer_step[li] += 1
-        code = H.hikv_decode_step(c.shape, c.cache, pol, q_all[n % n_inputs], kn_all[n % n_inputs],
+        p = pol
+        if not args.no_hint:
+            p = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
+                              len_hint=host_len[li])
+        code = H.hikv_decode_step(c.shape, c.cache, p, q_all[n % n_inputs], kn_all[n % n_inputs],
                                   vn_all[n % n_inputs], pos_all[n], out, ws)
         if code != 0:
             raise RuntimeError(f"hikv_decode_step: {H.status_string(code)}")
+        host_len[li] = np.minimum(host_len[li] + 1, budget).astype(np.int32)
 
     stream = torch.cuda.current_stream()
     # Compression step of every layer copy (32769 tokens -> budget).

@@ -119,6 +119,11 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ws)) return HIKV_EINVAL;
   const WsSizes sz = sizes_for(shape, policy);
   if (ws_bytes < sz.total) return HIKV_EINVAL;
+  if (policy->len_hint) {
+    const int U = shape->batch * shape->n_kv_heads;
+    for (int u = 0; u < U; ++u)
+      if (policy->len_hint[u] < 0 || policy->len_hint[u] + 1 > shape->capacity) return HIKV_EINVAL;
+  }
   if ((st = arch_ok()) != HIKV_OK) return st;
 
   StepArgs a = make_args(shape, cache, policy, ws_carve(ws, sz));
@@ -136,7 +141,10 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   const int dt = shape->kv_dtype;
   hipError_t e;
   if (a.r == 0) {
-    if (!multi_kernel_path()) return dev_err(launch_step(a, dt, s));
+    if (!multi_kernel_path()) {
+      if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
+      return dev_err(launch_step(a, dt, s));
+    }
     if ((e = launch_attn_tiles(a, dt, true, false, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
   } else {

@@ -102,6 +102,15 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   return w;
 }
 
+// Tile plan computed on the host from a caller-supplied copy of len[] (the
+// kernels then skip deriving it from device memory).  n == 0: no host plan.
+constexpr int kHostPlanUnits = 64;
+struct HostPlan {
+  int32_t n, T, ntiles;
+  int32_t base[kHostPlanUnits + 1];  // first tile of each unit; base[n] = ntiles
+  int32_t L[kHostPlanUnits];         // tokens after the append (0: unit not planned)
+};
+
 // Everything a decode-step kernel needs, passed by value.
 struct StepArgs {
   int B, Hq, Hkv, D, cap, G, n_units;
@@ -120,6 +129,7 @@ struct StepArgs {
   float *out;
   int32_t *dbg_channels, *dbg_tokens, *dbg_count;
   Ws ws;
+  HostPlan hp;
 };
 
 // ---------------------------------------------------------------------------

@@ -23,6 +23,9 @@ hipError_t launch_bulk_evict(const StepArgs &a, int dtype, const int32_t *newest
 // The Stage I step in two launches (attention tiles, then statistics,
 // output, importance and eviction).
 hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s);
+// Host-side tile plan from a host copy of len[] (fills a.hp); false when it
+// does not apply (too many units), in which case the kernels derive it.
+bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint);
 
 // Stage II.
 hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s);

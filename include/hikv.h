@@ -93,6 +93,13 @@ typedef struct hikv_policy {
   int32_t n_recent;        /* W: the W' = min(W, budget - S) newest positions are never evicted */
   int32_t stage2_channels; /* r: 0 = Stage II off; else 1..D channels per q-head ([HiKV] Sec. III-C) */
   int32_t stage2_tokens;   /* k_T >= 1: tokens in Stage II's exact softmax (used when r > 0) */
+  const int32_t *len_hint; /* optional HOST copy of len[] as it is before this call, or NULL.
+                              With at most 64 units the split-K tile plan is then computed on
+                              the host and passed with the launch, which saves the kernels a
+                              dependent device-memory round trip.  A hint with len + 1 >
+                              capacity or len < 0 is rejected (HIKV_EINVAL); a hint that
+                              disagrees with the device's len[] sets HIKV_EINVAL in the
+                              device status and that call's results are undefined. */
 } hikv_policy;
 
 /* Optional Stage II selections written by hikv_decode_step (device pointers,

@@ -34,12 +34,15 @@ def say(*a):
 
 class GpuRun:
     def __init__(self, state, n_q_heads, *, budget=None, budget_all=0, n_sink=0, n_recent=0,
-                 r=0, kT=0, scale=0.0):
+                 r=0, kT=0, scale=0.0, hint=False):
         self.Hq = n_q_heads
+        self.hint = hint
+        self.pol_args = None
         self.dev = H.DeviceCache(state, n_q_heads, scale=scale)
         self.budget_np = None if budget is None else np.ascontiguousarray(budget, dtype=np.int32)
         self.budget_t = None if budget is None else torch.from_numpy(self.budget_np).cuda()
         self.pol = H.make_policy(self.budget_t, budget_all, n_sink, n_recent, r, kT)
+        self.pol_args = (self.budget_t, budget_all, n_sink, n_recent, r, kT)
         self.kw = dict(budget=self.budget_np, budget_all=budget_all, n_sink=n_sink,
                        n_recent=n_recent, stage2_channels=r, stage2_tokens=kT, scale=scale)
         self.ws = H.workspace(self.dev.shape, self.pol)
@@ -54,10 +57,17 @@ class GpuRun:
                 sel_count=torch.full((sh.batch, n_q_heads), -7, dtype=torch.int32, device="cuda"))
             self.dbg = H.hikv_debug(*[self.dbg_t[f].data_ptr() for f, _ in H.hikv_debug._fields_])
 
-    def step(self, q, k_new, v_new, new_pos, expect=H.HIKV_OK):
+    def step(self, q, k_new, v_new, new_pos, expect=H.HIKV_OK, hint_override=None):
         qt, kt, vt = H.to_device(q), H.to_device(k_new), H.to_device(v_new)
         pt = torch.from_numpy(np.ascontiguousarray(new_pos, dtype=np.int32)).cuda()
-        code = H.hikv_decode_step(self.dev.shape, self.dev.cache, self.pol, qt, kt, vt, pt, self.out,
+        pol = self.pol
+        hint = None
+        if self.hint or hint_override is not None:
+            # the caller's own copy of len[] (here read back from the device)
+            hint = (np.ascontiguousarray(self.dev.len.cpu().numpy(), dtype=np.int32)
+                    if hint_override is None else np.ascontiguousarray(hint_override, dtype=np.int32))
+            pol = H.make_policy(*self.pol_args, len_hint=hint)
+        code = H.hikv_decode_step(self.dev.shape, self.dev.cache, pol, qt, kt, vt, pt, self.out,
                                   self.ws, debug=self.dbg)
         assert code == H.HIKV_OK, H.status_string(code)
         st = H.hikv_device_status(self.ws, clear=True)

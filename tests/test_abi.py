@@ -85,4 +85,9 @@ def test_decode_step_host_checks():
                                  1 << 30, None) == H.HIKV_EINVAL
     assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, 0, 0, fake,
                                  1 << 30, None) == H.HIKV_OK
+    import numpy as np
+    bad_hint = np.array([10, 64, 3, 3], dtype=np.int32)   # 64 + 1 > capacity 64
+    assert call(_shape(), pol=H.make_policy(budget_all=8, len_hint=bad_hint)) == H.HIKV_EINVAL
+    neg_hint = np.array([10, -1, 3, 3], dtype=np.int32)
+    assert call(_shape(), pol=H.make_policy(budget_all=8, len_hint=neg_hint)) == H.HIKV_EINVAL
     assert H.status_string(H.HIKV_ECAPACITY) == "cache capacity exceeded"

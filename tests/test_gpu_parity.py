@@ -78,6 +78,28 @@ def test_many_units_use_multi_kernel_path():
     lockstep(GpuRun(st, G * Hkv, budget_all=48, n_sink=2, n_recent=8), data, 1, tag="320 units")
 
 
+def test_host_length_hint_path():
+    """The caller's host copy of len[] drives the tile plan; results unchanged."""
+    w = W.workload("headkv32k", ctx=2000, steps=3, batch=2)
+    w.budgets = np.tile(W.dirichlet_budgets(78, 8, 8 * 150, 16, 600), (2, 1))
+    d = W.generate(w)
+    run = _run(w, d, hint=True)
+    lockstep(run, d, w.steps, tag="host-plan")
+    wt = W.workload("tiny", steps=5)
+    dt = W.generate(wt)
+    lockstep(_run(wt, dt, hint=True), dt, wt.steps, tag="host-plan tiny")
+
+
+def test_wrong_host_length_hint_is_reported():
+    w = W.workload("llama8b", ctx=300, steps=1, batch=1)
+    w.budget_all, w.n_recent = 100, 8
+    d = W.generate(w)
+    run = _run(w, d)
+    wrong = np.full((1, 8), 250, dtype=np.int32)      # device holds 300 per unit
+    run.step(d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], expect=H.HIKV_EINVAL,
+             hint_override=wrong)
+
+
 def test_llama8b_reduced_lockstep():
     w = W.workload("llama8b", ctx=1000, steps=3, batch=2)
     w.budget_all, w.n_recent = 256, 32
