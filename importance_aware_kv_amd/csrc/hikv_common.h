@@ -38,9 +38,10 @@ struct Ws {
   uint32_t *chmask;     // [B*Hq][D/32] Stage II channel mask
   int32_t *tsel;        // [B*Hq][k_T] Stage II exact-softmax slots
   int32_t *tcount;      // [B*Hq]
+  int32_t *urec;        // [n_units][4] per-unit plan of the step: first tile, tiles, tokens
 };
 
-constexpr int kWsParts = 16;
+constexpr int kWsParts = 17;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -69,6 +70,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
       sizeof(uint32_t) * B * Hq * ((D + 31) / 32),  // chmask
       sizeof(int32_t) * B * Hq * (size_t)(kT > 0 ? kT : 1),  // tsel
       sizeof(int32_t) * B * Hq,        // tcount
+      sizeof(int32_t) * 4 * U,         // urec
   };
   WsSizes w;
   size_t o = 0;
@@ -99,6 +101,7 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.chmask = reinterpret_cast<uint32_t *>(b + s.off[13]);
   w.tsel = reinterpret_cast<int32_t *>(b + s.off[14]);
   w.tcount = reinterpret_cast<int32_t *>(b + s.off[15]);
+  w.urec = reinterpret_cast<int32_t *>(b + s.off[16]);
   return w;
 }
 

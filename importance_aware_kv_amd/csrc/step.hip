@@ -55,6 +55,21 @@ __device__ __forceinline__ uint64_t ld_ag(const uint64_t *p) {
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Load a wave-uniform value through the vector memory path.  A scalar load
+// shares its counter (lgkmcnt) with the kernel-argument loads, so the first
+// wait for an argument would also wait for this round trip.  z is a zero the
+// compiler cannot see through (vzero(), taken once before any load: the asm
+// that makes it may otherwise wait for loads in flight).
+__device__ __forceinline__ int vzero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+template <typename T>
+__device__ __forceinline__ T ld_vec(const T *p, int z) {
+  return p[z];
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
@@ -62,21 +77,13 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
-// Per-tile description K1 hands to K2 (16 bytes).
-struct TileRec {
-  int32_t u_s;     // unit << 12 | tile index within the unit; -1: no tile
-  int32_t nt;      // tiles of the unit
-  int32_t t0_len;  // first token << 0 (t0); length packed in L below
-  int32_t L_t1;    // unused (kept for alignment)
-};
-
 struct Plan {
   int valid, u, s, nt, t0, t1, L, T;
 };
 
 // Every wave computes the same plan; lanes own contiguous unit ranges, so the
 // tile ids of a unit are consecutive.
-__device__ Plan wave_plan(const StepArgs &a, int tile, int ntarget) {
+__device__ Plan wave_plan(const StepArgs &a, int tile, int ntarget, bool write_rec) {
   const int lane = threadIdx.x & 63;
   const int U = a.n_units;
   const int per = (U + 63) >> 6;
@@ -114,6 +121,18 @@ __device__ Plan wave_plan(const StepArgs &a, int tile, int ntarget) {
   p.T = T;
   p.valid = m != 0ull;
   int info[4] = {0, 0, 0, 0};
+  if (write_rec) {  // the per-unit records the second launch reads
+    int bse = excl;
+    for (int k = 0; k < per; ++k) {
+      const int u = u0 + k;
+      if (u >= U) break;
+      const int len = a.len[u];
+      const int L = unit_error(a, u, len, 1) ? 0 : len + 1;
+      const int n = (L + T - 1) / T;
+      reinterpret_cast<int4 *>(a.ws.urec)[u] = make_int4(bse, n, L, 0);
+      bse += n;
+    }
+  }
   if (own) {
     int bse = excl;
     for (int k = 0; k < per; ++k) {
@@ -142,22 +161,23 @@ __device__ Plan wave_plan(const StepArgs &a, int tile, int ntarget) {
 }
 
 // Plan from the kernel arguments (host-computed from the caller's copy of
-// len[]): a uniform binary search over the tile bases.
+// len[]).  Lane i reads unit i's end tile and length, so the lookup costs one
+// round trip: the unit is the number of units that end at or before the tile.
 __device__ Plan host_plan(const StepArgs &a, int tile) {
+  const int lane = threadIdx.x & 63;
+  const int n = a.hp.n;
+  const int bend = a.hp.base[lane + 1];
+  const int Lv = a.hp.L[lane];
+  const int u = __popcll(__ballot(lane < n && bend <= tile));
   Plan p;
   p.T = a.hp.T;
-  p.valid = tile < a.hp.ntiles;
-  p.u = p.s = p.nt = p.t0 = p.t1 = p.L = 0;
-  if (!p.valid) return p;
-  int lo = 0, hi = a.hp.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.hp.base[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  p.u = lo;
-  p.s = tile - a.hp.base[lo];
-  p.nt = a.hp.base[lo + 1] - a.hp.base[lo];
-  p.L = a.hp.L[lo];
+  p.valid = u < n;
+  const int uu = p.valid ? u : 0;
+  const int b0 = uu ? __builtin_amdgcn_readlane(bend, uu - 1) : 0;
+  p.u = uu;
+  p.s = tile - b0;
+  p.nt = __builtin_amdgcn_readlane(bend, uu) - b0;
+  p.L = __builtin_amdgcn_readlane(Lv, uu);
   p.t0 = p.s * p.T;
   p.t1 = min(p.t0 + p.T, p.L);
   return p;
@@ -198,6 +218,113 @@ __device__ __forceinline__ void stage_sub(char *kb, char *vb, const char *kc, co
   }
 }
 
+// LDS reads of rows that arrived by DMA.  Written as one asm block so that the
+// compiler, which cannot tell the three sub-chunk buffers apart, does not
+// insert a vmcnt(0) before them (the explicit vmcnt chain already covers the
+// sub-chunk being read); the block waits for its own reads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ __forceinline__ void lds_read_rows(uint4 &k0, uint4 &k1, uint4 &v0, uint4 &v1, uint32_t ak0,
+                                              uint32_t ak1, uint32_t av0, uint32_t av1) {
+  u32x4 a, b, c, d;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(ak0), "v"(ak1), "v"(av0), "v"(av1)
+      : "memory");
+  k0 = make_uint4(a.x, a.y, a.z, a.w);
+  k1 = make_uint4(b.x, b.y, b.z, b.w);
+  v0 = make_uint4(c.x, c.y, c.z, c.w);
+  v1 = make_uint4(d.x, d.y, d.z, d.w);
+}
+
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Ends the wave here, so that the code after it does not merge with this path
+// at a common exit (where the compiler would wait for both paths' loads).
+__device__ __forceinline__ void end_wave() { __builtin_amdgcn_endpgm(); }
+
+// Reductions across the token rows of a wave.  A token row is LPR lanes wide
+// and the rows of a wave are lanes i, i ^ LPR, i ^ 2 LPR, ...  The permlane
+// swaps exchange 32- and 16-lane halves between two registers without LDS;
+// applied to two different values at once and followed by one add, each
+// swap halves the registers still to reduce (a reduce-scatter).  The swaps
+// are asm: the compiler builtin, given one value for both operands, treats
+// its two results as equal.
+__device__ __forceinline__ void permlane16_swap(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// Reduce N values per lane over the rows of a wave (rows LPR = 8, 16 or 32
+// lanes wide).  S = 1 swap step for 32-lane rows, else 2.  Afterwards v[i],
+// i < N >> S, holds in lane part p = lane >> (6 - S) the reduction of value
+// i + p * (N >> S); rows of 8 lanes are finished with DPP (row_ror:8), and
+// there lanes l and l ^ 8 hold the same results.
+template <int LPR>
+constexpr int swap_steps() { return LPR >= 32 ? 1 : 2; }
+template <int LPR, bool MAX, int N>
+__device__ __forceinline__ void rows_reduce(float (&v)[N]) {
+  constexpr int S = swap_steps<LPR>();
+  static_assert(N % (1 << S) == 0, "values must split over the lane parts");
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float x = v[i], y = v[i + N / 2];
+    permlane32_swap(x, y);
+    v[i] = op(x, y);
+  }
+  if constexpr (S == 2) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      float x = v[i], y = v[i + N / 4];
+      permlane16_swap(x, y);
+      v[i] = op(x, y);
+    }
+  }
+  if constexpr (LPR == 8) {
+#pragma unroll
+    for (int i = 0; i < (N >> S); ++i)
+      v[i] = op(v[i], __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[i]), 0x128,
+                                                                            0xf, 0xf, false)));
+  }
+}
+
+// Workgroup barrier for LDS data only.  __syncthreads() also waits for every
+// global load and store of the wave to complete, which costs a memory round
+// trip when none of them matter to the LDS exchange.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup barrier for data that arrived by global->LDS DMA.  The caller has
+// already waited for its own DMA with an explicit vmcnt; __syncthreads() would
+// add a full vmcnt(0) and serialise the sub-chunk pipeline.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Units a device-side error excludes from the step: zero their output rows
+// and record the first error (device-derived plans only; with a host plan the
+// second launch does this).
+template <int G, int D>
+__device__ void error_sweep(const StepArgs &a) {
+  for (int u = threadIdx.x; u < a.n_units; u += kThreads) {
+    const int err = unit_error(a, u, a.len[u], 1);
+    if (err) {
+      set_status(a.ws.status, err);
+      const int b = u / a.Hkv, j = u - b * a.Hkv;
+      for (int i = 0; i < G * D; ++i) a.out[((size_t)(b * a.Hq + j * G)) * D + i] = 0.f;
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -209,8 +336,12 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   constexpr int CH = LY::CH, LPR = LY::LPR, TPW = LY::TPW, UR = LY::UR, TS = LY::TS, NSUB = LY::NSUB,
                 TC = LY::TC, NI = LY::NI, SUBB = LY::SUBB;
   constexpr int RB = LY::RB;
-  // LDS: NSUB sub-chunks, each K then V.
+  constexpr int QB = G * D * EL;  // the group's queries, bytes
+  static_assert(QB <= 4 * 1024, "one q DMA instruction per wave");
+  // LDS: NSUB sub-chunks, each K then V; the group's queries.
   __shared__ __attribute__((aligned(16))) char smem[NSUB * 2 * SUBB];
+  __shared__ __attribute__((aligned(16))) char qs[QB];
+  __shared__ __attribute__((aligned(16))) float lgs[TC * G];  // the chunk's logits
   __shared__ float sm_ml[4][G][2];
   float(*sm_acc)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);  // reused after the chunks
   static_assert(4 * G * D * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
@@ -218,27 +349,13 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = a.n_units;
-  const Plan pl = a.hp.n ? host_plan(a, blockIdx.x) : wave_plan(a, blockIdx.x, (int)gridDim.x - U);
+  const Plan pl = a.hp.n ? host_plan(a, blockIdx.x)
+                         : wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
 
-  if (blockIdx.x == 0) {  // units skipped by a device-side error
-    for (int u = tid; u < U; u += kThreads) {
-      const int err = unit_error(a, u, a.len[u], 1);
-      if (err) {
-        set_status(a.ws.status, err);
-        const int b = u / a.Hkv, j = u - b * a.Hkv;
-        for (int i = 0; i < G * D; ++i) a.out[((size_t)(b * a.Hq + j * G)) * D + i] = 0.f;
-      }
-    }
+  if (!pl.valid) {
+    if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
+    return;
   }
-  if (tid == 0 && !a.hp.n) {  // hand the device-derived plan to the second launch
-    int4 rec = make_int4(-1, 0, 0, 0);
-    if (pl.valid) rec = make_int4(pl.u, pl.s, pl.nt, pl.L);
-    reinterpret_cast<int4 *>(a.ws.tinfo)[blockIdx.x] = rec;
-    if (blockIdx.x == 0) a.ws.plan[0] = pl.T;
-  }
-  if (!pl.valid) return;
-  // A host plan must describe the device's lengths.
-  const int len_dev = a.hp.n ? a.len[pl.u] : pl.L - 1;
 
   const int u = pl.u, b = u / a.Hkv, j = u - b * a.Hkv;
   const int Lold = pl.L - 1, t0 = pl.t0, t1 = pl.t1;
@@ -250,11 +367,13 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
   float *lg = a.ws.logits + (size_t)u * a.cap * G;
 
-  uint4 qf[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-    qf[g] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) +
-                                             ((size_t)(b * a.Hq + j * G + g) * D + c * CH) * EL);
+  // The group's queries go to LDS ahead of the first rows, so every wait
+  // below also covers them.
+  {
+    const int off = wave * 1024 + lane * 16;
+    const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
+    if (off < QB) dma16(qsrc + off, qs + wave * 1024);
+  }
   float m[G], l[G], acc[G][CH];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -264,33 +383,42 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
     for (int e = 0; e < CH; ++e) acc[g][e] = 0.f;
   }
   for (int cbase = t0; cbase < t1; cbase += TC) {
-    if (cbase != t0) __syncthreads();  // every wave is done with the previous chunk
-    // All sub-chunks of the chunk go out at once; each is consumed as it lands.
+    if (cbase != t0) lds_barrier();  // every wave is done with the previous chunk
 #pragma unroll
     for (int sc = 0; sc < NSUB; ++sc) {
       const int c0 = cbase + sc * TS;
       stage_sub<RB, NI>(smem + sc * 2 * SUBB, smem + sc * 2 * SUBB + SUBB, kc, vc, kn, vn, c0,
                         max(0, min(TS, t1 - c0)), t0, Lold, wave, lane);
     }
+    uint4 qf[G];
 #pragma unroll
     for (int sc = 0; sc < NSUB; ++sc) {
+      float sl[UR][G];
       const int c0 = cbase + sc * TS;
       if (sc == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 1)) : "memory");
       else if (sc == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 2)) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (c0 >= t1) continue;  // uniform: nothing left in this chunk
+      dma_barrier();
+      if (sc == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) qf[g] = *reinterpret_cast<const uint4 *>(qs + (g * D + c * CH) * EL);
+      }
+      const int nrows = min(TS, t1 - c0);  // <= 0: nothing left in this chunk
       const char *kb = smem + sc * 2 * SUBB;
       const char *vb = kb + SUBB;
-      const int nrows = min(TS, t1 - c0);
-      float sl[UR][G];
-      uint4 vf[UR];
+      static_assert(UR == 2, "two row groups per wave per sub-chunk");
+      uint4 kf2[UR], vf[UR];
+      {
+        const int row0 = wave * (TS / 4) + r, row1 = row0 + TPW;
+        lds_read_rows(kf2[0], kf2[1], vf[0], vf[1], lds_addr(kb + row0 * RB + c * 16),
+                      lds_addr(kb + row1 * RB + c * 16), lds_addr(vb + row0 * RB + c * 16),
+                      lds_addr(vb + row1 * RB + c * 16));
+      }
 #pragma unroll
       for (int i = 0; i < UR; ++i) {
         const int row = wave * (TS / 4) + i * TPW + r;
         const bool ok = row < nrows;
-        const uint4 kf = *reinterpret_cast<const uint4 *>(kb + row * RB + c * 16);
-        vf[i] = *reinterpret_cast<const uint4 *>(vb + row * RB + c * 16);
+        const uint4 kf = kf2[i];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float d;
@@ -308,8 +436,8 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
           d = row_sum<LPR>(d) * a.scale_log2;
           sl[i][g] = ok ? d : -INFINITY;
         }
-        if (c == 0 && ok) {
-          float *dst = lg + (size_t)(c0 + row) * G;
+        if (c == 0) {  // staged in LDS, written out once the chunk is done
+          float *dst = lgs + (sc * TS + row) * G;
           if constexpr (G % 4 == 0) {
 #pragma unroll
             for (int g = 0; g < G; g += 4)
@@ -351,386 +479,468 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
         l[g] = ls;
         m[g] = mx;
       }
-    }
-  }
-  if (a.hp.n && tid == 0 && len_dev != pl.L - 1) set_status(a.ws.status, HIKV_EINVAL);
-  // Merge the NS = 4 * TPW row streams into the tile partial.
-  constexpr int NS = 4 * TPW;
-  constexpr bool kLdsMerge = NS * G * D * 4 + NS * G * 8 + G * 8 <= NSUB * 2 * SUBB;
-  __syncthreads();  // the staging buffers become merge scratch
-  if constexpr (kLdsMerge) {
-    // Every stream writes its (m, l, P.V) to LDS; no cross-lane shuffles.
-    float *s_acc = reinterpret_cast<float *>(smem);   // [NS][G][D]
-    float *s_m = s_acc + NS * G * D;                  // [NS][G]
-    float *s_l = s_m + NS * G;                        // [NS][G]
-    float *s_M = s_l + NS * G;                        // [G] tile max, then [G] tile sum
-    const int sid = wave * TPW + r;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < CH; e += 4)
-        *reinterpret_cast<float4 *>(s_acc + (sid * G + g) * D + c * CH + e) =
-            make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
-      if (c == 0) {
-        s_m[sid * G + g] = m[g];
-        s_l[sid * G + g] = l[g];
-      }
-    }
-    __syncthreads();
-    if (tid < G) {
-      float M = -INFINITY;
-      for (int q = 0; q < NS; ++q) M = fmaxf(M, s_m[q * G + tid]);
-      const float Ms = (M == -INFINITY) ? 0.f : M;
-      float lv = 0.f;
-      for (int q = 0; q < NS; ++q) {
-        const float f = fast_exp2(s_m[q * G + tid] - Ms);
-        s_m[q * G + tid] = f;  // becomes the stream's rescale factor
-        lv += s_l[q * G + tid] * f;
-      }
-      s_M[tid] = M;
-      s_M[G + tid] = lv;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int g = idx / D;
-      float av = 0.f;
-#pragma unroll
-      for (int q = 0; q < NS; ++q) av += s_acc[(q * G) * D + idx] * s_m[q * G + g];
-      a.ws.part_acc[(size_t)tile * G * D + idx] = av;
-      if (idx - g * D == 0)
-        *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + g) * 2) = make_float2(s_M[g], s_M[G + g]);
-    }
-  } else {
-    // Rows of each wave through shuffles, then the waves through LDS.
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) {
+      // Keep this sub-chunk's arithmetic ahead of the next sub-chunk's wait:
+      // the empty asm statements consume the running state, and asm volatile
+      // statements keep their order (otherwise the compiler defers the
+      // softmax and P.V of every sub-chunk until the last one has landed).
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float mo = __shfl_xor(m[g], off), lo = __shfl_xor(l[g], off);
-        const float mx = fmaxf(m[g], mo);
-        const float mxs = (mx == -INFINITY) ? 0.f : mx;
-        const float ea = fast_exp2(m[g] - mxs), eb = fast_exp2(mo - mxs);
-        l[g] = l[g] * ea + lo * eb;
+        asm volatile("" : "+v"(m[g]), "+v"(l[g]));
 #pragma unroll
-        for (int e = 0; e < CH; ++e) acc[g][e] = acc[g][e] * ea + __shfl_xor(acc[g][e], off) * eb;
-        m[g] = mx;
+        for (int e = 0; e < CH; ++e) asm volatile("" : "+v"(acc[g][e]));
       }
+      sched_fence();
     }
-    if (r == 0) {
+    // The chunk's logits: each wave writes the rows it computed (global
+    // stores issued between the waits above would hold back the vmcnt chain).
+    {
+      constexpr int WR = (TS / 4) * G;  // floats per wave per sub-chunk
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < CH; ++e) sm_acc[wave][g][c * CH + e] = acc[g][e];
-      if (c == 0)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          sm_ml[wave][g][0] = m[g];
-          sm_ml[wave][g][1] = l[g];
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int g = idx / D, d = idx - g * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[w][g][0]);
-      const float Ms = (M == -INFINITY) ? 0.f : M;
-      float av = 0.f, lv = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float e = fast_exp2(sm_ml[w][g][0] - Ms);
-        av += sm_acc[w][g][d] * e;
-        lv += sm_ml[w][g][1] * e;
+      for (int q0 = 0; q0 < NSUB * WR; q0 += kWave) {
+        const int q = q0 + lane;
+        const int sc = q / WR, w = q - sc * WR;
+        const int row = wave * (TS / 4) + w / G;
+        const int n = cbase + sc * TS + row;
+        if (q < NSUB * WR && n < t1) lg[(size_t)n * G + (w % G)] = lgs[(sc * TS + row) * G + (w % G)];
       }
-      a.ws.part_acc[((size_t)tile * G + g) * D + d] = av;
-      if (d == 0) *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + g) * 2) = make_float2(M, lv);
     }
   }
+  // Tile partial.  Each token row kept its own running maximum; the rows of a
+  // wave are rescaled to the wave's maximum and summed in registers, then the
+  // four waves are combined through LDS.
+  constexpr int S = swap_steps<LPR>(), PW = kWave >> S;  // lanes per part
+  constexpr int GP = G < 4 ? 4 : G;                        // heads, padded
+  constexpr int NV = G * CH;
+  float mw[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) mw[g] = g < G ? m[g] : -INFINITY;
+  rows_reduce<LPR, true>(mw);
+  float Mw[G];  // the wave's maximum per head, in every lane
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    Mw[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mw[g % (GP >> S)]),
+                                                                (g / (GP >> S)) * PW));
+  float vals[NV], lw[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g < G) {
+      const float f = fast_exp2(m[g] - ((Mw[g] == -INFINITY) ? 0.f : Mw[g]));
+      lw[g] = l[g] * f;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) vals[g * CH + e] = acc[g][e] * f;
+    } else {
+      lw[g] = 0.f;
+    }
+  }
+  rows_reduce<LPR, false>(vals);
+  rows_reduce<LPR, false>(lw);
+  lds_barrier();  // every wave is done with the staging buffers: they become merge scratch
+  {
+    const int part = lane / PW, cc = lane % LPR;
+    if (LPR != 8 || (lane & 8) == 0) {
+#pragma unroll
+      for (int i = 0; i < (NV >> S); ++i) {
+        const int vi = i + part * (NV >> S);
+        sm_acc[wave][vi / CH][cc * CH + vi % CH] = vals[i];
+      }
+      if (cc == 0) {
+#pragma unroll
+        for (int i = 0; i < (GP >> S); ++i) {
+          const int gi = i + part * (GP >> S);
+          if (gi < G) sm_ml[wave][gi][1] = lw[i];
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sm_ml[wave][g][0] = Mw[g];
+    }
+  }
+  lds_barrier();
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[w][g][0]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float av = 0.f, lv = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float e = fast_exp2(sm_ml[w][g][0] - Ms);
+      av += sm_acc[w][g][d] * e;
+      lv += sm_ml[w][g][1] * e;
+    }
+    a.ws.part_acc[((size_t)tile * G + g) * D + d] = av;
+    if (d == 0) *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + g) * 2) = make_float2(M, lv);
+  }
+  if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
 
 // ---------------------------------------------------------------------------
-// K2: unit statistics, output, importance, eviction.
+// K2: per unit, importance blocks (softmax statistics, importance, eviction,
+// placement of the new token) and output blocks (one 64-output chunk each).
 // ---------------------------------------------------------------------------
+constexpr int kT2 = 1024;            // threads of a second-launch workgroup
+constexpr int kNW2 = kT2 / kWave;    // its waves
+
+template <int G>
+struct K2Lay {
+  static constexpr int NB = G <= 4 ? 9 : 5;  // tokens per thread per batch
+  static constexpr int CHUNK = NB * kT2;     // tokens per importance block
+};
+
 template <int EL, int D, int G>
-__global__ __launch_bounds__(kThreads) void k_finalize(StepArgs a) {
-  constexpr int RB = D * EL;
-  __shared__ float sm_stat[G][2];
-  __shared__ uint64_t sk[4];
-  __shared__ int ss[4];
-  __shared__ int s_last;
+__host__ __device__ constexpr int k2_noc() { return G * D / 64; }
+
+// Softmax statistics of a unit per head from its tiles' (max, sum) pairs:
+// sM[g] = max over tiles, sL[g] = sum over tiles of sum * 2^(max - sM[g]).
+// Pair i = tile * G + g; thread t owns pairs t, t + kT2, ... (all of head
+// t % G); v0 is its first pair, already loaded.  When sm_m is given, the
+// maxima of head gm are also left there per tile.
+template <int G>
+__device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 v0, float (*red)[G], float *sM,
+                           float *sL, float *sm_m, int gm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float mx = tid < npair ? v0.x : -INFINITY;
+  for (int i = tid + kT2; i < npair; i += kT2) mx = fmaxf(mx, pml[i].x);
+  if (sm_m) {
+    if (tid < npair && tid % G == gm) sm_m[tid / G] = v0.x;
+    for (int i = tid + kT2; i < npair; i += kT2)
+      if (i % G == gm) sm_m[i / G] = pml[i].x;
+  }
+#pragma unroll
+  for (int off = G; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane < G) red[wave][lane] = mx;
+  lds_barrier();
+  if (tid < G) {
+    float M = red[0][tid];
+    for (int w = 1; w < kNW2; ++w) M = fmaxf(M, red[w][tid]);
+    sM[tid] = M;
+  }
+  lds_barrier();
+  const float Mg = sM[tid % G];
+  const float Ms = (Mg == -INFINITY) ? 0.f : Mg;
+  float ls = tid < npair ? v0.y * fast_exp2(v0.x - Ms) : 0.f;
+  for (int i = tid + kT2; i < npair; i += kT2) {
+    const float2 v = pml[i];
+    ls += v.y * fast_exp2(v.x - Ms);
+  }
+#pragma unroll
+  for (int off = G; off < kWave; off <<= 1) ls += __shfl_xor(ls, off);
+  lds_barrier();  // every wave has read red
+  if (lane < G) red[wave][lane] = ls;
+  lds_barrier();
+  if (tid < G) {
+    float sum = 0.f;
+    for (int w = 0; w < kNW2; ++w) sum += red[w][tid];
+    sL[tid] = sum;
+  }
+  lds_barrier();
+}
+
+template <int EL, int D, int G>
+__global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
+  constexpr int RB = D * EL, NR = RB / 16, GD = G * D;
+  constexpr int NB = K2Lay<G>::NB, CHUNK = K2Lay<G>::CHUNK;
+  constexpr int NOC = k2_noc<EL, D, G>();
+  constexpr int NTW = 8;  // tiles per wave loaded in one batch by an output block
+  __shared__ float red[kNW2][G];
+  __shared__ float sM[G], sL[G];
+  __shared__ float sm_m[kMaxGrid];           // output blocks: tile maxima of their head
+  __shared__ float red_o[kNW2][kWave];       // output blocks: per-wave partial sums
+  __shared__ uint64_t sk[kNW2];
+  __shared__ int ss[kNW2];
+  __shared__ float s_newimp;
+  __shared__ int s_dst;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int u, s, nt, L, T;
+  const int vz = vzero();
+  const int nib = (int)(gridDim.x / (unsigned)a.n_units) - NOC;  // importance blocks per unit
+  const int u = blockIdx.x / (nib + NOC), r = blockIdx.x - u * (nib + NOC);
+  // The empty asm statements keep the compiler from merging the two plan
+  // sources into one load through a selected pointer (a flat load, waited
+  // for at once).
+  int tb, nt, L;
   if (a.hp.n) {
-    const Plan pl = host_plan(a, blockIdx.x);
-    if (!pl.valid) return;
-    u = pl.u, s = pl.s, nt = pl.nt, L = pl.L, T = pl.T;
-    if (unit_error(a, u, L - 1, 1)) return;  // device-side error: unit left alone
+    tb = a.hp.base[u];
+    nt = a.hp.base[u + 1] - tb;
+    L = a.hp.L[u];
+    asm volatile("" ::: "memory");
   } else {
-    const int4 rec = reinterpret_cast<const int4 *>(a.ws.tinfo)[blockIdx.x];
-    if (rec.x < 0) return;
-    u = rec.x, s = rec.y, nt = rec.z, L = rec.w;
-    T = a.ws.plan[0];
+    const int4 rec = reinterpret_cast<const int4 *>(a.ws.urec)[u];
+    tb = rec.x, nt = rec.y, L = rec.z;
+    asm volatile("" ::: "memory");
   }
+  if (nt <= 0) return;  // a unit the first launch excluded
+  const bool imp_blk = r < nib;
+  const int nb0 = imp_blk ? r * CHUNK : 0;
+  if (imp_blk && nb0 >= L && r > 0) return;  // no tokens here (nor the whole unit's eviction)
   const int b = u / a.Hkv, j = u - b * a.Hkv;
-  const int Lold = L - 1, t0 = s * T, t1 = min(t0 + T, L);
-  const int tile = blockIdx.x, tb = tile - s;
-  const int beta = unit_budget(a, u);
-  const int S = a.n_sink, Wp = min(a.n_recent, beta - S), newest = a.new_pos[b];
-  const bool over = L > beta;
-  const int n_evict = over ? L - beta : 0;
-  const bool bulk = n_evict > 1;
-  const float *lg = a.ws.logits + (size_t)u * a.cap * G;
+  const int Lold = L - 1;
+  const int npair = nt * G;
+  const float2 *pml = reinterpret_cast<const float2 *>(a.ws.part_ml) + (size_t)tb * G;
   float *impw = a.imp + (size_t)u * a.cap;
   int32_t *posw = a.pos + (size_t)u * a.cap;
+  const int S = a.n_sink;
 
-  // Own tokens' operands first (independent of the unit statistics).
-  const int n_first = t0 + tid;
-  float imp_first = 0.f;
-  int pos_first = newest;
-  float lg_first[G];
-  if (n_first < t1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) lg_first[g] = lg[(size_t)n_first * G + g];
-    if (n_first != Lold) {
-      imp_first = impw[n_first];
-      pos_first = posw[n_first];
-    }
-  }
+  // ---- One batch of independent loads: unconditional, from clamped (valid)
+  // addresses, validity applied where a value is used.  A load under a
+  // condition makes the compiler wait for it on the spot to merge it with a
+  // default value.
+  // (Issued inside each path: loads in flight where the two paths part would
+  // be waited for at the start of the second path.)
 
-  // Unit statistics per head (a wave per head, lanes over tiles).
-  for (int g = wave; g < G; g += 4) {
-    float Mx = -INFINITY, ls = 0.f;
-    for (int t0r = 0; t0r < nt; t0r += 256) {
-      float2 v[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t = t0r + lane + 64 * k;
-        v[k] = (t < nt) ? *reinterpret_cast<const float2 *>(a.ws.part_ml + ((size_t)(tb + t) * G + g) * 2)
-                        : make_float2(-INFINITY, 0.f);
-      }
-      float mr = fmaxf(fmaxf(v[0].x, v[1].x), fmaxf(v[2].x, v[3].x));
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mr = fmaxf(mr, __shfl_xor(mr, off));
-      const float mn = fmaxf(Mx, mr);
-      const float mns = (mn == -INFINITY) ? 0.f : mn;
-      float part = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) part += v[k].y * fast_exp2(v[k].x - mns);
-      part = wave_sum(part);
-      ls = ls * fast_exp2(Mx - mns) + part;
-      Mx = mn;
-    }
-    if (lane == 0) {
-      sm_stat[g][0] = Mx;
-      sm_stat[g][1] = ls;
-    }
-  }
-  __syncthreads();
-
-  // This tile's slice of the output.  Lanes run over the unit's tiles (LO
-  // lanes per output, loads issued first), a butterfly over those lanes sums
-  // them in a fixed order.
-  {
-    const int per = (G * D + nt - 1) / nt;
-    const int o0 = min(s * per, G * D), o1 = min(o0 + per, G * D);
-    const int n_o = o1 - o0;
-    int LO = 1;
-    while (LO < nt && LO < 64) LO <<= 1;
-    const int OW = 64 / LO;                 // outputs per wave per round
-    const int sub = lane / LO, tl = lane - sub * LO;
-    for (int ob = wave * OW; ob < n_o; ob += 4 * OW) {
-      const int oo = ob + sub;
-      const bool ok_o = oo < n_o;
-      const int o = o0 + (ok_o ? oo : 0), g = o / D;
-      const float Ms = (sm_stat[g][0] == -INFINITY) ? 0.f : sm_stat[g][0];
-      float av = 0.f;
-      for (int tb0 = 0; tb0 < nt; tb0 += 4 * LO) {
-        float va[4], vm[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int t = tb0 + tl + k * LO;
-          const bool ok = ok_o && t < nt;
-          va[k] = ok ? a.ws.part_acc[((size_t)(tb + t) * G) * D + o] : 0.f;
-          vm[k] = ok ? a.ws.part_ml[((size_t)(tb + t) * G + g) * 2] : -INFINITY;
+  // The importance path comes first in the code so that its loads are not
+  // held back by waits the compiler places where the two paths meet.
+  if (imp_blk) {
+    [&]() __attribute__((always_inline)) {
+      // ---------------- importance block ----------------
+      const int newest = ld_vec(a.new_pos + b, vz);
+      const int beta_ld = ld_vec(a.budget ? a.budget + u : a.new_pos + b, vz);
+      const float2 v0 = pml[min(tid, npair - 1)];
+      const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
+      const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
+      char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
+      char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
+      const float *lg = a.ws.logits + (size_t)u * a.cap * G;
+      const int len_dev = ld_vec(a.len + u, vz);
+      const int rt = tid % (2 * NR);
+      const uint4 nrow = *reinterpret_cast<const uint4 *>(rt < NR ? kn + rt * 16 : vn + (rt - NR) * 16);
+      float tl[NB][G], ti[NB];
+      int tp[NB];
+      auto load_batch = [&](int base) {
+    #pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int n = min(base + tid + i * kT2, Lold);
+          if constexpr (G % 4 == 0) {
+    #pragma unroll
+            for (int g = 0; g < G; g += 4) {
+              const float4 v4 = *reinterpret_cast<const float4 *>(lg + (size_t)n * G + g);
+              tl[i][g] = v4.x, tl[i][g + 1] = v4.y, tl[i][g + 2] = v4.z, tl[i][g + 3] = v4.w;
+            }
+          } else if constexpr (G == 2) {
+            const float2 v2 = *reinterpret_cast<const float2 *>(lg + (size_t)n * 2);
+            tl[i][0] = v2.x, tl[i][1] = v2.y;
+          } else {
+            tl[i][0] = lg[n];
+          }
+          ti[i] = impw[n];  // slot Lold holds no token yet: replaced below
+          tp[i] = posw[n];
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) av += va[k] * fast_exp2(vm[k] - Ms);
+      };
+      load_batch(nb0);
+      const int beta = a.budget ? beta_ld : a.budget_all;
+      unit_stats<G>(pml, npair, v0, red, sM, sL, nullptr, 0);
+      if (a.hp.n) {  // a host plan covers every unit: check it against the device
+        const int err = (L > a.cap) ? HIKV_ECAPACITY : ((beta < S || beta > a.cap) ? HIKV_EBUDGET : 0);
+        if (r == 0 && tid == 0) {
+          if (err) set_status(a.ws.status, err);
+          else if (len_dev != Lold) set_status(a.ws.status, HIKV_EINVAL);
+        }
+        if (err) return;
       }
-      for (int off = LO / 2; off > 0; off >>= 1) av += __shfl_xor(av, off);
-      if (ok_o && tl == 0) a.out[((size_t)(b * a.Hq + j * G)) * D + o] = av / sm_stat[g][1];
-    }
-  }
-
-  // Importance of this tile's tokens; lowest eviction key among candidates.
-  float Mg[G], ILg[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    Mg[g] = sm_stat[g][0];
-    ILg[g] = 1.f / sm_stat[g][1];
-  }
-  uint64_t best = ~0ull;
-  int best_slot = -1;
-  for (int n = n_first; n < t1; n += kThreads) {
-    const bool first = n == n_first;
-    float p = 0.f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) p += fast_exp2((first ? lg_first[g] : lg[(size_t)n * G + g]) - Mg[g]) * ILg[g];
-    const float io = first ? imp_first : ((n == Lold) ? 0.f : impw[n]);
-    const int pn = first ? pos_first : ((n == Lold) ? newest : posw[n]);
-    const float iv = io + p;
-    // Agent-scope (write-through) stores: the unit's last tile may overwrite
-    // the victim's slot in this launch, and a dirty copy in this XCD's L2
-    // must not be written back over it later.
-    if (n == Lold) st_ag(a.ws.fz_newimp + u, iv);
-    else st_ag(impw + n, iv);
-    if (over && !((pn < S) || (pn > newest - Wp))) {
-      const uint64_t k = evict_key(iv, pn);
-      if (k < best) {
-        best = k;
-        best_slot = n;
+      const bool over = L > beta;
+      if (over && r > 0) return;  // the unit's eviction needs all its tokens in one block
+      const int nb1 = over ? L : min(L, nb0 + CHUNK);
+      const int Wp = min(a.n_recent, beta - S);
+      const int n_evict = over ? L - beta : 0;
+      float Mg[G], ILg[G];
+    #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        Mg[g] = sM[g];
+        ILg[g] = 1.f / sL[g];
       }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t ko = __shfl_xor(best, off);
-    const int so = __shfl_xor(best_slot, off);
-    if (ko < best) {
-      best = ko;
-      best_slot = so;
-    }
-  }
-  if (lane == 0) {
-    sk[wave] = best;
-    ss[wave] = best_slot;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t kk = sk[0];
-    int vs = ss[0];
-    for (int w = 1; w < 4; ++w)
-      if (sk[w] < kk) {
-        kk = sk[w];
-        vs = ss[w];
-      }
-    st_ag(a.ws.tile_key + tile, kk);
-    st_ag(a.ws.tile_slot + tile, vs);
-  }
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.ws.ticket + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (uint32_t)(nt - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---------------- tail: the unit's last tile ----------------
-  asm volatile("" ::: "memory");
-  const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
-  const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
-  char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
-  char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
-  const float newimp = ld_ag(a.ws.fz_newimp + u);
-  int dst = Lold;  // slot that receives the new token; -1 when it is evicted itself
-  if (n_evict == 1) {
-    if (wave == 0) {
-      uint64_t kk = ~0ull;
-      int vs = -1;
-      for (int t = lane; t < nt; t += 64) {
-        const uint64_t k = ld_ag(a.ws.tile_key + tb + t);
-        const int sl = ld_ag(a.ws.tile_slot + tb + t);
-        if (k < kk) {
-          kk = k;
-          vs = sl;
+      // Steady state with the whole unit in one batch: the importance stays in
+      // registers until the victim is known, so no slot is written twice.
+      const bool defer = n_evict == 1 && nb1 - nb0 <= CHUNK;
+      uint64_t best = ~0ull;
+      int best_slot = -1;
+      for (int base = nb0; base < nb1; base += CHUNK) {
+        if (base != nb0) load_batch(base);
+    #pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int n = base + tid + i * kT2;
+          if (n < nb1) {
+            float p = 0.f;
+    #pragma unroll
+            for (int g = 0; g < G; ++g) p += fast_exp2(tl[i][g] - Mg[g]) * ILg[g];
+            const bool is_new = n == Lold;
+            const float iv = (is_new ? 0.f : ti[i]) + p;
+            const int pn = is_new ? newest : tp[i];
+            ti[i] = iv;
+            if (is_new) s_newimp = iv;
+            else if (!defer) impw[n] = iv;
+            if (over && !((pn < S) || (pn > newest - Wp))) {
+              const uint64_t k = evict_key(iv, pn);
+              if (k < best) {
+                best = k;
+                best_slot = n;
+              }
+            }
+          }
         }
       }
-#pragma unroll
+      if (!over) {
+        // Nothing to evict: the block holding slot Lold stores the new token there.
+        if (nb1 == L) {
+          lds_barrier();  // s_newimp
+          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
+          if (tid == 0) {
+            impw[Lold] = s_newimp;
+            posw[Lold] = newest;
+            a.len[u] = L;
+          }
+        }
+        return;
+      }
+    #pragma unroll
       for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t ko = __shfl_xor(kk, off);
-        const int so = __shfl_xor(vs, off);
-        if (ko < kk) {
-          kk = ko;
-          vs = so;
+        const uint64_t ko = __shfl_xor(best, off);
+        const int so = __shfl_xor(best_slot, off);
+        if (ko < best) {
+          best = ko;
+          best_slot = so;
         }
       }
-      if (lane == 0) s_last = vs;
-    }
-    __syncthreads();
-    dst = (s_last == Lold) ? -1 : s_last;
-  }
-  if (dst >= 0) {
-    for (int i = tid; i < RB / 16; i += kThreads) {
-      reinterpret_cast<uint4 *>(kw + (size_t)dst * RB)[i] = reinterpret_cast<const uint4 *>(kn)[i];
-      reinterpret_cast<uint4 *>(vw + (size_t)dst * RB)[i] = reinterpret_cast<const uint4 *>(vn)[i];
-    }
-    if (tid == 0) {
-      posw[dst] = newest;
-      impw[dst] = newimp;
-    }
-  }
-  if (!bulk) {
-    if (tid == 0 && a.len[u] != L - n_evict) a.len[u] = L - n_evict;
-  } else {
-    // The unit now holds L contiguous slots: select the n_evict lowest keys
-    // among the unprotected tokens and compact.
-    __syncthreads();
-    __shared__ uint32_t hist[256];
-    __shared__ int sc[kThreads];
-    __shared__ RadixState rs;
-    auto cand_key = [&](int n, uint64_t &key) -> bool {
-      const int pn = (n == Lold) ? newest : posw[n];
-      if ((pn < S) || (pn > newest - Wp)) return false;
-      key = evict_key((n == Lold) ? newimp : ld_ag(impw + n), pn);
-      return true;
-    };
-    radix_select_smallest<kThreads>(L, n_evict, cand_key, hist, &rs);
-    const uint64_t prefix = rs.prefix;
-    const int shift = rs.shift;
-    auto evicted = [&](int n) -> bool {
-      uint64_t key;
-      if (!cand_key(n, key)) return false;
-      return (key >> shift) <= (prefix >> shift);
-    };
-    const int per = (L + kThreads - 1) / kThreads;
-    const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
-    int nh = 0, nm = 0;
-    for (int n = n0; n < n1; ++n) {
-      const bool e = evicted(n);
-      nh += (n < beta && e);
-      nm += (n >= beta && !e);
-    }
-    int tot_h, tot_m;
-    int oh = block_excl_scan<kThreads>(nh, sc, &tot_h);
-    int om = block_excl_scan<kThreads>(nm, sc, &tot_m);
-    int32_t *holes = a.ws.holes + (size_t)u * a.cap;
-    int32_t *movers = a.ws.movers + (size_t)u * a.cap;
-    for (int n = n0; n < n1; ++n) {
-      const bool e = evicted(n);
-      if (n < beta && e) holes[oh++] = n;
-      if (n >= beta && !e) movers[om++] = n;
-    }
-    __syncthreads();
-    if (tot_h == tot_m) {
-      constexpr int CPR = RB / 16;
-      for (int idx = tid; idx < tot_m * CPR; idx += kThreads) {
-        const int i = idx / CPR, ci = idx - i * CPR;
-        const int src = movers[i], dd = holes[i];
-        reinterpret_cast<uint4 *>(kw + (size_t)dd * RB)[ci] = reinterpret_cast<const uint4 *>(kw + (size_t)src * RB)[ci];
-        reinterpret_cast<uint4 *>(vw + (size_t)dd * RB)[ci] = reinterpret_cast<const uint4 *>(vw + (size_t)src * RB)[ci];
+      if (lane == 0) {
+        sk[wave] = best;
+        ss[wave] = best_slot;
       }
-      for (int i = tid; i < tot_m; i += kThreads) {
-        const int src = movers[i], dd = holes[i];
-        posw[dd] = (src == Lold) ? newest : posw[src];
-        impw[dd] = (src == Lold) ? newimp : ld_ag(impw + src);
+      lds_barrier();
+      const float newimp = s_newimp;
+      if (n_evict == 1) {
+        // Steady state: the lowest key is the victim; the new token takes its
+        // slot, or is itself dropped.
+        if (tid == 0) {
+          uint64_t kk = sk[0];
+          int vs = ss[0];
+          for (int w = 1; w < kNW2; ++w)
+            if (sk[w] < kk) {
+              kk = sk[w];
+              vs = ss[w];
+            }
+          s_dst = (vs == Lold) ? -1 : vs;
+        }
+        lds_barrier();
+        const int dst = s_dst;
+        if (dst >= 0 && tid < 2 * NR)
+          reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)dst * RB)[tid % NR] = nrow;
+        if (defer) {
+    #pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            const int n = nb0 + tid + i * kT2;
+            if (n < nb1 && n != Lold) {
+              impw[n] = (n == dst) ? newimp : ti[i];
+              if (n == dst) posw[n] = newest;
+            }
+          }
+        } else if (dst >= 0) {
+          __syncthreads();  // the victim's own importance store has completed
+          if (tid == 0) {
+            posw[dst] = newest;
+            impw[dst] = newimp;
+          }
+        }
+        return;
       }
-      if (tid == 0) a.len[u] = beta;
-    } else if (tid == 0) {
-      set_status(a.ws.status, HIKV_EINVAL);
-    }
+      // Bulk: the new token goes to slot Lold, then the unit's L slots are cut to
+      // the budget: select the n_evict lowest keys among the unprotected tokens
+      // and move survivors from above the budget into the evicted slots below it.
+      if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
+      if (tid == 0) {
+        impw[Lold] = newimp;
+        posw[Lold] = newest;
+      }
+      __syncthreads();
+      __shared__ uint32_t hist[256];
+      __shared__ int sc[kT2];
+      __shared__ RadixState rs;
+      auto cand_key = [&](int n, uint64_t &key) -> bool {
+        const int pn = posw[n];
+        if ((pn < S) || (pn > newest - Wp)) return false;
+        key = evict_key(impw[n], pn);
+        return true;
+      };
+      radix_select_smallest<kT2>(L, n_evict, cand_key, hist, &rs);
+      const uint64_t prefix = rs.prefix;
+      const int shift = rs.shift;
+      auto evicted = [&](int n) -> bool {
+        uint64_t key;
+        if (!cand_key(n, key)) return false;
+        return (key >> shift) <= (prefix >> shift);
+      };
+      const int per = (L + kT2 - 1) / kT2;
+      const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
+      int nh = 0, nm = 0;
+      for (int n = n0; n < n1; ++n) {
+        const bool e = evicted(n);
+        nh += (n < beta && e);
+        nm += (n >= beta && !e);
+      }
+      int tot_h, tot_m;
+      int oh = block_excl_scan<kT2>(nh, sc, &tot_h);
+      int om = block_excl_scan<kT2>(nm, sc, &tot_m);
+      int32_t *holes = a.ws.holes + (size_t)u * a.cap;
+      int32_t *movers = a.ws.movers + (size_t)u * a.cap;
+      for (int n = n0; n < n1; ++n) {
+        const bool e = evicted(n);
+        if (n < beta && e) holes[oh++] = n;
+        if (n >= beta && !e) movers[om++] = n;
+      }
+      __syncthreads();
+      if (tot_h == tot_m) {
+        constexpr int CPR = RB / 16;
+        for (int idx = tid; idx < tot_m * CPR; idx += kT2) {
+          const int i = idx / CPR, ci = idx - i * CPR;
+          const int src = movers[i], dd = holes[i];
+          reinterpret_cast<uint4 *>(kw + (size_t)dd * RB)[ci] = reinterpret_cast<const uint4 *>(kw + (size_t)src * RB)[ci];
+          reinterpret_cast<uint4 *>(vw + (size_t)dd * RB)[ci] = reinterpret_cast<const uint4 *>(vw + (size_t)src * RB)[ci];
+        }
+        for (int i = tid; i < tot_m; i += kT2) {
+          const int src = movers[i], dd = holes[i];
+          posw[dd] = posw[src];
+          impw[dd] = impw[src];
+        }
+        if (tid == 0) a.len[u] = beta;
+      } else if (tid == 0) {
+        set_status(a.ws.status, HIKV_EINVAL);
+      }
+    }();
+    end_wave();
   }
-  if (tid == 0) a.ws.ticket[u] = 0;
+  // ---------------- output block: chunk c of the unit's G*D outputs ----
+  const int beta_ld = ld_vec(a.budget ? a.budget + u : a.new_pos + b, vz);
+  const float2 v0 = pml[min(tid, npair - 1)];
+  const int c = r - nib;
+  const int o = c * 64 + lane, g = (c * 64) / D;
+  const float *pacc = a.ws.part_acc + (size_t)tb * GD + o;
+  float pa[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) pa[i] = pacc[(size_t)min(wave + kNW2 * i, nt - 1) * GD];
+  const int beta = a.budget ? beta_ld : a.budget_all;
+  unit_stats<G>(pml, npair, v0, red, sM, sL, sm_m, g);
+  float *outu = a.out + (size_t)(b * a.Hq + j * G) * D;
+  if (a.hp.n && (L > a.cap || beta < S || beta > a.cap)) {  // unit left alone
+    if (wave == 0) outu[o] = 0.f;
+    end_wave();
+  }
+  const float Ms = (sM[g] == -INFINITY) ? 0.f : sM[g];
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int t = wave + kNW2 * i;
+    if (t < nt) acc += pa[i] * fast_exp2(sm_m[t] - Ms);
+  }
+  for (int t = wave + kNW2 * NTW; t < nt; t += kNW2) acc += pacc[(size_t)t * GD] * fast_exp2(sm_m[t] - Ms);
+  red_o[wave][lane] = acc;
+  lds_barrier();
+  if (wave == 0) {
+    float sum = 0.f;
+    for (int w = 0; w < kNW2; ++w) sum += red_o[w][lane];
+    outu[o] = sum / sL[g];
+  }
+
+  end_wave();
 }
 
 // ---------------------------------------------------------------------------
@@ -759,7 +969,12 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((k_attend<EL, D, G>), grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_finalize<EL, D, G>), grid, block, 0, s, a);
+  // Second launch: per unit, importance blocks to cover the capacity, then
+  // one output block per 64 outputs.
+  const int nib = (a.cap + K2Lay<G>::CHUNK - 1) / K2Lay<G>::CHUNK;
+  const long long g2 = (long long)a.n_units * (nib + k2_noc<EL, D, G>());
+  if (g2 > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)g2), dim3(kT2), 0, s, a);
   return hipGetLastError();
 }
 
