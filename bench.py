@@ -27,6 +27,28 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_attend_hbm_traffic_headkv32k.md")
+KERNEL_SOURCES = ("importance_aware_kv_amd/csrc/step.hip", "importance_aware_kv_amd/csrc/hikv_common.h",
+                  "importance_aware_kv_amd/csrc/hikv_block.h")
+
+
+def measured_traffic():
+    """HBM bytes per k_attend launch from the committed counter record, or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORD).read()
+    except OSError:
+        return None
+    tag = "<!-- traffic: "
+    if tag not in text:
+        return None
+    rec = json.loads(text.split(tag, 1)[1].split(" -->", 1)[0])
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def log(*a):
@@ -43,6 +65,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-hint", action="store_true", help="do not pass host lengths")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the run, copy this many bytes device-to-device 4 times (a plain copy "
+                         "kernel of known size, for calibrating memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no "
@@ -62,7 +87,9 @@ def main():
 
     n_inputs = 256
     w = W.workload(args.workload, steps=n_inputs)
-    per_layer_steps = 1 + (args.warmup + args.steps + args.layers - 1) // args.layers
+    # compression step + warm-up + the timed steps + the same number again for
+    # the per-kernel timing replay
+    per_layer_steps = 1 + (args.warmup + 2 * args.steps + args.layers - 1) // args.layers
     w.capacity = w.ctx + per_layer_steps + 1
     t0 = time.time()
     d = W.generate(w)
@@ -95,7 +122,7 @@ def main():
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     layer_step = [0] * args.layers
 
-    def step(li):
+    def step(li, events=None):
         c = layers[li]
         n = layer_step[li]
         layer_step[li] += 1
@@ -103,8 +130,11 @@ def main():
         if not args.no_hint:
             p = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
                               len_hint=host_len[li])
+        dbg = None
+        if events is not None:
+            dbg = H.hikv_debug(None, None, None, events[0].cuda_event, events[1].cuda_event)
         code = H.hikv_decode_step(c.shape, c.cache, p, q_all[n % n_inputs], kn_all[n % n_inputs],
-                                  vn_all[n % n_inputs], pos_all[n], out, ws)
+                                  vn_all[n % n_inputs], pos_all[n], out, ws, debug=dbg)
         if code != 0:
             raise RuntimeError(f"hikv_decode_step: {H.status_string(code)}")
         host_len[li] = np.minimum(host_len[li] + 1, budget).astype(np.int32)
@@ -155,6 +185,36 @@ def main():
     log(f"[bench] steady step: {ms_step * 1e3:.2f} us, {steps_per_s:.0f} steps/s, "
         f"{step_bytes / 1e6:.2f} MB/step algorithmic -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
+    # The dominant kernel, the attention launch: the same steps run once more,
+    # launched eagerly, with a pair of HIP events around every attention
+    # launch, recorded by the library on the stream that launch uses (event
+    # nodes inside a captured graph do not bracket the kernel's execution).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e_a, e_b in evs:  # materialise the events
+        e_a.record(stream)
+        e_b.record(stream)
+    torch.cuda.synchronize()
+    base2 = base + args.steps
+    for i in range(args.steps):
+        step((base2 + i) % args.layers, events=evs[i])
+    torch.cuda.synchronize()
+    H.check(H.hikv_device_status(ws), "device status after the timing replay")
+    attend_ms = sum(e_a.elapsed_time(e_b) for e_a, e_b in evs) / args.steps
+    attend_bytes = BM.attend_bytes(B, Hq, Hkv, D, w.el, live_steady)
+    attend_gbs = attend_bytes / (attend_ms * 1e-3) / 1e9
+    log(f"[bench] attention launch: {attend_ms * 1e3:.2f} us, {attend_bytes / 1e6:.2f} MB algorithmic -> "
+        f"{attend_gbs:.0f} GB/s ({attend_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 4 x {n * 4} bytes device-to-device")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, d, args.cpu_seconds)
@@ -183,13 +243,16 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(gbs, 1),
+            "achieved": round(attend_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "whole decode step (all kernels of one step, graph-replayed)",
-            "bytes_per_launch": step_bytes,
+            "frac": round(attend_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "kernel": "k_attend (split-K attention over the live K/V rows; HIP events per launch)",
+            "bytes_per_launch": attend_bytes,
+            "us_per_launch": round(attend_ms * 1e3, 3),
+            "whole_step": {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "bytes_per_step": step_bytes},
         },
         "compression_step_us": round(comp_ms * 1e3, 2),
         "cpu_baseline": cpu,

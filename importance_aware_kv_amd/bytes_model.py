@@ -31,3 +31,12 @@ def decode_step_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int
             + batch * n_kv_heads * 2 * row     # new k, v
             + batch * n_q_heads * head_dim * 4 # fp32 output
             + moves * 2 * (2 * row + 8))       # relocated rows (read + write)
+
+
+def attend_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, el: int,
+                 live_after_append) -> int:
+    """Bytes the attention launch must read: every live K and V row (the new
+    token's row included) and the queries."""
+    live = int(np.asarray(live_after_append, dtype=np.int64).sum())
+    row = head_dim * el
+    return live * 2 * row + batch * n_q_heads * row

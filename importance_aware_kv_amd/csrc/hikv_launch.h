@@ -22,7 +22,9 @@ hipError_t launch_bulk_evict(const StepArgs &a, int dtype, const int32_t *newest
 
 // The Stage I step in two launches (attention tiles, then statistics,
 // output, importance and eviction).
-hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s);
+// ev0/ev1 (may be null): events recorded around the attention launch.
+hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 // Host-side tile plan from a host copy of len[] (fills a.hp); false when it
 // does not apply (too many units), in which case the kernels derive it.
 bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint);

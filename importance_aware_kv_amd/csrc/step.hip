@@ -26,6 +26,8 @@
 //   one token (first step after a prefill) is compacted by its last tile with
 //   a radix select.
 
+#include <hip/hip_ext.h>
+
 #include "hikv_block.h"
 #include "hikv_launch.h"
 
@@ -962,13 +964,19 @@ static int attend_grid(int n_units) {
 }
 
 template <int EL, int D, int G>
-static hipError_t step_go(const StepArgs &a, hipStream_t s) {
+static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int g = attend_grid<EL, D, G>(a.n_units);
   if (g <= 0) return hipErrorInvalidValue;
   const dim3 grid(g), block(kThreads);
-  hipLaunchKernelGGL((k_attend<EL, D, G>), grid, block, 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (ev0 && ev1) {
+    // The events are recorded by the dispatch itself: they time the kernel's
+    // execution, not the command processor's way to it.
+    hipExtLaunchKernelGGL((k_attend<EL, D, G>), grid, block, 0, s, ev0, ev1, 0, a);
+  } else {
+    hipLaunchKernelGGL((k_attend<EL, D, G>), grid, block, 0, s, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   // Second launch: per unit, importance blocks to cover the capacity, then
   // one output block per 64 outputs.
   const int nib = (a.cap + K2Lay<G>::CHUNK - 1) / K2Lay<G>::CHUNK;
@@ -979,12 +987,12 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s) {
 }
 
 template <int EL, int D>
-static hipError_t step_g(const StepArgs &a, hipStream_t s) {
+static hipError_t step_g(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   switch (a.G) {
-    case 1: return step_go<EL, D, 1>(a, s);
-    case 2: return step_go<EL, D, 2>(a, s);
-    case 4: return step_go<EL, D, 4>(a, s);
-    case 8: return step_go<EL, D, 8>(a, s);
+    case 1: return step_go<EL, D, 1>(a, s, ev0, ev1);
+    case 2: return step_go<EL, D, 2>(a, s, ev0, ev1);
+    case 4: return step_go<EL, D, 4>(a, s, ev0, ev1);
+    case 8: return step_go<EL, D, 8>(a, s, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1041,13 +1049,13 @@ bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint) {
   return ok;
 }
 
-hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s) {
+hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (dtype == HIKV_BF16) {
-    if (a.D == 128) return step_g<2, 128>(a, s);
-    if (a.D == 64) return step_g<2, 64>(a, s);
+    if (a.D == 128) return step_g<2, 128>(a, s, ev0, ev1);
+    if (a.D == 64) return step_g<2, 64>(a, s, ev0, ev1);
   } else {
-    if (a.D == 128) return step_g<4, 128>(a, s);
-    if (a.D == 64) return step_g<4, 64>(a, s);
+    if (a.D == 128) return step_g<4, 128>(a, s, ev0, ev1);
+    if (a.D == 64) return step_g<4, 64>(a, s, ev0, ev1);
   }
   return hipErrorInvalidValue;
 }

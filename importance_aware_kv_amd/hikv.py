@@ -42,7 +42,8 @@ class hikv_policy(C.Structure):
 
 
 class hikv_debug(C.Structure):
-    _fields_ = [("sel_channels", C.c_void_p), ("sel_tokens", C.c_void_p), ("sel_count", C.c_void_p)]
+    _fields_ = [("sel_channels", C.c_void_p), ("sel_tokens", C.c_void_p), ("sel_count", C.c_void_p),
+                ("attend_start", C.c_void_p), ("attend_stop", C.c_void_p)]
 
 
 _lib = None

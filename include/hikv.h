@@ -102,12 +102,14 @@ typedef struct hikv_policy {
                               device status and that call's results are undefined. */
 } hikv_policy;
 
-/* Optional Stage II selections written by hikv_decode_step (device pointers,
- * each may be NULL).  For tests and inspection. */
+/* Optional outputs of hikv_decode_step for tests, inspection and profiling;
+ * every field may be NULL. */
 typedef struct hikv_debug {
-  int32_t *sel_channels;   /* [B][Hq][r] chosen channels, ascending */
-  int32_t *sel_tokens;     /* [B][Hq][k_T] positions of the exact-softmax tokens, ascending, -1 padded */
-  int32_t *sel_count;      /* [B][Hq] number of exact-softmax tokens, min(k_T, len + 1) */
+  int32_t *sel_channels;   /* [B][Hq][r] Stage II chosen channels, ascending (device) */
+  int32_t *sel_tokens;     /* [B][Hq][k_T] positions of the exact-softmax tokens, ascending, -1 padded (device) */
+  int32_t *sel_count;      /* [B][Hq] number of exact-softmax tokens, min(k_T, len + 1) (device) */
+  void *attend_start;      /* hipEvents (both or neither; caller-owned) that the dispatch of a Stage I */
+  void *attend_stop;       /* step's attention launch records when it starts and ends executing */
 } hikv_debug;
 
 /* Bytes of device workspace the decode step and hikv_evict need for this

@@ -55,7 +55,7 @@ class GpuRun:
                 sel_channels=torch.full((sh.batch, n_q_heads, r), -7, dtype=torch.int32, device="cuda"),
                 sel_tokens=torch.full((sh.batch, n_q_heads, kT), -7, dtype=torch.int32, device="cuda"),
                 sel_count=torch.full((sh.batch, n_q_heads), -7, dtype=torch.int32, device="cuda"))
-            self.dbg = H.hikv_debug(*[self.dbg_t[f].data_ptr() for f, _ in H.hikv_debug._fields_])
+            self.dbg = H.hikv_debug(*[self.dbg_t[f].data_ptr() for f in self.dbg_t])
 
     def step(self, q, k_new, v_new, new_pos, expect=H.HIKV_OK, hint_override=None):
         qt, kt, vt = H.to_device(q), H.to_device(k_new), H.to_device(v_new)
