@@ -27,10 +27,11 @@ struct Ws {
   uint32_t *ticket;     // [n_units] last-tile-arrives counters (self-resetting)
   int32_t *plan;        // [n_units + 4]: tile base per unit (exclusive prefix), then
                         //   [n_units] = total tiles, [+1] = tile size T
-  float *stats;         // [n_units][G][2] softmax max (log2 domain) and sum per q-head
+  float *stats;         // [n_units][G][2] softmax max and sum per q-head (multi-kernel path)
   float *part_ml;       // [max_tiles][G][2] per-tile partial max / sum
   float *part_acc;      // [max_tiles][G][D] per-tile partial P.V (unnormalised)
-  float *logits;        // [n_units][cap][G] log2-domain logits of this step
+  float *logits;        // [n_units][cap][G] this step's logits: scaled, log2 domain (multi-kernel
+                        //   and Stage II paths) or raw q.k (two-launch step; maxima raw too)
   uint64_t *tile_key;   // [max_tiles] lowest eviction key per tile
   int32_t *tile_slot;   // [max_tiles] its slot
   int32_t *holes;       // [n_units][cap] bulk compaction: evicted slots below budget

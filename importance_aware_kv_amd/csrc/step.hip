@@ -28,6 +28,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "hikv_block.h"
 #include "hikv_launch.h"
 
@@ -204,14 +206,19 @@ struct ALay {
 // bookkeeping); lanes past the tile read a clamped valid row into unused
 // buffer space; the new token's row (slot Lold, not yet in the cache) comes
 // from k_new / v_new.
-template <int RB, int NI>
+// SWZ (256-byte rows): the 16-byte chunk p of LDS row r holds source chunk
+// p ^ (r & 15), so that reads of one chunk column across 16 rows spread over
+// all LDS banks.
+template <int RB, int NI, bool SWZ = false>
 __device__ __forceinline__ void stage_sub(char *kb, char *vb, const char *kc, const char *vc,
                                           const char *kn, const char *vn, int c0, int nrows,
                                           int t0, int Lold, int wave, int lane) {
+  static_assert(!SWZ || RB == 256, "the swizzle is written for 256-byte rows");
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int off = ((i * 4 + wave) << 10) + (lane << 4);
-    const int row = off / RB, col = off - row * RB;
+    const int row = off / RB;
+    const int col = SWZ ? ((((off - row * RB) >> 4) ^ (row & 15)) << 4) : off - row * RB;
     const int n = (row < nrows) ? c0 + row : t0;  // t0 is always a live row of the tile
     const char *ks = (n == Lold) ? kn + col : kc + (size_t)n * RB + col;
     const char *vs = (n == Lold) ? vn + col : vc + (size_t)n * RB + col;
@@ -302,6 +309,99 @@ __device__ __forceinline__ void rows_reduce(float (&v)[N]) {
   }
 }
 
+// All-reduce over the lanes of a wave that are congruent modulo M (M a power
+// of two): DPP within 16-lane rows (xor 1, xor 2, then rotations by 4 and 8,
+// which combine the row's lanes of one residue), permlane swaps across rows.
+// No data goes through LDS.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <int STEP>
+__device__ __forceinline__ uint32_t dpp_step(uint32_t v) {
+  if constexpr (STEP == 1) return dpp_u<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (STEP == 2) return dpp_u<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (STEP == 4) return dpp_u<0x124>(v);  // row_ror:4
+  else return dpp_u<0x128>(v);                           // row_ror:8
+}
+__device__ __forceinline__ void swap16_u(uint32_t &a, uint32_t &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32_u(uint32_t &a, uint32_t &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+template <int M, typename Op>
+__device__ __forceinline__ float lanes_reduce(float v, Op op) {
+  auto step = [&](auto tag) {
+    constexpr int S = decltype(tag)::value;
+    v = op(v, __uint_as_float(dpp_step<S>(__float_as_uint(v))));
+  };
+  if constexpr (M <= 1) step(std::integral_constant<int, 1>{});
+  if constexpr (M <= 2) step(std::integral_constant<int, 2>{});
+  if constexpr (M <= 4) step(std::integral_constant<int, 4>{});
+  if constexpr (M <= 8) step(std::integral_constant<int, 8>{});
+  if constexpr (M <= 16) {
+    uint32_t a = __float_as_uint(v), b = a;
+    swap16_u(a, b);
+    v = op(__uint_as_float(a), __uint_as_float(b));
+  }
+  if constexpr (M <= 32) {
+    uint32_t a = __float_as_uint(v), b = a;
+    swap32_u(a, b);
+    v = op(__uint_as_float(a), __uint_as_float(b));
+  }
+  return v;
+}
+template <int M>
+__device__ __forceinline__ float lanes_max(float v) {
+  return lanes_reduce<M>(v, [](float x, float y) { return fmaxf(x, y); });
+}
+template <int M>
+__device__ __forceinline__ float lanes_sum(float v) {
+  return lanes_reduce<M>(v, [](float x, float y) { return x + y; });
+}
+
+// The smallest 64-bit eviction key of the wave, with the slot that holds it.
+struct KeySlot {
+  uint32_t hi, lo, slot;
+};
+__device__ __forceinline__ KeySlot key_min(KeySlot a, KeySlot b) {
+  const bool take_b = (b.hi < a.hi) || (b.hi == a.hi && b.lo < a.lo);
+  return take_b ? b : a;
+}
+__device__ __forceinline__ void wave_min_key(uint64_t &key, int &slot) {
+  KeySlot x{(uint32_t)(key >> 32), (uint32_t)key, (uint32_t)slot};
+  auto step = [&](auto tag) {
+    constexpr int S = decltype(tag)::value;
+    x = key_min(x, KeySlot{dpp_step<S>(x.hi), dpp_step<S>(x.lo), dpp_step<S>(x.slot)});
+  };
+  step(std::integral_constant<int, 1>{});
+  step(std::integral_constant<int, 2>{});
+  step(std::integral_constant<int, 4>{});
+  step(std::integral_constant<int, 8>{});
+  {
+    KeySlot a = x, b = x;
+    swap16_u(a.hi, b.hi);
+    swap16_u(a.lo, b.lo);
+    swap16_u(a.slot, b.slot);
+    x = key_min(a, b);
+  }
+  {
+    KeySlot a = x, b = x;
+    swap32_u(a.hi, b.hi);
+    swap32_u(a.lo, b.lo);
+    swap32_u(a.slot, b.slot);
+    x = key_min(a, b);
+  }
+  key = ((uint64_t)x.hi << 32) | x.lo;
+  slot = (int)x.slot;
+}
+
+// The value lane l holds (l wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Workgroup barrier for LDS data only.  __syncthreads() also waits for every
 // global load and store of the wave to complete, which costs a memory round
 // trip when none of them matter to the LDS exchange.
@@ -376,6 +476,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
     const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
     if (off < QB) dma16(qsrc + off, qs + wave * 1024);
   }
+  const float cs = a.scale_log2, tau = 8.f / cs;
   float m[G], l[G], acc[G][CH];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -435,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
             d = fmaf(__uint_as_float(qf[g].z), __uint_as_float(kf.z), d);
             d = fmaf(__uint_as_float(qf[g].w), __uint_as_float(kf.w), d);
           }
-          d = row_sum<LPR>(d) * a.scale_log2;
+          d = row_sum<LPR>(d);  // raw q.k; the scale enters in the exponent
           sl[i][g] = ok ? d : -INFINITY;
         }
         if (c == 0) {  // staged in LDS, written out once the chunk is done
@@ -453,17 +554,25 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        // Each row keeps a reference maximum m (raw q.k) and p = 2^((s - m) c).
+        // The reference moves (with a rescale of l and acc) only when the
+        // row's maximum passes it by more than 8 / c, i.e. when p could
+        // exceed 2^8; the branch is taken by the whole wave or not at all.
         float mx = m[g];
 #pragma unroll
         for (int i = 0; i < UR; ++i) mx = fmaxf(mx, sl[i][g]);
-        const float mxs = (mx == -INFINITY) ? 0.f : mx;
-        const float corr = fast_exp2(m[g] - mxs);
-        float ls = l[g] * corr;
+        if (__ballot(mx > m[g] + tau) != 0ull) {
+          const float corr = (mx == -INFINITY) ? 1.f : fast_exp2((m[g] - mx) * cs);
+          l[g] *= corr;
 #pragma unroll
-        for (int e = 0; e < CH; ++e) acc[g][e] *= corr;
+          for (int e = 0; e < CH; ++e) acc[g][e] *= corr;
+          m[g] = mx;
+        }
+        const float mc = (m[g] == -INFINITY) ? 0.f : m[g] * cs;
+        float ls = l[g];
 #pragma unroll
         for (int i = 0; i < UR; ++i) {
-          const float p = fast_exp2(sl[i][g] - mxs);
+          const float p = fast_exp2(fmaf(sl[i][g], cs, -mc));
           ls += p;
           if constexpr (EL == 2) {
             const uint32_t *vw = reinterpret_cast<const uint32_t *>(&vf[i]);
@@ -479,7 +588,6 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
           }
         }
         l[g] = ls;
-        m[g] = mx;
       }
       // Keep this sub-chunk's arithmetic ahead of the next sub-chunk's wait:
       // the empty asm statements consume the running state, and asm volatile
@@ -526,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
     if (g < G) {
-      const float f = fast_exp2(m[g] - ((Mw[g] == -INFINITY) ? 0.f : Mw[g]));
+      const float f = fast_exp2((m[g] - ((Mw[g] == -INFINITY) ? 0.f : Mw[g])) * cs);
       lw[g] = l[g] * f;
 #pragma unroll
       for (int e = 0; e < CH; ++e) vals[g * CH + e] = acc[g][e] * f;
@@ -568,12 +676,263 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
     float av = 0.f, lv = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float e = fast_exp2(sm_ml[w][g][0] - Ms);
+      const float e = fast_exp2((sm_ml[w][g][0] - Ms) * cs);
       av += sm_acc[w][g][d] * e;
       lv += sm_ml[w][g][1] * e;
     }
     a.ws.part_acc[((size_t)tile * G + g) * D + d] = av;
     if (d == 0) *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + g) * 2) = make_float2(M, lv);
+  }
+  if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
+}
+
+// ---------------------------------------------------------------------------
+// K1 for bf16 K and V with D = 128: the same tiles, staging and outputs, with
+// q.k and P.V on the matrix cores (v_mfma_f32_16x16x16_bf16).
+//
+// Per 32-token sub-chunk, wave w takes token group w & 1 (16 rows) and
+// channel half w >> 1 of P.V.  q.k is S = K Q^T (A = 16 K rows, B = the
+// group's queries, zero-padded to 16 columns), so each lane ends with the
+// scores of 4 tokens for one head -- exactly P's layout as the A operand of
+// P.V.  V enters as the B operand through LDS transpose reads.  P (fp32)
+// goes in as a bf16 pair hi + lo, which keeps it to about 16 bits.
+// Each head keeps one running maximum per wave, so the tokens of a wave need
+// no merge; the tile partial combines the two token groups.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte offset of element (row, ch) in a sub-chunk of 256-byte rows staged
+// with the swizzle of stage_sub.
+__device__ __forceinline__ uint32_t swz_off(int row, int ch) {
+  return (uint32_t)(row * 256 + ((((ch >> 3) ^ (row & 15)) << 4) | ((ch & 7) << 1)));
+}
+
+// The twelve LDS reads of one sub-chunk for one wave: eight 8-byte K reads
+// (q.k A operand) and four transpose reads of V (P.V B operand), at
+// immediate offsets from per-lane addresses, then one wait.  asm, for the
+// reason given at lds_read_rows.
+template <int KOFF, int VOFF>
+__device__ __forceinline__ void mfma_operands(uint64_t (&o)[12], const uint32_t (&ad)[12]) {
+  asm volatile(
+      "ds_read_b64 %0, %12 offset:%24\n\t"
+      "ds_read_b64 %1, %13 offset:%24\n\t"
+      "ds_read_b64 %2, %14 offset:%24\n\t"
+      "ds_read_b64 %3, %15 offset:%24\n\t"
+      "ds_read_b64 %4, %16 offset:%24\n\t"
+      "ds_read_b64 %5, %17 offset:%24\n\t"
+      "ds_read_b64 %6, %18 offset:%24\n\t"
+      "ds_read_b64 %7, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %9, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %11, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]),
+        "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "v"(ad[8]), "v"(ad[9]), "v"(ad[10]), "v"(ad[11]), "i"(KOFF), "i"(VOFF)
+      : "memory");
+}
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
+  constexpr int EL = 2, D = 128, RB = D * EL, SUBB = 8192, NSUB = 3, TS = SUBB / RB, TC = TS * NSUB,
+                NI = SUBB / 4096;
+  constexpr int QB = G * D * EL;
+  static_assert(TS == 32 && G <= 8, "two 16-token groups per sub-chunk; at most 8 heads per group");
+  __shared__ __attribute__((aligned(16))) char smem[NSUB * 2 * SUBB];
+  __shared__ __attribute__((aligned(16))) char qs[QB];
+  __shared__ __attribute__((aligned(16))) float lgs[TC * G];  // the chunk's logits
+  __shared__ float sm_ml[4][G][2];
+  float(*sm_acc)[G][64] = reinterpret_cast<float(*)[G][64]>(smem);  // reused after the chunks
+  static_assert(4 * G * 64 * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int U = a.n_units;
+  const Plan pl = a.hp.n ? host_plan(a, blockIdx.x)
+                         : wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
+  if (!pl.valid) {
+    if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
+    return;
+  }
+  const int u = pl.u, b = u / a.Hkv, j = u - b * a.Hkv;
+  const int Lold = pl.L - 1, t0 = pl.t0, t1 = pl.t1;
+  const int tile = blockIdx.x;
+  const char *kc = static_cast<const char *>(a.k_cache) + (size_t)u * a.cap * RB;
+  const char *vc = static_cast<const char *>(a.v_cache) + (size_t)u * a.cap * RB;
+  const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
+  const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
+  float *lg = a.ws.logits + (size_t)u * a.cap * G;
+  {
+    const int off = wave * 1024 + lane * 16;
+    const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
+    if (off < QB) dma16(qsrc + off, qs + wave * 1024);
+  }
+
+  const float cs = a.scale_log2, tau = 8.f / cs;
+  const int grp = wave & 1, half = wave >> 1;  // token group, channel half of P.V
+  const int hl = lane & 15, qd = lane >> 4;    // MFMA lane coordinates
+  // Per-lane LDS addresses (relative to the sub-chunk's K or V buffer).
+  uint32_t ad[12];
+  {
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ad[ks] = base + swz_off(grp * 16 + hl, 16 * ks + 4 * qd);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      ad[8 + t] = base + swz_off(grp * 16 + 4 * qd + (hl >> 2), half * 64 + 16 * t + 4 * (hl & 3));
+  }
+  f32x4_t O[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) O[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // head hl: running maximum (raw q.k) and this lane's partial sum
+  bf16x4_t qb[8];
+  for (int cbase = t0; cbase < t1; cbase += TC) {
+    if (cbase != t0) lds_barrier();  // every wave is done with the previous chunk
+#pragma unroll
+    for (int sc = 0; sc < NSUB; ++sc) {
+      const int c0 = cbase + sc * TS;
+      stage_sub<RB, NI, true>(smem + sc * 2 * SUBB, smem + sc * 2 * SUBB + SUBB, kc, vc, kn, vn, c0,
+                              max(0, min(TS, t1 - c0)), t0, Lold, wave, lane);
+    }
+#pragma unroll
+    for (int sc = 0; sc < NSUB; ++sc) {
+      const int c0 = cbase + sc * TS;
+      if (sc == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 1)) : "memory");
+      else if (sc == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 2)) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      dma_barrier();
+      if (sc == 0) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          uint2 w = make_uint2(0, 0);
+          if (hl < G) w = *reinterpret_cast<const uint2 *>(qs + (hl * D + 16 * ks + 4 * qd) * EL);
+          qb[ks] = __builtin_bit_cast(bf16x4_t, w);
+        }
+      }
+      uint64_t rd[12];
+      if (sc == 0) mfma_operands<0, SUBB>(rd, ad);
+      else if (sc == 1) mfma_operands<2 * SUBB, 3 * SUBB>(rd, ad);
+      else mfma_operands<4 * SUBB, 5 * SUBB>(rd, ad);
+      // q.k: lane (qd, hl) gets the raw scores of tokens 4 qd + i of its group for head hl.
+      f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) S = mfma16(__builtin_bit_cast(bf16x4_t, rd[ks]), qb[ks], S);
+      const int nrows = min(TS, t1 - c0);
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = (grp * 16 + 4 * qd + i < nrows) ? S[i] : -INFINITY;
+      if (half == 0 && hl < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lgs[(sc * TS + grp * 16 + 4 * qd + i) * G + hl] = sv[i];
+      }
+      // Softmax of head hl: one running maximum per wave, moved (with a
+      // rescale of l and of the head's output rows) only when the scores pass
+      // it by more than 8 / cs.
+      float mx = fmaxf(fmaxf(m, fmaxf(sv[0], sv[1])), fmaxf(sv[2], sv[3]));
+      {
+        float w2 = mx;
+        permlane16_swap(mx, w2);
+        mx = fmaxf(mx, w2);
+        w2 = mx;
+        permlane32_swap(mx, w2);
+        mx = fmaxf(mx, w2);
+      }
+      if (__ballot(mx > m + tau) != 0ull) {
+        const float corr = (mx == -INFINITY) ? 1.f : fast_exp2((m - mx) * cs);
+        l *= corr;
+        m = mx;
+        // Output row i of this lane is head 4 qd + i; its factor lives in lane (head).
+        float fi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float fa = lane_value(corr, i < G ? i : G - 1);
+          if constexpr (G > 4) {
+            const float fb = lane_value(corr, 4 + i);
+            fi[i] = qd == 0 ? fa : fb;
+          } else {
+            fi[i] = fa;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[t][i] *= fi[i];
+      }
+      const float mc = (m == -INFINITY) ? 0.f : m * cs;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = fast_exp2(fmaf(sv[i], cs, -mc));
+        l += pv[i];
+      }
+      bf16x4_t phi, plo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        phi[i] = (__bf16)pv[i];
+        plo[i] = (__bf16)(pv[i] - (float)phi[i]);
+      }
+      // P.V for the wave's 64 channels: O[head][ch] += P[head][tok] V[tok][ch].
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x4_t vb4 = __builtin_bit_cast(bf16x4_t, rd[8 + t]);
+        O[t] = mfma16(phi, vb4, O[t]);
+        O[t] = mfma16(plo, vb4, O[t]);
+      }
+      asm volatile("" : "+v"(m), "+v"(l));
+      sched_fence();
+    }
+    // The chunk's logits: the two half-0 waves write their own rows.
+    if (half == 0) {
+      constexpr int WR = 16 * G;  // floats per wave per sub-chunk
+#pragma unroll
+      for (int q0 = 0; q0 < NSUB * WR; q0 += kWave) {
+        const int q = q0 + lane;
+        const int sc = q / WR, w = q - sc * WR;
+        const int row = grp * 16 + w / G;
+        const int n = cbase + sc * TS + row;
+        if (q < NSUB * WR && n < t1) lg[(size_t)n * G + (w % G)] = lgs[(sc * TS + row) * G + (w % G)];
+      }
+    }
+  }
+  // Tile partial: l summed over the lane rows of each head; the two token
+  // groups (waves 2 h and 2 h + 1 for channel half h) combined through LDS.
+  {
+    float w2 = l;
+    permlane16_swap(l, w2);
+    l += w2;
+    w2 = l;
+    permlane32_swap(l, w2);
+    l += w2;
+  }
+  lds_barrier();  // every wave is done with the staging buffers: they become merge scratch
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = 4 * qd + i;
+      if (head < G) sm_acc[wave][head][16 * t + hl] = O[t][i];
+    }
+  if (qd == 0 && hl < G) {
+    sm_ml[wave][hl][0] = m;
+    sm_ml[wave][hl][1] = l;
+  }
+  lds_barrier();
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D, ch = idx - h * D, w0 = 2 * (ch >> 6), w1 = w0 + 1;
+    const float m0 = sm_ml[w0][h][0], m1 = sm_ml[w1][h][0];
+    const float M = fmaxf(m0, m1);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    const float e0 = fast_exp2((m0 - Ms) * cs), e1 = fast_exp2((m1 - Ms) * cs);
+    a.ws.part_acc[((size_t)tile * G + h) * D + ch] = sm_acc[w0][h][ch & 63] * e0 + sm_acc[w1][h][ch & 63] * e1;
+    if (ch == 0)
+      *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + h) * 2) =
+          make_float2(M, sm_ml[w0][h][1] * e0 + sm_ml[w1][h][1] * e1);
   }
   if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
@@ -595,14 +954,16 @@ template <int EL, int D, int G>
 __host__ __device__ constexpr int k2_noc() { return G * D / 64; }
 
 // Softmax statistics of a unit per head from its tiles' (max, sum) pairs:
-// sM[g] = max over tiles, sL[g] = sum over tiles of sum * 2^(max - sM[g]).
-// Pair i = tile * G + g; thread t owns pairs t, t + kT2, ... (all of head
-// t % G); v0 is its first pair, already loaded.  When sm_m is given, the
-// maxima of head gm are also left there per tile.
+// M = max over tiles, L = sum over tiles of sum * 2^(max - M).  Pair i =
+// tile * G + g; thread t owns pairs t, t + kT2, ... (all of head t % G); v0 is
+// its first pair, already loaded.  Every wave finishes the reduction itself,
+// so lane l leaves with M and L of head l % G (no broadcast barrier).  When
+// sm_m is given, the maxima of head gm are also left there per tile.
 template <int G>
-__device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 v0, float (*red)[G], float *sM,
-                           float *sL, float *sm_m, int gm) {
+__device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 v0, float cs, float (*red)[G],
+                                           float (*red2)[G], float &Mlane, float &Llane, float *sm_m, int gm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NV = kNW2 * G, KV = (NV + kWave - 1) / kWave;
   float mx = tid < npair ? v0.x : -INFINITY;
   for (int i = tid + kT2; i < npair; i += kT2) mx = fmaxf(mx, pml[i].x);
   if (sm_m) {
@@ -610,34 +971,33 @@ __device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 
     for (int i = tid + kT2; i < npair; i += kT2)
       if (i % G == gm) sm_m[i / G] = pml[i].x;
   }
-#pragma unroll
-  for (int off = G; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = lanes_max<G>(mx);
   if (lane < G) red[wave][lane] = mx;
   lds_barrier();
-  if (tid < G) {
-    float M = red[0][tid];
-    for (int w = 1; w < kNW2; ++w) M = fmaxf(M, red[w][tid]);
-    sM[tid] = M;
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KV; ++k) {
+    const int idx = lane + kWave * k;  // idx % G == lane % G
+    if (idx < NV) M = fmaxf(M, red[idx / G][idx % G]);
   }
-  lds_barrier();
-  const float Mg = sM[tid % G];
-  const float Ms = (Mg == -INFINITY) ? 0.f : Mg;
-  float ls = tid < npair ? v0.y * fast_exp2(v0.x - Ms) : 0.f;
+  M = lanes_max<G>(M);
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+  float ls = tid < npair ? v0.y * fast_exp2((v0.x - Ms) * cs) : 0.f;
   for (int i = tid + kT2; i < npair; i += kT2) {
     const float2 v = pml[i];
-    ls += v.y * fast_exp2(v.x - Ms);
+    ls += v.y * fast_exp2((v.x - Ms) * cs);
   }
+  ls = lanes_sum<G>(ls);
+  if (lane < G) red2[wave][lane] = ls;
+  lds_barrier();
+  float L = 0.f;
 #pragma unroll
-  for (int off = G; off < kWave; off <<= 1) ls += __shfl_xor(ls, off);
-  lds_barrier();  // every wave has read red
-  if (lane < G) red[wave][lane] = ls;
-  lds_barrier();
-  if (tid < G) {
-    float sum = 0.f;
-    for (int w = 0; w < kNW2; ++w) sum += red[w][tid];
-    sL[tid] = sum;
+  for (int k = 0; k < KV; ++k) {
+    const int idx = lane + kWave * k;
+    if (idx < NV) L += red2[idx / G][idx % G];
   }
-  lds_barrier();
+  Mlane = M;
+  Llane = lanes_sum<G>(L);
 }
 
 template <int EL, int D, int G>
@@ -646,14 +1006,12 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
   constexpr int NB = K2Lay<G>::NB, CHUNK = K2Lay<G>::CHUNK;
   constexpr int NOC = k2_noc<EL, D, G>();
   constexpr int NTW = 8;  // tiles per wave loaded in one batch by an output block
-  __shared__ float red[kNW2][G];
-  __shared__ float sM[G], sL[G];
+  __shared__ float red[kNW2][G], red2[kNW2][G];
   __shared__ float sm_m[kMaxGrid];           // output blocks: tile maxima of their head
   __shared__ float red_o[kNW2][kWave];       // output blocks: per-wave partial sums
   __shared__ uint64_t sk[kNW2];
   __shared__ int ss[kNW2];
   __shared__ float s_newimp;
-  __shared__ int s_dst;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
@@ -732,7 +1090,8 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
       };
       load_batch(nb0);
       const int beta = a.budget ? beta_ld : a.budget_all;
-      unit_stats<G>(pml, npair, v0, red, sM, sL, nullptr, 0);
+      float Mlane, Llane;
+      unit_stats<G>(pml, npair, v0, a.scale_log2, red, red2, Mlane, Llane, nullptr, 0);
       if (a.hp.n) {  // a host plan covers every unit: check it against the device
         const int err = (L > a.cap) ? HIKV_ECAPACITY : ((beta < S || beta > a.cap) ? HIKV_EBUDGET : 0);
         if (r == 0 && tid == 0) {
@@ -749,8 +1108,9 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
       float Mg[G], ILg[G];
     #pragma unroll
       for (int g = 0; g < G; ++g) {
-        Mg[g] = sM[g];
-        ILg[g] = 1.f / sL[g];
+        const float Mr = lane_value(Mlane, g);  // raw q.k units
+        Mg[g] = (Mr == -INFINITY) ? 0.f : Mr * a.scale_log2;
+        ILg[g] = 1.f / lane_value(Llane, g);
       }
       // Steady state with the whole unit in one batch: the importance stays in
       // registers until the victim is known, so no slot is written twice.
@@ -765,7 +1125,7 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
           if (n < nb1) {
             float p = 0.f;
     #pragma unroll
-            for (int g = 0; g < G; ++g) p += fast_exp2(tl[i][g] - Mg[g]) * ILg[g];
+            for (int g = 0; g < G; ++g) p += fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
             const bool is_new = n == Lold;
             const float iv = (is_new ? 0.f : ti[i]) + p;
             const int pn = is_new ? newest : tp[i];
@@ -795,15 +1155,7 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
         }
         return;
       }
-    #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t ko = __shfl_xor(best, off);
-        const int so = __shfl_xor(best_slot, off);
-        if (ko < best) {
-          best = ko;
-          best_slot = so;
-        }
-      }
+      wave_min_key(best, best_slot);
       if (lane == 0) {
         sk[wave] = best;
         ss[wave] = best_slot;
@@ -812,19 +1164,12 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
       const float newimp = s_newimp;
       if (n_evict == 1) {
         // Steady state: the lowest key is the victim; the new token takes its
-        // slot, or is itself dropped.
-        if (tid == 0) {
-          uint64_t kk = sk[0];
-          int vs = ss[0];
-          for (int w = 1; w < kNW2; ++w)
-            if (sk[w] < kk) {
-              kk = sk[w];
-              vs = ss[w];
-            }
-          s_dst = (vs == Lold) ? -1 : vs;
-        }
-        lds_barrier();
-        const int dst = s_dst;
+        // slot, or is itself dropped.  Every wave reduces the waves' minima.
+        uint64_t kk = lane < kNW2 ? sk[lane] : ~0ull;
+        int vs = lane < kNW2 ? ss[lane] : -1;
+        wave_min_key(kk, vs);
+        const int victim = __builtin_amdgcn_readfirstlane(vs);
+        const int dst = (victim == Lold) ? -1 : victim;
         if (dst >= 0 && tid < 2 * NR)
           reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)dst * RB)[tid % NR] = nrow;
         if (defer) {
@@ -920,26 +1265,29 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
 #pragma unroll
   for (int i = 0; i < NTW; ++i) pa[i] = pacc[(size_t)min(wave + kNW2 * i, nt - 1) * GD];
   const int beta = a.budget ? beta_ld : a.budget_all;
-  unit_stats<G>(pml, npair, v0, red, sM, sL, sm_m, g);
+  float Mlane, Llane;
+  unit_stats<G>(pml, npair, v0, a.scale_log2, red, red2, Mlane, Llane, sm_m, g);
+  const float Mo = lane_value(Mlane, g), Lo = lane_value(Llane, g);
   float *outu = a.out + (size_t)(b * a.Hq + j * G) * D;
   if (a.hp.n && (L > a.cap || beta < S || beta > a.cap)) {  // unit left alone
     if (wave == 0) outu[o] = 0.f;
     end_wave();
   }
-  const float Ms = (sM[g] == -INFINITY) ? 0.f : sM[g];
+  const float Ms = (Mo == -INFINITY) ? 0.f : Mo;
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
     const int t = wave + kNW2 * i;
-    if (t < nt) acc += pa[i] * fast_exp2(sm_m[t] - Ms);
+    if (t < nt) acc += pa[i] * fast_exp2((sm_m[t] - Ms) * a.scale_log2);
   }
-  for (int t = wave + kNW2 * NTW; t < nt; t += kNW2) acc += pacc[(size_t)t * GD] * fast_exp2(sm_m[t] - Ms);
+  for (int t = wave + kNW2 * NTW; t < nt; t += kNW2)
+    acc += pacc[(size_t)t * GD] * fast_exp2((sm_m[t] - Ms) * a.scale_log2);
   red_o[wave][lane] = acc;
   lds_barrier();
   if (wave == 0) {
     float sum = 0.f;
     for (int w = 0; w < kNW2; ++w) sum += red_o[w][lane];
-    outu[o] = sum / sL[g];
+    outu[o] = sum / Lo;
   }
 
   end_wave();
@@ -948,6 +1296,16 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
+// The attention kernel of a configuration: matrix cores for bf16 with
+// D = 128, vector ALUs otherwise.
+template <int EL, int D, int G>
+static constexpr bool use_mfma() { return EL == 2 && D == 128; }
+template <int EL, int D, int G>
+static void (*attend_kernel())(StepArgs) {
+  if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G>;
+  else return k_attend<EL, D, G>;
+}
+
 template <int EL, int D, int G>
 static int attend_grid(int n_units) {
   static int per_cu_cache[64];
@@ -955,7 +1313,8 @@ static int attend_grid(int n_units) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (per_cu_cache[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attend<EL, D, G>, kThreads, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<EL, D, G>(), kThreads, 0) != hipSuccess)
+      return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     per_cu_cache[dev] = per_cu * cus;
   }
@@ -969,12 +1328,13 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   if (g <= 0) return hipErrorInvalidValue;
   const dim3 grid(g), block(kThreads);
   hipError_t e;
+  void (*kern)(StepArgs) = attend_kernel<EL, D, G>();
   if (ev0 && ev1) {
     // The events are recorded by the dispatch itself: they time the kernel's
     // execution, not the command processor's way to it.
-    hipExtLaunchKernelGGL((k_attend<EL, D, G>), grid, block, 0, s, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, a);
   } else {
-    hipLaunchKernelGGL((k_attend<EL, D, G>), grid, block, 0, s, a);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Second launch: per unit, importance blocks to cover the capacity, then
