@@ -15,6 +15,10 @@ constexpr int kTileMin = 64;        // smallest split-K tile, tokens
 constexpr int kTilesTarget = 512;   // split-K tiles aimed for per step (2 per CU)
 constexpr int kMaxGrid = 2048;      // upper bound on resident workgroups (256 CUs x 8)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kImpChunk = 2048;     // tokens per importance block of the step's second launch
+
+// Importance blocks per unit in the step's second launch.
+inline int imp_blocks(int cap) { return (cap + kImpChunk - 1) / kImpChunk; }
 
 // ---------------------------------------------------------------------------
 // Workspace layout.  Offsets are 256-byte aligned; everything is derived from
@@ -40,9 +44,11 @@ struct Ws {
   int32_t *tsel;        // [B*Hq][k_T] Stage II exact-softmax slots
   int32_t *tcount;      // [B*Hq]
   int32_t *urec;        // [n_units][4] per-unit plan of the step: first tile, tiles, tokens
+  int32_t *icand;       // [n_units][imp_blocks(cap)][4] per importance block: its lowest
+                        //   eviction key (low, high word) and that key's slot
 };
 
-constexpr int kWsParts = 17;
+constexpr int kWsParts = 18;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -72,6 +78,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
       sizeof(int32_t) * B * Hq * (size_t)(kT > 0 ? kT : 1),  // tsel
       sizeof(int32_t) * B * Hq,        // tcount
       sizeof(int32_t) * 4 * U,         // urec
+      sizeof(int32_t) * 4 * U * (size_t)imp_blocks(cap),  // icand
   };
   WsSizes w;
   size_t o = 0;
@@ -103,6 +110,7 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.tsel = reinterpret_cast<int32_t *>(b + s.off[14]);
   w.tcount = reinterpret_cast<int32_t *>(b + s.off[15]);
   w.urec = reinterpret_cast<int32_t *>(b + s.off[16]);
+  w.icand = reinterpret_cast<int32_t *>(b + s.off[17]);
   return w;
 }
 
@@ -181,10 +189,27 @@ __device__ __forceinline__ uint32_t ord_f32(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inverse of ord_f32.
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
+}
+
 // Eviction key: smaller = evicted first.  Lower importance first; among
 // equal importance the higher position first (so the lower one is kept).
 __device__ __forceinline__ uint64_t evict_key(float imp, int32_t pos) {
   return ((uint64_t)ord_f32(imp) << 32) | (uint64_t)(~(uint32_t)pos);
+}
+
+// Stores, loads and a counter increment that are coherent across the whole
+// device (all XCDs' L2 caches) without a cache-wide write-back.
+__device__ __forceinline__ void store_agent(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ticket_agent(uint32_t *p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int unit_budget(const StepArgs &a, int u) {

@@ -946,8 +946,9 @@ constexpr int kNW2 = kT2 / kWave;    // its waves
 
 template <int G>
 struct K2Lay {
-  static constexpr int NB = G <= 4 ? 9 : 5;  // tokens per thread per batch
-  static constexpr int CHUNK = NB * kT2;     // tokens per importance block
+  static constexpr int CHUNK = kImpChunk;    // tokens per importance block
+  static constexpr int NB = CHUNK / kT2;     // tokens per thread per batch
+  static_assert(NB * kT2 == CHUNK, "an importance block takes whole batches");
 };
 
 template <int EL, int D, int G>
@@ -1001,7 +1002,7 @@ __device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 
 }
 
 template <int EL, int D, int G>
-__global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
+__global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k_finalize(StepArgs a) {
   constexpr int RB = D * EL, NR = RB / 16, GD = G * D;
   constexpr int NB = K2Lay<G>::NB, CHUNK = K2Lay<G>::CHUNK;
   constexpr int NOC = k2_noc<EL, D, G>();
@@ -1012,6 +1013,7 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
   __shared__ uint64_t sk[kNW2];
   __shared__ int ss[kNW2];
   __shared__ float s_newimp;
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
@@ -1101,10 +1103,14 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
         if (err) return;
       }
       const bool over = L > beta;
-      if (over && r > 0) return;  // the unit's eviction needs all its tokens in one block
-      const int nb1 = over ? L : min(L, nb0 + CHUNK);
-      const int Wp = min(a.n_recent, beta - S);
       const int n_evict = over ? L - beta : 0;
+      // One eviction (the steady state) is spread over the unit's blocks like
+      // the importance; more than one needs every token in one block.
+      const bool bulk = n_evict > 1;
+      if (bulk && r > 0) return;
+      const int nb1 = bulk ? L : min(L, nb0 + CHUNK);
+      const int nact = (L + CHUNK - 1) / CHUNK;  // blocks holding tokens of the unit
+      const int Wp = min(a.n_recent, beta - S);
       float Mg[G], ILg[G];
     #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1112,9 +1118,9 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
         Mg[g] = (Mr == -INFINITY) ? 0.f : Mr * a.scale_log2;
         ILg[g] = 1.f / lane_value(Llane, g);
       }
-      // Steady state with the whole unit in one batch: the importance stays in
-      // registers until the victim is known, so no slot is written twice.
-      const bool defer = n_evict == 1 && nb1 - nb0 <= CHUNK;
+      // Steady state: the importance stays in registers until the block's
+      // lowest key is known, so no slot is written twice.
+      const bool defer = n_evict == 1;
       uint64_t best = ~0ull;
       int best_slot = -1;
       for (int base = nb0; base < nb1; base += CHUNK) {
@@ -1161,18 +1167,74 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
         ss[wave] = best_slot;
       }
       lds_barrier();
-      const float newimp = s_newimp;
+      float newimp = s_newimp;  // valid in the block holding slot Lold
       if (n_evict == 1) {
         // Steady state: the lowest key is the victim; the new token takes its
         // slot, or is itself dropped.  Every wave reduces the waves' minima.
         uint64_t kk = lane < kNW2 ? sk[lane] : ~0ull;
         int vs = lane < kNW2 ? ss[lane] : -1;
         wave_min_key(kk, vs);
-        const int victim = __builtin_amdgcn_readfirstlane(vs);
+        int victim = __builtin_amdgcn_readfirstlane(vs);
+        if (nact > 1) {
+          // Every importance value of the block is final except the one at its
+          // lowest key.  That slot, its key and its importance (the key's high
+          // word) go out with agent-coherent stores; the unit's last block to
+          // take a ticket finds the victim among all blocks' lowest keys and
+          // stores the deferred values, so no slot is written twice.
+    #pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            const int n = nb0 + tid + i * kT2;
+            if (n < nb1 && n != Lold && n != victim) impw[n] = ti[i];
+          }
+          int32_t *cand = a.ws.icand + (size_t)u * nib * 4;
+          if (tid == 0) {
+            store_agent(cand + 4 * r, (int32_t)(uint32_t)kk);
+            store_agent(cand + 4 * r + 1, (int32_t)(uint32_t)(kk >> 32));
+            store_agent(cand + 4 * r + 2, victim);
+            if (nb1 == L) store_agent(reinterpret_cast<int32_t *>(a.ws.fz_newimp) + u, __float_as_int(newimp));
+            // The stores above are complete before the ticket is taken.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            s_last = ticket_agent(a.ws.ticket + u) == (uint32_t)(nact - 1);
+          }
+          __syncthreads();
+          if (!s_last || wave != 0) return;  // the rest is wave 0's
+          kk = ~0ull;
+          vs = -1;
+          uint32_t chi = 0xffffffffu;
+          int cslot = -1;
+          if (lane < nact) {
+            const uint32_t lo = (uint32_t)load_agent(cand + 4 * lane);
+            chi = (uint32_t)load_agent(cand + 4 * lane + 1);
+            cslot = load_agent(cand + 4 * lane + 2);
+            kk = ((uint64_t)chi << 32) | lo;
+            vs = cslot;
+          }
+          for (int i = lane + kWave; i < nact; i += kWave) {  // more blocks than lanes
+            const uint64_t k = ((uint64_t)(uint32_t)load_agent(cand + 4 * i + 1) << 32) |
+                               (uint32_t)load_agent(cand + 4 * i);
+            if (k < kk) {
+              kk = k;
+              vs = load_agent(cand + 4 * i + 2);
+            }
+          }
+          wave_min_key(kk, vs);
+          victim = __builtin_amdgcn_readfirstlane(vs);
+          newimp = __int_as_float(load_agent(reinterpret_cast<const int32_t *>(a.ws.fz_newimp) + u));
+          // The deferred importance of the blocks' lowest-key slots but the victim.
+          if (wave == 0) {
+            if (cslot >= 0 && cslot != victim && cslot != Lold) impw[cslot] = unord_f32(chi);
+            for (int i = lane + kWave; i < nact; i += kWave) {
+              const int sl = load_agent(cand + 4 * i + 2);
+              if (sl >= 0 && sl != victim && sl != Lold)
+                impw[sl] = unord_f32((uint32_t)load_agent(cand + 4 * i + 1));
+            }
+          }
+          if (tid == 0) store_agent(reinterpret_cast<int32_t *>(a.ws.ticket) + u, 0);
+        }
         const int dst = (victim == Lold) ? -1 : victim;
         if (dst >= 0 && tid < 2 * NR)
           reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)dst * RB)[tid % NR] = nrow;
-        if (defer) {
+        if (nact == 1) {
     #pragma unroll
           for (int i = 0; i < NB; ++i) {
             const int n = nb0 + tid + i * kT2;
@@ -1181,12 +1243,9 @@ __global__ __launch_bounds__(kT2) void k_finalize(StepArgs a) {
               if (n == dst) posw[n] = newest;
             }
           }
-        } else if (dst >= 0) {
-          __syncthreads();  // the victim's own importance store has completed
-          if (tid == 0) {
-            posw[dst] = newest;
-            impw[dst] = newimp;
-          }
+        } else if (dst >= 0 && tid == 0) {
+          posw[dst] = newest;
+          impw[dst] = newimp;
         }
         return;
       }
@@ -1339,7 +1398,7 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Second launch: per unit, importance blocks to cover the capacity, then
   // one output block per 64 outputs.
-  const int nib = (a.cap + K2Lay<G>::CHUNK - 1) / K2Lay<G>::CHUNK;
+  const int nib = imp_blocks(a.cap);
   const long long g2 = (long long)a.n_units * (nib + k2_noc<EL, D, G>());
   if (g2 > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)g2), dim3(kT2), 0, s, a);

@@ -117,6 +117,20 @@ def test_headkv_ragged_budgets_lockstep():
     say("headkv reduced worst row err", worst)
 
 
+@pytest.mark.parametrize("n_recent", [128, 0], ids=["window", "no-window"])
+def test_long_units_split_eviction_lockstep(n_recent):
+    """Steady-state eviction in units longer than one importance block of the
+    second launch (2048 tokens): each block's lowest key meets the others' in
+    the unit's last block to finish.  Budgets put the new token alone in the
+    last block (2048), next to one old token (2049), and across 2-4 blocks;
+    without a recent window the new token itself can be the victim."""
+    w = W.workload("headkv32k", ctx=7000, steps=4, batch=1)
+    w.budgets = np.array([[2048, 4097, 6143, 100, 3000, 64, 2049, 5000]], dtype=np.int32)
+    w.n_recent = n_recent
+    d = W.generate(w)
+    lockstep(_run(w, d), d, w.steps, tag=f"split eviction n_recent={n_recent}")
+
+
 def test_longctx_g8_lockstep_and_full_attention():
     w = W.workload("longctx128k", ctx=3000, steps=2, batch=1)
     w.budget_all, w.n_recent = 256, 64
