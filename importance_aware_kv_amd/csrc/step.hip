@@ -73,6 +73,16 @@ template <typename T>
 __device__ __forceinline__ T ld_vec(const T *p, int z) {
   return p[z];
 }
+// A load of global memory through a uniform pointer the compiler cannot
+// trace to its origin, so that it is neither merged with another load of the
+// same address nor split into per-branch loads.
+template <typename T>
+__device__ __forceinline__ T ld_opaque(const T *p, int z) {
+  using GP = const __attribute__((address_space(1))) T *;
+  GP g = (GP)p;
+  asm("" : "+s"(g));
+  return g[z];
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
@@ -1058,7 +1068,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     [&]() __attribute__((always_inline)) {
       // ---------------- importance block ----------------
       const int newest = ld_vec(a.new_pos + b, vz);
-      const int beta_ld = ld_vec(a.budget ? a.budget + u : a.new_pos + b, vz);
+      const int beta_ld = ld_opaque(a.budget ? a.budget + u : a.new_pos + b, vz);
       const float2 v0 = pml[min(tid, npair - 1)];
       const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
       const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
@@ -1315,7 +1325,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     end_wave();
   }
   // ---------------- output block: chunk c of the unit's G*D outputs ----
-  const int beta_ld = ld_vec(a.budget ? a.budget + u : a.new_pos + b, vz);
+  const int beta_ld = ld_opaque(a.budget ? a.budget + u : a.new_pos + b, vz);
   const float2 v0 = pml[min(tid, npair - 1)];
   const int c = r - nib;
   const int o = c * 64 + lane, g = (c * 64) / D;
