@@ -27,13 +27,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_attend_hbm_traffic_headkv32k.md")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_attend_mfma_hbm_traffic_headkv32k.md")
 KERNEL_SOURCES = ("importance_aware_kv_amd/csrc/step.hip", "importance_aware_kv_amd/csrc/hikv_common.h",
                   "importance_aware_kv_amd/csrc/hikv_block.h")
 
 
 def measured_traffic():
-    """HBM bytes per k_attend launch from the committed counter record, or None
+    """HBM bytes per attention launch from the committed counter record, or None
     when the kernel sources changed since the counters were taken."""
     import hashlib
     try:
@@ -248,7 +248,8 @@ def main():
             "unit": "GB/s",
             "frac": round(attend_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
-            "kernel": "k_attend (split-K attention over the live K/V rows; HIP events per launch)",
+            "kernel": "k_attend_mfma<4> (split-K attention over the live K/V rows on matrix cores; "
+                      "HIP events per launch)",
             "bytes_per_launch": attend_bytes,
             "us_per_launch": round(attend_ms * 1e3, 3),
             "whole_step": {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
