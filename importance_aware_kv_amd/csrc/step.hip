@@ -175,13 +175,13 @@ __device__ Plan wave_plan(const StepArgs &a, int tile, int ntarget, bool write_r
 }
 
 // Plan from the kernel arguments (host-computed from the caller's copy of
-// len[]).  Lane i reads unit i's end tile and length, so the lookup costs one
-// round trip: the unit is the number of units that end at or before the tile.
-__device__ Plan host_plan(const StepArgs &a, int tile) {
+// len[]).  Lane i holds unit i's end tile and length (bend, Lv: loaded by the
+// caller before it knows whether there is a host plan, so that the lookup
+// costs one round trip); the unit is the number of units that end at or
+// before the tile.
+__device__ Plan host_plan(const StepArgs &a, int tile, int bend, int Lv) {
   const int lane = threadIdx.x & 63;
   const int n = a.hp.n;
-  const int bend = a.hp.base[lane + 1];
-  const int Lv = a.hp.L[lane];
   const int u = __popcll(__ballot(lane < n && bend <= tile));
   Plan p;
   p.T = a.hp.T;
@@ -461,8 +461,17 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = a.n_units;
-  const Plan pl = a.hp.n ? host_plan(a, blockIdx.x)
-                         : wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
+  // The host plan's words are loaded before its presence is known (the kernel
+  // arguments are always readable); the device plan's path uses them too, after
+  // its own loads, so that the compiler issues them ahead of the branch.
+  const int hp_bend = a.hp.base[lane + 1], hp_len = a.hp.L[lane];
+  Plan pl;
+  if (a.hp.n) {
+    pl = host_plan(a, blockIdx.x, hp_bend, hp_len);
+  } else {
+    pl = wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
+    asm volatile("" ::"v"(hp_bend), "v"(hp_len));
+  }
 
   if (!pl.valid) {
     if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
@@ -764,8 +773,17 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = a.n_units;
-  const Plan pl = a.hp.n ? host_plan(a, blockIdx.x)
-                         : wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
+  // The host plan's words are loaded before its presence is known (the kernel
+  // arguments are always readable); the device plan's path uses them too, after
+  // its own loads, so that the compiler issues them ahead of the branch.
+  const int hp_bend = a.hp.base[lane + 1], hp_len = a.hp.L[lane];
+  Plan pl;
+  if (a.hp.n) {
+    pl = host_plan(a, blockIdx.x, hp_bend, hp_len);
+  } else {
+    pl = wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
+    asm volatile("" ::"v"(hp_bend), "v"(hp_len));
+  }
   if (!pl.valid) {
     if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
     return;
@@ -1027,21 +1045,23 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
-  const int nib = (int)(gridDim.x / (unsigned)a.n_units) - NOC;  // importance blocks per unit
-  const int u = blockIdx.x / (nib + NOC), r = blockIdx.x - u * (nib + NOC);
-  // The empty asm statements keep the compiler from merging the two plan
-  // sources into one load through a selected pointer (a flat load, waited
-  // for at once).
+  // Grid: x = the unit's workgroup (nib importance blocks, then NOC output
+  // blocks), y = the unit, so that the unit is known without a load.
+  const int nib = (int)gridDim.x - NOC;  // importance blocks per unit
+  const int u = blockIdx.y, r = blockIdx.x;
+  // The host plan's words (kernel arguments, clamped to its table) are loaded
+  // with the flag that says whether there is one, so that the host plan costs
+  // one round trip; the device plan's path uses them too, after its own load,
+  // so that the compiler issues them ahead of the branch.
+  const int uh = min(u, kHostPlanUnits - 1);
+  const int hb0 = a.hp.base[uh], hb1 = a.hp.base[uh + 1], hlen = a.hp.L[uh];
   int tb, nt, L;
   if (a.hp.n) {
-    tb = a.hp.base[u];
-    nt = a.hp.base[u + 1] - tb;
-    L = a.hp.L[u];
-    asm volatile("" ::: "memory");
+    tb = hb0, nt = hb1 - hb0, L = hlen;
   } else {
     const int4 rec = reinterpret_cast<const int4 *>(a.ws.urec)[u];
     tb = rec.x, nt = rec.y, L = rec.z;
-    asm volatile("" ::: "memory");
+    asm volatile("" ::"s"(hb0), "s"(hb1), "s"(hlen));
   }
   if (nt <= 0) return;  // a unit the first launch excluded
   const bool imp_blk = r < nib;
@@ -1409,9 +1429,8 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   // Second launch: per unit, importance blocks to cover the capacity, then
   // one output block per 64 outputs.
   const int nib = imp_blocks(a.cap);
-  const long long g2 = (long long)a.n_units * (nib + k2_noc<EL, D, G>());
-  if (g2 > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)g2), dim3(kT2), 0, s, a);
+  hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)(nib + k2_noc<EL, D, G>()), (unsigned)a.n_units),
+                     dim3(kT2), 0, s, a);
   return hipGetLastError();
 }
 
