@@ -24,6 +24,11 @@ ARCH = os.environ.get("HIKV_ARCH", "gfx950")
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results and accumulators in ordinary VGPRs: the attention
+    # kernel's outputs are also rescaled by vector instructions, and with
+    # accumulation registers the compiler copies them back and forth around
+    # every P.V step.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
