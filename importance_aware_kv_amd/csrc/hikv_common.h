@@ -201,7 +201,9 @@ __device__ __forceinline__ uint64_t evict_key(float imp, int32_t pos) {
 }
 
 // Stores, loads and a counter increment that are coherent across the whole
-// device (all XCDs' L2 caches) without a cache-wide write-back.
+// device (all XCDs' L2 caches) without a cache-wide write-back.  The stores
+// write through to memory: a kernel's results stored this way leave little
+// for the write-back at its end, which the next launch waits for.
 __device__ __forceinline__ void store_agent(int32_t *p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -210,6 +212,9 @@ __device__ __forceinline__ int32_t load_agent(const int32_t *p) {
 }
 __device__ __forceinline__ uint32_t ticket_agent(uint32_t *p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent_f(float *p, float v) {
+  store_agent(reinterpret_cast<int32_t *>(p), __float_as_int(v));
 }
 
 __device__ __forceinline__ int unit_budget(const StepArgs &a, int u) {

@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
         const int sc = q / WR, w = q - sc * WR;
         const int row = wave * (TS / 4) + w / G;
         const int n = cbase + sc * TS + row;
-        if (q < NSUB * WR && n < t1) lg[(size_t)n * G + (w % G)] = lgs[(sc * TS + row) * G + (w % G)];
+        if (q < NSUB * WR && n < t1) store_agent_f(lg + (size_t)n * G + (w % G), lgs[(sc * TS + row) * G + (w % G)]);
       }
     }
   }
@@ -699,8 +699,11 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
       av += sm_acc[w][g][d] * e;
       lv += sm_ml[w][g][1] * e;
     }
-    a.ws.part_acc[((size_t)tile * G + g) * D + d] = av;
-    if (d == 0) *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + g) * 2) = make_float2(M, lv);
+    store_agent_f(a.ws.part_acc + ((size_t)tile * G + g) * D + d, av);
+    if (d == 0) {
+      store_agent_f(a.ws.part_ml + ((size_t)tile * G + g) * 2, M);
+      store_agent_f(a.ws.part_ml + ((size_t)tile * G + g) * 2 + 1, lv);
+    }
   }
   if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
@@ -915,7 +918,9 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
       asm volatile("" : "+v"(m), "+v"(l));
       sched_fence();
     }
-    // The chunk's logits: the two half-0 waves write their own rows.
+    // The chunk's logits: the two half-0 waves write their own rows.  This
+    // launch's results are stored write-through, which leaves little for the
+    // write-back at its end that the second launch waits for.
     if (half == 0) {
       constexpr int WR = 16 * G;  // floats per wave per sub-chunk
 #pragma unroll
@@ -924,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
         const int sc = q / WR, w = q - sc * WR;
         const int row = grp * 16 + w / G;
         const int n = cbase + sc * TS + row;
-        if (q < NSUB * WR && n < t1) lg[(size_t)n * G + (w % G)] = lgs[(sc * TS + row) * G + (w % G)];
+        if (q < NSUB * WR && n < t1) store_agent_f(lg + (size_t)n * G + (w % G), lgs[(sc * TS + row) * G + (w % G)]);
       }
     }
   }
@@ -957,10 +962,12 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
     const float M = fmaxf(m0, m1);
     const float Ms = (M == -INFINITY) ? 0.f : M;
     const float e0 = fast_exp2((m0 - Ms) * cs), e1 = fast_exp2((m1 - Ms) * cs);
-    a.ws.part_acc[((size_t)tile * G + h) * D + ch] = sm_acc[w0][h][ch & 63] * e0 + sm_acc[w1][h][ch & 63] * e1;
+    store_agent_f(a.ws.part_acc + ((size_t)tile * G + h) * D + ch, sm_acc[w0][h][ch & 63] * e0 + sm_acc[w1][h][ch & 63] * e1);
     if (ch == 0)
-      *reinterpret_cast<float2 *>(a.ws.part_ml + ((size_t)tile * G + h) * 2) =
-          make_float2(M, sm_ml[w0][h][1] * e0 + sm_ml[w1][h][1] * e1);
+    {
+      store_agent_f(a.ws.part_ml + ((size_t)tile * G + h) * 2, M);
+      store_agent_f(a.ws.part_ml + ((size_t)tile * G + h) * 2 + 1, sm_ml[w0][h][1] * e0 + sm_ml[w1][h][1] * e1);
+    }
   }
   if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
