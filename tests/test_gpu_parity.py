@@ -287,15 +287,16 @@ def _unit_state(state, b, j):
     return {k: np.ascontiguousarray(state[k][b:b + 1, j:j + 1]) for k in ("k", "v", "pos", "imp", "len")}
 
 
-@pytest.mark.parametrize("name", ["headkv32k", "llama8b"])
+@pytest.mark.parametrize("name", ["headkv32k", "llama8b", "longctx128k", "longctx128k_full", "twostage"])
 def test_full_size_sampled_units(name):
-    """Full-size workload, the launch configuration the benchmark times: the
-    compression step and two steady steps; sampled units against the oracle,
-    and properties on every unit."""
-    w = W.workload(name, steps=3)
+    """Every workload at full size, in the launch configuration the benchmark
+    times (host length hints): the first step (compression, or a full
+    131073-token attention pass) and two steady steps; sampled units against
+    the oracle, and properties on every unit."""
+    w = W.workload(name.replace("_full", ""), steps=3, full=name.endswith("_full"))
     say(f"[gpu] full-size {name}: generating inputs")
     d = W.generate(w)
-    run = _run(w, d)
+    run = _run(w, d, hint=True)
     G = w.group
     rng = np.random.Generator(np.random.PCG64(5))
     samples = [(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)]
@@ -324,7 +325,8 @@ def test_full_size_sampled_units(name):
             vn = np.ascontiguousarray(d["v_new"][t][b:b + 1, j:j + 1])
             npos = d["new_pos"][t][b:b + 1]
             kw = dict(budget=budget[b:b + 1, j:j + 1], budget_all=0, n_sink=w.n_sink,
-                      n_recent=w.n_recent, stage2_channels=0, stage2_tokens=0, scale=0.0)
+                      n_recent=w.n_recent, stage2_channels=w.stage2_channels,
+                      stage2_tokens=w.stage2_tokens, scale=0.0)
             code, want, dref = ref.decode_step(u_ref, G, q, kn, vn, npos, **kw)
             assert code == 0
             e = row_errors(out[b:b + 1, j * G:(j + 1) * G], want)
