@@ -186,9 +186,10 @@ def main():
         f"{step_bytes / 1e6:.2f} MB/step algorithmic -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     # The dominant kernel, the attention launch: the same steps run once more,
-    # launched eagerly, with a pair of HIP events around every attention
-    # launch, recorded by the library on the stream that launch uses (event
-    # nodes inside a captured graph do not bracket the kernel's execution).
+    # launched eagerly and back to back, with a pair of HIP events around every
+    # attention launch, recorded by the library on the stream that launch uses
+    # (event nodes inside a captured graph do not bracket the kernel's
+    # execution).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for e_a, e_b in evs:  # materialise the events
@@ -196,9 +197,18 @@ def main():
         e_b.record(stream)
     torch.cuda.synchronize()
     base2 = base + args.steps
+    # A GPU-side wait ahead of the replay lets the host enqueue every step
+    # before the first runs, so the launches run back to back as in the graph
+    # (no idle gaps while the host catches up).
+    sleep_cycles = 500_000_000
+    torch.cuda._sleep(sleep_cycles)
+    t_enq = time.perf_counter()
     for i in range(args.steps):
         step((base2 + i) % args.layers, events=evs[i])
+    t_enq = time.perf_counter() - t_enq
     torch.cuda.synchronize()
+    log(f"[bench] timing replay: {args.steps} steps enqueued in {t_enq * 1e3:.1f} ms behind a "
+        f"~{sleep_cycles / 2.4e6:.0f} ms GPU wait (the host blocks once the hardware queue is full)")
     H.check(H.hikv_device_status(ws), "device status after the timing replay")
     attend_ms = sum(e_a.elapsed_time(e_b) for e_a, e_b in evs) / args.steps
     attend_bytes = BM.attend_bytes(B, Hq, Hkv, D, w.el, live_steady)
