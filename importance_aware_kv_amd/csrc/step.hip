@@ -1052,10 +1052,12 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
-  // Grid: x = the unit's workgroup (nib importance blocks, then NOC output
-  // blocks), y = the unit, so that the unit is known without a load.
-  const int nib = (int)gridDim.x - NOC;  // importance blocks per unit
-  const int u = blockIdx.y, r = blockIdx.x;
+  // Grid: x = the unit, y = the unit's workgroup (nib importance blocks, then
+  // NOC output blocks), so that the unit is known without a load and every
+  // unit's importance blocks, which end the step, are dispatched before any
+  // output block.
+  const int nib = (int)gridDim.y - NOC;  // importance blocks per unit
+  const int u = blockIdx.x, r = blockIdx.y;
   // The host plan's words (kernel arguments, clamped to its table) are loaded
   // with the flag that says whether there is one, so that the host plan costs
   // one round trip; the device plan's path uses them too, after its own load,
@@ -1436,7 +1438,7 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   // Second launch: per unit, importance blocks to cover the capacity, then
   // one output block per 64 outputs.
   const int nib = imp_blocks(a.cap);
-  hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)(nib + k2_noc<EL, D, G>()), (unsigned)a.n_units),
+  hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)a.n_units, (unsigned)(nib + k2_noc<EL, D, G>())),
                      dim3(kT2), 0, s, a);
   return hipGetLastError();
 }
