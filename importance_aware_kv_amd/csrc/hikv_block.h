@@ -113,4 +113,67 @@ __device__ void radix_select_smallest(int n_items, int k, F key_of, uint32_t *hi
   }
 }
 
+// The same selection over a contiguous array of keys, UINT64_MAX marking an
+// item that does not take part (a real key equals it only for a NaN
+// importance at position 0).  Each pass streams the array with KPT
+// independent loads per thread in flight.
+template <int NT, int KPT>
+__device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint32_t *hist,
+                                  RadixState *st) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    st->prefix = 0;
+    st->shift = 64;
+    st->krem = k;
+    st->done = 0;
+  }
+  __syncthreads();
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    const uint64_t prefix = st->prefix;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_items; base += NT * KPT) {
+      uint64_t kk[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) kk[j] = keys[min(base + tid + j * NT, n_items - 1)];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const uint64_t key = kk[j];
+        if (base + tid + j * NT < n_items && key != ~0ull &&
+            (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))))
+          atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t krem = (uint32_t)st->krem;
+      const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
+                     h3 = hist[4 * tid + 3];
+      const uint32_t s = h0 + h1 + h2 + h3;
+      const uint32_t incl = wave_incl_scan_u32(s);
+      const uint32_t excl = incl - s;
+      if (excl < krem && incl >= krem) {
+        const uint32_t hh[4] = {h0, h1, h2, h3};
+        uint32_t cum = excl;
+        int d = 3;
+        for (int i = 0; i < 4; ++i) {
+          if (cum + hh[i] >= krem) {
+            d = i;
+            break;
+          }
+          cum += hh[i];
+        }
+        const uint32_t rem = krem - cum;
+        st->prefix = prefix | ((uint64_t)(4 * tid + d) << shift);
+        st->shift = shift;
+        st->krem = (int)rem;
+        st->done = (hh[d] == rem) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (st->done) break;
+  }
+}
+
 }  // namespace hikv

@@ -46,9 +46,11 @@ struct Ws {
   int32_t *urec;        // [n_units][4] per-unit plan of the step: first tile, tiles, tokens
   int32_t *icand;       // [n_units][imp_blocks(cap)][4] per importance block: its lowest
                         //   eviction key (low, high word) and that key's slot
+  uint64_t *bkeys;      // [n_units][cap] bulk eviction: every slot's eviction key
+                        //   (UINT64_MAX for a protected token)
 };
 
-constexpr int kWsParts = 18;
+constexpr int kWsParts = 19;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -79,6 +81,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
       sizeof(int32_t) * B * Hq,        // tcount
       sizeof(int32_t) * 4 * U,         // urec
       sizeof(int32_t) * 4 * U * (size_t)imp_blocks(cap),  // icand
+      sizeof(uint64_t) * U * cap,      // bkeys
   };
   WsSizes w;
   size_t o = 0;
@@ -111,6 +114,7 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.tcount = reinterpret_cast<int32_t *>(b + s.off[15]);
   w.urec = reinterpret_cast<int32_t *>(b + s.off[16]);
   w.icand = reinterpret_cast<int32_t *>(b + s.off[17]);
+  w.bkeys = reinterpret_cast<uint64_t *>(b + s.off[18]);
   return w;
 }
 
