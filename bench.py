@@ -140,9 +140,11 @@ def main():
         host_len[li] = np.minimum(host_len[li] + 1, budget).astype(np.int32)
 
     stream = torch.cuda.current_stream()
-    # Compression step of every layer copy (32769 tokens -> budget).
+    # Compression step of every layer copy (32769 tokens -> budget), queued
+    # behind a GPU-side wait so that the steps run back to back.
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(100_000_000)
     e0.record(stream)
     for li in range(args.layers):
         step(li)
