@@ -116,11 +116,16 @@ __device__ void radix_select_smallest(int n_items, int k, F key_of, uint32_t *hi
 // The same selection over a contiguous array of keys, UINT64_MAX marking an
 // item that does not take part (a real key equals it only for a NaN
 // importance at position 0).  Each pass streams the array with KPT
-// independent loads per thread in flight.
+// independent loads per thread in flight.  Every wave counts into a
+// histogram of its own (whist: NT / 64 x 256 words): the digits of one pass
+// are often nearly all equal, and a shared histogram would serialise the
+// whole block on one or two bins.
 template <int NT, int KPT>
 __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint32_t *hist,
-                                  RadixState *st) {
+                                  uint32_t *whist, RadixState *st) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
+  uint32_t *mine = whist + (tid >> 6) * 256;
   if (tid == 0) {
     st->prefix = 0;
     st->shift = 64;
@@ -131,7 +136,7 @@ __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
     const uint64_t prefix = st->prefix;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    for (int i = tid; i < NW * 256; i += NT) whist[i] = 0;
     __syncthreads();
     for (int base = 0; base < n_items; base += NT * KPT) {
       uint64_t kk[KPT];
@@ -140,10 +145,24 @@ __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const uint64_t key = kk[j];
-        if (base + tid + j * NT < n_items && key != ~0ull &&
-            (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))))
-          atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        const bool in = base + tid + j * NT < n_items && key != ~0ull &&
+                        (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)));
+        const int d = in ? (int)((key >> shift) & 255u) : 256;
+        // The lanes that share the first lane's digit are counted at once.
+        const int d0 = __builtin_amdgcn_readfirstlane(d);
+        const uint64_t same = __ballot(d == d0);
+        if (d == d0) {
+          if (d0 < 256 && (tid & 63) == __builtin_ctzll(same)) atomicAdd(&mine[d0], (uint32_t)__popcll(same));
+        } else if (d < 256) {
+          atomicAdd(&mine[d], 1u);
+        }
       }
+    }
+    __syncthreads();
+    for (int i = tid; i < 256; i += NT) {
+      uint32_t c = 0;
+      for (int w = 0; w < NW; ++w) c += whist[w * 256 + i];
+      hist[i] = c;
     }
     __syncthreads();
     if (tid < 64) {

@@ -1301,9 +1301,10 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       }
       __syncthreads();  // every key is stored
       __shared__ uint32_t hist[256];
+      __shared__ uint32_t whist[kNW2 * 256];
       __shared__ int sc[kT2];
       __shared__ RadixState rs;
-      radix_select_keys<kT2, 8>(bkeys, L, n_evict, hist, &rs);
+      radix_select_keys<kT2, 8>(bkeys, L, n_evict, hist, whist, &rs);
       const uint64_t lim = rs.prefix >> rs.shift;
       const int shift = rs.shift;
       // Slots [n0, n1) of this thread, contiguous; their evicted flags stay in
