@@ -548,67 +548,36 @@ __global__ __launch_bounds__(kBulkThreads) void k_bulk_evict(StepArgs a, const i
   const int32_t *pos = a.pos + (size_t)u * a.cap;
   const int k_evict = L - beta;
 
-  __shared__ uint32_t hist[256];
-  __shared__ int sc[kBulkThreads];
-  __shared__ RadixState rs;
-  auto cand_key = [&](int n, uint64_t &key) -> bool {
-    const int pn = pos[n];
-    if ((pn < S) || (pn > newest - Wp)) return false;
-    key = evict_key(imp[n], pn);
-    return true;
-  };
-  radix_select_smallest<kBulkThreads>(L, k_evict, cand_key, hist, &rs);
-  const uint64_t prefix = rs.prefix;
-  const int shift = rs.shift;
-
-  // Flags: evicted = unprotected and key at or below the boundary prefix.
-  auto evicted = [&](int n) -> bool {
-    const int pn = pos[n];
-    if ((pn < S) || (pn > newest - Wp)) return false;
-    return (evict_key(imp[n], pn) >> shift) <= (prefix >> shift);
-  };
-  // Holes in [0, beta) and movers in [beta, L), in slot order.
-  const int per = (L + kBulkThreads - 1) / kBulkThreads;
-  const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
-  int nh = 0, nm = 0;
-  for (int n = n0; n < n1; ++n) {
-    const bool e = evicted(n);
-    if (n < beta && e) ++nh;
-    if (n >= beta && !e) ++nm;
-  }
-  int tot_h, tot_m;
-  int oh = block_excl_scan<kBulkThreads>(nh, sc, &tot_h);
-  int om = block_excl_scan<kBulkThreads>(nm, sc, &tot_m);
-  int32_t *holes = a.ws.holes + (size_t)u * a.cap;
-  int32_t *movers = a.ws.movers + (size_t)u * a.cap;
-  for (int n = n0; n < n1; ++n) {
-    const bool e = evicted(n);
-    if (n < beta && e) holes[oh++] = n;
-    if (n >= beta && !e) movers[om++] = n;
+  // Every slot's eviction key (UINT64_MAX for a protected token), then the
+  // selection and compaction.
+  uint64_t *keys = a.ws.bkeys + (size_t)u * a.cap;
+  constexpr int KB = 8;
+  for (int base = 0; base < L; base += kBulkThreads * KB) {
+    int pk[KB];
+    float ik[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int n = min(base + tid + j * kBulkThreads, L - 1);
+      pk[j] = pos[n];
+      ik[j] = imp[n];
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int n = base + tid + j * kBulkThreads;
+      if (n < L) keys[n] = ((pk[j] < S) || (pk[j] > newest - Wp)) ? ~0ull : evict_key(ik[j], pk[j]);
+    }
   }
   __syncthreads();
-  if (tot_h != tot_m) {  // cannot happen for distinct positions; fail safe
-    if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
-    return;
-  }
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t whist[kBulkThreads / 64 * 256];
+  __shared__ int sc[kBulkThreads];
+  __shared__ RadixState rs;
   constexpr int RB = D * EL;
-  constexpr int CPR = RB / 16;  // 16-byte chunks per row
-  char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
-  char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
-  for (int idx = tid; idx < tot_m * CPR; idx += kBulkThreads) {
-    const int i = idx / CPR, cidx = idx - i * CPR;
-    const int src = movers[i], dst = holes[i];
-    reinterpret_cast<uint4 *>(kw + (size_t)dst * RB)[cidx] = reinterpret_cast<const uint4 *>(kw + (size_t)src * RB)[cidx];
-    reinterpret_cast<uint4 *>(vw + (size_t)dst * RB)[cidx] = reinterpret_cast<const uint4 *>(vw + (size_t)src * RB)[cidx];
-  }
-  float *impw = a.imp + (size_t)u * a.cap;
-  int32_t *posw = a.pos + (size_t)u * a.cap;
-  for (int i = tid; i < tot_m; i += kBulkThreads) {
-    const int src = movers[i], dst = holes[i];
-    posw[dst] = posw[src];
-    impw[dst] = impw[src];
-  }
-  if (tid == 0) a.len[u] = beta;
+  bulk_compact<kBulkThreads, RB>(keys, L, beta, k_evict, static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB,
+                                 static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB,
+                                 a.pos + (size_t)u * a.cap, a.imp + (size_t)u * a.cap,
+                                 a.ws.holes + (size_t)u * a.cap, a.ws.movers + (size_t)u * a.cap, a.len + u,
+                                 a.ws.status, hist, whist, sc, &rs);
 }
 
 // ---------------------------------------------------------------------------

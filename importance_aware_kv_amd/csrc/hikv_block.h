@@ -195,4 +195,87 @@ __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint
   }
 }
 
+// Bulk eviction of one unit by one workgroup of NT threads, from the
+// eviction keys of its L slots (keys[n]; UINT64_MAX for a protected token):
+// the n_evict smallest keys are evicted, then the survivors at or above the
+// budget move into the evicted slots below it (K and V rows of RB bytes,
+// position, importance), and *len_u = beta.  holes and movers are the unit's
+// [cap] lists in the workspace.  Every thread of the workgroup calls it.
+template <int NT, int RB>
+__device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int beta, int n_evict, char *kw, char *vw,
+                             int32_t *posw, float *impw, int32_t *holes, int32_t *movers,
+                             int32_t *len_u, int32_t *status, uint32_t *hist, uint32_t *whist, int *sc,
+                             RadixState *rs) {
+  const int tid = threadIdx.x;
+  radix_select_keys<NT, 8>(keys, L, n_evict, hist, whist, rs);
+  const uint64_t lim = rs->prefix >> rs->shift;
+  const int shift = rs->shift;
+  // Slots [n0, n1) of this thread, contiguous; their evicted flags stay in a
+  // mask between the counting and the listing pass (up to 64 slots per
+  // thread; beyond that the keys are read again).
+  const int per = (L + NT - 1) / NT;
+  const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
+  uint64_t emask = 0;
+  int nh = 0, nm = 0;
+  for (int g0 = n0; g0 < n1; g0 += 8) {
+    uint64_t kk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kk[j] = keys[min(g0 + j, n1 - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = g0 + j;
+      const bool e = n < n1 && kk[j] != ~0ull && (kk[j] >> shift) <= lim;
+      if (e && n - n0 < 64) emask |= 1ull << (n - n0);
+      nh += (n < n1 && n < beta && e);
+      nm += (n < n1 && n >= beta && !e);
+    }
+  }
+  int tot_h, tot_m;
+  int oh = block_excl_scan<NT>(nh, sc, &tot_h);
+  int om = block_excl_scan<NT>(nm, sc, &tot_m);
+  for (int n = n0; n < n1; ++n) {
+    bool e;
+    if (n - n0 < 64) {
+      e = (emask >> (n - n0)) & 1;
+    } else {
+      const uint64_t key = keys[n];
+      e = key != ~0ull && (key >> shift) <= lim;
+    }
+    if (n < beta && e) holes[oh++] = n;
+    if (n >= beta && !e) movers[om++] = n;
+  }
+  __syncthreads();
+  if (tot_h != tot_m) {  // cannot happen for distinct positions; fail safe
+    if (tid == 0) set_status(status, HIKV_EINVAL);
+    return;
+  }
+  // A round copies two groups of NT / CPR rows, CPR threads per row, with
+  // every load of the round issued before its stores (hole and mover rows are
+  // distinct, so nothing a round stores is loaded in it).
+  constexpr int CPR = RB / 16, RPG = NT / CPR;
+  const int ci = tid % CPR, rr = tid / CPR;
+  for (int i0 = 0; i0 < tot_m; i0 += 2 * RPG) {
+    const int ia = i0 + rr, ib = i0 + RPG + rr;
+    const int ja = min(ia, tot_m - 1), jb = min(ib, tot_m - 1);
+    const int sa = movers[ja], da = holes[ja], sb = movers[jb], db = holes[jb];
+    const uint4 ka = reinterpret_cast<const uint4 *>(kw + (size_t)sa * RB)[ci];
+    const uint4 va = reinterpret_cast<const uint4 *>(vw + (size_t)sa * RB)[ci];
+    const uint4 kb = reinterpret_cast<const uint4 *>(kw + (size_t)sb * RB)[ci];
+    const uint4 vb = reinterpret_cast<const uint4 *>(vw + (size_t)sb * RB)[ci];
+    const int pa = posw[sa], pb = posw[sb];
+    const float xa = impw[sa], xb = impw[sb];
+    if (ia < tot_m) {
+      reinterpret_cast<uint4 *>(kw + (size_t)da * RB)[ci] = ka;
+      reinterpret_cast<uint4 *>(vw + (size_t)da * RB)[ci] = va;
+      if (ci == 0) posw[da] = pa, impw[da] = xa;
+    }
+    if (ib < tot_m) {
+      reinterpret_cast<uint4 *>(kw + (size_t)db * RB)[ci] = kb;
+      reinterpret_cast<uint4 *>(vw + (size_t)db * RB)[ci] = vb;
+      if (ci == 0) posw[db] = pb, impw[db] = xb;
+    }
+  }
+  if (tid == 0) *len_u = beta;
+}
+
 }  // namespace hikv

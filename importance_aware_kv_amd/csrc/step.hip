@@ -1304,78 +1304,8 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       __shared__ uint32_t whist[kNW2 * 256];
       __shared__ int sc[kT2];
       __shared__ RadixState rs;
-      radix_select_keys<kT2, 8>(bkeys, L, n_evict, hist, whist, &rs);
-      const uint64_t lim = rs.prefix >> rs.shift;
-      const int shift = rs.shift;
-      // Slots [n0, n1) of this thread, contiguous; their evicted flags stay in
-      // a mask between the counting and the listing pass (up to 64 slots per
-      // thread; beyond that the keys are read again).
-      const int per = (L + kT2 - 1) / kT2;
-      const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
-      uint64_t emask = 0;
-      int nh = 0, nm = 0;
-      for (int g0 = n0; g0 < n1; g0 += 8) {
-        uint64_t kk[8];
-    #pragma unroll
-        for (int j = 0; j < 8; ++j) kk[j] = bkeys[min(g0 + j, n1 - 1)];
-    #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int n = g0 + j;
-          const bool e = n < n1 && kk[j] != ~0ull && (kk[j] >> shift) <= lim;
-          if (e && n - n0 < 64) emask |= 1ull << (n - n0);
-          nh += (n < n1 && n < beta && e);
-          nm += (n < n1 && n >= beta && !e);
-        }
-      }
-      int tot_h, tot_m;
-      int oh = block_excl_scan<kT2>(nh, sc, &tot_h);
-      int om = block_excl_scan<kT2>(nm, sc, &tot_m);
-      int32_t *holes = a.ws.holes + (size_t)u * a.cap;
-      int32_t *movers = a.ws.movers + (size_t)u * a.cap;
-      for (int n = n0; n < n1; ++n) {
-        bool e;
-        if (n - n0 < 64) {
-          e = (emask >> (n - n0)) & 1;
-        } else {
-          const uint64_t key = bkeys[n];
-          e = key != ~0ull && (key >> shift) <= lim;
-        }
-        if (n < beta && e) holes[oh++] = n;
-        if (n >= beta && !e) movers[om++] = n;
-      }
-      __syncthreads();
-      if (tot_h == tot_m) {
-        // Survivors at or above the budget move into the evicted slots below
-        // it.  A round copies two groups of kT2 / CPR rows, CPR threads per
-        // row, with every load of the round issued before its stores (hole and
-        // mover rows are distinct, so nothing a round stores is loaded in it).
-        constexpr int CPR = RB / 16, RPG = kT2 / CPR;
-        const int ci = tid % CPR, rr = tid / CPR;
-        for (int i0 = 0; i0 < tot_m; i0 += 2 * RPG) {
-          const int ia = i0 + rr, ib = i0 + RPG + rr;
-          const int ja = min(ia, tot_m - 1), jb = min(ib, tot_m - 1);
-          const int sa = movers[ja], da = holes[ja], sb = movers[jb], db = holes[jb];
-          const uint4 ka = reinterpret_cast<const uint4 *>(kw + (size_t)sa * RB)[ci];
-          const uint4 va = reinterpret_cast<const uint4 *>(vw + (size_t)sa * RB)[ci];
-          const uint4 kb = reinterpret_cast<const uint4 *>(kw + (size_t)sb * RB)[ci];
-          const uint4 vb = reinterpret_cast<const uint4 *>(vw + (size_t)sb * RB)[ci];
-          const int pa = posw[sa], pb = posw[sb];
-          const float xa = impw[sa], xb = impw[sb];
-          if (ia < tot_m) {
-            reinterpret_cast<uint4 *>(kw + (size_t)da * RB)[ci] = ka;
-            reinterpret_cast<uint4 *>(vw + (size_t)da * RB)[ci] = va;
-            if (ci == 0) posw[da] = pa, impw[da] = xa;
-          }
-          if (ib < tot_m) {
-            reinterpret_cast<uint4 *>(kw + (size_t)db * RB)[ci] = kb;
-            reinterpret_cast<uint4 *>(vw + (size_t)db * RB)[ci] = vb;
-            if (ci == 0) posw[db] = pb, impw[db] = xb;
-          }
-        }
-        if (tid == 0) a.len[u] = beta;
-      } else if (tid == 0) {
-        set_status(a.ws.status, HIKV_EINVAL);
-      }
+      bulk_compact<kT2, RB>(bkeys, L, beta, n_evict, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
+                            a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs);
     }();
     end_wave();
   }
