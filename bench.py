@@ -86,11 +86,15 @@ def main():
     dev_name = torch.cuda.get_device_name(0)
 
     n_inputs = 256
-    w = W.workload(args.workload, steps=n_inputs)
+    full = args.workload.endswith("_full")
+    w = W.workload(args.workload[:-5] if full else args.workload, steps=n_inputs, full=full)
     # compression step + warm-up + the timed steps + the same number again for
     # the per-kernel timing replay
     per_layer_steps = 1 + (args.warmup + 2 * args.steps + args.layers - 1) // args.layers
     w.capacity = w.ctx + per_layer_steps + 1
+    if full:  # full attention: the budget is the whole capacity, nothing is ever evicted
+        w.budget_all = w.capacity
+    stage2 = w.stage2_channels > 0
     t0 = time.time()
     d = W.generate(w)
     log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f}s on {dev_name}")
@@ -122,10 +126,14 @@ def main():
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
     layer_step = [0] * args.layers
 
+    live_log = []  # tokens attended per step (sum over units), in launch order
+
     def step(li, events=None):
         c = layers[li]
         n = layer_step[li]
         layer_step[li] += 1
+        live_log.append(int((host_len[li] + 1).sum()))
+        moves_log.append(int((host_len[li] + 1 > budget).sum()))
         p = pol
         if not args.no_hint:
             p = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
@@ -139,6 +147,7 @@ def main():
             raise RuntimeError(f"hikv_decode_step: {H.status_string(code)}")
         host_len[li] = np.minimum(host_len[li] + 1, budget).astype(np.int32)
 
+    moves_log = []
     stream = torch.cuda.current_stream()
     # Compression step of every layer copy (32769 tokens -> budget), queued
     # behind a GPU-side wait so that the steps run back to back.
@@ -156,7 +165,7 @@ def main():
     assert np.array_equal(layers[0].len.cpu().numpy(), live_after), "compression did not reach the budgets"
     comp_bytes = BM.decode_step_bytes(B, Hq, Hkv, D, w.el, np.full((B, Hkv), w.ctx + 1),
                                       int(np.minimum(budget, w.ctx + 1).sum()))
-    log(f"[bench] compression step: {comp_ms * 1e3:.1f} us/layer "
+    log(f"[bench] {'first' if full else 'compression'} step: {comp_ms * 1e3:.1f} us/layer "
         f"({comp_bytes / comp_ms / 1e6:.0f} GB/s algorithmic)")
 
     # Warm-up steady steps, eager.
@@ -167,6 +176,7 @@ def main():
 
     # Timed steady steps: one HIP graph, replayed once.
     base = args.warmup
+    mark = len(live_log)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(args.steps):
@@ -181,8 +191,12 @@ def main():
     H.check(H.hikv_device_status(ws), "device status after timed steps")
     ms_step = ms_total / args.steps
     steps_per_s = 1e3 / ms_step
-    live_steady = budget + 1
-    step_bytes = BM.decode_step_bytes(B, Hq, Hkv, D, w.el, live_steady, B * Hkv)
+    # bytes of the average timed step (every step is alike in the budgeted steady
+    # state; a full-attention step attends one token more than the one before)
+    live_avg = sum(live_log[mark:]) / args.steps
+    moves_avg = sum(moves_log[mark:]) / args.steps
+    step_bytes = int(BM.decode_step_bytes(B, Hq, Hkv, D, w.el, [0], 0) + live_avg * (2 * D * w.el + 12)
+                     + moves_avg * 2 * (2 * D * w.el + 8))
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"[bench] steady step: {ms_step * 1e3:.2f} us, {steps_per_s:.0f} steps/s, "
         f"{step_bytes / 1e6:.2f} MB/step algorithmic -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
@@ -213,7 +227,11 @@ def main():
         f"~{sleep_cycles / 2.4e6:.0f} ms GPU wait (the host blocks once the hardware queue is full)")
     H.check(H.hikv_device_status(ws), "device status after the timing replay")
     attend_ms = sum(e_a.elapsed_time(e_b) for e_a, e_b in evs) / args.steps
-    attend_bytes = BM.attend_bytes(B, Hq, Hkv, D, w.el, live_steady)
+    live_rep = sum(live_log[-args.steps:]) / args.steps
+    if stage2:  # the reduced-channel logits pass reads every live K row whole, and q
+        attend_bytes = int(live_rep * D * w.el + B * Hq * D * w.el)
+    else:
+        attend_bytes = int(BM.attend_bytes(B, Hq, Hkv, D, w.el, [0]) + live_rep * 2 * D * w.el)
     attend_gbs = attend_bytes / (attend_ms * 1e-3) / 1e9
     log(f"[bench] attention launch: {attend_ms * 1e3:.2f} us, {attend_bytes / 1e6:.2f} MB algorithmic -> "
         f"{attend_gbs:.0f} GB/s ({attend_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
@@ -243,11 +261,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.el == 2 else "f32",
         "data": "synthetic",
         "config": {
-            "workload": "headkv32k steady state: batch 4, 32 q / 8 KV heads, D 128, bf16 KV, "
-                        "32768-token prefill, per-KV-head budgets " + ",".join(map(str, budget[0])),
+            "workload": workload_text(w, budget, full),
             "global_batch": B,
             "seq_len": w.ctx,
             "layers_cycled": args.layers,
@@ -259,18 +276,42 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(attend_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "kernel": "k_attend_mfma<4> (split-K attention over the live K/V rows on matrix cores; "
-                      "HIP events per launch)",
+            "traffic": measured_traffic() if args.workload == "headkv32k" else None,
+            "kernel": kernel_text(w),
             "bytes_per_launch": attend_bytes,
             "us_per_launch": round(attend_ms * 1e3, 3),
             "whole_step": {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                            "bytes_per_step": step_bytes},
         },
-        "compression_step_us": round(comp_ms * 1e3, 2),
+        ("first_step_us" if full else "compression_step_us"): round(comp_ms * 1e3, 2),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def workload_text(w, budget, full):
+    heads = f"{w.n_q_heads} q / {w.n_kv_heads} KV heads"
+    dt = "bf16" if w.el == 2 else "fp32"
+    if full:
+        pol = "budget = capacity (full attention, no eviction)"
+    elif w.budgets is not None:
+        pol = "per-KV-head budgets " + ",".join(map(str, budget[0]))
+    else:
+        pol = f"budget {w.budget_all}"
+    s2 = f", Stage II r = {w.stage2_channels}, k_T = {w.stage2_tokens}" if w.stage2_channels else ""
+    return (f"{w.name} {'decode' if full else 'steady state'}: batch {w.batch}, {heads}, D {w.head_dim}, "
+            f"{dt} KV, {w.ctx}-token prefill, {pol}, sinks {w.n_sink}, recent {w.n_recent}{s2}")
+
+
+def kernel_text(w):
+    if w.stage2_channels:
+        return (f"k_attn_tiles<2,{w.head_dim},{w.group},false,true> (Stage II reduced-channel logits over "
+                "every live K row; HIP events per launch)")
+    if w.el == 2 and w.head_dim == 128:
+        return (f"k_attend_mfma<{w.group}> (split-K attention over the live K/V rows on matrix cores; "
+                "HIP events per launch)")
+    return (f"k_attend<{w.el},{w.head_dim},{w.group}> (split-K attention over the live K/V rows; "
+            "HIP events per launch)")
 
 
 def cpu_baseline(w, d, seconds):
@@ -281,7 +322,8 @@ def cpu_baseline(w, d, seconds):
     from oracle import ref
     st = ref.copy_state(d)
     budget = w.budget_array()
-    kw = dict(budget=budget, n_sink=w.n_sink, n_recent=w.n_recent, debug=False)
+    kw = dict(budget=budget, n_sink=w.n_sink, n_recent=w.n_recent, debug=False,
+              stage2_channels=w.stage2_channels, stage2_tokens=w.stage2_tokens)
     ref.decode_step(st, w.n_q_heads, d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], **kw)
     n = 0
     t0 = time.perf_counter()

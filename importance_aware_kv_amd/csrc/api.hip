@@ -139,22 +139,22 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int dt = shape->kv_dtype;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (debug && debug->attend_start && debug->attend_stop) {
+    ev0 = static_cast<hipEvent_t>(debug->attend_start);
+    ev1 = static_cast<hipEvent_t>(debug->attend_stop);
+  }
   hipError_t e;
   if (a.r == 0) {
     if (!multi_kernel_path()) {
       if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
-      hipEvent_t ev0 = nullptr, ev1 = nullptr;
-      if (debug && debug->attend_start && debug->attend_stop) {
-        ev0 = static_cast<hipEvent_t>(debug->attend_start);
-        ev1 = static_cast<hipEvent_t>(debug->attend_stop);
-      }
       return dev_err(launch_step(a, dt, s, ev0, ev1));
     }
-    if ((e = launch_attn_tiles(a, dt, true, false, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_attn_tiles(a, dt, true, false, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
   } else {
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
-    if ((e = launch_attn_tiles(a, dt, false, true, s)) != hipSuccess) return dev_err(e);
+    if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);

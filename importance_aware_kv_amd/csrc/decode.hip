@@ -25,6 +25,8 @@
 // max/rescale rule.  Logits are kept in the log2 domain (scale * log2 e) so
 // every exponential is a single v_exp_f32.
 
+#include <hip/hip_ext.h>
+
 #include "hikv_block.h"
 #include "hikv_launch.h"
 
@@ -584,14 +586,20 @@ __global__ __launch_bounds__(kBulkThreads) void k_bulk_evict(StepArgs a, const i
 // Launchers.
 // ---------------------------------------------------------------------------
 template <int EL, int D>
-static hipError_t attn_dispatch_g(const StepArgs &a, bool with_v, bool masked, hipStream_t s) {
+static hipError_t attn_dispatch_g(const StepArgs &a, bool with_v, bool masked, hipStream_t s,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid(max_tiles_for(a.n_units)), block(256);
-#define HIKV_ATTN(GG)                                                                    \
-  case GG:                                                                               \
-    if (with_v && !masked) hipLaunchKernelGGL((k_attn_tiles<EL, D, GG, true, false>), grid, block, 0, s, a); \
-    else if (!with_v && masked) hipLaunchKernelGGL((k_attn_tiles<EL, D, GG, false, true>), grid, block, 0, s, a); \
-    else if (!with_v && !masked) hipLaunchKernelGGL((k_attn_tiles<EL, D, GG, false, false>), grid, block, 0, s, a); \
-    else hipLaunchKernelGGL((k_attn_tiles<EL, D, GG, true, true>), grid, block, 0, s, a); \
+  // With events, the dispatch itself records them around the kernel's execution.
+  auto go = [&](void (*kern)(StepArgs)) {
+    if (ev0 && ev1) hipExtLaunchKernelGGL(kern, grid, block, 0, s, ev0, ev1, 0, a);
+    else hipLaunchKernelGGL(kern, grid, block, 0, s, a);
+  };
+#define HIKV_ATTN(GG)                                                 \
+  case GG:                                                            \
+    if (with_v && !masked) go(k_attn_tiles<EL, D, GG, true, false>);  \
+    else if (!with_v && masked) go(k_attn_tiles<EL, D, GG, false, true>); \
+    else if (!with_v && !masked) go(k_attn_tiles<EL, D, GG, false, false>); \
+    else go(k_attn_tiles<EL, D, GG, true, true>);                     \
     break;
   switch (a.G) {
     HIKV_ATTN(1)
@@ -604,13 +612,14 @@ static hipError_t attn_dispatch_g(const StepArgs &a, bool with_v, bool masked, h
   return hipGetLastError();
 }
 
-hipError_t launch_attn_tiles(const StepArgs &a, int dtype, bool with_v, bool masked, hipStream_t s) {
+hipError_t launch_attn_tiles(const StepArgs &a, int dtype, bool with_v, bool masked, hipStream_t s,
+                             hipEvent_t ev0, hipEvent_t ev1) {
   if (dtype == HIKV_BF16) {
-    if (a.D == 128) return attn_dispatch_g<2, 128>(a, with_v, masked, s);
-    if (a.D == 64) return attn_dispatch_g<2, 64>(a, with_v, masked, s);
+    if (a.D == 128) return attn_dispatch_g<2, 128>(a, with_v, masked, s, ev0, ev1);
+    if (a.D == 64) return attn_dispatch_g<2, 64>(a, with_v, masked, s, ev0, ev1);
   } else {
-    if (a.D == 128) return attn_dispatch_g<4, 128>(a, with_v, masked, s);
-    if (a.D == 64) return attn_dispatch_g<4, 64>(a, with_v, masked, s);
+    if (a.D == 128) return attn_dispatch_g<4, 128>(a, with_v, masked, s, ev0, ev1);
+    if (a.D == 64) return attn_dispatch_g<4, 64>(a, with_v, masked, s, ev0, ev1);
   }
   return hipErrorInvalidValue;
 }

@@ -7,9 +7,9 @@ namespace hikv {
 
 // Split-K decode attention over the live slots of every unit (append
 // included).  with_v=false: logits + softmax statistics only (Stage II's
-// reduced-channel pass).
+// reduced-channel pass).  ev0/ev1 (may be null): events recorded around it.
 hipError_t launch_attn_tiles(const StepArgs &a, int dtype, bool with_v, bool masked,
-                             hipStream_t s);
+                             hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Per (unit, q-head): merge tile partials; write out (when with_v) and stats.
 hipError_t launch_combine(const StepArgs &a, bool with_v, hipStream_t s);
 // Per tile: importance += probabilities; steady-state single eviction.

@@ -237,6 +237,27 @@ __device__ __forceinline__ void stage_sub(char *kb, char *vb, const char *kc, co
   }
 }
 
+// The same staging done by LW of the workgroup's waves only (wave index wl
+// among them): each issues 8 / LW loads for K and as many for V per sub-chunk.
+template <int LW>
+__device__ __forceinline__ void stage_sub_by(char *kb, char *vb, const char *kc, const char *vc,
+                                             const char *kn, const char *vn, int c0, int nrows,
+                                             int t0, int Lold, int wl, int lane) {
+  constexpr int RB = 256;
+#pragma unroll
+  for (int i = 0; i < 8 / LW; ++i) {
+    const int piece = i * LW + wl;  // 1 KB piece of the 8 KB sub-chunk: four 256-byte rows
+    const int off = (piece << 10) + (lane << 4);
+    const int row = off / RB;
+    const int col = (((off - row * RB) >> 4) ^ (row & 15)) << 4;
+    const int n = (row < nrows) ? c0 + row : t0;  // t0 is always a live row of the tile
+    const char *ks = (n == Lold) ? kn + col : kc + (size_t)n * RB + col;
+    const char *vs = (n == Lold) ? vn + col : vc + (size_t)n * RB + col;
+    __builtin_amdgcn_global_load_lds(ks, kb + (piece << 10), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vs, vb + (piece << 10), 16, 0, 0);
+  }
+}
+
 // LDS reads of rows that arrived by DMA.  Written as one asm block so that the
 // compiler, which cannot tell the three sub-chunk buffers apart, does not
 // insert a vmcnt(0) before them (the explicit vmcnt chain already covers the
@@ -757,21 +778,32 @@ __device__ __forceinline__ void mfma_operands(uint64_t (&o)[12], const uint32_t 
       : "memory");
 }
 
+// Wait until the sub-chunk being consumed has landed: at most k * STEP loads
+// (those of the k sub-chunks issued after it, 0 <= k <= K) may be outstanding.
+template <int STEP, int K>
+__device__ __forceinline__ void vm_wait_ahead(int k) {
+  if constexpr (K == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (k >= K) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * STEP) : "memory");
+    else vm_wait_ahead<STEP, K - 1>(k);
+  }
+}
+
 __device__ __forceinline__ f32x4_t mfma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-template <int G>
+template <int G, int NSUB>
 __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
-  constexpr int EL = 2, D = 128, RB = D * EL, SUBB = 8192, NSUB = 3, TS = SUBB / RB, TC = TS * NSUB,
-                NI = SUBB / 4096;
+  constexpr int EL = 2, D = 128, RB = D * EL, SUBB = 8192, TS = SUBB / RB, NI = SUBB / 4096;
   constexpr int QB = G * D * EL;
   static_assert(TS == 32 && G <= 8, "two 16-token groups per sub-chunk; at most 8 heads per group");
   __shared__ __attribute__((aligned(16))) char smem[NSUB * 2 * SUBB];
   __shared__ __attribute__((aligned(16))) char qs[QB];
-  __shared__ __attribute__((aligned(16))) float lgs[TC * G];  // the chunk's logits
+  __shared__ __attribute__((aligned(16))) float lgs[2 * 16 * G];  // logits of a sub-chunk, per token group
   __shared__ float sm_ml[4][G][2];
-  float(*sm_acc)[G][64] = reinterpret_cast<float(*)[G][64]>(smem);  // reused after the chunks
+  float(*sm_acc)[G][64] = reinterpret_cast<float(*)[G][64]>(smem);  // reused after the loop
   static_assert(4 * G * 64 * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -799,6 +831,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
   const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
   float *lg = a.ws.logits + (size_t)u * a.cap * G;
+  // The plan's loads are all consumed by now.  A wait the compiler can see
+  // (vmcnt(0) only) tells it so; otherwise it waits for them, and with them
+  // for every DMA issued below, at the first reuse of their registers.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   {
     const int off = wave * 1024 + lane * 16;
     const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
@@ -823,115 +859,148 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   for (int t = 0; t < 4; ++t) O[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;  // head hl: running maximum (raw q.k) and this lane's partial sum
   bf16x4_t qb[8];
-  for (int cbase = t0; cbase < t1; cbase += TC) {
-    if (cbase != t0) lds_barrier();  // every wave is done with the previous chunk
+  // The tile streams through a ring of NSUB sub-chunk buffers: the first NSUB
+  // are issued up front, and each buffer is refilled as soon as every wave is
+  // done with it, so that loads stay in flight while earlier sub-chunks are
+  // computed.  Waves 2 and 3 issue every K/V load and waves 0 and 1 every
+  // logit store: loads and stores share one completion counter, so a wave
+  // that waited for its loads with stores in flight would wait for the
+  // stores too, and the ring would stall on every store's round trip.
+  const bool loader = wave >= 2;
+  const int nsc = (t1 - t0 + TS - 1) / TS;
+  if (loader) {
 #pragma unroll
     for (int sc = 0; sc < NSUB; ++sc) {
-      const int c0 = cbase + sc * TS;
-      stage_sub<RB, NI, true>(smem + sc * 2 * SUBB, smem + sc * 2 * SUBB + SUBB, kc, vc, kn, vn, c0,
-                              max(0, min(TS, t1 - c0)), t0, Lold, wave, lane);
-    }
-#pragma unroll
-    for (int sc = 0; sc < NSUB; ++sc) {
-      const int c0 = cbase + sc * TS;
-      if (sc == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 1)) : "memory");
-      else if (sc == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 2)) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      dma_barrier();
-      if (sc == 0) {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          uint2 w = make_uint2(0, 0);
-          if (hl < G) w = *reinterpret_cast<const uint2 *>(qs + (hl * D + 16 * ks + 4 * qd) * EL);
-          qb[ks] = __builtin_bit_cast(bf16x4_t, w);
-        }
+      if (sc < nsc) {
+        const int c0 = t0 + sc * TS;
+        stage_sub_by<2>(smem + sc * 2 * SUBB, smem + sc * 2 * SUBB + SUBB, kc, vc, kn, vn, c0,
+                        min(TS, t1 - c0), t0, Lold, wave - 2, lane);
       }
-      uint64_t rd[12];
-      if (sc == 0) mfma_operands<0, SUBB>(rd, ad);
-      else if (sc == 1) mfma_operands<2 * SUBB, 3 * SUBB>(rd, ad);
+    }
+  }
+  float *lgw = lgs + (wave & 1) * 16 * G;  // the wave's logit rows (token-group waves of half 0)
+  const uint32_t lgw_a = lds_addr(lgw);
+  for (int i = 0; i < nsc; ++i) {
+    const int c0 = t0 + i * TS, bsel = i % NSUB;
+    // Sub-chunk i has landed once at most the loads issued after it are
+    // outstanding (loads complete in order; stores in between can only make
+    // the wait longer).  Issued before this wait: the first min(nsc, NSUB),
+    // and one refill per earlier iteration but the first.
+    if (loader) {
+      const int ahead = min(nsc, NSUB + max(0, i - 1)) - (i + 1);
+      vm_wait_ahead<4 * NI, NSUB - 1>(ahead);
+    } else if (i == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // q (no store issued yet)
+    }
+    dma_barrier();  // every wave's rows of sub-chunk i are in; every wave is done with i - 1
+    if (loader && i >= 1 && i + NSUB - 1 < nsc) {
+      const int cr = t0 + (i + NSUB - 1) * TS, br = (i - 1) % NSUB;
+      stage_sub_by<2>(smem + br * 2 * SUBB, smem + br * 2 * SUBB + SUBB, kc, vc, kn, vn, cr,
+                      min(TS, t1 - cr), t0, Lold, wave - 2, lane);
+    }
+    if (i == 0) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint2 w = make_uint2(0, 0);
+        if (hl < G) w = *reinterpret_cast<const uint2 *>(qs + (hl * D + 16 * ks + 4 * qd) * EL);
+        qb[ks] = __builtin_bit_cast(bf16x4_t, w);
+      }
+    }
+    uint64_t rd[12];
+    if constexpr (NSUB <= 3) {
+      if (bsel == 0) mfma_operands<0, SUBB>(rd, ad);
+      else if (bsel == 1) mfma_operands<2 * SUBB, 3 * SUBB>(rd, ad);
       else mfma_operands<4 * SUBB, 5 * SUBB>(rd, ad);
-      // q.k: lane (qd, hl) gets the raw scores of tokens 4 qd + i of its group for head hl.
-      f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+      uint32_t adb[12];
+      const uint32_t boff = (uint32_t)(bsel * 2 * SUBB);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) S = mfma16(__builtin_bit_cast(bf16x4_t, rd[ks]), qb[ks], S);
-      const int nrows = min(TS, t1 - c0);
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = (grp * 16 + 4 * qd + i < nrows) ? S[i] : -INFINITY;
-      if (half == 0 && hl < G) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lgs[(sc * TS + grp * 16 + 4 * qd + i) * G + hl] = sv[i];
-      }
-      // Softmax of head hl: one running maximum per wave, moved (with a
-      // rescale of l and of the head's output rows) only when the scores pass
-      // it by more than 8 / cs.
-      float mx = fmaxf(fmaxf(m, fmaxf(sv[0], sv[1])), fmaxf(sv[2], sv[3]));
-      {
-        float w2 = mx;
-        permlane16_swap(mx, w2);
-        mx = fmaxf(mx, w2);
-        w2 = mx;
-        permlane32_swap(mx, w2);
-        mx = fmaxf(mx, w2);
-      }
-      if (__ballot(mx > m + tau) != 0ull) {
-        const float corr = (mx == -INFINITY) ? 1.f : fast_exp2((m - mx) * cs);
-        l *= corr;
-        m = mx;
-        // Output row i of this lane is head 4 qd + i; its factor lives in lane (head).
-        float fi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float fa = lane_value(corr, i < G ? i : G - 1);
-          if constexpr (G > 4) {
-            const float fb = lane_value(corr, 4 + i);
-            fi[i] = qd == 0 ? fa : fb;
-          } else {
-            fi[i] = fa;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[t][i] *= fi[i];
-      }
-      const float mc = (m == -INFINITY) ? 0.f : m * cs;
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = fast_exp2(fmaf(sv[i], cs, -mc));
-        l += pv[i];
-      }
-      bf16x4_t phi, plo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        phi[i] = (__bf16)pv[i];
-        plo[i] = (__bf16)(pv[i] - (float)phi[i]);
-      }
-      // P.V for the wave's 64 channels: O[head][ch] += P[head][tok] V[tok][ch].
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x4_t vb4 = __builtin_bit_cast(bf16x4_t, rd[8 + t]);
-        O[t] = mfma16(phi, vb4, O[t]);
-        O[t] = mfma16(plo, vb4, O[t]);
-      }
-      asm volatile("" : "+v"(m), "+v"(l));
-      sched_fence();
+      for (int k = 0; k < 12; ++k) adb[k] = ad[k] + boff;
+      mfma_operands<0, SUBB>(rd, adb);
     }
-    // The chunk's logits: the two half-0 waves write their own rows.  This
-    // launch's results are stored write-through, which leaves little for the
-    // write-back at its end that the second launch waits for.
+    // q.k: lane (qd, hl) gets the raw scores of tokens 4 qd + i of its group for head hl.
+    f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) S = mfma16(__builtin_bit_cast(bf16x4_t, rd[ks]), qb[ks], S);
+    const int nrows = min(TS, t1 - c0);
+    float sv[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) sv[r4] = (grp * 16 + 4 * qd + r4 < nrows) ? S[r4] : -INFINITY;
+    // The sub-chunk's logits: each half-0 wave gathers its 16 rows x G heads
+    // in its own LDS rows and stores them with coalesced write-through stores
+    // (little is left for the write-back at the end of the launch, which the
+    // second launch waits for).
     if (half == 0) {
-      constexpr int WR = 16 * G;  // floats per wave per sub-chunk
+      if (hl < G) {
 #pragma unroll
-      for (int q0 = 0; q0 < NSUB * WR; q0 += kWave) {
+        for (int r4 = 0; r4 < 4; ++r4) lgw[(4 * qd + r4) * G + hl] = sv[r4];
+      }
+      float* lgd = lg + (size_t)(c0 + grp * 16) * G;
+      const int vrows = nrows - grp * 16;  // rows of this token group in the tile
+#pragma unroll
+      for (int q0 = 0; q0 < 16 * G; q0 += kWave) {
         const int q = q0 + lane;
-        const int sc = q / WR, w = q - sc * WR;
-        const int row = grp * 16 + w / G;
-        const int n = cbase + sc * TS + row;
-        if (q < NSUB * WR && n < t1) store_agent_f(lg + (size_t)n * G + (w % G), lgs[(sc * TS + row) * G + (w % G)]);
+        float x;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(x) : "v"(lgw_a + 4 * min(q, 16 * G - 1)) : "memory");
+        if (q < 16 * G && q / G < vrows) store_agent_f(lgd + q, x);
       }
     }
+    // Softmax of head hl: one running maximum per wave, moved (with a
+    // rescale of l and of the head's output rows) only when the scores pass
+    // it by more than 8 / cs.
+    float mx = fmaxf(fmaxf(m, fmaxf(sv[0], sv[1])), fmaxf(sv[2], sv[3]));
+    {
+      float w2 = mx;
+      permlane16_swap(mx, w2);
+      mx = fmaxf(mx, w2);
+      w2 = mx;
+      permlane32_swap(mx, w2);
+      mx = fmaxf(mx, w2);
+    }
+    if (__ballot(mx > m + tau) != 0ull) {
+      const float corr = (mx == -INFINITY) ? 1.f : fast_exp2((m - mx) * cs);
+      l *= corr;
+      m = mx;
+      // Output row r4 of this lane is head 4 qd + r4; its factor lives in lane (head).
+      float fi[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float fa = lane_value(corr, r4 < G ? r4 : G - 1);
+        if constexpr (G > 4) {
+          const float fb = lane_value(corr, 4 + r4);
+          fi[r4] = qd == 0 ? fa : fb;
+        } else {
+          fi[r4] = fa;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) O[t][r4] *= fi[r4];
+    }
+    const float mc = (m == -INFINITY) ? 0.f : m * cs;
+    float pv[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      pv[r4] = fast_exp2(fmaf(sv[r4], cs, -mc));
+      l += pv[r4];
+    }
+    bf16x4_t phi, plo;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      phi[r4] = (__bf16)pv[r4];
+      plo[r4] = (__bf16)(pv[r4] - (float)phi[r4]);
+    }
+    // P.V for the wave's 64 channels: O[head][ch] += P[head][tok] V[tok][ch].
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x4_t vb4 = __builtin_bit_cast(bf16x4_t, rd[8 + t]);
+      O[t] = mfma16(phi, vb4, O[t]);
+      O[t] = mfma16(plo, vb4, O[t]);
+    }
+    asm volatile("" : "+v"(m), "+v"(l));
+    sched_fence();
   }
   // Tile partial: l summed over the lane rows of each head; the two token
   // groups (waves 2 h and 2 h + 1 for channel half h) combined through LDS.
@@ -1356,7 +1425,7 @@ template <int EL, int D, int G>
 static constexpr bool use_mfma() { return EL == 2 && D == 128; }
 template <int EL, int D, int G>
 static void (*attend_kernel())(StepArgs) {
-  if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G>;
+  if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G, 3>;
   else return k_attend<EL, D, G>;
 }
 
@@ -1365,15 +1434,16 @@ static int attend_grid(int n_units) {
   static int per_cu_cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (per_cu_cache[dev] == 0) {
+  int &pc = per_cu_cache[dev];
+  if (pc == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<EL, D, G>(), kThreads, 0) != hipSuccess)
       return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    per_cu_cache[dev] = per_cu * cus;
+    pc = per_cu * cus;
   }
   // One resident round of tiles, and at least 64 tiles beyond one per unit.
-  return min(max(per_cu_cache[dev], n_units + 64), kMaxGrid);
+  return min(max(pc, n_units + 64), kMaxGrid);
 }
 
 template <int EL, int D, int G>

@@ -108,8 +108,10 @@ typedef struct hikv_debug {
   int32_t *sel_channels;   /* [B][Hq][r] Stage II chosen channels, ascending (device) */
   int32_t *sel_tokens;     /* [B][Hq][k_T] positions of the exact-softmax tokens, ascending, -1 padded (device) */
   int32_t *sel_count;      /* [B][Hq] number of exact-softmax tokens, min(k_T, len + 1) (device) */
-  void *attend_start;      /* hipEvents (both or neither; caller-owned) that the dispatch of a Stage I */
-  void *attend_stop;       /* step's attention launch records when it starts and ends executing */
+  void *attend_start;      /* hipEvents (both or neither; caller-owned) that the dispatch of the step's */
+  void *attend_stop;       /* attention launch records when it starts and ends executing (Stage I: the
+                              launch over every live K and V row; Stage II: the reduced-channel logits
+                              pass over every live K row) */
 } hikv_debug;
 
 /* Bytes of device workspace the decode step and hikv_evict need for this
