@@ -112,7 +112,9 @@ def main():
                                c.len.data_ptr())
         layers.append(c)
     budget_t = torch.from_numpy(budget).cuda()
-    pol = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
+    # per-KV-head budgets go as a device array; one budget for every unit as budget_all
+    b_arr, b_all = (budget_t, 0) if w.budgets is not None else (None, w.budget_all)
+    pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
     ws = H.workspace(layers[0].shape, pol)
     # The caller's host copy of every layer's lengths (a serving loop tracks
     # them anyway); passed as the length hint so the tile plan is made on the
@@ -136,7 +138,7 @@ def main():
         moves_log.append(int((host_len[li] + 1 > budget).sum()))
         p = pol
         if not args.no_hint:
-            p = H.make_policy(budget_t, 0, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
+            p = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
                               len_hint=host_len[li])
         dbg = None
         if events is not None:

@@ -159,8 +159,17 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);
   }
+  // With the caller's lengths and one budget for every unit, the host knows
+  // whether any unit ends more than one token over budget; if none does, the
+  // bulk-eviction launch has nothing to do and is left out.
+  if (policy->len_hint && !policy->budget) {
+    a.no_bulk = 1;
+    const int U = shape->batch * shape->n_kv_heads;
+    for (int u = 0; u < U; ++u)
+      if (policy->len_hint[u] + 1 - policy->budget_all > 1) a.no_bulk = 0;
+  }
   if ((e = launch_accumulate(a, dt, s)) != hipSuccess) return dev_err(e);
-  if ((e = launch_bulk_evict(a, dt, new_pos, true, s)) != hipSuccess) return dev_err(e);
+  if (!a.no_bulk && (e = launch_bulk_evict(a, dt, new_pos, true, s)) != hipSuccess) return dev_err(e);
   return HIKV_OK;
 }
 

@@ -421,6 +421,9 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
   const int newest = a.new_pos[b];
   const bool over = L > beta;
   const int t0 = lt * T, t1 = min(t0 + T, L);
+  // More than one token over budget needs the bulk eviction, which the host
+  // leaves out when the caller's lengths say that no unit needs it.
+  if (a.no_bulk && L - beta > 1 && lt == 0 && tid == 0) set_status(a.ws.status, HIKV_EINVAL);
 
   float M[G], IL[G];
 #pragma unroll
@@ -438,7 +441,10 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) p += fast_exp2(lg[(size_t)n * G + g] - M[g]) * IL[g];
     const float iv = ((n == L - 1) ? 0.f : imp[n]) + p;
-    imp[n] = iv;
+    // Written through to memory: the unit's last tile may move slot L - 1's
+    // value into the victim's slot, and no slot may be left dirty in two
+    // caches.
+    store_agent_f(imp + n, iv);
     if (over) {
       const int pn = pos[n];
       const bool prot = (pn < S) || (pn > newest - Wp);
@@ -465,29 +471,29 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
     }
     __syncthreads();
   }
+  // The tile's lowest key goes out with device-coherent stores, and every
+  // store of the tile is complete before its ticket is taken; the unit's
+  // last tile then reads them all with device-coherent loads.  (No cache-wide
+  // write-back: a fence here costs more than the whole kernel's work.)
   if (tid == 0) {
-    a.ws.tile_key[tile] = sk[0];
-    a.ws.tile_slot[tile] = ss[0];
+    __hip_atomic_store(&a.ws.tile_key[tile], sk[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_agent(&a.ws.tile_slot[tile], ss[0]);
   }
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.ws.ticket[u], 1u);
-    last_flag = (prev == (uint32_t)(ntile_u - 1));
-  }
+  if (tid == 0) last_flag = ticket_agent(&a.ws.ticket[u]) == (uint32_t)(ntile_u - 1);
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
   if (over && L - beta == 1) {
     const int tb = a.ws.plan[u];
     if (tid == 0) {
       uint64_t kk = ~0ull;
       int vs = -1;
       for (int t = tb; t < tb + ntile_u; ++t) {
-        const uint64_t k = a.ws.tile_key[t];
+        const uint64_t k = __hip_atomic_load(&a.ws.tile_key[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (k < kk) {
           kk = k;
-          vs = a.ws.tile_slot[t];
+          vs = load_agent(&a.ws.tile_slot[t]);
         }
       }
       last_flag = vs;  // reuse as victim slot broadcast
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
       }
       if (tid == 0) {
         a.pos[(size_t)u * a.cap + v] = pos[last];
-        a.imp[(size_t)u * a.cap + v] = imp[last];
+        store_agent_f(a.imp + (size_t)u * a.cap + v, __int_as_float(load_agent(reinterpret_cast<const int32_t *>(imp + last))));
       }
     }
     if (tid == 0) a.len[u] = (v >= 0) ? L - 1 : L;

@@ -140,6 +140,7 @@ struct StepArgs {
   const int32_t *budget;     // may be null
   int32_t budget_all, n_sink, n_recent;
   int32_t r, kT;             // Stage II
+  int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;
   float *out;

@@ -32,26 +32,33 @@ __device__ __forceinline__ bool unit_has_tiles(const StepArgs &a, int u) {
   return nt > 0;
 }
 
-// S1: one wave per (b, q-head): rank every channel by (|q| desc, index asc).
+// S1: one wave per (b, q-head): the r channels of largest |q| (ties: lower
+// channel).  Lane l holds channels l and l + 64.  |q| as its IEEE bits orders
+// like the value (non-negative floats); the r-th largest bit pattern is found
+// one bit at a time from the top (count of lanes at or above a trial
+// threshold by ballot), then the channels above it are taken, and of those
+// equal to it the lowest-numbered ones that complete r.
 __global__ __launch_bounds__(64) void k_stage2_channels(StepArgs a, int el) {
   const int bh = blockIdx.x, lane = threadIdx.x;
   const int D = a.D;
-  __shared__ float aq[128];
-  for (int d = lane; d < D; d += 64) aq[d] = load_abs(a.q, (size_t)bh * D + d, el);
-  __syncthreads();
-  bool sel[2] = {false, false};
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int d = lane + 64 * t;
-    if (d >= D) continue;
-    const float x = aq[d];
-    int rank = 0;
-    for (int e = 0; e < D; ++e) {
-      const float y = aq[e];
-      rank += (y > x) || (y == x && e < d);
-    }
-    sel[t] = rank < a.r;
+  const uint32_t v0 = __float_as_uint(load_abs(a.q, (size_t)bh * D + lane, el));
+  const uint32_t v1 = D > 64 ? __float_as_uint(load_abs(a.q, (size_t)bh * D + 64 + lane, el)) : 0u;
+  const bool has1 = D > 64;
+  auto count_ge = [&](uint32_t t) {
+    return __popcll(__ballot(v0 >= t)) + (has1 ? __popcll(__ballot(v1 >= t)) : 0);
+  };
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (count_ge(cand) >= a.r) thr = cand;
   }
+  const uint64_t gt0 = __ballot(v0 > thr), gt1 = has1 ? __ballot(v1 > thr) : 0ull;
+  const uint64_t eq0 = __ballot(v0 == thr), eq1 = has1 ? __ballot(v1 == thr) : 0ull;
+  const int need = a.r - __popcll(gt0) - __popcll(gt1);  // equal channels still to take
+  const uint64_t below = (1ull << lane) - 1ull;
+  bool sel[2];
+  sel[0] = v0 > thr || (v0 == thr && __popcll(eq0 & below) < need);
+  sel[1] = has1 && (v1 > thr || (v1 == thr && __popcll(eq0) + __popcll(eq1 & below) < need));
   const uint64_t b0 = __ballot(sel[0]);
   const uint64_t b1 = __ballot(sel[1]);
   if (lane == 0) {
@@ -171,16 +178,22 @@ __global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
   float m = -INFINITY, l = 0.f, acc[CH];
 #pragma unroll
   for (int e = 0; e < CH; ++e) acc[e] = 0.f;
-  for (int base = wave * TPW * U; base < nt; base += 4 * TPW * U) {
-    uint4 kf[U], vf[U];
+  // The selected slots go to LDS a chunk at a time, so that the K/V row loads
+  // do not wait for an index load; the row loads run one step ahead of the
+  // arithmetic (two register buffers).
+  constexpr int CHK = 1024, STEP = 4 * TPW * U;
+  __shared__ int s_n[CHK];
+  auto load_rows = [&](int cn, int base, uint4 (&kf)[U], uint4 (&vf)[U]) {
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int t = base + i * TPW + r;
-      const bool ok = t < nt;
-      const int n = ok ? tsel[t] : 0;
+      const bool ok = t < cn;
+      const int n = ok ? s_n[t] : 0;
       kf[i] = ok ? *reinterpret_cast<const uint4 *>(kc + (size_t)n * RB + c * 16) : make_uint4(0, 0, 0, 0);
       vf[i] = ok ? *reinterpret_cast<const uint4 *>(vc + (size_t)n * RB + c * 16) : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto consume = [&](int cn, int base, const uint4 (&kf)[U], const uint4 (&vf)[U]) {
     float s[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
         d = fmaf(__uint_as_float(qf.w), __uint_as_float(kf[i].w), d);
       }
       d = row_sum<LPR>(d) * a.scale_log2;
-      s[i] = (base + i * TPW + r < nt) ? d : -INFINITY;
+      s[i] = (base + i * TPW + r < cn) ? d : -INFINITY;
     }
     float mx = m;
 #pragma unroll
@@ -225,6 +238,22 @@ __global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
       }
     }
     m = mx;
+  };
+  for (int cb = 0; cb < nt; cb += CHK) {
+    const int cn = min(CHK, nt - cb);
+    __syncthreads();  // the previous chunk's indices are no longer read
+    for (int i = tid; i < cn; i += 256) s_n[i] = tsel[cb + i];
+    __syncthreads();
+    uint4 ka[U], va[U], kb[U], vb[U];
+    int base = wave * TPW * U;
+    load_rows(cn, base, ka, va);
+    for (; base < cn; base += 2 * STEP) {
+      load_rows(cn, base + STEP, kb, vb);
+      consume(cn, base, ka, va);
+      if (base + STEP >= cn) break;
+      load_rows(cn, base + 2 * STEP, ka, va);
+      consume(cn, base + STEP, kb, vb);
+    }
   }
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {

@@ -1463,7 +1463,14 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Second launch: per unit, importance blocks to cover the capacity, then
   // one output block per 64 outputs.
-  const int nib = imp_blocks(a.cap);
+  // With a host plan the longest unit is known: no importance blocks beyond
+  // its length are launched (they would only start and exit).
+  int nib = imp_blocks(a.cap);
+  if (a.hp.n) {
+    int mx = 1;
+    for (int u = 0; u < a.hp.n; ++u) mx = max(mx, a.hp.L[u]);
+    nib = min(nib, (mx + kImpChunk - 1) / kImpChunk);
+  }
   hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)a.n_units, (unsigned)(nib + k2_noc<EL, D, G>())),
                      dim3(kT2), 0, s, a);
   return hipGetLastError();

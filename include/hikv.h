@@ -96,7 +96,10 @@ typedef struct hikv_policy {
   const int32_t *len_hint; /* optional HOST copy of len[] as it is before this call, or NULL.
                               With at most 64 units the split-K tile plan is then computed on
                               the host and passed with the launch, which saves the kernels a
-                              dependent device-memory round trip.  A hint with len + 1 >
+                              dependent device-memory round trip.  On the Stage II path with
+                              budget == NULL, a hint under which no unit ends more than one
+                              token over budget_all also leaves out the bulk-eviction launch.
+                              A hint with len + 1 >
                               capacity or len < 0 is rejected (HIKV_EINVAL); a hint that
                               disagrees with the device's len[] sets HIKV_EINVAL in the
                               device status and that call's results are undefined. */

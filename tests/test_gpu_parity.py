@@ -100,6 +100,28 @@ def test_wrong_host_length_hint_is_reported():
              hint_override=wrong)
 
 
+def test_twostage_host_hint_skips_bulk_launch():
+    """Stage II with the caller's lengths: the compression step still runs
+    the bulk eviction, the steady steps leave its launch out; results equal
+    the oracle's either way."""
+    w = W.workload("twostage", ctx=700, steps=4, batch=2)
+    w.budget_all, w.n_recent = 200, 16
+    d = W.generate(w)
+    lockstep(_run(w, d, hint=True), d, w.steps, tag="twostage-hint")
+
+
+def test_wrong_host_length_hint_stage2_is_reported():
+    """A hint under which no unit needs the bulk eviction, while the device's
+    lengths need it, is reported as HIKV_EINVAL."""
+    w = W.workload("twostage", ctx=300, steps=1, batch=1)
+    w.budget_all, w.n_recent = 100, 8
+    d = W.generate(w)
+    run = _run(w, d)
+    wrong = np.full((1, 8), 99, dtype=np.int32)       # device holds 300 per unit
+    run.step(d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], expect=H.HIKV_EINVAL,
+             hint_override=wrong)
+
+
 def test_llama8b_reduced_lockstep():
     w = W.workload("llama8b", ctx=1000, steps=3, batch=2)
     w.budget_all, w.n_recent = 256, 32
