@@ -115,7 +115,13 @@ def main():
     # per-KV-head budgets go as a device array; one budget for every unit as budget_all
     b_arr, b_all = (budget_t, 0) if w.budgets is not None else (None, w.budget_all)
     pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
-    ws = H.workspace(layers[0].shape, pol)
+    # One workspace per layer copy: a workspace carries its cache's pending
+    # eviction from one step to the next.
+    wss = [H.workspace(layers[0].shape, pol) for _ in range(args.layers)]
+
+    def device_status(what):
+        for wsl in wss:
+            H.check(H.hikv_device_status(wsl), what)
     # The caller's host copy of every layer's lengths (a serving loop tracks
     # them anyway); passed as the length hint so the tile plan is made on the
     # host.  --no-hint measures the device-derived plan instead.
@@ -134,8 +140,10 @@ def main():
         c = layers[li]
         n = layer_step[li]
         layer_step[li] += 1
-        live_log.append(int((host_len[li] + 1).sum()))
-        moves_log.append(int((host_len[li] + 1 > budget).sum()))
+        # live tokens of the step (a pending eviction's dead slot is not one)
+        live_now = host_len[li] + 1 - (host_len[li] > budget)
+        live_log.append(int(live_now.sum()))
+        moves_log.append(int((live_now > budget).sum()))
         p = pol
         if not args.no_hint:
             p = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
@@ -144,10 +152,16 @@ def main():
         if events is not None:
             dbg = H.hikv_debug(None, None, None, events[0].cuda_event, events[1].cuda_event)
         code = H.hikv_decode_step(c.shape, c.cache, p, q_all[n % n_inputs], kn_all[n % n_inputs],
-                                  vn_all[n % n_inputs], pos_all[n], out, ws, debug=dbg)
+                                  vn_all[n % n_inputs], pos_all[n], out, wss[li], debug=dbg)
         if code != 0:
             raise RuntimeError(f"hikv_decode_step: {H.status_string(code)}")
-        host_len[li] = np.minimum(host_len[li] + 1, budget).astype(np.int32)
+        # The caller's copy of len[] after the step: a unit over its budget by one
+        # keeps budget + 1 slots with that eviction pending (the next step writes
+        # its new token into the dead slot); a bulk cut leaves exactly the budget.
+        old = host_len[li]
+        pending = old > budget
+        live = old + 1 - pending
+        host_len[li] = np.where(live > budget + 1, budget, np.where(pending, old, old + 1)).astype(np.int32)
 
     moves_log = []
     stream = torch.cuda.current_stream()
@@ -162,7 +176,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     comp_ms = e0.elapsed_time(e1) / args.layers
-    H.check(H.hikv_device_status(ws), "device status after compression")
+    device_status("device status after compression")
     live_after = np.minimum(w.ctx + 1, budget)
     assert np.array_equal(layers[0].len.cpu().numpy(), live_after), "compression did not reach the budgets"
     comp_bytes = BM.decode_step_bytes(B, Hq, Hkv, D, w.el, np.full((B, Hkv), w.ctx + 1),
@@ -174,7 +188,7 @@ def main():
     for i in range(args.warmup):
         step(i % args.layers)
     torch.cuda.synchronize()
-    H.check(H.hikv_device_status(ws), "device status after warm-up")
+    device_status("device status after warm-up")
 
     # Timed steady steps: one HIP graph, replayed once.
     base = args.warmup
@@ -190,7 +204,7 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
-    H.check(H.hikv_device_status(ws), "device status after timed steps")
+    device_status("device status after timed steps")
     ms_step = ms_total / args.steps
     steps_per_s = 1e3 / ms_step
     # bytes of the average timed step (every step is alike in the budgeted steady
@@ -227,7 +241,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] timing replay: {args.steps} steps enqueued in {t_enq * 1e3:.1f} ms behind a "
         f"~{sleep_cycles / 2.4e6:.0f} ms GPU wait (the host blocks once the hardware queue is full)")
-    H.check(H.hikv_device_status(ws), "device status after the timing replay")
+    device_status("device status after the timing replay")
     attend_ms = sum(e_a.elapsed_time(e_b) for e_a, e_b in evs) / args.steps
     live_rep = sum(live_log[-args.steps:]) / args.steps
     if stage2:  # the reduced-channel logits pass reads every live K row whole, and q

@@ -150,9 +150,13 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
       if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
       return dev_err(launch_step(a, dt, s, ev0, ev1));
     }
+    // The four-launch path evicts in place: an eviction a two-launch step
+    // left pending is resolved first.
+    if ((e = launch_settle(a, dt, nullptr, true, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, true, false, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
   } else {
+    if ((e = launch_settle(a, dt, nullptr, true, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);
@@ -186,8 +190,37 @@ extern "C" int hikv_evict(const hikv_shape *shape, const hikv_cache *cache,
   if (ws_bytes < sz.total) return HIKV_EINVAL;
   if ((st = arch_ok()) != HIKV_OK) return st;
   StepArgs a = make_args(shape, cache, policy, ws_carve(ws, sz));
-  return dev_err(launch_bulk_evict(a, shape->kv_dtype, newest_pos, false,
-                                   static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_settle(a, shape->kv_dtype, nullptr, true, s);
+  if (e != hipSuccess) return dev_err(e);
+  return dev_err(launch_bulk_evict(a, shape->kv_dtype, newest_pos, false, s));
+}
+
+namespace {
+int settle_common(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                  const void *ws, size_t ws_bytes, int32_t *slot_out, bool apply, void *stream) {
+  int st = check_shape(shape);
+  if (st != HIKV_OK) return st;
+  if ((st = check_policy(shape, policy)) != HIKV_OK) return st;
+  if (shape->batch == 0) return HIKV_OK;
+  if ((st = check_cache(cache)) != HIKV_OK) return st;
+  if (!ws || !aligned16(ws) || (!apply && !slot_out)) return HIKV_EINVAL;
+  const WsSizes sz = sizes_for(shape, policy);
+  if (ws_bytes < sz.total) return HIKV_EINVAL;
+  if ((st = arch_ok()) != HIKV_OK) return st;
+  StepArgs a = make_args(shape, cache, policy, ws_carve(const_cast<void *>(ws), sz));
+  return dev_err(launch_settle(a, shape->kv_dtype, slot_out, apply, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" int hikv_settle(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                           void *ws, size_t ws_bytes, void *stream) {
+  return settle_common(shape, cache, policy, ws, ws_bytes, nullptr, true, stream);
+}
+
+extern "C" int hikv_pending(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                            const void *ws, size_t ws_bytes, int32_t *slot_out, void *stream) {
+  return settle_common(shape, cache, policy, ws, ws_bytes, slot_out, false, stream);
 }
 
 extern "C" size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t n_obs) {

@@ -25,6 +25,10 @@ hipError_t launch_bulk_evict(const StepArgs &a, int dtype, const int32_t *newest
 // ev0/ev1 (may be null): events recorded around the attention launch.
 hipError_t launch_step(const StepArgs &a, int dtype, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
+// The pending eviction a two-launch step leaves: its slot per unit to
+// slot_out (device [n_units], may be null; -1 when none) and, with apply, the
+// unit compacted as if evicted in place.
+hipError_t launch_settle(const StepArgs &a, int dtype, int32_t *slot_out, bool apply, hipStream_t s);
 // Host-side tile plan from a host copy of len[] (fills a.hp); false when it
 // does not apply (too many units), in which case the kernels derive it.
 bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint);

@@ -433,6 +433,75 @@ __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// ---------------------------------------------------------------------------
+// Pending eviction.  A two-launch step that evicts one token leaves the choice
+// of the victim to the next call: it stores, per unit, the number n of its
+// importance blocks (pend[u]) and each block's lowest eviction key and its
+// slot (icand[u][i], i < n).  The evicted slot is the one whose key is the
+// smallest; until a later call resolves it, the slot is dead.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int pend_stride(const StepArgs &a) { return (a.cap + kImpChunk - 1) / kImpChunk; }
+
+// The lookup in the attention launch goes through LDS: the count (every lane
+// of wave 0 fetches the same word) and up to 64 candidates per round.
+struct PendLds {
+  int32_t cnt[kWave];
+  int32_t cand[kWave][4];
+  int32_t dead[4];
+};
+
+// Wave 0 of a tile, before its first rows: the count and the first 64
+// candidates of unit u, by DMA (no register loads whose waits the compiler
+// would place), issued ahead of the rows so that the first wait covers them.
+__device__ __forceinline__ void pend_fetch(const StepArgs &a, int u, PendLds &pd, int lane) {
+  const int nbm = pend_stride(a);
+  __builtin_amdgcn_global_load_lds(a.ws.pend + u, &pd.cnt[0], 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(a.ws.icand + ((size_t)u * nbm + min(lane, nbm - 1)) * 4, &pd.cand[0][0], 16, 0,
+                                   0);
+}
+
+// Wave 0, once the fetch has landed: the dead slot (-1 if none), left in
+// pd.dead[0] for the other waves of the tile; with record, also stored for
+// the second launch of the step.  More than 64 candidates take a round trip
+// per further 64.
+__device__ __forceinline__ int pend_resolve(const StepArgs &a, int u, PendLds &pd, int lane, bool record) {
+  const int nbm = pend_stride(a);
+  int n;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(n) : "v"(lds_addr(&pd.cnt[0])) : "memory");
+  n = __builtin_amdgcn_readfirstlane(min(n, nbm));
+  uint64_t key = ~0ull;
+  int slot = -1;
+  for (int base = 0; base < n; base += kWave) {
+    if (base > 0) {
+      __builtin_amdgcn_global_load_lds(a.ws.icand + ((size_t)u * nbm + min(base + lane, nbm - 1)) * 4,
+                                       &pd.cand[0][0], 16, 0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    u32x4 e;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(e) : "v"(lds_addr(&pd.cand[lane][0])) : "memory");
+    const uint64_t k = ((uint64_t)e.y << 32) | e.x;
+    if (base + lane < n && k < key) {
+      key = k;
+      slot = (int)e.z;
+    }
+  }
+  wave_min_key(key, slot);
+  const int d = (key == ~0ull) ? -1 : slot;
+  if (lane == 0) {
+    pd.dead[0] = d;
+    if (record) store_agent(a.ws.dslot + u, d);
+  }
+  // The LDS write is complete before the barrier that follows (a DMA barrier
+  // does not wait for LDS operations).
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  return d;
+}
+__device__ __forceinline__ int pend_read(PendLds &pd) {
+  int d;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(d) : "v"(lds_addr(&pd.dead[0])) : "memory");
+  return __builtin_amdgcn_readfirstlane(d);
+}
+
 // Workgroup barrier for LDS data only.  __syncthreads() also waits for every
 // global load and store of the wave to complete, which costs a memory round
 // trip when none of them matter to the LDS exchange.
@@ -476,6 +545,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   __shared__ __attribute__((aligned(16))) char qs[QB];
   __shared__ __attribute__((aligned(16))) float lgs[TC * G];  // the chunk's logits
   __shared__ float sm_ml[4][G][2];
+  __shared__ __attribute__((aligned(16))) PendLds pd;
   float(*sm_acc)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);  // reused after the chunks
   static_assert(4 * G * D * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
   static_assert(NSUB == 3, "the vmcnt chain below is written for three sub-chunks");
@@ -509,8 +579,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
   float *lg = a.ws.logits + (size_t)u * a.cap * G;
 
-  // The group's queries go to LDS ahead of the first rows, so every wait
-  // below also covers them.
+  // The pending eviction's candidates and the group's queries go to LDS
+  // ahead of the first rows, so every wait below also covers them.
+  if (wave == 0) pend_fetch(a, u, pd, lane);
+  int dead = -1;  // the pending eviction's slot: masked
   {
     const int off = wave * 1024 + lane * 16;
     const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
@@ -541,7 +613,10 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
       if (sc == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 1)) : "memory");
       else if (sc == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI * (NSUB - 2)) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const bool first = cbase == t0 && sc == 0;
+      if (first && wave == 0) pend_resolve(a, u, pd, lane, t0 == 0);
       dma_barrier();
+      if (first) dead = pend_read(pd);
       if (sc == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) qf[g] = *reinterpret_cast<const uint4 *>(qs + (g * D + c * CH) * EL);
@@ -560,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
 #pragma unroll
       for (int i = 0; i < UR; ++i) {
         const int row = wave * (TS / 4) + i * TPW + r;
-        const bool ok = row < nrows;
+        const bool ok = row < nrows && c0 + row != dead;
         const uint4 kf = kf2[i];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -803,6 +878,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   __shared__ __attribute__((aligned(16))) char qs[QB];
   __shared__ __attribute__((aligned(16))) float lgs[2 * 16 * G];  // logits of a sub-chunk, per token group
   __shared__ float sm_ml[4][G][2];
+  __shared__ __attribute__((aligned(16))) PendLds pd;
   float(*sm_acc)[G][64] = reinterpret_cast<float(*)[G][64]>(smem);  // reused after the loop
   static_assert(4 * G * 64 * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
 
@@ -835,6 +911,9 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   // (vmcnt(0) only) tells it so; otherwise it waits for them, and with them
   // for every DMA issued below, at the first reuse of their registers.
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  // The pending eviction's candidates, then q, ahead of the rows.
+  if (wave == 0) pend_fetch(a, u, pd, lane);
+  int dead = -1;  // the pending eviction's slot: masked
   {
     const int off = wave * 1024 + lane * 16;
     const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
@@ -890,9 +969,11 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
       const int ahead = min(nsc, NSUB + max(0, i - 1)) - (i + 1);
       vm_wait_ahead<4 * NI, NSUB - 1>(ahead);
     } else if (i == 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // q (no store issued yet)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // q and the candidates (no store issued yet)
+      if (wave == 0) pend_resolve(a, u, pd, lane, t0 == 0);
     }
     dma_barrier();  // every wave's rows of sub-chunk i are in; every wave is done with i - 1
+    if (i == 0) dead = pend_read(pd);
     if (loader && i >= 1 && i + NSUB - 1 < nsc) {
       const int cr = t0 + (i + NSUB - 1) * TS, br = (i - 1) % NSUB;
       stage_sub_by<2>(smem + br * 2 * SUBB, smem + br * 2 * SUBB + SUBB, kc, vc, kn, vn, cr,
@@ -925,7 +1006,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
     const int nrows = min(TS, t1 - c0);
     float sv[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) sv[r4] = (grp * 16 + 4 * qd + r4 < nrows) ? S[r4] : -INFINITY;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row = grp * 16 + 4 * qd + r4;
+      sv[r4] = (row < nrows && c0 + row != dead) ? S[r4] : -INFINITY;
+    }
     // The sub-chunk's logits: each half-0 wave gathers its 16 rows x G heads
     // in its own LDS rows and stores them with coalesced write-through stores
     // (little is left for the write-back at the end of the launch, which the
@@ -1174,6 +1258,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
       const float *lg = a.ws.logits + (size_t)u * a.cap * G;
       const int len_dev = ld_vec(a.len + u, vz);
+      const int dead_ld = ld_vec(a.ws.dslot + u, vz);
       const int rt = tid % (2 * NR);
       const uint4 nrow = *reinterpret_cast<const uint4 *>(rt < NR ? kn + rt * 16 : vn + (rt - NR) * 16);
       float tl[NB][G], ti[NB];
@@ -1210,15 +1295,22 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         }
         if (err) return;
       }
-      const bool over = L > beta;
-      const int n_evict = over ? L - beta : 0;
+      // The pending eviction of the previous step (found by the attention
+      // launch): a dead slot, not live and not attended, that the new token
+      // takes over unless the unit is cut in bulk.
+      const int dead = dead_ld;
+      const int live = L - (dead >= 0 ? 1 : 0);
+      const bool over = live > beta;
+      const int n_evict = over ? live - beta : 0;
       // One eviction (the steady state) is spread over the unit's blocks like
-      // the importance; more than one needs every token in one block.
+      // the importance, and its victim is left pending for the next call;
+      // more than one (a bulk cut) needs every token in one block.
       const bool bulk = n_evict > 1;
       if (bulk && r > 0) return;
       const int nb1 = bulk ? L : min(L, nb0 + CHUNK);
       const int nact = (L + CHUNK - 1) / CHUNK;  // blocks holding tokens of the unit
       const int Wp = min(a.n_recent, beta - S);
+      const int fs = (dead >= 0 && !bulk) ? dead : Lold;  // the new token's slot
       float Mg[G], ILg[G];
     #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1226,9 +1318,6 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         Mg[g] = (Mr == -INFINITY) ? 0.f : Mr * a.scale_log2;
         ILg[g] = 1.f / lane_value(Llane, g);
       }
-      // Steady state: the importance stays in registers until the block's
-      // lowest key is known, so no slot is written twice.
-      const bool defer = n_evict == 1;
       uint64_t *bkeys = a.ws.bkeys + (size_t)u * a.cap;  // bulk: every slot's key
       uint64_t best = ~0ull;
       int best_slot = -1;
@@ -1237,143 +1326,83 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int n = base + tid + i * kT2;
-          if (n < nb1) {
+          if (n < nb1 && n != dead) {
             float p = 0.f;
     #pragma unroll
             for (int g = 0; g < G; ++g) p += fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
             const bool is_new = n == Lold;
             const float iv = (is_new ? 0.f : ti[i]) + p;
             const int pn = is_new ? newest : tp[i];
-            ti[i] = iv;
             if (is_new) s_newimp = iv;
-            else if (!defer) impw[n] = iv;
+            else impw[n] = iv;
             const bool cand = !((pn < S) || (pn > newest - Wp));
             if (over && cand) {
               const uint64_t k = evict_key(iv, pn);
               if (k < best) {
                 best = k;
-                best_slot = n;
+                best_slot = is_new ? fs : n;
               }
             }
             if (bulk) bkeys[n] = cand ? evict_key(iv, pn) : ~0ull;
+          } else if (bulk && n < nb1) {
+            bkeys[n] = 0;  // the dead slot: the first to go
           }
         }
       }
-      if (!over) {
-        // Nothing to evict: the block holding slot Lold stores the new token there.
+      if (!bulk) {
+        wave_min_key(best, best_slot);
+        if (lane == 0) {
+          sk[wave] = best;
+          ss[wave] = best_slot;
+        }
+        lds_barrier();  // s_newimp, the waves' lowest keys
         if (nb1 == L) {
-          lds_barrier();  // s_newimp
-          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
+          // The block holding slot Lold places the new token: into the dead
+          // slot, or appended at Lold.
+          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)fs * RB)[tid % NR] = nrow;
           if (tid == 0) {
-            impw[Lold] = s_newimp;
-            posw[Lold] = newest;
-            a.len[u] = L;
+            impw[fs] = s_newimp;
+            posw[fs] = newest;
+            if (dead < 0) a.len[u] = L;
           }
         }
-        return;
-      }
-      wave_min_key(best, best_slot);
-      if (lane == 0) {
-        sk[wave] = best;
-        ss[wave] = best_slot;
-      }
-      lds_barrier();
-      float newimp = s_newimp;  // valid in the block holding slot Lold
-      if (n_evict == 1) {
-        // Steady state: the lowest key is the victim; the new token takes its
-        // slot, or is itself dropped.  Every wave reduces the waves' minima.
-        uint64_t kk = lane < kNW2 ? sk[lane] : ~0ull;
-        int vs = lane < kNW2 ? ss[lane] : -1;
-        wave_min_key(kk, vs);
-        int victim = __builtin_amdgcn_readfirstlane(vs);
-        if (nact > 1) {
-          // Every importance value of the block is final except the one at its
-          // lowest key.  That slot, its key and its importance (the key's high
-          // word) go out with agent-coherent stores; the unit's last block to
-          // take a ticket finds the victim among all blocks' lowest keys and
-          // stores the deferred values, so no slot is written twice.
-    #pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            const int n = nb0 + tid + i * kT2;
-            if (n < nb1 && n != Lold && n != victim) impw[n] = ti[i];
-          }
-          int32_t *cand = a.ws.icand + (size_t)u * nib * 4;
-          if (tid == 0) {
-            store_agent(cand + 4 * r, (int32_t)(uint32_t)kk);
-            store_agent(cand + 4 * r + 1, (int32_t)(uint32_t)(kk >> 32));
-            store_agent(cand + 4 * r + 2, victim);
-            if (nb1 == L) store_agent(reinterpret_cast<int32_t *>(a.ws.fz_newimp) + u, __float_as_int(newimp));
-            // The stores above are complete before the ticket is taken.
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            s_last = ticket_agent(a.ws.ticket + u) == (uint32_t)(nact - 1);
-          }
-          __syncthreads();
-          if (!s_last || wave != 0) return;  // the rest is wave 0's
-          kk = ~0ull;
-          vs = -1;
-          uint32_t chi = 0xffffffffu;
-          int cslot = -1;
-          if (lane < nact) {
-            const uint32_t lo = (uint32_t)load_agent(cand + 4 * lane);
-            chi = (uint32_t)load_agent(cand + 4 * lane + 1);
-            cslot = load_agent(cand + 4 * lane + 2);
-            kk = ((uint64_t)chi << 32) | lo;
-            vs = cslot;
-          }
-          for (int i = lane + kWave; i < nact; i += kWave) {  // more blocks than lanes
-            const uint64_t k = ((uint64_t)(uint32_t)load_agent(cand + 4 * i + 1) << 32) |
-                               (uint32_t)load_agent(cand + 4 * i);
-            if (k < kk) {
-              kk = k;
-              vs = load_agent(cand + 4 * i + 2);
-            }
-          }
-          wave_min_key(kk, vs);
-          victim = __builtin_amdgcn_readfirstlane(vs);
-          newimp = __int_as_float(load_agent(reinterpret_cast<const int32_t *>(a.ws.fz_newimp) + u));
-          // The deferred importance of the blocks' lowest-key slots but the victim.
+        int32_t *cand = a.ws.icand + (size_t)u * pend_stride(a) * 4;
+        if (n_evict == 1) {
+          // The eviction stays pending: each block leaves its lowest key.
           if (wave == 0) {
-            if (cslot >= 0 && cslot != victim && cslot != Lold) impw[cslot] = unord_f32(chi);
-            for (int i = lane + kWave; i < nact; i += kWave) {
-              const int sl = load_agent(cand + 4 * i + 2);
-              if (sl >= 0 && sl != victim && sl != Lold)
-                impw[sl] = unord_f32((uint32_t)load_agent(cand + 4 * i + 1));
+            uint64_t kk = lane < kNW2 ? sk[lane] : ~0ull;
+            int vs = lane < kNW2 ? ss[lane] : -1;
+            wave_min_key(kk, vs);
+            if (lane == 0) {
+              cand[4 * r] = (int32_t)(uint32_t)kk;
+              cand[4 * r + 1] = (int32_t)(uint32_t)(kk >> 32);
+              cand[4 * r + 2] = vs;
+              if (r == 0) a.ws.pend[u] = nact;
             }
           }
-          if (tid == 0) store_agent(reinterpret_cast<int32_t *>(a.ws.ticket) + u, 0);
-        }
-        const int dst = (victim == Lold) ? -1 : victim;
-        if (dst >= 0 && tid < 2 * NR)
-          reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)dst * RB)[tid % NR] = nrow;
-        if (nact == 1) {
-    #pragma unroll
-          for (int i = 0; i < NB; ++i) {
-            const int n = nb0 + tid + i * kT2;
-            if (n < nb1 && n != Lold) {
-              impw[n] = (n == dst) ? newimp : ti[i];
-              if (n == dst) posw[n] = newest;
-            }
-          }
-        } else if (dst >= 0 && tid == 0) {
-          posw[dst] = newest;
-          impw[dst] = newimp;
+        } else if (r == 0 && tid == 0) {
+          a.ws.pend[u] = 0;
         }
         return;
       }
-      // Bulk: the new token goes to slot Lold, then the unit's L slots are cut to
-      // the budget: select the n_evict lowest keys among the unprotected tokens
-      // and move survivors from above the budget into the evicted slots below it.
+      // Bulk: the new token goes to slot Lold, then the unit's L slots (the
+      // dead one included, keyed to go first) are cut to the budget: select
+      // the L - beta lowest keys among the unprotected tokens and move
+      // survivors from above the budget into the evicted slots below it.
+      lds_barrier();  // s_newimp
+      const float newimp = s_newimp;
       if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
       if (tid == 0) {
         impw[Lold] = newimp;
         posw[Lold] = newest;
+        a.ws.pend[u] = 0;
       }
       __syncthreads();  // every key is stored
       __shared__ uint32_t hist[256];
       __shared__ uint32_t whist[kNW2 * 256];
       __shared__ int sc[kT2];
       __shared__ RadixState rs;
-      bulk_compact<kT2, RB>(bkeys, L, beta, n_evict, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
+      bulk_compact<kT2, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
                             a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs);
     }();
     end_wave();
@@ -1414,6 +1443,68 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   }
 
   end_wave();
+}
+
+// ---------------------------------------------------------------------------
+// Resolution of the pending eviction, one wave per unit: the dead slot (the
+// lowest of the unit's candidate keys), reported in slot_out when given
+// (-1: none pending); with apply, the unit's last slot moves into it (K and V
+// rows, position, importance) and len drops by one, as if the step had
+// evicted in place.
+// ---------------------------------------------------------------------------
+template <int RB>
+__global__ __launch_bounds__(kWave) void k_settle(StepArgs a, int32_t *slot_out, int apply) {
+  const int u = blockIdx.x, lane = threadIdx.x;
+  const int nbm = pend_stride(a);
+  const int n = min(__builtin_amdgcn_readfirstlane(a.ws.pend[u]), nbm);
+  const int4 *ic = reinterpret_cast<const int4 *>(a.ws.icand) + (size_t)u * nbm;
+  uint64_t key = ~0ull;
+  int slot = -1;
+  for (int i = lane; i < n; i += kWave) {
+    const int4 e = ic[i];
+    const uint64_t k = ((uint64_t)(uint32_t)e.y << 32) | (uint32_t)e.x;
+    if (k < key) {
+      key = k;
+      slot = e.z;
+    }
+  }
+  wave_min_key(key, slot);
+  const int d = (key == ~0ull) ? -1 : slot;
+  if (slot_out && lane == 0) slot_out[u] = d;
+  if (!apply || n == 0) return;
+  if (d >= 0) {
+    const int last = a.len[u] - 1;
+    if (d != last) {
+      static_assert(2 * RB <= kWave * 16, "one wave moves a K and a V row");
+      char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
+      char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
+      char *base = lane < RB / 16 ? kw : vw;
+      const int off = (lane % (RB / 16)) * 16;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (lane < 2 * (RB / 16)) x = *reinterpret_cast<const uint4 *>(base + (size_t)last * RB + off);
+      const int32_t p = a.pos[(size_t)u * a.cap + last];
+      const float im = a.imp[(size_t)u * a.cap + last];
+      if (lane < 2 * (RB / 16)) *reinterpret_cast<uint4 *>(base + (size_t)d * RB + off) = x;
+      if (lane == 0) {
+        a.pos[(size_t)u * a.cap + d] = p;
+        a.imp[(size_t)u * a.cap + d] = im;
+      }
+    }
+    if (lane == 0) a.len[u] = last;
+  }
+  if (lane == 0) a.ws.pend[u] = 0;
+}
+
+hipError_t launch_settle(const StepArgs &a, int dtype, int32_t *slot_out, bool apply, hipStream_t s) {
+  const int rb = a.D * (dtype == HIKV_BF16 ? 2 : 4);
+  const dim3 grid((unsigned)a.n_units), block(kWave);
+  switch (rb) {
+    case 128: hipLaunchKernelGGL(k_settle<128>, grid, block, 0, s, a, slot_out, apply ? 1 : 0); break;
+    case 256: hipLaunchKernelGGL(k_settle<256>, grid, block, 0, s, a, slot_out, apply ? 1 : 0); break;
+    case 512: hipLaunchKernelGGL(k_settle<512>, grid, block, 0, s, a, slot_out, apply ? 1 : 0); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

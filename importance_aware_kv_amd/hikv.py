@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(PKG, "libhikv.so")
 HIKV_F32, HIKV_BF16 = 0, 1
 HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
 
-EXPORTS = ("hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_prefill_workspace_bytes",
-           "hikv_prefill_scores", "hikv_device_status", "hikv_status_string")
+EXPORTS = ("hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_settle", "hikv_pending",
+           "hikv_prefill_workspace_bytes", "hikv_prefill_scores", "hikv_device_status", "hikv_status_string")
 
 
 class hikv_shape(C.Structure):
@@ -69,6 +69,10 @@ def lib():
         L.hikv_decode_step.restype = C.c_int
         L.hikv_evict.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, sz, vp]
         L.hikv_evict.restype = C.c_int
+        L.hikv_settle.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, sz, vp]
+        L.hikv_settle.restype = C.c_int
+        L.hikv_pending.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, sz, vp, vp]
+        L.hikv_pending.restype = C.c_int
         L.hikv_prefill_workspace_bytes.argtypes = [P(hikv_shape), i32]
         L.hikv_prefill_workspace_bytes.restype = sz
         L.hikv_prefill_scores.argtypes = [P(hikv_shape), P(hikv_cache), vp, vp, i32, i32, vp, sz, vp]
@@ -133,6 +137,16 @@ def hikv_decode_step(shape, cache, policy, q, k_new, v_new, new_pos, out, ws, de
 def hikv_evict(shape, cache, policy, newest_pos, ws, stream=None) -> int:
     return lib().hikv_evict(C.byref(shape), C.byref(cache), C.byref(policy), _p(newest_pos), _p(ws),
                             ws.numel() * ws.element_size(), _stream(stream))
+
+
+def hikv_settle(shape, cache, policy, ws, stream=None) -> int:
+    return lib().hikv_settle(C.byref(shape), C.byref(cache), C.byref(policy), _p(ws),
+                             ws.numel() * ws.element_size(), _stream(stream))
+
+
+def hikv_pending(shape, cache, policy, ws, slot_out, stream=None) -> int:
+    return lib().hikv_pending(C.byref(shape), C.byref(cache), C.byref(policy), _p(ws),
+                              ws.numel() * ws.element_size(), _p(slot_out), _stream(stream))
 
 
 def hikv_prefill_scores(shape, cache, q_obs, q_pos, n_obs, window, ws, stream=None) -> int:

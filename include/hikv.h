@@ -119,7 +119,10 @@ typedef struct hikv_debug {
 
 /* Bytes of device workspace the decode step and hikv_evict need for this
  * shape and policy.  The workspace must be zero-filled before its first use;
- * the library leaves it ready for the next call.  0 on a bad shape. */
+ * the library leaves it ready for the next call.  It also carries each
+ * unit's pending eviction (see hikv_decode_step) from one call to the next:
+ * use one workspace per cache, for every call on that cache.  0 on a bad
+ * shape. */
 size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
 
 /* One decode step for every unit ([HiKV] Algorithm 1 with [Blog] Sec. 3 H2O
@@ -137,6 +140,18 @@ size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
  *      pos > new_pos[b] - W') and the budget - |protected| other tokens with
  *      the highest (importance, then lower position); compact them into
  *      slots [0, budget); len[u] = budget.
+ * Pending eviction (Stage I, r == 0): when step 4 evicts exactly one token,
+ * the call leaves the choice of the victim to the next call and does not
+ * compact: len[u] stays budget + 1, and one of those slots, the victim, is
+ * dead (its row, position and importance are stale).  The next decode step
+ * neither attends to it nor counts it, and writes its new token there; a bulk
+ * cut (more than one token over budget) removes it first.  hikv_settle()
+ * resolves it (the cache then holds exactly the kept set, as in step 4) and
+ * hikv_pending() reports the dead slot without changing anything; the Stage II
+ * path and hikv_evict() settle first.  Results (out, the kept set once
+ * settled) are those of step 4 in every case.  A unit whose budget + 2
+ * exceeds the capacity therefore runs out of slots (HIKV_ECAPACITY) one call
+ * after it reaches its budget.
  * q: [B][Hq][D]; k_new, v_new: [B][Hkv][D]; new_pos: [B] int32;
  * out: [B][Hq][D] float32.  `debug` may be NULL. */
 int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
@@ -146,9 +161,25 @@ int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache, const hik
 
 /* Compress every unit over its budget to exactly its budget with step 4 of
  * hikv_decode_step, using the current importance; newest_pos[b] anchors the
- * recent window ([Blog] Sec. 3 H2O; [Kelle] Sec. 4.1, prefill eviction). */
+ * recent window ([Blog] Sec. 3 H2O; [Kelle] Sec. 4.1, prefill eviction).
+ * A pending eviction is settled first. */
 int hikv_evict(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
                const int32_t *newest_pos, void *ws, size_t ws_bytes, void *stream);
+
+/* Resolve every unit's pending eviction (see hikv_decode_step): the unit's
+ * last slot moves into the dead one (K and V rows, position, importance) and
+ * len[u] drops by one, which is the in-place compaction of step 4 ([Kelle]
+ * Sec. 2.2: slot order does not matter).  Units with none pending are left
+ * alone.  `policy` and `ws` are those of the decode steps on this cache.
+ * Call it before reading the cache directly or handing it to
+ * hikv_prefill_scores(). */
+int hikv_settle(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Write each unit's dead slot (-1 when no eviction is pending) to slot_out
+ * ([B][Hkv] int32, device) without changing the cache or the workspace. */
+int hikv_pending(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                 const void *ws, size_t ws_bytes, int32_t *slot_out, void *stream);
 
 /* Workspace bytes hikv_prefill_scores needs for n_obs observation queries. */
 size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t n_obs);

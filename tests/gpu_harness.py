@@ -57,6 +57,33 @@ class GpuRun:
                 sel_count=torch.full((sh.batch, n_q_heads), -7, dtype=torch.int32, device="cuda"))
             self.dbg = H.hikv_debug(*[self.dbg_t[f].data_ptr() for f in self.dbg_t])
 
+    def pending(self):
+        """Each unit's dead slot (-1: no eviction pending), read without changing anything."""
+        sh = self.dev.shape
+        out = torch.full((sh.batch, sh.n_kv_heads), -7, dtype=torch.int32, device="cuda")
+        H.check(H.hikv_pending(sh, self.dev.cache, self.pol, self.ws, out), "hikv_pending")
+        return out.cpu().numpy()
+
+    def state(self):
+        """The cache as the method defines it: the device state with every
+        pending eviction applied the way hikv_settle applies it (the unit's
+        last slot moves into the dead one), computed on the host so that the
+        device keeps running with its evictions pending."""
+        st = self.dev.to_numpy()
+        dead = self.pending()
+        for b in range(dead.shape[0]):
+            for j in range(dead.shape[1]):
+                d = int(dead[b, j])
+                if d < 0:
+                    continue
+                last = int(st["len"][b, j]) - 1
+                assert 0 <= d <= last, (b, j, d, last)
+                if d != last:
+                    for f in ("k", "v", "pos", "imp"):
+                        st[f][b, j, d] = st[f][b, j, last]
+                st["len"][b, j] = last
+        return st
+
     def step(self, q, k_new, v_new, new_pos, expect=H.HIKV_OK, hint_override=None):
         qt, kt, vt = H.to_device(q), H.to_device(k_new), H.to_device(v_new)
         pt = torch.from_numpy(np.ascontiguousarray(new_pos, dtype=np.int32)).cuda()
@@ -163,10 +190,10 @@ def lockstep(run: GpuRun, data, steps, *, tag="", start_state=None):
     worst = 0.0
     swaps = 0
     for t in range(steps):
-        pre = run.dev.to_numpy()
+        pre = run.state()
         say(f"[gpu] {tag} step {t}: decode_step B={pre['len'].shape[0]} Hkv={pre['len'].shape[1]}")
         out, dbg = run.step(data["q"][t], data["k_new"][t], data["v_new"][t], data["new_pos"][t])
-        post = run.dev.to_numpy()
+        post = run.state()
         st = ref.copy_state(pre)
         code, want, dref = ref.decode_step(st, run.Hq, data["q"][t], data["k_new"][t],
                                            data["v_new"][t], data["new_pos"][t], **run.kw)

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ("hikv_decode_step", "hikv_evict", "hikv_prefill_scores", "hikv_workspace_bytes",
-                 "hikv_device_status", "hikv_status_string"):
+    for want in ("hikv_decode_step", "hikv_evict", "hikv_settle", "hikv_pending", "hikv_prefill_scores",
+                 "hikv_workspace_bytes", "hikv_device_status", "hikv_status_string"):
         assert want in names
     assert set(names) == set(H.EXPORTS)
 
@@ -91,3 +91,12 @@ def test_decode_step_host_checks():
     neg_hint = np.array([10, -1, 3, 3], dtype=np.int32)
     assert call(_shape(), pol=H.make_policy(budget_all=8, len_hint=neg_hint)) == H.HIKV_EINVAL
     assert H.status_string(H.HIKV_ECAPACITY) == "cache capacity exceeded"
+    # settle / pending: host checks only (no device work is enqueued on error)
+    assert L.hikv_settle(C.byref(_shape()), C.byref(cache), C.byref(pol), None, 1 << 30, None) == H.HIKV_EINVAL
+    assert L.hikv_settle(C.byref(_shape()), C.byref(cache), C.byref(pol), fake, 16, None) == H.HIKV_EINVAL
+    assert L.hikv_settle(C.byref(_shape(head_dim=96)), C.byref(cache), C.byref(pol), fake, 1 << 30,
+                         None) == H.HIKV_EUNSUPPORTED
+    assert L.hikv_pending(C.byref(_shape()), C.byref(cache), C.byref(pol), fake, 1 << 30, None,
+                          None) == H.HIKV_EINVAL                                      # no output
+    assert L.hikv_settle(C.byref(_shape(batch=0)), C.byref(cache), C.byref(pol), fake, 1 << 30,
+                         None) == H.HIKV_OK

@@ -48,7 +48,7 @@ def test_tiny_free_running_matches_oracle():
                                      d["new_pos"][t], budget_all=w.budget_all, n_sink=w.n_sink,
                                      n_recent=w.n_recent)
         assert row_errors(out, want).max() <= 1e-5, t
-        g = run.dev.to_numpy()
+        g = run.state()
         assert list(ref.live_positions(g, 0, 0)) == list(ref.live_positions(st, 0, 0)), t
 
 
@@ -120,6 +120,63 @@ def test_wrong_host_length_hint_stage2_is_reported():
     wrong = np.full((1, 8), 99, dtype=np.int32)       # device holds 300 per unit
     run.step(d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], expect=H.HIKV_EINVAL,
              hint_override=wrong)
+
+
+def test_settle_applies_the_pending_eviction():
+    """Steps that leave an eviction pending, then hikv_settle: the device
+    cache becomes the settled view the harness computes (the unit's last slot
+    moved into the dead one), and nothing stays pending."""
+    w = W.workload("headkv32k", ctx=1500, steps=4, batch=2)
+    w.budgets = np.tile(W.dirichlet_budgets(91, 8, 8 * 100, 16, 500), (2, 1))
+    d = W.generate(w)
+    run = _run(w, d, hint=True)
+    lockstep(run, d, w.steps, tag="settle")
+    assert (run.pending() >= 0).any()              # the steady steps left evictions pending
+    view = run.state()
+    H.check(H.hikv_settle(run.dev.shape, run.dev.cache, run.pol, run.ws), "hikv_settle")
+    got = run.dev.to_numpy()
+    for f in ("k", "v", "pos", "imp", "len"):
+        assert np.array_equal(got[f], view[f]), f
+    assert (run.pending() == -1).all()
+
+
+def test_stage2_step_after_pending_eviction():
+    """A Stage II step on a cache whose last two-launch step left an eviction
+    pending settles it first: outputs and kept sets equal the oracle's."""
+    w = W.workload("llama8b", ctx=600, steps=3, batch=2)
+    w.budget_all, w.n_recent = 128, 16
+    d = W.generate(w)
+    st = ref.copy_state(d)
+    G = w.group
+    kw1 = dict(budget_all=w.budget_all, n_sink=w.n_sink, n_recent=w.n_recent)
+    kw2 = dict(kw1, stage2_channels=32, stage2_tokens=64)
+    # one workspace sized for both policies: the persistent part sits at fixed offsets
+    run = GpuRun(ref.copy_state(d), w.n_q_heads, budget_all=w.budget_all, n_sink=w.n_sink,
+                 n_recent=w.n_recent, r=32, kT=64)
+    pol1 = H.make_policy(None, w.budget_all, w.n_sink, w.n_recent)
+    for t in range(3):
+        q, kn, vn, npos = d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t]
+        stage2 = t == 2
+        if stage2:
+            out, _ = run.step(q, kn, vn, npos)
+        else:
+            qt, kt, vt = H.to_device(q), H.to_device(kn), H.to_device(vn)
+            pt = torch.from_numpy(np.ascontiguousarray(npos, dtype=np.int32)).cuda()
+            H.check(H.hikv_decode_step(run.dev.shape, run.dev.cache, pol1, qt, kt, vt, pt, run.out, run.ws))
+            assert H.hikv_device_status(run.ws) == 0
+            out = run.out.cpu().numpy()
+        code, want, _ = ref.decode_step(st, w.n_q_heads, q, kn, vn, npos, **(kw2 if stage2 else kw1))
+        assert code == 0
+        assert row_errors(out, want).max() <= OUT_TOL[w.dtype], t
+        if t == 1:
+            assert (run.pending() >= 0).all()       # steady Stage I step: pending everywhere
+        got = run.state()
+        assert np.array_equal(got["len"], st["len"]), t
+        for b in range(w.batch):
+            for j in range(w.n_kv_heads):
+                assert sorted(ref.live_positions(got, b, j).tolist()) == \
+                    sorted(ref.live_positions(st, b, j).tolist()), (t, b, j)
+    assert (run.pending() == -1).all()               # the Stage II step settled and evicted in place
 
 
 def test_llama8b_reduced_lockstep():
@@ -195,7 +252,7 @@ def test_stage2_r_equals_d_reduces_to_stage1():
     oa, _ = a.step(data["q"], data["k_new"], data["v_new"], data["new_pos"])
     ob, _ = b.step(data["q"], data["k_new"], data["v_new"], data["new_pos"])
     assert row_errors(ob, oa.astype(np.float64)).max() <= 1e-5
-    sa, sb = a.dev.to_numpy(), b.dev.to_numpy()
+    sa, sb = a.state(), b.state()
     for bb in range(B):
         for j in range(Hkv):
             assert list(ref.live_positions(sa, bb, j)) == list(ref.live_positions(sb, bb, j))
@@ -209,7 +266,7 @@ def test_edge_cases_streaming_zero_budget_errors():
     # unit 3 is full -> capacity error, unit left unchanged, zero output
     run = GpuRun(ref.copy_state(st), G * Hkv, budget=np.array([[0, 12, 12, 12]]), n_sink=0, n_recent=4)
     out, _ = run.step(data["q"], data["k_new"], data["v_new"], data["new_pos"], expect=H.HIKV_ECAPACITY)
-    post = run.dev.to_numpy()
+    post = run.state()
     assert post["len"].tolist() == [[0, 12, 12, 40]]   # budget 0 empties unit 0
     assert np.all(out[0, 6:8] == 0)
     for f in ("k", "v", "pos", "imp"):
@@ -219,7 +276,7 @@ def test_edge_cases_streaming_zero_budget_errors():
     d2 = W.random_step(16, B, G * Hkv, Hkv, D, W.BF16, st2["newest"])
     run2 = GpuRun(ref.copy_state(st2), G * Hkv, budget=np.array([[8, 2, 8, 8]]), n_sink=4, n_recent=2)
     run2.step(d2["q"], d2["k_new"], d2["v_new"], d2["new_pos"], expect=H.HIKV_EBUDGET)
-    assert run2.dev.to_numpy()["len"].tolist() == [[6, 20, 8, 8]]
+    assert run2.state()["len"].tolist() == [[6, 20, 8, 8]]
     # StreamingLLM: with contiguous history, budget = S + W keeps exactly the
     # sinks and the window, and matches the oracle
     lens3 = [35, 35, 35, 35]
@@ -231,7 +288,7 @@ def test_edge_cases_streaming_zero_budget_errors():
     d3 = {k: v[None] for k, v in W.random_step(14, B, G * Hkv, Hkv, D, W.BF16, 35).items()}
     run3 = GpuRun(ref.copy_state(st3), G * Hkv, budget_all=7, n_sink=3, n_recent=4)
     lockstep(run3, d3, 1, tag="streaming")
-    post3 = run3.dev.to_numpy()
+    post3 = run3.state()
     for j in range(Hkv):
         live = sorted(ref.live_positions(post3, 0, j).tolist())
         assert live == [0, 1, 2, 32, 33, 34, 35], (j, live)
@@ -249,7 +306,7 @@ def test_evict_standalone_matches_oracle():
         code = H.hikv_evict(run.dev.shape, run.dev.cache, run.pol, torch.from_numpy(newest).cuda(), run.ws)
         assert code == 0
         assert H.hikv_device_status(run.ws) == 0
-        post = run.dev.to_numpy()
+        post = run.state()
         want = ref.copy_state(st)
         c, dref = ref.evict(want, G * Hkv, newest, budget=budget, n_sink=1, n_recent=16)
         assert c == 0
@@ -281,7 +338,7 @@ def test_prefill_scores_match_oracle(window, n_obs):
                                  torch.from_numpy(qpos).cuda(), n_obs, window, ws)
     assert code == 0
     torch.cuda.synchronize()
-    got = run.dev.to_numpy()
+    got = run.state()
     want = ref.copy_state(st)
     assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=window) == 0
     np.testing.assert_allclose(got["imp"], want["imp"], rtol=2e-3, atol=2e-5)
@@ -299,7 +356,7 @@ def test_repeat_step_is_bit_identical():
             out, _ = run.step(d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t])
             o.append(out)
         outs.append(np.stack(o))
-        states.append(run.dev.to_numpy())
+        states.append(run.state())
     assert np.array_equal(outs[0], outs[1])
     for f in ("k", "v", "pos", "imp", "len"):
         assert np.array_equal(states[0][f], states[1][f]), f
@@ -324,10 +381,10 @@ def test_full_size_sampled_units(name):
     samples = [(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(3)]
     budget = w.budget_array()
     for t in range(w.steps):
-        pre = run.dev.to_numpy()
+        pre = run.state()
         say(f"[gpu] full-size {name} step {t}")
         out, _ = run.step(d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t])
-        post = run.dev.to_numpy()
+        post = run.state()
         newest = int(d["new_pos"][t, 0])
         # properties on every unit
         want_len = np.minimum(pre["len"] + 1, budget)
