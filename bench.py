@@ -106,18 +106,17 @@ def main():
         c = H.DeviceCache.__new__(H.DeviceCache)
         c.torch = torch
         c.dtype, c.shape = layers[0].dtype, layers[0].shape
-        for f in ("k", "v", "pos", "imp", "len"):
+        for f in ("k", "v", "pos", "imp", "len", "evict"):
             setattr(c, f, getattr(layers[0], f).clone())
-        c.cache = H.hikv_cache(c.k.data_ptr(), c.v.data_ptr(), c.pos.data_ptr(), c.imp.data_ptr(),
-                               c.len.data_ptr())
+        c.cache = c.make_cache()
         layers.append(c)
     budget_t = torch.from_numpy(budget).cuda()
     # per-KV-head budgets go as a device array; one budget for every unit as budget_all
     b_arr, b_all = (budget_t, 0) if w.budgets is not None else (None, w.budget_all)
     pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
-    # One workspace per layer copy: a workspace carries its cache's pending
-    # eviction from one step to the next.
-    wss = [H.workspace(layers[0].shape, pol) for _ in range(args.layers)]
+    # One workspace (scratch) serves every layer copy, as it would every layer
+    # of a model; each cache carries its own pending-eviction state.
+    wss = [H.workspace(layers[0].shape, pol)]
 
     def device_status(what):
         for wsl in wss:
@@ -140,8 +139,9 @@ def main():
         c = layers[li]
         n = layer_step[li]
         layer_step[li] += 1
-        # live tokens of the step (a pending eviction's dead slot is not one)
-        live_now = host_len[li] + 1 - (host_len[li] > budget)
+        # live tokens of the step (a pending eviction's dead slot is not one;
+        # the Stage II path evicts in place and leaves none pending)
+        live_now = host_len[li] + 1 - ((host_len[li] > budget) & (not stage2))
         live_log.append(int(live_now.sum()))
         moves_log.append(int((live_now > budget).sum()))
         p = pol
@@ -152,16 +152,19 @@ def main():
         if events is not None:
             dbg = H.hikv_debug(None, None, None, events[0].cuda_event, events[1].cuda_event)
         code = H.hikv_decode_step(c.shape, c.cache, p, q_all[n % n_inputs], kn_all[n % n_inputs],
-                                  vn_all[n % n_inputs], pos_all[n], out, wss[li], debug=dbg)
+                                  vn_all[n % n_inputs], pos_all[n], out, wss[0], debug=dbg)
         if code != 0:
             raise RuntimeError(f"hikv_decode_step: {H.status_string(code)}")
         # The caller's copy of len[] after the step: a unit over its budget by one
         # keeps budget + 1 slots with that eviction pending (the next step writes
         # its new token into the dead slot); a bulk cut leaves exactly the budget.
         old = host_len[li]
-        pending = old > budget
-        live = old + 1 - pending
-        host_len[li] = np.where(live > budget + 1, budget, np.where(pending, old, old + 1)).astype(np.int32)
+        if stage2:
+            host_len[li] = np.minimum(old + 1, budget).astype(np.int32)
+        else:
+            pending = old > budget
+            live = old + 1 - pending
+            host_len[li] = np.where(live > budget + 1, budget, np.where(pending, old, old + 1)).astype(np.int32)
 
     moves_log = []
     stream = torch.cuda.current_stream()
@@ -324,7 +327,7 @@ def kernel_text(w):
         return (f"k_attn_tiles<2,{w.head_dim},{w.group},false,true> (Stage II reduced-channel logits over "
                 "every live K row; HIP events per launch)")
     if w.el == 2 and w.head_dim == 128:
-        return (f"k_attend_mfma<{w.group}> (split-K attention over the live K/V rows on matrix cores; "
+        return (f"k_attend_mfma<{w.group},3> (split-K attention over the live K/V rows on matrix cores; "
                 "HIP events per launch)")
     return (f"k_attend<{w.el},{w.head_dim},{w.group}> (split-K attention over the live K/V rows; "
             "HIP events per launch)")

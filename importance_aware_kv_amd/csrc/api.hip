@@ -50,8 +50,8 @@ int check_policy(const hikv_shape *s, const hikv_policy *p) {
 }
 
 int check_cache(const hikv_cache *c) {
-  if (!c || !c->k || !c->v || !c->pos || !c->imp || !c->len) return HIKV_EINVAL;
-  if (!aligned16(c->k) || !aligned16(c->v)) return HIKV_EINVAL;
+  if (!c || !c->k || !c->v || !c->pos || !c->imp || !c->len || !c->evict) return HIKV_EINVAL;
+  if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->evict)) return HIKV_EINVAL;
   return HIKV_OK;
 }
 
@@ -79,6 +79,7 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
   a.pos = c->pos;
   a.imp = c->imp;
   a.len = c->len;
+  a.evict = c->evict;
   a.budget = p->budget;
   a.budget_all = p->budget_all;
   a.n_sink = p->n_sink;
@@ -99,6 +100,11 @@ bool multi_kernel_path() {
 }
 
 }  // namespace
+
+extern "C" size_t hikv_state_bytes(const hikv_shape *shape) {
+  if (check_shape(shape) != HIKV_OK) return 0;
+  return sizeof(int32_t) * (size_t)shape->batch * shape->n_kv_heads * (size_t)state_words(shape->capacity);
+}
 
 extern "C" size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy) {
   if (check_shape(shape) != HIKV_OK) return 0;
@@ -156,7 +162,7 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     if ((e = launch_attn_tiles(a, dt, true, false, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
   } else {
-    if ((e = launch_settle(a, dt, nullptr, true, s)) != hipSuccess) return dev_err(e);
+    // (the channel-select launch also settles a pending eviction first)
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);

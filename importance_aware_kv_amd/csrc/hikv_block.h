@@ -278,4 +278,59 @@ __device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int be
   if (tid == 0) *len_u = beta;
 }
 
+// ---------------------------------------------------------------------------
+// The cache's pending eviction (hikv_cache.evict; see the two-launch step):
+// the dead slot of unit u, or -1 when none is pending.  One whole wave; every
+// lane returns the slot.
+// ---------------------------------------------------------------------------
+__device__ inline int pending_slot_wave(const StepArgs &a, int u) {
+  const int lane = threadIdx.x & 63;
+  const int nbm = imp_blocks(a.cap);
+  const int32_t *rec = a.evict + (size_t)u * state_words(a.cap);
+  const int n = min(rec[0], nbm);
+  uint32_t khi = ~0u, klo = ~0u;
+  int slot = -1;
+  for (int i = lane; i < n; i += 64) {
+    const int4 e = reinterpret_cast<const int4 *>(rec + 4)[i];
+    const uint32_t h = (uint32_t)e.y, l = (uint32_t)e.x;
+    if (h < khi || (h == khi && l < klo)) khi = h, klo = l, slot = e.z;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t h = (uint32_t)__shfl_xor((int)khi, off), l = (uint32_t)__shfl_xor((int)klo, off);
+    const int s = __shfl_xor(slot, off);
+    if (h < khi || (h == khi && l < klo)) khi = h, klo = l, slot = s;
+  }
+  return (khi == ~0u && klo == ~0u) ? -1 : slot;
+}
+
+// Resolve unit u's pending eviction in place (one whole wave): the unit's
+// last slot moves into the dead one (K and V rows of rb bytes, position,
+// importance), len drops by one and nothing stays pending ([Kelle] Sec. 2.2:
+// slot order does not matter).
+__device__ inline void settle_unit(const StepArgs &a, int u, int rb) {
+  const int lane = threadIdx.x & 63;
+  int32_t *rec = a.evict + (size_t)u * state_words(a.cap);
+  if (rec[0] == 0) return;
+  const int d = pending_slot_wave(a, u);
+  if (d >= 0) {
+    const int last = a.len[u] - 1;
+    if (d != last) {
+      const int nc = rb / 16;  // 16-byte pieces of a row; one wave moves a K and a V row
+      char *base = static_cast<char *>(lane < nc ? a.k_w : a.v_w) + (size_t)u * a.cap * rb;
+      const int off = (lane % nc) * 16;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (lane < 2 * nc) x = *reinterpret_cast<const uint4 *>(base + (size_t)last * rb + off);
+      const int32_t p = a.pos[(size_t)u * a.cap + last];
+      const float im = a.imp[(size_t)u * a.cap + last];
+      if (lane < 2 * nc) *reinterpret_cast<uint4 *>(base + (size_t)d * rb + off) = x;
+      if (lane == 0) {
+        a.pos[(size_t)u * a.cap + d] = p;
+        a.imp[(size_t)u * a.cap + d] = im;
+      }
+    }
+    if (lane == 0) a.len[u] = last;
+  }
+  if (lane == 0) rec[0] = 0;
+}
+
 }  // namespace hikv

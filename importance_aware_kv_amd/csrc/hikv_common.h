@@ -18,13 +18,20 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kImpChunk = 2048;     // tokens per importance block of the step's second launch
 
 // Importance blocks per unit in the step's second launch.
-inline int imp_blocks(int cap) { return (cap + kImpChunk - 1) / kImpChunk; }
+__host__ __device__ inline int imp_blocks(int cap) { return (cap + kImpChunk - 1) / kImpChunk; }
+
+// Per-unit record of the cache's pending eviction (hikv_cache.evict), in
+// int32 words: [0] the number n of candidates (0: none pending), [1] the dead
+// slot as the attention launch of the current step found it, then from word 4
+// one 4-word candidate per importance block of the step that left it: the
+// block's lowest eviction key (low, high word) and that key's slot.
+__host__ __device__ inline int state_words(int cap) { return 4 * (imp_blocks(cap) + 1); }
 
 // ---------------------------------------------------------------------------
 // Workspace layout.  Offsets are 256-byte aligned; everything is derived from
 // the shape and policy alone, so the host can size it without the device.
-// The parts that persist between calls (status, the pending eviction) come
-// first, at offsets that depend on the shape only.
+// Scratch only (and a sticky status word): one workspace can serve every
+// cache of one shape, call after call on one stream.
 // ---------------------------------------------------------------------------
 struct Ws {
   int32_t *status;      // [1] sticky first device-side error
@@ -46,18 +53,11 @@ struct Ws {
   int32_t *tsel;        // [B*Hq][k_T] Stage II exact-softmax slots
   int32_t *tcount;      // [B*Hq]
   int32_t *urec;        // [n_units][4] per-unit plan of the step: first tile, tiles, tokens
-  int32_t *icand;       // [n_units][imp_blocks(cap)][4] per importance block of the last
-                        //   two-launch step: its lowest eviction key (low, high word) and
-                        //   that key's slot; persists between calls (pending eviction)
   uint64_t *bkeys;      // [n_units][cap] bulk eviction: every slot's eviction key
                         //   (UINT64_MAX for a protected token)
-  int32_t *pend;        // [n_units] eviction left pending by the last two-launch step: the
-                        //   number of its candidates in icand (0: none); persists between calls
-  int32_t *dslot;       // [n_units] the pending eviction's slot as the attention launch found
-                        //   it (-1: none), for the second launch of the same step
 };
 
-constexpr int kWsParts = 21;
+constexpr int kWsParts = 18;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -71,9 +71,6 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
   const size_t U = (size_t)B * Hkv, G = (size_t)(Hq / Hkv), MT = (size_t)max_tiles_for((int)U);
   const size_t sz[kWsParts] = {
       512,                             // status (+ spare)
-      sizeof(int32_t) * 4 * U * (size_t)imp_blocks(cap),  // icand
-      sizeof(int32_t) * U,             // pend
-      sizeof(int32_t) * U,             // dslot
       sizeof(int32_t) * 4 * MT,        // tinfo
       sizeof(float) * U,               // fz_newimp
       sizeof(uint32_t) * U,            // ticket
@@ -106,26 +103,23 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   char *b = static_cast<char *>(base);
   Ws w;
   w.status = reinterpret_cast<int32_t *>(b + s.off[0]);
-  w.icand = reinterpret_cast<int32_t *>(b + s.off[1]);
-  w.pend = reinterpret_cast<int32_t *>(b + s.off[2]);
-  w.dslot = reinterpret_cast<int32_t *>(b + s.off[3]);
-  w.tinfo = reinterpret_cast<int32_t *>(b + s.off[4]);
-  w.fz_newimp = reinterpret_cast<float *>(b + s.off[5]);
-  w.ticket = reinterpret_cast<uint32_t *>(b + s.off[6]);
-  w.plan = reinterpret_cast<int32_t *>(b + s.off[7]);
-  w.stats = reinterpret_cast<float *>(b + s.off[8]);
-  w.part_ml = reinterpret_cast<float *>(b + s.off[9]);
-  w.part_acc = reinterpret_cast<float *>(b + s.off[10]);
-  w.logits = reinterpret_cast<float *>(b + s.off[11]);
-  w.tile_key = reinterpret_cast<uint64_t *>(b + s.off[12]);
-  w.tile_slot = reinterpret_cast<int32_t *>(b + s.off[13]);
-  w.holes = reinterpret_cast<int32_t *>(b + s.off[14]);
-  w.movers = reinterpret_cast<int32_t *>(b + s.off[15]);
-  w.chmask = reinterpret_cast<uint32_t *>(b + s.off[16]);
-  w.tsel = reinterpret_cast<int32_t *>(b + s.off[17]);
-  w.tcount = reinterpret_cast<int32_t *>(b + s.off[18]);
-  w.urec = reinterpret_cast<int32_t *>(b + s.off[19]);
-  w.bkeys = reinterpret_cast<uint64_t *>(b + s.off[20]);
+  w.tinfo = reinterpret_cast<int32_t *>(b + s.off[1]);
+  w.fz_newimp = reinterpret_cast<float *>(b + s.off[2]);
+  w.ticket = reinterpret_cast<uint32_t *>(b + s.off[3]);
+  w.plan = reinterpret_cast<int32_t *>(b + s.off[4]);
+  w.stats = reinterpret_cast<float *>(b + s.off[5]);
+  w.part_ml = reinterpret_cast<float *>(b + s.off[6]);
+  w.part_acc = reinterpret_cast<float *>(b + s.off[7]);
+  w.logits = reinterpret_cast<float *>(b + s.off[8]);
+  w.tile_key = reinterpret_cast<uint64_t *>(b + s.off[9]);
+  w.tile_slot = reinterpret_cast<int32_t *>(b + s.off[10]);
+  w.holes = reinterpret_cast<int32_t *>(b + s.off[11]);
+  w.movers = reinterpret_cast<int32_t *>(b + s.off[12]);
+  w.chmask = reinterpret_cast<uint32_t *>(b + s.off[13]);
+  w.tsel = reinterpret_cast<int32_t *>(b + s.off[14]);
+  w.tcount = reinterpret_cast<int32_t *>(b + s.off[15]);
+  w.urec = reinterpret_cast<int32_t *>(b + s.off[16]);
+  w.bkeys = reinterpret_cast<uint64_t *>(b + s.off[17]);
   return w;
 }
 
@@ -148,6 +142,7 @@ struct StepArgs {
   int32_t *pos;
   float *imp;
   int32_t *len;
+  int32_t *evict;            // [U][state_words(cap)] pending eviction (cache state)
   const int32_t *budget;     // may be null
   int32_t budget_all, n_sink, n_recent;
   int32_t r, kT;             // Stage II

@@ -41,6 +41,13 @@ __device__ __forceinline__ bool unit_has_tiles(const StepArgs &a, int u) {
 __global__ __launch_bounds__(64) void k_stage2_channels(StepArgs a, int el) {
   const int bh = blockIdx.x, lane = threadIdx.x;
   const int D = a.D;
+  // This path evicts in place: the first q-head of each KV group resolves an
+  // eviction a two-launch step left pending on the unit, before any launch
+  // that reads the cache.
+  {
+    const int b = bh / a.Hq, h = bh - b * a.Hq;
+    if (h % a.G == 0) settle_unit(a, b * a.Hkv + h / a.G, D * el);
+  }
   const uint32_t v0 = __float_as_uint(load_abs(a.q, (size_t)bh * D + lane, el));
   const uint32_t v1 = D > 64 ? __float_as_uint(load_abs(a.q, (size_t)bh * D + 64 + lane, el)) : 0u;
   const bool has1 = D > 64;

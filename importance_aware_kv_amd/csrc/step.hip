@@ -435,52 +435,58 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 
 // ---------------------------------------------------------------------------
 // Pending eviction.  A two-launch step that evicts one token leaves the choice
-// of the victim to the next call: it stores, per unit, the number n of its
-// importance blocks (pend[u]) and each block's lowest eviction key and its
-// slot (icand[u][i], i < n).  The evicted slot is the one whose key is the
-// smallest; until a later call resolves it, the slot is dead.
+// of the victim to the next call: it stores, in the unit's record of the
+// cache's pending-eviction state (hikv_cache.evict), the number n of its
+// importance blocks and each block's lowest eviction key and its slot.  The
+// evicted slot is the one whose key is the smallest; until a later call
+// resolves it, the slot is dead.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int pend_stride(const StepArgs &a) { return (a.cap + kImpChunk - 1) / kImpChunk; }
+__device__ __forceinline__ int pend_stride(const StepArgs &a) { return imp_blocks(a.cap); }
+// The unit's record: [0] count, [1] dead slot, candidates from word 4.
+__device__ __forceinline__ int32_t *unit_state(const StepArgs &a, int u) {
+  return a.evict + (size_t)u * state_words(a.cap);
+}
 
-// The lookup in the attention launch goes through LDS: the count (every lane
-// of wave 0 fetches the same word) and up to 64 candidates per round.
+// The lookup in the attention launch goes through LDS, 64 records of 16 bytes
+// at a time: lane 0 fetches the header (count, slot) and lanes 1..63 the
+// first 63 candidates; later rounds fetch 64 candidates each.
 struct PendLds {
-  int32_t cnt[kWave];
-  int32_t cand[kWave][4];
+  int32_t rec[kWave][4];
   int32_t dead[4];
 };
 
-// Wave 0 of a tile, before its first rows: the count and the first 64
-// candidates of unit u, by DMA (no register loads whose waits the compiler
-// would place), issued ahead of the rows so that the first wait covers them.
+// Wave 0 of a tile, before its first rows: the first 16-byte records of unit
+// u's state, by DMA (no register loads whose waits the compiler would place),
+// issued ahead of the rows so that the first wait covers them.
 __device__ __forceinline__ void pend_fetch(const StepArgs &a, int u, PendLds &pd, int lane) {
   const int nbm = pend_stride(a);
-  __builtin_amdgcn_global_load_lds(a.ws.pend + u, &pd.cnt[0], 4, 0, 0);
-  __builtin_amdgcn_global_load_lds(a.ws.icand + ((size_t)u * nbm + min(lane, nbm - 1)) * 4, &pd.cand[0][0], 16, 0,
-                                   0);
+  const int32_t *rec = unit_state(a, u);
+  __builtin_amdgcn_global_load_lds(rec + 4 * min(lane, nbm), &pd.rec[0][0], 16, 0, 0);
 }
 
 // Wave 0, once the fetch has landed: the dead slot (-1 if none), left in
 // pd.dead[0] for the other waves of the tile; with record, also stored for
-// the second launch of the step.  More than 64 candidates take a round trip
+// the second launch of the step.  More than 63 candidates take a round trip
 // per further 64.
 __device__ __forceinline__ int pend_resolve(const StepArgs &a, int u, PendLds &pd, int lane, bool record) {
   const int nbm = pend_stride(a);
   int n;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(n) : "v"(lds_addr(&pd.cnt[0])) : "memory");
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(n) : "v"(lds_addr(&pd.rec[0][0])) : "memory");
   n = __builtin_amdgcn_readfirstlane(min(n, nbm));
   uint64_t key = ~0ull;
   int slot = -1;
-  for (int base = 0; base < n; base += kWave) {
+  // Record r (r >= 1) of the state is candidate r - 1; round base holds
+  // records base .. base + 63.
+  for (int base = 0; base <= n; base += kWave) {
     if (base > 0) {
-      __builtin_amdgcn_global_load_lds(a.ws.icand + ((size_t)u * nbm + min(base + lane, nbm - 1)) * 4,
-                                       &pd.cand[0][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(unit_state(a, u) + 4 * min(base + lane, nbm), &pd.rec[0][0], 16, 0, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     u32x4 e;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(e) : "v"(lds_addr(&pd.cand[lane][0])) : "memory");
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(e) : "v"(lds_addr(&pd.rec[lane][0])) : "memory");
+    const int r = base + lane;
     const uint64_t k = ((uint64_t)e.y << 32) | e.x;
-    if (base + lane < n && k < key) {
+    if (r >= 1 && r <= n && k < key) {
       key = k;
       slot = (int)e.z;
     }
@@ -489,7 +495,7 @@ __device__ __forceinline__ int pend_resolve(const StepArgs &a, int u, PendLds &p
   const int d = (key == ~0ull) ? -1 : slot;
   if (lane == 0) {
     pd.dead[0] = d;
-    if (record) store_agent(a.ws.dslot + u, d);
+    if (record) store_agent(unit_state(a, u) + 1, d);
   }
   // The LDS write is complete before the barrier that follows (a DMA barrier
   // does not wait for LDS operations).
@@ -1258,7 +1264,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
       const float *lg = a.ws.logits + (size_t)u * a.cap * G;
       const int len_dev = ld_vec(a.len + u, vz);
-      const int dead_ld = ld_vec(a.ws.dslot + u, vz);
+      const int dead_ld = ld_vec(unit_state(a, u) + 1, vz);
       const int rt = tid % (2 * NR);
       const uint4 nrow = *reinterpret_cast<const uint4 *>(rt < NR ? kn + rt * 16 : vn + (rt - NR) * 16);
       float tl[NB][G], ti[NB];
@@ -1366,7 +1372,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
             if (dead < 0) a.len[u] = L;
           }
         }
-        int32_t *cand = a.ws.icand + (size_t)u * pend_stride(a) * 4;
+        int32_t *cand = unit_state(a, u) + 4;
         if (n_evict == 1) {
           // The eviction stays pending: each block leaves its lowest key.
           if (wave == 0) {
@@ -1377,11 +1383,11 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
               cand[4 * r] = (int32_t)(uint32_t)kk;
               cand[4 * r + 1] = (int32_t)(uint32_t)(kk >> 32);
               cand[4 * r + 2] = vs;
-              if (r == 0) a.ws.pend[u] = nact;
+              if (r == 0) unit_state(a, u)[0] = nact;
             }
           }
         } else if (r == 0 && tid == 0) {
-          a.ws.pend[u] = 0;
+          unit_state(a, u)[0] = 0;
         }
         return;
       }
@@ -1395,7 +1401,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       if (tid == 0) {
         impw[Lold] = newimp;
         posw[Lold] = newest;
-        a.ws.pend[u] = 0;
+        unit_state(a, u)[0] = 0;
       }
       __syncthreads();  // every key is stored
       __shared__ uint32_t hist[256];
@@ -1452,58 +1458,18 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
 // rows, position, importance) and len drops by one, as if the step had
 // evicted in place.
 // ---------------------------------------------------------------------------
-template <int RB>
-__global__ __launch_bounds__(kWave) void k_settle(StepArgs a, int32_t *slot_out, int apply) {
-  const int u = blockIdx.x, lane = threadIdx.x;
-  const int nbm = pend_stride(a);
-  const int n = min(__builtin_amdgcn_readfirstlane(a.ws.pend[u]), nbm);
-  const int4 *ic = reinterpret_cast<const int4 *>(a.ws.icand) + (size_t)u * nbm;
-  uint64_t key = ~0ull;
-  int slot = -1;
-  for (int i = lane; i < n; i += kWave) {
-    const int4 e = ic[i];
-    const uint64_t k = ((uint64_t)(uint32_t)e.y << 32) | (uint32_t)e.x;
-    if (k < key) {
-      key = k;
-      slot = e.z;
-    }
+__global__ __launch_bounds__(kWave) void k_settle(StepArgs a, int32_t *slot_out, int apply, int rb) {
+  const int u = blockIdx.x;
+  if (slot_out) {
+    const int d = pending_slot_wave(a, u);
+    if (threadIdx.x == 0) slot_out[u] = d;
   }
-  wave_min_key(key, slot);
-  const int d = (key == ~0ull) ? -1 : slot;
-  if (slot_out && lane == 0) slot_out[u] = d;
-  if (!apply || n == 0) return;
-  if (d >= 0) {
-    const int last = a.len[u] - 1;
-    if (d != last) {
-      static_assert(2 * RB <= kWave * 16, "one wave moves a K and a V row");
-      char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
-      char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
-      char *base = lane < RB / 16 ? kw : vw;
-      const int off = (lane % (RB / 16)) * 16;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (lane < 2 * (RB / 16)) x = *reinterpret_cast<const uint4 *>(base + (size_t)last * RB + off);
-      const int32_t p = a.pos[(size_t)u * a.cap + last];
-      const float im = a.imp[(size_t)u * a.cap + last];
-      if (lane < 2 * (RB / 16)) *reinterpret_cast<uint4 *>(base + (size_t)d * RB + off) = x;
-      if (lane == 0) {
-        a.pos[(size_t)u * a.cap + d] = p;
-        a.imp[(size_t)u * a.cap + d] = im;
-      }
-    }
-    if (lane == 0) a.len[u] = last;
-  }
-  if (lane == 0) a.ws.pend[u] = 0;
+  if (apply) settle_unit(a, u, rb);
 }
 
 hipError_t launch_settle(const StepArgs &a, int dtype, int32_t *slot_out, bool apply, hipStream_t s) {
   const int rb = a.D * (dtype == HIKV_BF16 ? 2 : 4);
-  const dim3 grid((unsigned)a.n_units), block(kWave);
-  switch (rb) {
-    case 128: hipLaunchKernelGGL(k_settle<128>, grid, block, 0, s, a, slot_out, apply ? 1 : 0); break;
-    case 256: hipLaunchKernelGGL(k_settle<256>, grid, block, 0, s, a, slot_out, apply ? 1 : 0); break;
-    case 512: hipLaunchKernelGGL(k_settle<512>, grid, block, 0, s, a, slot_out, apply ? 1 : 0); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(k_settle, dim3((unsigned)a.n_units), dim3(kWave), 0, s, a, slot_out, apply ? 1 : 0, rb);
   return hipGetLastError();
 }
 

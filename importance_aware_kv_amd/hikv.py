@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, "libhikv.so")
 HIKV_F32, HIKV_BF16 = 0, 1
 HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
 
-EXPORTS = ("hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_settle", "hikv_pending",
+EXPORTS = ("hikv_state_bytes", "hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_settle", "hikv_pending",
            "hikv_prefill_workspace_bytes", "hikv_prefill_scores", "hikv_device_status", "hikv_status_string")
 
 
@@ -32,7 +32,7 @@ class hikv_shape(C.Structure):
 
 class hikv_cache(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("pos", C.c_void_p), ("imp", C.c_void_p),
-                ("len", C.c_void_p)]
+                ("len", C.c_void_p), ("evict", C.c_void_p)]
 
 
 class hikv_policy(C.Structure):
@@ -62,6 +62,8 @@ def lib():
         L = C.CDLL(LIB_PATH)
         P = C.POINTER
         vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        L.hikv_state_bytes.argtypes = [P(hikv_shape)]
+        L.hikv_state_bytes.restype = sz
         L.hikv_workspace_bytes.argtypes = [P(hikv_shape), P(hikv_policy)]
         L.hikv_workspace_bytes.restype = sz
         L.hikv_decode_step.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, vp, vp,
@@ -117,6 +119,10 @@ def status_string(code: int) -> str:
 def check(code: int, what: str = "hikv call"):
     if code != HIKV_OK:
         raise RuntimeError(f"{what} failed: {code} ({status_string(code)})")
+
+
+def hikv_state_bytes(shape: hikv_shape) -> int:
+    return lib().hikv_state_bytes(C.byref(shape))
 
 
 def hikv_workspace_bytes(shape: hikv_shape, policy: Optional[hikv_policy]) -> int:
@@ -176,8 +182,16 @@ class DeviceCache:
         self.pos = torch.from_numpy(np.ascontiguousarray(state["pos"])).to(device)
         self.imp = torch.from_numpy(np.ascontiguousarray(state["imp"])).to(device)
         self.len = torch.from_numpy(np.ascontiguousarray(state["len"])).to(device)
-        self.cache = hikv_cache(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(),
-                                self.imp.data_ptr(), self.len.data_ptr())
+        # the pending-eviction state: zero (nothing pending) with a fresh cache
+        n = hikv_state_bytes(self.shape)
+        if n == 0:
+            raise RuntimeError("invalid cache shape")
+        self.evict = torch.zeros((n + 15) // 16 * 4, dtype=torch.int32, device=device)
+        self.cache = self.make_cache()
+
+    def make_cache(self) -> "hikv_cache":
+        return hikv_cache(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(),
+                          self.imp.data_ptr(), self.len.data_ptr(), self.evict.data_ptr())
 
     def _to(self, a, device):
         t = self.torch.from_numpy(np.ascontiguousarray(a))
@@ -203,6 +217,7 @@ class DeviceCache:
             getattr(self, name).copy_(src)
         for name in ("pos", "imp", "len"):
             getattr(self, name).copy_(self.torch.from_numpy(np.ascontiguousarray(state[name])))
+        self.evict.zero_()  # a host state has no eviction pending
 
 
 def to_device(a: np.ndarray, device="cuda"):

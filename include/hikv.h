@@ -84,6 +84,8 @@ typedef struct hikv_cache {
   int32_t *pos;   /* [B][Hkv][capacity] */
   float *imp;     /* [B][Hkv][capacity] cumulative importance ([Blog] Sec. 3 H2O) */
   int32_t *len;   /* [B][Hkv] */
+  int32_t *evict; /* the cache's pending-eviction state (see hikv_decode_step): hikv_state_bytes()
+                     bytes, 16-byte aligned, zero-filled together with a fresh cache */
 } hikv_cache;
 
 typedef struct hikv_policy {
@@ -117,12 +119,15 @@ typedef struct hikv_debug {
                               pass over every live K row) */
 } hikv_debug;
 
+/* Bytes of hikv_cache.evict for this shape (a few words per unit).  0 on a
+ * bad shape. */
+size_t hikv_state_bytes(const hikv_shape *shape);
+
 /* Bytes of device workspace the decode step and hikv_evict need for this
  * shape and policy.  The workspace must be zero-filled before its first use;
- * the library leaves it ready for the next call.  It also carries each
- * unit's pending eviction (see hikv_decode_step) from one call to the next:
- * use one workspace per cache, for every call on that cache.  0 on a bad
- * shape. */
+ * the library leaves it ready for the next call.  It holds scratch only (and
+ * the status word): one workspace serves every cache of the shape, for calls
+ * ordered on one stream.  0 on a bad shape. */
 size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
 
 /* One decode step for every unit ([HiKV] Algorithm 1 with [Blog] Sec. 3 H2O
@@ -143,7 +148,8 @@ size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
  * Pending eviction (Stage I, r == 0): when step 4 evicts exactly one token,
  * the call leaves the choice of the victim to the next call and does not
  * compact: len[u] stays budget + 1, and one of those slots, the victim, is
- * dead (its row, position and importance are stale).  The next decode step
+ * dead (its row, position and importance are stale); the choice is kept in
+ * cache->evict.  The next decode step
  * neither attends to it nor counts it, and writes its new token there; a bulk
  * cut (more than one token over budget) removes it first.  hikv_settle()
  * resolves it (the cache then holds exactly the kept set, as in step 4) and
@@ -171,6 +177,8 @@ int hikv_evict(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
  * len[u] drops by one, which is the in-place compaction of step 4 ([Kelle]
  * Sec. 2.2: slot order does not matter).  Units with none pending are left
  * alone.  `policy` and `ws` are those of the decode steps on this cache.
+ * The pending state is part of the cache, so it stays with the cache across
+ * workspaces.
  * Call it before reading the cache directly or handing it to
  * hikv_prefill_scores(). */
 int hikv_settle(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,

@@ -63,7 +63,7 @@ def test_decode_step_host_checks():
     L = H.lib()
     pol = H.make_policy(budget_all=32, n_sink=4, n_recent=8)
     fake = C.c_void_p(0x1000)
-    cache = H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    cache = H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
 
     def call(shape, cache=cache, pol=pol, q=fake, ws=fake, ws_bytes=1 << 30):
         return L.hikv_decode_step(C.byref(shape), C.byref(cache), C.byref(pol), q, fake, fake, fake,
@@ -73,7 +73,13 @@ def test_decode_step_host_checks():
     assert call(_shape(head_dim=96)) == H.HIKV_EUNSUPPORTED
     assert call(_shape(n_q_heads=48, n_kv_heads=3)) == H.HIKV_EUNSUPPORTED          # G = 16
     assert call(_shape(batch=4096, n_kv_heads=2, n_q_heads=2)) == H.HIKV_EUNSUPPORTED  # units
-    assert call(_shape(), cache=H.hikv_cache(0, 0x1000, 0x1000, 0x1000, 0x1000)) == H.HIKV_EINVAL
+    assert call(_shape(), cache=H.hikv_cache(0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)) == H.HIKV_EINVAL
+    assert call(_shape(), cache=H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0)) == H.HIKV_EINVAL
+    assert call(_shape(), cache=H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1004)) == H.HIKV_EINVAL
+    # pending-eviction state: 4 words per unit plus 4 per 2048-slot importance block
+    assert H.hikv_state_bytes(_shape()) == 4 * 2 * 2 * 8
+    assert H.hikv_state_bytes(_shape(capacity=5000)) == 4 * 2 * 2 * 16
+    assert H.hikv_state_bytes(_shape(head_dim=96)) == 0
     assert call(_shape(), q=None) == H.HIKV_EINVAL
     assert call(_shape(), q=C.c_void_p(0x1008)) == H.HIKV_EINVAL                    # alignment
     assert call(_shape(), ws_bytes=16) == H.HIKV_EINVAL                             # workspace
