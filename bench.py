@@ -147,6 +147,7 @@ def main():
         p = pol
         if not args.no_hint:
             p = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
+                              budget_hint=budget if b_arr is not None else None,
                               len_hint=host_len[li])
         dbg = None
         if events is not None:

@@ -154,6 +154,17 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   if (a.r == 0) {
     if (!multi_kernel_path()) {
       if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
+      // With host copies of the lengths and budgets, a step that cuts some
+      // unit by more than one token moves its survivors in a launch of its own.
+      if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
+        const int U = shape->batch * shape->n_kv_heads;
+        for (int u = 0; u < U; ++u) {
+          const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
+          const int len = policy->len_hint[u];
+          const int live = len + 1 - (len > beta ? 1 : 0);  // a unit over budget holds a dead slot
+          if (live - beta > 1) a.bulk_split = 1;
+        }
+      }
       return dev_err(launch_step(a, dt, s, ev0, ev1));
     }
     // The four-launch path evicts in place: an eviction a two-launch step

@@ -200,12 +200,14 @@ __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint
 // the n_evict smallest keys are evicted, then the survivors at or above the
 // budget move into the evicted slots below it (K and V rows of RB bytes,
 // position, importance), and *len_u = beta.  holes and movers are the unit's
-// [cap] lists in the workspace.  Every thread of the workgroup calls it.
+// [cap] lists in the workspace.  With nmoves_u given, the moves are left to a
+// later launch: the number of rows to move goes to *nmoves_u instead.  Every
+// thread of the workgroup calls it.
 template <int NT, int RB>
 __device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int beta, int n_evict, char *kw, char *vw,
                              int32_t *posw, float *impw, int32_t *holes, int32_t *movers,
                              int32_t *len_u, int32_t *status, uint32_t *hist, uint32_t *whist, int *sc,
-                             RadixState *rs) {
+                             RadixState *rs, int32_t *nmoves_u = nullptr) {
   const int tid = threadIdx.x;
   radix_select_keys<NT, 8>(keys, L, n_evict, hist, whist, rs);
   const uint64_t lim = rs->prefix >> rs->shift;
@@ -247,6 +249,13 @@ __device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int be
   __syncthreads();
   if (tot_h != tot_m) {  // cannot happen for distinct positions; fail safe
     if (tid == 0) set_status(status, HIKV_EINVAL);
+    return;
+  }
+  if (nmoves_u) {
+    if (tid == 0) {
+      *nmoves_u = tot_m;
+      *len_u = beta;
+    }
     return;
   }
   // A round copies two groups of NT / CPR rows, CPR threads per row, with

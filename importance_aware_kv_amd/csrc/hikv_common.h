@@ -55,9 +55,10 @@ struct Ws {
   int32_t *urec;        // [n_units][4] per-unit plan of the step: first tile, tiles, tokens
   uint64_t *bkeys;      // [n_units][cap] bulk eviction: every slot's eviction key
                         //   (UINT64_MAX for a protected token)
+  int32_t *nmoves;      // [n_units] bulk eviction: rows the move launch relocates (0: none)
 };
 
-constexpr int kWsParts = 18;
+constexpr int kWsParts = 19;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -88,6 +89,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
       sizeof(int32_t) * B * Hq,        // tcount
       sizeof(int32_t) * 4 * U,         // urec
       sizeof(uint64_t) * U * cap,      // bkeys
+      sizeof(int32_t) * U,             // nmoves
   };
   WsSizes w;
   size_t o = 0;
@@ -120,6 +122,7 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.tcount = reinterpret_cast<int32_t *>(b + s.off[15]);
   w.urec = reinterpret_cast<int32_t *>(b + s.off[16]);
   w.bkeys = reinterpret_cast<uint64_t *>(b + s.off[17]);
+  w.nmoves = reinterpret_cast<int32_t *>(b + s.off[18]);
   return w;
 }
 
@@ -147,6 +150,7 @@ struct StepArgs {
   int32_t budget_all, n_sink, n_recent;
   int32_t r, kT;             // Stage II
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
+  int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;
   float *out;

@@ -1217,6 +1217,9 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   // output block.
   const int nib = (int)gridDim.y - NOC;  // importance blocks per unit
   const int u = blockIdx.x, r = blockIdx.y;
+  // The move launch that may follow reads every unit's count: none unless a
+  // bulk cut below says otherwise (the same thread writes both).
+  if (a.bulk_split && r == 0 && tid == 0) a.ws.nmoves[u] = 0;
   // The host plan's words (kernel arguments, clamped to its table) are loaded
   // with the flag that says whether there is one, so that the host plan costs
   // one round trip; the device plan's path uses them too, after its own load,
@@ -1409,7 +1412,8 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       __shared__ int sc[kT2];
       __shared__ RadixState rs;
       bulk_compact<kT2, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
-                            a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs);
+                            a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs,
+                            a.bulk_split ? a.ws.nmoves + u : nullptr);
     }();
     end_wave();
   }
@@ -1449,6 +1453,49 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   }
 
   end_wave();
+}
+
+// ---------------------------------------------------------------------------
+// Third launch of a step that cuts units in bulk (when the host can tell): the
+// rows the second launch listed move from above the budget into the evicted
+// slots below it (K and V rows, position, importance), spread over gridDim.y
+// workgroups per unit.  Hole and mover lists pair up in order; every source
+// and destination is distinct, so the moves are independent.
+// ---------------------------------------------------------------------------
+template <int RB>
+__global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
+  constexpr int CPR = RB / 16, RPP = 256 / CPR;  // threads per row, rows per pass
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int nm = a.ws.nmoves[u];
+  const int per = (nm + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int i0 = (int)blockIdx.y * per, i1 = min(nm, i0 + per);
+  if (i0 >= i1) return;
+  const int ci = tid % CPR, rr = tid / CPR;
+  const int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
+  char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
+  char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
+  int32_t *posw = a.pos + (size_t)u * a.cap;
+  float *impw = a.imp + (size_t)u * a.cap;
+  // Two rows per thread group in flight: every load of a pass before its stores.
+  for (int i = i0 + rr; i < i1; i += 2 * RPP) {
+    const int ib = i + RPP;
+    const int jb = min(ib, i1 - 1);
+    const int sa = movers[i], da = holes[i], sb = movers[jb], db = holes[jb];
+    const uint4 ka = reinterpret_cast<const uint4 *>(kw + (size_t)sa * RB)[ci];
+    const uint4 va = reinterpret_cast<const uint4 *>(vw + (size_t)sa * RB)[ci];
+    const uint4 kb = reinterpret_cast<const uint4 *>(kw + (size_t)sb * RB)[ci];
+    const uint4 vb = reinterpret_cast<const uint4 *>(vw + (size_t)sb * RB)[ci];
+    const int pa = posw[sa], pb = posw[sb];
+    const float xa = impw[sa], xb = impw[sb];
+    reinterpret_cast<uint4 *>(kw + (size_t)da * RB)[ci] = ka;
+    reinterpret_cast<uint4 *>(vw + (size_t)da * RB)[ci] = va;
+    if (ci == 0) posw[da] = pa, impw[da] = xa;
+    if (ib < i1) {
+      reinterpret_cast<uint4 *>(kw + (size_t)db * RB)[ci] = kb;
+      reinterpret_cast<uint4 *>(vw + (size_t)db * RB)[ci] = vb;
+      if (ci == 0) posw[db] = pb, impw[db] = xb;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1530,7 +1577,14 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   }
   hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)a.n_units, (unsigned)(nib + k2_noc<EL, D, G>())),
                      dim3(kT2), 0, s, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.bulk_split) {
+    // 128 workgroups per unit: at most a few passes of 16 rows each for the
+    // largest cuts.
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, 128u), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int EL, int D>

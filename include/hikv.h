@@ -105,6 +105,11 @@ typedef struct hikv_policy {
                               capacity or len < 0 is rejected (HIKV_EINVAL); a hint that
                               disagrees with the device's len[] sets HIKV_EINVAL in the
                               device status and that call's results are undefined. */
+  const int32_t *budget_hint; /* optional HOST copy of budget[] (used with len_hint when budget
+                              is not NULL), or NULL.  With both copies the host can tell a step
+                              that cuts a unit by more than one token (the first step after a
+                              prefill): the survivors' rows are then moved by a launch of many
+                              workgroups per unit instead of one.  Results never depend on it. */
 } hikv_policy;
 
 /* Optional outputs of hikv_decode_step for tests, inspection and profiling;

@@ -93,7 +93,7 @@ class GpuRun:
             # the caller's own copy of len[] (here read back from the device)
             hint = (np.ascontiguousarray(self.dev.len.cpu().numpy(), dtype=np.int32)
                     if hint_override is None else np.ascontiguousarray(hint_override, dtype=np.int32))
-            pol = H.make_policy(*self.pol_args, len_hint=hint)
+            pol = H.make_policy(*self.pol_args, len_hint=hint, budget_hint=self.budget_np)
         code = H.hikv_decode_step(self.dev.shape, self.dev.cache, pol, qt, kt, vt, pt, self.out,
                                   self.ws, debug=self.dbg)
         assert code == H.HIKV_OK, H.status_string(code)
