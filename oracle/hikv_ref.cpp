@@ -160,6 +160,7 @@ void evict_unit(const Dims &d, const Unit &x, const hikv_ref_policy *pol, int be
 
 bool policy_ok(const Dims &d, const hikv_ref_policy *pol) {
   if (!pol || pol->n_sink < 0 || pol->n_recent < 0) return false;
+  if (pol->accumulate != HIKV_REF_ACC_ALL && pol->accumulate != HIKV_REF_ACC_RECENT) return false;
   if (pol->stage2_channels < 0 || pol->stage2_channels > d.D) return false;
   if (pol->stage2_channels > 0 && pol->stage2_tokens < 1) return false;
   return true;
@@ -287,9 +288,13 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
         for (int c = 0; c < d.D; ++c) out[((size_t)b * d.Hq + h) * d.D + c] = (float)o[c];
       }
 
-      // Accumulate: every live token gets the probability it received.
+      // Accumulate: every live token gets the probability it received, or,
+      // with the HiKV dual bank, only the tokens of the recent window (the
+      // window eviction protects); older scores stay frozen.
+      const int Wacc = std::min(pol->n_recent, beta - pol->n_sink);
       double total = 0.0;
       for (int n = 0; n < L; ++n) {
+        if (pol->accumulate == HIKV_REF_ACC_RECENT && !(x.pos[n] > new_pos[b] - Wacc)) continue;
         x.imp[n] = (float)((double)x.imp[n] + added[n]);
         total += added[n];
       }

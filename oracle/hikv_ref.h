@@ -23,6 +23,10 @@
  *    matter), Sec. 4.1 (per-head eviction by accumulated attention; prefill
  *    importance as attention column sums; initial and recent tokens kept).
  *  - Not All Heads Matter (HeadKV), Sec. 3.2 (per-head budgets).
+ *  - HiKV Sec. III-B (dual bank: the score of a token sums the probabilities
+ *    it receives while in the recent bank, then stays frozen; promotion into
+ *    the important bank iff that score beats the bank's lowest) and
+ *    Sec. III-D (bank initialisation from windowed prompt scores).
  */
 #ifndef HIKV_REF_H
 #define HIKV_REF_H
@@ -55,11 +59,22 @@ typedef struct {
   int32_t *len;     /* [B][Hkv] live slots are [0, len) */
 } hikv_ref_cache;
 
+/* Which tokens a step's attention probabilities are added to.
+ * ALL: every live token (H2O's cumulative score).
+ * RECENT: only the W' = min(n_recent, budget - n_sink) newest positions (the
+ * protected window); everything older keeps a frozen score.  With n_sink 0
+ * and n_recent = budget / 2 this is HiKV's dual bank (Sec. III-B): the window
+ * is the recent bank, the rest the important bank, and each token's score is
+ * the sum of the W' probabilities it received from its own step on. */
+#define HIKV_REF_ACC_ALL 0
+#define HIKV_REF_ACC_RECENT 1
+
 typedef struct {
   const int32_t *budget; /* [B][Hkv] or NULL -> budget_all */
   int32_t budget_all, n_sink, n_recent;
   int32_t stage2_channels; /* r; 0 = Stage II off */
   int32_t stage2_tokens;   /* tokens kept for the exact softmax (k_T) */
+  int32_t accumulate;      /* HIKV_REF_ACC_ALL | HIKV_REF_ACC_RECENT */
 } hikv_ref_policy;
 
 /* Optional per-step debug outputs; any pointer may be NULL. */

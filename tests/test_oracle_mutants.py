@@ -40,6 +40,14 @@ MUTANTS = [
      "  return elem(x.k, d.dtype, (size_t)n * d.D + c);"),
     ("stage2_tokens_tie_by_higher_pos", "            return x.pos[a] < x.pos[bb];",
      "            return x.pos[a] > x.pos[bb];"),
+    ("dual_bank_accumulates_everywhere",
+     "if (pol->accumulate == HIKV_REF_ACC_RECENT && !(x.pos[n] > new_pos[b] - Wacc)) continue;", ""),
+    ("dual_bank_window_off_by_one", "!(x.pos[n] > new_pos[b] - Wacc)", "!(x.pos[n] >= new_pos[b] - Wacc)"),
+    ("dual_bank_window_not_capped_by_budget",
+     "const int Wacc = std::min(pol->n_recent, beta - pol->n_sink);", "const int Wacc = pol->n_recent;"),
+    ("dual_bank_freezes_the_window",
+     "if (pol->accumulate == HIKV_REF_ACC_RECENT && !(x.pos[n] > new_pos[b] - Wacc)) continue;",
+     "if (pol->accumulate == HIKV_REF_ACC_RECENT && (x.pos[n] > new_pos[b] - Wacc)) continue;"),
 ]
 
 
