@@ -113,7 +113,8 @@ def main():
     budget_t = torch.from_numpy(budget).cuda()
     # per-KV-head budgets go as a device array; one budget for every unit as budget_all
     b_arr, b_all = (budget_t, 0) if w.budgets is not None else (None, w.budget_all)
-    pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens)
+    pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
+                        accumulate=w.accumulate)
     # One workspace (scratch) serves every layer copy, as it would every layer
     # of a model; each cache carries its own pending-eviction state.
     wss = [H.workspace(layers[0].shape, pol)]
@@ -148,7 +149,7 @@ def main():
         if not args.no_hint:
             p = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
                               budget_hint=budget if b_arr is not None else None,
-                              len_hint=host_len[li])
+                              len_hint=host_len[li], accumulate=w.accumulate)
         dbg = None
         if events is not None:
             dbg = H.hikv_debug(None, None, None, events[0].cuda_event, events[1].cuda_event)
@@ -319,6 +320,8 @@ def workload_text(w, budget, full):
     else:
         pol = f"budget {w.budget_all}"
     s2 = f", Stage II r = {w.stage2_channels}, k_T = {w.stage2_tokens}" if w.stage2_channels else ""
+    if w.accumulate:
+        s2 += ", HiKV dual bank (scores accumulate only in the recent window, frozen outside it)"
     return (f"{w.name} {'decode' if full else 'steady state'}: batch {w.batch}, {heads}, D {w.head_dim}, "
             f"{dt} KV, {w.ctx}-token prefill, {pol}, sinks {w.n_sink}, recent {w.n_recent}{s2}")
 
@@ -343,7 +346,8 @@ def cpu_baseline(w, d, seconds):
     st = ref.copy_state(d)
     budget = w.budget_array()
     kw = dict(budget=budget, n_sink=w.n_sink, n_recent=w.n_recent, debug=False,
-              stage2_channels=w.stage2_channels, stage2_tokens=w.stage2_tokens)
+              stage2_channels=w.stage2_channels, stage2_tokens=w.stage2_tokens,
+              accumulate=w.accumulate)
     ref.decode_step(st, w.n_q_heads, d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], **kw)
     n = 0
     t0 = time.perf_counter()

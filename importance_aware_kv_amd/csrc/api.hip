@@ -44,6 +44,7 @@ int check_shape(const hikv_shape *s) {
 int check_policy(const hikv_shape *s, const hikv_policy *p) {
   if (!p) return HIKV_EINVAL;
   if (p->n_sink < 0 || p->n_recent < 0) return HIKV_EINVAL;
+  if (p->accumulate != HIKV_ACC_ALL && p->accumulate != HIKV_ACC_RECENT) return HIKV_EINVAL;
   if (p->stage2_channels < 0 || p->stage2_channels > s->head_dim) return HIKV_EINVAL;
   if (p->stage2_channels > 0 && p->stage2_tokens < 1) return HIKV_EINVAL;
   return HIKV_OK;
@@ -84,6 +85,7 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
   a.budget_all = p->budget_all;
   a.n_sink = p->n_sink;
   a.n_recent = p->n_recent;
+  a.acc_recent = p->accumulate == HIKV_ACC_RECENT;
   a.r = p->stage2_channels;
   a.kT = p->stage2_channels > 0 ? p->stage2_tokens : 0;
   a.ws = ws;

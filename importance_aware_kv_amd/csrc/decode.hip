@@ -440,13 +440,17 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
     float p = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) p += fast_exp2(lg[(size_t)n * G + g] - M[g]) * IL[g];
-    const float iv = ((n == L - 1) ? 0.f : imp[n]) + p;
+    const bool is_new = n == L - 1;
+    const int pn = (over || a.acc_recent) ? pos[n] : 0;
+    // HiKV's dual bank: only the recent window accumulates; older scores are
+    // frozen and not rewritten (the new token's slot is always written).
+    const bool acc = !a.acc_recent || pn > newest - Wp;
+    const float iv = (is_new ? 0.f : imp[n]) + (acc ? p : 0.f);
     // Written through to memory: the unit's last tile may move slot L - 1's
     // value into the victim's slot, and no slot may be left dirty in two
     // caches.
-    store_agent_f(imp + n, iv);
+    if (acc || is_new) store_agent_f(imp + n, iv);
     if (over) {
-      const int pn = pos[n];
       const bool prot = (pn < S) || (pn > newest - Wp);
       if (!prot) {
         const uint64_t k = evict_key(iv, pn);

@@ -148,6 +148,7 @@ struct StepArgs {
   int32_t *evict;            // [U][state_words(cap)] pending eviction (cache state)
   const int32_t *budget;     // may be null
   int32_t budget_all, n_sink, n_recent;
+  int32_t acc_recent;        // importance accumulates only inside the protected window (HiKV dual bank)
   int32_t r, kT;             // Stage II
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
   int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit

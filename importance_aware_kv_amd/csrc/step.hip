@@ -1340,11 +1340,15 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     #pragma unroll
             for (int g = 0; g < G; ++g) p += fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
             const bool is_new = n == Lold;
-            const float iv = (is_new ? 0.f : ti[i]) + p;
             const int pn = is_new ? newest : tp[i];
+            const bool recent = pn > newest - Wp;
+            // HiKV's dual bank: only the recent window accumulates; the
+            // scores of older tokens are frozen (and not rewritten).
+            const bool acc = !a.acc_recent || recent;
+            const float iv = (is_new ? 0.f : ti[i]) + (acc ? p : 0.f);
             if (is_new) s_newimp = iv;
-            else impw[n] = iv;
-            const bool cand = !((pn < S) || (pn > newest - Wp));
+            else if (acc) impw[n] = iv;
+            const bool cand = !((pn < S) || recent);
             if (over && cand) {
               const uint64_t k = evict_key(iv, pn);
               if (k < best) {

@@ -88,6 +88,7 @@ class Workload:
     stage2_tokens: int = 0
     recipe: str = "normal"   # normal | planted | lognormal_keys
     capacity: int = 0        # slots per (batch, KV head); 0 -> ctx + steps
+    accumulate: int = 0      # 0: every live token accumulates; 1: only the recent window (HiKV dual bank)
 
     @property
     def group(self) -> int:
@@ -133,6 +134,11 @@ def workload(name: str, *, ctx: Optional[int] = None, steps: Optional[int] = Non
     elif name == "longctx128k":
         w = Workload("longctx128k", 1003, 2, 64, 8, 128, BF16, 131072, 32, 4096, 4, 256,
                      recipe="lognormal_keys")
+    elif name == "hikv_dualbank":
+        # HiKV Stage I: B_I = L_p / r_I with r_I = 4 on an 8K prompt, split
+        # into a recent bank and an important bank of B_I / 2 each, no sinks.
+        w = Workload("hikv_dualbank", 1005, 8, 32, 8, 128, BF16, 8192, 128, 2048, 0, 1024,
+                     recipe="planted", accumulate=1)
     elif name == "twostage":
         w = Workload("twostage", 1004, 8, 32, 8, 128, BF16, 8192, 128, 1024, 4, 128,
                      stage2_channels=32, stage2_tokens=256, recipe="planted")
@@ -153,7 +159,7 @@ def workload(name: str, *, ctx: Optional[int] = None, steps: Optional[int] = Non
     return w
 
 
-WORKLOAD_NAMES = ("tiny", "llama8b", "headkv32k", "longctx128k", "twostage")
+WORKLOAD_NAMES = ("tiny", "llama8b", "headkv32k", "longctx128k", "twostage", "hikv_dualbank")
 
 
 def _pack(x: np.ndarray, dtype: int) -> np.ndarray:

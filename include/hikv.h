@@ -88,6 +88,9 @@ typedef struct hikv_cache {
                      bytes, 16-byte aligned, zero-filled together with a fresh cache */
 } hikv_cache;
 
+#define HIKV_ACC_ALL 0
+#define HIKV_ACC_RECENT 1
+
 typedef struct hikv_policy {
   const int32_t *budget;   /* [B][Hkv] device per-unit budgets ([HeadKV] Sec. 3.2), or NULL */
   int32_t budget_all;      /* budget of every unit when `budget` is NULL */
@@ -110,6 +113,16 @@ typedef struct hikv_policy {
                               that cuts a unit by more than one token (the first step after a
                               prefill): the survivors' rows are then moved by a launch of many
                               workgroups per unit instead of one.  Results never depend on it. */
+  int32_t accumulate;      /* which tokens a step's attention probabilities are added to:
+                              HIKV_ACC_ALL: every live token (H2O's cumulative score).
+                              HIKV_ACC_RECENT: only the W' newest positions (the window that
+                              eviction protects); older tokens keep a frozen score.  With
+                              n_sink 0 and n_recent = budget/2 this is HiKV's dual bank
+                              ([HiKV] Sec. III-B): the window is the recent bank, the rest the
+                              important bank, each score sums the W' probabilities a token
+                              received from its own step on, and a token leaving the window
+                              displaces the bank's lowest score iff its own is higher.  Any
+                              other value is HIKV_EINVAL. */
 } hikv_policy;
 
 /* Optional outputs of hikv_decode_step for tests, inspection and profiling;

@@ -34,17 +34,19 @@ def say(*a):
 
 class GpuRun:
     def __init__(self, state, n_q_heads, *, budget=None, budget_all=0, n_sink=0, n_recent=0,
-                 r=0, kT=0, scale=0.0, hint=False):
+                 r=0, kT=0, scale=0.0, hint=False, accumulate=H.HIKV_ACC_ALL):
         self.Hq = n_q_heads
         self.hint = hint
         self.pol_args = None
         self.dev = H.DeviceCache(state, n_q_heads, scale=scale)
         self.budget_np = None if budget is None else np.ascontiguousarray(budget, dtype=np.int32)
         self.budget_t = None if budget is None else torch.from_numpy(self.budget_np).cuda()
-        self.pol = H.make_policy(self.budget_t, budget_all, n_sink, n_recent, r, kT)
+        self.acc = accumulate
+        self.pol = H.make_policy(self.budget_t, budget_all, n_sink, n_recent, r, kT, accumulate=accumulate)
         self.pol_args = (self.budget_t, budget_all, n_sink, n_recent, r, kT)
         self.kw = dict(budget=self.budget_np, budget_all=budget_all, n_sink=n_sink,
-                       n_recent=n_recent, stage2_channels=r, stage2_tokens=kT, scale=scale)
+                       n_recent=n_recent, stage2_channels=r, stage2_tokens=kT, scale=scale,
+                       accumulate=accumulate)
         self.ws = H.workspace(self.dev.shape, self.pol)
         self.r, self.kT = r, kT
         sh = self.dev.shape
@@ -93,7 +95,8 @@ class GpuRun:
             # the caller's own copy of len[] (here read back from the device)
             hint = (np.ascontiguousarray(self.dev.len.cpu().numpy(), dtype=np.int32)
                     if hint_override is None else np.ascontiguousarray(hint_override, dtype=np.int32))
-            pol = H.make_policy(*self.pol_args, len_hint=hint, budget_hint=self.budget_np)
+            pol = H.make_policy(*self.pol_args, len_hint=hint, budget_hint=self.budget_np,
+                                accumulate=self.acc)
         code = H.hikv_decode_step(self.dev.shape, self.dev.cache, pol, qt, kt, vt, pt, self.out,
                                   self.ws, debug=self.dbg)
         assert code == H.HIKV_OK, H.status_string(code)

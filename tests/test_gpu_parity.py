@@ -25,7 +25,8 @@ def _gpu():
 
 def _run(w, data, **extra):
     kw = dict(budget=data["budget"] if w.budgets is not None else None, budget_all=w.budget_all,
-              n_sink=w.n_sink, n_recent=w.n_recent, r=w.stage2_channels, kT=w.stage2_tokens)
+              n_sink=w.n_sink, n_recent=w.n_recent, r=w.stage2_channels, kT=w.stage2_tokens,
+              accumulate=w.accumulate)
     kw.update(extra)
     return GpuRun(ref.copy_state(data), w.n_q_heads, **kw)
 
@@ -366,7 +367,8 @@ def _unit_state(state, b, j):
     return {k: np.ascontiguousarray(state[k][b:b + 1, j:j + 1]) for k in ("k", "v", "pos", "imp", "len")}
 
 
-@pytest.mark.parametrize("name", ["headkv32k", "llama8b", "longctx128k", "longctx128k_full", "twostage"])
+@pytest.mark.parametrize("name", ["headkv32k", "llama8b", "longctx128k", "longctx128k_full", "twostage",
+                                  "hikv_dualbank"])
 def test_full_size_sampled_units(name):
     """Every workload at full size, in the launch configuration the benchmark
     times (host length hints): the first step (compression, or a full
@@ -405,9 +407,84 @@ def test_full_size_sampled_units(name):
             npos = d["new_pos"][t][b:b + 1]
             kw = dict(budget=budget[b:b + 1, j:j + 1], budget_all=0, n_sink=w.n_sink,
                       n_recent=w.n_recent, stage2_channels=w.stage2_channels,
-                      stage2_tokens=w.stage2_tokens, scale=0.0)
+                      stage2_tokens=w.stage2_tokens, scale=0.0, accumulate=w.accumulate)
             code, want, dref = ref.decode_step(u_ref, G, q, kn, vn, npos, **kw)
             assert code == 0
             e = row_errors(out[b:b + 1, j * G:(j + 1) * G], want)
             assert e.max() <= OUT_TOL[w.dtype], (name, t, b, j, float(e.max()))
             check_kept(u_pre, _unit_state(post, b, j), u_ref, dref, kw, npos, where=f"{name} {t} {b} {j}")
+
+
+# ---------------------------------------------------------------------------
+# HiKV dual bank: scores accumulate only inside the recent window (the recent
+# bank) and stay frozen outside it (the important bank).
+# ---------------------------------------------------------------------------
+def _frozen_scores(d, ctx, seed):
+    """A mid-run cache: the prompt tokens carry seeded scores (so that the
+    frozen ones decide the kept set), the decode steps then add to the window."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d["imp"][:, :, :ctx] = (rng.random(d["imp"][:, :, :ctx].shape) * 2.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("path", ["two-launch", "two-launch-hint", "multi-kernel", "stage2"])
+def test_dual_bank_lockstep(path, monkeypatch):
+    """First step cuts 1001 tokens to the budget (bulk), the rest evict one
+    token each; no sinks, window = half the budget."""
+    w = W.workload("llama8b", ctx=1000, steps=5, batch=2)
+    w.budget_all, w.n_sink, w.n_recent, w.accumulate = 256, 0, 128, H.HIKV_ACC_RECENT
+    if path == "stage2":
+        w.stage2_channels, w.stage2_tokens = 32, 64
+    if path == "multi-kernel":
+        monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
+    d = W.generate(w)
+    _frozen_scores(d, w.ctx, 61)
+    worst, _ = lockstep(_run(w, d, hint=path == "two-launch-hint"), d, w.steps, tag=f"dual bank {path}")
+    say(f"dual bank {path} worst row err", worst)
+
+
+def test_dual_bank_long_units_lockstep():
+    """Units longer than one importance block (2048 tokens) of the second
+    launch, ragged budgets, window 1024 capped by the small budgets."""
+    w = W.workload("headkv32k", ctx=7000, steps=4, batch=1)
+    w.budgets = np.array([[2048, 4097, 6143, 100, 3000, 64, 2049, 5000]], dtype=np.int32)
+    w.n_sink, w.n_recent, w.accumulate = 0, 1024, H.HIKV_ACC_RECENT
+    d = W.generate(w)
+    _frozen_scores(d, w.ctx, 62)
+    lockstep(_run(w, d, hint=True), d, w.steps, tag="dual bank long units")
+
+
+def test_dual_bank_init_from_windowed_prefill():
+    """HiKV's bank initialisation: every prompt query adds its causal
+    attention row to the tokens within W' steps of it, one cut keeps the
+    last W' prompt tokens and the top W' of the rest; decode steps follow."""
+    w = W.workload("llama8b", ctx=160, steps=4, batch=2)
+    Wn = 24
+    w.budget_all, w.n_sink, w.n_recent, w.accumulate = 2 * Wn, 0, Wn, H.HIKV_ACC_RECENT
+    d = W.generate(w)
+    L = w.ctx
+    rng = np.random.Generator(np.random.PCG64(63))
+    qo = W.bf16_bits(rng.standard_normal((w.batch, w.n_q_heads, L, w.head_dim)).astype(np.float32))
+    qpos = np.broadcast_to(np.arange(L, dtype=np.int32), (w.batch, L)).copy()
+    run = _run(w, d)
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(run.dev.shape, L), dtype=torch.uint8, device="cuda")
+    say("[gpu] dual bank init: prefill scores")
+    assert H.hikv_prefill_scores(run.dev.shape, run.dev.cache, H.to_device(qo), torch.from_numpy(qpos).cuda(),
+                                 L, Wn, ws) == 0
+    torch.cuda.synchronize()
+    scored = run.state()
+    want = ref.copy_state(d)
+    assert ref.prefill_scores(want, w.n_q_heads, qo, qpos, window=Wn) == 0
+    np.testing.assert_allclose(scored["imp"], want["imp"], rtol=2e-3, atol=2e-5)
+    say("[gpu] dual bank init: evict")
+    newest = np.full((w.batch,), L - 1, dtype=np.int32)
+    assert H.hikv_evict(run.dev.shape, run.dev.cache, run.pol, torch.from_numpy(newest).cuda(), run.ws) == 0
+    assert H.hikv_device_status(run.ws) == 0
+    post = run.state()
+    cut = ref.copy_state(scored)          # the oracle cuts the GPU's own scores
+    assert ref.evict(cut, w.n_q_heads, newest, budget_all=2 * Wn, n_sink=0, n_recent=Wn)[0] == 0
+    for b in range(w.batch):
+        for j in range(w.n_kv_heads):
+            got = ref.live_positions(post, b, j)
+            assert list(got) == list(ref.live_positions(cut, b, j)), (b, j)
+            assert set(range(L - Wn, L)) <= set(got.tolist())
+    lockstep(run, d, w.steps, tag="dual bank after init")
