@@ -162,7 +162,9 @@ bool policy_ok(const Dims &d, const hikv_ref_policy *pol) {
   if (!pol || pol->n_sink < 0 || pol->n_recent < 0) return false;
   if (pol->accumulate != HIKV_REF_ACC_ALL && pol->accumulate != HIKV_REF_ACC_RECENT) return false;
   if (pol->stage2_channels < 0 || pol->stage2_channels > d.D) return false;
-  if (pol->stage2_channels > 0 && pol->stage2_tokens < 1) return false;
+  if (pol->stage2_v != HIKV_REF_S2V_TOPK && pol->stage2_v != HIKV_REF_S2V_CHUNK) return false;
+  if (pol->stage2_channels > 0 && pol->stage2_v == HIKV_REF_S2V_TOPK && pol->stage2_tokens < 1)
+    return false;
   return true;
 }
 
@@ -248,6 +250,39 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
           }
           std::vector<double> pt = softmax(st);
           for (int n = 0; n < L; ++n) added[n] += pt[n];
+          if (dbg && dbg->sel_channels) {
+            std::vector<int> e = E;
+            std::sort(e.begin(), e.end());
+            for (int i = 0; i < r; ++i) dbg->sel_channels[((size_t)b * d.Hq + h) * r + i] = e[i];
+          }
+          if (dbg && dbg->approx_logits)
+            for (int n = 0; n < L; ++n)
+              dbg->approx_logits[((size_t)b * d.Hq + h) * d.cap + n] = st[n];
+          if (pol->stage2_v == HIKV_REF_S2V_CHUNK) {
+            // V side, HiKV's chunked selection: the live tokens in position
+            // order, cut into chunks of D; each chunk keeps its r largest
+            // probabilities (ties: lower position) and the output sums those
+            // probabilities times their V rows, with no renormalisation.
+            std::vector<int> byp(L);
+            for (int n = 0; n < L; ++n) byp[n] = n;
+            std::sort(byp.begin(), byp.end(), [&](int a, int bb) { return x.pos[a] < x.pos[bb]; });
+            int kept_total = 0;
+            for (int c0 = 0; c0 < L; c0 += d.D) {
+              const int m = std::min(d.D, L - c0);
+              std::vector<int> chunk(byp.begin() + c0, byp.begin() + c0 + m);
+              std::sort(chunk.begin(), chunk.end(), [&](int a, int bb) {
+                if (pt[a] != pt[bb]) return pt[a] > pt[bb];
+                return x.pos[a] < x.pos[bb];
+              });
+              const int keep = std::min(r, m);
+              for (int i = 0; i < keep; ++i)
+                for (int c = 0; c < d.D; ++c) o[c] += pt[chunk[i]] * val_elem(d, x, chunk[i], c);
+              kept_total += keep;
+            }
+            if (dbg && dbg->sel_count) dbg->sel_count[(size_t)b * d.Hq + h] = kept_total;
+            for (int c = 0; c < d.D; ++c) out[((size_t)b * d.Hq + h) * d.D + c] = (float)o[c];
+            continue;
+          }
           // Tokens kept for the exact pass: largest approximate logit first.
           std::vector<int> order(L);
           for (int n = 0; n < L; ++n) order[n] = n;
@@ -268,11 +303,6 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
           for (int i = 0; i < nt; ++i)
             for (int c = 0; c < d.D; ++c) o[c] += p[i] * val_elem(d, x, T[i], c);
 
-          if (dbg && dbg->sel_channels) {
-            std::vector<int> e = E;
-            std::sort(e.begin(), e.end());
-            for (int i = 0; i < r; ++i) dbg->sel_channels[((size_t)b * d.Hq + h) * r + i] = e[i];
-          }
           if (dbg && dbg->sel_tokens) {
             std::vector<int32_t> tp(nt);
             for (int i = 0; i < nt; ++i) tp[i] = x.pos[T[i]];
@@ -281,9 +311,6 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
               dbg->sel_tokens[((size_t)b * d.Hq + h) * kT + i] = i < nt ? tp[i] : -1;
           }
           if (dbg && dbg->sel_count) dbg->sel_count[(size_t)b * d.Hq + h] = nt;
-          if (dbg && dbg->approx_logits)
-            for (int n = 0; n < L; ++n)
-              dbg->approx_logits[((size_t)b * d.Hq + h) * d.cap + n] = st[n];
         }
         for (int c = 0; c < d.D; ++c) out[((size_t)b * d.Hq + h) * d.D + c] = (float)o[c];
       }

@@ -27,6 +27,8 @@
  *    it receives while in the recent bank, then stays frozen; promotion into
  *    the important bank iff that score beats the bank's lowest) and
  *    Sec. III-D (bank initialisation from windowed prompt scores).
+ *  - HiKV Sec. III-C and Algorithm 1 (Stage II V side: chunks of d_h entries
+ *    of P, top-B_II per chunk, P.V over the kept rows).
  */
 #ifndef HIKV_REF_H
 #define HIKV_REF_H
@@ -69,19 +71,30 @@ typedef struct {
 #define HIKV_REF_ACC_ALL 0
 #define HIKV_REF_ACC_RECENT 1
 
+/* What Stage II does with the approximate probabilities on the V side.
+ * TOPK: the k_T tokens with the largest approximate logit get an exact
+ * (full-channel) softmax, renormalised over them, and P.V over them.
+ * CHUNK: HiKV Sec. III-C literally: the approximate P over the live tokens in
+ * position order is cut into chunks of D tokens (the last one shorter); each
+ * chunk keeps its r largest entries (ties: lower position); the output is the
+ * sum of those entries times their V rows, not renormalised. */
+#define HIKV_REF_S2V_TOPK 0
+#define HIKV_REF_S2V_CHUNK 1
+
 typedef struct {
   const int32_t *budget; /* [B][Hkv] or NULL -> budget_all */
   int32_t budget_all, n_sink, n_recent;
   int32_t stage2_channels; /* r; 0 = Stage II off */
   int32_t stage2_tokens;   /* tokens kept for the exact softmax (k_T) */
   int32_t accumulate;      /* HIKV_REF_ACC_ALL | HIKV_REF_ACC_RECENT */
+  int32_t stage2_v;        /* HIKV_REF_S2V_TOPK | HIKV_REF_S2V_CHUNK (used when r > 0) */
 } hikv_ref_policy;
 
 /* Optional per-step debug outputs; any pointer may be NULL. */
 typedef struct {
   int32_t *sel_channels; /* [B][Hq][r]  chosen channels, ascending */
   int32_t *sel_tokens;   /* [B][Hq][k_T] positions of the exact-softmax set, ascending, -1 padded */
-  int32_t *sel_count;    /* [B][Hq]     size of that set */
+  int32_t *sel_count;    /* [B][Hq]     size of that set (CHUNK: tokens kept over all chunks) */
   double *approx_logits; /* [B][Hq][cap] Stage II approximate logit per pre-eviction slot */
   float *imp_pre_evict;  /* [B][Hkv][cap] importance after accumulation, pre-eviction slot order */
   uint8_t *kept;         /* [B][Hkv][cap] 1 if that pre-eviction slot survives eviction */

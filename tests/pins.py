@@ -49,6 +49,14 @@ What pins what:
       (partial inside the window); the kept set is the sinks, the window and
       the top scores of every token that has left the window (brute force);
       the heap model fed the same ejections holds the same bank.
+  stage2_chunks_reduce_to_attention -- HiKV's chunked V side with r = D
+      (every channel; every chunk keeps all its entries) is exact attention:
+      the library's SDPA.
+  stage2_chunks_select_by_probability -- with V rows one-hot by position
+      rank, the output reads back what each chunk of D consecutive positions
+      kept: min(r, chunk size) entries, equal to the library's softmax of the
+      channel-masked query (no renormalisation), none smaller than an entry
+      the chunk dropped; permuting the slots changes nothing.
 """
 
 from __future__ import annotations
@@ -595,8 +603,83 @@ def dual_bank_matches_its_definition(seed=41):
                     assert sorted(l for _, l in heaps[j].entries()) == sorted(top), (t, j)
 
 
+def stage2_chunks_reduce_to_attention(seed=47):
+    B, Hkv, G, D, cap = 1, 2, 2, 16, 64
+    Hq = Hkv * G
+    st = W.random_cache(seed, B, Hq, Hkv, D, W.F32, cap, [[40, 17]])   # 41 and 18 tokens: ragged chunks
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.F32, st["newest"])
+    before = ref.copy_state(st)
+    scale = 1.0 / math.sqrt(D)
+    code, out, dbg = ref.decode_step(st, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"],
+                                     budget_all=cap, stage2_channels=D, stage2_v=ref.S2V_CHUNK)
+    assert code == 0
+    for j in range(Hkv):
+        k, v, _, _ = _unit_rows(before, 0, j, W.F32)
+        k = np.concatenate([k, widen(step["k_new"][0, j], W.F32)[None]])
+        v = np.concatenate([v, widen(step["v_new"][0, j], W.F32)[None]])
+        q = widen(step["q"][0, j * G:(j + 1) * G], W.F32)[:, None, :]
+        want = sdpa(q, k[None], v[None], scale)[:, 0, :]
+        assert rel_err(out[0, j * G:(j + 1) * G], want) < 1e-6, j
+        assert np.all(dbg["sel_count"][0, j * G:(j + 1) * G] == k.shape[0])
+
+
+def stage2_chunks_select_by_probability(seed=53):
+    G, D, cap, r, n_old = 3, 16, 64, 5, 39              # 40 tokens: chunks of 16, 16 and 8
+    st0 = W.random_cache(seed, 1, G, 1, D, W.F32, cap, [[n_old]])
+    step = W.random_step(seed + 1, 1, G, 1, D, W.F32, st0["newest"])
+    L = n_old + 1
+    scale = 1.0 / math.sqrt(D)
+    pos = np.append(st0["pos"][0, 0, :n_old], step["new_pos"][0])
+    order = np.argsort(pos, kind="stable")               # slots by position
+    rank = np.empty(L, dtype=np.int64)
+    rank[order] = np.arange(L)
+    k = np.concatenate([widen(st0["k"][0, 0, :n_old], W.F32), widen(step["k_new"][0, 0], W.F32)[None]])
+    P = []
+    for g in range(G):
+        qg = widen(step["q"][0, g], W.F32)
+        E = np.argsort(-np.abs(qg), kind="stable")[:r]    # the r largest |q_d|, lower index first
+        qm = np.zeros_like(qg)
+        qm[E] = qg[E]
+        P.append(sdpa(qm[None, None], k[None], np.eye(L)[None], scale)[0, 0])
+    outs = []
+    for c0 in range(0, L, D):
+        m = min(D, L - c0)
+        st = ref.copy_state(st0)
+        st["v"][0, 0] = 0.0
+        vnew = np.zeros((1, 1, D), np.float32)
+        for s in range(L):                                # V row of a chunk member: one-hot of its rank
+            if c0 <= rank[s] < c0 + m:
+                if s < n_old:
+                    st["v"][0, 0, s, rank[s] - c0] = 1.0
+                else:
+                    vnew[0, 0, rank[s] - c0] = 1.0
+        kw = dict(budget_all=cap, stage2_channels=r, stage2_v=ref.S2V_CHUNK)
+        code, out, _ = ref.decode_step(st, G, step["q"], step["k_new"], vnew, step["new_pos"], **kw)
+        assert code == 0
+        outs.append(out)
+        members = order[c0:c0 + m]
+        for g in range(G):
+            got = out[0, g, :m].astype(np.float64)
+            assert np.all(out[0, g, m:] == 0)
+            kept = got > 0
+            assert kept.sum() == min(r, m), (c0, g, int(kept.sum()))
+            want = P[g][members]
+            assert np.abs(got[kept] - want[kept]).max() <= 1e-6 * want[kept].max(), (c0, g)
+            if (~kept).any():
+                assert want[kept].min() >= want[~kept].max(), (c0, g)
+        # the same chunk with the cache's slots permuted
+        perm = np.random.Generator(np.random.PCG64(seed + c0)).permutation(n_old)
+        sp = ref.copy_state(st0)
+        for f in ("k", "v", "pos", "imp"):
+            src = (st if f == "v" else st0)[f][0, 0, :n_old]
+            sp[f][0, 0, :n_old] = src[perm]
+        code, outp, _ = ref.decode_step(sp, G, step["q"], step["k_new"], vnew, step["new_pos"], **kw)
+        assert code == 0 and np.abs(outp - out).max() <= 1e-12, c0
+
+
 ALL = [attention_matches_library, rows_sum_to_group, streaming_closed_form, eviction_brute_force,
        golden_cases, permutation_invariance, channel_permutation, conservation,
        stage2_reduces_to_stage1, stage2_selection, equal_keys_closed_form, prefill_column_sums,
        errors_leave_unit_unchanged, heap_worked_examples, heap_keeps_the_top_scores,
-       dual_bank_matches_its_definition]
+       dual_bank_matches_its_definition, stage2_chunks_reduce_to_attention,
+       stage2_chunks_select_by_probability]

@@ -48,6 +48,17 @@ MUTANTS = [
     ("dual_bank_freezes_the_window",
      "if (pol->accumulate == HIKV_REF_ACC_RECENT && !(x.pos[n] > new_pos[b] - Wacc)) continue;",
      "if (pol->accumulate == HIKV_REF_ACC_RECENT && (x.pos[n] > new_pos[b] - Wacc)) continue;"),
+    ("chunks_by_slot", "std::sort(byp.begin(), byp.end(), [&](int a, int bb) { return x.pos[a] < x.pos[bb]; });",
+     ""),
+    ("chunks_keep_smallest", "if (pt[a] != pt[bb]) return pt[a] > pt[bb];", "if (pt[a] != pt[bb]) return pt[a] < pt[bb];"),
+    ("chunks_of_r_tokens", "for (int c0 = 0; c0 < L; c0 += d.D) {", "for (int c0 = 0; c0 < L; c0 += r) {"),
+    ("chunks_keep_one_more", "const int keep = std::min(r, m);", "const int keep = std::min(r + 1, m);"),
+    ("chunks_use_exact_logits", "            st[n] = d.scale * acc;\n          }\n          std::vector<double> pt = softmax(st);",
+     "            st[n] = d.scale * acc;\n          }\n          std::vector<double> pt = softmax(st);\n"
+     "          if (pol->stage2_v == HIKV_REF_S2V_CHUNK) {\n"
+     "            for (int n = 0; n < L; ++n) {\n              double a2 = 0.0;\n"
+     "              for (int c = 0; c < d.D; ++c) a2 += qh[c] * key_elem(d, x, n, c);\n"
+     "              st[n] = d.scale * a2;\n            }\n            pt = softmax(st);\n          }"),
 ]
 
 
