@@ -38,8 +38,9 @@ MUTANTS = [
      "int keep_n = std::max(0, beta - n_prot - 1);"),
     ("value_rows_from_keys", "  return elem(x.v, d.dtype, (size_t)n * d.D + c);",
      "  return elem(x.k, d.dtype, (size_t)n * d.D + c);"),
-    ("stage2_tokens_tie_by_higher_pos", "            return x.pos[a] < x.pos[bb];",
-     "            return x.pos[a] > x.pos[bb];"),
+    ("stage2_tokens_tie_by_higher_pos",
+     "if (st[a] != st[bb]) return st[a] > st[bb];\n            return x.pos[a] < x.pos[bb];",
+     "if (st[a] != st[bb]) return st[a] > st[bb];\n            return x.pos[a] > x.pos[bb];"),
     ("dual_bank_accumulates_everywhere",
      "if (pol->accumulate == HIKV_REF_ACC_RECENT && !(x.pos[n] > new_pos[b] - Wacc)) continue;", ""),
     ("dual_bank_window_off_by_one", "!(x.pos[n] > new_pos[b] - Wacc)", "!(x.pos[n] >= new_pos[b] - Wacc)"),
