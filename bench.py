@@ -114,7 +114,7 @@ def main():
     # per-KV-head budgets go as a device array; one budget for every unit as budget_all
     b_arr, b_all = (budget_t, 0) if w.budgets is not None else (None, w.budget_all)
     pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
-                        accumulate=w.accumulate)
+                        accumulate=w.accumulate, stage2_v=w.stage2_v)
     # One workspace (scratch) serves every layer copy, as it would every layer
     # of a model; each cache carries its own pending-eviction state.
     wss = [H.workspace(layers[0].shape, pol)]
@@ -149,7 +149,7 @@ def main():
         if not args.no_hint:
             p = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
                               budget_hint=budget if b_arr is not None else None,
-                              len_hint=host_len[li], accumulate=w.accumulate)
+                              len_hint=host_len[li], accumulate=w.accumulate, stage2_v=w.stage2_v)
         dbg = None
         if events is not None:
             dbg = H.hikv_debug(None, None, None, events[0].cuda_event, events[1].cuda_event)
@@ -320,6 +320,9 @@ def workload_text(w, budget, full):
     else:
         pol = f"budget {w.budget_all}"
     s2 = f", Stage II r = {w.stage2_channels}, k_T = {w.stage2_tokens}" if w.stage2_channels else ""
+    if w.stage2_channels and w.stage2_v:
+        s2 = (f", Stage II r = {w.stage2_channels} channels and, on the V side, the top {w.stage2_channels} "
+              f"entries of P per chunk of {w.head_dim} positions (HiKV)")
     if w.accumulate:
         s2 += ", HiKV dual bank (scores accumulate only in the recent window, frozen outside it)"
     return (f"{w.name} {'decode' if full else 'steady state'}: batch {w.batch}, {heads}, D {w.head_dim}, "
@@ -347,7 +350,7 @@ def cpu_baseline(w, d, seconds):
     budget = w.budget_array()
     kw = dict(budget=budget, n_sink=w.n_sink, n_recent=w.n_recent, debug=False,
               stage2_channels=w.stage2_channels, stage2_tokens=w.stage2_tokens,
-              accumulate=w.accumulate)
+              accumulate=w.accumulate, stage2_v=w.stage2_v)
     ref.decode_step(st, w.n_q_heads, d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], **kw)
     n = 0
     t0 = time.perf_counter()

@@ -46,7 +46,8 @@ int check_policy(const hikv_shape *s, const hikv_policy *p) {
   if (p->n_sink < 0 || p->n_recent < 0) return HIKV_EINVAL;
   if (p->accumulate != HIKV_ACC_ALL && p->accumulate != HIKV_ACC_RECENT) return HIKV_EINVAL;
   if (p->stage2_channels < 0 || p->stage2_channels > s->head_dim) return HIKV_EINVAL;
-  if (p->stage2_channels > 0 && p->stage2_tokens < 1) return HIKV_EINVAL;
+  if (p->stage2_v != HIKV_S2V_TOPK && p->stage2_v != HIKV_S2V_CHUNK) return HIKV_EINVAL;
+  if (p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_TOPK && p->stage2_tokens < 1) return HIKV_EINVAL;
   return HIKV_OK;
 }
 
@@ -57,8 +58,9 @@ int check_cache(const hikv_cache *c) {
 }
 
 WsSizes sizes_for(const hikv_shape *s, const hikv_policy *p) {
-  const int kT = (p && p->stage2_channels > 0) ? p->stage2_tokens : 1;
-  return ws_sizes(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->capacity, kT);
+  const bool chunks = p && p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_CHUNK;
+  const int kT = (p && p->stage2_channels > 0 && !chunks) ? p->stage2_tokens : 1;
+  return ws_sizes(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->capacity, kT, chunks);
 }
 
 StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *p, const Ws &ws) {
@@ -87,7 +89,8 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
   a.n_recent = p->n_recent;
   a.acc_recent = p->accumulate == HIKV_ACC_RECENT;
   a.r = p->stage2_channels;
-  a.kT = p->stage2_channels > 0 ? p->stage2_tokens : 0;
+  a.s2_chunks = p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_CHUNK;
+  a.kT = (p->stage2_channels > 0 && !a.s2_chunks) ? p->stage2_tokens : 0;
   a.ws = ws;
   return a;
 }
@@ -179,8 +182,14 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);
-    if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
-    if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);
+    if (a.s2_chunks) {
+      if ((e = launch_chunk_rank(a, s)) != hipSuccess) return dev_err(e);
+      if ((e = launch_chunk_pv(a, dt, s)) != hipSuccess) return dev_err(e);
+      if ((e = launch_chunk_reduce(a, s)) != hipSuccess) return dev_err(e);
+    } else {
+      if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
+      if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);
+    }
   }
   // With the caller's lengths and one budget for every unit, the host knows
   // whether any unit ends more than one token over budget; if none does, the

@@ -56,9 +56,11 @@ struct Ws {
   uint64_t *bkeys;      // [n_units][cap] bulk eviction: every slot's eviction key
                         //   (UINT64_MAX for a protected token)
   int32_t *nmoves;      // [n_units] bulk eviction: rows the move launch relocates (0: none)
+  float *chunk_acc;     // [n_units][ceil(cap/D)][G][D] Stage II chunked V side: each chunk's P.V
+  int32_t *chunk_cnt;   // [n_units][ceil(cap/D)][G] tokens each chunk kept per q-head
 };
 
-constexpr int kWsParts = 19;
+constexpr int kWsParts = 21;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -68,8 +70,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline int max_tiles_for(int n_units) { return kMaxGrid + n_units + 8; }
 
-inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
+inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chunks) {
   const size_t U = (size_t)B * Hkv, G = (size_t)(Hq / Hkv), MT = (size_t)max_tiles_for((int)U);
+  const size_t NC = chunks ? (size_t)((cap + D - 1) / D) : 0;
   const size_t sz[kWsParts] = {
       512,                             // status (+ spare)
       sizeof(int32_t) * 4 * MT,        // tinfo
@@ -90,6 +93,8 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT) {
       sizeof(int32_t) * 4 * U,         // urec
       sizeof(uint64_t) * U * cap,      // bkeys
       sizeof(int32_t) * U,             // nmoves
+      sizeof(float) * U * NC * G * D,  // chunk_acc
+      sizeof(int32_t) * U * NC * G,    // chunk_cnt
   };
   WsSizes w;
   size_t o = 0;
@@ -123,6 +128,8 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.urec = reinterpret_cast<int32_t *>(b + s.off[16]);
   w.bkeys = reinterpret_cast<uint64_t *>(b + s.off[17]);
   w.nmoves = reinterpret_cast<int32_t *>(b + s.off[18]);
+  w.chunk_acc = reinterpret_cast<float *>(b + s.off[19]);
+  w.chunk_cnt = reinterpret_cast<int32_t *>(b + s.off[20]);
   return w;
 }
 
@@ -150,6 +157,7 @@ struct StepArgs {
   int32_t budget_all, n_sink, n_recent;
   int32_t acc_recent;        // importance accumulates only inside the protected window (HiKV dual bank)
   int32_t r, kT;             // Stage II
+  int32_t s2_chunks;         // Stage II V side: HiKV's per-chunk top-r of P (else exact top-k_T)
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
   int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit
   const void *q, *k_new, *v_new;

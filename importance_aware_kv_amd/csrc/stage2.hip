@@ -10,8 +10,8 @@
 //   p~   = softmax(s~) feeds the importance (accumulation kernel)
 //   T    = the k_T tokens of largest s~ (ties: lower position)       [kernel S2]
 //   out  = exact full-D softmax over T only, times V                 [kernel S3]
-// The page's V side selects rows per chunk of P with no renormalisation; the
-// workload definition used here renormalises over a global top-k_T instead.
+// That is the V side with HIKV_S2V_TOPK.  HIKV_S2V_CHUNK is the page's own V
+// side: rows selected per chunk of P, with no renormalisation (kernels C1-C3).
 
 #include "hikv_block.h"
 #include "hikv_launch.h"
@@ -296,6 +296,246 @@ __global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
     }
     outp[d] = av / lv;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Stage II V side as HiKV states it (Sec. III-C, Algorithm 1): the reduced-
+// logit probabilities P over the live tokens, taken in position order, are
+// cut into chunks of D tokens; each chunk keeps its r largest entries (ties:
+// lower position), and the output sums those entries times their V rows with
+// no renormalisation.  Three launches: the position order (C1), one
+// workgroup per chunk for the selection and its P.V (C2), and the sum of the
+// chunks per q-head (C3, a fixed order, so results repeat bit for bit).
+// ---------------------------------------------------------------------------
+
+// C1: every live token counts the live tokens before it in position order
+// (lower position, or the same position and a lower slot, so that the ranks
+// are a permutation whatever the caller's positions) and writes its slot at
+// that rank.  The unit's positions go through LDS a tile at a time and are
+// read as broadcasts.
+constexpr int kRankThreads = 256, kRankTile = 2048;
+
+__global__ __launch_bounds__(kRankThreads) void k_chunk_rank(StepArgs a) {
+  const int u = blockIdx.y, tid = threadIdx.x;
+  if (!unit_has_tiles(a, u)) return;
+  const int L = a.len[u] + 1;  // the new token sits in slot L - 1
+  if ((int)blockIdx.x * kRankThreads >= L) return;
+  const int n = blockIdx.x * kRankThreads + tid;
+  const int32_t *pos = a.pos + (size_t)u * a.cap;
+  const int32_t p = pos[min(n, L - 1)];
+  __shared__ int4 sp[kRankTile / 4];
+  int *spi = reinterpret_cast<int *>(sp);
+  int rank = 0;
+  for (int t0 = 0; t0 < L; t0 += kRankTile) {
+    const int tn = min(kRankTile, L - t0);
+    __syncthreads();  // the previous tile is no longer read
+    for (int i = tid; i < kRankTile; i += kRankThreads) spi[i] = i < tn ? pos[t0 + i] : INT_MAX;
+    __syncthreads();
+    const int n4 = (tn + 3) / 4;
+    for (int i = 0; i < n4; ++i) {
+      const int4 q = sp[i];
+      const int sl = t0 + 4 * i;  // padding sits at slots >= L > n: never counted
+      rank += (q.x < p) | ((q.x == p) & (sl < n));
+      rank += (q.y < p) | ((q.y == p) & (sl + 1 < n));
+      rank += (q.z < p) | ((q.z == p) & (sl + 2 < n));
+      rank += (q.w < p) | ((q.w == p) & (sl + 3 < n));
+    }
+  }
+  if (n < L) a.ws.holes[(size_t)u * a.cap + rank] = n;
+}
+
+// C2: one workgroup per (chunk, unit).  Wave w selects for q-heads w, w + 4:
+// lane l holds the chunk's entries l and l + 64; the r-th largest
+// probability is found one bit at a time by ballot counts (the IEEE bits of
+// a non-negative float order like its value), and of the entries equal to
+// it the lowest-ranked complete r.  The rows any q-head kept are then read
+// once, 16 bytes per lane, and each lane sums p * v for every q-head.
+template <int EL, int D, int G>
+__global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
+  constexpr int CH = 16 / EL;      // V elements per 16-byte load
+  constexpr int LPR = D / CH;      // lanes per V row
+  constexpr int RG = 256 / LPR;    // rows read at once by the workgroup
+  constexpr int MAXIT = D / RG;    // rows per lane group, at most
+  constexpr int RB = D * EL;
+  constexpr int NPL = D / 64;      // chunk entries per lane in the selection
+  const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!unit_has_tiles(a, u)) return;
+  const int L = a.len[u] + 1;
+  const int c0 = c * D;
+  if (c0 >= L) return;
+  const int m = min(D, L - c0);
+  const int keep = min(a.r, m);
+  const size_t NC = (size_t)((a.cap + D - 1) / D);
+  __shared__ int s_slot[D];
+  __shared__ float s_p[G][D];
+  __shared__ int s_list[D];
+  __shared__ int s_nlist;
+  __shared__ float s_red[4][G * D];
+  const int32_t *ord = a.ws.holes + (size_t)u * a.cap;
+  for (int t = tid; t < D; t += 256) s_slot[t] = t < m ? min(max(ord[c0 + t], 0), L - 1) : 0;
+  __syncthreads();
+  const float *lg = a.ws.logits + (size_t)u * a.cap * G;
+  for (int g = wave; g < G; g += 4) {
+    const float M = a.ws.stats[((size_t)u * G + g) * 2];
+    const float IL = 1.f / a.ws.stats[((size_t)u * G + g) * 2 + 1];
+    float pv[NPL];
+    uint32_t kv[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int t = lane + 64 * i;
+      const bool ok = t < m;
+      pv[i] = ok ? fast_exp2(lg[(size_t)s_slot[t] * G + g] - M) * IL : 0.f;
+      kv[i] = ok ? __float_as_uint(pv[i]) + 1u : 0u;  // 0: no token of the chunk
+    }
+    auto count_ge = [&](uint32_t thr) {
+      int k = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) k += __popcll(__ballot(kv[i] >= thr));
+      return k;
+    };
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      if (count_ge(cand) >= keep) thr = cand;
+    }
+    int need = keep;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) need -= __popcll(__ballot(kv[i] > thr));
+    const uint64_t below = (1ull << lane) - 1ull;
+    int eq_before = 0, kept = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const uint64_t eq = __ballot(kv[i] == thr);
+      const bool sel = kv[i] > thr || (kv[i] == thr && eq_before + __popcll(eq & below) < need);
+      eq_before += __popcll(eq);
+      kept += __popcll(__ballot(sel));
+      s_p[g][lane + 64 * i] = sel ? pv[i] : 0.f;
+    }
+    if (lane == 0) a.ws.chunk_cnt[((size_t)u * NC + c) * G + g] = kept;
+  }
+  __syncthreads();
+  if (wave == 0) {  // the rows some q-head kept, in chunk order
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int t = lane + 64 * i;
+      bool any = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) any |= s_p[g][t] > 0.f;
+      const uint64_t bm = __ballot(any);
+      if (any) s_list[base + __popcll(bm & ((1ull << lane) - 1ull))] = t;
+      base += __popcll(bm);
+    }
+    if (lane == 0) s_nlist = base;
+  }
+  __syncthreads();
+  const int nl = s_nlist;
+  const int rg = tid / LPR, cl = tid - rg * LPR;
+  const char *vc = static_cast<const char *>(a.v_cache) + (size_t)u * a.cap * RB;
+  uint4 vf[MAXIT];
+  int tt[MAXIT];
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {  // every row load first, from clamped addresses
+    const int li = rg + i * RG;
+    tt[i] = nl > 0 ? s_list[min(li, nl - 1)] : 0;  // s_slot[0] always holds a live slot
+    vf[i] = *reinterpret_cast<const uint4 *>(vc + (size_t)s_slot[tt[i]] * RB + cl * 16);
+  }
+  float acc[G][CH];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[g][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    const bool live = rg + i * RG < nl;
+    float vv[CH];
+    if constexpr (EL == 2) {
+      const uint32_t *w = reinterpret_cast<const uint32_t *>(&vf[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[2 * e] = bf_lo(w[e]), vv[2 * e + 1] = bf_hi(w[e]);
+    } else {
+      const float *f = reinterpret_cast<const float *>(&vf[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = f[e];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float p = live ? s_p[g][tt[i]] : 0.f;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[g][e] = fmaf(p, vv[e], acc[g][e]);
+    }
+  }
+  // Sum over the lane groups of a wave, then over the waves.
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+  if (lane < LPR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) s_red[wave][g * D + cl * CH + e] = acc[g][e];
+  }
+  __syncthreads();
+  float *dst = a.ws.chunk_acc + ((size_t)u * NC + c) * G * D;
+  for (int i = tid; i < G * D; i += 256) dst[i] = s_red[0][i] + s_red[1][i] + s_red[2][i] + s_red[3][i];
+}
+
+// C3: per unit, the G output rows are the sums of its chunks' partials, in
+// chunk order; the debug count is the tokens all chunks kept.
+__global__ __launch_bounds__(256) void k_chunk_reduce(StepArgs a) {
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int G = a.G, D = a.D;
+  const int b = u / a.Hkv, j = u - b * a.Hkv;
+  const size_t NC = (size_t)((a.cap + D - 1) / D);
+  float *outp = a.out + ((size_t)b * a.Hq + (size_t)j * G) * D;  // the group's rows are adjacent
+  const bool ok = unit_has_tiles(a, u);
+  const int nc = ok ? (a.len[u] + 1 + D - 1) / D : 0;
+  for (int i = tid; i < G * D; i += 256) {
+    float s = 0.f;
+    for (int c = 0; c < nc; ++c) s += a.ws.chunk_acc[((size_t)u * NC + c) * G * D + i];
+    outp[i] = s;
+  }
+  if (a.dbg_count && tid < G) {
+    int k = 0;
+    for (int c = 0; c < nc; ++c) k += a.ws.chunk_cnt[((size_t)u * NC + c) * G + tid];
+    a.dbg_count[(size_t)b * a.Hq + (size_t)j * G + tid] = k;
+  }
+}
+
+hipError_t launch_chunk_rank(const StepArgs &a, hipStream_t s) {
+  const dim3 grid((a.cap + kRankThreads - 1) / kRankThreads, a.n_units);
+  hipLaunchKernelGGL(k_chunk_rank, grid, dim3(kRankThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int EL, int D>
+static void chunk_pv_g(const StepArgs &a, dim3 grid, hipStream_t s) {
+  switch (a.G) {
+    case 1: hipLaunchKernelGGL((k_chunk_pv<EL, D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_chunk_pv<EL, D, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_chunk_pv<EL, D, 4>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_chunk_pv<EL, D, 8>), grid, dim3(256), 0, s, a); break;
+  }
+}
+
+hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s) {
+  const dim3 grid((a.cap + a.D - 1) / a.D, a.n_units);
+  if (dtype == HIKV_BF16) {
+    if (a.D == 128) chunk_pv_g<2, 128>(a, grid, s);
+    else chunk_pv_g<2, 64>(a, grid, s);
+  } else {
+    if (a.D == 128) chunk_pv_g<4, 128>(a, grid, s);
+    else chunk_pv_g<4, 64>(a, grid, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_reduce(const StepArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_chunk_reduce, dim3(a.n_units), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s) {

@@ -89,6 +89,7 @@ class Workload:
     recipe: str = "normal"   # normal | planted | lognormal_keys
     capacity: int = 0        # slots per (batch, KV head); 0 -> ctx + steps
     accumulate: int = 0      # 0: every live token accumulates; 1: only the recent window (HiKV dual bank)
+    stage2_v: int = 0        # Stage II V side: 0 exact softmax over top-k_T; 1 HiKV's per-chunk top-r of P
 
     @property
     def group(self) -> int:
@@ -135,10 +136,18 @@ def workload(name: str, *, ctx: Optional[int] = None, steps: Optional[int] = Non
         w = Workload("longctx128k", 1003, 2, 64, 8, 128, BF16, 131072, 32, 4096, 4, 256,
                      recipe="lognormal_keys")
     elif name == "hikv_dualbank":
-        # HiKV Stage I: B_I = L_p / r_I with r_I = 4 on an 8K prompt, split
-        # into a recent bank and an important bank of B_I / 2 each, no sinks.
-        w = Workload("hikv_dualbank", 1005, 8, 32, 8, 128, BF16, 8192, 128, 2048, 0, 1024,
+        # HiKV Stage I on its evaluation prompt length (4096): B_I = L_p / r_I
+        # with r_I = 4, split into a recent bank and an important bank of
+        # B_I / 2 each, no sinks; a serving batch of 8.
+        w = Workload("hikv_dualbank", 1005, 8, 32, 8, 128, BF16, 4096, 128, 1024, 0, 512,
                      recipe="planted", accumulate=1)
+    elif name == "hikv_hier":
+        # HiKV's two stages together, on its evaluation prompt length: the
+        # dual bank (B_I = 4096 / 4, banks of 512, no sinks) and Stage II
+        # with r_II = 4 (B_II = 32 channels of q, 32 tokens per chunk of 128
+        # entries of P).
+        w = Workload("hikv_hier", 1006, 8, 32, 8, 128, BF16, 4096, 128, 1024, 0, 512,
+                     stage2_channels=32, recipe="planted", accumulate=1, stage2_v=1)
     elif name == "twostage":
         w = Workload("twostage", 1004, 8, 32, 8, 128, BF16, 8192, 128, 1024, 4, 128,
                      stage2_channels=32, stage2_tokens=256, recipe="planted")
@@ -159,7 +168,7 @@ def workload(name: str, *, ctx: Optional[int] = None, steps: Optional[int] = Non
     return w
 
 
-WORKLOAD_NAMES = ("tiny", "llama8b", "headkv32k", "longctx128k", "twostage", "hikv_dualbank")
+WORKLOAD_NAMES = ("tiny", "llama8b", "headkv32k", "longctx128k", "twostage", "hikv_dualbank", "hikv_hier")
 
 
 def _pack(x: np.ndarray, dtype: int) -> np.ndarray:

@@ -91,6 +91,9 @@ typedef struct hikv_cache {
 #define HIKV_ACC_ALL 0
 #define HIKV_ACC_RECENT 1
 
+#define HIKV_S2V_TOPK 0
+#define HIKV_S2V_CHUNK 1
+
 typedef struct hikv_policy {
   const int32_t *budget;   /* [B][Hkv] device per-unit budgets ([HeadKV] Sec. 3.2), or NULL */
   int32_t budget_all;      /* budget of every unit when `budget` is NULL */
@@ -123,14 +126,28 @@ typedef struct hikv_policy {
                               received from its own step on, and a token leaving the window
                               displaces the bank's lowest score iff its own is higher.  Any
                               other value is HIKV_EINVAL. */
+  int32_t stage2_v;        /* Stage II's V side (used when r > 0):
+                              HIKV_S2V_TOPK: the k_T tokens with the largest reduced logit get
+                              an exact full-channel softmax, renormalised over them, and P.V.
+                              HIKV_S2V_CHUNK: [HiKV] Sec. III-C and Algorithm 1 literally: the
+                              reduced-logit probabilities P of the live tokens, in position
+                              order, are cut into chunks of D tokens (the last one shorter);
+                              each chunk keeps its r largest entries (ties: lower position) and
+                              the output is the sum of those entries times their V rows, not
+                              renormalised (stage2_tokens is not used).  The chunk order costs
+                              O(len^2) comparisons per unit and step, meant for the budgets the
+                              pages use (a few thousand tokens).  Any other value is
+                              HIKV_EINVAL. */
 } hikv_policy;
 
 /* Optional outputs of hikv_decode_step for tests, inspection and profiling;
  * every field may be NULL. */
 typedef struct hikv_debug {
   int32_t *sel_channels;   /* [B][Hq][r] Stage II chosen channels, ascending (device) */
-  int32_t *sel_tokens;     /* [B][Hq][k_T] positions of the exact-softmax tokens, ascending, -1 padded (device) */
-  int32_t *sel_count;      /* [B][Hq] number of exact-softmax tokens, min(k_T, len + 1) (device) */
+  int32_t *sel_tokens;     /* [B][Hq][k_T] positions of the exact-softmax tokens, ascending, -1 padded
+                              (device; not written with HIKV_S2V_CHUNK) */
+  int32_t *sel_count;      /* [B][Hq] number of exact-softmax tokens, min(k_T, len + 1); with
+                              HIKV_S2V_CHUNK the tokens kept over all chunks (device) */
   void *attend_start;      /* hipEvents (both or neither; caller-owned) that the dispatch of the step's */
   void *attend_stop;       /* attention launch records when it starts and ends executing (Stage I: the
                               launch over every live K and V row; Stage II: the reduced-channel logits

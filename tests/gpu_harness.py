@@ -8,7 +8,11 @@ back to the host), runs one step, and the two results are compared:
     importance lies within 1e-6 (relative) of the kept/evicted boundary;
   * surviving rows: K, V bytes identical, importance within 1e-5 relative;
   * Stage II: chosen channel sets equal; exact-softmax token sets equal
-    except near-ties of the reduced logit.
+    except near-ties of the reduced logit.  With HiKV's chunked V side the
+    kept-token counts are equal, and a q-head whose chunk selection has a
+    near-tie at its boundary (the r-th and the next probability within
+    CHUNK_TIE_RTOL of each other in the oracle) is left out of the output
+    check: either choice is a correct result.
 """
 
 from __future__ import annotations
@@ -25,6 +29,7 @@ from oracle import ref
 OUT_TOL = {W.F32: 1e-5, W.BF16: 2e-3}
 TIE_RTOL = 1e-6
 IMP_RTOL = 1e-5
+CHUNK_TIE_RTOL = 1e-4
 
 
 def say(*a):
@@ -34,7 +39,8 @@ def say(*a):
 
 class GpuRun:
     def __init__(self, state, n_q_heads, *, budget=None, budget_all=0, n_sink=0, n_recent=0,
-                 r=0, kT=0, scale=0.0, hint=False, accumulate=H.HIKV_ACC_ALL):
+                 r=0, kT=0, scale=0.0, hint=False, accumulate=H.HIKV_ACC_ALL,
+                 stage2_v=H.HIKV_S2V_TOPK):
         self.Hq = n_q_heads
         self.hint = hint
         self.pol_args = None
@@ -42,11 +48,13 @@ class GpuRun:
         self.budget_np = None if budget is None else np.ascontiguousarray(budget, dtype=np.int32)
         self.budget_t = None if budget is None else torch.from_numpy(self.budget_np).cuda()
         self.acc = accumulate
-        self.pol = H.make_policy(self.budget_t, budget_all, n_sink, n_recent, r, kT, accumulate=accumulate)
+        self.s2v = stage2_v
+        self.pol = H.make_policy(self.budget_t, budget_all, n_sink, n_recent, r, kT, accumulate=accumulate,
+                                 stage2_v=stage2_v)
         self.pol_args = (self.budget_t, budget_all, n_sink, n_recent, r, kT)
         self.kw = dict(budget=self.budget_np, budget_all=budget_all, n_sink=n_sink,
                        n_recent=n_recent, stage2_channels=r, stage2_tokens=kT, scale=scale,
-                       accumulate=accumulate)
+                       accumulate=accumulate, stage2_v=stage2_v)
         self.ws = H.workspace(self.dev.shape, self.pol)
         self.r, self.kT = r, kT
         sh = self.dev.shape
@@ -96,7 +104,7 @@ class GpuRun:
             hint = (np.ascontiguousarray(self.dev.len.cpu().numpy(), dtype=np.int32)
                     if hint_override is None else np.ascontiguousarray(hint_override, dtype=np.int32))
             pol = H.make_policy(*self.pol_args, len_hint=hint, budget_hint=self.budget_np,
-                                accumulate=self.acc)
+                                accumulate=self.acc, stage2_v=self.s2v)
         code = H.hikv_decode_step(self.dev.shape, self.dev.cache, pol, qt, kt, vt, pt, self.out,
                                   self.ws, debug=self.dbg)
         assert code == H.HIKV_OK, H.status_string(code)
@@ -187,6 +195,29 @@ def check_stage2(dbg_gpu, dbg_ref, pre, new_pos, Hq, kT, where=""):
     return n_tie
 
 
+def chunk_near_ties(dbg_ref, pre, new_pos, Hq, r):
+    """[B][Hq] True where some chunk of D positions has its r-th and next
+    largest probability within CHUNK_TIE_RTOL (oracle's reduced logits)."""
+    B, Hkv = pre["len"].shape
+    D = pre["k"].shape[-1]
+    G = Hq // Hkv
+    tie = np.zeros((B, Hq), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            j = h // G
+            L = int(pre["len"][b, j]) + 1
+            pos = np.append(pre["pos"][b, j, :L - 1], new_pos[b])
+            s = dbg_ref["approx_logits"][b, h, :L]
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            order = np.argsort(pos, kind="stable")
+            for c0 in range(0, L, D):
+                pc = np.sort(p[order[c0:c0 + D]])[::-1]
+                if len(pc) > r and pc[r - 1] - pc[r] <= CHUNK_TIE_RTOL * pc[r - 1]:
+                    tie[b, h] = True
+    return tie
+
+
 def lockstep(run: GpuRun, data, steps, *, tag="", start_state=None):
     """Run `steps` decode steps on the GPU, checking each against the oracle."""
     dtype = run.dev.dtype
@@ -201,9 +232,15 @@ def lockstep(run: GpuRun, data, steps, *, tag="", start_state=None):
         code, want, dref = ref.decode_step(st, run.Hq, data["q"][t], data["k_new"][t],
                                            data["v_new"][t], data["new_pos"][t], **run.kw)
         assert code == 0
-        if run.r > 0:
-            check_stage2(dbg, dref, pre, data["new_pos"][t], run.Hq, run.kT, where=f"{tag} step {t}")
         e = row_errors(out, want)
+        if run.r > 0 and run.s2v == H.HIKV_S2V_CHUNK:
+            assert np.array_equal(dbg["sel_count"], dref["sel_count"]), (tag, t)
+            assert np.array_equal(dbg["sel_channels"], dref["sel_channels"]), (tag, t)
+            tie = chunk_near_ties(dref, pre, data["new_pos"][t], run.Hq, run.r)
+            e = np.where(tie, 0.0, e)
+            say(f"[gpu] {tag} step {t}: {int(tie.sum())} q-heads with a chunk near-tie left out")
+        elif run.r > 0:
+            check_stage2(dbg, dref, pre, data["new_pos"][t], run.Hq, run.kT, where=f"{tag} step {t}")
         worst = max(worst, float(e.max()))
         assert e.max() <= OUT_TOL[dtype], (tag, t, float(e.max()), np.unravel_index(e.argmax(), e.shape))
         assert np.array_equal(post["len"], st["len"]), (tag, t)

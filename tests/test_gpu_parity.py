@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import GpuRun, check_kept, lockstep, row_errors, say, OUT_TOL
+from gpu_harness import GpuRun, check_kept, chunk_near_ties, lockstep, row_errors, say, OUT_TOL
 from importance_aware_kv_amd import hikv as H
 from importance_aware_kv_amd import workloads as W
 from oracle import ref
@@ -26,7 +26,7 @@ def _gpu():
 def _run(w, data, **extra):
     kw = dict(budget=data["budget"] if w.budgets is not None else None, budget_all=w.budget_all,
               n_sink=w.n_sink, n_recent=w.n_recent, r=w.stage2_channels, kT=w.stage2_tokens,
-              accumulate=w.accumulate)
+              accumulate=w.accumulate, stage2_v=w.stage2_v)
     kw.update(extra)
     return GpuRun(ref.copy_state(data), w.n_q_heads, **kw)
 
@@ -368,7 +368,7 @@ def _unit_state(state, b, j):
 
 
 @pytest.mark.parametrize("name", ["headkv32k", "llama8b", "longctx128k", "longctx128k_full", "twostage",
-                                  "hikv_dualbank"])
+                                  "hikv_dualbank", "hikv_hier"])
 def test_full_size_sampled_units(name):
     """Every workload at full size, in the launch configuration the benchmark
     times (host length hints): the first step (compression, or a full
@@ -407,10 +407,13 @@ def test_full_size_sampled_units(name):
             npos = d["new_pos"][t][b:b + 1]
             kw = dict(budget=budget[b:b + 1, j:j + 1], budget_all=0, n_sink=w.n_sink,
                       n_recent=w.n_recent, stage2_channels=w.stage2_channels,
-                      stage2_tokens=w.stage2_tokens, scale=0.0, accumulate=w.accumulate)
+                      stage2_tokens=w.stage2_tokens, scale=0.0, accumulate=w.accumulate,
+                      stage2_v=w.stage2_v)
             code, want, dref = ref.decode_step(u_ref, G, q, kn, vn, npos, **kw)
             assert code == 0
             e = row_errors(out[b:b + 1, j * G:(j + 1) * G], want)
+            if w.stage2_v == H.HIKV_S2V_CHUNK:
+                e = np.where(chunk_near_ties(dref, u_pre, npos, G, w.stage2_channels), 0.0, e)
             assert e.max() <= OUT_TOL[w.dtype], (name, t, b, j, float(e.max()))
             check_kept(u_pre, _unit_state(post, b, j), u_ref, dref, kw, npos, where=f"{name} {t} {b} {j}")
 
@@ -488,3 +491,64 @@ def test_dual_bank_init_from_windowed_prefill():
             assert list(got) == list(ref.live_positions(cut, b, j)), (b, j)
             assert set(range(L - Wn, L)) <= set(got.tolist())
     lockstep(run, d, w.steps, tag="dual bank after init")
+
+
+# ---------------------------------------------------------------------------
+# HiKV's Stage II V side: top-r of P per chunk of D positions, no
+# renormalisation.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_stage2_chunks_shape_matrix(dtype, D, G):
+    """Units of 1, 2, 64, 151, 261 and 400 tokens: one-token and exactly-one
+    chunk cases and ragged last chunks, r = D / 4."""
+    B, Hkv = 2, 3
+    Hq = G * Hkv
+    cap = 400
+    lens = np.array([[0, 150, 399], [1, 63, 260]])
+    st = W.random_cache(300 + G + D, B, Hq, Hkv, D, dtype, cap, lens)
+    data = W.random_step(400 + G, B, Hq, Hkv, D, dtype, st["newest"])
+    data = {k: v[None] for k, v in data.items()}
+    budget = np.array([[40, 100, 120], [1, 64, 300]], dtype=np.int32)
+    run = GpuRun(st, Hq, budget=budget, n_sink=1, n_recent=8, r=D // 4, stage2_v=H.HIKV_S2V_CHUNK)
+    lockstep(run, data, 1, tag=f"chunks dt={dtype} D={D} G={G}")
+
+
+def test_stage2_chunks_r_equals_d_is_full_attention():
+    B, Hkv, G, D, cap = 2, 2, 4, 128, 300
+    st = W.random_cache(9, B, G * Hkv, Hkv, D, W.BF16, cap, [[100, 250], [3, 180]])
+    data = W.random_step(10, B, G * Hkv, Hkv, D, W.BF16, st["newest"])
+    a = GpuRun(ref.copy_state(st), G * Hkv, budget_all=64, n_sink=4, n_recent=16)
+    b = GpuRun(ref.copy_state(st), G * Hkv, budget_all=64, n_sink=4, n_recent=16, r=D,
+               stage2_v=H.HIKV_S2V_CHUNK)
+    oa, _ = a.step(data["q"], data["k_new"], data["v_new"], data["new_pos"])
+    ob, dbg = b.step(data["q"], data["k_new"], data["v_new"], data["new_pos"])
+    assert row_errors(ob, oa.astype(np.float64)).max() <= 1e-5
+    lens = np.array([[101, 251], [4, 181]])
+    assert np.array_equal(dbg["sel_count"], np.repeat(lens, G, axis=1))
+
+
+@pytest.mark.parametrize("dual_bank", [False, True], ids=["h2o", "dual-bank"])
+def test_stage2_chunks_lockstep(dual_bank):
+    """Several steps: the first cuts 901 tokens to 300, the rest evict one each."""
+    w = W.workload("twostage", ctx=900, steps=4, batch=2)
+    w.budget_all, w.n_recent, w.stage2_v = 300, 32, H.HIKV_S2V_CHUNK
+    if dual_bank:
+        w.n_sink, w.n_recent, w.accumulate = 0, 150, H.HIKV_ACC_RECENT
+    d = W.generate(w)
+    if dual_bank:
+        _frozen_scores(d, w.ctx, 64)
+    lockstep(_run(w, d), d, w.steps, tag=f"chunks lockstep dual_bank={dual_bank}")
+
+
+def test_stage2_chunks_repeat_is_bit_identical():
+    w = W.workload("hikv_hier", ctx=700, steps=2, batch=2)
+    w.budget_all, w.n_recent = 200, 100
+    d = W.generate(w)
+    outs = []
+    for _ in range(2):
+        run = _run(w, d)
+        outs.append(np.stack([run.step(d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t])[0]
+                              for t in range(w.steps)]))
+    assert np.array_equal(outs[0], outs[1])
