@@ -183,9 +183,7 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);
     if (a.s2_chunks) {
-      if ((e = launch_chunk_rank(a, s)) != hipSuccess) return dev_err(e);
       if ((e = launch_chunk_pv(a, dt, s)) != hipSuccess) return dev_err(e);
-      if ((e = launch_chunk_reduce(a, s)) != hipSuccess) return dev_err(e);
     } else {
       if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
       if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);

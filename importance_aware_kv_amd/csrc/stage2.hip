@@ -11,7 +11,7 @@
 //   T    = the k_T tokens of largest s~ (ties: lower position)       [kernel S2]
 //   out  = exact full-D softmax over T only, times V                 [kernel S3]
 // That is the V side with HIKV_S2V_TOPK.  HIKV_S2V_CHUNK is the page's own V
-// side: rows selected per chunk of P, with no renormalisation (kernels C1-C3).
+// side: rows selected per chunk of P, with no renormalisation (kernel k_chunk_pv).
 
 #include "hikv_block.h"
 #include "hikv_launch.h"
@@ -303,53 +303,31 @@ __global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
 // logit probabilities P over the live tokens, taken in position order, are
 // cut into chunks of D tokens; each chunk keeps its r largest entries (ties:
 // lower position), and the output sums those entries times their V rows with
-// no renormalisation.  Three launches: the position order (C1), one
-// workgroup per chunk for the selection and its P.V (C2), and the sum of the
-// chunks per q-head (C3, a fixed order, so results repeat bit for bit).
+// no renormalisation.
+//
+// One launch, one workgroup per (chunk, unit):
+//  1. the position order: positions are distinct, so a token's rank is the
+//     number of live positions below its own.  The unit's positions are set
+//     as bits of an LDS bitmap over [min, max] and per-word popcount
+//     prefixes are scanned; rank = prefix of its word + popcount of the
+//     word's lower bits.  Each workgroup ranks the whole unit and keeps the
+//     D tokens of its own chunk, with their logits (loaded in the same pass
+//     as the positions).  Positions spanning more than the bitmap covers are
+//     ranked by counting (every token against every other), much slower.
+//     With repeated positions ranks collide: results are then undefined, and
+//     every slot taken from the chunk is clamped, so memory stays in bounds.
+//  2. wave w selects for q-heads w, w + 4: lane l holds the chunk's entries l
+//     and l + 64; the r-th largest probability is found one bit at a time by
+//     ballot counts (the IEEE bits of a non-negative float order like its
+//     value), and of the entries equal to it the lowest-ranked complete r.
+//  3. the rows any q-head kept are read once, 16 bytes per lane, and each
+//     lane sums p * v for every q-head.
+//  4. the partials go out with device-coherent stores, each workgroup takes
+//     a ticket, and the unit's last one adds the chunks up in chunk order
+//     (results repeat bit for bit).
 // ---------------------------------------------------------------------------
+constexpr int kChunkBits = 1 << 17;  // position span the rank bitmap covers (16 KB)
 
-// C1: every live token counts the live tokens before it in position order
-// (lower position, or the same position and a lower slot, so that the ranks
-// are a permutation whatever the caller's positions) and writes its slot at
-// that rank.  The unit's positions go through LDS a tile at a time and are
-// read as broadcasts.
-constexpr int kRankThreads = 256, kRankTile = 2048;
-
-__global__ __launch_bounds__(kRankThreads) void k_chunk_rank(StepArgs a) {
-  const int u = blockIdx.y, tid = threadIdx.x;
-  if (!unit_has_tiles(a, u)) return;
-  const int L = a.len[u] + 1;  // the new token sits in slot L - 1
-  if ((int)blockIdx.x * kRankThreads >= L) return;
-  const int n = blockIdx.x * kRankThreads + tid;
-  const int32_t *pos = a.pos + (size_t)u * a.cap;
-  const int32_t p = pos[min(n, L - 1)];
-  __shared__ int4 sp[kRankTile / 4];
-  int *spi = reinterpret_cast<int *>(sp);
-  int rank = 0;
-  for (int t0 = 0; t0 < L; t0 += kRankTile) {
-    const int tn = min(kRankTile, L - t0);
-    __syncthreads();  // the previous tile is no longer read
-    for (int i = tid; i < kRankTile; i += kRankThreads) spi[i] = i < tn ? pos[t0 + i] : INT_MAX;
-    __syncthreads();
-    const int n4 = (tn + 3) / 4;
-    for (int i = 0; i < n4; ++i) {
-      const int4 q = sp[i];
-      const int sl = t0 + 4 * i;  // padding sits at slots >= L > n: never counted
-      rank += (q.x < p) | ((q.x == p) & (sl < n));
-      rank += (q.y < p) | ((q.y == p) & (sl + 1 < n));
-      rank += (q.z < p) | ((q.z == p) & (sl + 2 < n));
-      rank += (q.w < p) | ((q.w == p) & (sl + 3 < n));
-    }
-  }
-  if (n < L) a.ws.holes[(size_t)u * a.cap + rank] = n;
-}
-
-// C2: one workgroup per (chunk, unit).  Wave w selects for q-heads w, w + 4:
-// lane l holds the chunk's entries l and l + 64; the r-th largest
-// probability is found one bit at a time by ballot counts (the IEEE bits of
-// a non-negative float order like its value), and of the entries equal to
-// it the lowest-ranked complete r.  The rows any q-head kept are then read
-// once, 16 bytes per lane, and each lane sums p * v for every q-head.
 template <int EL, int D, int G>
 __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
   constexpr int CH = 16 / EL;      // V elements per 16-byte load
@@ -358,23 +336,153 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
   constexpr int MAXIT = D / RG;    // rows per lane group, at most
   constexpr int RB = D * EL;
   constexpr int NPL = D / 64;      // chunk entries per lane in the selection
+  constexpr int NW = kChunkBits / 32, WPT = NW / 256;
+  constexpr int KR = G <= 4 ? 8 : 4;  // tokens per thread whose position and logits stay in registers
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (!unit_has_tiles(a, u)) return;
-  const int L = a.len[u] + 1;
+  const int b = u / a.Hkv, j = u - b * a.Hkv;
+  float *outp = a.out + ((size_t)b * a.Hq + (size_t)j * G) * D;  // the group's rows are adjacent
+  if (!unit_has_tiles(a, u)) {  // a unit the step skipped (an error): zero output
+    if (c == 0) {
+      for (int i = tid; i < G * D; i += 256) outp[i] = 0.f;
+      if (a.dbg_count && tid < G) a.dbg_count[(size_t)b * a.Hq + (size_t)j * G + tid] = 0;
+    }
+    return;
+  }
+  const int L = a.len[u] + 1;  // the new token sits in slot L - 1
   const int c0 = c * D;
   if (c0 >= L) return;
   const int m = min(D, L - c0);
   const int keep = min(a.r, m);
   const size_t NC = (size_t)((a.cap + D - 1) / D);
+  __shared__ uint32_t bits[NW];
+  __shared__ int wpre[NW];
   __shared__ int s_slot[D];
-  __shared__ float s_p[G][D];
+  __shared__ float s_p[G][D];  // the chunk's logits, then the kept probabilities
   __shared__ int s_list[D];
   __shared__ int s_nlist;
   __shared__ float s_red[4][G * D];
-  const int32_t *ord = a.ws.holes + (size_t)u * a.cap;
-  for (int t = tid; t < D; t += 256) s_slot[t] = t < m ? min(max(ord[c0 + t], 0), L - 1) : 0;
-  __syncthreads();
+  __shared__ int s_lo[4], s_hi[4], s_wsum[4];
+  const int32_t *pos = a.pos + (size_t)u * a.cap;
   const float *lg = a.ws.logits + (size_t)u * a.cap * G;
+  // With repeated positions a rank can be missed: such an entry keeps slot 0
+  // and a logit of -inf (probability 0).
+  for (int t = tid; t < D; t += 256) {
+    s_slot[t] = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) s_p[g][t] = -INFINITY;
+  }
+
+  // 1. Ranks.  The first KR * 256 tokens keep position and logits in
+  // registers; later ones (long units) are read again.
+  int ps[KR];
+  float lv[KR][G];
+  int lo = INT_MAX, hi = INT_MIN;
+#pragma unroll
+  for (int i = 0; i < KR; ++i) {
+    const int n = tid + 256 * i;
+    const int nn = min(n, L - 1);
+    ps[i] = pos[nn];
+#pragma unroll
+    for (int g = 0; g < G; ++g) lv[i][g] = lg[(size_t)nn * G + g];
+    if (n < L) lo = min(lo, ps[i]), hi = max(hi, ps[i]);
+  }
+  for (int n = tid + 256 * KR; n < L; n += 256) {
+    const int p = pos[n];
+    lo = min(lo, p), hi = max(hi, p);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off));
+    hi = max(hi, __shfl_xor(hi, off));
+  }
+  if (lane == 0) s_lo[wave] = lo, s_hi[wave] = hi;
+  __syncthreads();
+  lo = min(min(s_lo[0], s_lo[1]), min(s_lo[2], s_lo[3]));
+  hi = max(max(s_hi[0], s_hi[1]), max(s_hi[2], s_hi[3]));
+  const bool dense = (int64_t)hi - lo + 1 <= kChunkBits;
+  auto place = [&](int n, int rank, const float *l) {
+    const int t = rank - c0;
+    if (t >= 0 && t < m) {
+      s_slot[t] = n;
+#pragma unroll
+      for (int g = 0; g < G; ++g) s_p[g][t] = l[g];
+    }
+  };
+  if (dense) {
+    const int nw = (int)(((int64_t)hi - lo + 32) / 32);
+    for (int w = tid; w < nw; w += 256) bits[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KR; ++i)
+      if (tid + 256 * i < L) atomicOr(&bits[(ps[i] - lo) >> 5], 1u << ((ps[i] - lo) & 31));
+    for (int n = tid + 256 * KR; n < L; n += 256) {
+      const int d = pos[n] - lo;
+      atomicOr(&bits[d >> 5], 1u << (d & 31));
+    }
+    __syncthreads();
+    // exclusive prefix of the popcounts per word: WPT words per thread, a
+    // wave scan of the thread sums, then the four waves
+    int cnt[WPT], ts = 0;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int w = tid * WPT + k;
+      cnt[k] = w < nw ? __popc(bits[w]) : 0;
+      ts += cnt[k];
+    }
+    int incl = ts;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int base = incl - ts;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int w = tid * WPT + k;
+      if (w < nw) wpre[w] = base;
+      base += cnt[k];
+    }
+    __syncthreads();
+    auto rank_of = [&](int p) {
+      const int d = p - lo;
+      return wpre[d >> 5] + __popc(bits[d >> 5] & ((1u << (d & 31)) - 1u));
+    };
+#pragma unroll
+    for (int i = 0; i < KR; ++i)
+      if (tid + 256 * i < L) place(tid + 256 * i, rank_of(ps[i]), lv[i]);
+    for (int n = tid + 256 * KR; n < L; n += 256) {
+      float l[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) l[g] = lg[(size_t)n * G + g];
+      place(n, rank_of(pos[n]), l);
+    }
+  } else {
+    int *sp = reinterpret_cast<int *>(bits);  // position tiles in the bitmap's space
+    for (int nb = 0; nb < L; nb += 256) {
+      const int n = nb + tid;
+      const int p = pos[min(n, L - 1)];
+      int rank = 0;
+      for (int t0 = 0; t0 < L; t0 += NW) {
+        const int tn = min(NW, L - t0);
+        __syncthreads();
+        for (int i = tid; i < tn; i += 256) sp[i] = pos[t0 + i];
+        __syncthreads();
+        for (int i = 0; i < tn; ++i) rank += sp[i] < p;
+      }
+      if (n < L) {
+        float l[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) l[g] = lg[(size_t)n * G + g];
+        place(n, rank, l);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. Selection.
   for (int g = wave; g < G; g += 4) {
     const float M = a.ws.stats[((size_t)u * G + g) * 2];
     const float IL = 1.f / a.ws.stats[((size_t)u * G + g) * 2 + 1];
@@ -384,7 +492,7 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
     for (int i = 0; i < NPL; ++i) {
       const int t = lane + 64 * i;
       const bool ok = t < m;
-      pv[i] = ok ? fast_exp2(lg[(size_t)s_slot[t] * G + g] - M) * IL : 0.f;
+      pv[i] = ok ? fast_exp2(s_p[g][t] - M) * IL : 0.f;
       kv[i] = ok ? __float_as_uint(pv[i]) + 1u : 0u;  // 0: no token of the chunk
     }
     auto count_ge = [&](uint32_t thr) {
@@ -411,11 +519,11 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
       kept += __popcll(__ballot(sel));
       s_p[g][lane + 64 * i] = sel ? pv[i] : 0.f;
     }
-    if (lane == 0) a.ws.chunk_cnt[((size_t)u * NC + c) * G + g] = kept;
+    if (lane == 0) store_agent(&a.ws.chunk_cnt[((size_t)u * NC + c) * G + g], kept);
   }
   __syncthreads();
   if (wave == 0) {  // the rows some q-head kept, in chunk order
-    int base = 0;
+    int nbase = 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const int t = lane + 64 * i;
@@ -423,12 +531,14 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) any |= s_p[g][t] > 0.f;
       const uint64_t bm = __ballot(any);
-      if (any) s_list[base + __popcll(bm & ((1ull << lane) - 1ull))] = t;
-      base += __popcll(bm);
+      if (any) s_list[nbase + __popcll(bm & ((1ull << lane) - 1ull))] = t;
+      nbase += __popcll(bm);
     }
-    if (lane == 0) s_nlist = base;
+    if (lane == 0) s_nlist = nbase;
   }
   __syncthreads();
+
+  // 3. P.V over the kept rows.
   const int nl = s_nlist;
   const int rg = tid / LPR, cl = tid - rg * LPR;
   const char *vc = static_cast<const char *>(a.v_cache) + (size_t)u * a.cap * RB;
@@ -437,8 +547,9 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {  // every row load first, from clamped addresses
     const int li = rg + i * RG;
-    tt[i] = nl > 0 ? s_list[min(li, nl - 1)] : 0;  // s_slot[0] always holds a live slot
-    vf[i] = *reinterpret_cast<const uint4 *>(vc + (size_t)s_slot[tt[i]] * RB + cl * 16);
+    tt[i] = nl > 0 ? s_list[min(li, nl - 1)] : 0;
+    const int sl = min(max(s_slot[tt[i]], 0), L - 1);
+    vf[i] = *reinterpret_cast<const uint4 *>(vc + (size_t)sl * RB + cl * 16);
   }
   float acc[G][CH];
 #pragma unroll
@@ -465,7 +576,6 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
       for (int e = 0; e < CH; ++e) acc[g][e] = fmaf(p, vv[e], acc[g][e]);
     }
   }
-  // Sum over the lane groups of a wave, then over the waves.
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1)
 #pragma unroll
@@ -479,36 +589,30 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
       for (int e = 0; e < CH; ++e) s_red[wave][g * D + cl * CH + e] = acc[g][e];
   }
   __syncthreads();
-  float *dst = a.ws.chunk_acc + ((size_t)u * NC + c) * G * D;
-  for (int i = tid; i < G * D; i += 256) dst[i] = s_red[0][i] + s_red[1][i] + s_red[2][i] + s_red[3][i];
-}
 
-// C3: per unit, the G output rows are the sums of its chunks' partials, in
-// chunk order; the debug count is the tokens all chunks kept.
-__global__ __launch_bounds__(256) void k_chunk_reduce(StepArgs a) {
-  const int u = blockIdx.x, tid = threadIdx.x;
-  const int G = a.G, D = a.D;
-  const int b = u / a.Hkv, j = u - b * a.Hkv;
-  const size_t NC = (size_t)((a.cap + D - 1) / D);
-  float *outp = a.out + ((size_t)b * a.Hq + (size_t)j * G) * D;  // the group's rows are adjacent
-  const bool ok = unit_has_tiles(a, u);
-  const int nc = ok ? (a.len[u] + 1 + D - 1) / D : 0;
+  // 4. Partials out, ticket, and the last workgroup's sum over the chunks.
+  float *dst = a.ws.chunk_acc + ((size_t)u * NC + c) * G * D;
+  for (int i = tid; i < G * D; i += 256)
+    store_agent_f(dst + i, s_red[0][i] + s_red[1][i] + s_red[2][i] + s_red[3][i]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ int s_last;
+  const int nc = (L + D - 1) / D;
+  if (tid == 0) s_last = ticket_agent(&a.ws.ticket[u]) == (uint32_t)(nc - 1);
+  __syncthreads();
+  if (!s_last) return;
   for (int i = tid; i < G * D; i += 256) {
-    float s = 0.f;
-    for (int c = 0; c < nc; ++c) s += a.ws.chunk_acc[((size_t)u * NC + c) * G * D + i];
-    outp[i] = s;
+    float sum = 0.f;
+    for (int cc = 0; cc < nc; ++cc)
+      sum += __int_as_float(load_agent(reinterpret_cast<const int32_t *>(a.ws.chunk_acc + ((size_t)u * NC + cc) * G * D + i)));
+    outp[i] = sum;
   }
   if (a.dbg_count && tid < G) {
     int k = 0;
-    for (int c = 0; c < nc; ++c) k += a.ws.chunk_cnt[((size_t)u * NC + c) * G + tid];
+    for (int cc = 0; cc < nc; ++cc) k += load_agent(&a.ws.chunk_cnt[((size_t)u * NC + cc) * G + tid]);
     a.dbg_count[(size_t)b * a.Hq + (size_t)j * G + tid] = k;
   }
-}
-
-hipError_t launch_chunk_rank(const StepArgs &a, hipStream_t s) {
-  const dim3 grid((a.cap + kRankThreads - 1) / kRankThreads, a.n_units);
-  hipLaunchKernelGGL(k_chunk_rank, grid, dim3(kRankThreads), 0, s, a);
-  return hipGetLastError();
+  if (tid == 0) a.ws.ticket[u] = 0;  // the accumulation launch counts on it from zero
 }
 
 template <int EL, int D>
@@ -530,11 +634,6 @@ hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s) {
     if (a.D == 128) chunk_pv_g<4, 128>(a, grid, s);
     else chunk_pv_g<4, 64>(a, grid, s);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_chunk_reduce(const StepArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_chunk_reduce, dim3(a.n_units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

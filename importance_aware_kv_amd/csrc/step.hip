@@ -16,15 +16,18 @@
 //   lands; q.k is reduced over a token row's lanes with DPP and every row
 //   keeps an online softmax; the tile writes its logits, (max, sum) per head
 //   and P.V partial.
-// K2 k_finalize -- the same tiles.  The launch boundary makes K1's writes
-//   visible, so each tile reads its unit's partials with plain loads: unit
-//   softmax statistics, a slice of the output (tiles of a unit split the
-//   G*D outputs), the importance of its own tokens and its lowest eviction
-//   key.  The last tile of the unit to finish (atomic ticket) picks the
-//   victim and writes the new token straight into the victim's slot, so no
-//   row is ever moved in the steady state.  A unit that must shed more than
-//   one token (first step after a prefill) is compacted by its last tile with
-//   a radix select.
+// K2 k_finalize -- importance blocks (2048 tokens of a unit each) and output
+//   blocks.  The launch boundary makes K1's writes visible.  An importance
+//   block turns its tokens' logits into probabilities with the unit's
+//   statistics, adds them to the importance (with the HiKV dual bank only
+//   inside the recent window), and leaves its lowest eviction key in the
+//   cache's pending-eviction record; the next call's attention launch takes
+//   the lowest of those as the victim, skips it, and the new token is then
+//   written into its slot, so no row moves in the steady state.  A unit that
+//   must shed more than one token (the first step after a prefill) is cut in
+//   bulk by a radix select; with the caller's lengths and budgets the row
+//   moves of that cut go to a third launch (k_bulk_moves).  Output blocks
+//   combine the tiles' partials.
 
 #include <hip/hip_ext.h>
 

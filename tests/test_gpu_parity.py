@@ -552,3 +552,19 @@ def test_stage2_chunks_repeat_is_bit_identical():
         outs.append(np.stack([run.step(d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t])[0]
                               for t in range(w.steps)]))
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_stage2_chunks_positions_beyond_the_rank_bitmap():
+    """Positions spread over a span wider than the rank bitmap (131072):
+    the chunk order falls back to counting; results stay the same."""
+    B, Hkv, G, D, cap = 1, 2, 4, 128, 700
+    st = W.random_cache(41, B, G * Hkv, Hkv, D, W.BF16, cap, [[500, 299]])
+    rng = np.random.Generator(np.random.PCG64(42))
+    newest = 400000
+    for j in range(Hkv):
+        n = int(st["len"][0, j])
+        st["pos"][0, j, :n] = rng.permutation(rng.choice(newest, size=n, replace=False)).astype(np.int32)
+    data = W.random_step(43, B, G * Hkv, Hkv, D, W.BF16, newest)
+    data = {k: v[None] for k, v in data.items()}
+    run = GpuRun(st, G * Hkv, budget_all=200, n_sink=2, n_recent=16, r=32, stage2_v=H.HIKV_S2V_CHUNK)
+    lockstep(run, data, 1, tag="chunks sparse positions")
