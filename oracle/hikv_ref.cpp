@@ -160,7 +160,9 @@ void evict_unit(const Dims &d, const Unit &x, const hikv_ref_policy *pol, int be
 
 bool policy_ok(const Dims &d, const hikv_ref_policy *pol) {
   if (!pol || pol->n_sink < 0 || pol->n_recent < 0) return false;
-  if (pol->accumulate != HIKV_REF_ACC_ALL && pol->accumulate != HIKV_REF_ACC_RECENT) return false;
+  if (pol->accumulate != HIKV_REF_ACC_ALL && pol->accumulate != HIKV_REF_ACC_RECENT &&
+      pol->accumulate != HIKV_REF_ACC_LOGIT)
+    return false;
   if (pol->stage2_channels < 0 || pol->stage2_channels > d.D) return false;
   if (pol->stage2_v != HIKV_REF_S2V_TOPK && pol->stage2_v != HIKV_REF_S2V_CHUNK) return false;
   if (pol->stage2_channels > 0 && pol->stage2_v == HIKV_REF_S2V_TOPK && pol->stage2_tokens < 1)
@@ -211,6 +213,7 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
       const int L = *x.len;
 
       std::vector<double> added(L, 0.0);  // importance this step, per slot
+      const bool by_logit = pol->accumulate == HIKV_REF_ACC_LOGIT;
       for (int g = 0; g < d.G; ++g) {
         const int h = j * d.G + g;
         std::vector<double> qh(d.D);
@@ -229,7 +232,7 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
           std::vector<double> p = softmax(s);
           for (int n = 0; n < L; ++n) {
             for (int c = 0; c < d.D; ++c) o[c] += p[n] * val_elem(d, x, n, c);
-            added[n] += p[n];
+            added[n] += by_logit ? s[n] : p[n];
           }
         } else {
           // Stage II, K side: channels with the largest |q_d|.
@@ -249,7 +252,7 @@ extern "C" int hikv_ref_decode_step(const hikv_ref_shape *shape, const hikv_ref_
             st[n] = d.scale * acc;
           }
           std::vector<double> pt = softmax(st);
-          for (int n = 0; n < L; ++n) added[n] += pt[n];
+          for (int n = 0; n < L; ++n) added[n] += by_logit ? st[n] : pt[n];
           if (dbg && dbg->sel_channels) {
             std::vector<int> e = E;
             std::sort(e.begin(), e.end());

@@ -29,6 +29,8 @@
  *    Sec. III-D (bank initialisation from windowed prompt scores).
  *  - HiKV Sec. III-C and Algorithm 1 (Stage II V side: chunks of d_h entries
  *    of P, top-B_II per chunk, P.V over the kept rows).
+ *  - Kelle Sec. 4.1 (Eq. 3) and Sec. 5.3 (importance as summed attention
+ *    scores taken before the softmax).
  */
 #ifndef HIKV_REF_H
 #define HIKV_REF_H
@@ -70,6 +72,10 @@ typedef struct {
  * the sum of the W' probabilities it received from its own step on. */
 #define HIKV_REF_ACC_ALL 0
 #define HIKV_REF_ACC_RECENT 1
+/* LOGIT: every live token gains the pre-softmax logit scale * q.k it gets
+ * from the group's queries (Kelle Sec. 5.3: the scores are summed without the
+ * softmax); with Stage II on, the reduced logit. */
+#define HIKV_REF_ACC_LOGIT 2
 
 /* What Stage II does with the approximate probabilities on the V side.
  * TOPK: the k_T tokens with the largest approximate logit get an exact
@@ -86,7 +92,7 @@ typedef struct {
   int32_t budget_all, n_sink, n_recent;
   int32_t stage2_channels; /* r; 0 = Stage II off */
   int32_t stage2_tokens;   /* tokens kept for the exact softmax (k_T) */
-  int32_t accumulate;      /* HIKV_REF_ACC_ALL | HIKV_REF_ACC_RECENT */
+  int32_t accumulate;      /* HIKV_REF_ACC_ALL | HIKV_REF_ACC_RECENT | HIKV_REF_ACC_LOGIT */
   int32_t stage2_v;        /* HIKV_REF_S2V_TOPK | HIKV_REF_S2V_CHUNK (used when r > 0) */
 } hikv_ref_policy;
 

@@ -38,7 +38,7 @@ class Policy(C.Structure):
                 ("stage2_tokens", C.c_int32), ("accumulate", C.c_int32), ("stage2_v", C.c_int32)]
 
 
-ACC_ALL, ACC_RECENT = 0, 1
+ACC_ALL, ACC_RECENT, ACC_LOGIT = 0, 1, 2
 S2V_TOPK, S2V_CHUNK = 0, 1
 
 

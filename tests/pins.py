@@ -57,6 +57,10 @@ What pins what:
       kept: min(r, chunk size) entries, equal to the library's softmax of the
       channel-masked query (no renormalisation), none smaller than an entry
       the chunk dropped; permuting the slots changes nothing.
+  logit_accumulation_matches_library -- Kelle's importance (accumulate =
+      LOGIT): a step adds the group's pre-softmax logits scale * q.k (a
+      library matmul; with Stage II on, of the channel-masked query) to every
+      live token, and the kept set is the brute-force one for that importance.
 """
 
 from __future__ import annotations
@@ -677,9 +681,42 @@ def stage2_chunks_select_by_probability(seed=53):
         assert code == 0 and np.abs(outp - out).max() <= 1e-12, c0
 
 
+def logit_accumulation_matches_library(seed=59):
+    B, Hkv, G, D, cap = 1, 2, 3, 16, 40
+    Hq = Hkv * G
+    st0 = W.random_cache(seed, B, Hq, Hkv, D, W.F32, cap, [[15, 8]])
+    step = W.random_step(seed + 1, B, Hq, Hkv, D, W.F32, st0["newest"])
+    scale = 1.0 / math.sqrt(D)
+    beta, S, R = 12, 2, 4
+    newest = int(step["new_pos"][0])
+    for r in (0, 5):
+        st = ref.copy_state(st0)
+        code, _, dbg = ref.decode_step(st, Hq, step["q"], step["k_new"], step["v_new"], step["new_pos"],
+                                       budget_all=beta, n_sink=S, n_recent=R, stage2_channels=r,
+                                       stage2_tokens=8 if r else 0, accumulate=ref.ACC_LOGIT)
+        assert code == 0
+        for j in range(Hkv):
+            k, _, pos, imp = _unit_rows(st0, 0, j, W.F32)
+            k = np.concatenate([k, widen(step["k_new"][0, j], W.F32)[None]])
+            pos = np.append(pos, newest)
+            L = k.shape[0]
+            q = widen(step["q"][0, j * G:(j + 1) * G], W.F32)
+            if r:
+                for g in range(G):
+                    keep_ch = np.argsort(-np.abs(q[g]), kind="stable")[:r]
+                    mask = np.zeros(D, dtype=bool)
+                    mask[keep_ch] = True
+                    q[g, ~mask] = 0.0
+            want = np.matmul(q, k.T).sum(0) * scale            # [L]
+            got = dbg["imp_pre_evict"][0, j, :L].astype(np.float64) - np.append(imp, 0.0)
+            assert np.abs(got - want).max() <= 1e-5 * max(1.0, np.abs(want).max()), (r, j)
+            kept = _brute_kept(pos, dbg["imp_pre_evict"][0, j, :L].astype(np.float64), beta, S, R, newest)
+            assert set(ref.live_positions(st, 0, j).tolist()) == kept, (r, j)
+
+
 ALL = [attention_matches_library, rows_sum_to_group, streaming_closed_form, eviction_brute_force,
        golden_cases, permutation_invariance, channel_permutation, conservation,
        stage2_reduces_to_stage1, stage2_selection, equal_keys_closed_form, prefill_column_sums,
        errors_leave_unit_unchanged, heap_worked_examples, heap_keeps_the_top_scores,
        dual_bank_matches_its_definition, stage2_chunks_reduce_to_attention,
-       stage2_chunks_select_by_probability]
+       stage2_chunks_select_by_probability, logit_accumulation_matches_library]

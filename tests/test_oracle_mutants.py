@@ -21,7 +21,7 @@ MUTANTS = [
     ("tie_keeps_newer", "      return x.pos[a] < x.pos[b];\n    });",
      "      return x.pos[a] > x.pos[b];\n    });"),
     ("window_off_by_one", "(x.pos[n] > newest - W)", "(x.pos[n] >= newest - W)"),
-    ("importance_from_logits", "            added[n] += p[n];", "            added[n] += s[n];"),
+    ("importance_from_logits", "added[n] += by_logit ? s[n] : p[n];", "added[n] += s[n];"),
     ("gqa_group_strided", "        const int h = j * d.G + g;\n        std::vector<double> qh",
      "        const int h = g * d.Hkv + j;\n        std::vector<double> qh"),
     ("stage2_smallest_channels", "if (fa != fb) return fa > fb;", "if (fa != fb) return fa < fb;"),
@@ -54,6 +54,8 @@ MUTANTS = [
     ("chunks_keep_smallest", "if (pt[a] != pt[bb]) return pt[a] > pt[bb];", "if (pt[a] != pt[bb]) return pt[a] < pt[bb];"),
     ("chunks_of_r_tokens", "for (int c0 = 0; c0 < L; c0 += d.D) {", "for (int c0 = 0; c0 < L; c0 += r) {"),
     ("chunks_keep_one_more", "const int keep = std::min(r, m);", "const int keep = std::min(r + 1, m);"),
+    ("logit_acc_uses_probabilities", "added[n] += by_logit ? s[n] : p[n];", "added[n] += p[n];"),
+    ("logit_acc_stage2_uses_probabilities", "added[n] += by_logit ? st[n] : pt[n];", "added[n] += pt[n];"),
     ("chunks_use_exact_logits", "            st[n] = d.scale * acc;\n          }\n          std::vector<double> pt = softmax(st);",
      "            st[n] = d.scale * acc;\n          }\n          std::vector<double> pt = softmax(st);\n"
      "          if (pol->stage2_v == HIKV_REF_S2V_CHUNK) {\n"
