@@ -62,6 +62,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--workload", default="headkv32k")
+    ap.add_argument("--accumulate", choices=["all", "recent", "logit"], default=None,
+                    help="override the workload's importance accumulation (H2O probabilities, HiKV's "
+                         "recent window only, Kelle's pre-softmax logits)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-hint", action="store_true", help="do not pass host lengths")
@@ -88,6 +91,8 @@ def main():
     n_inputs = 256
     full = args.workload.endswith("_full")
     w = W.workload(args.workload[:-5] if full else args.workload, steps=n_inputs, full=full)
+    if args.accumulate is not None:
+        w.accumulate = {"all": H.HIKV_ACC_ALL, "recent": H.HIKV_ACC_RECENT, "logit": H.HIKV_ACC_LOGIT}[args.accumulate]
     # compression step + warm-up + the timed steps + the same number again for
     # the per-kernel timing replay
     per_layer_steps = 1 + (args.warmup + 2 * args.steps + args.layers - 1) // args.layers
@@ -323,8 +328,10 @@ def workload_text(w, budget, full):
     if w.stage2_channels and w.stage2_v:
         s2 = (f", Stage II r = {w.stage2_channels} channels and, on the V side, the top {w.stage2_channels} "
               f"entries of P per chunk of {w.head_dim} positions (HiKV)")
-    if w.accumulate:
+    if w.accumulate == 1:
         s2 += ", HiKV dual bank (scores accumulate only in the recent window, frozen outside it)"
+    elif w.accumulate == 2:
+        s2 += ", Kelle importance (pre-softmax logits summed)"
     return (f"{w.name} {'decode' if full else 'steady state'}: batch {w.batch}, {heads}, D {w.head_dim}, "
             f"{dt} KV, {w.ctx}-token prefill, {pol}, sinks {w.n_sink}, recent {w.n_recent}{s2}")
 

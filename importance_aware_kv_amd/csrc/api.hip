@@ -44,7 +44,8 @@ int check_shape(const hikv_shape *s) {
 int check_policy(const hikv_shape *s, const hikv_policy *p) {
   if (!p) return HIKV_EINVAL;
   if (p->n_sink < 0 || p->n_recent < 0) return HIKV_EINVAL;
-  if (p->accumulate != HIKV_ACC_ALL && p->accumulate != HIKV_ACC_RECENT) return HIKV_EINVAL;
+  if (p->accumulate != HIKV_ACC_ALL && p->accumulate != HIKV_ACC_RECENT && p->accumulate != HIKV_ACC_LOGIT)
+    return HIKV_EINVAL;
   if (p->stage2_channels < 0 || p->stage2_channels > s->head_dim) return HIKV_EINVAL;
   if (p->stage2_v != HIKV_S2V_TOPK && p->stage2_v != HIKV_S2V_CHUNK) return HIKV_EINVAL;
   if (p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_TOPK && p->stage2_tokens < 1) return HIKV_EINVAL;
@@ -88,6 +89,7 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
   a.n_sink = p->n_sink;
   a.n_recent = p->n_recent;
   a.acc_recent = p->accumulate == HIKV_ACC_RECENT;
+  a.acc_logit = p->accumulate == HIKV_ACC_LOGIT;
   a.r = p->stage2_channels;
   a.s2_chunks = p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_CHUNK;
   a.kT = (p->stage2_channels > 0 && !a.s2_chunks) ? p->stage2_tokens : 0;

@@ -439,7 +439,8 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
   for (int n = t0 + tid; n < t1; n += 256) {
     float p = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) p += fast_exp2(lg[(size_t)n * G + g] - M[g]) * IL[g];
+    for (int g = 0; g < G; ++g)  // Kelle's score: the logit itself (stored in log2 units)
+      p += a.acc_logit ? lg[(size_t)n * G + g] * 0.69314718055994531f : fast_exp2(lg[(size_t)n * G + g] - M[g]) * IL[g];
     const bool is_new = n == L - 1;
     const int pn = (over || a.acc_recent) ? pos[n] : 0;
     // HiKV's dual bank: only the recent window accumulates; older scores are

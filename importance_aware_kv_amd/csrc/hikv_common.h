@@ -156,6 +156,7 @@ struct StepArgs {
   const int32_t *budget;     // may be null
   int32_t budget_all, n_sink, n_recent;
   int32_t acc_recent;        // importance accumulates only inside the protected window (HiKV dual bank)
+  int32_t acc_logit;         // importance accumulates pre-softmax logits (Kelle)
   int32_t r, kT;             // Stage II
   int32_t s2_chunks;         // Stage II V side: HiKV's per-chunk top-r of P (else exact top-k_T)
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it

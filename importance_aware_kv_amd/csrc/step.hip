@@ -1323,6 +1323,8 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       const int nact = (L + CHUNK - 1) / CHUNK;  // blocks holding tokens of the unit
       const int Wp = min(a.n_recent, beta - S);
       const int fs = (dead >= 0 && !bulk) ? dead : Lold;  // the new token's slot
+      // Kelle's pre-softmax score: the logit scale * q.k (raw q.k times scale)
+      const float scale_nat = a.scale_log2 * 0.69314718055994531f;
       float Mg[G], ILg[G];
     #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1341,7 +1343,8 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
           if (n < nb1 && n != dead) {
             float p = 0.f;
     #pragma unroll
-            for (int g = 0; g < G; ++g) p += fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
+            for (int g = 0; g < G; ++g)
+              p += a.acc_logit ? tl[i][g] * scale_nat : fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
             const bool is_new = n == Lold;
             const int pn = is_new ? newest : tp[i];
             const bool recent = pn > newest - Wp;

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libhikv.so")
 
 HIKV_F32, HIKV_BF16 = 0, 1
-HIKV_ACC_ALL, HIKV_ACC_RECENT = 0, 1
+HIKV_ACC_ALL, HIKV_ACC_RECENT, HIKV_ACC_LOGIT = 0, 1, 2
 HIKV_S2V_TOPK, HIKV_S2V_CHUNK = 0, 1
 HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
 

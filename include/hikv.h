@@ -90,6 +90,7 @@ typedef struct hikv_cache {
 
 #define HIKV_ACC_ALL 0
 #define HIKV_ACC_RECENT 1
+#define HIKV_ACC_LOGIT 2
 
 #define HIKV_S2V_TOPK 0
 #define HIKV_S2V_CHUNK 1
@@ -124,8 +125,12 @@ typedef struct hikv_policy {
                               ([HiKV] Sec. III-B): the window is the recent bank, the rest the
                               important bank, each score sums the W' probabilities a token
                               received from its own step on, and a token leaving the window
-                              displaces the bank's lowest score iff its own is higher.  Any
-                              other value is HIKV_EINVAL. */
+                              displaces the bank's lowest score iff its own is higher.
+                              HIKV_ACC_LOGIT: every live token gains the pre-softmax logit
+                              scale * q.k it gets from the group's q-heads ([Kelle] Sec. 4.1
+                              Eq. 3 and Sec. 5.3: attention scores summed without the
+                              softmax); with Stage II on, the reduced logit.  Scores can be
+                              negative.  Any other value is HIKV_EINVAL. */
   int32_t stage2_v;        /* Stage II's V side (used when r > 0):
                               HIKV_S2V_TOPK: the k_T tokens with the largest reduced logit get
                               an exact full-channel softmax, renormalised over them, and P.V.

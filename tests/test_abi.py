@@ -84,7 +84,12 @@ def test_decode_step_host_checks():
     assert call(_shape(), q=C.c_void_p(0x1008)) == H.HIKV_EINVAL                    # alignment
     assert call(_shape(), ws_bytes=16) == H.HIKV_EINVAL                             # workspace
     assert call(_shape(), pol=H.make_policy(budget_all=8, n_recent=-2)) == H.HIKV_EINVAL
-    assert call(_shape(), pol=H.make_policy(budget_all=8, accumulate=2)) == H.HIKV_EINVAL  # unknown mode
+    assert call(_shape(), pol=H.make_policy(budget_all=8, accumulate=3)) == H.HIKV_EINVAL  # unknown mode
+    assert call(_shape(), pol=H.make_policy(budget_all=8, stage2_channels=8, stage2_v=2)) == H.HIKV_EINVAL
+    # the chunked V side needs no k_T; the exact top-k_T side does
+    assert call(_shape(batch=0), pol=H.make_policy(budget_all=8, stage2_channels=8,
+                                                   stage2_v=H.HIKV_S2V_CHUNK)) == H.HIKV_OK
+    assert call(_shape(), pol=H.make_policy(budget_all=8, stage2_channels=8)) == H.HIKV_EINVAL
     assert call(_shape(batch=0), pol=H.make_policy(budget_all=8, accumulate=H.HIKV_ACC_RECENT)) == H.HIKV_OK
     assert call(_shape(batch=0)) == H.HIKV_OK                                       # empty batch
     assert L.hikv_evict(C.byref(_shape()), C.byref(cache), C.byref(pol), None, fake, 1 << 30,

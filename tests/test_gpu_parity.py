@@ -568,3 +568,20 @@ def test_stage2_chunks_positions_beyond_the_rank_bitmap():
     data = {k: v[None] for k, v in data.items()}
     run = GpuRun(st, G * Hkv, budget_all=200, n_sink=2, n_recent=16, r=32, stage2_v=H.HIKV_S2V_CHUNK)
     lockstep(run, data, 1, tag="chunks sparse positions")
+
+
+# ---------------------------------------------------------------------------
+# Kelle's importance: pre-softmax logits summed (accumulate = LOGIT).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path", ["two-launch", "two-launch-hint", "multi-kernel", "stage2", "stage2-chunks"])
+def test_logit_accumulation_lockstep(path, monkeypatch):
+    w = W.workload("llama8b", ctx=1000, steps=4, batch=2)
+    w.budget_all, w.n_recent, w.accumulate = 256, 32, H.HIKV_ACC_LOGIT
+    if path.startswith("stage2"):
+        w.stage2_channels, w.stage2_tokens = 32, 64
+        if path == "stage2-chunks":
+            w.stage2_v = H.HIKV_S2V_CHUNK
+    if path == "multi-kernel":
+        monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
+    d = W.generate(w)
+    lockstep(_run(w, d, hint=path == "two-launch-hint"), d, w.steps, tag=f"logit accumulation {path}")
