@@ -255,7 +255,10 @@ extern "C" size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t 
   if (check_shape(shape) != HIKV_OK || n_obs < 0) return 0;
   const size_t U = (size_t)shape->batch * shape->n_kv_heads;
   const size_t G = (size_t)(shape->n_q_heads / shape->n_kv_heads);
-  return 256 + align256(sizeof(float) * U * G * (size_t)(n_obs > 0 ? n_obs : 1) * 2);
+  const size_t nobs = n_obs > 0 ? (size_t)n_obs : 1;
+  const size_t nkt = ((size_t)shape->capacity + 63) / 64, nqt = (nobs + 63) / 64;
+  return 256 + align256(sizeof(float) * U * G * nobs * 2) + align256(sizeof(int32_t) * U * nkt * 2) +
+         align256(sizeof(int32_t) * (size_t)shape->batch * nqt * 2);
 }
 
 extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *cache,
@@ -290,6 +293,12 @@ extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *ca
   p.q_pos = q_pos;
   p.status = static_cast<int32_t *>(ws);
   p.stats = reinterpret_cast<float *>(static_cast<char *>(ws) + 256);
+  {
+    const size_t U = (size_t)p.n_units, nkt = ((size_t)p.cap + 63) / 64;
+    char *r = static_cast<char *>(ws) + 256 + align256(sizeof(float) * U * p.G * (size_t)n_obs * 2);
+    p.krange = reinterpret_cast<int32_t *>(r);
+    p.qrange = reinterpret_cast<int32_t *>(r + align256(sizeof(int32_t) * U * nkt * 2));
+  }
   return dev_err(launch_prefill(p, shape->kv_dtype, static_cast<hipStream_t>(stream)));
 }
 

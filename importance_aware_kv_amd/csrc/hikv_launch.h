@@ -50,6 +50,8 @@ struct PrefillArgs {
   const void *q_obs;
   const int32_t *q_pos;
   float *stats;       // [U][G][n_obs][2]
+  int32_t *krange;    // [U][ceil(cap/64)][2] lowest, highest position of each 64-slot tile
+  int32_t *qrange;    // [B][ceil(n_obs/64)][2] lowest, highest position of each 64-query tile
   int32_t *status;
 };
 hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s);

@@ -585,3 +585,58 @@ def test_logit_accumulation_lockstep(path, monkeypatch):
         monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
     d = W.generate(w)
     lockstep(_run(w, d, hint=path == "two-launch-hint"), d, w.steps, tag=f"logit accumulation {path}")
+
+
+# ---------------------------------------------------------------------------
+# Prompt-side scores at scale (matrix cores for bf16, vector ALUs for fp32).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D", [(W.BF16, 128), (W.BF16, 64), (W.F32, 128)], ids=["bf16-128", "bf16-64", "f32-128"])
+@pytest.mark.parametrize("window,n_obs,shuffle", [(0, 300, True), (64, 300, False), (64, 37, True), (0, 1, False)])
+def test_prefill_scores_tiles(dtype, D, window, n_obs, shuffle):
+    """300 prompt tokens in 5 key tiles (the last one ragged), all or the last
+    n_obs queries, slots in position order or shuffled, a pre-existing score."""
+    B, Hkv, G = 2, 2, 4
+    L, cap = 300, 320
+    rng = np.random.Generator(np.random.PCG64(50 + window + n_obs + D))
+    st = W.random_cache(51 + D, B, G * Hkv, Hkv, D, dtype, cap, [[L, L], [L, L - 45]])
+    for b in range(B):
+        for j in range(Hkv):
+            n = int(st["len"][b, j])
+            p = np.arange(n, dtype=np.int32)
+            st["pos"][b, j, :n] = rng.permutation(p) if shuffle else p
+    qf = rng.standard_normal((B, G * Hkv, n_obs, D)).astype(np.float32)
+    qo = W.bf16_bits(qf) if dtype == W.BF16 else qf
+    qpos = np.broadcast_to(np.arange(L - n_obs, L, dtype=np.int32), (B, n_obs)).copy()
+    run = GpuRun(ref.copy_state(st), G * Hkv, budget_all=cap)
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(run.dev.shape, n_obs), dtype=torch.uint8, device="cuda")
+    say(f"[gpu] prefill tiles dtype={dtype} D={D} window={window} n_obs={n_obs}")
+    assert H.hikv_prefill_scores(run.dev.shape, run.dev.cache, H.to_device(qo), torch.from_numpy(qpos).cuda(),
+                                 n_obs, window, ws) == 0
+    torch.cuda.synchronize()
+    got = run.state()
+    want = ref.copy_state(st)
+    assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=window) == 0
+    np.testing.assert_allclose(got["imp"], want["imp"], rtol=1e-3, atol=1e-5)
+
+
+@pytest.mark.parametrize("window", [0, 512])
+def test_prefill_scores_long_prompt(window):
+    """A 2048-token prompt scored by all its queries (HiKV's bank
+    initialisation uses window B_I / 2)."""
+    B, Hkv, G, D, L = 1, 1, 4, 128, 2048
+    rng = np.random.Generator(np.random.PCG64(60 + window))
+    st = W.random_cache(61, B, G * Hkv, Hkv, D, W.BF16, L, [[L]])
+    st["pos"][0, 0, :L] = np.arange(L, dtype=np.int32)
+    st["imp"][:] = 0.0
+    qo = W.bf16_bits(rng.standard_normal((B, G * Hkv, L, D)).astype(np.float32))
+    qpos = np.arange(L, dtype=np.int32)[None].copy()
+    run = GpuRun(ref.copy_state(st), G * Hkv, budget_all=L)
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(run.dev.shape, L), dtype=torch.uint8, device="cuda")
+    say(f"[gpu] prefill long window={window}")
+    assert H.hikv_prefill_scores(run.dev.shape, run.dev.cache, H.to_device(qo), torch.from_numpy(qpos).cuda(),
+                                 L, window, ws) == 0
+    torch.cuda.synchronize()
+    got = run.state()
+    want = ref.copy_state(st)
+    assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=window) == 0
+    np.testing.assert_allclose(got["imp"], want["imp"], rtol=1e-3, atol=1e-5)
