@@ -27,6 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
+FP32_PEAK_TFLOPS = 157.3         # fp32 vector peak
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_attend_mfma_hbm_traffic_headkv32k.md")
 KERNEL_SOURCES = ("importance_aware_kv_amd/csrc/step.hip", "importance_aware_kv_amd/csrc/hikv_common.h",
                   "importance_aware_kv_amd/csrc/hikv_block.h")
@@ -62,6 +64,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--workload", default="headkv32k")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time hikv_prefill_scores over every prompt query (on by default for the "
+                         "HiKV dual-bank workloads, with the recent bank's window)")
     ap.add_argument("--accumulate", choices=["all", "recent", "logit"], default=None,
                     help="override the workload's importance accumulation (H2O probabilities, HiKV's "
                          "recent window only, Kelle's pre-softmax logits)")
@@ -175,6 +180,9 @@ def main():
 
     moves_log = []
     stream = torch.cuda.current_stream()
+    prefill = None
+    if (args.prefill or w.accumulate == H.HIKV_ACC_RECENT) and not full:
+        prefill = measure_prefill(w, layers[0], budget, log)
     # Compression step of every layer copy (32769 tokens -> budget), queued
     # behind a GPU-side wait so that the steps run back to back.
     torch.cuda.synchronize()
@@ -312,7 +320,58 @@ def main():
         ("first_step_us" if full else "compression_step_us"): round(comp_ms * 1e3, 2),
         "cpu_baseline": cpu,
     }
+    if prefill is not None:
+        line["prefill_scores"] = prefill
     print(json.dumps(line), flush=True)
+
+
+def measure_prefill(w, layer, budget, log, reps=3):
+    """Prompt-side scores as HiKV initialises its banks (Sec. III-D): every
+    prompt query adds its causal attention row to the tokens within the
+    window (the recent bank's size) of it; window 0 (other workloads) counts
+    every query.  Timed on a copy of one layer's prefilled cache, with seeded
+    synthetic prompt queries; the decode measurement does not use it."""
+    import torch
+
+    from importance_aware_kv_amd import hikv as H
+    B, Hq, D, L = w.batch, w.n_q_heads, w.head_dim, w.ctx
+    c = H.DeviceCache.__new__(H.DeviceCache)
+    c.torch = torch
+    c.dtype, c.shape = layer.dtype, layer.shape
+    for f in ("k", "v", "pos", "imp", "len", "evict"):
+        setattr(c, f, getattr(layer, f).clone())
+    c.imp.zero_()
+    c.cache = c.make_cache()
+    window = int(min(w.n_recent, int(budget.min()) - w.n_sink)) if w.accumulate == H.HIKV_ACC_RECENT else 0
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 17)
+    qdt = torch.bfloat16 if w.el == 2 else torch.float32
+    qo = torch.randn((B, Hq, L, D), generator=gen, device="cuda", dtype=torch.float32).to(qdt)
+    qpos = torch.arange(L, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(c.shape, L), dtype=torch.uint8, device="cuda")
+
+    def call():
+        H.check(H.hikv_prefill_scores(c.shape, c.cache, qo, qpos, L, window, ws), "hikv_prefill_scores")
+
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    causal = L * (L + 1) // 2                                   # (query, visible key) pairs
+    inwin = causal if window == 0 else window * (window + 1) // 2 + (L - window) * window
+    flops = 2 * D * (causal + inwin) * B * Hq                  # q.k for the statistics, again for the sums
+    tf = flops / (us * 1e-6) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if w.el == 2 else FP32_PEAK_TFLOPS
+    log(f"[bench] prefill scores: {L} queries, window {window}: {us:.1f} us, {tf:.1f} TFLOP/s")
+    del qo
+    return {"queries": L, "window": window, "us": round(us, 1), "bound": "mfma" if w.el == 2 else "alu",
+            "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+            "flops": flops}
 
 
 def workload_text(w, budget, full):
