@@ -271,6 +271,9 @@ extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *ca
   if ((st = check_cache(cache)) != HIKV_OK) return st;
   if (!q_obs || !q_pos || !ws || !aligned16(q_obs) || !aligned16(ws)) return HIKV_EINVAL;
   if (ws_bytes < hikv_prefill_workspace_bytes(shape, n_obs)) return HIKV_EINVAL;
+  // the matrix-core passes track at most 32768 tiles of 64 (keys or queries)
+  if (shape->kv_dtype == HIKV_BF16 && ((long long)shape->capacity > 32768LL * 64 || (long long)n_obs > 32768LL * 64))
+    return HIKV_EUNSUPPORTED;
   if ((st = arch_ok()) != HIKV_OK) return st;
   PrefillArgs p;
   memset(&p, 0, sizeof p);

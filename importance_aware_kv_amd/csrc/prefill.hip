@@ -123,28 +123,34 @@ __global__ __launch_bounds__(256) void k_prefill_accum(PrefillArgs p) {
 
 // ---------------------------------------------------------------------------
 // The same two passes on the matrix cores (bf16), for prompts of thousands of
-// tokens: S = q.k tiles of 64 queries x 64 keys from v_mfma_f32_16x16x16_bf16,
+// tokens: S = q.k tiles of 64 queries x 64 keys from v_mfma_f32_16x16x32_bf16
 // with K rows as the A operand (16 keys) and q rows as the B operand (16
-// queries), so a lane holds four keys of one query.
+// queries), so a lane holds four keys of one query.  A lane feeds both
+// operands the same eight of the 32 contracted elements (the sum over them
+// does not depend on which eight).  Each wave keeps all four blocks of its
+// stationary operand in registers, so one LDS read of the streaming operand
+// feeds four products.
 //   R   per 64-slot key tile of each unit, the lowest and highest position of
 //       its live slots; per 64-query tile of each batch row, the lowest and
 //       highest query position.  Tiles that cannot meet are skipped below.
 //   S1  one workgroup per (64-query tile, unit, q-head): the queries stay in
-//       registers, the unit's key tiles pass through LDS; each lane keeps an
-//       online max and sum of its four keys per tile, merged at the end.
+//       registers, the unit's key tiles pass through LDS, wave w taking keys
+//       16w..16w+15 of each; every lane keeps an online max and sum per
+//       query block, merged over lanes and waves at the end.
 //   S2  one workgroup per (64-slot key tile, unit): the keys stay in
 //       registers, the query tiles of every q-head of the group pass through
-//       LDS with their statistics; each lane sums its four keys' probability
-//       over its queries, the sums meet across lanes at the end, and the
-//       tile adds them to its importance.  No float atomics: repeatable.
+//       LDS with their statistics, wave w taking queries 16w..16w+15 of
+//       each; every lane sums its keys' probabilities over its queries, and
+//       the sums meet over lanes and waves at the end and are added to the
+//       tile's importance.  No float atomics: repeatable.
 // ---------------------------------------------------------------------------
 constexpr int kPT = 64;  // rows of a key or query tile
 
-typedef __bf16 pbf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float pf32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ pf32x4_t pmfma(pbf16x4_t a, pbf16x4_t b, pf32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+__device__ __forceinline__ pf32x4_t pmfma(pbf16x8_t a, pbf16x8_t b, pf32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(64) void k_prefill_ranges(PrefillArgs p) {
@@ -175,162 +181,328 @@ __global__ __launch_bounds__(64) void k_prefill_ranges(PrefillArgs p) {
   }
 }
 
-// 64 rows of D bf16 from global memory (row r of the tile -> global row
-// row0 + r, clamped to last) into LDS rows of D * 2 + 16 bytes (the pad
-// keeps the 16 rows an MFMA operand read touches in distinct banks).
+// A tile of 64 rows of D bf16 moves global memory -> registers (issued one
+// tile ahead of its use) -> LDS rows of D * 2 + 16 bytes (the pad spreads
+// the 16 rows an operand read touches over the banks).  Row r of the tile
+// is global row row0 + r, clamped to last.
+typedef unsigned int pu32x4_t __attribute__((ext_vector_type(4)));
+
 template <int D>
-__device__ __forceinline__ void stage_rows(char *lds, const char *src, size_t stride, int row0, int last,
+struct TileShape {
+  static constexpr int RB = D * 2, LRB = RB + 16, CPR = RB / 16, RPP = 256 / CPR, REPS = kPT / RPP;
+};
+
+template <int D>
+__device__ __forceinline__ void tile_fetch(pu32x4_t (&v)[TileShape<D>::REPS], const char *src, int row0, int last,
                                            int tid) {
-  constexpr int RB = D * 2, LRB = RB + 16, CPR = RB / 16, RPP = 256 / CPR;
+  using T = TileShape<D>;
 #pragma unroll
-  for (int rep = 0; rep < kPT / RPP; ++rep) {
-    const int r = rep * RPP + tid / CPR, c = tid % CPR;
-    const int gr = min(row0 + r, last);
-    const uint4 v = *reinterpret_cast<const uint4 *>(src + (size_t)gr * stride + c * 16);
-    *reinterpret_cast<uint4 *>(lds + r * LRB + c * 16) = v;
+  for (int rep = 0; rep < T::REPS; ++rep) {
+    const int r = rep * T::RPP + tid / T::CPR, c = tid % T::CPR;
+    v[rep] = *reinterpret_cast<const pu32x4_t *>(src + (size_t)min(row0 + r, last) * T::RB + c * 16);
   }
 }
 
 template <int D>
+__device__ __forceinline__ void tile_put(const pu32x4_t (&v)[TileShape<D>::REPS], char *lds, int tid) {
+  using T = TileShape<D>;
+#pragma unroll
+  for (int rep = 0; rep < T::REPS; ++rep) {
+    const int r = rep * T::RPP + tid / T::CPR, c = tid % T::CPR;
+    *reinterpret_cast<pu32x4_t *>(lds + r * T::LRB + c * 16) = v[rep];
+  }
+}
+
+// Which tiles of a loop are worth visiting, as a bitmask in LDS (one bit per
+// tile, at most kMaxTiles), built by the whole workgroup; next() finds the
+// next set bit after t (or n when none is left).
+constexpr int kMaxTiles = 32768;
+struct TileMask {
+  uint32_t *w;
+  int n;
+  __device__ __forceinline__ int next(int t) const {
+    int i = t + 1;
+    while (i < n) {
+      const uint32_t m = w[i >> 5] >> (i & 31);
+      if (m) return min(i + __builtin_ctz(m), n);
+      i = (i | 31) + 1;
+    }
+    return n;
+  }
+};
+
+template <int D>
 __global__ __launch_bounds__(256) void k_prefill_stats_mfma(PrefillArgs p) {
-  constexpr int RB = D * 2, LRB = RB + 16, KS = D / 16;
+  constexpr int RB = D * 2, LRB = RB + 16, KS = D / 32;
   const int qt = blockIdx.x, ug = blockIdx.y, g = ug % p.G, u = ug / p.G;
   const int b = u / p.Hkv, j = u - b * p.Hkv, h = j * p.G + g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, col = lane & 15;
   const int L = min(p.len[u], p.cap);
   const int nkt = (p.cap + kPT - 1) / kPT, nqt = (p.n_obs + kPT - 1) / kPT;
-  const int i = qt * kPT + wave * 16 + col;  // this lane's query
-  const int ic = min(i, p.n_obs - 1);
-  const int qp = p.q_pos[(size_t)b * p.n_obs + ic];
-  const char *qrow = static_cast<const char *>(p.q_obs) + (((size_t)(b * p.Hq + h)) * p.n_obs + ic) * RB;
-  pbf16x4_t qb[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const pbf16x4_t *>(qrow + ks * 32 + quad * 8);
+  const int ntile = (L + kPT - 1) / kPT;
   const int qmax = p.qrange[((size_t)b * nqt + qt) * 2 + 1];
+  __shared__ uint32_t sMask[kMaxTiles / 32], sFull[kMaxTiles / 32];
   __shared__ __attribute__((aligned(16))) char sK[kPT * LRB];
   __shared__ int sP[kPT];
+  __shared__ float sML[4][kPT][2];
+  const int qmin = p.qrange[((size_t)b * nqt + qt) * 2];
+  // key tiles with some key at or before the tile's last query; of those,
+  // the complete ones wholly at or before its first query need no mask
+  for (int w = tid; w < (ntile + 31) / 32; w += 256) sMask[w] = 0u, sFull[w] = 0u;
+  __syncthreads();
+  for (int t = tid; t < ntile; t += 256) {
+    if (p.krange[((size_t)u * nkt + t) * 2] <= qmax) atomicOr(&sMask[t >> 5], 1u << (t & 31));
+    if (p.krange[((size_t)u * nkt + t) * 2 + 1] <= qmin && (t + 1) * kPT <= L)
+      atomicOr(&sFull[t >> 5], 1u << (t & 31));
+  }
+  const char *qbase = static_cast<const char *>(p.q_obs) + ((size_t)(b * p.Hq + h)) * p.n_obs * RB;
+  pbf16x8_t qb[4][KS];  // B operands: the tile's four query blocks
+  int qp[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int ic = min(qt * kPT + blk * 16 + col, p.n_obs - 1);
+    qp[blk] = p.q_pos[(size_t)b * p.n_obs + ic];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[blk][ks] = *reinterpret_cast<const pbf16x8_t *>(qbase + (size_t)ic * RB + ks * 64 + quad * 16);
+  }
   const char *kc = static_cast<const char *>(p.k_cache) + (size_t)u * p.cap * RB;
   const int32_t *pos = p.pos + (size_t)u * p.cap;
-  float m = -INFINITY, l = 0.f;
-  for (int kt = 0; kt * kPT < L; ++kt) {
-    if (p.krange[((size_t)u * nkt + kt) * 2] > qmax) continue;  // every key after every query
+  __syncthreads();
+  const TileMask mask{sMask, ntile};
+  float m[4], l[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) m[blk] = -INFINITY, l[blk] = 0.f;
+  pu32x4_t pre[TileShape<D>::REPS];
+  int ppos = INT_MAX;
+  int kt = mask.next(-1);
+  {  // unconditional (a clamped tile when none is used), so that pre stays in registers
+    const int kf = min(kt, ntile - 1);
+    tile_fetch<D>(pre, kc, kf * kPT, L - 1, tid);
+    if (tid < kPT && kf * kPT + tid < L) ppos = pos[kf * kPT + tid];
+  }
+  while (kt < ntile) {
     __syncthreads();  // the previous tile is no longer read
-    stage_rows<D>(sK, kc, RB, kt * kPT, L - 1, tid);
-    if (tid < kPT) sP[tid] = kt * kPT + tid < L ? pos[kt * kPT + tid] : INT_MAX;
+    tile_put<D>(pre, sK, tid);
+    if (tid < kPT) sP[tid] = ppos;
     __syncthreads();
+    const int kn = mask.next(kt);
+    {  // the next tile's loads fly while this one is computed (after the
+       // last one: the current tile again, unused)
+      const int kf = kn < ntile ? kn : kt;
+      tile_fetch<D>(pre, kc, kf * kPT, L - 1, tid);
+      ppos = (tid < kPT && kf * kPT + tid < L) ? pos[kf * kPT + tid] : INT_MAX;
+    }
+    pf32x4_t S[4];
 #pragma unroll
-    for (int kb = 0; kb < kPT / 16; ++kb) {
-      pf32x4_t S = {0.f, 0.f, 0.f, 0.f};
-      const char *arow = sK + (kb * 16 + col) * LRB + quad * 8;
+    for (int blk = 0; blk < 4; ++blk) S[blk] = (pf32x4_t){0.f, 0.f, 0.f, 0.f};
+    const char *arow = sK + (wave * 16 + col) * LRB + quad * 16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S = pmfma(*reinterpret_cast<const pbf16x4_t *>(arow + ks * 32), qb[ks], S);
-      float s[4], mx = m;
+    for (int ks = 0; ks < KS; ++ks) {
+      const pbf16x8_t a = *reinterpret_cast<const pbf16x8_t *>(arow + ks * 64);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) S[blk] = pmfma(a, qb[blk][ks], S[blk]);
+    }
+    if ((sFull[kt >> 5] >> (kt & 31)) & 1u) {  // every key visible to every query
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const float r = fmaxf(fmaxf(S[blk][0], S[blk][1]), fmaxf(S[blk][2], S[blk][3])) * p.scale_log2;
+        const float mx = fmaxf(m[blk], r);
+        float lv = l[blk] * fast_exp2(m[blk] - mx);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) lv += fast_exp2(fmaf(S[blk][ii], p.scale_log2, -mx));
+        l[blk] = lv;
+        m[blk] = mx;
+      }
+      kt = kn;
+      continue;
+    }
+    int kp[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) kp[ii] = sP[wave * 16 + quad * 4 + ii];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      float sv[4], mx = m[blk];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int kp = sP[kb * 16 + quad * 4 + ii];
-        s[ii] = kp <= qp ? S[ii] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[ii]);
+        sv[ii] = kp[ii] <= qp[blk] ? S[blk][ii] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[ii]);
       }
       if (mx != -INFINITY) {
-        l *= fast_exp2(m - mx);
+        float lv = l[blk] * fast_exp2(m[blk] - mx);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) l += fast_exp2(s[ii] - mx);
-        m = mx;
+        for (int ii = 0; ii < 4; ++ii) lv += fast_exp2(sv[ii] - mx);
+        l[blk] = lv;
+        m[blk] = mx;
       }
     }
+    kt = kn;
   }
-  // the four lanes of a query (quads) merge their running max and sum
+  // merge the four lanes of a query (quads), then the four waves
 #pragma unroll
-  for (int off = 16; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(m, off), lo = __shfl_xor(l, off);
-    const float mx = fmaxf(m, mo);
-    const float mxs = (mx == -INFINITY) ? 0.f : mx;
-    l = l * fast_exp2(m - mxs) + lo * fast_exp2(mo - mxs);
-    m = mx;
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+      const float mo = __shfl_xor(m[blk], off), lo = __shfl_xor(l[blk], off);
+      const float mx = fmaxf(m[blk], mo);
+      const float mxs = (mx == -INFINITY) ? 0.f : mx;
+      l[blk] = l[blk] * fast_exp2(m[blk] - mxs) + lo * fast_exp2(mo - mxs);
+      m[blk] = mx;
+    }
+    if (quad == 0) {
+      sML[wave][blk * 16 + col][0] = m[blk];
+      sML[wave][blk * 16 + col][1] = l[blk];
+    }
   }
-  if (quad == 0 && i < p.n_obs) {
-    const size_t sid = (((size_t)u * p.G + g) * p.n_obs + i) * 2;
-    p.stats[sid] = m;
-    p.stats[sid + 1] = l;
+  __syncthreads();
+  if (tid < kPT) {
+    const int i = qt * kPT + tid;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sML[w][tid][0]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float lv = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) lv += sML[w][tid][1] * fast_exp2(sML[w][tid][0] - Ms);
+    if (i < p.n_obs) {
+      const size_t sid = (((size_t)u * p.G + g) * p.n_obs + i) * 2;
+      p.stats[sid] = M;
+      p.stats[sid + 1] = lv;
+    }
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void k_prefill_accum_mfma(PrefillArgs p) {
-  constexpr int RB = D * 2, LRB = RB + 16, KS = D / 16;
+  constexpr int RB = D * 2, LRB = RB + 16, KS = D / 32;
   const int kt = blockIdx.x, u = blockIdx.y;
   const int b = u / p.Hkv, j = u - b * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, col = lane & 15;
   const int L = min(p.len[u], p.cap);
   if (kt * kPT >= L) return;
   const int nkt = (p.cap + kPT - 1) / kPT, nqt = (p.n_obs + kPT - 1) / kPT;
+  const int kmin = p.krange[((size_t)u * nkt + kt) * 2], kmax = p.krange[((size_t)u * nkt + kt) * 2 + 1];
+  __shared__ uint32_t sMask[kMaxTiles / 32], sFull[kMaxTiles / 32];
+  __shared__ __attribute__((aligned(16))) char sQ[kPT * LRB];
+  __shared__ float sM[kPT];
+  __shared__ int sQP[kPT];
+  __shared__ float sC[4][kPT];
+  // query tiles that can meet a key of this tile (causal, within the
+  // window); of those, the ones that meet every key with every query
+  for (int w = tid; w < (nqt + 31) / 32; w += 256) sMask[w] = 0u, sFull[w] = 0u;
+  __syncthreads();
+  for (int t = tid; t < nqt; t += 256) {
+    const int qlo = p.qrange[((size_t)b * nqt + t) * 2], qhi = p.qrange[((size_t)b * nqt + t) * 2 + 1];
+    const bool meet = (int64_t)qhi >= kmin && (p.window == 0 || (int64_t)qlo - kmax < p.window);
+    const bool all = (int64_t)qlo >= kmax && (p.window == 0 || (int64_t)qhi - kmin < p.window);
+    if (meet) atomicOr(&sMask[t >> 5], 1u << (t & 31));
+    if (all) atomicOr(&sFull[t >> 5], 1u << (t & 31));
+  }
   const char *kc = static_cast<const char *>(p.k_cache) + (size_t)u * p.cap * RB;
   const int32_t *pos = p.pos + (size_t)u * p.cap;
-  // A operand: the wave's 16 keys stay in registers
-  const int kr = min(kt * kPT + wave * 16 + col, L - 1);
-  pbf16x4_t ka[KS];
+  pbf16x8_t ka[4][KS];  // A operands: the tile's four key blocks
+  int kp[4][4];         // positions of this lane's output keys (INT_MAX: none)
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    ka[ks] = *reinterpret_cast<const pbf16x4_t *>(kc + (size_t)kr * RB + ks * 32 + quad * 8);
-  int kp[4];  // positions of this lane's four output keys (INT_MAX: no key)
+  for (int kb = 0; kb < 4; ++kb) {
+    const int kr = min(kt * kPT + kb * 16 + col, L - 1);
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int n = kt * kPT + wave * 16 + quad * 4 + ii;
-    kp[ii] = n < L ? pos[n] : INT_MAX;
-  }
-  const int kmin = p.krange[((size_t)u * nkt + kt) * 2], kmax = p.krange[((size_t)u * nkt + kt) * 2 + 1];
-  __shared__ __attribute__((aligned(16))) char sQ[kPT * LRB];
-  __shared__ float sM[kPT], sIL[kPT];
-  __shared__ int sQP[kPT];
-  float cs[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int g = 0; g < p.G; ++g) {
-    const int h = j * p.G + g;
-    const char *qbase = static_cast<const char *>(p.q_obs) + ((size_t)(b * p.Hq + h)) * p.n_obs * RB;
-    for (int qt = 0; qt < nqt; ++qt) {
-      const int qlo = p.qrange[((size_t)b * nqt + qt) * 2], qhi = p.qrange[((size_t)b * nqt + qt) * 2 + 1];
-      if ((int64_t)qhi < kmin) continue;                                   // every query before every key
-      if (p.window > 0 && (int64_t)qlo - kmax >= p.window) continue;       // every query past the window
-      __syncthreads();
-      stage_rows<D>(sQ, qbase, RB, qt * kPT, p.n_obs - 1, tid);
-      if (tid < kPT) {
-        const int i = qt * kPT + tid;
-        const bool ok = i < p.n_obs;
-        const size_t sid = (((size_t)u * p.G + g) * p.n_obs + (ok ? i : 0)) * 2;
-        const float lv = ok ? p.stats[sid + 1] : 0.f;
-        sM[tid] = ok ? p.stats[sid] : 0.f;
-        sIL[tid] = lv > 0.f ? 1.f / lv : 0.f;
-        sQP[tid] = ok ? p.q_pos[(size_t)b * p.n_obs + i] : INT_MIN;
-      }
-      __syncthreads();
+    for (int ks = 0; ks < KS; ++ks)
+      ka[kb][ks] = *reinterpret_cast<const pbf16x8_t *>(kc + (size_t)kr * RB + ks * 64 + quad * 16);
 #pragma unroll
-      for (int qb = 0; qb < kPT / 16; ++qb) {
-        pf32x4_t S = {0.f, 0.f, 0.f, 0.f};
-        const char *brow = sQ + (qb * 16 + col) * LRB + quad * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) S = pmfma(ka[ks], *reinterpret_cast<const pbf16x4_t *>(brow + ks * 32), S);
-        const int qi = qb * 16 + col;
-        const int qp = sQP[qi];
-        const float mq = sM[qi], il = sIL[qi];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int64_t d = (int64_t)qp - kp[ii];
-          const bool ok = d >= 0 && (p.window == 0 || d < p.window);
-          cs[ii] += ok ? fast_exp2(S[ii] * p.scale_log2 - mq) * il : 0.f;
-        }
-      }
+    for (int ii = 0; ii < 4; ++ii) {
+      const int n = kt * kPT + kb * 16 + quad * 4 + ii;
+      kp[kb][ii] = n < L ? pos[n] : INT_MAX;
     }
   }
-  // the 16 lanes of a quad hold the same keys for different queries
+  __syncthreads();
+  const TileMask mask{sMask, nqt};
+  float cs[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) cs[kb][ii] = 0.f;
+  const char *qhead = static_cast<const char *>(p.q_obs) + ((size_t)(b * p.Hq + j * p.G)) * p.n_obs * RB;
+  const size_t hstride = (size_t)p.n_obs * RB;  // q-heads of a group are adjacent
+  pu32x4_t pre[TileShape<D>::REPS];
+  float pm = 0.f, pl = 0.f;
+  int pq = INT_MIN;
+  auto fetch = [&](int g, int qt) {
+    tile_fetch<D>(pre, qhead + (size_t)g * hstride, qt * kPT, p.n_obs - 1, tid);
+    if (tid < kPT) {
+      const int i = qt * kPT + tid;
+      const bool ok = i < p.n_obs;
+      const size_t sid = (((size_t)u * p.G + g) * p.n_obs + (ok ? i : 0)) * 2;
+      pm = ok ? p.stats[sid] : 0.f;
+      pl = ok ? p.stats[sid + 1] : 0.f;
+      pq = ok ? p.q_pos[(size_t)b * p.n_obs + i] : INT_MIN;
+    }
+  };
+  const int q0 = mask.next(-1);
+  int g = 0, qt = q0;
+  fetch(0, min(q0, nqt - 1));  // unconditional, so that pre stays in registers
+  while (q0 < nqt && g < p.G) {
+    __syncthreads();  // the previous tile is no longer read
+    tile_put<D>(pre, sQ, tid);
+    if (tid < kPT) {  // p = exp2(s - m - log2 l); a query that sees nothing gets none
+      sM[tid] = pl > 0.f ? pm + __log2f(pl) : INFINITY;
+      sQP[tid] = pq;
+    }
+    __syncthreads();
+    int gn = g, qn = mask.next(qt);
+    if (qn >= nqt) gn = g + 1, qn = q0;
+    // the next tile's loads fly while this one is computed (after the last
+    // one: the current tile again, unused)
+    if (gn < p.G) fetch(gn, qn);
+    else fetch(g, qt);
+    pf32x4_t S[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) S[kb] = (pf32x4_t){0.f, 0.f, 0.f, 0.f};
+    const char *brow = sQ + (wave * 16 + col) * LRB + quad * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const pbf16x8_t bq = *reinterpret_cast<const pbf16x8_t *>(brow + ks * 64);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) S[kb] = pmfma(ka[kb][ks], bq, S[kb]);
+    }
+    const int qi = wave * 16 + col;
+    const float mq = sM[qi];
+    if ((sFull[qt >> 5] >> (qt & 31)) & 1u) {  // every pair counts
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) cs[kb][ii] += fast_exp2(fmaf(S[kb][ii], p.scale_log2, -mq));
+    } else {
+      const int qp = sQP[qi];
+      const uint32_t win = p.window > 0 ? (uint32_t)p.window : 0xffffffffu;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          // distance qp - kp without overflow: unsigned once kp <= qp
+          const bool ok = kp[kb][ii] <= qp && (uint32_t)qp - (uint32_t)kp[kb][ii] < win;
+          cs[kb][ii] += ok ? fast_exp2(fmaf(S[kb][ii], p.scale_log2, -mq)) : 0.f;
+        }
+    }
+    g = gn, qt = qn;
+  }
+  // the 16 lanes of a quad hold the same keys for different queries; then
+  // the four waves (different queries) meet in LDS
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) cs[ii] += __shfl_xor(cs[ii], off);
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) cs[kb][ii] += __shfl_xor(cs[kb][ii], off);
   if (col == 0) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int n = kt * kPT + wave * 16 + quad * 4 + ii;
-      if (n < L) p.imp[(size_t)u * p.cap + n] += cs[ii];
-    }
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sC[wave][kb * 16 + quad * 4 + ii] = cs[kb][ii];
+  }
+  __syncthreads();
+  if (tid < kPT) {
+    const int n = kt * kPT + tid;
+    if (n < L) p.imp[(size_t)u * p.cap + n] += sC[0][tid] + sC[1][tid] + sC[2][tid] + sC[3][tid];
   }
 }
 
