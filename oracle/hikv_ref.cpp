@@ -365,9 +365,9 @@ extern "C" int hikv_ref_evict(const hikv_ref_shape *shape, const hikv_ref_cache 
 
 extern "C" int hikv_ref_prefill_scores(const hikv_ref_shape *shape, const hikv_ref_cache *cache,
                                        const void *q_obs, const int32_t *q_pos, int32_t n_obs,
-                                       int32_t window) {
+                                       int32_t window, int32_t pool) {
   Dims d;
-  if (!read_dims(shape, &d) || !cache || n_obs < 0 || window < 0) return HIKV_REF_EINVAL;
+  if (!read_dims(shape, &d) || !cache || n_obs < 0 || window < 0 || pool < 0) return HIKV_REF_EINVAL;
   if (d.B == 0 || n_obs == 0) return HIKV_REF_OK;
   if (!q_obs || !q_pos) return HIKV_REF_EINVAL;
   for (int b = 0; b < d.B; ++b)
@@ -402,6 +402,19 @@ extern "C" int hikv_ref_prefill_scores(const hikv_ref_shape *shape, const hikv_r
             added[vis[t]] += p[t];
           }
         }
+      }
+      if (pool > 1) {
+        // SnapKV's pooling: the largest score over positions p .. p+pool-1
+        // among the cached tokens (positions are distinct).
+        std::vector<double> pooled(L);
+        for (int n = 0; n < L; ++n) {
+          pooled[n] = added[n];
+          for (int m = 0; m < L; ++m) {
+            const int64_t dp = (int64_t)x.pos[m] - x.pos[n];
+            if (dp >= 0 && dp < pool) pooled[n] = std::max(pooled[n], added[m]);
+          }
+        }
+        added = pooled;
       }
       for (int n = 0; n < L; ++n) x.imp[n] = (float)((double)x.imp[n] + added[n]);
     }

@@ -31,6 +31,8 @@
  *    of P, top-B_II per chunk, P.V over the kept rows).
  *  - Kelle Sec. 4.1 (Eq. 3) and Sec. 5.3 (importance as summed attention
  *    scores taken before the softmax).
+ *  - "KV Cache Compression and Dynamic Pruning in Production Serving",
+ *    SnapKV section (observation-window scores, 1-D max pooling).
  */
 #ifndef HIKV_REF_H
 #define HIKV_REF_H
@@ -125,11 +127,13 @@ int hikv_ref_evict(const hikv_ref_shape *shape, const hikv_ref_cache *cache,
  * q_pos[b][i]) and q-head of the group, the causal softmax row over the
  * cached tokens (those with pos <= q_pos) is added to those tokens'
  * importance.  window == 0: every such entry counts (column sums);
- * window > 0: an entry counts only when 0 <= q_pos - pos < window. */
+ * window > 0: an entry counts only when 0 <= q_pos - pos < window.
+ * pool > 1 (SnapKV's 1-D max pooling): a token at position p adds instead
+ * the largest of this call's scores over the cached positions p .. p+pool-1. */
 int hikv_ref_prefill_scores(const hikv_ref_shape *shape, const hikv_ref_cache *cache,
                             const void *q_obs /* [B][Hq][n_obs][D] */,
                             const int32_t *q_pos /* [B][n_obs] */, int32_t n_obs,
-                            int32_t window);
+                            int32_t window, int32_t pool);
 
 #ifdef __cplusplus
 }

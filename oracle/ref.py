@@ -71,7 +71,7 @@ def lib():
                                            C.c_void_p, C.c_void_p, C.c_void_p, P(Debug)]
         L.hikv_ref_evict.argtypes = [P(Shape), P(Cache), P(Policy), C.c_void_p, P(Debug)]
         L.hikv_ref_prefill_scores.argtypes = [P(Shape), P(Cache), C.c_void_p, C.c_void_p,
-                                              C.c_int32, C.c_int32]
+                                              C.c_int32, C.c_int32, C.c_int32]
         for f in (L.hikv_ref_decode_step, L.hikv_ref_evict, L.hikv_ref_prefill_scores):
             f.restype = C.c_int
         _libs[path] = L
@@ -166,7 +166,7 @@ def evict(state, n_q_heads, newest_pos, *, budget=None, budget_all=0, n_sink=0, 
     return st, dbg
 
 
-def prefill_scores(state, n_q_heads, q_obs, q_pos, window=0, scale=0.0):
+def prefill_scores(state, n_q_heads, q_obs, q_pos, window=0, scale=0.0, pool=0):
     L = lib()
     sh = shape_of(state, n_q_heads, scale)
     q_obs = np.ascontiguousarray(q_obs)
@@ -174,7 +174,7 @@ def prefill_scores(state, n_q_heads, q_obs, q_pos, window=0, scale=0.0):
     n_obs = q_obs.shape[2] if q_obs.ndim == 4 else 0
     cache = cache_of(state)
     return L.hikv_ref_prefill_scores(C.byref(sh), C.byref(cache), _ptr(q_obs), _ptr(q_pos),
-                                     int(n_obs), int(window))
+                                     int(n_obs), int(window), int(pool))
 
 
 def live_positions(state, b, j):

@@ -61,6 +61,11 @@ What pins what:
       LOGIT): a step adds the group's pre-softmax logits scale * q.k (a
       library matmul; with Stage II on, of the channel-masked query) to every
       live token, and the kept set is the brute-force one for that importance.
+  snapkv_pooling_matches_library -- pool = k: every token gains the largest
+      of the observation scores (library attention weights) over positions
+      p .. p+k-1, computed as a sliding-window maximum (numpy) over the
+      position axis with absent positions at -inf; slots shuffled, positions
+      with gaps.
 """
 
 from __future__ import annotations
@@ -714,9 +719,42 @@ def logit_accumulation_matches_library(seed=59):
             assert set(ref.live_positions(st, 0, j).tolist()) == kept, (r, j)
 
 
+def snapkv_pooling_matches_library(seed=67):
+    from numpy.lib.stride_tricks import sliding_window_view
+    B, Hkv, G, D = 1, 2, 2, 16
+    Hq = Hkv * G
+    L, n_obs, k = 30, 6, 5
+    rng = np.random.Generator(np.random.PCG64(seed))
+    scale = 1.0 / math.sqrt(D)
+    for gaps in (False, True):
+        posv = (np.arange(L) * (3 if gaps else 1) + (rng.integers(0, 2, L) if gaps else 0)).astype(np.int32)
+        posv = np.sort(posv)
+        keys = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+        qo = rng.standard_normal((B, Hq, n_obs, D)).astype(np.float32)
+        qpos = posv[-n_obs:][None].copy()                     # the last prompt tokens observe
+        perm = rng.permutation(L)
+        st = dict(k=np.ascontiguousarray(keys[:, :, perm]), v=np.zeros_like(keys),
+                  pos=np.ascontiguousarray(np.broadcast_to(posv[perm], (B, Hkv, L))),
+                  imp=np.zeros((B, Hkv, L), np.float32), len=np.full((B, Hkv), L, np.int32))
+        assert ref.prefill_scores(st, Hq, qo, qpos, window=0, pool=k) == 0
+        for j in range(Hkv):
+            A = np.zeros(L)                                    # observation scores, position order
+            for g in range(G):
+                mask = qpos[0][:, None] >= posv[None, :]
+                P = sdpa(qo[0, j * G + g][None], keys[0, j][None], np.eye(L)[None], scale, mask)[0]
+                A += P.sum(0)
+            span = np.full(int(posv[-1]) + k, -np.inf)
+            span[posv] = A
+            pooled = sliding_window_view(span, k).max(axis=1)[posv]
+            got = np.zeros(L)
+            got[np.searchsorted(posv, st["pos"][0, j])] = st["imp"][0, j]
+            assert np.abs(got - pooled).max() < 1e-5, (gaps, j)
+
+
 ALL = [attention_matches_library, rows_sum_to_group, streaming_closed_form, eviction_brute_force,
        golden_cases, permutation_invariance, channel_permutation, conservation,
        stage2_reduces_to_stage1, stage2_selection, equal_keys_closed_form, prefill_column_sums,
        errors_leave_unit_unchanged, heap_worked_examples, heap_keeps_the_top_scores,
        dual_bank_matches_its_definition, stage2_chunks_reduce_to_attention,
-       stage2_chunks_select_by_probability, logit_accumulation_matches_library]
+       stage2_chunks_select_by_probability, logit_accumulation_matches_library,
+       snapkv_pooling_matches_library]

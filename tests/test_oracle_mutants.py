@@ -56,6 +56,8 @@ MUTANTS = [
     ("chunks_keep_one_more", "const int keep = std::min(r, m);", "const int keep = std::min(r + 1, m);"),
     ("logit_acc_uses_probabilities", "added[n] += by_logit ? s[n] : p[n];", "added[n] += p[n];"),
     ("logit_acc_stage2_uses_probabilities", "added[n] += by_logit ? st[n] : pt[n];", "added[n] += pt[n];"),
+    ("pool_window_one_longer", "if (dp >= 0 && dp < pool)", "if (dp >= 0 && dp <= pool)"),
+    ("pool_looks_backward", "if (dp >= 0 && dp < pool)", "if (dp <= 0 && dp > -pool)"),
     ("chunks_use_exact_logits", "            st[n] = d.scale * acc;\n          }\n          std::vector<double> pt = softmax(st);",
      "            st[n] = d.scale * acc;\n          }\n          std::vector<double> pt = softmax(st);\n"
      "          if (pol->stage2_v == HIKV_REF_S2V_CHUNK) {\n"
