@@ -258,15 +258,17 @@ extern "C" size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t 
   const size_t nobs = n_obs > 0 ? (size_t)n_obs : 1;
   const size_t nkt = ((size_t)shape->capacity + 63) / 64, nqt = (nobs + 63) / 64;
   return 256 + align256(sizeof(float) * U * G * nobs * 2) + align256(sizeof(int32_t) * U * nkt * 2) +
-         align256(sizeof(int32_t) * (size_t)shape->batch * nqt * 2);
+         align256(sizeof(int32_t) * (size_t)shape->batch * nqt * 2) +
+         3 * align256(sizeof(int32_t) * U * (size_t)shape->capacity);
 }
 
 extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *cache,
                                    const void *q_obs, const int32_t *q_pos, int32_t n_obs,
-                                   int32_t window, void *ws, size_t ws_bytes, void *stream) {
+                                   int32_t window, int32_t pool, void *ws, size_t ws_bytes,
+                                   void *stream) {
   int st = check_shape(shape);
   if (st != HIKV_OK) return st;
-  if (n_obs < 0 || window < 0) return HIKV_EINVAL;
+  if (n_obs < 0 || window < 0 || pool < 0) return HIKV_EINVAL;
   if (shape->batch == 0 || n_obs == 0) return HIKV_OK;
   if ((st = check_cache(cache)) != HIKV_OK) return st;
   if (!q_obs || !q_pos || !ws || !aligned16(q_obs) || !aligned16(ws)) return HIKV_EINVAL;
@@ -286,6 +288,7 @@ extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *ca
   p.n_units = p.B * p.Hkv;
   p.n_obs = n_obs;
   p.window = window;
+  p.pool = pool;
   const double scale = shape->scale > 0.f ? (double)shape->scale : 1.0 / sqrt((double)shape->head_dim);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
   p.k_cache = cache->k;
@@ -300,7 +303,13 @@ extern "C" int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *ca
     const size_t U = (size_t)p.n_units, nkt = ((size_t)p.cap + 63) / 64;
     char *r = static_cast<char *>(ws) + 256 + align256(sizeof(float) * U * p.G * (size_t)n_obs * 2);
     p.krange = reinterpret_cast<int32_t *>(r);
-    p.qrange = reinterpret_cast<int32_t *>(r + align256(sizeof(int32_t) * U * nkt * 2));
+    r += align256(sizeof(int32_t) * U * nkt * 2);
+    p.qrange = reinterpret_cast<int32_t *>(r);
+    r += align256(sizeof(int32_t) * (size_t)p.B * (((size_t)n_obs + 63) / 64) * 2);
+    const size_t per = align256(sizeof(int32_t) * U * (size_t)p.cap);
+    p.padd = reinterpret_cast<float *>(r);
+    p.pord = reinterpret_cast<int32_t *>(r + per);
+    p.prank = reinterpret_cast<int32_t *>(r + 2 * per);
   }
   return dev_err(launch_prefill(p, shape->kv_dtype, static_cast<hipStream_t>(stream)));
 }

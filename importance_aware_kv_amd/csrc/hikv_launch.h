@@ -41,7 +41,7 @@ hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s);
 
 // Prefill scores.
 struct PrefillArgs {
-  int B, Hq, Hkv, D, cap, G, n_units, n_obs, window;
+  int B, Hq, Hkv, D, cap, G, n_units, n_obs, window, pool;
   float scale_log2;
   const void *k_cache;
   const int32_t *pos;
@@ -52,6 +52,9 @@ struct PrefillArgs {
   float *stats;       // [U][G][n_obs][2]
   int32_t *krange;    // [U][ceil(cap/64)][2] lowest, highest position of each 64-slot tile
   int32_t *qrange;    // [B][ceil(n_obs/64)][2] lowest, highest position of each 64-query tile
+  float *padd;        // [U][cap] this call's score per slot (pooling only)
+  int32_t *pord;      // [U][cap] slots in position order (pooling only)
+  int32_t *prank;     // [U][cap] each slot's rank in that order (pooling only)
   int32_t *status;
 };
 hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s);

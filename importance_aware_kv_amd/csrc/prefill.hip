@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) void k_prefill_accum(PrefillArgs p) {
         sum += fast_exp2(s - p.stats[sid]) / p.stats[sid + 1];
       }
     }
-    if (c == 0) p.imp[(size_t)u * p.cap + n] += sum;
+    if (c == 0) {
+      if (p.pool > 1) p.padd[(size_t)u * p.cap + n] = sum;  // pooled below
+      else p.imp[(size_t)u * p.cap + n] += sum;
+    }
   }
 }
 
@@ -502,11 +505,133 @@ __global__ __launch_bounds__(256) void k_prefill_accum_mfma(PrefillArgs p) {
   __syncthreads();
   if (tid < kPT) {
     const int n = kt * kPT + tid;
-    if (n < L) p.imp[(size_t)u * p.cap + n] += sC[0][tid] + sC[1][tid] + sC[2][tid] + sC[3][tid];
+    if (n < L) {
+      const float sum = sC[0][tid] + sC[1][tid] + sC[2][tid] + sC[3][tid];
+      if (p.pool > 1) p.padd[(size_t)u * p.cap + n] = sum;  // pooled below
+      else p.imp[(size_t)u * p.cap + n] += sum;
+    }
   }
 }
 
+// ---------------------------------------------------------------------------
+// SnapKV's pooling ("KV Cache Compression and Dynamic Pruning in Production
+// Serving", SnapKV section): a token at position p adds the largest of this
+// call's scores over the live positions p .. p+pool-1.
+//   P1  one workgroup per unit: the position order.  The live positions are
+//       set as bits of an LDS bitmap over [min, max]; popcount prefixes per
+//       group of 32 words are scanned; a slot's rank is its group prefix plus
+//       the popcounts before it in the group.  Spans beyond the bitmap are
+//       ranked by counting.  Writes order[rank] = slot and rank[slot].
+//   P2  one thread per slot: walks forward in position order while the
+//       positions stay below p + pool and adds the largest score.
+// ---------------------------------------------------------------------------
+constexpr int kPoolBits = 1 << 19;  // 64 KB of LDS
+
+static hipError_t launch_prefill_scores(const PrefillArgs &p, int dtype, hipStream_t s);
+
+__global__ __launch_bounds__(256) void k_pool_rank(PrefillArgs p) {
+  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = min(p.len[u], p.cap);
+  if (L <= 0) return;
+  const int32_t *pos = p.pos + (size_t)u * p.cap;
+  int32_t *ord = p.pord + (size_t)u * p.cap, *rk = p.prank + (size_t)u * p.cap;
+  __shared__ uint32_t bits[kPoolBits / 32];
+  __shared__ int gpre[kPoolBits / 1024];
+  __shared__ int s_lo[4], s_hi[4], s_ws[4];
+  int lo = INT_MAX, hi = INT_MIN;
+  for (int n = tid; n < L; n += 256) lo = min(lo, pos[n]), hi = max(hi, pos[n]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lo = min(lo, __shfl_xor(lo, off)), hi = max(hi, __shfl_xor(hi, off));
+  if (lane == 0) s_lo[wave] = lo, s_hi[wave] = hi;
+  __syncthreads();
+  lo = min(min(s_lo[0], s_lo[1]), min(s_lo[2], s_lo[3]));
+  hi = max(max(s_hi[0], s_hi[1]), max(s_hi[2], s_hi[3]));
+  if ((int64_t)hi - lo + 1 > kPoolBits) {  // counting, positions staged through LDS
+    int *sp = reinterpret_cast<int *>(bits);
+    constexpr int kTile = kPoolBits / 32;
+    for (int nb = 0; nb < L; nb += 256) {
+      const int n = nb + tid;
+      const int pn = pos[min(n, L - 1)];
+      int r = 0;
+      for (int t0 = 0; t0 < L; t0 += kTile) {
+        const int tn = min(kTile, L - t0);
+        __syncthreads();
+        for (int i = tid; i < tn; i += 256) sp[i] = pos[t0 + i];
+        __syncthreads();
+        for (int i = 0; i < tn; ++i) r += sp[i] < pn;
+      }
+      if (n < L) {
+        r = min(r, L - 1);
+        ord[r] = n;
+        rk[n] = r;
+      }
+    }
+    return;
+  }
+  const int nw = (int)(((int64_t)hi - lo + 32) / 32), ng = (nw + 31) / 32;
+  for (int w = tid; w < nw; w += 256) bits[w] = 0u;
+  __syncthreads();
+  for (int n = tid; n < L; n += 256) {
+    const int d = pos[n] - lo;
+    atomicOr(&bits[d >> 5], 1u << (d & 31));
+  }
+  __syncthreads();
+  // groups of 32 words: ng <= 512, two per thread, then a block scan
+  int c0 = 0, c1 = 0;
+  for (int k = 0; k < 32; ++k) {
+    const int w0 = (2 * tid) * 32 + k, w1 = (2 * tid + 1) * 32 + k;
+    if (w0 < nw) c0 += __popc(bits[w0]);
+    if (w1 < nw) c1 += __popc(bits[w1]);
+  }
+  const int ts = c0 + c1;
+  int incl = ts;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_ws[wave] = incl;
+  __syncthreads();
+  int base = incl - ts;
+  for (int w = 0; w < wave; ++w) base += s_ws[w];
+  if (2 * tid < ng) gpre[2 * tid] = base;
+  if (2 * tid + 1 < ng) gpre[2 * tid + 1] = base + c0;
+  __syncthreads();
+  for (int n = tid; n < L; n += 256) {
+    const int d = pos[n] - lo, w = d >> 5;
+    int r = gpre[w >> 5];
+    for (int k = w & ~31; k < w; ++k) r += __popc(bits[k]);
+    r = min(r + __popc(bits[w] & ((1u << (d & 31)) - 1u)), L - 1);
+    ord[r] = n;
+    rk[n] = r;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pool_apply(PrefillArgs p) {
+  const int u = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  const int L = min(p.len[u], p.cap);
+  if (n >= L) return;
+  const size_t o = (size_t)u * p.cap;
+  const int r = min(max(p.prank[o + n], 0), L - 1);
+  const int64_t p0 = p.pos[o + n];
+  float best = p.padd[o + n];
+  for (int m = r + 1; m < L && m - r < p.pool; ++m) {
+    const int sl = min(max(p.pord[o + m], 0), L - 1);
+    if ((int64_t)p.pos[o + sl] - p0 >= p.pool) break;
+    best = fmaxf(best, p.padd[o + sl]);
+  }
+  p.imp[o + n] += best;
+}
+
 hipError_t launch_prefill(const PrefillArgs &p, int dtype, hipStream_t s) {
+  hipError_t e = launch_prefill_scores(p, dtype, s);
+  if (e != hipSuccess || p.pool <= 1) return e;
+  hipLaunchKernelGGL(k_pool_rank, dim3(p.n_units), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pool_apply, dim3((p.cap + 255) / 256, p.n_units), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+static hipError_t launch_prefill_scores(const PrefillArgs &p, int dtype, hipStream_t s) {
   const dim3 blk(256);
   if (dtype == HIKV_BF16) {  // matrix cores
     const int nkt = (p.cap + kPT - 1) / kPT, nqt = (p.n_obs + kPT - 1) / kPT;

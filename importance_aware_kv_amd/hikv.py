@@ -80,7 +80,7 @@ def lib():
         L.hikv_pending.restype = C.c_int
         L.hikv_prefill_workspace_bytes.argtypes = [P(hikv_shape), i32]
         L.hikv_prefill_workspace_bytes.restype = sz
-        L.hikv_prefill_scores.argtypes = [P(hikv_shape), P(hikv_cache), vp, vp, i32, i32, vp, sz, vp]
+        L.hikv_prefill_scores.argtypes = [P(hikv_shape), P(hikv_cache), vp, vp, i32, i32, i32, vp, sz, vp]
         L.hikv_prefill_scores.restype = C.c_int
         L.hikv_device_status.argtypes = [vp, C.c_int, vp]
         L.hikv_device_status.restype = C.c_int
@@ -160,9 +160,9 @@ def hikv_pending(shape, cache, policy, ws, slot_out, stream=None) -> int:
                               ws.numel() * ws.element_size(), _p(slot_out), _stream(stream))
 
 
-def hikv_prefill_scores(shape, cache, q_obs, q_pos, n_obs, window, ws, stream=None) -> int:
+def hikv_prefill_scores(shape, cache, q_obs, q_pos, n_obs, window, ws, stream=None, pool=0) -> int:
     return lib().hikv_prefill_scores(C.byref(shape), C.byref(cache), _p(q_obs), _p(q_pos), n_obs,
-                                     window, _p(ws), ws.numel() * ws.element_size(), _stream(stream))
+                                     window, pool, _p(ws), ws.numel() * ws.element_size(), _stream(stream))
 
 
 def hikv_device_status(ws, clear=True, stream=None) -> int:

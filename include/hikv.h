@@ -237,9 +237,15 @@ size_t hikv_prefill_workspace_bytes(const hikv_shape *shape, int32_t n_obs);
  * observation query i at position q_pos[b][i] and every q-head of a KV group,
  * the causal softmax row over the unit's live tokens with pos <= q_pos is
  * formed; a token's share is added to its importance when window == 0, or
- * when 0 <= q_pos - pos < window.  q_obs: [B][Hq][n_obs][D]; q_pos: [B][n_obs]. */
+ * when 0 <= q_pos - pos < window.  q_obs: [B][Hq][n_obs][D]; q_pos: [B][n_obs].
+ * pool > 1 applies SnapKV's 1-D max pooling ([Blog] SnapKV section): the
+ * token at position p adds the largest of this call's scores over the live
+ * positions p .. p+pool-1 instead of its own (0 or 1: no pooling).
+ * Positions of a unit must be distinct.  bf16 caches run on the matrix cores
+ * (capacity and n_obs at most 2^21: HIKV_EUNSUPPORTED beyond); fp32 caches
+ * on the vector ALUs.  window < 0, pool < 0 or n_obs < 0: HIKV_EINVAL. */
 int hikv_prefill_scores(const hikv_shape *shape, const hikv_cache *cache, const void *q_obs,
-                        const int32_t *q_pos, int32_t n_obs, int32_t window, void *ws,
+                        const int32_t *q_pos, int32_t n_obs, int32_t window, int32_t pool, void *ws,
                         size_t ws_bytes, void *stream);
 
 /* Synchronise `stream`, return the first device-side error recorded in `ws`

@@ -94,9 +94,11 @@ def test_decode_step_host_checks():
     assert call(_shape(batch=0)) == H.HIKV_OK                                       # empty batch
     assert L.hikv_evict(C.byref(_shape()), C.byref(cache), C.byref(pol), None, fake, 1 << 30,
                         None) == H.HIKV_EINVAL
-    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, -1, 0, fake,
+    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, 0, 0, -1, fake,
                                  1 << 30, None) == H.HIKV_EINVAL
-    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, 0, 0, fake,
+    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, -1, 0, 0, fake,
+                                 1 << 30, None) == H.HIKV_EINVAL
+    assert L.hikv_prefill_scores(C.byref(_shape()), C.byref(cache), fake, fake, 0, 0, 0, fake,
                                  1 << 30, None) == H.HIKV_OK
     import numpy as np
     bad_hint = np.array([10, 64, 3, 3], dtype=np.int32)   # 64 + 1 > capacity 64

@@ -640,3 +640,39 @@ def test_prefill_scores_long_prompt(window):
     want = ref.copy_state(st)
     assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=window) == 0
     np.testing.assert_allclose(got["imp"], want["imp"], rtol=1e-3, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["dense", "gaps", "beyond-bitmap"])
+def test_prefill_scores_snapkv_pooling(dtype, layout):
+    """SnapKV: the last 32 prompt tokens observe, scores max-pooled over 7
+    positions.  Slots shuffled; positions dense, with gaps, or spread wider
+    than the rank bitmap (counting fallback)."""
+    B, Hkv, G, D = 2, 2, 4, 128
+    L, cap, n_obs, pool = 300, 320, 32, 7
+    rng = np.random.Generator(np.random.PCG64(70 + len(layout)))
+    st = W.random_cache(71, B, G * Hkv, Hkv, D, dtype, cap, [[L, L], [L, L - 45]])
+    for b in range(B):
+        for j in range(Hkv):
+            n = int(st["len"][b, j])
+            if layout == "dense":
+                p = np.arange(n)
+            elif layout == "gaps":
+                p = np.sort(rng.choice(3 * n, size=n, replace=False))
+            else:
+                p = np.sort(rng.choice(1_500_000, size=n, replace=False))
+            st["pos"][b, j, :n] = rng.permutation(p).astype(np.int32)
+            st["imp"][b, j, :n] = 0.0
+    qf = rng.standard_normal((B, G * Hkv, n_obs, D)).astype(np.float32)
+    qo = W.bf16_bits(qf) if dtype == W.BF16 else qf
+    qpos = np.stack([np.sort(st["pos"][b, 0, :L])[-n_obs:] for b in range(B)]).astype(np.int32)
+    run = GpuRun(ref.copy_state(st), G * Hkv, budget_all=cap)
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(run.dev.shape, n_obs), dtype=torch.uint8, device="cuda")
+    say(f"[gpu] snapkv pooling dtype={dtype} layout={layout}")
+    assert H.hikv_prefill_scores(run.dev.shape, run.dev.cache, H.to_device(qo), torch.from_numpy(qpos).cuda(),
+                                 n_obs, 0, ws, pool=pool) == 0
+    torch.cuda.synchronize()
+    got = run.state()
+    want = ref.copy_state(st)
+    assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=0, pool=pool) == 0
+    np.testing.assert_allclose(got["imp"], want["imp"], rtol=1e-3, atol=1e-5)
