@@ -424,6 +424,24 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
   // More than one token over budget needs the bulk eviction, which the host
   // leaves out when the caller's lengths say that no unit needs it.
   if (a.no_bulk && L - beta > 1 && lt == 0 && tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+  // HiKV's chunked V side: the unit's first tile adds up the chunks' P.V
+  // partials in chunk order (the launch boundary made them visible).
+  if (a.s2_chunks && lt == 0) {
+    const int Dd = a.D;
+    const size_t NC = (size_t)((a.cap + Dd - 1) / Dd);
+    const int nc = (L + Dd - 1) / Dd;
+    float *outp = a.out + ((size_t)b * a.Hq + (size_t)(u - b * a.Hkv) * G) * Dd;
+    for (int i = tid; i < G * Dd; i += 256) {
+      float sum = 0.f;
+      for (int cc = 0; cc < nc; ++cc) sum += a.ws.chunk_acc[((size_t)u * NC + cc) * G * Dd + i];
+      outp[i] = sum;
+    }
+    if (a.dbg_count && tid < G) {
+      int k = 0;
+      for (int cc = 0; cc < nc; ++cc) k += a.ws.chunk_cnt[((size_t)u * NC + cc) * G + tid];
+      a.dbg_count[(size_t)b * a.Hq + (size_t)(u - b * a.Hkv) * G + tid] = k;
+    }
+  }
 
   float M[G], IL[G];
 #pragma unroll

@@ -322,9 +322,8 @@ __global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
 //     value), and of the entries equal to it the lowest-ranked complete r.
 //  3. the rows any q-head kept are read once, 16 bytes per lane, and each
 //     lane sums p * v for every q-head.
-//  4. the partials go out with device-coherent stores, each workgroup takes
-//     a ticket, and the unit's last one adds the chunks up in chunk order
-//     (results repeat bit for bit).
+//  4. the partials go out; the accumulation launch that follows adds each
+//     unit's chunks up in chunk order (results repeat bit for bit).
 // ---------------------------------------------------------------------------
 constexpr int kChunkBits = 1 << 17;  // position span the rank bitmap covers (16 KB)
 
@@ -519,7 +518,7 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
       kept += __popcll(__ballot(sel));
       s_p[g][lane + 64 * i] = sel ? pv[i] : 0.f;
     }
-    if (lane == 0) store_agent(&a.ws.chunk_cnt[((size_t)u * NC + c) * G + g], kept);
+    if (lane == 0) a.ws.chunk_cnt[((size_t)u * NC + c) * G + g] = kept;
   }
   __syncthreads();
   if (wave == 0) {  // the rows some q-head kept, in chunk order
@@ -590,29 +589,9 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
   }
   __syncthreads();
 
-  // 4. Partials out, ticket, and the last workgroup's sum over the chunks.
+  // 4. Partials out; k_accumulate adds them up.
   float *dst = a.ws.chunk_acc + ((size_t)u * NC + c) * G * D;
-  for (int i = tid; i < G * D; i += 256)
-    store_agent_f(dst + i, s_red[0][i] + s_red[1][i] + s_red[2][i] + s_red[3][i]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  __shared__ int s_last;
-  const int nc = (L + D - 1) / D;
-  if (tid == 0) s_last = ticket_agent(&a.ws.ticket[u]) == (uint32_t)(nc - 1);
-  __syncthreads();
-  if (!s_last) return;
-  for (int i = tid; i < G * D; i += 256) {
-    float sum = 0.f;
-    for (int cc = 0; cc < nc; ++cc)
-      sum += __int_as_float(load_agent(reinterpret_cast<const int32_t *>(a.ws.chunk_acc + ((size_t)u * NC + cc) * G * D + i)));
-    outp[i] = sum;
-  }
-  if (a.dbg_count && tid < G) {
-    int k = 0;
-    for (int cc = 0; cc < nc; ++cc) k += load_agent(&a.ws.chunk_cnt[((size_t)u * NC + cc) * G + tid]);
-    a.dbg_count[(size_t)b * a.Hq + (size_t)j * G + tid] = k;
-  }
-  if (tid == 0) a.ws.ticket[u] = 0;  // the accumulation launch counts on it from zero
+  for (int i = tid; i < G * D; i += 256) dst[i] = s_red[0][i] + s_red[1][i] + s_red[2][i] + s_red[3][i];
 }
 
 template <int EL, int D>
