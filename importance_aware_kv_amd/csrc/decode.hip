@@ -431,9 +431,16 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
     const size_t NC = (size_t)((a.cap + Dd - 1) / Dd);
     const int nc = (L + Dd - 1) / Dd;
     float *outp = a.out + ((size_t)b * a.Hq + (size_t)(u - b * a.Hkv) * G) * Dd;
+    const float *ca = a.ws.chunk_acc + (size_t)u * NC * G * Dd;
     for (int i = tid; i < G * Dd; i += 256) {
       float sum = 0.f;
-      for (int cc = 0; cc < nc; ++cc) sum += a.ws.chunk_acc[((size_t)u * NC + cc) * G * Dd + i];
+      for (int c0 = 0; c0 < nc; c0 += 8) {  // eight loads in flight, added in chunk order
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = c0 + e < nc ? ca[(size_t)(c0 + e) * G * Dd + i] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += v[e];
+      }
       outp[i] = sum;
     }
     if (a.dbg_count && tid < G) {
