@@ -183,7 +183,8 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     // (the channel-select launch also settles a pending eviction first)
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
-    if ((e = launch_combine(a, false, s)) != hipSuccess) return dev_err(e);
+    // (no combine launch: the launches that need the unit statistics take
+    // them from the tiles' partials themselves)
     if (a.s2_chunks) {
       if ((e = launch_chunk_pv(a, dt, s)) != hipSuccess) return dev_err(e);
     } else {

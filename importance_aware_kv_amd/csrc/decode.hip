@@ -453,8 +453,9 @@ __global__ __launch_bounds__(256) void k_accumulate(StepArgs a) {
   float M[G], IL[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    M[g] = a.ws.stats[((size_t)u * G + g) * 2];
-    IL[g] = 1.f / a.ws.stats[((size_t)u * G + g) * 2 + 1];
+    float Sg;
+    unit_softmax_stats(a, u, g, M[g], Sg);
+    IL[g] = 1.f / Sg;
   }
   const float *lg = a.ws.logits + (size_t)u * a.cap * G;
   float *imp = a.imp + (size_t)u * a.cap;

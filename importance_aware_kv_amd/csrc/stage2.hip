@@ -371,6 +371,19 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
     for (int g = 0; g < G; ++g) s_p[g][t] = -INFINITY;
   }
 
+  // The unit statistics of this wave's q-heads (w, w + 4), loaded now so
+  // that they arrive with the positions.
+  float Mw[2] = {0.f, 0.f}, ILw[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int g = wave + 4 * k;
+    if (g < G) {
+      float Sg;
+      unit_softmax_stats(a, u, g, Mw[k], Sg);
+      ILw[k] = 1.f / Sg;
+    }
+  }
+
   // 1. Ranks.  The first KR * 256 tokens keep position and logits in
   // registers; later ones (long units) are read again.
   int ps[KR];
@@ -483,8 +496,7 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
 
   // 2. Selection.
   for (int g = wave; g < G; g += 4) {
-    const float M = a.ws.stats[((size_t)u * G + g) * 2];
-    const float IL = 1.f / a.ws.stats[((size_t)u * G + g) * 2 + 1];
+    const float M = Mw[g >> 2], IL = ILw[g >> 2];
     float pv[NPL];
     uint32_t kv[NPL];
 #pragma unroll
