@@ -188,8 +188,7 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     if (a.s2_chunks) {
       if ((e = launch_chunk_pv(a, dt, s)) != hipSuccess) return dev_err(e);
     } else {
-      if ((e = launch_stage2_tokens(a, s)) != hipSuccess) return dev_err(e);
-      if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);
+      if ((e = launch_stage2_exact(a, dt, s)) != hipSuccess) return dev_err(e);  // selection + exact pass
     }
   }
   // With the caller's lengths and one budget for every unit, the host knows

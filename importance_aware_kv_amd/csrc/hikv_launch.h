@@ -35,7 +35,6 @@ bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint);
 
 // Stage II.
 hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s);
-hipError_t launch_stage2_tokens(const StepArgs &a, hipStream_t s);
 hipError_t launch_stage2_exact(const StepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s);
 

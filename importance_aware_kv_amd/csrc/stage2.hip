@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64) void k_stage2_channels(StepArgs a, int el) {
 // (ties: lower position), gathered in slot order.
 constexpr int kSelThreads = 256;
 
-__global__ __launch_bounds__(kSelThreads) void k_stage2_tokens(StepArgs a) {
+__device__ __forceinline__ void stage2_tokens(const StepArgs &a) {
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int b = bh / a.Hq, h = bh - b * a.Hq, j = h / a.G, g = h - j * a.G;
   const int u = b * a.Hkv + j;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kSelThreads) void k_stage2_tokens(StepArgs a) {
 // them only, P.V.  Same lane layout as the attention kernel: LPR lanes per
 // row, one online softmax per row, rows and waves merged at the end.
 template <int EL, int D>
-__global__ __launch_bounds__(256) void k_stage2_exact(StepArgs a) {
+__device__ __forceinline__ void stage2_exact(const StepArgs &a) {
   constexpr int CH = 16 / EL, LPR = D / CH, TPW = kWave / LPR;
   constexpr int U = (16 / TPW) > 0 ? 16 / TPW : 1;
   constexpr int RB = D * EL;
@@ -634,19 +634,26 @@ hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_stage2_tokens(const StepArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_stage2_tokens, dim3(a.B * a.Hq), dim3(kSelThreads), 0, s, a);
-  return hipGetLastError();
+
+// S2 + S3 in one launch per (b, q-head): the selected slots go to global
+// memory and are read back by the same workgroup after a barrier (all of
+// its waves share one CU's cache, so the barrier's fences make them
+// visible), which saves a launch and its drain.
+template <int EL, int D>
+__global__ __launch_bounds__(256) void k_stage2_select_exact(StepArgs a) {
+  stage2_tokens(a);
+  __syncthreads();
+  stage2_exact<EL, D>(a);
 }
 
 hipError_t launch_stage2_exact(const StepArgs &a, int dtype, hipStream_t s) {
   const dim3 grid(a.B * a.Hq), block(256);
   if (dtype == HIKV_BF16) {
-    if (a.D == 128) hipLaunchKernelGGL((k_stage2_exact<2, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_stage2_exact<2, 64>), grid, block, 0, s, a);
+    if (a.D == 128) hipLaunchKernelGGL((k_stage2_select_exact<2, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_stage2_select_exact<2, 64>), grid, block, 0, s, a);
   } else {
-    if (a.D == 128) hipLaunchKernelGGL((k_stage2_exact<4, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_stage2_exact<4, 64>), grid, block, 0, s, a);
+    if (a.D == 128) hipLaunchKernelGGL((k_stage2_select_exact<4, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_stage2_select_exact<4, 64>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
