@@ -29,6 +29,7 @@
 
 #include "hikv_block.h"
 #include "hikv_launch.h"
+#include "hikv_stats.h"
 
 namespace hikv {
 

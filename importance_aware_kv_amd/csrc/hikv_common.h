@@ -242,23 +242,6 @@ __device__ __forceinline__ void store_agent_f(float *p, float v) {
   store_agent(reinterpret_cast<int32_t *>(p), __float_as_int(v));
 }
 
-// A unit's softmax statistics for q-head g of its group (log2-domain max and
-// sum over every live token) from its split-K tiles' partials, in tile
-// order: the same values the combine launch writes, so the launches after
-// the attention tiles need not wait for it.
-__device__ __forceinline__ void unit_softmax_stats(const StepArgs &a, int u, int g, float &M, float &S) {
-  const int U = a.n_units;
-  const int t0 = a.ws.plan[u], t1 = (u + 1 < U) ? a.ws.plan[u + 1] : a.ws.plan[U];
-  const float *pm = a.ws.part_ml;
-  float m = -INFINITY;
-  for (int t = t0; t < t1; ++t) m = fmaxf(m, pm[((size_t)t * a.G + g) * 2]);
-  const float ms = (m == -INFINITY) ? 0.f : m;
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += pm[((size_t)t * a.G + g) * 2 + 1] * fast_exp2(pm[((size_t)t * a.G + g) * 2] - ms);
-  M = m;
-  S = s;
-}
-
 __device__ __forceinline__ int unit_budget(const StepArgs &a, int u) {
   return a.budget ? a.budget[u] : a.budget_all;
 }

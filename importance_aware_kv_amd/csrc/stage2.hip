@@ -15,6 +15,7 @@
 
 #include "hikv_block.h"
 #include "hikv_launch.h"
+#include "hikv_stats.h"
 
 namespace hikv {
 

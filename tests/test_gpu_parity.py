@@ -676,3 +676,37 @@ def test_prefill_scores_snapkv_pooling(dtype, layout):
     want = ref.copy_state(st)
     assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=0, pool=pool) == 0
     np.testing.assert_allclose(got["imp"], want["imp"], rtol=1e-3, atol=1e-5)
+
+
+def test_variant_edge_cases():
+    """Dual bank with no window (nothing accumulates), the chunked V side
+    keeping one entry per chunk, and Kelle's logits with sinks and a window."""
+    w = W.workload("llama8b", ctx=600, steps=3, batch=2)
+    d = W.generate(w)
+    _frozen_scores(d, w.ctx, 81)
+    cases = [
+        dict(budget_all=200, n_sink=0, n_recent=0, accumulate=H.HIKV_ACC_RECENT),
+        dict(budget_all=200, n_sink=4, n_recent=16, r=8, kT=0, stage2_v=H.HIKV_S2V_CHUNK),
+        dict(budget_all=100, n_sink=4, n_recent=16, r=1, kT=0, stage2_v=H.HIKV_S2V_CHUNK,
+             accumulate=H.HIKV_ACC_LOGIT),
+    ]
+    for i, kw in enumerate(cases):
+        run = GpuRun(ref.copy_state(d), w.n_q_heads, hint=True, **kw)
+        lockstep(run, d, w.steps, tag=f"variant edge {i}")
+
+
+def test_prefill_pool_wider_than_the_prompt():
+    B, Hkv, G, D, L = 1, 2, 2, 128, 90
+    rng = np.random.Generator(np.random.PCG64(82))
+    st = W.random_cache(83, B, G * Hkv, Hkv, D, W.BF16, 96, [[L, L - 7]])
+    st["imp"][:] = 0.0
+    qo = W.bf16_bits(rng.standard_normal((B, G * Hkv, 8, D)).astype(np.float32))
+    qpos = np.full((B, 8), int(st["pos"].max()), dtype=np.int32) - np.arange(8, dtype=np.int32)[None]
+    run = GpuRun(ref.copy_state(st), G * Hkv, budget_all=96)
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(run.dev.shape, 8), dtype=torch.uint8, device="cuda")
+    assert H.hikv_prefill_scores(run.dev.shape, run.dev.cache, H.to_device(qo), torch.from_numpy(qpos).cuda(),
+                                 8, 0, ws, pool=1000) == 0
+    torch.cuda.synchronize()
+    want = ref.copy_state(st)
+    assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=0, pool=1000) == 0
+    np.testing.assert_allclose(run.state()["imp"], want["imp"], rtol=1e-3, atol=1e-5)
