@@ -710,3 +710,13 @@ def test_prefill_pool_wider_than_the_prompt():
     want = ref.copy_state(st)
     assert ref.prefill_scores(want, G * Hkv, qo, qpos, window=0, pool=1000) == 0
     np.testing.assert_allclose(run.state()["imp"], want["imp"], rtol=1e-3, atol=1e-5)
+
+
+def test_stage2_exact_over_more_than_one_slot_chunk():
+    """k_T above the 1024 slots the exact pass stages in LDS at a time: the
+    selected slots are read back from memory by the workgroup that wrote
+    them, over two chunks."""
+    w = W.workload("twostage", ctx=1800, steps=2, batch=1)
+    w.budget_all, w.n_recent, w.stage2_tokens = 1700, 32, 1500
+    d = W.generate(w)
+    lockstep(_run(w, d), d, w.steps, tag="stage2 k_T 1500")
