@@ -720,3 +720,35 @@ def test_stage2_exact_over_more_than_one_slot_chunk():
     w.budget_all, w.n_recent, w.stage2_tokens = 1700, 32, 1500
     d = W.generate(w)
     lockstep(_run(w, d), d, w.steps, tag="stage2 k_T 1500")
+
+
+@pytest.mark.parametrize("L", [16384, 40000])
+def test_prefill_scores_conserve_mass_at_size(L):
+    """At prompt sizes the oracle cannot finish: every query's softmax row
+    sums to one, so with every prompt position observing (window 0) the
+    added importance of a unit sums to n_obs * G; with a window it is at most
+    that, and every score is non-negative."""
+    B, Hkv, G, D = 1, 2, 4, 128
+    rng = np.random.Generator(np.random.PCG64(90 + L))
+    kf = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    st = dict(k=W.bf16_bits(kf), v=np.zeros((B, Hkv, L, D), np.uint16),
+              pos=np.ascontiguousarray(np.broadcast_to(rng.permutation(L).astype(np.int32), (B, Hkv, L))),
+              imp=np.zeros((B, Hkv, L), np.float32), len=np.full((B, Hkv), L, np.int32))
+    del kf
+    qo = W.bf16_bits(rng.standard_normal((B, G * Hkv, L, D)).astype(np.float32))
+    qpos = np.arange(L, dtype=np.int32)[None].copy()
+    run = GpuRun(st, G * Hkv, budget_all=L)
+    ws = torch.zeros(H.hikv_prefill_workspace_bytes(run.dev.shape, L), dtype=torch.uint8, device="cuda")
+    for window in (0, 1000):
+        run.dev.imp.zero_()
+        say(f"[gpu] prefill mass L={L} window={window}")
+        assert H.hikv_prefill_scores(run.dev.shape, run.dev.cache, H.to_device(qo), torch.from_numpy(qpos).cuda(),
+                                     L, window, ws) == 0
+        torch.cuda.synchronize()
+        imp = run.dev.imp.cpu().numpy().astype(np.float64)
+        assert imp.min() >= 0.0
+        tot = imp.sum(axis=-1)
+        if window == 0:
+            assert np.abs(tot - L * G).max() <= 1e-3 * L * G, tot
+        else:
+            assert np.all(tot <= L * G * (1 + 1e-4)), tot
