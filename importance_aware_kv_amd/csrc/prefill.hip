@@ -237,11 +237,13 @@ struct TileMask {
 template <int D>
 __global__ __launch_bounds__(256) void k_prefill_stats_mfma(PrefillArgs p) {
   constexpr int RB = D * 2, LRB = RB + 16, KS = D / 32;
-  const int qt = blockIdx.x, ug = blockIdx.y, g = ug % p.G, u = ug / p.G;
+  const int nkt = (p.cap + kPT - 1) / kPT, nqt = (p.n_obs + kPT - 1) / kPT;
+  // last query tiles first: in a causal prompt they see the most keys, so
+  // the longest workgroups start first and the short ones fill the tail
+  const int qt = nqt - 1 - (int)blockIdx.x, ug = blockIdx.y, g = ug % p.G, u = ug / p.G;
   const int b = u / p.Hkv, j = u - b * p.Hkv, h = j * p.G + g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, quad = lane >> 4, col = lane & 15;
   const int L = min(p.len[u], p.cap);
-  const int nkt = (p.cap + kPT - 1) / kPT, nqt = (p.n_obs + kPT - 1) / kPT;
   const int ntile = (L + kPT - 1) / kPT;
   const int qmax = p.qrange[((size_t)b * nqt + qt) * 2 + 1];
   __shared__ uint32_t sMask[kMaxTiles / 32], sFull[kMaxTiles / 32];
