@@ -11,6 +11,14 @@ Cold measurement: the steps cycle over L independent layer copies (like
 successive layers of a model), so the ~34 MB a step touches is not resident
 in the 256 MB Infinity Cache when the step starts.
 
+--workload selects another seeded workload with the same protocol: llama8b,
+longctx128k, longctx128k_full (no eviction), twostage (Stage II, exact
+top-k_T V side), hikv_dualbank (HiKV's dual-bank Stage I; also times the
+bank initialisation's prompt scores), hikv_hier (dual bank plus HiKV's
+chunked Stage II V side), tiny.  --accumulate overrides the importance
+accumulation (H2O probabilities, HiKV's recent window, Kelle's logits);
+--prefill times the prompt scores on any workload.
+
 Prints one JSON line (stdout).  Diagnostics go to stderr.
 """
 
