@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG, "libhikv.so")
 HIKV_F32, HIKV_BF16 = 0, 1
 HIKV_ACC_ALL, HIKV_ACC_RECENT, HIKV_ACC_LOGIT = 0, 1, 2
 HIKV_S2V_TOPK, HIKV_S2V_CHUNK = 0, 1
+HIKV_PATH_AUTO, HIKV_PATH_MULTI_LAUNCH = 0, 1
 HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
 
 EXPORTS = ("hikv_state_bytes", "hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_settle", "hikv_pending",
@@ -46,7 +47,7 @@ class hikv_policy(C.Structure):
 
 class hikv_debug(C.Structure):
     _fields_ = [("sel_channels", C.c_void_p), ("sel_tokens", C.c_void_p), ("sel_count", C.c_void_p),
-                ("attend_start", C.c_void_p), ("attend_stop", C.c_void_p)]
+                ("attend_start", C.c_void_p), ("attend_stop", C.c_void_p), ("stage1_path", C.c_int32)]
 
 
 _lib = None
@@ -193,6 +194,17 @@ class DeviceCache:
             raise RuntimeError("invalid cache shape")
         self.evict = torch.zeros((n + 15) // 16 * 4, dtype=torch.int32, device=device)
         self.cache = self.make_cache()
+
+    def clone(self) -> "DeviceCache":
+        """A device copy of this cache (rows, positions, importance, lengths and
+        the pending-eviction state)."""
+        c = DeviceCache.__new__(DeviceCache)
+        c.torch = self.torch
+        c.dtype, c.shape = self.dtype, self.shape
+        for f in ("k", "v", "pos", "imp", "len", "evict"):
+            setattr(c, f, getattr(self, f).clone())
+        c.cache = c.make_cache()
+        return c
 
     def make_cache(self) -> "hikv_cache":
         return hikv_cache(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(),

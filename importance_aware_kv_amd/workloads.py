@@ -272,3 +272,10 @@ def random_step(seed: int, B: int, Hq: int, Hkv: int, D: int, dtype: int, new_po
     vn = rng.standard_normal((B, Hkv, D), dtype=np.float32)
     return dict(q=_pack(q, dtype), k_new=_pack(kn, dtype), v_new=_pack(vn, dtype),
                 new_pos=np.broadcast_to(np.asarray(new_pos, dtype=np.int32), (B,)).copy())
+
+
+def random_steps(seed: int, n: int, B: int, Hq: int, Hkv: int, D: int, dtype: int, first_pos: int):
+    """n decode steps of random q, k, v (positions first_pos, first_pos + 1, ...),
+    stacked on a leading step axis."""
+    steps = [random_step(seed + 7919 * t, B, Hq, Hkv, D, dtype, first_pos + t) for t in range(n)]
+    return {k: np.stack([s[k] for s in steps]) for k in steps[0]}

@@ -157,7 +157,15 @@ typedef struct hikv_debug {
   void *attend_stop;       /* attention launch records when it starts and ends executing (Stage I: the
                               launch over every live K and V row; Stage II: the reduced-channel logits
                               pass over every live K row) */
+  int32_t stage1_path;     /* Stage I launch sequence: HIKV_PATH_AUTO (the library's choice) or
+                              HIKV_PATH_MULTI_LAUNCH (settle, attention tiles, combine, accumulate
+                              and bulk eviction as separate launches, evicting in place; kept to
+                              compare against).  Results are the same on every path.  Any other
+                              value is HIKV_EINVAL. */
 } hikv_debug;
+
+#define HIKV_PATH_AUTO 0
+#define HIKV_PATH_MULTI_LAUNCH 1
 
 /* Bytes of hikv_cache.evict for this shape (a few words per unit).  0 on a
  * bad shape. */

@@ -40,7 +40,7 @@ def say(*a):
 class GpuRun:
     def __init__(self, state, n_q_heads, *, budget=None, budget_all=0, n_sink=0, n_recent=0,
                  r=0, kT=0, scale=0.0, hint=False, accumulate=H.HIKV_ACC_ALL,
-                 stage2_v=H.HIKV_S2V_TOPK):
+                 stage2_v=H.HIKV_S2V_TOPK, stage1_path=H.HIKV_PATH_AUTO):
         self.Hq = n_q_heads
         self.hint = hint
         self.pol_args = None
@@ -65,7 +65,9 @@ class GpuRun:
                 sel_channels=torch.full((sh.batch, n_q_heads, r), -7, dtype=torch.int32, device="cuda"),
                 sel_tokens=torch.full((sh.batch, n_q_heads, kT), -7, dtype=torch.int32, device="cuda"),
                 sel_count=torch.full((sh.batch, n_q_heads), -7, dtype=torch.int32, device="cuda"))
-            self.dbg = H.hikv_debug(*[self.dbg_t[f].data_ptr() for f in self.dbg_t])
+            self.dbg = H.hikv_debug(*[self.dbg_t[f].data_ptr() for f in self.dbg_t], None, None, stage1_path)
+        elif stage1_path != H.HIKV_PATH_AUTO:
+            self.dbg = H.hikv_debug(None, None, None, None, None, stage1_path)
 
     def pending(self):
         """Each unit's dead slot (-1: no eviction pending), read without changing anything."""
@@ -75,24 +77,12 @@ class GpuRun:
         return out.cpu().numpy()
 
     def state(self):
-        """The cache as the method defines it: the device state with every
-        pending eviction applied the way hikv_settle applies it (the unit's
-        last slot moves into the dead one), computed on the host so that the
-        device keeps running with its evictions pending."""
-        st = self.dev.to_numpy()
-        dead = self.pending()
-        for b in range(dead.shape[0]):
-            for j in range(dead.shape[1]):
-                d = int(dead[b, j])
-                if d < 0:
-                    continue
-                last = int(st["len"][b, j]) - 1
-                assert 0 <= d <= last, (b, j, d, last)
-                if d != last:
-                    for f in ("k", "v", "pos", "imp"):
-                        st[f][b, j, d] = st[f][b, j, last]
-                st["len"][b, j] = last
-        return st
+        """The cache as the method defines it after the last step: a device
+        copy of the cache settled by hikv_settle (every deferred or pending
+        eviction applied), so that the device keeps running on its own state."""
+        c = self.dev.clone()
+        H.check(H.hikv_settle(c.shape, c.cache, self.pol, self.ws), "hikv_settle")
+        return c.to_numpy()
 
     def step(self, q, k_new, v_new, new_pos, expect=H.HIKV_OK, hint_override=None):
         qt, kt, vt = H.to_device(q), H.to_device(k_new), H.to_device(v_new)
@@ -112,7 +102,7 @@ class GpuRun:
         assert st == expect, (st, H.status_string(st))
         out = self.out.cpu().numpy()
         dbg = None
-        if self.dbg is not None:
+        if self.r > 0:
             dbg = {k: v.cpu().numpy() for k, v in self.dbg_t.items()}
         return out, dbg
 

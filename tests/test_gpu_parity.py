@@ -53,21 +53,17 @@ def test_tiny_free_running_matches_oracle():
         assert list(ref.live_positions(g, 0, 0)) == list(ref.live_positions(st, 0, 0)), t
 
 
-@pytest.fixture
-def multi_kernel_path(monkeypatch):
-    """Route Stage I through the multi-kernel path instead of the single launch."""
-    monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
-    yield
+MULTI = dict(stage1_path=H.HIKV_PATH_MULTI_LAUNCH)  # Stage I as separate launches, evicting in place
 
 
-def test_multi_kernel_path_lockstep(multi_kernel_path):
+def test_multi_kernel_path_lockstep():
     w = W.workload("llama8b", ctx=900, steps=3, batch=2)
     w.budget_all, w.n_recent = 200, 16
     d = W.generate(w)
-    lockstep(_run(w, d), d, w.steps, tag="multi-kernel")
+    lockstep(_run(w, d, **MULTI), d, w.steps, tag="multi-kernel")
     wt = W.workload("tiny", steps=6)
     dt = W.generate(wt)
-    lockstep(_run(wt, dt), dt, wt.steps, tag="multi-kernel tiny")
+    lockstep(_run(wt, dt, **MULTI), dt, wt.steps, tag="multi-kernel tiny")
 
 
 def test_many_units_use_multi_kernel_path():
@@ -111,6 +107,77 @@ def test_twostage_host_hint_skips_bulk_launch():
     lockstep(_run(w, d, hint=True), d, w.steps, tag="twostage-hint")
 
 
+def test_wrong_host_length_hint_in_the_steady_state_is_reported():
+    """A hint one short of the device's length in the steady state (the
+    one-launch step's case: no bulk cut either way) is reported as
+    HIKV_EINVAL, and that unit's cache is left as it was."""
+    w = W.workload("llama8b", ctx=300, steps=3, batch=1)
+    w.budget_all, w.n_recent = 100, 8
+    d = W.generate(w)
+    run = _run(w, d, hint=True)
+    for t in range(2):
+        run.step(d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t])
+    before = run.state()
+    wrong = np.ascontiguousarray(run.dev.len.cpu().numpy() - 1, dtype=np.int32)
+    run.step(d["q"][2], d["k_new"][2], d["v_new"][2], d["new_pos"][2], expect=H.HIKV_EINVAL,
+             hint_override=wrong)
+    after = run.state()
+    for f in ("k", "v", "pos", "imp", "len"):
+        assert np.array_equal(before[f], after[f]), f
+
+
+def test_paths_interleave_on_one_cache():
+    """One cache driven by every Stage I launch sequence in turn -- one launch
+    (host lengths), two launches (none), the multi-launch sequence -- and by
+    Stage II steps, hikv_settle and hikv_evict; each step checked against the
+    oracle run from the settled state before it."""
+    w = W.workload("headkv32k", ctx=1200, steps=14, batch=2)
+    w.budgets = np.tile(W.dirichlet_budgets(93, 8, 8 * 120, 16, 500), (2, 1))
+    d = W.generate(w)
+    budget = w.budget_array()
+    run = _run(w, d, r=32, kT=64)   # workspace sized for Stage II too
+    bt = torch.from_numpy(budget).cuda()
+    modes = ["fused", "fused", "two", "fused", "multi", "fused", "fused", "stage2", "fused", "two",
+             "settle", "two", "fused", "evict"]
+    multi = H.hikv_debug(None, None, None, None, None, H.HIKV_PATH_MULTI_LAUNCH)
+    for t, mode in enumerate(modes):
+        pre = run.state()
+        q, kn, vn, npos = d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t]
+        say(f"[gpu] interleave step {t}: {mode}")
+        if mode in ("settle", "evict"):
+            if mode == "settle":
+                H.check(H.hikv_settle(run.dev.shape, run.dev.cache, run.pol, run.ws))
+            else:
+                newest = torch.from_numpy(np.ascontiguousarray(d["new_pos"][t - 1], dtype=np.int32)).cuda()
+                H.check(H.hikv_evict(run.dev.shape, run.dev.cache, run.pol, newest, run.ws))
+            assert H.hikv_device_status(run.ws) == 0
+            got = run.dev.to_numpy()
+            assert (run.pending() == -1).all()
+            for f in ("pos", "len"):
+                assert np.array_equal(got[f], pre[f]), (t, f)
+            continue
+        r, kT = (32, 64) if mode == "stage2" else (0, 0)
+        lh = np.ascontiguousarray(run.dev.len.cpu().numpy(), dtype=np.int32)
+        pol = H.make_policy(bt, 0, w.n_sink, w.n_recent, r, kT, len_hint=lh if mode == "fused" else None,
+                            budget_hint=budget if mode == "fused" else None)
+        qt, kt, vt = H.to_device(q), H.to_device(kn), H.to_device(vn)
+        pt = torch.from_numpy(np.ascontiguousarray(npos, dtype=np.int32)).cuda()
+        H.check(H.hikv_decode_step(run.dev.shape, run.dev.cache, pol, qt, kt, vt, pt, run.out, run.ws,
+                                   debug=multi if mode == "multi" else None))
+        assert H.hikv_device_status(run.ws) == 0, (t, mode)
+        out = run.out.cpu().numpy()
+        post = run.state()
+        st = ref.copy_state(pre)
+        kw = dict(budget=budget, budget_all=0, n_sink=w.n_sink, n_recent=w.n_recent, stage2_channels=r,
+                  stage2_tokens=kT, scale=0.0)
+        code, want, dref = ref.decode_step(st, w.n_q_heads, q, kn, vn, npos, **kw)
+        assert code == 0
+        e = row_errors(out, want)
+        assert e.max() <= OUT_TOL[w.dtype], (t, mode, float(e.max()))
+        assert np.array_equal(post["len"], st["len"]), (t, mode)
+        check_kept(pre, post, st, dref, kw, npos, where=f"interleave {t} {mode}")
+
+
 def test_wrong_host_length_hint_stage2_is_reported():
     """A hint under which no unit needs the bulk eviction, while the device's
     lengths need it, is reported as HIKV_EINVAL."""
@@ -141,9 +208,11 @@ def test_settle_applies_the_pending_eviction():
     assert (run.pending() == -1).all()
 
 
-def test_stage2_step_after_pending_eviction():
-    """A Stage II step on a cache whose last two-launch step left an eviction
-    pending settles it first: outputs and kept sets equal the oracle's."""
+@pytest.mark.parametrize("hint", [True, False], ids=["fused", "two-launch"])
+def test_stage2_step_after_pending_eviction(hint):
+    """A Stage II step on a cache whose last Stage I step left an eviction
+    pending (deferred, after the one-launch step) settles it first: outputs
+    and kept sets equal the oracle's."""
     w = W.workload("llama8b", ctx=600, steps=3, batch=2)
     w.budget_all, w.n_recent = 128, 16
     d = W.generate(w)
@@ -163,7 +232,11 @@ def test_stage2_step_after_pending_eviction():
         else:
             qt, kt, vt = H.to_device(q), H.to_device(kn), H.to_device(vn)
             pt = torch.from_numpy(np.ascontiguousarray(npos, dtype=np.int32)).cuda()
-            H.check(H.hikv_decode_step(run.dev.shape, run.dev.cache, pol1, qt, kt, vt, pt, run.out, run.ws))
+            p1 = pol1
+            if hint:
+                lh = np.ascontiguousarray(run.dev.len.cpu().numpy(), dtype=np.int32)
+                p1 = H.make_policy(None, w.budget_all, w.n_sink, w.n_recent, len_hint=lh)
+            H.check(H.hikv_decode_step(run.dev.shape, run.dev.cache, p1, qt, kt, vt, pt, run.out, run.ws))
             assert H.hikv_device_status(run.ws) == 0
             out = run.out.cpu().numpy()
         code, want, _ = ref.decode_step(st, w.n_q_heads, q, kn, vn, npos, **(kw2 if stage2 else kw1))
@@ -180,25 +253,33 @@ def test_stage2_step_after_pending_eviction():
     assert (run.pending() == -1).all()               # the Stage II step settled and evicted in place
 
 
-def test_llama8b_reduced_lockstep():
-    w = W.workload("llama8b", ctx=1000, steps=3, batch=2)
+# Stage I paths of a bf16, D = 128 cache: with the caller's lengths (hint) the
+# steady steps run as one launch (fused.hip); without, as two launches.
+PATHS = pytest.mark.parametrize("hint", [True, False], ids=["fused", "two-launch"])
+
+
+@PATHS
+def test_llama8b_reduced_lockstep(hint):
+    w = W.workload("llama8b", ctx=1000, steps=5, batch=2)
     w.budget_all, w.n_recent = 256, 32
     d = W.generate(w)
-    worst, _ = lockstep(_run(w, d), d, w.steps, tag="llama8b-small")
+    worst, _ = lockstep(_run(w, d, hint=hint), d, w.steps, tag="llama8b-small")
     say("llama8b reduced worst row err", worst)
 
 
-def test_headkv_ragged_budgets_lockstep():
-    w = W.workload("headkv32k", ctx=2000, steps=3, batch=2)
+@PATHS
+def test_headkv_ragged_budgets_lockstep(hint):
+    w = W.workload("headkv32k", ctx=2000, steps=5, batch=2)
     w.budgets = np.tile(W.dirichlet_budgets(77, 8, 8 * 160, 16, 600), (2, 1))
     w.n_recent = 128                              # budgets below S + W clamp the window
     d = W.generate(w)
-    worst, _ = lockstep(_run(w, d), d, w.steps, tag="headkv-small")
+    worst, _ = lockstep(_run(w, d, hint=hint), d, w.steps, tag="headkv-small")
     say("headkv reduced worst row err", worst)
 
 
+@PATHS
 @pytest.mark.parametrize("n_recent", [128, 0], ids=["window", "no-window"])
-def test_long_units_split_eviction_lockstep(n_recent):
+def test_long_units_split_eviction_lockstep(n_recent, hint):
     """Steady-state eviction in units longer than one importance block of the
     second launch (2048 tokens): each block's lowest key meets the others' in
     the unit's last block to finish.  Budgets put the new token alone in the
@@ -208,17 +289,18 @@ def test_long_units_split_eviction_lockstep(n_recent):
     w.budgets = np.array([[2048, 4097, 6143, 100, 3000, 64, 2049, 5000]], dtype=np.int32)
     w.n_recent = n_recent
     d = W.generate(w)
-    lockstep(_run(w, d), d, w.steps, tag=f"split eviction n_recent={n_recent}")
+    lockstep(_run(w, d, hint=hint), d, w.steps, tag=f"split eviction n_recent={n_recent}")
 
 
-def test_longctx_g8_lockstep_and_full_attention():
-    w = W.workload("longctx128k", ctx=3000, steps=2, batch=1)
+@PATHS
+def test_longctx_g8_lockstep_and_full_attention(hint):
+    w = W.workload("longctx128k", ctx=3000, steps=4, batch=1)
     w.budget_all, w.n_recent = 256, 64
     d = W.generate(w)
-    lockstep(_run(w, d), d, w.steps, tag="longctx-small")
-    wf = W.workload("longctx128k", ctx=3000, steps=2, batch=1, full=True)
+    lockstep(_run(w, d, hint=hint), d, w.steps, tag="longctx-small")
+    wf = W.workload("longctx128k", ctx=3000, steps=3, batch=1, full=True)
     df = W.generate(wf)
-    lockstep(_run(wf, df), df, wf.steps, tag="longctx-small-full")
+    lockstep(_run(wf, df, hint=hint), df, wf.steps, tag="longctx-small-full")
 
 
 def test_twostage_lockstep():
@@ -228,20 +310,23 @@ def test_twostage_lockstep():
     lockstep(_run(w, d), d, w.steps, tag="twostage-small")
 
 
+@PATHS
 @pytest.mark.parametrize("dtype", [W.F32, W.BF16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
-def test_shape_matrix(dtype, D, G):
+def test_shape_matrix(dtype, D, G, hint):
+    """Units that grow, sit at their budget, and are cut in bulk on the
+    first step; the steady steps after it (one launch for bf16, D = 128 with
+    the caller's lengths)."""
     B, Hkv = 2, 3
     Hq = G * Hkv
-    cap = 400
+    cap = 410
     lens = np.array([[0, 150, 399], [1, 63, 260]])
     st = W.random_cache(100 + G + D, B, Hq, Hkv, D, dtype, cap, lens)
-    data = W.random_step(200 + G, B, Hq, Hkv, D, dtype, st["newest"])
-    data = {k: v[None] for k, v in data.items()}
+    data = W.random_steps(200 + G, 4, B, Hq, Hkv, D, dtype, st["newest"])
     budget = np.array([[40, 100, 120], [1, 64, 300]], dtype=np.int32)
-    run = GpuRun(st, Hq, budget=budget, n_sink=1, n_recent=8)
-    lockstep(run, data, 1, tag=f"matrix dt={dtype} D={D} G={G}")
+    run = GpuRun(st, Hq, budget=budget, n_sink=1, n_recent=8, hint=hint)
+    lockstep(run, data, 4, tag=f"matrix dt={dtype} D={D} G={G} hint={hint}")
 
 
 def test_stage2_r_equals_d_reduces_to_stage1():
@@ -345,13 +430,14 @@ def test_prefill_scores_match_oracle(window, n_obs):
     np.testing.assert_allclose(got["imp"], want["imp"], rtol=2e-3, atol=2e-5)
 
 
-def test_repeat_step_is_bit_identical():
-    w = W.workload("llama8b", ctx=700, steps=2, batch=2)
+@PATHS
+def test_repeat_step_is_bit_identical(hint):
+    w = W.workload("llama8b", ctx=700, steps=4, batch=2)
     w.budget_all, w.n_recent = 200, 16
     d = W.generate(w)
     outs, states = [], []
     for _ in range(2):
-        run = _run(w, d)
+        run = _run(w, d, hint=hint)
         o = []
         for t in range(w.steps):
             out, _ = run.step(d["q"][t], d["k_new"][t], d["v_new"][t], d["new_pos"][t])
@@ -430,18 +516,17 @@ def _frozen_scores(d, ctx, seed):
 
 
 @pytest.mark.parametrize("path", ["two-launch", "two-launch-hint", "multi-kernel", "stage2"])
-def test_dual_bank_lockstep(path, monkeypatch):
+def test_dual_bank_lockstep(path):
     """First step cuts 1001 tokens to the budget (bulk), the rest evict one
     token each; no sinks, window = half the budget."""
     w = W.workload("llama8b", ctx=1000, steps=5, batch=2)
     w.budget_all, w.n_sink, w.n_recent, w.accumulate = 256, 0, 128, H.HIKV_ACC_RECENT
     if path == "stage2":
         w.stage2_channels, w.stage2_tokens = 32, 64
-    if path == "multi-kernel":
-        monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
+    extra = MULTI if path == "multi-kernel" else {}
     d = W.generate(w)
     _frozen_scores(d, w.ctx, 61)
-    worst, _ = lockstep(_run(w, d, hint=path == "two-launch-hint"), d, w.steps, tag=f"dual bank {path}")
+    worst, _ = lockstep(_run(w, d, hint=path == "two-launch-hint", **extra), d, w.steps, tag=f"dual bank {path}")
     say(f"dual bank {path} worst row err", worst)
 
 
@@ -574,17 +659,16 @@ def test_stage2_chunks_positions_beyond_the_rank_bitmap():
 # Kelle's importance: pre-softmax logits summed (accumulate = LOGIT).
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("path", ["two-launch", "two-launch-hint", "multi-kernel", "stage2", "stage2-chunks"])
-def test_logit_accumulation_lockstep(path, monkeypatch):
+def test_logit_accumulation_lockstep(path):
     w = W.workload("llama8b", ctx=1000, steps=4, batch=2)
     w.budget_all, w.n_recent, w.accumulate = 256, 32, H.HIKV_ACC_LOGIT
     if path.startswith("stage2"):
         w.stage2_channels, w.stage2_tokens = 32, 64
         if path == "stage2-chunks":
             w.stage2_v = H.HIKV_S2V_CHUNK
-    if path == "multi-kernel":
-        monkeypatch.setenv("HIKV_MULTI_KERNEL", "1")
+    extra = MULTI if path == "multi-kernel" else {}
     d = W.generate(w)
-    lockstep(_run(w, d, hint=path == "two-launch-hint"), d, w.steps, tag=f"logit accumulation {path}")
+    lockstep(_run(w, d, hint=path == "two-launch-hint", **extra), d, w.steps, tag=f"logit accumulation {path}")
 
 
 # ---------------------------------------------------------------------------
