@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhikv.so")
-SOURCES = ["api.hip", "decode.hip", "step.hip", "fused.hip", "stage2.hip", "prefill.hip"]
+SOURCES = ["api.hip", "decode.hip", "step.hip", "stage2.hip", "prefill.hip"]
 ARCH = os.environ.get("HIKV_ARCH", "gfx950")
 
 CFLAGS = [

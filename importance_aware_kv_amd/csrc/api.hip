@@ -4,7 +4,6 @@
 // hikv_device_status, which is documented to synchronise).
 
 #include <math.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include "hikv_launch.h"
@@ -84,8 +83,6 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
   a.imp = c->imp;
   a.len = c->len;
   a.evict = c->evict;
-  a.lazy = s->kv_dtype == HIKV_BF16 && s->head_dim == 128;
-  a.state_stride = unit_state_words(s->capacity, a.G, a.lazy != 0);
   a.budget = p->budget;
   a.budget_all = p->budget_all;
   a.n_sink = p->n_sink;
@@ -105,9 +102,7 @@ inline int dev_err(hipError_t e) { return e == hipSuccess ? HIKV_OK : HIKV_EDEVI
 
 extern "C" size_t hikv_state_bytes(const hikv_shape *shape) {
   if (check_shape(shape) != HIKV_OK) return 0;
-  const bool lazy = shape->kv_dtype == HIKV_BF16 && shape->head_dim == 128;
-  return sizeof(int32_t) * (size_t)shape->batch * shape->n_kv_heads *
-         (size_t)unit_state_words(shape->capacity, shape->n_q_heads / shape->n_kv_heads, lazy);
+  return sizeof(int32_t) * (size_t)shape->batch * shape->n_kv_heads * (size_t)state_words(shape->capacity);
 }
 
 extern "C" size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy) {
@@ -159,37 +154,19 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   hipError_t e;
   if (a.r == 0) {
     if (path == HIKV_PATH_AUTO) {
-      // With host copies of the lengths and budgets the host knows each unit's
-      // cut: a unit over its budget holds one token pending (a step evicts it),
-      // and a unit with more than one token to shed is cut in bulk.
-      const int U = shape->batch * shape->n_kv_heads;
-      bool know = policy->len_hint && (!policy->budget || policy->budget_hint);
-      bool any_bulk = false, any_single = false;
-      if (know) {
+      if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
+      // With host copies of the lengths and budgets, a step that cuts some
+      // unit by more than one token moves its survivors in a launch of its own.
+      if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
+        const int U = shape->batch * shape->n_kv_heads;
         for (int u = 0; u < U; ++u) {
           const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
           const int len = policy->len_hint[u];
-          const int live = len + 1 - (len > beta ? 1 : 0);
-          if (live - beta > 1) any_bulk = true;
-          if (live - beta == 1) any_single = true;
+          const int live = len + 1 - (len > beta ? 1 : 0);  // a unit over budget holds a dead slot
+          if (live - beta > 1) a.bulk_split = 1;
         }
       }
-      // bf16 rows with D = 128 and no bulk cut: the one-launch step.
-      if (a.lazy && know && !any_bulk && fused_host_plan(a, policy->len_hint))
-        return dev_err(launch_fused_step(a, s, ev0, ev1));
-      // Otherwise the two-launch step, on a cache whose deferred state (if
-      // any) is applied first; it leaves a single eviction pending in its own
-      // form, which the one-launch step does not read, so that is resolved
-      // after it.
-      if (a.lazy && (e = launch_settle_lazy(a, nullptr, true, s)) != hipSuccess) return dev_err(e);
-      if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
-      // a step that cuts some unit by more than one token moves its survivors
-      // in a launch of its own
-      if (know && any_bulk) a.bulk_split = 1;
-      if ((e = launch_step(a, dt, s, ev0, ev1)) != hipSuccess) return dev_err(e);
-      if (a.lazy && (!know || any_single) && (e = launch_settle_lazy(a, nullptr, true, s)) != hipSuccess)
-        return dev_err(e);
-      return HIKV_OK;
+      return dev_err(launch_step(a, dt, s, ev0, ev1));
     }
     // The four-launch path evicts in place: an eviction a two-launch step
     // left pending is resolved first.
@@ -197,9 +174,7 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     if ((e = launch_attn_tiles(a, dt, true, false, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
   } else {
-    // (the channel-select launch also settles a pending eviction of the
-    // two-launch form first; the deferred form is applied before it)
-    if (a.lazy && (e = launch_settle_lazy(a, nullptr, true, s)) != hipSuccess) return dev_err(e);
+    // (the channel-select launch also settles a pending eviction first)
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, false, true, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     // (no combine launch: the launches that need the unit statistics take

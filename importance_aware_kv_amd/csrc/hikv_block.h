@@ -295,7 +295,7 @@ __device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int be
 __device__ inline int pending_slot_wave(const StepArgs &a, int u) {
   const int lane = threadIdx.x & 63;
   const int nbm = imp_blocks(a.cap);
-  const int32_t *rec = a.evict + (size_t)u * a.state_stride;
+  const int32_t *rec = a.evict + (size_t)u * state_words(a.cap);
   const int n = min(rec[0], nbm);
   uint32_t khi = ~0u, klo = ~0u;
   int slot = -1;
@@ -318,7 +318,7 @@ __device__ inline int pending_slot_wave(const StepArgs &a, int u) {
 // slot order does not matter).
 __device__ inline void settle_unit(const StepArgs &a, int u, int rb) {
   const int lane = threadIdx.x & 63;
-  int32_t *rec = a.evict + (size_t)u * a.state_stride;
+  int32_t *rec = a.evict + (size_t)u * state_words(a.cap);
   if (rec[0] == 0) return;
   const int d = pending_slot_wave(a, u);
   if (d >= 0) {

@@ -27,32 +27,6 @@ __host__ __device__ inline int imp_blocks(int cap) { return (cap + kImpChunk - 1
 // block's lowest eviction key (low, high word) and that key's slot.
 __host__ __device__ inline int state_words(int cap) { return 4 * (imp_blocks(cap) + 1); }
 
-// Caches of bf16 rows with D = 128 (the fused step) carry, after those words,
-// a deferred-step record: the last step's softmax statistics and queries, so
-// that the next step can add that step's probabilities to the importance.
-// Words:
-constexpr int kLzFlag = 0;    // 1: the record holds a step whose probabilities are not yet added
-constexpr int kLzOver = 1;    // that step must evict one token (chosen from the keys the probabilities give)
-constexpr int kLzNewest = 2;  // its new token's position
-constexpr int kLzWp = 3;      // its protected window W'
-constexpr int kLzSink = 4;    // its sink count S
-constexpr int kLzAcc = 5;     // its accumulation mode (HIKV_ACC_*)
-constexpr int kLzCs = 6;      // its logit scale * log2(e), float bits
-constexpr int kLzM = 8;       // [G] per q-head maximum logit * logit scale * log2(e) (float)
-constexpr int kLzIL = 16;     // [G] per q-head 1 / softmax sum (float)
-constexpr int kLzQ = 32;      // [G][128] bf16: the step's queries
-__host__ __device__ inline int lazy_words(int G) { return kLzQ + 64 * G; }
-// The whole per-unit stride of hikv_cache.evict.
-__host__ __device__ inline int unit_state_words(int cap, int G, bool lazy) {
-  return state_words(cap) + (lazy ? lazy_words(G) : 0);
-}
-
-// Per split-K tile of the fused step: the token the tile held out of the
-// attention (its lowest eviction key), int32 words: [0] key low, [1] key
-// high, [2] slot, [3] 1 when there is one, [4 .. 4+G) its logit per q-head
-// (raw q.k, float), [12 .. 76) its V row, bf16 pairs.
-constexpr int kHoldWords = 80;
-
 // ---------------------------------------------------------------------------
 // Workspace layout.  Offsets are 256-byte aligned; everything is derived from
 // the shape and policy alone, so the host can size it without the device.
@@ -84,10 +58,9 @@ struct Ws {
   int32_t *nmoves;      // [n_units] bulk eviction: rows the move launch relocates (0: none)
   float *chunk_acc;     // [n_units][ceil(cap/D)][G][D] Stage II chunked V side: each chunk's P.V
   int32_t *chunk_cnt;   // [n_units][ceil(cap/D)][G] tokens each chunk kept per q-head
-  int32_t *hold;        // [max_tiles][kHoldWords] fused step: each tile's held-out token
 };
 
-constexpr int kWsParts = 22;
+constexpr int kWsParts = 21;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -122,7 +95,6 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chu
       sizeof(int32_t) * U,             // nmoves
       sizeof(float) * U * NC * G * D,  // chunk_acc
       sizeof(int32_t) * U * NC * G,    // chunk_cnt
-      sizeof(int32_t) * MT * kHoldWords,  // hold
   };
   WsSizes w;
   size_t o = 0;
@@ -158,7 +130,6 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.nmoves = reinterpret_cast<int32_t *>(b + s.off[18]);
   w.chunk_acc = reinterpret_cast<float *>(b + s.off[19]);
   w.chunk_cnt = reinterpret_cast<int32_t *>(b + s.off[20]);
-  w.hold = reinterpret_cast<int32_t *>(b + s.off[21]);
   return w;
 }
 
@@ -181,9 +152,7 @@ struct StepArgs {
   int32_t *pos;
   float *imp;
   int32_t *len;
-  int32_t *evict;            // [U][state_stride] pending eviction (cache state)
-  int32_t state_stride;      // words per unit of evict: unit_state_words(cap, G, lazy)
-  int32_t lazy;              // the cache carries the deferred-step record (bf16, D = 128)
+  int32_t *evict;            // [U][state_words(cap)] pending eviction (cache state)
   const int32_t *budget;     // may be null
   int32_t budget_all, n_sink, n_recent;
   int32_t acc_recent;        // importance accumulates only inside the protected window (HiKV dual bank)

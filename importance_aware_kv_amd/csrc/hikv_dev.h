@@ -1,6 +1,6 @@
-// hikv_dev.h -- device helpers of the split-K attention kernels (the two-launch
-// step and the fused step): plans, global->LDS staging, lane reductions,
-// eviction keys, the pending-eviction lookup and matrix-core operands.
+// hikv_dev.h -- device helpers of the two-launch step's split-K attention kernels:
+// plans, global->LDS staging, lane reductions, eviction keys, the
+// pending-eviction lookup and matrix-core operands.
 #pragma once
 
 #include "hikv_common.h"
@@ -415,7 +415,7 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 __device__ __forceinline__ int pend_stride(const StepArgs &a) { return imp_blocks(a.cap); }
 // The unit's record: [0] count, [1] dead slot, candidates from word 4.
 __device__ __forceinline__ int32_t *unit_state(const StepArgs &a, int u) {
-  return a.evict + (size_t)u * a.state_stride;
+  return a.evict + (size_t)u * state_words(a.cap);
 }
 
 // The lookup in the attention launch goes through LDS, 64 records of 16 bytes
@@ -556,6 +556,25 @@ __device__ __forceinline__ void mfma_operands(uint64_t (&o)[12], const uint32_t 
 
 // Wait until the sub-chunk being consumed has landed: at most k * STEP loads
 // (those of the k sub-chunks issued after it, 0 <= k <= K) may be outstanding.
+// Eight 8-byte LDS reads 32 bytes apart from one per-lane address, one wait.
+// asm: the array was filled by DMA, and a compiler-visible read of DMA'd LDS
+// makes the compiler wait for every load in flight, the ring's included.
+__device__ __forceinline__ void lds_read8_b64(uint64_t (&o)[8], uint32_t addr) {
+  asm volatile(
+      "ds_read_b64 %0, %8\n\t"
+      "ds_read_b64 %1, %8 offset:32\n\t"
+      "ds_read_b64 %2, %8 offset:64\n\t"
+      "ds_read_b64 %3, %8 offset:96\n\t"
+      "ds_read_b64 %4, %8 offset:128\n\t"
+      "ds_read_b64 %5, %8 offset:160\n\t"
+      "ds_read_b64 %6, %8 offset:192\n\t"
+      "ds_read_b64 %7, %8 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr)
+      : "memory");
+}
+
 template <int STEP, int K>
 __device__ __forceinline__ void vm_wait_ahead(int k) {
   if constexpr (K == 0) {

@@ -33,18 +33,6 @@ hipError_t launch_settle(const StepArgs &a, int dtype, int32_t *slot_out, bool a
 // does not apply (too many units), in which case the kernels derive it.
 bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint);
 
-// The Stage I step in one launch (bf16, D = 128; host plan from
-// fused_host_plan, no unit cut by more than one token).  The step leaves its
-// probabilities and its victim deferred in the cache (see fused.hip).
-hipError_t launch_fused_step(const StepArgs &a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-// The fused step's host plan (its own resident grid); false when it does not apply.
-bool fused_host_plan(StepArgs &a, const int32_t *len_hint);
-int fused_grid(int G);       // resident workgroups of the fused step
-int fused_max_tiles(int G);  // tiles of one unit its combine can take
-// Resolve the deferred state (or the two-launch form) of every unit; see
-// launch_settle.
-hipError_t launch_settle_lazy(const StepArgs &a, int32_t *slot_out, bool apply, hipStream_t s);
-
 // Stage II.
 hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_stage2_exact(const StepArgs &a, int dtype, hipStream_t s);

@@ -426,12 +426,12 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
                       min(TS, t1 - cr), t0, Lold, wave - 2, lane);
     }
     if (i == 0) {
+      // the group's queries as the B operand (head hl in column hl); read by
+      // asm so that the compiler does not wait for the ring's loads here
+      uint64_t w[8];
+      lds_read8_b64(w, lds_addr(qs + ((hl < G ? hl : 0) * D + 4 * qd) * EL));
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        uint2 w = make_uint2(0, 0);
-        if (hl < G) w = *reinterpret_cast<const uint2 *>(qs + (hl * D + 16 * ks + 4 * qd) * EL);
-        qb[ks] = __builtin_bit_cast(bf16x4_t, w);
-      }
+      for (int ks = 0; ks < 8; ++ks) qb[ks] = __builtin_bit_cast(bf16x4_t, hl < G ? w[ks] : 0ull);
     }
     uint64_t rd[12];
     if constexpr (NSUB <= 3) {
@@ -962,7 +962,6 @@ __global__ __launch_bounds__(kWave) void k_settle(StepArgs a, int32_t *slot_out,
 }
 
 hipError_t launch_settle(const StepArgs &a, int dtype, int32_t *slot_out, bool apply, hipStream_t s) {
-  if (a.lazy) return launch_settle_lazy(a, slot_out, apply, s);  // either form of a pending eviction
   const int rb = a.D * (dtype == HIKV_BF16 ? 2 : 4);
   hipLaunchKernelGGL(k_settle, dim3((unsigned)a.n_units), dim3(kWave), 0, s, a, slot_out, apply ? 1 : 0, rb);
   return hipGetLastError();
@@ -1048,12 +1047,11 @@ static hipError_t step_g(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipEv
 
 // Fill a.hp from a host copy of len[] exactly as the kernels would derive the
 // plan from the device copy.  Returns false when no host plan applies.
-// g: the launch's resident grid (0: the two-launch attention launch's).
 template <int EL, int D, int G>
-static bool host_plan_fill(StepArgs &a, const int32_t *len_hint, int g = 0) {
+static bool host_plan_fill(StepArgs &a, const int32_t *len_hint) {
   const int U = a.n_units;
   if (U > kHostPlanUnits) return false;
-  if (g <= 0) g = attend_grid<EL, D, G>(U);
+  const int g = attend_grid<EL, D, G>(U);
   if (g <= U) return false;
   long long tot = 0;
   for (int u = 0; u < U; ++u) tot += len_hint[u] + 1;
@@ -1083,26 +1081,6 @@ static bool host_plan_g(StepArgs &a, const int32_t *len_hint) {
     case 8: return host_plan_fill<EL, D, 8>(a, len_hint);
     default: return false;
   }
-}
-
-bool fused_host_plan(StepArgs &a, const int32_t *len_hint) {
-  a.hp.n = 0;
-  const int g = fused_grid(a.G);
-  bool ok = false;
-  switch (a.G) {
-    case 1: ok = host_plan_fill<2, 128, 1>(a, len_hint, g); break;
-    case 2: ok = host_plan_fill<2, 128, 2>(a, len_hint, g); break;
-    case 4: ok = host_plan_fill<2, 128, 4>(a, len_hint, g); break;
-    case 8: ok = host_plan_fill<2, 128, 8>(a, len_hint, g); break;
-    default: ok = false;
-  }
-  if (ok) {
-    const int mt = fused_max_tiles(a.G);
-    for (int u = 0; u < a.hp.n; ++u)
-      if (a.hp.base[u + 1] - a.hp.base[u] > mt) ok = false;
-  }
-  if (!ok) a.hp.n = 0;
-  return ok;
 }
 
 bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint) {

@@ -76,13 +76,9 @@ def test_decode_step_host_checks():
     assert call(_shape(), cache=H.hikv_cache(0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)) == H.HIKV_EINVAL
     assert call(_shape(), cache=H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0)) == H.HIKV_EINVAL
     assert call(_shape(), cache=H.hikv_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1004)) == H.HIKV_EINVAL
-    # pending-eviction state: 4 words per unit plus 4 per 2048-slot importance block,
-    # and for bf16 rows with D = 128 the deferred-step record (32 words and the
-    # group's G x 128 bf16 queries)
-    assert H.hikv_state_bytes(_shape()) == 4 * 2 * 2 * (8 + 32 + 64 * 4)
-    assert H.hikv_state_bytes(_shape(capacity=5000)) == 4 * 2 * 2 * (16 + 32 + 64 * 4)
-    assert H.hikv_state_bytes(_shape(kv_dtype=H.HIKV_F32)) == 4 * 2 * 2 * 8
-    assert H.hikv_state_bytes(_shape(head_dim=64)) == 4 * 2 * 2 * 8
+    # pending-eviction state: 4 words per unit plus 4 per 2048-slot importance block
+    assert H.hikv_state_bytes(_shape()) == 4 * 2 * 2 * 8
+    assert H.hikv_state_bytes(_shape(capacity=5000)) == 4 * 2 * 2 * 16
     assert H.hikv_state_bytes(_shape(head_dim=96)) == 0
     assert call(_shape(), q=None) == H.HIKV_EINVAL
     assert call(_shape(), q=C.c_void_p(0x1008)) == H.HIKV_EINVAL                    # alignment
