@@ -216,14 +216,29 @@ class DeviceCache:
             t = t.view(self.torch.int16)
         return t.to(device)
 
-    def to_numpy(self) -> dict:
-        k = self.k.cpu().numpy()
-        v = self.v.cpu().numpy()
+    def to_numpy(self, units=None, slots=None) -> dict:
+        """Host copy of the cache.  units: optional list of (b, j) pairs, each
+        becoming a batch row with one KV head; slots: copy only the first
+        `slots` slots of every unit (the rest of the capacity is left out)."""
+        torch = self.torch
+        n = self.k.shape[2] if slots is None else min(int(slots), self.k.shape[2])
+
+        def take(t):
+            if units is None:
+                return t[:, :, :n]
+            return torch.stack([t[b, j, :n] for b, j in units])[:, None]
+
+        k = take(self.k).cpu().numpy()
+        v = take(self.v).cpu().numpy()
         if self.dtype == HIKV_BF16:
             k = k.view(np.uint16)
             v = v.view(np.uint16)
-        return dict(k=k, v=v, pos=self.pos.cpu().numpy(), imp=self.imp.cpu().numpy(),
-                    len=self.len.cpu().numpy())
+        ln = self.len.cpu().numpy()
+        if units is not None:
+            ln = np.array([[ln[b, j]] for b, j in units], dtype=ln.dtype)
+        return dict(k=np.ascontiguousarray(k), v=np.ascontiguousarray(v),
+                    pos=np.ascontiguousarray(take(self.pos).cpu().numpy()),
+                    imp=np.ascontiguousarray(take(self.imp).cpu().numpy()), len=ln)
 
     def load(self, state: dict):
         """Overwrite the device state with a host state of the same shape."""

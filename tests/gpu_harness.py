@@ -5,14 +5,16 @@ back to the host), runs one step, and the two results are compared:
   * output rows (b, h): max|o - r| / max|r| <= 2e-3 (bf16 storage) or 1e-5
     (fp32 storage);
   * kept position sets per (b, KV head): equal, except positions whose oracle
-    importance lies within 1e-6 (relative) of the kept/evicted boundary;
+    importance lies within 1e-6 (relative) of the kept/evicted boundary
+    (probability sums); for Kelle's logit sums, which cross zero, within the
+    rounding-error bound of the GPU's fp32 logits instead (logit_tol);
   * surviving rows: K, V bytes identical, importance within 1e-5 relative;
   * Stage II: chosen channel sets equal; exact-softmax token sets equal
-    except near-ties of the reduced logit.  With HiKV's chunked V side the
-    kept-token counts are equal, and a q-head whose chunk selection has a
-    near-tie at its boundary (the r-th and the next probability within
-    CHUNK_TIE_RTOL of each other in the oracle) is left out of the output
-    check: either choice is a correct result.
+    except tokens whose reduced logit is within the fp32 rounding-error bound
+    of the selection threshold (reduced_tol).  With HiKV's chunked V side
+    the kept-token counts are equal, and where a chunk's r-th and next
+    reduced logit lie within that bound of each other the GPU's output must
+    equal the oracle's with that pair swapped.
 """
 
 from __future__ import annotations
@@ -29,7 +31,6 @@ from oracle import ref
 OUT_TOL = {W.F32: 1e-5, W.BF16: 2e-3}
 TIE_RTOL = 1e-6
 IMP_RTOL = 1e-5
-CHUNK_TIE_RTOL = 1e-4
 
 
 def say(*a):
@@ -76,13 +77,20 @@ class GpuRun:
         H.check(H.hikv_pending(sh, self.dev.cache, self.pol, self.ws, out), "hikv_pending")
         return out.cpu().numpy()
 
-    def state(self):
+    def state(self, units=None, room=None):
         """The cache as the method defines it after the last step: a device
-        copy of the cache settled by hikv_settle (every deferred or pending
-        eviction applied), so that the device keeps running on its own state."""
+        copy of the cache settled by hikv_settle (every pending eviction
+        applied), so that the device keeps running on its own state.
+        units: optional (b, j) pairs to copy (each a batch row of one KV head);
+        room: copy only the slots up to the longest unit plus `room` (enough
+        for the oracle to append), instead of the whole capacity."""
         c = self.dev.clone()
         H.check(H.hikv_settle(c.shape, c.cache, self.pol, self.ws), "hikv_settle")
-        return c.to_numpy()
+        slots = None
+        if room is not None:
+            beta_max = int(self.budget_np.max()) if self.budget_np is not None else int(self.kw["budget_all"])
+            slots = max(int(c.len.max().item()) + room, beta_max)   # the oracle checks budget <= capacity
+        return c.to_numpy(units=units, slots=slots)
 
     def step(self, q, k_new, v_new, new_pos, expect=H.HIKV_OK, hint_override=None):
         qt, kt, vt = H.to_device(q), H.to_device(k_new), H.to_device(v_new)
@@ -107,6 +115,46 @@ class GpuRun:
         return out, dbg
 
 
+U32 = 2.0 ** -24   # unit roundoff of fp32
+
+
+def _f64(x):
+    return W.bf16_bits_to_f32(x).astype(np.float64) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def unit_rows(pre, b, j, new_row, field="k"):
+    """The unit's L - 1 cached rows and the appended one, fp64 [L][D]."""
+    L = int(pre["len"][b, j]) + 1
+    return np.concatenate([_f64(pre[field][b, j, :L - 1]), _f64(new_row)[None]], axis=0)
+
+
+def abs_dot(q_rows, K, channels=None):
+    """sum_d |q_d k_d| per (q-head, token): [G][L], over `channels` per head if given."""
+    qa = np.abs(q_rows)
+    if channels is not None:
+        m = np.zeros_like(qa)
+        for h in range(qa.shape[0]):
+            m[h, channels[h]] = 1.0
+        qa = qa * m
+    return qa @ np.abs(K).T
+
+
+def reduced_tol(q_rows, K, channels, scale):
+    """fp32 rounding-error bound of the GPU's reduced logits (Stage II):
+    products of bf16 values are exact in fp32, and n terms summed in fp32
+    (any order) then scaled carry at most (n + 2) u sum|terms| of error."""
+    n = len(channels[0])
+    return (n + 2) * U32 * scale * abs_dot(q_rows, K, channels)
+
+
+def logit_tol(q_rows, K, channels, scale):
+    """fp32 rounding-error bound of one step's logit importance of every
+    token (Kelle: sum over the group's q-heads of scale * q.k; reduced
+    channels with Stage II): (n + 2) u scale sum|q_d k_d| per head, summed."""
+    n = K.shape[1] if channels is None else len(channels[0])
+    return ((n + 2) * U32 * scale * abs_dot(q_rows, K, channels)).sum(0)
+
+
 def row_errors(out, want):
     den = np.maximum(np.abs(want).max(-1), 1e-30)
     return np.abs(out.astype(np.float64) - want).max(-1) / den
@@ -117,8 +165,10 @@ def _positions(state, b, j):
     return state["pos"][b, j, :n]
 
 
-def check_kept(pre, post_gpu, post_ref, dbg_ref, kw, new_pos, where=""):
-    """Kept sets equal up to near-ties; surviving rows identical."""
+def check_kept(pre, post_gpu, post_ref, dbg_ref, kw, new_pos, where="", q=None, k_new=None):
+    """Kept sets equal up to near-ties; surviving rows identical.  q, k_new
+    (the step's inputs) are needed for Kelle's logit importance, whose tie
+    window is the rounding-error bound of the step's fp32 logits."""
     B, Hkv = post_ref["len"].shape
     n_swaps = 0
     logit = kw.get("accumulate", H.HIKV_ACC_ALL) == H.HIKV_ACC_LOGIT
@@ -142,28 +192,50 @@ def check_kept(pre, post_gpu, post_ref, dbg_ref, kw, new_pos, where=""):
                 prot = (pos_pre < S) | (pos_pre > new_pos[b] - Wp)
                 cand_kept = kept & ~prot
                 assert cand_kept.any(), (where, "kept sets differ with no candidate kept", b, j)
-                thr = imp_pre[cand_kept].min()
+                thr_slot = int(np.nonzero(cand_kept)[0][np.argmin(imp_pre[cand_kept])])
+                thr = imp_pre[thr_slot]
                 slot_of = {int(p): i for i, p in enumerate(pos_pre)}
-                # logit sums (Kelle) are compared on an absolute scale: they
-                # cross zero, and fp32 logits differ from fp64 by ~1e-6
-                tie_tol = (1e-5 * max(1.0, abs(thr)) if logit else TIE_RTOL * abs(thr) + 1e-30)
+                if logit:
+                    # Kelle's sums cross zero: the window is the bound on this
+                    # step's fp32 logits plus the rounding of the stored sums
+                    assert q is not None and k_new is not None, (where, "logit tie rule needs q and k_new")
+                    G = q.shape[1] // Hkv
+                    qf = _f64(q[b, j * G:(j + 1) * G])
+                    scale = kw.get("scale", 0.0) or 1.0 / np.sqrt(qf.shape[1])
+                    ch = dbg_ref["sel_channels"][b, j * G:(j + 1) * G] if kw.get("stage2_channels", 0) else None
+                    tol = logit_tol(qf, unit_rows(pre, b, j, k_new[b, j]), ch, scale) + 2 * U32 * np.abs(imp_pre)
                 for p in diff:
                     s = slot_of[int(p)]
                     assert not prot[s], (where, "protected token differs", b, j, p)
-                    assert abs(imp_pre[s] - thr) <= tie_tol, \
-                        (where, "kept sets differ beyond a near-tie", b, j, p, imp_pre[s], thr)
+                    win = (tol[s] + tol[thr_slot]) if logit else TIE_RTOL * abs(thr) + 1e-30
+                    assert abs(imp_pre[s] - thr) <= win, \
+                        (where, "kept sets differ beyond a near-tie", b, j, p, imp_pre[s], thr, win)
                 n_swaps += len(diff) // 2
-            g_rows = ref.live_rows(post_gpu, b, j)
-            r_rows = ref.live_rows(post_ref, b, j)
-            for p in gs & rs:
-                gk, gv, gi = g_rows[p]
-                rk, rv, ri = r_rows[p]
-                assert gk == rk and gv == rv, (where, "row bytes differ", b, j, p)
-                assert abs(gi - ri) <= IMP_RTOL * max(abs(ri), imp_floor), (where, "importance", b, j, p, gi, ri)
+            # the rows both keep: K, V bytes identical, importance close
+            common = np.array(sorted(gs & rs), dtype=np.int64)
+            gi = _slots_of(post_gpu, b, j, common)
+            ri = _slots_of(post_ref, b, j, common)
+            assert np.array_equal(post_gpu["k"][b, j][gi], post_ref["k"][b, j][ri]), (where, "K rows differ", b, j)
+            assert np.array_equal(post_gpu["v"][b, j][gi], post_ref["v"][b, j][ri]), (where, "V rows differ", b, j)
+            gimp = post_gpu["imp"][b, j][gi].astype(np.float64)
+            rimp = post_ref["imp"][b, j][ri].astype(np.float64)
+            bad = np.abs(gimp - rimp) > IMP_RTOL * np.maximum(np.abs(rimp), imp_floor)
+            assert not bad.any(), (where, "importance", b, j, common[bad][:4], gimp[bad][:4], rimp[bad][:4])
     return n_swaps
 
 
-def check_stage2(dbg_gpu, dbg_ref, pre, new_pos, Hq, kT, where=""):
+def _slots_of(state, b, j, positions):
+    """Slots holding the given positions in unit (b, j) (positions distinct)."""
+    n = int(state["len"][b, j])
+    pos = state["pos"][b, j, :n].astype(np.int64)
+    order = np.argsort(pos, kind="stable")
+    idx = np.searchsorted(pos[order], positions)
+    return order[idx]
+
+
+def check_stage2(dbg_gpu, dbg_ref, pre, new_pos, Hq, kT, where="", q=None, k_new=None, scale=0.0):
+    """Stage II's chosen channel sets equal; token sets equal except tokens
+    within the fp32 rounding-error bound of the selection threshold."""
     B = dbg_ref["sel_count"].shape[0]
     Hkv = pre["len"].shape[1]
     G = Hq // Hkv
@@ -181,22 +253,31 @@ def check_stage2(dbg_gpu, dbg_ref, pre, new_pos, Hq, kT, where=""):
                 L = int(pre["len"][b, j]) + 1
                 pos_pre = np.append(pre["pos"][b, j, :L - 1], new_pos[b])
                 s = dbg_ref["approx_logits"][b, h, :L]
-                thr = np.sort(s)[::-1][cnt - 1]
+                thr_slot = int(np.argsort(-s, kind="stable")[cnt - 1])
+                qf = _f64(q[b, h:h + 1])
+                sc = scale or 1.0 / np.sqrt(qf.shape[1])
+                tol = reduced_tol(qf, unit_rows(pre, b, j, k_new[b, j]),
+                                  dbg_ref["sel_channels"][b, h:h + 1], sc)[0]
                 slot_of = {int(p): i for i, p in enumerate(pos_pre)}
                 for p in gt ^ rt:
-                    d = abs(s[slot_of[int(p)]] - thr)
-                    assert d <= 1e-4 * (1.0 + abs(thr)), (where, "token sets differ", b, h, p, d)
+                    i = slot_of[int(p)]
+                    d = abs(s[i] - s[thr_slot])
+                    assert d <= tol[i] + tol[thr_slot], (where, "token sets differ", b, h, p, d, tol[i])
                 n_tie += 1
     return n_tie
 
 
-def chunk_near_ties(dbg_ref, pre, new_pos, Hq, r):
-    """[B][Hq] True where some chunk of D positions has its r-th and next
-    largest probability within CHUNK_TIE_RTOL (oracle's reduced logits)."""
+def chunk_alternatives(dbg_ref, pre, new_pos, q, k_new, v_new, Hq, r, want, scale=0.0):
+    """HiKV's chunked V side: for every (b, h), the oracle's output and the
+    outputs in which near-tie chunks (r-th and next reduced logit within the
+    rounding-error bound) keep the other token of the pair.  Returns
+    alts[b][h] = list of output rows (the first the oracle's) and the count of
+    heads whose tie window holds more than one pair (accepted as is)."""
     B, Hkv = pre["len"].shape
     D = pre["k"].shape[-1]
     G = Hq // Hkv
-    tie = np.zeros((B, Hq), dtype=bool)
+    alts = [[[want[b, h].astype(np.float64)] for h in range(Hq)] for b in range(B)]
+    ambiguous = 0
     for b in range(B):
         for h in range(Hq):
             j = h // G
@@ -205,12 +286,49 @@ def chunk_near_ties(dbg_ref, pre, new_pos, Hq, r):
             s = dbg_ref["approx_logits"][b, h, :L]
             p = np.exp(s - s.max())
             p /= p.sum()
+            qf = _f64(q[b, h:h + 1])
+            sc = scale or 1.0 / np.sqrt(D)
+            # the GPU ranks a chunk by probability: exp2 of its fp32 logit adds
+            # about 2 ulp of relative error, i.e. 4 u / scale of logit
+            tol = reduced_tol(qf, unit_rows(pre, b, j, k_new[b, j]), dbg_ref["sel_channels"][b, h:h + 1], sc)[0]
+            tol = tol + 4 * U32 / sc
+            V = None
+            deltas = []
             order = np.argsort(pos, kind="stable")
             for c0 in range(0, L, D):
-                pc = np.sort(p[order[c0:c0 + D]])[::-1]
-                if len(pc) > r and pc[r - 1] - pc[r] <= CHUNK_TIE_RTOL * pc[r - 1]:
-                    tie[b, h] = True
-    return tie
+                idx = order[c0:c0 + D]
+                if len(idx) <= r:
+                    continue
+                rk = idx[np.argsort(-s[idx], kind="stable")]
+                a_, b_ = rk[r - 1], rk[r]
+                if abs(s[a_] - s[b_]) > tol[a_] + tol[b_]:
+                    continue
+                if len(rk) > r + 1 and abs(s[rk[r + 1]] - s[a_]) <= tol[a_] + tol[rk[r + 1]]:
+                    ambiguous += 1
+                    alts[b][h] = None
+                    break
+                if V is None:
+                    V = unit_rows(pre, b, j, v_new[b, j], field="v")
+                deltas.append(p[b_] * V[b_] - p[a_] * V[a_])
+            if alts[b][h] is None or not deltas:
+                continue
+            base = alts[b][h][0]
+            for mask in range(1, 1 << min(len(deltas), 4)):
+                alts[b][h].append(base + sum(deltas[i] for i in range(len(deltas)) if mask >> i & 1))
+    return alts, ambiguous
+
+
+def chunk_row_errors(out, alts):
+    """Per (b, h): the smallest row error against any of the valid outputs
+    (0 where the tie window was ambiguous)."""
+    B, Hq = out.shape[:2]
+    e = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            if alts[b][h] is None:
+                continue
+            e[b, h] = min(float(row_errors(out[b:b + 1, h:h + 1], a[None, None])[0, 0]) for a in alts[b][h])
+    return e
 
 
 def lockstep(run: GpuRun, data, steps, *, tag="", start_state=None):
@@ -228,16 +346,19 @@ def lockstep(run: GpuRun, data, steps, *, tag="", start_state=None):
                                            data["v_new"][t], data["new_pos"][t], **run.kw)
         assert code == 0
         e = row_errors(out, want)
+        q, kn, vn, npos = data["q"][t], data["k_new"][t], data["v_new"][t], data["new_pos"][t]
         if run.r > 0 and run.s2v == H.HIKV_S2V_CHUNK:
             assert np.array_equal(dbg["sel_count"], dref["sel_count"]), (tag, t)
             assert np.array_equal(dbg["sel_channels"], dref["sel_channels"]), (tag, t)
-            tie = chunk_near_ties(dref, pre, data["new_pos"][t], run.Hq, run.r)
-            e = np.where(tie, 0.0, e)
-            say(f"[gpu] {tag} step {t}: {int(tie.sum())} q-heads with a chunk near-tie left out")
+            alts, amb = chunk_alternatives(dref, pre, npos, q, kn, vn, run.Hq, run.r, want, run.kw["scale"])
+            e = chunk_row_errors(out, alts)
+            n_alt = sum(len(a) > 1 for row in alts for a in row if a is not None)
+            say(f"[gpu] {tag} step {t}: {n_alt} q-heads matched with a near-tie chunk swapped allowed, {amb} ambiguous")
         elif run.r > 0:
-            check_stage2(dbg, dref, pre, data["new_pos"][t], run.Hq, run.kT, where=f"{tag} step {t}")
+            check_stage2(dbg, dref, pre, npos, run.Hq, run.kT, where=f"{tag} step {t}", q=q, k_new=kn,
+                         scale=run.kw["scale"])
         worst = max(worst, float(e.max()))
         assert e.max() <= OUT_TOL[dtype], (tag, t, float(e.max()), np.unravel_index(e.argmax(), e.shape))
         assert np.array_equal(post["len"], st["len"]), (tag, t)
-        swaps += check_kept(pre, post, st, dref, run.kw, data["new_pos"][t], where=f"{tag} step {t}")
+        swaps += check_kept(pre, post, st, dref, run.kw, npos, where=f"{tag} step {t}", q=q, k_new=kn)
     return worst, swaps
