@@ -6,9 +6,17 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "hikv_launch.h"
 
 using namespace hikv;
+
+// The allocation-free entry point's scratch (hikv_decode_step_static): one
+// array per GPU the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address: each device's address is looked
+// up once, with that device current, and kept (scratch_of_current_device).
+static __device__ __attribute__((aligned(256))) char scratch[HIKV_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -111,19 +119,19 @@ extern "C" size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_polic
   return sizes_for(shape, policy).total;
 }
 
-extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache,
-                                const hikv_policy *policy, const void *q, const void *k_new,
-                                const void *v_new, const int32_t *new_pos, float *out, void *ws,
-                                size_t ws_bytes, const hikv_debug *debug, void *stream) {
+namespace {
+
+// Host checks shared by the decode entry points (everything but the workspace).
+int check_decode_args(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                      const void *q, const void *k_new, const void *v_new, const int32_t *new_pos,
+                      const float *out, const hikv_debug *debug) {
   int st = check_shape(shape);
   if (st != HIKV_OK) return st;
   if ((st = check_policy(shape, policy)) != HIKV_OK) return st;
   if (shape->batch == 0) return HIKV_OK;
   if ((st = check_cache(cache)) != HIKV_OK) return st;
-  if (!q || !k_new || !v_new || !new_pos || !out || !ws) return HIKV_EINVAL;
-  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ws)) return HIKV_EINVAL;
-  const WsSizes sz = sizes_for(shape, policy);
-  if (ws_bytes < sz.total) return HIKV_EINVAL;
+  if (!q || !k_new || !v_new || !new_pos || !out) return HIKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return HIKV_EINVAL;
   if (policy->len_hint) {
     const int U = shape->batch * shape->n_kv_heads;
     for (int u = 0; u < U; ++u)
@@ -131,9 +139,21 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   }
   const int path = debug ? debug->stage1_path : HIKV_PATH_AUTO;
   if (path != HIKV_PATH_AUTO && path != HIKV_PATH_MULTI_LAUNCH) return HIKV_EINVAL;
-  if ((st = arch_ok()) != HIKV_OK) return st;
+  return HIKV_OK;
+}
 
-  StepArgs a = make_args(shape, cache, policy, ws_carve(ws, sz));
+__global__ void k_zero_words(int32_t *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// The launch sequence of one decode step on a carved workspace.  clear_tickets:
+// zero the per-unit counters first (a workspace whose previous contents are
+// not this shape's own, before a path that counts tiles).
+int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy, const void *q,
+               const void *k_new, const void *v_new, const int32_t *new_pos, float *out, const Ws &w,
+               const hikv_debug *debug, void *stream, bool clear_tickets) {
+  const int path = debug ? debug->stage1_path : HIKV_PATH_AUTO;
+  StepArgs a = make_args(shape, cache, policy, w);
   a.q = q;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -152,6 +172,11 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
     ev1 = static_cast<hipEvent_t>(debug->attend_stop);
   }
   hipError_t e;
+  if (clear_tickets && (a.r > 0 || path == HIKV_PATH_MULTI_LAUNCH)) {
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<int32_t *>(a.ws.ticket), a.n_units);
+    if ((e = hipGetLastError()) != hipSuccess) return dev_err(e);
+  }
   if (a.r == 0) {
     if (path == HIKV_PATH_AUTO) {
       if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
@@ -197,6 +222,53 @@ extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache
   if ((e = launch_accumulate(a, dt, s)) != hipSuccess) return dev_err(e);
   if (!a.no_bulk && (e = launch_bulk_evict(a, dt, new_pos, true, s)) != hipSuccess) return dev_err(e);
   return HIKV_OK;
+}
+
+std::atomic<void *> scratch_ptr[64];  // each device's address of `scratch` (below)
+
+int scratch_of_current_device(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HIKV_EDEVICE;
+  if (dev < 0 || dev >= 64) return HIKV_EUNSUPPORTED;
+  void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HIKV_EDEVICE;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return HIKV_OK;
+}
+
+}  // namespace
+
+extern "C" int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache,
+                                const hikv_policy *policy, const void *q, const void *k_new,
+                                const void *v_new, const int32_t *new_pos, float *out, void *ws,
+                                size_t ws_bytes, const hikv_debug *debug, void *stream) {
+  int st = check_decode_args(shape, cache, policy, q, k_new, v_new, new_pos, out, debug);
+  if (st != HIKV_OK || shape->batch == 0) return st;
+  if (!ws || !aligned16(ws)) return HIKV_EINVAL;
+  const WsSizes sz = sizes_for(shape, policy);
+  if (ws_bytes < sz.total) return HIKV_EINVAL;
+  if ((st = arch_ok()) != HIKV_OK) return st;
+  return run_decode(shape, cache, policy, q, k_new, v_new, new_pos, out, ws_carve(ws, sz), debug, stream, false);
+}
+
+extern "C" int hikv_decode_step_static(const hikv_shape *shape, const hikv_cache *cache,
+                                       const hikv_policy *policy, const void *q, const void *k_new,
+                                       const void *v_new, const int32_t *new_pos, float *out,
+                                       int32_t *status, const hikv_debug *debug, void *stream) {
+  int st = check_decode_args(shape, cache, policy, q, k_new, v_new, new_pos, out, debug);
+  if (st != HIKV_OK || shape->batch == 0) return st;
+  if (!status || (reinterpret_cast<uintptr_t>(status) & 3u)) return HIKV_EINVAL;
+  const WsSizes sz = sizes_for(shape, policy);
+  if (sz.total > (size_t)HIKV_STATIC_SCRATCH_BYTES) return HIKV_EINVAL;
+  if ((st = arch_ok()) != HIKV_OK) return st;
+  void *base = nullptr;
+  if ((st = scratch_of_current_device(&base)) != HIKV_OK) return st;
+  Ws w = ws_carve(base, sz);
+  w.status = status;  // device-side errors go to the caller's word
+  return run_decode(shape, cache, policy, q, k_new, v_new, new_pos, out, w, debug, stream, true);
 }
 
 extern "C" int hikv_evict(const hikv_shape *shape, const hikv_cache *cache,

@@ -22,8 +22,10 @@ HIKV_ACC_ALL, HIKV_ACC_RECENT, HIKV_ACC_LOGIT = 0, 1, 2
 HIKV_S2V_TOPK, HIKV_S2V_CHUNK = 0, 1
 HIKV_PATH_AUTO, HIKV_PATH_MULTI_LAUNCH = 0, 1
 HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
+HIKV_STATIC_SCRATCH_BYTES = 64 << 20
 
-EXPORTS = ("hikv_state_bytes", "hikv_workspace_bytes", "hikv_decode_step", "hikv_evict", "hikv_settle", "hikv_pending",
+EXPORTS = ("hikv_state_bytes", "hikv_workspace_bytes", "hikv_decode_step", "hikv_decode_step_static", "hikv_evict",
+           "hikv_settle", "hikv_pending",
            "hikv_prefill_workspace_bytes", "hikv_prefill_scores", "hikv_device_status", "hikv_status_string")
 
 
@@ -73,6 +75,9 @@ def lib():
         L.hikv_decode_step.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, vp, vp,
                                        vp, vp, sz, P(hikv_debug), vp]
         L.hikv_decode_step.restype = C.c_int
+        L.hikv_decode_step_static.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, vp, vp,
+                                              vp, vp, P(hikv_debug), vp]
+        L.hikv_decode_step_static.restype = C.c_int
         L.hikv_evict.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, vp, sz, vp]
         L.hikv_evict.restype = C.c_int
         L.hikv_settle.argtypes = [P(hikv_shape), P(hikv_cache), P(hikv_policy), vp, sz, vp]
@@ -144,6 +149,14 @@ def hikv_decode_step(shape, cache, policy, q, k_new, v_new, new_pos, out, ws, de
     return lib().hikv_decode_step(C.byref(shape), C.byref(cache), C.byref(policy), _p(q), _p(k_new),
                                   _p(v_new), _p(new_pos), _p(out), _p(ws), ws.numel() * ws.element_size(),
                                   C.byref(debug) if debug is not None else None, _stream(stream))
+
+
+def hikv_decode_step_static(shape, cache, policy, q, k_new, v_new, new_pos, out, status, debug=None,
+                            stream=None) -> int:
+    """hikv_decode_step on the library's static scratch; status: a device int32 tensor (one word)."""
+    return lib().hikv_decode_step_static(C.byref(shape), C.byref(cache), C.byref(policy), _p(q), _p(k_new),
+                                         _p(v_new), _p(new_pos), _p(out), _p(status),
+                                         C.byref(debug) if debug is not None else None, _stream(stream))
 
 
 def hikv_evict(shape, cache, policy, newest_pos, ws, stream=None) -> int:

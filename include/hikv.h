@@ -213,6 +213,27 @@ int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache, const hik
                      const int32_t *new_pos, float *out, void *ws, size_t ws_bytes,
                      const hikv_debug *debug, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it): hikv_decode_step
+ * with the workspace taken from a static array the library holds on each GPU
+ * (HIKV_STATIC_SCRATCH_BYTES, allocated with the library's code on that GPU
+ * and held until the process ends) instead of a caller's buffer.  Nothing is
+ * allocated or freed.  The call is rejected with HIKV_EINVAL when
+ * hikv_workspace_bytes(shape, policy) exceeds HIKV_STATIC_SCRATCH_BYTES.
+ * Device-side errors are recorded in *status (a caller-owned device int32,
+ * sticky like the workspace's status word: zero it before the first call and
+ * after reading a nonzero value).  Every call on one GPU uses that GPU's one
+ * array: calls that overlap in time on one GPU (different streams, or host
+ * threads enqueueing concurrently) race and must not be made; calls ordered
+ * on one stream are safe, whatever their shapes.  The scratch keeps the last
+ * call's contents; the call clears what must start at zero itself.  Results
+ * are those of hikv_decode_step on the same inputs. */
+#define HIKV_STATIC_SCRATCH_BYTES (64u << 20)
+int hikv_decode_step_static(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
+                            const void *q, const void *k_new, const void *v_new,
+                            const int32_t *new_pos, float *out, int32_t *status,
+                            const hikv_debug *debug, void *stream);
+
 /* Compress every unit over its budget to exactly its budget with step 4 of
  * hikv_decode_step, using the current importance; newest_pos[b] anchors the
  * recent window ([Blog] Sec. 3 H2O; [Kelle] Sec. 4.1, prefill eviction).

@@ -109,6 +109,13 @@ def test_decode_step_host_checks():
     dbg = H.hikv_debug(None, None, None, None, None, 5)
     assert L.hikv_decode_step(C.byref(_shape()), C.byref(cache), C.byref(pol), fake, fake, fake, fake,
                               fake, fake, 1 << 30, C.byref(dbg), None) == H.HIKV_EINVAL
+    # the allocation-free variant: no status word, or a workspace beyond its static scratch
+    assert L.hikv_decode_step_static(C.byref(_shape()), C.byref(cache), C.byref(pol), fake, fake, fake, fake,
+                                     fake, None, None, None) == H.HIKV_EINVAL
+    big = _shape(batch=64, n_kv_heads=8, n_q_heads=64, capacity=200000)
+    assert H.hikv_workspace_bytes(big, pol) > H.HIKV_STATIC_SCRATCH_BYTES
+    assert L.hikv_decode_step_static(C.byref(big), C.byref(cache), C.byref(pol), fake, fake, fake, fake,
+                                     fake, fake, None, None) == H.HIKV_EINVAL
     assert H.status_string(H.HIKV_ECAPACITY) == "cache capacity exceeded"
     # settle / pending: host checks only (no device work is enqueued on error)
     assert L.hikv_settle(C.byref(_shape()), C.byref(cache), C.byref(pol), None, 1 << 30, None) == H.HIKV_EINVAL
