@@ -22,7 +22,7 @@ HIKV_ACC_ALL, HIKV_ACC_RECENT, HIKV_ACC_LOGIT = 0, 1, 2
 HIKV_S2V_TOPK, HIKV_S2V_CHUNK = 0, 1
 HIKV_PATH_AUTO, HIKV_PATH_MULTI_LAUNCH = 0, 1
 HIKV_OK, HIKV_EINVAL, HIKV_EUNSUPPORTED, HIKV_EDEVICE, HIKV_ECAPACITY, HIKV_EBUDGET = 0, -1, -2, -3, -4, -5
-HIKV_STATIC_SCRATCH_BYTES = 64 << 20
+HIKV_STATIC_SCRATCH_BYTES = 128 << 20
 
 EXPORTS = ("hikv_state_bytes", "hikv_workspace_bytes", "hikv_decode_step", "hikv_decode_step_static", "hikv_evict",
            "hikv_settle", "hikv_pending",

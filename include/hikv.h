@@ -139,10 +139,11 @@ typedef struct hikv_policy {
                               order, are cut into chunks of D tokens (the last one shorter);
                               each chunk keeps its r largest entries (ties: lower position) and
                               the output is the sum of those entries times their V rows, not
-                              renormalised (stage2_tokens is not used).  The chunk order costs
-                              O(len^2) comparisons per unit and step, meant for the budgets the
-                              pages use (a few thousand tokens).  Any other value is
-                              HIKV_EINVAL. */
+                              renormalised (stage2_tokens is not used).  The position order is
+                              found once per unit and step with a bitmap over windows of 2^18
+                              positions: len * ceil(position span / 2^18) work per unit (one
+                              pass while the live positions span at most 262144).  Any other
+                              value is HIKV_EINVAL. */
 } hikv_policy;
 
 /* Optional outputs of hikv_decode_step for tests, inspection and profiling;
@@ -228,7 +229,7 @@ int hikv_decode_step(const hikv_shape *shape, const hikv_cache *cache, const hik
  * on one stream are safe, whatever their shapes.  The scratch keeps the last
  * call's contents; the call clears what must start at zero itself.  Results
  * are those of hikv_decode_step on the same inputs. */
-#define HIKV_STATIC_SCRATCH_BYTES (64u << 20)
+#define HIKV_STATIC_SCRATCH_BYTES (128u << 20)
 int hikv_decode_step_static(const hikv_shape *shape, const hikv_cache *cache, const hikv_policy *policy,
                             const void *q, const void *k_new, const void *v_new,
                             const int32_t *new_pos, float *out, int32_t *status,
