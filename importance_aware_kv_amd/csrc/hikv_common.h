@@ -58,9 +58,10 @@ struct Ws {
   int32_t *nmoves;      // [n_units] bulk eviction: rows the move launch relocates (0: none)
   float *chunk_acc;     // [n_units][ceil(cap/D)][G][D] Stage II chunked V side: each chunk's P.V
   int32_t *chunk_cnt;   // [n_units][ceil(cap/D)][G] tokens each chunk kept per q-head
+  int32_t *order;       // [n_units][cap] Stage II chunked V side: the live slots in position order
 };
 
-constexpr int kWsParts = 21;
+constexpr int kWsParts = 22;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -95,6 +96,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chu
       sizeof(int32_t) * U,             // nmoves
       sizeof(float) * U * NC * G * D,  // chunk_acc
       sizeof(int32_t) * U * NC * G,    // chunk_cnt
+      chunks ? sizeof(int32_t) * U * cap : 0,  // order
   };
   WsSizes w;
   size_t o = 0;
@@ -130,6 +132,7 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.nmoves = reinterpret_cast<int32_t *>(b + s.off[18]);
   w.chunk_acc = reinterpret_cast<float *>(b + s.off[19]);
   w.chunk_cnt = reinterpret_cast<int32_t *>(b + s.off[20]);
+  w.order = reinterpret_cast<int32_t *>(b + s.off[21]);
   return w;
 }
 

@@ -306,17 +306,19 @@ __device__ __forceinline__ void stage2_exact(const StepArgs &a) {
 // lower position), and the output sums those entries times their V rows with
 // no renormalisation.
 //
-// One launch, one workgroup per (chunk, unit):
-//  1. the position order: positions are distinct, so a token's rank is the
-//     number of live positions below its own.  The unit's positions are set
-//     as bits of an LDS bitmap over [min, max] and per-word popcount
-//     prefixes are scanned; rank = prefix of its word + popcount of the
-//     word's lower bits.  Each workgroup ranks the whole unit and keeps the
-//     D tokens of its own chunk, with their logits (loaded in the same pass
-//     as the positions).  Positions spanning more than the bitmap covers are
-//     ranked by counting (every token against every other), much slower.
-//     With repeated positions ranks collide: results are then undefined, and
-//     every slot taken from the chunk is clamped, so memory stays in bounds.
+// Two launches:
+//  k_pos_rank, one workgroup per unit: the position order.  Positions are
+//  distinct, so a token's rank is the number of live positions below its
+//  own: the positions are set as bits of an LDS bitmap over a window of
+//  kRankBits positions, the per-word popcounts are scanned, and rank =
+//  tokens in earlier windows + prefix of its word + popcount of the word's
+//  lower bits; the slot is written at its rank.  A span of positions wider
+//  than one window takes one pass over the unit's positions per window, so
+//  the cost is len * ceil(span / kRankBits) (one pass for spans up to 262144
+//  positions).  With repeated positions ranks collide: results are then
+//  undefined, and every slot read back is clamped, so memory stays in bounds.
+//  k_chunk_pv, one workgroup per (chunk, unit):
+//  1. the chunk's D slots are read from the order, with their logits;
 //  2. wave w selects for q-heads w, w + 4: lane l holds the chunk's entries l
 //     and l + 64; the r-th largest probability is found one bit at a time by
 //     ballot counts (the IEEE bits of a non-negative float order like its
@@ -326,7 +328,109 @@ __device__ __forceinline__ void stage2_exact(const StepArgs &a) {
 //  4. the partials go out; the accumulation launch that follows adds each
 //     unit's chunks up in chunk order (results repeat bit for bit).
 // ---------------------------------------------------------------------------
-constexpr int kChunkBits = 1 << 17;  // position span the rank bitmap covers (16 KB)
+constexpr int kRankBits = 1 << 18;  // positions one bitmap window covers (32 KB)
+constexpr int kRankThreads = 1024;
+
+__global__ __launch_bounds__(kRankThreads) void k_pos_rank(StepArgs a) {
+  constexpr int NW = kRankBits / 32, WPT = NW / kRankThreads, KR = 8, NWV = kRankThreads / kWave;
+  __shared__ uint32_t bits[NW];
+  __shared__ int wpre[NW];
+  __shared__ int s_lo[NWV], s_hi[NWV], s_wsum[NWV];
+  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!unit_has_tiles(a, u)) return;
+  const int L = a.len[u] + 1;  // the new token sits in slot L - 1
+  const int32_t *pos = a.pos + (size_t)u * a.cap;
+  int32_t *order = a.ws.order + (size_t)u * a.cap;
+  // The first KR * kRankThreads positions stay in registers.
+  int ps[KR];
+  int lo = INT_MAX, hi = INT_MIN;
+#pragma unroll
+  for (int i = 0; i < KR; ++i) {
+    const int n = tid + kRankThreads * i;
+    ps[i] = pos[min(n, L - 1)];
+    if (n < L) lo = min(lo, ps[i]), hi = max(hi, ps[i]);
+  }
+  for (int n = tid + kRankThreads * KR; n < L; n += kRankThreads) {
+    const int p = pos[n];
+    lo = min(lo, p), hi = max(hi, p);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off));
+    hi = max(hi, __shfl_xor(hi, off));
+  }
+  if (lane == 0) s_lo[wave] = lo, s_hi[wave] = hi;
+  __syncthreads();
+  lo = s_lo[0], hi = s_hi[0];
+  for (int w = 1; w < NWV; ++w) lo = min(lo, s_lo[w]), hi = max(hi, s_hi[w]);
+  int done = 0;  // tokens in the windows before this one
+  for (int64_t w0 = lo; w0 <= (int64_t)hi; w0 += kRankBits) {
+    const int64_t nw64 = ((int64_t)hi - w0 + 32) / 32;
+    const int nw = (int)(nw64 < NW ? nw64 : NW);
+    for (int w = tid; w < nw; w += kRankThreads) bits[w] = 0u;
+    __syncthreads();
+    auto in_win = [&](int p) { return (int64_t)p >= w0 && (int64_t)p < w0 + kRankBits; };
+#pragma unroll
+    for (int i = 0; i < KR; ++i)
+      if (tid + kRankThreads * i < L && in_win(ps[i])) {
+        const int d = (int)(ps[i] - w0);
+        atomicOr(&bits[d >> 5], 1u << (d & 31));
+      }
+    for (int n = tid + kRankThreads * KR; n < L; n += kRankThreads) {
+      const int p = pos[n];
+      if (in_win(p)) {
+        const int d = (int)(p - w0);
+        atomicOr(&bits[d >> 5], 1u << (d & 31));
+      }
+    }
+    __syncthreads();
+    // exclusive prefix of the popcounts per word: WPT words per thread, a
+    // wave scan of the thread sums, then the waves
+    int cnt[WPT], ts = 0;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int w = tid * WPT + k;
+      cnt[k] = w < nw ? __popc(bits[w]) : 0;
+      ts += cnt[k];
+    }
+    int incl = ts;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int base = done + incl - ts, total = 0;
+    for (int w = 0; w < NWV; ++w) {
+      if (w < wave) base += s_wsum[w];
+      total += s_wsum[w];
+    }
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int w = tid * WPT + k;
+      if (w < nw) wpre[w] = base;
+      base += cnt[k];
+    }
+    __syncthreads();
+    auto rank_of = [&](int p) -> int {  // clamped: repeated positions stay in bounds
+      const int d = (int)(p - w0);
+      const int rk = wpre[d >> 5] + __popc(bits[d >> 5] & ((1u << (d & 31)) - 1u));
+      return rk < L - 1 ? rk : L - 1;
+    };
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int n = tid + kRankThreads * i;
+      if (n < L && in_win(ps[i])) order[rank_of(ps[i])] = n;
+    }
+    for (int n = tid + kRankThreads * KR; n < L; n += kRankThreads) {
+      const int p = pos[n];
+      if (in_win(p)) order[rank_of(p)] = n;
+    }
+    done += total;
+    __syncthreads();  // the bitmap is rebuilt for the next window
+  }
+}
 
 template <int EL, int D, int G>
 __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
@@ -336,8 +440,6 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
   constexpr int MAXIT = D / RG;    // rows per lane group, at most
   constexpr int RB = D * EL;
   constexpr int NPL = D / 64;      // chunk entries per lane in the selection
-  constexpr int NW = kChunkBits / 32, WPT = NW / 256;
-  constexpr int KR = G <= 4 ? 8 : 4;  // tokens per thread whose position and logits stay in registers
   const int c = blockIdx.x, u = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = u / a.Hkv, j = u - b * a.Hkv;
   float *outp = a.out + ((size_t)b * a.Hq + (size_t)j * G) * D;  // the group's rows are adjacent
@@ -354,24 +456,12 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
   const int m = min(D, L - c0);
   const int keep = min(a.r, m);
   const size_t NC = (size_t)((a.cap + D - 1) / D);
-  __shared__ uint32_t bits[NW];
-  __shared__ int wpre[NW];
   __shared__ int s_slot[D];
   __shared__ float s_p[G][D];  // the chunk's logits, then the kept probabilities
   __shared__ int s_list[D];
   __shared__ int s_nlist;
   __shared__ float s_red[4][G * D];
-  __shared__ int s_lo[4], s_hi[4], s_wsum[4];
-  const int32_t *pos = a.pos + (size_t)u * a.cap;
   const float *lg = a.ws.logits + (size_t)u * a.cap * G;
-  // With repeated positions a rank can be missed: such an entry keeps slot 0
-  // and a logit of -inf (probability 0).
-  for (int t = tid; t < D; t += 256) {
-    s_slot[t] = 0;
-#pragma unroll
-    for (int g = 0; g < G; ++g) s_p[g][t] = -INFINITY;
-  }
-
   // The unit statistics of this wave's q-heads (w, w + 4), loaded now so
   // that they arrive with the positions.
   float Mw[2] = {0.f, 0.f}, ILw[2] = {0.f, 0.f};
@@ -385,113 +475,13 @@ __global__ __launch_bounds__(256) void k_chunk_pv(StepArgs a) {
     }
   }
 
-  // 1. Ranks.  The first KR * 256 tokens keep position and logits in
-  // registers; later ones (long units) are read again.
-  int ps[KR];
-  float lv[KR][G];
-  int lo = INT_MAX, hi = INT_MIN;
+  // 1. The chunk's slots in position order, and their logits.
+  const int32_t *order = a.ws.order + (size_t)u * a.cap + c0;
+  for (int t = tid; t < m; t += 256) {
+    const int n = min(max(order[t], 0), L - 1);
+    s_slot[t] = n;
 #pragma unroll
-  for (int i = 0; i < KR; ++i) {
-    const int n = tid + 256 * i;
-    const int nn = min(n, L - 1);
-    ps[i] = pos[nn];
-#pragma unroll
-    for (int g = 0; g < G; ++g) lv[i][g] = lg[(size_t)nn * G + g];
-    if (n < L) lo = min(lo, ps[i]), hi = max(hi, ps[i]);
-  }
-  for (int n = tid + 256 * KR; n < L; n += 256) {
-    const int p = pos[n];
-    lo = min(lo, p), hi = max(hi, p);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, __shfl_xor(lo, off));
-    hi = max(hi, __shfl_xor(hi, off));
-  }
-  if (lane == 0) s_lo[wave] = lo, s_hi[wave] = hi;
-  __syncthreads();
-  lo = min(min(s_lo[0], s_lo[1]), min(s_lo[2], s_lo[3]));
-  hi = max(max(s_hi[0], s_hi[1]), max(s_hi[2], s_hi[3]));
-  const bool dense = (int64_t)hi - lo + 1 <= kChunkBits;
-  auto place = [&](int n, int rank, const float *l) {
-    const int t = rank - c0;
-    if (t >= 0 && t < m) {
-      s_slot[t] = n;
-#pragma unroll
-      for (int g = 0; g < G; ++g) s_p[g][t] = l[g];
-    }
-  };
-  if (dense) {
-    const int nw = (int)(((int64_t)hi - lo + 32) / 32);
-    for (int w = tid; w < nw; w += 256) bits[w] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KR; ++i)
-      if (tid + 256 * i < L) atomicOr(&bits[(ps[i] - lo) >> 5], 1u << ((ps[i] - lo) & 31));
-    for (int n = tid + 256 * KR; n < L; n += 256) {
-      const int d = pos[n] - lo;
-      atomicOr(&bits[d >> 5], 1u << (d & 31));
-    }
-    __syncthreads();
-    // exclusive prefix of the popcounts per word: WPT words per thread, a
-    // wave scan of the thread sums, then the four waves
-    int cnt[WPT], ts = 0;
-#pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-      const int w = tid * WPT + k;
-      cnt[k] = w < nw ? __popc(bits[w]) : 0;
-      ts += cnt[k];
-    }
-    int incl = ts;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
-    int base = incl - ts;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-#pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-      const int w = tid * WPT + k;
-      if (w < nw) wpre[w] = base;
-      base += cnt[k];
-    }
-    __syncthreads();
-    auto rank_of = [&](int p) {
-      const int d = p - lo;
-      return wpre[d >> 5] + __popc(bits[d >> 5] & ((1u << (d & 31)) - 1u));
-    };
-#pragma unroll
-    for (int i = 0; i < KR; ++i)
-      if (tid + 256 * i < L) place(tid + 256 * i, rank_of(ps[i]), lv[i]);
-    for (int n = tid + 256 * KR; n < L; n += 256) {
-      float l[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) l[g] = lg[(size_t)n * G + g];
-      place(n, rank_of(pos[n]), l);
-    }
-  } else {
-    int *sp = reinterpret_cast<int *>(bits);  // position tiles in the bitmap's space
-    for (int nb = 0; nb < L; nb += 256) {
-      const int n = nb + tid;
-      const int p = pos[min(n, L - 1)];
-      int rank = 0;
-      for (int t0 = 0; t0 < L; t0 += NW) {
-        const int tn = min(NW, L - t0);
-        __syncthreads();
-        for (int i = tid; i < tn; i += 256) sp[i] = pos[t0 + i];
-        __syncthreads();
-        for (int i = 0; i < tn; ++i) rank += sp[i] < p;
-      }
-      if (n < L) {
-        float l[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) l[g] = lg[(size_t)n * G + g];
-        place(n, rank, l);
-      }
-    }
+    for (int g = 0; g < G; ++g) s_p[g][t] = lg[(size_t)n * G + g];
   }
   __syncthreads();
 
@@ -618,6 +608,7 @@ static void chunk_pv_g(const StepArgs &a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s) {
+  hipLaunchKernelGGL(k_pos_rank, dim3((unsigned)a.n_units), dim3(kRankThreads), 0, s, a);
   const dim3 grid((a.cap + a.D - 1) / a.D, a.n_units);
   if (dtype == HIKV_BF16) {
     if (a.D == 128) chunk_pv_g<2, 128>(a, grid, s);

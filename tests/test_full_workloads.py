@@ -79,23 +79,29 @@ def _kept_differ_by_ties(post_gpu, post_ref, pre_ref, dref, kw, npos):
 
 
 # workload, full-attention pass, units sampled for the oracle (None: all),
-# steps (None: the workload's own count)
+# steps (None: the workload's own count), overrides of the workload's fields
 CASES = [
-    ("llama8b", False, None, None),
-    ("headkv32k", False, None, None),
-    ("longctx128k", False, None, None),
-    ("longctx128k", True, [(0, 2), (1, 7)], None),
-    ("twostage", False, None, None),
-    ("hikv_dualbank", False, None, 48),
-    ("hikv_hier", False, None, 48),
+    ("llama8b", False, None, None, None),
+    ("headkv32k", False, None, None, None),
+    ("longctx128k", False, None, None, None),
+    ("longctx128k", True, [(0, 2), (1, 7)], None, None),
+    ("twostage", False, None, None, None),
+    ("hikv_dualbank", False, None, 48, None),
+    ("hikv_hier", False, None, 48, None),
+    # HiKV's chunked Stage II V side on 131072-token units: the first step
+    # orders and chunks 131073 live tokens per unit, then steady steps
+    ("longctx128k", False, [(0, 1), (1, 6)], 6,
+     dict(stage2_channels=32, stage2_v=H.HIKV_S2V_CHUNK, name="longctx128k_chunks")),
 ]
 
 
-@pytest.mark.parametrize("name,full,sample,steps", CASES,
-                         ids=[c[0] + ("_full" if c[1] else "") for c in CASES])
-def test_whole_workload_lockstep_and_free_running(name, full, sample, steps):
+@pytest.mark.parametrize("name,full,sample,steps,over", CASES,
+                         ids=[(c[4] or {}).get("name", c[0] + ("_full" if c[1] else "")) for c in CASES])
+def test_whole_workload_lockstep_and_free_running(name, full, sample, steps, over):
     t_start = time.time()
     w = W.workload(name, full=full, steps=steps)
+    for k, v in (over or {}).items():
+        setattr(w, k, v)
     say(f"[gpu] {w.name}: {w.steps} steps, B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} ctx={w.ctx}; generating")
     d = W.generate(w)
     G = w.group

@@ -585,13 +585,14 @@ def test_stage2_chunks_repeat_is_bit_identical():
     assert np.array_equal(outs[0], outs[1])
 
 
-def test_stage2_chunks_positions_beyond_the_rank_bitmap():
-    """Positions spread over a span wider than the rank bitmap (131072):
-    the chunk order falls back to counting; results stay the same."""
+@pytest.mark.parametrize("newest", [400000, 5000000], ids=["2-windows", "20-windows"])
+def test_stage2_chunks_positions_beyond_the_rank_bitmap(newest):
+    """Positions spread over a span wider than one window of the position
+    ranking's bitmap (262144 positions): one pass per window; results stay
+    the same."""
     B, Hkv, G, D, cap = 1, 2, 4, 128, 700
     st = W.random_cache(41, B, G * Hkv, Hkv, D, W.BF16, cap, [[500, 299]])
     rng = np.random.Generator(np.random.PCG64(42))
-    newest = 400000
     for j in range(Hkv):
         n = int(st["len"][0, j])
         st["pos"][0, j, :n] = rng.permutation(rng.choice(newest, size=n, replace=False)).astype(np.int32)
