@@ -188,7 +188,12 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
           const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
           const int len = policy->len_hint[u];
           const int live = len + 1 - (len > beta ? 1 : 0);  // a unit over budget holds a dead slot
-          if (live - beta > 1) a.bulk_split = 1;
+          if (live - beta > 1) {
+            a.bulk_split = 1;
+            // survivors at or above the budget: at most the budget, and at
+            // most the len + 1 - beta slots there
+            a.bulk_rows = max(a.bulk_rows, min(beta, len + 1 - beta));
+          }
         }
       }
       return dev_err(launch_step(a, dt, s, ev0, ev1));

@@ -609,7 +609,7 @@ __global__ __launch_bounds__(kBulkThreads) void k_bulk_evict(StepArgs a, const i
   }
   __syncthreads();
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t whist[kBulkThreads / 64 * 256];
+  __shared__ __attribute__((aligned(16))) uint32_t whist[kBulkThreads / 64 * 256];
   __shared__ int sc[kBulkThreads];
   __shared__ RadixState rs;
   constexpr int RB = D * EL;

@@ -5,21 +5,30 @@
 
 namespace hikv {
 
+// Exclusive prefix sum over the workgroup (NT threads, a multiple of 64):
+// a scan within each wave, then the wave totals (sc: at least NT / 64 ints).
 template <int NT>
 __device__ int block_excl_scan(int v, int *sc, int *total) {
-  const int t = threadIdx.x;
-  sc[t] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int x = (t >= off) ? sc[t - off] : 0;
-    __syncthreads();
-    sc[t] += x;
-    __syncthreads();
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  const int incl = sc[t];
-  *total = sc[NT - 1];
+  if (lane == 63) sc[wave] = incl;
   __syncthreads();
-  return incl - v;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = sc[w];
+    if (w < wave) base += x;
+    tot += x;
+  }
+  *total = tot;
+  __syncthreads();  // sc is free for the next call
+  return base + incl - v;
 }
 
 template <int NT>
@@ -91,21 +100,16 @@ __device__ void radix_select_smallest(int n_items, int k, F key_of, uint32_t *hi
       const uint32_t incl = wave_incl_scan_u32(s);
       const uint32_t excl = incl - s;
       if (excl < krem && incl >= krem) {
-        const uint32_t hh[4] = {h0, h1, h2, h3};
-        uint32_t cum = excl;
-        int d = 3;
-        for (int i = 0; i < 4; ++i) {
-          if (cum + hh[i] >= krem) {
-            d = i;
-            break;
-          }
-          cum += hh[i];
-        }
+        // (named values: a small array indexed at run time goes to scratch)
+        const uint32_t c1 = excl + h0, c2 = c1 + h1, c3 = c2 + h2;
+        const int d = c1 >= krem ? 0 : (c2 >= krem ? 1 : (c3 >= krem ? 2 : 3));
+        const uint32_t cum = d == 0 ? excl : (d == 1 ? c1 : (d == 2 ? c2 : c3));
+        const uint32_t hd = d == 0 ? h0 : (d == 1 ? h1 : (d == 2 ? h2 : h3));
         const uint32_t rem = krem - cum;
         st->prefix = prefix | ((uint64_t)(4 * tid + d) << shift);
         st->shift = shift;
         st->krem = (int)rem;
-        st->done = (hh[d] == rem) ? 1 : 0;
+        st->done = (hd == rem) ? 1 : 0;
       }
     }
     __syncthreads();
@@ -173,21 +177,16 @@ __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint
       const uint32_t incl = wave_incl_scan_u32(s);
       const uint32_t excl = incl - s;
       if (excl < krem && incl >= krem) {
-        const uint32_t hh[4] = {h0, h1, h2, h3};
-        uint32_t cum = excl;
-        int d = 3;
-        for (int i = 0; i < 4; ++i) {
-          if (cum + hh[i] >= krem) {
-            d = i;
-            break;
-          }
-          cum += hh[i];
-        }
+        // (named values: a small array indexed at run time goes to scratch)
+        const uint32_t c1 = excl + h0, c2 = c1 + h1, c3 = c2 + h2;
+        const int d = c1 >= krem ? 0 : (c2 >= krem ? 1 : (c3 >= krem ? 2 : 3));
+        const uint32_t cum = d == 0 ? excl : (d == 1 ? c1 : (d == 2 ? c2 : c3));
+        const uint32_t hd = d == 0 ? h0 : (d == 1 ? h1 : (d == 2 ? h2 : h3));
         const uint32_t rem = krem - cum;
         st->prefix = prefix | ((uint64_t)(4 * tid + d) << shift);
         st->shift = shift;
         st->krem = (int)rem;
-        st->done = (hh[d] == rem) ? 1 : 0;
+        st->done = (hd == rem) ? 1 : 0;
       }
     }
     __syncthreads();
@@ -195,58 +194,56 @@ __device__ void radix_select_keys(const uint64_t *keys, int n_items, int k, uint
   }
 }
 
-// Bulk eviction of one unit by one workgroup of NT threads, from the
-// eviction keys of its L slots (keys[n]; UINT64_MAX for a protected token):
-// the n_evict smallest keys are evicted, then the survivors at or above the
+// The listing and moves of a unit's bulk eviction, once the threshold is
+// known: a slot is evicted when its key (keys[n]; UINT64_MAX for a protected
+// token) satisfies (key >> shift) <= lim.  The survivors at or above the
 // budget move into the evicted slots below it (K and V rows of RB bytes,
 // position, importance), and *len_u = beta.  holes and movers are the unit's
-// [cap] lists in the workspace.  With nmoves_u given, the moves are left to a
-// later launch: the number of rows to move goes to *nmoves_u instead.  Every
-// thread of the workgroup calls it.
+// [cap] lists in the workspace, both in ascending slot order.  With nmoves_u
+// given, the moves are left to a later launch: the number of rows to move
+// goes to *nmoves_u instead.  ebits: NT words of LDS scratch.  Every thread
+// of the workgroup calls it.
 template <int NT, int RB>
-__device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int beta, int n_evict, char *kw, char *vw,
-                             int32_t *posw, float *impw, int32_t *holes, int32_t *movers,
-                             int32_t *len_u, int32_t *status, uint32_t *hist, uint32_t *whist, int *sc,
-                             RadixState *rs, int32_t *nmoves_u = nullptr) {
-  const int tid = threadIdx.x;
-  radix_select_keys<NT, 8>(keys, L, n_evict, hist, whist, rs);
-  const uint64_t lim = rs->prefix >> rs->shift;
-  const int shift = rs->shift;
-  // Slots [n0, n1) of this thread, contiguous; their evicted flags stay in a
-  // mask between the counting and the listing pass (up to 64 slots per
-  // thread; beyond that the keys are read again).
-  const int per = (L + NT - 1) / NT;
-  const int n0 = min(tid * per, L), n1 = min(n0 + per, L);
-  uint64_t emask = 0;
-  int nh = 0, nm = 0;
-  for (int g0 = n0; g0 < n1; g0 += 8) {
-    uint64_t kk[8];
+__device__ __forceinline__ void bulk_list(const uint64_t *keys, int L, int beta, uint64_t lim, int shift,
+                                          char *kw, char *vw, int32_t *posw, float *impw, int32_t *holes,
+                                          int32_t *movers, int32_t *len_u, int32_t *status, uint64_t *ebits,
+                                          int *sc, int32_t *nmoves_u) {
+  constexpr int NW = NT / 64, SEG = NT * 64, KPT = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tot_h = 0, tot_m = 0;  // over the earlier segments
+  for (int s0 = 0; s0 < L; s0 += SEG) {
+    // The segment's evicted flags, one bit per slot (word w: slots s0 + 64 w
+    // ...): keys read coalesced, one ballot per 64 slots.  Words wholly past
+    // L are left as they are: no slot of theirs is counted.
+    for (int j0 = 0; j0 < SEG / NT && s0 + j0 * NT < L; j0 += KPT) {
+      uint64_t kk[KPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kk[j] = keys[min(g0 + j, n1 - 1)];
+      for (int j = 0; j < KPT; ++j) kk[j] = keys[min(s0 + (j0 + j) * NT + tid, L - 1)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = g0 + j;
-      const bool e = n < n1 && kk[j] != ~0ull && (kk[j] >> shift) <= lim;
-      if (e && n - n0 < 64) emask |= 1ull << (n - n0);
-      nh += (n < n1 && n < beta && e);
-      nm += (n < n1 && n >= beta && !e);
+      for (int j = 0; j < KPT; ++j) {
+        const int n = s0 + (j0 + j) * NT + tid;
+        const uint64_t m = __ballot(n < L && kk[j] != ~0ull && (kk[j] >> shift) <= lim);
+        if (lane == 0 && j0 + j < SEG / NT) ebits[(j0 + j) * NW + wave] = m;
+      }
     }
+    __syncthreads();
+    const uint64_t e = ebits[tid];
+    const int nb = s0 + 64 * tid;  // the first slot of this thread's word
+    auto below = [&](int lim_slot) -> uint64_t {  // the word's bits of slots < lim_slot
+      const int c = lim_slot - nb;
+      return c <= 0 ? 0ull : (c >= 64 ? ~0ull : ((1ull << c) - 1ull));
+    };
+    const uint64_t valid = below(L), low = below(beta);
+    const uint64_t hm = e & valid & low, mm = ~e & valid & ~low;
+    int th, tm;
+    int ih = tot_h + block_excl_scan<NT>(__popcll(hm), sc, &th);
+    int im = tot_m + block_excl_scan<NT>(__popcll(mm), sc, &tm);
+    for (uint64_t x = hm; x; x &= x - 1ull) holes[ih++] = nb + __builtin_ctzll(x);
+    for (uint64_t x = mm; x; x &= x - 1ull) movers[im++] = nb + __builtin_ctzll(x);
+    tot_h += th;
+    tot_m += tm;
+    __syncthreads();  // ebits is rebuilt for the next segment
   }
-  int tot_h, tot_m;
-  int oh = block_excl_scan<NT>(nh, sc, &tot_h);
-  int om = block_excl_scan<NT>(nm, sc, &tot_m);
-  for (int n = n0; n < n1; ++n) {
-    bool e;
-    if (n - n0 < 64) {
-      e = (emask >> (n - n0)) & 1;
-    } else {
-      const uint64_t key = keys[n];
-      e = key != ~0ull && (key >> shift) <= lim;
-    }
-    if (n < beta && e) holes[oh++] = n;
-    if (n >= beta && !e) movers[om++] = n;
-  }
-  __syncthreads();
   if (tot_h != tot_m) {  // cannot happen for distinct positions; fail safe
     if (tid == 0) set_status(status, HIKV_EINVAL);
     return;
@@ -285,6 +282,20 @@ __device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int be
     }
   }
   if (tid == 0) *len_u = beta;
+}
+
+// Bulk eviction of one unit by one workgroup of NT threads, from the
+// eviction keys of its L slots: the n_evict smallest keys are evicted (a
+// radix select over the keys), then bulk_list.
+template <int NT, int RB>
+__device__ __forceinline__ void bulk_compact(const uint64_t *keys, int L, int beta, int n_evict, char *kw, char *vw,
+                             int32_t *posw, float *impw, int32_t *holes, int32_t *movers,
+                             int32_t *len_u, int32_t *status, uint32_t *hist, uint32_t *whist, int *sc,
+                             RadixState *rs, int32_t *nmoves_u = nullptr) {
+  radix_select_keys<NT, 8>(keys, L, n_evict, hist, whist, rs);
+  // the select's per-wave histograms (NT / 64 x 256 words) are free again
+  bulk_list<NT, RB>(keys, L, beta, rs->prefix >> rs->shift, rs->shift, kw, vw, posw, impw, holes, movers, len_u,
+                    status, reinterpret_cast<uint64_t *>(whist), sc, nmoves_u);
 }
 
 // ---------------------------------------------------------------------------

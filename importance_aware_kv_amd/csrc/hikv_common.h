@@ -59,9 +59,13 @@ struct Ws {
   float *chunk_acc;     // [n_units][ceil(cap/D)][G][D] Stage II chunked V side: each chunk's P.V
   int32_t *chunk_cnt;   // [n_units][ceil(cap/D)][G] tokens each chunk kept per q-head
   int32_t *order;       // [n_units][cap] Stage II chunked V side: the live slots in position order
+  uint32_t *bhist;      // [n_units][imp_blocks(cap)][kBulkBins] bulk cut: each block's key histogram
+  int32_t *bsel;        // [n_units][4] bulk cut: tokens to evict, budget, tokens, flag (1: cut in bulk)
 };
 
-constexpr int kWsParts = 22;
+constexpr int kWsParts = 24;
+// Bulk cut: a histogram of the eviction keys' top kBulkBits bits per importance block.
+constexpr int kBulkBits = 11, kBulkBins = 1 << kBulkBits, kBulkShift = 64 - kBulkBits;
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -97,6 +101,8 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chu
       sizeof(float) * U * NC * G * D,  // chunk_acc
       sizeof(int32_t) * U * NC * G,    // chunk_cnt
       chunks ? sizeof(int32_t) * U * cap : 0,  // order
+      sizeof(uint32_t) * U * (size_t)imp_blocks(cap) * kBulkBins,  // bhist
+      sizeof(int32_t) * 4 * U,         // bsel
   };
   WsSizes w;
   size_t o = 0;
@@ -133,6 +139,8 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.chunk_acc = reinterpret_cast<float *>(b + s.off[19]);
   w.chunk_cnt = reinterpret_cast<int32_t *>(b + s.off[20]);
   w.order = reinterpret_cast<int32_t *>(b + s.off[21]);
+  w.bhist = reinterpret_cast<uint32_t *>(b + s.off[22]);
+  w.bsel = reinterpret_cast<int32_t *>(b + s.off[23]);
   return w;
 }
 
@@ -164,6 +172,7 @@ struct StepArgs {
   int32_t s2_chunks;         // Stage II V side: HiKV's per-chunk top-r of P (else exact top-k_T)
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
   int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit
+  int32_t bulk_rows;         // with bulk_split: the host's bound on the rows any unit's cut moves
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;
   float *out;

@@ -25,9 +25,11 @@
 //   the lowest of those as the victim, skips it, and the new token is then
 //   written into its slot, so no row moves in the steady state.  A unit that
 //   must shed more than one token (the first step after a prefill) is cut in
-//   bulk by a radix select; with the caller's lengths and budgets the row
-//   moves of that cut go to a third launch (k_bulk_moves).  Output blocks
-//   combine the tiles' partials.
+//   bulk by a radix select; with the caller's lengths and budgets the cut is
+//   spread over the unit's importance blocks (keys and a key histogram each)
+//   and finished by two more launches (k_bulk_select: the threshold and the
+//   lists of rows to move; k_bulk_moves: the moves).  Output blocks combine
+//   the tiles' partials.
 
 #include <hip/hip_ext.h>
 
@@ -648,6 +650,13 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   __shared__ int ss[kNW2];
   __shared__ float s_newimp;
   __shared__ int s_last;
+  // bulk cut: radix-select scratch (one block per unit), or the block's key
+  // histogram (kBulkBins words of whist) when the cut is spread over blocks
+  __shared__ uint32_t hist[256];
+  __shared__ __attribute__((aligned(16))) uint32_t whist[kNW2 * 256];
+  __shared__ int sc[kT2];
+  __shared__ RadixState rs;
+  static_assert(kBulkBins <= kNW2 * 256, "the key histogram fits the radix scratch");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
@@ -659,7 +668,10 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   const int u = blockIdx.x, r = blockIdx.y;
   // The move launch that may follow reads every unit's count: none unless a
   // bulk cut below says otherwise (the same thread writes both).
-  if (a.bulk_split && r == 0 && tid == 0) a.ws.nmoves[u] = 0;
+  if (a.bulk_split && r == 0 && tid == 0) {
+    a.ws.nmoves[u] = 0;
+    a.ws.bsel[4 * u + 3] = 0;
+  }
   // The host plan's words (kernel arguments, clamped to its table) are loaded
   // with the flag that says whether there is one, so that the host plan costs
   // one round trip; the device plan's path uses them too, after its own load,
@@ -755,8 +767,12 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       // the importance, and its victim is left pending for the next call;
       // more than one (a bulk cut) needs every token in one block.
       const bool bulk = n_evict > 1;
-      if (bulk && r > 0) return;
-      const int nb1 = bulk ? L : min(L, nb0 + CHUNK);
+      // With the caller's lengths a bulk cut is spread over the unit's blocks
+      // (each leaves its keys and a histogram of them; k_bulk_select finishes
+      // the cut); without them one block takes every token.
+      const bool split = bulk && a.bulk_split;
+      if (bulk && !split && r > 0) return;
+      const int nb1 = (bulk && !split) ? L : min(L, nb0 + CHUNK);
       const int nact = (L + CHUNK - 1) / CHUNK;  // blocks holding tokens of the unit
       const int Wp = min(a.n_recent, beta - S);
       const int fs = (dead >= 0 && !bulk) ? dead : Lold;  // the new token's slot
@@ -772,11 +788,16 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       uint64_t *bkeys = a.ws.bkeys + (size_t)u * a.cap;  // bulk: every slot's key
       uint64_t best = ~0ull;
       int best_slot = -1;
+      if (split) {
+        for (int i = tid; i < kBulkBins; i += kT2) whist[i] = 0u;
+        __syncthreads();
+      }
       for (int base = nb0; base < nb1; base += CHUNK) {
         if (base != nb0) load_batch(base);
     #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int n = base + tid + i * kT2;
+          int hbin = kBulkBins;  // the key's histogram bin (a spread bulk cut), or none
           if (n < nb1 && n != dead) {
             float p = 0.f;
     #pragma unroll
@@ -799,11 +820,44 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
                 best_slot = is_new ? fs : n;
               }
             }
-            if (bulk) bkeys[n] = cand ? evict_key(iv, pn) : ~0ull;
+            if (bulk) {
+              const uint64_t kk = cand ? evict_key(iv, pn) : ~0ull;
+              bkeys[n] = kk;
+              if (cand) hbin = (int)(kk >> kBulkShift);
+            }
           } else if (bulk && n < nb1) {
             bkeys[n] = 0;  // the dead slot: the first to go
+            hbin = 0;
+          }
+          if (split) {
+            // Nearby importances share bins: the lanes with the first lane's
+            // bin are counted with one atomic.
+            const int h0 = __builtin_amdgcn_readfirstlane(hbin);
+            const uint64_t same = __ballot(hbin == h0);
+            if (hbin == h0) {
+              if (h0 < kBulkBins && lane == __builtin_ctzll(same)) atomicAdd(&whist[h0], (uint32_t)__popcll(same));
+            } else if (hbin < kBulkBins) {
+              atomicAdd(&whist[hbin], 1u);
+            }
           }
         }
+      }
+      if (split) {
+        __syncthreads();  // the histogram, s_newimp
+        uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
+        for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
+        if (nb1 == L) {  // the block holding slot Lold appends the new token there
+          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
+          if (tid == 0) {
+            impw[Lold] = s_newimp;
+            posw[Lold] = newest;
+          }
+        }
+        if (r == 0 && tid == 0) {
+          unit_state(a, u)[0] = 0;
+          reinterpret_cast<int4 *>(a.ws.bsel)[u] = make_int4(n_evict, beta, L, 1);
+        }
+        return;
       }
       if (!bulk) {
         wave_min_key(best, best_slot);
@@ -854,13 +908,9 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         unit_state(a, u)[0] = 0;
       }
       __syncthreads();  // every key is stored
-      __shared__ uint32_t hist[256];
-      __shared__ uint32_t whist[kNW2 * 256];
-      __shared__ int sc[kT2];
-      __shared__ RadixState rs;
       bulk_compact<kT2, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
                             a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs,
-                            a.bulk_split ? a.ws.nmoves + u : nullptr);
+                            nullptr);
     }();
     end_wave();
   }
@@ -903,47 +953,285 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
 }
 
 // ---------------------------------------------------------------------------
-// Third launch of a step that cuts units in bulk (when the host can tell): the
-// rows the second launch listed move from above the budget into the evicted
-// slots below it (K and V rows, position, importance), spread over gridDim.y
-// workgroups per unit.  Hole and mover lists pair up in order; every source
-// and destination is distinct, so the moves are independent.
+// Third launch of a step that cuts units in bulk (when the host can tell),
+// one workgroup per unit.  The importance blocks left every slot's eviction
+// key and a histogram of the keys' top kBulkBits bits each; the n_evict
+// smallest keys go:
+//  1. the summed histograms give the bin that holds the n_evict-th smallest
+//     key (need: how many of the bin's keys go; cnt: how many it holds);
+//     while the bin holds more than kBulkCand keys, one pass over the keys
+//     histograms the next kBulkBits bits of those in it (a narrower bin);
+//  2. one pass over the keys marks the slots whose key lies below the bin
+//     (an LDS bitmap, one bit per slot) and gathers the bin's keys and slots;
+//  3. the need-th smallest of those is found in LDS (radix passes of 8 bits
+//     below the bits the bin fixes), and their slots up to it are marked;
+//  4. the holes (marked slots below the budget) and movers (unmarked live
+//     slots at or above it) are listed in ascending order for the moves.
+// Each pass over the keys has up to kBulkKpt of them per thread in flight.
+// Units longer than the bitmap covers list from the keys instead.
+// ---------------------------------------------------------------------------
+constexpr int kBulkCand = 4096;        // keys of the threshold's bin gathered in LDS
+constexpr int kBulkMapSlots = 1 << 18;  // slots the LDS bitmap covers (32 KB)
+constexpr int kBulkKpt = 16;            // keys per thread per pass in flight
+
+template <int RB>
+__global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
+  static_assert(kBulkBins == 2 * kT2, "two histogram bins per thread");
+  constexpr int NT = kT2, KPT = kBulkKpt, NMW = kBulkMapSlots / 64;
+  __shared__ uint32_t h[kBulkBins];
+  __shared__ uint64_t ck[kBulkCand];
+  __shared__ int cs[kBulkCand];
+  __shared__ uint64_t eb[NMW];
+  __shared__ int sc[kNW2];
+  __shared__ int s_bin, s_need, s_cnt, s_nc;
+  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int4 bs = reinterpret_cast<const int4 *>(a.ws.bsel)[u];
+  if (bs.w != 1) return;  // not cut in bulk
+  const int k = bs.x, beta = bs.y, L = bs.z;
+  const uint64_t *keys = a.ws.bkeys + (size_t)u * a.cap;
+
+  // The bin of a 2 x kT2-bin histogram (bins 2 tid, 2 tid + 1 in c0, c1)
+  // holding the need-th smallest counted key.
+  auto find_bin = [&](uint32_t c0, uint32_t c1, int need) {
+    if (tid == 0) s_bin = -1;
+    int tot;
+    const int ex = block_excl_scan<NT>((int)(c0 + c1), sc, &tot);
+    if (ex < need && ex + (int)(c0 + c1) >= need) {
+      const bool first = ex + (int)c0 >= need;
+      s_bin = first ? 2 * tid : 2 * tid + 1;
+      s_need = first ? need - ex : need - ex - (int)c0;
+      s_cnt = first ? (int)c0 : (int)c1;
+    }
+    __syncthreads();
+  };
+
+  // 1. The threshold's bin.
+  {
+    const int nbk = (L + kImpChunk - 1) / kImpChunk;
+    const uint32_t *bh = a.ws.bhist + (size_t)u * imp_blocks(a.cap) * kBulkBins + 2 * tid;
+    uint32_t c0 = 0, c1 = 0;
+#pragma unroll 4
+    for (int r = 0; r < nbk; ++r) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(bh + (size_t)r * kBulkBins);
+      c0 += v.x;
+      c1 += v.y;
+    }
+    find_bin(c0, c1, k);
+  }
+  if (s_bin < 0) {  // fewer candidates than tokens to evict: cannot happen
+    if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+    return;
+  }
+  uint64_t prefix = (uint64_t)s_bin;  // the bin: the keys' top pbits bits
+  int pbits = kBulkBits, need = s_need, cnt = s_cnt;
+  while (cnt > kBulkCand && pbits < 64) {
+    const int nb = min(kBulkBits, 64 - pbits), sh = 64 - pbits - nb;
+    for (int i = tid; i < kBulkBins; i += NT) h[i] = 0u;
+    __syncthreads();
+    for (int n0 = 0; n0 < L; n0 += KPT * NT) {
+      uint64_t kk[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) kk[j] = keys[min(n0 + j * NT + tid, L - 1)];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool in = n0 + j * NT + tid < L && kk[j] != ~0ull && (kk[j] >> (64 - pbits)) == prefix;
+        const int d = in ? (int)((kk[j] >> sh) & ((1ull << nb) - 1ull)) : kBulkBins;
+        const int d0 = __builtin_amdgcn_readfirstlane(d);
+        const uint64_t same = __ballot(d == d0);
+        if (d == d0) {
+          if (d0 < kBulkBins && lane == __builtin_ctzll(same)) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+        } else if (d < kBulkBins) {
+          atomicAdd(&h[d], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    find_bin(h[2 * tid], h[2 * tid + 1], need);
+    if (s_bin < 0) {
+      if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+      return;
+    }
+    prefix = (prefix << nb) | (uint64_t)s_bin;
+    pbits += nb;
+    need = s_need;
+    cnt = s_cnt;
+  }
+  const int tsh = 64 - pbits;  // bits below the bin's
+  const bool all = need == cnt;  // the whole bin goes
+  const bool use_map = L <= kBulkMapSlots;
+
+  // 2. Slots below the bin marked; the bin's keys gathered.
+  if (tid == 0) s_nc = 0;
+  __syncthreads();
+  for (int n0 = 0; n0 < L; n0 += KPT * NT) {
+    uint64_t kk[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kk[j] = keys[min(n0 + j * NT + tid, L - 1)];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int n = n0 + j * NT + tid;
+      const bool valid = n < L && kk[j] != ~0ull;
+      const uint64_t top = tsh >= 64 ? 0ull : (kk[j] >> tsh);
+      const bool ev = valid && (top < prefix || (all && top == prefix));
+      const bool c = valid && !all && top == prefix;
+      if (use_map) {
+        const uint64_t m = __ballot(ev);
+        if (lane == 0 && n0 + j * NT < L) eb[(n0 + j * NT) / 64 + wave] = m;
+      }
+      const uint64_t mc = __ballot(c);  // one atomic per wave
+      int b0 = 0;
+      if (lane == 0 && mc) b0 = atomicAdd(&s_nc, __popcll(mc));
+      b0 = __shfl(b0, 0);
+      const int i = b0 + __popcll(mc & ((1ull << lane) - 1ull));
+      if (c && i < kBulkCand) ck[i] = kk[j], cs[i] = n;
+    }
+  }
+  __syncthreads();
+  if (!all && s_nc != cnt) {  // the histograms and the keys disagree: cannot happen
+    if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+    return;
+  }
+
+  // 3. The need-th smallest key of the bin: radix passes of 8 bits over the
+  // gathered keys, below the bits the bin fixes.  T: the largest key that goes.
+  uint64_t T;
+  if (all) {
+    T = (prefix << tsh) | (tsh == 0 ? 0ull : ((1ull << tsh) - 1ull));
+  } else {
+    uint64_t pre = prefix << tsh;  // the bits fixed so far
+    int rem = tsh, nd = need, nc = cnt;
+    while (rem > 0 && nd < nc) {
+      const int nb = min(8, rem), sh = rem - nb;
+      if (tid < 256) h[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < cnt; i += NT) {
+        const uint64_t key = ck[i];
+        const bool in = (key >> rem) == (pre >> rem);
+        const int d = in ? (int)((key >> sh) & ((1ull << nb) - 1ull)) : 256;
+        const int d0 = __builtin_amdgcn_readfirstlane(d);
+        const uint64_t same = __ballot(d == d0);
+        if (d == d0) {
+          if (d0 < 256 && lane == __builtin_ctzll(same)) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+        } else if (d < 256) {
+          atomicAdd(&h[d], 1u);
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const uint32_t h0 = h[4 * lane], h1 = h[4 * lane + 1], h2 = h[4 * lane + 2], h3 = h[4 * lane + 3];
+        const uint32_t s4 = h0 + h1 + h2 + h3;
+        const uint32_t incl = wave_incl_scan_u32(s4), excl = incl - s4;
+        if (excl < (uint32_t)nd && incl >= (uint32_t)nd) {
+          // (named values: a small array indexed at run time goes to scratch)
+          const uint32_t c1 = excl + h0, c2 = c1 + h1, c3 = c2 + h2, want = (uint32_t)nd;
+          const int d = c1 >= want ? 0 : (c2 >= want ? 1 : (c3 >= want ? 2 : 3));
+          const uint32_t cum = d == 0 ? excl : (d == 1 ? c1 : (d == 2 ? c2 : c3));
+          s_bin = 4 * lane + d;
+          s_need = nd - (int)cum;
+          s_cnt = (int)(d == 0 ? h0 : (d == 1 ? h1 : (d == 2 ? h2 : h3)));
+        }
+      }
+      __syncthreads();
+      pre |= (uint64_t)s_bin << sh;
+      nd = s_need;
+      nc = s_cnt;
+      rem = sh;
+      __syncthreads();  // h is cleared for the next pass
+    }
+    T = pre | (rem == 0 ? 0ull : ((1ull << rem) - 1ull));
+    if (use_map)
+      for (int i = tid; i < cnt; i += NT)
+        if (ck[i] <= T) atomicOr(reinterpret_cast<unsigned long long *>(&eb[cs[i] >> 6]), 1ull << (cs[i] & 63));
+  }
+  char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
+  char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
+  int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
+  if (!use_map) {  // a key goes exactly when it is at most T
+    bulk_list<NT, RB>(keys, L, beta, T, 0, kw, vw, a.pos + (size_t)u * a.cap, a.imp + (size_t)u * a.cap, holes,
+                      movers, a.len + u, a.ws.status, reinterpret_cast<uint64_t *>(ck), sc, a.ws.nmoves + u);
+    return;
+  }
+  __syncthreads();  // the bitmap is complete
+
+  // 4. Holes and movers from the bitmap: each thread takes a run of words.
+  const int nw = (L + 63) / 64, wpt = (nw + NT - 1) / NT;
+  const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
+  auto below = [](int c) -> uint64_t { return c <= 0 ? 0ull : (c >= 64 ? ~0ull : ((1ull << c) - 1ull)); };
+  int nh = 0, nm = 0;
+  for (int w = w0; w < w1; ++w) {
+    const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(beta - 64 * w);
+    nh += __popcll(e & valid & low);
+    nm += __popcll(~e & valid & ~low);
+  }
+  int th, tm;
+  int ih = block_excl_scan<NT>(nh, sc, &th);
+  int im = block_excl_scan<NT>(nm, sc, &tm);
+  for (int w = w0; w < w1; ++w) {
+    const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(beta - 64 * w);
+    for (uint64_t x = e & valid & low; x; x &= x - 1ull) holes[ih++] = 64 * w + __builtin_ctzll(x);
+    for (uint64_t x = ~e & valid & ~low; x; x &= x - 1ull) movers[im++] = 64 * w + __builtin_ctzll(x);
+  }
+  if (tid == 0) {
+    if (th != tm) {  // cannot happen for distinct positions; fail safe
+      set_status(a.ws.status, HIKV_EINVAL);
+    } else {
+      a.ws.nmoves[u] = tm;
+      a.len[u] = beta;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fourth launch of a step that cuts units in bulk (when the host can tell): the
+// rows k_bulk_select listed move from above the budget into the evicted
+// slots below it (K and V rows, position, importance): workgroup y of a unit
+// takes moves [64 y, 64 y + 64) (bf16 rows of 128; fewer for wider rows),
+// the host sizing the grid from its bound on any unit's moves.  Hole and
+// mover lists pair up in order; every source and destination is distinct, so
+// the moves are independent.
 // ---------------------------------------------------------------------------
 template <int RB>
 __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
-  constexpr int CPR = RB / 16, RPP = 256 / CPR;  // threads per row, rows per pass
+  constexpr int CPR = RB / 16, RPP = 256 / CPR;  // threads per row, rows per pass (4 passes)
   const int u = blockIdx.x, tid = threadIdx.x;
-  const int nm = a.ws.nmoves[u];
-  const int per = (nm + (int)gridDim.y - 1) / (int)gridDim.y;
-  const int i0 = (int)blockIdx.y * per, i1 = min(nm, i0 + per);
-  if (i0 >= i1) return;
   const int ci = tid % CPR, rr = tid / CPR;
+  const int i0 = (int)blockIdx.y * RPP * 4 + rr;  // this group's moves: i0, i0 + RPP, ...
   const int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
   char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
   char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
   int32_t *posw = a.pos + (size_t)u * a.cap;
   float *impw = a.imp + (size_t)u * a.cap;
-  // Two rows per thread group in flight: every load of a pass before its stores.
-  for (int i = i0 + rr; i < i1; i += 2 * RPP) {
-    const int ib = i + RPP;
-    const int jb = min(ib, i1 - 1);
-    const int sa = movers[i], da = holes[i], sb = movers[jb], db = holes[jb];
-    const uint4 ka = reinterpret_cast<const uint4 *>(kw + (size_t)sa * RB)[ci];
-    const uint4 va = reinterpret_cast<const uint4 *>(vw + (size_t)sa * RB)[ci];
-    const uint4 kb = reinterpret_cast<const uint4 *>(kw + (size_t)sb * RB)[ci];
-    const uint4 vb = reinterpret_cast<const uint4 *>(vw + (size_t)sb * RB)[ci];
-    const int pa = posw[sa], pb = posw[sb];
-    const float xa = impw[sa], xb = impw[sb];
-    reinterpret_cast<uint4 *>(kw + (size_t)da * RB)[ci] = ka;
-    reinterpret_cast<uint4 *>(vw + (size_t)da * RB)[ci] = va;
-    if (ci == 0) posw[da] = pa, impw[da] = xa;
-    if (ib < i1) {
-      reinterpret_cast<uint4 *>(kw + (size_t)db * RB)[ci] = kb;
-      reinterpret_cast<uint4 *>(vw + (size_t)db * RB)[ci] = vb;
-      if (ci == 0) posw[db] = pb, impw[db] = xb;
+  // The count and the group's list entries are loaded together (the entries
+  // from clamped addresses; an entry past the count is a stale slot number,
+  // clamped, read and not used), so the rows follow one round trip later.
+  // Four moves per thread group in named registers (arrays of 16-byte
+  // vectors are not kept in registers by the compiler).
+  const int nm = a.ws.nmoves[u];
+  const int ia = i0, ib = i0 + RPP, ic = i0 + 2 * RPP, id = i0 + 3 * RPP;
+  auto ent = [&](const int32_t *l, int i) { return min(max(l[min(i, a.cap - 1)], 0), a.cap - 1); };
+  const int sa = ent(movers, ia), sb = ent(movers, ib), sc = ent(movers, ic), sd = ent(movers, id);
+  const int da = ent(holes, ia), db = ent(holes, ib), dc = ent(holes, ic), dd = ent(holes, id);
+  if ((int)blockIdx.y * RPP * 4 >= nm) return;  // past this unit's moves
+  auto row = [&](const char *base, int slot) { return reinterpret_cast<const uint4 *>(base + (size_t)slot * RB)[ci]; };
+  const uint4 ka = row(kw, sa), kb = row(kw, sb), kc = row(kw, sc), kd = row(kw, sd);
+  const uint4 va = row(vw, sa), vb = row(vw, sb), vc = row(vw, sc), vd = row(vw, sd);
+  const int pa = posw[sa], pb = posw[sb], pc = posw[sc], pd = posw[sd];
+  const float xa = impw[sa], xb = impw[sb], xc = impw[sc], xd = impw[sd];
+  auto put = [&](int i, int dst, const uint4 &k, const uint4 &v, int p, float x) {
+    if (i < nm) {
+      reinterpret_cast<uint4 *>(kw + (size_t)dst * RB)[ci] = k;
+      reinterpret_cast<uint4 *>(vw + (size_t)dst * RB)[ci] = v;
+      if (ci == 0) posw[dst] = p, impw[dst] = x;
     }
-  }
+  };
+  put(ia, da, ka, va, pa, xa);
+  put(ib, db, kb, vb, pb, xb);
+  put(ic, dc, kc, vc, pc, xc);
+  put(id, dd, kd, vd, pd, xd);
 }
+
+template <int RB>
+static constexpr int bulk_moves_per_block() { return (256 / (RB / 16)) * 4; }
 
 // ---------------------------------------------------------------------------
 // Resolution of the pending eviction, one wave per unit: the dead slot (the
@@ -1026,9 +1314,11 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
                      dim3(kT2), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.bulk_split) {
-    // 128 workgroups per unit: at most a few passes of 16 rows each for the
-    // largest cuts.
-    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, 128u), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int per = bulk_moves_per_block<D * EL>();
+    const unsigned gy = (unsigned)max(1, (a.bulk_rows + per - 1) / per);
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, gy), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -290,6 +290,39 @@ def test_long_units_split_eviction_lockstep(n_recent, hint):
 
 
 @PATHS
+@pytest.mark.parametrize("pattern", ["equal", "two-level"])
+def test_bulk_cut_threshold_bin_edge_cases(pattern, hint):
+    """Bulk cuts at the edges of the key-histogram selection.  "equal": every
+    K row of a unit is the same, so every token gets the same probability and
+    (from zero) the same importance: the threshold's histogram bin holds every
+    candidate (11900 keys: more than the 8192 the selection gathers in LDS;
+    7400 in the second unit: gathered) and positions decide.  "two-level":
+    exactly the tokens to evict have a low importance, so the threshold's bin
+    is taken whole."""
+    B, Hkv, G, D, cap, S, Wn, beta = 1, 2, 4, 128, 12100, 4, 64, 500
+    st = W.random_cache(61, B, G * Hkv, Hkv, D, W.BF16, cap, [[12000, 7500]])
+    newest = st["newest"]
+    if pattern == "equal":
+        st["k"][:] = st["k"][:, :, :1]
+        st["imp"][:] = 0.0
+    else:
+        rng = np.random.Generator(np.random.PCG64(62))
+        st["imp"][:] = 0.5
+        wp = min(Wn, beta - S)
+        for j in range(Hkv):
+            n = int(st["len"][0, j])
+            p = st["pos"][0, j, :n]
+            cand = np.nonzero((p >= S) & (p <= newest - wp))[0]
+            n_evict = n + 1 - beta
+            keep = rng.choice(cand, size=len(cand) - n_evict, replace=False)
+            st["imp"][0, j, keep] = 1000.0
+    data = W.random_step(63, B, G * Hkv, Hkv, D, W.BF16, newest)
+    data = {k: v[None] for k, v in data.items()}
+    run = GpuRun(st, G * Hkv, budget_all=beta, n_sink=S, n_recent=Wn, hint=hint)
+    lockstep(run, data, 1, tag=f"bulk cut {pattern}")
+
+
+@PATHS
 def test_longctx_g8_lockstep_and_full_attention(hint):
     w = W.workload("longctx128k", ctx=3000, steps=4, batch=1)
     w.budget_all, w.n_recent = 256, 64
