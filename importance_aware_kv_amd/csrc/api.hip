@@ -67,7 +67,7 @@ int check_cache(const hikv_cache *c) {
 
 WsSizes sizes_for(const hikv_shape *s, const hikv_policy *p) {
   const bool chunks = p && p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_CHUNK;
-  const int kT = (p && p->stage2_channels > 0 && !chunks) ? p->stage2_tokens : 1;
+  const int kT = (p && p->stage2_channels > 0 && !chunks) ? p->stage2_tokens : 0;  // 0: no exact top-k_T pass
   return ws_sizes(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->capacity, kT, chunks);
 }
 
@@ -203,6 +203,30 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
     if ((e = launch_settle(a, dt, nullptr, true, s)) != hipSuccess) return dev_err(e);
     if ((e = launch_attn_tiles(a, dt, true, false, s, ev0, ev1)) != hipSuccess) return dev_err(e);
     if ((e = launch_combine(a, true, s)) != hipSuccess) return dev_err(e);
+  } else if (!a.s2_chunks && dt == HIKV_BF16 && a.D == 128 && a.kT <= kS2TwoMaxTokens &&
+             path == HIKV_PATH_AUTO) {
+    // Stage II with the exact top-k_T V side in two launches (like Stage I:
+    // an eviction of one token is left pending).  Its bulk cut always leaves
+    // the row moves to launches of their own; with the caller's lengths and
+    // budgets they are launched only when some unit is cut in bulk.
+    a.s2_two = 1;
+    if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
+    if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
+      const int U = shape->batch * shape->n_kv_heads;
+      for (int u = 0; u < U; ++u) {
+        const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
+        const int len = policy->len_hint[u];
+        const int live = len + 1 - (len > beta ? 1 : 0);
+        if (live - beta > 1) {
+          a.bulk_split = 1;
+          a.bulk_rows = max(a.bulk_rows, min(beta, len + 1 - beta));
+        }
+      }
+    } else {
+      a.bulk_split = 1;
+      a.bulk_rows = a.cap;
+    }
+    return dev_err(launch_step(a, dt, s, ev0, ev1));
   } else {
     // (the channel-select launch also settles a pending eviction first)
     if ((e = launch_stage2_channels(a, dt, s)) != hipSuccess) return dev_err(e);

@@ -61,9 +61,11 @@ struct Ws {
   int32_t *order;       // [n_units][cap] Stage II chunked V side: the live slots in position order
   uint32_t *bhist;      // [n_units][imp_blocks(cap)][kBulkBins] bulk cut: each block's key histogram
   int32_t *bsel;        // [n_units][4] bulk cut: tokens to evict, budget, tokens, flag (1: cut in bulk)
+  float *logits2;       // [n_units][cap][G] Stage II in two launches: the exact logits (raw q.k)
+  uint64_t *s2keys;     // [n_units][G][cap] Stage II in two launches: selection keys of long units
 };
 
-constexpr int kWsParts = 24;
+constexpr int kWsParts = 26;
 // Bulk cut: a histogram of the eviction keys' top kBulkBits bits per importance block.
 constexpr int kBulkBits = 11, kBulkBins = 1 << kBulkBits, kBulkShift = 64 - kBulkBits;
 struct WsSizes {
@@ -103,6 +105,8 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chu
       chunks ? sizeof(int32_t) * U * cap : 0,  // order
       sizeof(uint32_t) * U * (size_t)imp_blocks(cap) * kBulkBins,  // bhist
       sizeof(int32_t) * 4 * U,         // bsel
+      (kT > 0 && !chunks) ? sizeof(float) * U * cap * G : 0,     // logits2
+      (kT > 0 && !chunks) ? sizeof(uint64_t) * U * G * cap : 0,  // s2keys
   };
   WsSizes w;
   size_t o = 0;
@@ -141,12 +145,16 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.order = reinterpret_cast<int32_t *>(b + s.off[21]);
   w.bhist = reinterpret_cast<uint32_t *>(b + s.off[22]);
   w.bsel = reinterpret_cast<int32_t *>(b + s.off[23]);
+  w.logits2 = reinterpret_cast<float *>(b + s.off[24]);
+  w.s2keys = reinterpret_cast<uint64_t *>(b + s.off[25]);
   return w;
 }
 
 // Tile plan computed on the host from a caller-supplied copy of len[] (the
 // kernels then skip deriving it from device memory).  n == 0: no host plan.
 constexpr int kHostPlanUnits = 64;
+// Stage II in two launches lists its selected tokens in LDS: k_T up to this.
+constexpr int kS2TwoMaxTokens = 2048;
 struct HostPlan {
   int32_t n, T, ntiles;
   int32_t base[kHostPlanUnits + 1];  // first tile of each unit; base[n] = ntiles
@@ -173,6 +181,7 @@ struct StepArgs {
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
   int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit
   int32_t bulk_rows;         // with bulk_split: the host's bound on the rows any unit's cut moves
+  int32_t s2_two;            // Stage II (exact top-k_T V side) in the two-launch sequence
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;
   float *out;

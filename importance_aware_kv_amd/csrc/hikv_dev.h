@@ -575,6 +575,104 @@ __device__ __forceinline__ void lds_read8_b64(uint64_t (&o)[8], uint32_t addr) {
       : "memory");
 }
 
+// Stage II's attention launch stages K only: a sub-chunk of 64 rows of 256
+// bytes (16 KB, the swizzle of stage_sub), issued by LW waves (wave wl among
+// them), 16 / LW loads each.
+template <int LW>
+__device__ __forceinline__ void stage_k_by(char *kb, const char *kc, const char *kn, int c0, int nrows, int t0,
+                                           int Lold, int wl, int lane) {
+  constexpr int RB = 256;
+#pragma unroll
+  for (int i = 0; i < 16 / LW; ++i) {
+    const int piece = i * LW + wl;  // 1 KB piece of the 16 KB sub-chunk: four rows
+    const int off = (piece << 10) + (lane << 4);
+    const int row = off / RB;
+    const int col = (((off - row * RB) >> 4) ^ (row & 15)) << 4;
+    const int n = (row < nrows) ? c0 + row : t0;  // t0 is always a live row of the tile
+    const char *ks = (n == Lold) ? kn + col : kc + (size_t)n * RB + col;
+    __builtin_amdgcn_global_load_lds(ks, kb + (piece << 10), 16, 0, 0);
+  }
+}
+
+// The eight 8-byte K reads of one wave's 16 rows (the q.k A operand), at an
+// immediate offset (the ring buffer), then one wait; asm, for the reason given
+// at lds_read_rows.
+template <int OFF>
+__device__ __forceinline__ void mfma_k_operands(uint64_t (&o)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b64 %0, %8 offset:%16\n\t"
+      "ds_read_b64 %1, %9 offset:%16\n\t"
+      "ds_read_b64 %2, %10 offset:%16\n\t"
+      "ds_read_b64 %3, %11 offset:%16\n\t"
+      "ds_read_b64 %4, %12 offset:%16\n\t"
+      "ds_read_b64 %5, %13 offset:%16\n\t"
+      "ds_read_b64 %6, %14 offset:%16\n\t"
+      "ds_read_b64 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "i"(OFF)
+      : "memory");
+}
+
+// LDS accesses the compiler must not order against the DMA ring (it would
+// wait for every load in flight): one 32-bit write, no wait; one 32-bit and
+// two 16-bit reads with their wait.
+__device__ __forceinline__ void lds_write_b32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ float lds_read_f32(uint32_t addr) {
+  float x;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+  return x;
+}
+__device__ __forceinline__ void lds_read_u16x2(uint32_t &a, uint32_t &b, uint32_t addr_a, uint32_t addr_b) {
+  asm volatile("ds_read_u16 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b) : "v"(addr_a), "v"(addr_b) : "memory");
+}
+__device__ __forceinline__ uint64_t lds_read_u64(uint32_t addr) {
+  uint64_t x;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+  return x;
+}
+
+// Wave-wide scan and reductions with DPP (GFX9 row shifts within rows of 16
+// lanes, then the row broadcasts of lanes 15 and 31), in place of shuffle
+// chains through the LDS crossbar.  A lane whose DPP source lies outside its
+// row keeps the identity (`old`).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += dpp_u32<0x111>(0u, v);       // row_shr:1
+  v += dpp_u32<0x112>(0u, v);       // row_shr:2
+  v += dpp_u32<0x114>(0u, v);       // row_shr:4
+  v += dpp_u32<0x118>(0u, v);       // row_shr:8
+  v += dpp_u32<0x142, 0xA>(0u, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_u32<0x143, 0xC>(0u, v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// Maximum and sum over the wave (every lane gets the result).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const uint32_t ninf = __float_as_uint(-INFINITY);
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x111>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x112>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x114>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x118>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x142, 0xA>(ninf, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x143, 0xC>(ninf, __float_as_uint(v))));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __uint_as_float(dpp_u32<0x111>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x112>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x114>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x118>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x142, 0xA>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x143, 0xC>(0u, __float_as_uint(v)));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
 template <int STEP, int K>
 __device__ __forceinline__ void vm_wait_ahead(int k) {
   if constexpr (K == 0) {

@@ -574,6 +574,250 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Stage II's first launch (bf16 K, D = 128; "HiKV", Sec. III-C): per tile,
+// the exact logits q.k and the reduced logits over each q-head's r channels
+// of largest |q_d| (ties: lower channel) of every live token, from one matrix
+// product: the B operand carries the group's queries in columns [0, G) and
+// the same queries masked to their channels in columns [G, 2G).  Only K is
+// read (the output is formed over the selected tokens in the second launch).
+//
+// The tile streams 64-token sub-chunks of K (16 KB) through a ring of NSUB
+// buffers; wave w takes rows [16 w, 16 w + 16) of each.  Waves 2 and 3 issue
+// the loads, waves 0 and 1 the stores (as in k_attend_mfma): every wave puts
+// its scores into an LDS buffer of the sub-chunk, which waves 0 and 1 store
+// one iteration later (exact logits to ws.logits2, reduced ones to
+// ws.logits, token-major like Stage I's).  The softmax statistics of the
+// reduced logits (running maximum and sum per column) give the tile's
+// (max, sum) pair per head in ws.part_ml, the form the importance blocks of
+// the second launch read.  At the first sub-chunk the waves pick the
+// channels (each head's mask, one bit per channel, from a bitwise search for
+// the r-th largest |q_d| with ballot counts).
+// ---------------------------------------------------------------------------
+template <int G, int NSUB>
+__global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
+  constexpr int EL = 2, D = 128, RB = D * EL, TS = 64, SUBB = TS * RB, QB = G * D * EL, NC = 2 * G;
+  static_assert(NC <= 16 && NSUB <= 3, "exact and reduced columns fit one 16-column tile; ring offsets fit");
+  __shared__ __attribute__((aligned(16))) char smem[NSUB * SUBB];
+  __shared__ __attribute__((aligned(16))) char qs[QB];
+  __shared__ __attribute__((aligned(16))) float lgs[2][TS][NC];  // a sub-chunk's scores, two buffers
+  __shared__ __attribute__((aligned(16))) uint64_t s_mask[G][2];
+  __shared__ float sm_ml[4][G][2];
+  __shared__ __attribute__((aligned(16))) PendLds pd;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int U = a.n_units;
+  const int hp_bend = a.hp.base[lane + 1], hp_len = a.hp.L[lane];
+  Plan pl;
+  if (a.hp.n) {
+    pl = host_plan(a, blockIdx.x, hp_bend, hp_len);
+  } else {
+    pl = wave_plan(a, blockIdx.x, (int)gridDim.x - U, blockIdx.x == 0 && wave == 0);
+    asm volatile("" ::"v"(hp_bend), "v"(hp_len));
+  }
+  if (!pl.valid) {
+    if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
+    return;
+  }
+  const int u = pl.u, b = u / a.Hkv, j = u - b * a.Hkv;
+  const int Lold = pl.L - 1, t0 = pl.t0, t1 = pl.t1;
+  const int tile = blockIdx.x;
+  const char *kc = static_cast<const char *>(a.k_cache) + (size_t)u * a.cap * RB;
+  const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
+  float *lgr = a.ws.logits + (size_t)u * a.cap * G;   // reduced
+  float *lge = a.ws.logits2 + (size_t)u * a.cap * G;  // exact
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // (see k_attend_mfma)
+  if (wave == 0) pend_fetch(a, u, pd, lane);
+  int dead = -1;
+  {
+    const int off = wave * 1024 + lane * 16;
+    const char *qsrc = static_cast<const char *>(a.q) + (size_t)(b * a.Hq + j * G) * D * EL;
+    if (off < QB) dma16(qsrc + off, qs + wave * 1024);
+  }
+  const float cs = a.scale_log2, tau = 8.f / cs;
+  const int hl = lane & 15, qd = lane >> 4;
+  uint32_t ad[8];
+  {
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ad[ks] = base + swz_off(wave * 16 + hl, 16 * ks + 4 * qd);
+  }
+  const uint32_t lgs_a = lds_addr(&lgs[0][0][0]);
+  float m = -INFINITY, l = 0.f;  // column hl: running maximum (raw) and this lane's partial sum
+  bf16x4_t qb[8];
+  const bool loader = wave >= 2;
+  const int nsc = (t1 - t0 + TS - 1) / TS;
+  if (loader) {
+#pragma unroll
+    for (int sc = 0; sc < NSUB; ++sc) {
+      if (sc < nsc) {
+        const int c0 = t0 + sc * TS;
+        stage_k_by<2>(smem + sc * SUBB, kc, kn, c0, min(TS, t1 - c0), t0, Lold, wave - 2, lane);
+      }
+    }
+  }
+  // Waves 0 and 1: the scores of sub-chunk ip (rows [32 w, 32 w + 32)) to
+  // both logit arrays, coalesced write-through stores.
+  auto store_logits = [&](int ip) {
+    const int c0p = t0 + ip * TS, nr = min(TS, t1 - c0p);
+    const uint32_t src = lgs_a + (uint32_t)((ip & 1) * TS * NC) * 4u;
+#pragma unroll
+    for (int q0 = 0; q0 < 32 * G; q0 += kWave) {
+      const int qq = q0 + lane, row = 32 * wave + qq / G, g = qq % G;
+      const int rc = min(row, TS - 1);  // (lanes past the 32 G values read a valid row, unused)
+      const float xe = lds_read_f32(src + (uint32_t)(rc * NC + g) * 4u);
+      const float xr = lds_read_f32(src + (uint32_t)(rc * NC + G + g) * 4u);
+      if (qq < 32 * G && row < nr) {
+        store_agent_f(lge + (size_t)(c0p + row) * G + g, xe);
+        store_agent_f(lgr + (size_t)(c0p + row) * G + g, xr);
+      }
+    }
+  };
+  for (int i = 0; i < nsc; ++i) {
+    const int c0 = t0 + i * TS, bsel = i % NSUB;
+    if (loader) {
+      const int ahead = min(nsc, NSUB + max(0, i - 1)) - (i + 1);
+      vm_wait_ahead<16 / 2, NSUB - 1>(ahead);
+    } else if (i == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // q and the candidates (no store issued yet)
+      if (wave == 0) pend_resolve(a, u, pd, lane, t0 == 0);
+    }
+    // Every wave's rows of sub-chunk i are in, every wave is done with
+    // i - 1, and the scores of i - 1 are in LDS.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (i == 0) {
+      dead = pend_read(pd);
+      // (q is in LDS: waves 0 and 1, which issued its loads, waited for them
+      // before the barrier)
+      {
+        // The channels of heads g = wave, wave + 4: r largest |q_d|, ties to
+        // the lower channel; lane l holds channels l and l + 64.  |q| of a
+        // bf16 q has its low 16 fp32 bits zero: bits 30 .. 16 are searched.
+        for (int g = wave; g < G; g += 4) {
+          uint32_t x0, x1;
+          lds_read_u16x2(x0, x1, lds_addr(qs + (g * D + lane) * EL), lds_addr(qs + (g * D + lane + 64) * EL));
+          const uint32_t a0 = (x0 << 16) & 0x7FFFFFFFu, a1 = (x1 << 16) & 0x7FFFFFFFu;  // |q| as fp32 bits
+          uint32_t thr = 0;
+          for (int bit = 30; bit >= 16; --bit) {
+            const uint32_t c = thr | (1u << bit);
+            if (__popcll(__ballot(a0 >= c)) + __popcll(__ballot(a1 >= c)) >= a.r) thr = c;
+          }
+          const bool g0 = a0 > thr, g1 = a1 > thr;
+          const int need = a.r - __popcll(__ballot(g0)) - __popcll(__ballot(g1));
+          const uint64_t e0 = __ballot(a0 == thr), e1 = __ballot(a1 == thr);
+          const uint64_t below = (1ull << lane) - 1ull;
+          const bool s0 = g0 || (a0 == thr && __popcll(e0 & below) < need);
+          const bool s1 = g1 || (a1 == thr && __popcll(e0) + __popcll(e1 & below) < need);
+          const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
+          if (lane == 0) {  // (asm: a compiler-visible LDS store would wait for the ring)
+            asm volatile("ds_write_b64 %0, %1" ::"v"(lds_addr(&s_mask[g][0])), "v"(m0) : "memory");
+            asm volatile("ds_write_b64 %0, %1" ::"v"(lds_addr(&s_mask[g][1])), "v"(m1) : "memory");
+          }
+          if (a.dbg_channels && t0 == 0) {  // the chosen channels, ascending
+            int32_t *dc = a.dbg_channels + ((size_t)b * a.Hq + j * G + g) * a.r;
+            if (s0) dc[__popcll(m0 & below)] = lane;
+            if (s1) dc[__popcll(m0) + __popcll(m1 & below)] = lane + 64;
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the masks
+      // B operands: column hl < G the query of head hl; G <= hl < 2G the
+      // query of head hl - G with the unchosen channels zeroed; others zero.
+      const int gh = hl < G ? hl : (hl < NC ? hl - G : 0);
+      uint64_t w[8];
+      lds_read8_b64(w, lds_addr(qs + (gh * D + 4 * qd) * EL));
+      const uint64_t mlo = lds_read_u64(lds_addr(&s_mask[gh][0])), mhi = lds_read_u64(lds_addr(&s_mask[gh][1]));
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int c = 16 * ks + 4 * qd;  // the lane's four channels c .. c + 3
+        const uint32_t nib = (uint32_t)(((c < 64 ? mlo : mhi) >> (c & 63)) & 0xFull);
+        uint64_t keep = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((nib >> e) & 1u) keep |= 0xFFFFull << (16 * e);
+        if (hl < G) keep = ~0ull;
+        else if (hl >= NC) keep = 0;
+        qb[ks] = __builtin_bit_cast(bf16x4_t, w[ks] & keep);
+      }
+    }
+    if (loader && i >= 1 && i + NSUB - 1 < nsc) {
+      const int cr = t0 + (i + NSUB - 1) * TS, br = (i - 1) % NSUB;
+      stage_k_by<2>(smem + br * SUBB, kc, kn, cr, min(TS, t1 - cr), t0, Lold, wave - 2, lane);
+    }
+    if (!loader && i >= 1) store_logits(i - 1);
+    uint64_t rd[8];
+    if (bsel == 0) mfma_k_operands<0>(rd, ad);
+    else if (bsel == 1) mfma_k_operands<SUBB>(rd, ad);
+    else mfma_k_operands<2 * SUBB>(rd, ad);
+    // lane (qd, hl): column hl of tokens 4 qd + 0..3 of the wave's rows
+    f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) S = mfma16(__builtin_bit_cast(bf16x4_t, rd[ks]), qb[ks], S);
+    const int nrows = min(TS, t1 - c0);
+    float sv[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row = wave * 16 + 4 * qd + r4;
+      sv[r4] = (row < nrows && c0 + row != dead) ? S[r4] : -INFINITY;
+    }
+    if (hl < NC) {
+      const uint32_t dst = lgs_a + (uint32_t)(((i & 1) * TS + wave * 16 + 4 * qd) * NC + hl) * 4u;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) lds_write_b32(dst + (uint32_t)(r4 * NC) * 4u, sv[r4]);
+    }
+    // Softmax statistics per column (the reduced columns are kept): one
+    // running maximum per wave, moved when the scores pass it by 8 / cs.
+    float mx = fmaxf(fmaxf(m, fmaxf(sv[0], sv[1])), fmaxf(sv[2], sv[3]));
+    {
+      float w2 = mx;
+      permlane16_swap(mx, w2);
+      mx = fmaxf(mx, w2);
+      w2 = mx;
+      permlane32_swap(mx, w2);
+      mx = fmaxf(mx, w2);
+    }
+    if (__ballot(mx > m + tau) != 0ull) {
+      const float corr = (mx == -INFINITY) ? 1.f : fast_exp2((m - mx) * cs);
+      l *= corr;
+      m = mx;
+    }
+    const float mc = (m == -INFINITY) ? 0.f : m * cs;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) l += fast_exp2(fmaf(sv[r4], cs, -mc));
+    asm volatile("" : "+v"(m), "+v"(l));
+    sched_fence();
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (!loader && nsc > 0) store_logits(nsc - 1);
+  // Tile partial of the reduced columns: l over the column's lanes, then the
+  // four waves (token groups) combined.
+  {
+    float w2 = l;
+    permlane16_swap(l, w2);
+    l += w2;
+    w2 = l;
+    permlane32_swap(l, w2);
+    l += w2;
+  }
+  if (qd == 0 && hl >= G && hl < NC) {
+    sm_ml[wave][hl - G][0] = m;
+    sm_ml[wave][hl - G][1] = l;
+  }
+  lds_barrier();
+  if (tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[w][tid][0]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Ls += sm_ml[w][tid][1] * fast_exp2((sm_ml[w][tid][0] - Ms) * cs);
+    store_agent_f(a.ws.part_ml + ((size_t)tile * G + tid) * 2, M);
+    store_agent_f(a.ws.part_ml + ((size_t)tile * G + tid) * 2 + 1, Ls);
+  }
+  if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
+}
+
+// ---------------------------------------------------------------------------
 // K2: per unit, importance blocks (softmax statistics, importance, eviction,
 // placement of the new token) and output blocks (one 64-output chunk each).
 // ---------------------------------------------------------------------------
@@ -637,11 +881,354 @@ __device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 
   Llane = lanes_sum<G>(L);
 }
 
-template <int EL, int D, int G>
+// ---------------------------------------------------------------------------
+// Stage II's output for head g of unit u (an output block of the second
+// launch, bf16 V, D = 128): of the live tokens (the dead slot of a pending
+// eviction is not one), the k_T with the largest reduced logit, ties to the
+// lower position (key: the logit's order bits, then the complemented
+// position); then their exact softmax and P.V.  The new token (slot L - 1)
+// has position new_pos[b] and its V row in v_new (the importance blocks of
+// the same launch write it into the cache).
+//
+// Selection.  Units of up to kS2Wave tokens (the steady state): every key
+// goes to LDS and wave 0 alone finds the threshold -- a histogram of the
+// keys' top 11 bits, the bin holding the k_T-th largest, and a bitwise
+// search over the low 53 bits of that bin's keys (gathered in LDS, 1024 at
+// most) -- with no workgroup barrier in between.  Longer units, or a bin
+// with more keys: radix passes of 8 bits from the top over the workgroup.
+// Keys of the first kS2Kr * kT2 tokens stay in registers; longer units
+// recompute the rest from the logits each pass.
+// ---------------------------------------------------------------------------
+constexpr int kS2Kr = 2;
+constexpr int kS2List = kS2TwoMaxTokens;  // selected tokens listed in LDS
+constexpr int kS2Wave = kS2Kr * kT2;      // units up to this many tokens: the histogram selection
+static_assert(kS2List * 8 <= 16384 && kS2Wave * 8 <= 16384, "the list and the keys share a 16 KB buffer");
+
+template <int G>
+__device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, int L, int dead, int newest,
+                                             bool skip) {
+  constexpr int D = 128, RB = 256, NW = kNW2;
+  __shared__ uint32_t h[256];
+  __shared__ __attribute__((aligned(16))) float s2red[NW][D + 8];  // P.V partials; the selection's histogram before
+  __shared__ __attribute__((aligned(16))) char s_buf[16384];   // the keys, then the list of selected tokens
+  __shared__ float s_pm[NW], s_ps[NW];
+  __shared__ uint64_t s_T;
+  __shared__ int s_d, s_need, s_cnt, s_fall;
+  __shared__ uint64_t s_bm[kS2Kr * NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = u / a.Hkv, j = u - b * a.Hkv, hq = j * G + g;
+  float *outp = a.out + ((size_t)b * a.Hq + hq) * D;
+  if (skip) {  // a unit the step leaves alone
+    if (tid < D) outp[tid] = 0.f;
+    if (a.dbg_count && tid == 0) a.dbg_count[(size_t)b * a.Hq + hq] = 0;
+    return;
+  }
+  const float *lgr = a.ws.logits + (size_t)u * a.cap * G + g;
+  const float *lge = a.ws.logits2 + (size_t)u * a.cap * G + g;
+  const int32_t *posw = a.pos + (size_t)u * a.cap;
+  const int Lold = L - 1;
+  // (loads from clamped addresses, then selects: a load under a condition
+  // makes the compiler wait for it where the paths meet)
+  auto key_of = [&](int n) -> uint64_t {
+    const int nc = min(n, Lold);
+    const float lv = lgr[(size_t)nc * G];
+    const int pv = posw[nc];
+    const int p = n == Lold ? newest : pv;
+    const bool live_n = n < L && n != dead;
+    return live_n ? (((uint64_t)ord_f32(lv) << 32) | (uint64_t)(~(uint32_t)p)) : 0ull;
+  };
+  uint64_t kr[kS2Kr];
+  float er[kS2Kr];
+#pragma unroll
+  for (int i = 0; i < kS2Kr; ++i) {
+    const int n = tid + i * kT2;
+    kr[i] = key_of(n);
+    er[i] = lge[(size_t)min(n, Lold) * G];
+  }
+  const int live = L - (dead >= 0 && dead < L ? 1 : 0);
+  const int kT = min(a.kT, live);
+  const bool all = kT >= live;  // every live token
+  uint64_t T = 1ull;            // selected: key >= T (keys are distinct)
+  bool radix = !all && L > kS2Wave;
+  if (!all && L <= kS2Wave) {
+    // Keys in registers cover the unit (L <= kS2Kr * kT2).  A histogram of
+    // their top 11 bits (padded: bin b at word b + b / 32, so that a lane's
+    // 32 consecutive bins sit in distinct banks), the bin holding the kT-th
+    // largest (wave 0), that bin's keys gathered (128 at most), and a bitwise
+    // search over their low 53 bits in registers, counted by ballots (wave 0).
+    static_assert(kS2Wave <= kS2Kr * kT2, "the keys of a unit fit the registers");
+    uint32_t *h2 = reinterpret_cast<uint32_t *>(&s2red[0][0]);          // 2112 words
+    uint64_t *cand = reinterpret_cast<uint64_t *>(s_buf);                 // 128 keys
+    auto pidx = [](int bin) { return bin + (bin >> 5); };
+    for (int i = tid; i < 2112; i += kT2) h2[i] = 0u;
+    if (tid == 0) s_fall = 0, s_cnt = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kS2Kr; ++i) {
+      const uint64_t key = kr[i];
+      const int d = key ? (int)(key >> 53) : 2048;
+      const int d0 = __builtin_amdgcn_readfirstlane(d);
+      const uint64_t same = __ballot(d == d0);
+      if (d == d0) {
+        if (d0 < 2048 && lane == __builtin_ctzll(same)) atomicAdd(&h2[pidx(d0)], (uint32_t)__popcll(same));
+      } else if (d < 2048) {
+        atomicAdd(&h2[pidx(d)], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l: bins 2047 - 32 l down to 2016 - 32 l; the lane whose range
+      // holds the kT-th largest, then that range's bins one per lane
+      uint32_t c = 0;
+#pragma unroll 8
+      for (int q = 0; q < 32; ++q) c += h2[pidx(2047 - 32 * lane - q)];
+      const uint32_t incl = wave_incl_scan_dpp(c), excl = incl - c;
+      const uint64_t lm = __ballot(excl < (uint32_t)kT && incl >= (uint32_t)kT);
+      const int lt = lm ? __builtin_ctzll(lm) : 0;
+      const uint32_t ex_t = __shfl(excl, lt);
+      const uint32_t hb = lane < 32 ? h2[pidx(2047 - 32 * lt - lane)] : 0u;
+      const uint32_t in2 = wave_incl_scan_dpp(hb) + ex_t, ex2 = in2 - hb;
+      const uint64_t qm = __ballot(lane < 32 && ex2 < (uint32_t)kT && in2 >= (uint32_t)kT);
+      const int qq = qm ? __builtin_ctzll(qm) : 0;
+      const int cntb = (int)__shfl(hb, qq), exq = (int)__shfl(ex2, qq);  // (every lane of the wave)
+      if (lane == 0) {
+        const bool ok = lm && qm;
+        s_d = ok ? 2047 - 32 * lt - qq : -1;
+        s_need = kT - exq;
+        s_fall = !ok || cntb > 128;
+        s_T = (uint64_t)(ok ? 2047 - 32 * lt - qq : 0) << 53;  // the whole bin, unless refined below
+      }
+    }
+    __syncthreads();
+    const int bin = s_d, needb = s_need;
+    radix = s_fall != 0;
+    if (!radix) {
+      // the bin's keys, gathered (one atomic per wave)
+#pragma unroll
+      for (int i = 0; i < kS2Kr; ++i) {
+        const uint64_t key = kr[i];
+        const bool in = key && (int)(key >> 53) == bin;
+        const uint64_t mk = __ballot(in);
+        int base = 0;
+        if (lane == 0 && mk) base = atomicAdd(&s_cnt, __popcll(mk));
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (in) cand[base + __popcll(mk & ((1ull << lane) - 1ull))] = key;
+      }
+      __syncthreads();
+      const int nc = s_cnt;
+      // the needb-th largest of the bin's keys: the one with needb - 1 larger
+      // (keys are distinct)
+      if (needb < nc && tid < nc) {
+        const uint64_t c = cand[tid];
+        int rank = 0;
+        for (int i = 0; i < nc; ++i) rank += cand[i] > c;
+        if (rank == needb - 1) s_T = c;
+      }
+      __syncthreads();
+      T = s_T;
+    }
+  }
+  if (radix) {
+    // The kT-th largest key by 8-bit radix passes from the top over the
+    // whole workgroup; need = how many of the keys under the current prefix
+    // are still to take.
+    uint64_t prefix = 0;
+    int rem = 64, need = kT;
+    while (rem > 0) {
+      const int sh = rem - 8;
+      if (tid < 256) h[tid] = 0u;
+      __syncthreads();
+      auto count = [&](uint64_t key) {
+        const bool in = key != 0ull && (rem == 64 || (key >> rem) == (prefix >> rem));
+        const int d = in ? (int)((key >> sh) & 255ull) : 256;
+        const int d0 = __builtin_amdgcn_readfirstlane(d);
+        const uint64_t same = __ballot(d == d0);
+        if (d == d0) {
+          if (d0 < 256 && lane == __builtin_ctzll(same)) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+        } else if (d < 256) {
+          atomicAdd(&h[d], 1u);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < kS2Kr; ++i) count(kr[i]);
+      for (int n = tid + kS2Kr * kT2; n < L; n += kT2) count(key_of(n));
+      __syncthreads();
+      if (wave == 0) {
+        // lane l: digits 255 - 4 l ... 252 - 4 l (descending); the digit at
+        // which the count from the top reaches need
+        const uint32_t c0 = h[255 - 4 * lane], c1 = h[254 - 4 * lane], c2 = h[253 - 4 * lane],
+                       c3 = h[252 - 4 * lane];
+        const uint32_t s4 = c0 + c1 + c2 + c3;
+        const uint32_t incl = wave_incl_scan_u32(s4), excl = incl - s4, want = (uint32_t)need;
+        if (excl < want && incl >= want) {
+          const uint32_t a1 = excl + c0, a2 = a1 + c1, a3 = a2 + c2;
+          const int q = a1 >= want ? 0 : (a2 >= want ? 1 : (a3 >= want ? 2 : 3));
+          const uint32_t above = q == 0 ? excl : (q == 1 ? a1 : (q == 2 ? a2 : a3));
+          s_d = 255 - 4 * lane - q;
+          s_need = need - (int)above;
+          s_cnt = (int)(q == 0 ? c0 : (q == 1 ? c1 : (q == 2 ? c2 : c3)));
+        }
+      }
+      __syncthreads();
+      prefix |= (uint64_t)s_d << sh;
+      rem = sh;
+      need = s_need;
+      if (need == s_cnt) break;  // the whole digit is taken: prefix, lower bits 0, is the threshold
+      __syncthreads();
+    }
+    T = prefix;
+  }
+  auto sel = [&](uint64_t key) { return key != 0ull && key >= T; };
+
+  // Exact softmax over the selected tokens: the maximum over the wave, each
+  // thread's sum relative to it and the wave's, then the waves' pairs merged.
+  const float cs = a.scale_log2;
+  float tm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kS2Kr; ++i)
+    if (sel(kr[i])) tm = fmaxf(tm, er[i]);
+  for (int n = tid + kS2Kr * kT2; n < L; n += kT2)
+    if (sel(key_of(n))) tm = fmaxf(tm, lge[(size_t)n * G]);
+  const float wm = wave_max_dpp(tm);
+  const float wms = (wm == -INFINITY) ? 0.f : wm * cs;
+  float ts_ = 0.f;
+#pragma unroll
+  for (int i = 0; i < kS2Kr; ++i)
+    if (sel(kr[i])) ts_ += fast_exp2(fmaf(er[i], cs, -wms));
+  for (int n = tid + kS2Kr * kT2; n < L; n += kT2)
+    if (sel(key_of(n))) ts_ += fast_exp2(fmaf(lge[(size_t)n * G], cs, -wms));
+  const float wsum = wave_sum_dpp(ts_);
+  if (lane == 0) s_pm[wave] = wm, s_ps[wave] = wsum;  // (published by the list's barriers)
+
+  // The selected tokens and their exact logits into an LDS list, in token
+  // order (the P.V sums then repeat bit for bit): per chunk of kS2Kr * kT2
+  // tokens, a bitmap of the selected ones (one ballot per 64 tokens), then
+  // each token's place from the bits before it.  The two-launch path is
+  // taken for k_T <= kS2List only.
+  int *s_list = reinterpret_cast<int *>(s_buf);
+  float *s_e = reinterpret_cast<float *>(s_buf + kS2List * 4);
+  constexpr int CW = kS2Kr * NW;  // bitmap words per chunk
+  int done = 0;
+  for (int c0 = 0; c0 < L; c0 += kS2Kr * kT2) {
+    bool tk[kS2Kr];
+    float ek[kS2Kr];
+#pragma unroll
+    for (int i = 0; i < kS2Kr; ++i) {
+      const int n = c0 + tid + i * kT2;
+      const uint64_t key = c0 == 0 ? kr[i] : key_of(n);
+      tk[i] = n < L && sel(key);
+      ek[i] = c0 == 0 ? er[i] : lge[(size_t)min(n, Lold) * G];
+      const uint64_t m = __ballot(tk[i]);
+      if (lane == 0) s_bm[i * NW + wave] = m;
+    }
+    __syncthreads();
+    // exclusive prefix of the words' counts: lane l < CW holds word l
+    const uint32_t wc = lane < CW ? (uint32_t)__popcll(s_bm[lane]) : 0u;
+    const uint32_t wi = wave_incl_scan_dpp(wc), we = wi - wc;
+#pragma unroll
+    for (int i = 0; i < kS2Kr; ++i) {
+      const int w = i * NW + wave;
+      const uint64_t m = s_bm[w];
+      const int pos = done + (int)__builtin_amdgcn_readlane(we, w) + __popcll(m & ((1ull << lane) - 1ull));
+      if (tk[i] && pos < kS2List) {
+        s_list[pos] = c0 + tid + i * kT2;
+        s_e[pos] = ek[i];
+      }
+    }
+    done += (int)__builtin_amdgcn_readlane(wi, CW - 1);
+    __syncthreads();  // the list so far (and s_bm is free again)
+  }
+  float pm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) pm = fmaxf(pm, s_pm[w]);
+  const float Ms = (pm == -INFINITY) ? 0.f : pm * cs;
+  float ps = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ps += s_ps[w] * fast_exp2(fmaf(s_pm[w], cs, -Ms));
+  const float inv = 1.f / ps;
+  const int nsel = min(done, kS2List);
+
+  // P.V: 16 lanes per V row (8 channels each), 64 rows at a time; group q
+  // takes list entries q, q + 64, ... (four rows in flight).
+  const int grp = tid >> 4, cl = tid & 15;
+  const char *vc = static_cast<const char *>(a.v_cache) + (size_t)u * a.cap * RB + cl * 16;
+  const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB + cl * 16;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add_row = [&](const uint4 &v4, float p) {
+    const uint32_t w4[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(p, __uint_as_float(w4[e] << 16), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(p, __uint_as_float(w4[e] & 0xFFFF0000u), acc[2 * e + 1]);
+    }
+  };
+  constexpr int GS = kT2 / 16;  // row groups
+  for (int i0 = grp; i0 < nsel; i0 += 4 * GS) {
+    int nn[4];
+    float pp[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r * GS;
+      nn[r] = i < nsel ? s_list[i] : -1;
+      pp[r] = i < nsel ? fast_exp2(fmaf(s_e[i], cs, -Ms)) * inv : 0.f;
+    }
+    const uint4 v0 = *reinterpret_cast<const uint4 *>(nn[0] == Lold ? vn : vc + (size_t)max(nn[0], 0) * RB);
+    const uint4 v1 = *reinterpret_cast<const uint4 *>(nn[1] == Lold ? vn : vc + (size_t)max(nn[1], 0) * RB);
+    const uint4 v2 = *reinterpret_cast<const uint4 *>(nn[2] == Lold ? vn : vc + (size_t)max(nn[2], 0) * RB);
+    const uint4 v3 = *reinterpret_cast<const uint4 *>(nn[3] == Lold ? vn : vc + (size_t)max(nn[3], 0) * RB);
+    add_row(v0, pp[0]);
+    add_row(v1, pp[1]);
+    add_row(v2, pp[2]);
+    add_row(v3, pp[3]);
+  }
+  // the four groups of a wave (lanes 16 apart: permlane swaps), then the waves
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float w2 = acc[e];
+    permlane16_swap(acc[e], w2);
+    acc[e] += w2;
+    w2 = acc[e];
+    permlane32_swap(acc[e], w2);
+    acc[e] += w2;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s2red[wave][cl * 8 + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) o += s2red[w][tid];
+    outp[tid] = o;
+  }
+  if (a.dbg_count && tid == 0) a.dbg_count[(size_t)b * a.Hq + hq] = kT;
+  if (a.dbg_tokens) {
+    // the selected positions, ascending, -1 padded (debug only: each
+    // selected token is ranked by counting)
+    int32_t *dt = a.dbg_tokens + ((size_t)b * a.Hq + hq) * a.kT;
+    for (int i = tid; i < a.kT; i += kT2) dt[i] = -1;
+    __syncthreads();
+    for (int n = tid; n < L; n += kT2) {
+      const uint64_t kn_ = key_of(n);
+      if (!sel(kn_)) continue;
+      const uint32_t pn = ~(uint32_t)kn_;
+      int rank = 0;
+      for (int m2 = 0; m2 < L; ++m2) {
+        const uint64_t km = key_of(m2);
+        rank += sel(km) && (~(uint32_t)km) < pn;
+      }
+      if (rank < a.kT) dt[rank] = (int32_t)pn;
+    }
+  }
+}
+
+template <int EL, int D, int G, bool S2 = false>
 __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k_finalize(StepArgs a) {
   constexpr int RB = D * EL, NR = RB / 16, GD = G * D;
   constexpr int NB = K2Lay<G>::NB, CHUNK = K2Lay<G>::CHUNK;
-  constexpr int NOC = k2_noc<EL, D, G>();
+  // output blocks per unit: Stage I one per 64 outputs, Stage II one per head
+  constexpr int NOC = S2 ? G : k2_noc<EL, D, G>();
   constexpr int NTW = 8;  // tiles per wave loaded in one batch by an output block
   __shared__ float red[kNW2][G], red2[kNW2][G];
   __shared__ float sm_m[kMaxGrid];           // output blocks: tile maxima of their head
@@ -711,7 +1298,10 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     [&]() __attribute__((always_inline)) {
       // ---------------- importance block ----------------
       const int newest = ld_vec(a.new_pos + b, vz);
-      const int beta_ld = ld_opaque(a.budget ? a.budget + u : a.new_pos + b, vz);
+      // (the Stage II instance loads it plainly: there the pointer is not kept
+      // in scalar registers, which the opaque load's constraint requires)
+      const int *bp = a.budget ? a.budget + u : a.new_pos + b;
+      const int beta_ld = S2 ? ld_vec(bp, vz) : ld_opaque(bp, vz);
       const float2 v0 = pml[min(tid, npair - 1)];
       const char *kn = static_cast<const char *>(a.k_new) + (size_t)u * RB;
       const char *vn = static_cast<const char *>(a.v_new) + (size_t)u * RB;
@@ -769,8 +1359,10 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       const bool bulk = n_evict > 1;
       // With the caller's lengths a bulk cut is spread over the unit's blocks
       // (each leaves its keys and a histogram of them; k_bulk_select finishes
-      // the cut); without them one block takes every token.
-      const bool split = bulk && a.bulk_split;
+      // the cut); without them one block takes every token.  Stage II always
+      // spreads it: its output blocks read V rows, which must not move during
+      // this launch.
+      const bool split = bulk && (a.bulk_split || S2);
       if (bulk && !split && r > 0) return;
       const int nb1 = (bulk && !split) ? L : min(L, nb0 + CHUNK);
       const int nact = (L + CHUNK - 1) / CHUNK;  // blocks holding tokens of the unit
@@ -914,6 +1506,13 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     }();
     end_wave();
   }
+  if constexpr (S2) {
+    // ---------------- Stage II output block: head r - nib ----------------
+    const int beta = a.budget ? ld_vec(a.budget + u, vz) : a.budget_all;
+    const int dead = ld_vec(unit_state(a, u) + 1, vz);
+    const int newest = ld_vec(a.new_pos + b, vz);
+    s2_out_block<G>(a, u, r - nib, L, dead, newest, a.hp.n && (L > a.cap || beta < S || beta > a.cap));
+  } else {
   // ---------------- output block: chunk c of the unit's G*D outputs ----
   const int beta_ld = ld_opaque(a.budget ? a.budget + u : a.new_pos + b, vz);
   const float2 v0 = pml[min(tid, npair - 1)];
@@ -947,6 +1546,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
     float sum = 0.f;
     for (int w = 0; w < kNW2; ++w) sum += red_o[w][lane];
     outu[o] = sum / Lo;
+  }
   }
 
   end_wave();
@@ -1262,13 +1862,14 @@ hipError_t launch_settle(const StepArgs &a, int dtype, int32_t *slot_out, bool a
 // D = 128, vector ALUs otherwise.
 template <int EL, int D, int G>
 static constexpr bool use_mfma() { return EL == 2 && D == 128; }
-template <int EL, int D, int G>
+template <int EL, int D, int G, bool S2 = false>
 static void (*attend_kernel())(StepArgs) {
-  if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G, 3>;
+  if constexpr (S2) return k_attend_s2<G, 3>;
+  else if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G, 3>;
   else return k_attend<EL, D, G>;
 }
 
-template <int EL, int D, int G>
+template <int EL, int D, int G, bool S2 = false>
 static int attend_grid(int n_units) {
   static int per_cu_cache[64];
   int dev = 0;
@@ -1276,7 +1877,8 @@ static int attend_grid(int n_units) {
   int &pc = per_cu_cache[dev];
   if (pc == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<EL, D, G>(), kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<EL, D, G, S2>(), kThreads, 0) !=
+        hipSuccess)
       return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     pc = per_cu * cus;
@@ -1324,8 +1926,52 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   return hipSuccess;
 }
 
+// Stage II in two launches (bf16, D = 128): the attention launch over K, the
+// second launch (importance blocks and one output block per head), and the
+// bulk cut's select and moves when some unit is cut in bulk.
+template <int G>
+static hipError_t step_go_s2(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr int EL = 2, D = 128;
+  const int g = attend_grid<EL, D, G, true>(a.n_units);
+  if (g <= 0) return hipErrorInvalidValue;
+  hipError_t e;
+  void (*kern)(StepArgs) = attend_kernel<EL, D, G, true>();
+  if (ev0 && ev1) hipExtLaunchKernelGGL(kern, dim3(g), dim3(kThreads), 0, s, ev0, ev1, 0, a);
+  else hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int nib = imp_blocks(a.cap);
+  if (a.hp.n) {
+    int mx = 1;
+    for (int u = 0; u < a.hp.n; ++u) mx = max(mx, a.hp.L[u]);
+    nib = min(nib, (mx + kImpChunk - 1) / kImpChunk);
+  }
+  hipLaunchKernelGGL((k_finalize<EL, D, G, true>), dim3((unsigned)a.n_units, (unsigned)(nib + G)), dim3(kT2), 0, s,
+                     a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.bulk_split) {
+    hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int per = bulk_moves_per_block<D * EL>();
+    const unsigned gy = (unsigned)max(1, (a.bulk_rows + per - 1) / per);
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, gy), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
 template <int EL, int D>
 static hipError_t step_g(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if constexpr (EL == 2 && D == 128) {
+    if (a.s2_two) {
+      switch (a.G) {
+        case 1: return step_go_s2<1>(a, s, ev0, ev1);
+        case 2: return step_go_s2<2>(a, s, ev0, ev1);
+        case 4: return step_go_s2<4>(a, s, ev0, ev1);
+        case 8: return step_go_s2<8>(a, s, ev0, ev1);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   switch (a.G) {
     case 1: return step_go<EL, D, 1>(a, s, ev0, ev1);
     case 2: return step_go<EL, D, 2>(a, s, ev0, ev1);
@@ -1341,7 +1987,9 @@ template <int EL, int D, int G>
 static bool host_plan_fill(StepArgs &a, const int32_t *len_hint) {
   const int U = a.n_units;
   if (U > kHostPlanUnits) return false;
-  const int g = attend_grid<EL, D, G>(U);
+  int g = 0;
+  if constexpr (EL == 2 && D == 128) g = a.s2_two ? attend_grid<EL, D, G, true>(U) : attend_grid<EL, D, G>(U);
+  else g = attend_grid<EL, D, G>(U);
   if (g <= U) return false;
   long long tot = 0;
   for (int u = 0; u < U; ++u) tot += len_hint[u] + 1;

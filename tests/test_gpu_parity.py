@@ -213,8 +213,9 @@ def test_settle_applies_the_pending_eviction():
 
 @PATHS
 def test_stage2_step_after_pending_eviction(hint):
-    """A Stage II step on a cache whose last two-launch step left an eviction
-    pending settles it first: outputs and kept sets equal the oracle's."""
+    """A Stage II step on a cache whose last Stage I step left an eviction
+    pending takes the dead slot for its new token, as a Stage I step would:
+    outputs and kept sets equal the oracle's."""
     w = W.workload("llama8b", ctx=600, steps=3, batch=2)
     w.budget_all, w.n_recent = 128, 16
     d = W.generate(w)
@@ -252,7 +253,9 @@ def test_stage2_step_after_pending_eviction(hint):
             for j in range(w.n_kv_heads):
                 assert sorted(ref.live_positions(got, b, j).tolist()) == \
                     sorted(ref.live_positions(st, b, j).tolist()), (t, b, j)
-    assert (run.pending() == -1).all()               # the Stage II step settled and evicted in place
+    # the Stage II step (two launches for bf16 K with D = 128 and the exact
+    # top-k_T V side) also leaves its one-token eviction pending
+    assert (run.pending() >= 0).all()
 
 
 @PATHS
@@ -461,8 +464,11 @@ def test_prefill_scores_match_oracle(window, n_obs):
 
 
 @PATHS
-def test_repeat_step_is_bit_identical(hint):
-    w = W.workload("llama8b", ctx=700, steps=4, batch=2)
+@pytest.mark.parametrize("name", ["llama8b", "twostage"])
+def test_repeat_step_is_bit_identical(hint, name):
+    """The same steps on the same state give the same bytes (Stage I, and
+    Stage II with its selected tokens summed in token order)."""
+    w = W.workload(name, ctx=2500, steps=4, batch=2)
     w.budget_all, w.n_recent = 200, 16
     d = W.generate(w)
     outs, states = [], []
