@@ -158,11 +158,13 @@ typedef struct hikv_debug {
   void *attend_stop;       /* attention launch records when it starts and ends executing (Stage I: the
                               launch over every live K and V row; Stage II: the reduced-channel logits
                               pass over every live K row) */
-  int32_t stage1_path;     /* Stage I launch sequence: HIKV_PATH_AUTO (the library's choice) or
-                              HIKV_PATH_MULTI_LAUNCH (settle, attention tiles, combine, accumulate
-                              and bulk eviction as separate launches, evicting in place; kept to
-                              compare against).  Results are the same on every path.  Any other
-                              value is HIKV_EINVAL. */
+  int32_t stage1_path;     /* launch sequence: HIKV_PATH_AUTO (the library's choice) or
+                              HIKV_PATH_MULTI_LAUNCH (Stage I: settle, attention tiles, combine,
+                              accumulate and bulk eviction as separate launches; Stage II: channel
+                              select, reduced-logit tiles, selection and exact pass, accumulate
+                              and bulk eviction; both evicting in place; kept to compare
+                              against).  Results are the same on every path.  Any other value is
+                              HIKV_EINVAL. */
 } hikv_debug;
 
 #define HIKV_PATH_AUTO 0
@@ -194,7 +196,9 @@ size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
  *      pos > new_pos[b] - W') and the budget - |protected| other tokens with
  *      the highest (importance, then lower position); compact them into
  *      slots [0, budget); len[u] = budget.
- * Pending eviction (Stage I, r == 0): when step 4 evicts exactly one token,
+ * Pending eviction (Stage I, r == 0; and Stage II with the exact top-k_T V
+ * side for bf16 K and V with D = 128 and k_T <= 2048, which runs in the same
+ * two launches): when step 4 evicts exactly one token,
  * the call leaves the choice of the victim to the next call and does not
  * compact: len[u] stays budget + 1, and one of those slots, the victim, is
  * dead (its row, position and importance are stale); the choice is kept in
@@ -202,9 +206,9 @@ size_t hikv_workspace_bytes(const hikv_shape *shape, const hikv_policy *policy);
  * neither attends to it nor counts it, and writes its new token there; a bulk
  * cut (more than one token over budget) removes it first.  hikv_settle()
  * resolves it (the cache then holds exactly the kept set, as in step 4) and
- * hikv_pending() reports the dead slot without changing anything; the Stage II
- * path and hikv_evict() settle first.  Results (out, the kept set once
- * settled) are those of step 4 in every case.  A unit whose budget + 2
+ * hikv_pending() reports the dead slot without changing anything; the other
+ * Stage II variants and hikv_evict() settle first and evict in place.
+ * Results (out, the kept set once settled) are those of step 4 in every case.  A unit whose budget + 2
  * exceeds the capacity therefore runs out of slots (HIKV_ECAPACITY) one call
  * after it reaches its budget.
  * q: [B][Hq][D]; k_new, v_new: [B][Hkv][D]; new_pos: [B] int32;
