@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhikv.so")
 SOURCES = ["api.hip", "decode.hip", "step.hip", "stage2.hip", "prefill.hip"]
+# measurement aids for the benchmark (a streaming read, an empty kernel): a
+# library of their own, not part of the decode path
+CALIB_LIB = os.path.join(PKG, "libhikv_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 ARCH = os.environ.get("HIKV_ARCH", "gfx950")
 
 CFLAGS = [
@@ -50,18 +54,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile, SOURCES + CALIB_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
         print(LIB)
+        print(CALIB_LIB)
     return LIB
 
 

@@ -179,6 +179,40 @@ def hikv_prefill_scores(shape, cache, q_obs, q_pos, n_obs, window, ws, stream=No
                                      window, pool, _p(ws), ws.numel() * ws.element_size(), _stream(stream))
 
 
+# ---------------------------------------------------------------------------
+# Measurement aids (include/hikv_calib.h, libhikv_calib.so): used by the
+# benchmark only, not part of the decode path.
+# ---------------------------------------------------------------------------
+CALIB_PATH = os.path.join(PKG, "libhikv_calib.so")
+CALIB_EXPORTS = ("hikv_calib_stream", "hikv_calib_empty")
+_calib = None
+
+
+def calib_lib():
+    global _calib
+    if _calib is None:
+        if not os.path.exists(CALIB_PATH):
+            raise LibraryMissing(f"{CALIB_PATH} is not built; run `python -m importance_aware_kv_amd.build`")
+        L = C.CDLL(CALIB_PATH)
+        vp = C.c_void_p
+        L.hikv_calib_stream.argtypes = [vp, vp, C.c_int64, C.c_int64, vp, C.c_int32, vp, vp, vp, vp]
+        L.hikv_calib_stream.restype = C.c_int
+        L.hikv_calib_empty.argtypes = [C.c_int32, vp]
+        L.hikv_calib_empty.restype = C.c_int
+        _calib = L
+    return _calib
+
+
+def hikv_calib_stream(k, v, cap, row_bytes, tiles, sink, ev_start=None, ev_stop=None, stream=None) -> int:
+    """tiles: device int32 [n][3] (unit, t0, t1); sink: device uint32-sized [n]."""
+    return calib_lib().hikv_calib_stream(_p(k), _p(v), cap, row_bytes, _p(tiles), tiles.shape[0], _p(sink),
+                                         ev_start, ev_stop, _stream(stream))
+
+
+def hikv_calib_empty(n, stream=None) -> int:
+    return calib_lib().hikv_calib_empty(n, _stream(stream))
+
+
 def hikv_device_status(ws, clear=True, stream=None) -> int:
     return lib().hikv_device_status(_p(ws), 1 if clear else 0, _stream(stream))
 

@@ -38,6 +38,27 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+CALIB_HEADER = os.path.join(ROOT, "include", "hikv_calib.h")
+
+
+def test_calibration_library_exports_its_header():
+    """The measurement aids (a streaming read, an empty kernel) are a library
+    of their own; argument checks return codes without a GPU."""
+    src = re.sub(r"/\*.*?\*/", "", open(CALIB_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(hikv_[a-z_]+)\s*\(", src)))
+    assert set(names) == set(H.CALIB_EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", H.CALIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (hikv_\w+)", out))
+    L = H.calib_lib()
+    fake = C.c_void_p(16)
+    assert L.hikv_calib_stream(None, fake, 64, 256, fake, 1, fake, None, None, None) == -1
+    assert L.hikv_calib_stream(fake, fake, 64, 100, fake, 1, fake, None, None, None) == -1   # row bytes % 16
+    assert L.hikv_calib_stream(fake, fake, 64, 256, fake, 1, fake, fake, None, None) == -1   # one event
+    assert L.hikv_calib_stream(fake, fake, 64, 256, fake, 0, fake, None, None, None) == 0    # nothing to do
+    assert L.hikv_calib_empty(-1, None) == -1
+
+
 def _shape(**kw):
     d = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, capacity=64, kv_dtype=H.HIKV_BF16,
              scale=0.0)
