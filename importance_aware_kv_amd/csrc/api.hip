@@ -183,6 +183,7 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
       // With host copies of the lengths and budgets, a step that cuts some
       // unit by more than one token moves its survivors in a launch of its own.
       if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
+        a.bulk_known = 1;
         const int U = shape->batch * shape->n_kv_heads;
         for (int u = 0; u < U; ++u) {
           const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;

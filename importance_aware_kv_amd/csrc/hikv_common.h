@@ -181,6 +181,7 @@ struct StepArgs {
   int32_t no_bulk;           // the host skipped the bulk-eviction launch (length hint): flag a unit that needed it
   int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit
   int32_t bulk_rows;         // with bulk_split: the host's bound on the rows any unit's cut moves
+  int32_t bulk_known;        // the host foresaw every bulk cut of the step (lengths and budgets known)
   int32_t s2_two;            // Stage II (exact top-k_T V side) in the two-launch sequence
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;

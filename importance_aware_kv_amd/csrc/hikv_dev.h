@@ -182,6 +182,12 @@ struct ALay {
   static constexpr int NI = SUBB / 4096;        // DMA instructions per wave per sub-chunk, K or V
 };
 
+// Cache policy of the K and V row loads: non-temporal.  A step reads every
+// live row once, and the rows of all the layers of a model far exceed the
+// caches; marked as streaming they do not push out the small per-token arrays
+// (importance, positions, logits) that the same layer's next step reads again.
+constexpr int kRowCpol = 2;
+
 // Stage one sub-chunk of K and V rows into LDS with the global->LDS DMA.
 // Every lane issues exactly NI loads for K and NI for V (constant vmcnt
 // bookkeeping); lanes past the tile read a clamped valid row into unused
@@ -203,8 +209,8 @@ __device__ __forceinline__ void stage_sub(char *kb, char *vb, const char *kc, co
     const int n = (row < nrows) ? c0 + row : t0;  // t0 is always a live row of the tile
     const char *ks = (n == Lold) ? kn + col : kc + (size_t)n * RB + col;
     const char *vs = (n == Lold) ? vn + col : vc + (size_t)n * RB + col;
-    __builtin_amdgcn_global_load_lds(ks, kb + ((i * 4 + wave) << 10), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vs, vb + ((i * 4 + wave) << 10), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ks, kb + ((i * 4 + wave) << 10), 16, 0, kRowCpol);
+    __builtin_amdgcn_global_load_lds(vs, vb + ((i * 4 + wave) << 10), 16, 0, kRowCpol);
   }
 }
 
@@ -224,8 +230,8 @@ __device__ __forceinline__ void stage_sub_by(char *kb, char *vb, const char *kc,
     const int n = (row < nrows) ? c0 + row : t0;  // t0 is always a live row of the tile
     const char *ks = (n == Lold) ? kn + col : kc + (size_t)n * RB + col;
     const char *vs = (n == Lold) ? vn + col : vc + (size_t)n * RB + col;
-    __builtin_amdgcn_global_load_lds(ks, kb + (piece << 10), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vs, vb + (piece << 10), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ks, kb + (piece << 10), 16, 0, kRowCpol);
+    __builtin_amdgcn_global_load_lds(vs, vb + (piece << 10), 16, 0, kRowCpol);
   }
 }
 
@@ -590,7 +596,7 @@ __device__ __forceinline__ void stage_k_by(char *kb, const char *kc, const char 
     const int col = (((off - row * RB) >> 4) ^ (row & 15)) << 4;
     const int n = (row < nrows) ? c0 + row : t0;  // t0 is always a live row of the tile
     const char *ks = (n == Lold) ? kn + col : kc + (size_t)n * RB + col;
-    __builtin_amdgcn_global_load_lds(ks, kb + (piece << 10), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ks, kb + (piece << 10), 16, 0, kRowCpol);
   }
 }
 
@@ -632,6 +638,11 @@ __device__ __forceinline__ void lds_read_u16x2(uint32_t &a, uint32_t &b, uint32_
 __device__ __forceinline__ uint64_t lds_read_u64(uint32_t addr) {
   uint64_t x;
   asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+  return x;
+}
+__device__ __forceinline__ uint4 lds_read_u128(uint32_t addr) {
+  uint4 x;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
   return x;
 }
 
@@ -685,6 +696,34 @@ __device__ __forceinline__ void vm_wait_ahead(int k) {
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Two 16x16x16 products summed by one 16x16x32 instruction: lane (qd, hl)
+// holds terms 8 qd .. 8 qd + 7 of the longer sum, here the terms of (a0, b0)
+// and then those of (a1, b1); a sum does not depend on which lane holds which
+// of its terms, so c + a0 b0 + a1 b1 comes out of one instruction.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4_t mfma32_2(bf16x4_t a0, bf16x4_t a1, bf16x4_t b0, bf16x4_t b1, f32x4_t c) {
+  const bf16x8_t a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  const bf16x8_t b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// q.k of a 16-row K operand (eight 4-channel pieces per lane) against the
+// queries: four 32-channel instructions in two independent chains (the K
+// pieces are rd[0..7]).
+template <int N>
+__device__ __forceinline__ f32x4_t qk16(const uint64_t (&rd)[N], const bf16x4_t (&qb)[8]) {
+  static_assert(N >= 8, "eight K pieces");
+  f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+  for (int j = 0; j < 4; j += 2) {
+    s0 = mfma32_2(__builtin_bit_cast(bf16x4_t, rd[2 * j]), __builtin_bit_cast(bf16x4_t, rd[2 * j + 1]), qb[2 * j],
+                  qb[2 * j + 1], s0);
+    s1 = mfma32_2(__builtin_bit_cast(bf16x4_t, rd[2 * j + 2]), __builtin_bit_cast(bf16x4_t, rd[2 * j + 3]),
+                  qb[2 * j + 2], qb[2 * j + 3], s1);
+  }
+  return s0 + s1;
 }
 
 

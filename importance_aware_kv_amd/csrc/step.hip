@@ -448,9 +448,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
       mfma_operands<0, SUBB>(rd, adb);
     }
     // q.k: lane (qd, hl) gets the raw scores of tokens 4 qd + i of its group for head hl.
-    f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) S = mfma16(__builtin_bit_cast(bf16x4_t, rd[ks]), qb[ks], S);
+    const f32x4_t S = qk16(rd, qb);
     const int nrows = min(TS, t1 - c0);
     float sv[4];
 #pragma unroll
@@ -528,8 +526,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bf16x4_t vb4 = __builtin_bit_cast(bf16x4_t, rd[8 + t]);
-      O[t] = mfma16(phi, vb4, O[t]);
-      O[t] = mfma16(plo, vb4, O[t]);
+      O[t] = mfma32_2(phi, plo, vb4, vb4, O[t]);  // P = hi + lo, both against the same V
     }
     asm volatile("" : "+v"(m), "+v"(l));
     sched_fence();
@@ -749,9 +746,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
     else if (bsel == 1) mfma_k_operands<SUBB>(rd, ad);
     else mfma_k_operands<2 * SUBB>(rd, ad);
     // lane (qd, hl): column hl of tokens 4 qd + 0..3 of the wave's rows
-    f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) S = mfma16(__builtin_bit_cast(bf16x4_t, rd[ks]), qb[ks], S);
+    const f32x4_t S = qk16(rd, qb);
     const int nrows = min(TS, t1 - c0);
     float sv[4];
 #pragma unroll
@@ -1223,7 +1218,28 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
   }
 }
 
-template <int EL, int D, int G, bool S2 = false>
+// A bulk cut of a whole unit in one importance block, out of line.  With the
+// caller's lengths and budgets the host splits every bulk cut it can foresee
+// over launches of their own; the one it cannot (a unit one token over budget
+// that holds no pending eviction) takes this call.  Inlined, its registers would push the
+// steady path's values into scratch, and reloading them waits for every store
+// the block has issued.  The LDS buffers keep their address space across the
+// call.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) int lds_int;
+typedef __attribute__((address_space(3))) RadixState lds_radix;
+template <int RB>
+__device__ __attribute__((noinline)) void bulk_cut_unit(const uint64_t *keys, int L, int beta, char *kw, char *vw,
+                                                        int32_t *posw, float *impw, int32_t *holes, int32_t *movers,
+                                                        int32_t *len_u, int32_t *status, lds_u32 *hist,
+                                                        lds_u32 *whist, lds_int *sc, lds_radix *rs) {
+  bulk_compact<kT2, RB>(keys, L, beta, L - beta, kw, vw, posw, impw, holes, movers, len_u, status,
+                        (uint32_t *)hist, (uint32_t *)whist, (int *)sc, (RadixState *)rs, nullptr);
+}
+
+// IB: the in-block bulk cut inlined (when the host cannot foresee bulk cuts,
+// any unit may be cut in bulk in this block), or called out of line.
+template <int EL, int D, int G, bool S2 = false, bool IB = false>
 __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k_finalize(StepArgs a) {
   constexpr int RB = D * EL, NR = RB / 16, GD = G * D;
   constexpr int NB = K2Lay<G>::NB, CHUNK = K2Lay<G>::CHUNK;
@@ -1237,6 +1253,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   __shared__ int ss[kNW2];
   __shared__ float s_newimp;
   __shared__ int s_last;
+  __shared__ __attribute__((aligned(16))) uint4 s_nrow[kWave];  // the new token's K and V rows
   // bulk cut: radix-select scratch (one block per unit), or the block's key
   // histogram (kBulkBins words of whist) when the cut is spread over blocks
   __shared__ uint32_t hist[256];
@@ -1310,8 +1327,13 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       const float *lg = a.ws.logits + (size_t)u * a.cap * G;
       const int len_dev = ld_vec(a.len + u, vz);
       const int dead_ld = ld_vec(unit_state(a, u) + 1, vz);
-      const int rt = tid % (2 * NR);
-      const uint4 nrow = *reinterpret_cast<const uint4 *>(rt < NR ? kn + rt * 16 : vn + (rt - NR) * 16);
+      // The new token's K and V rows (2 NR pieces of 16 bytes) go to LDS by
+      // DMA from wave 0, ahead of the batch, to be written out at the end:
+      // held in registers they would take VGPRs the batch needs.
+      if (wave == 0) {
+        const int rt = min(lane, 2 * NR - 1);
+        dma16(rt < NR ? kn + rt * 16 : vn + (rt - NR) * 16, s_nrow);
+      }
       float tl[NB][G], ti[NB];
       int tp[NB];
       auto load_batch = [&](int base) {
@@ -1384,24 +1406,42 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         for (int i = tid; i < kBulkBins; i += kT2) whist[i] = 0u;
         __syncthreads();
       }
-      for (int base = nb0; base < nb1; base += CHUNK) {
-        if (base != nb0) load_batch(base);
+      // One batch of the block's tokens: probabilities, importance, the
+      // block's lowest eviction key and, in a bulk cut, every key.
+      auto batch = [&](int base) __attribute__((always_inline)) {
+        // Every loaded value is used before the first store: a load still
+        // outstanding on some path would make the compiler wait for the
+        // stores issued after it as well.
+        float ivs[NB];
+        int pns[NB];
+    #pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int n = base + tid + i * kT2;
+          float p = 0.f;
+    #pragma unroll
+          for (int g = 0; g < G; ++g)
+            p += a.acc_logit ? tl[i][g] * scale_nat : fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
+          const bool is_new = n == Lold;
+          const int pn = is_new ? newest : tp[i];
+          // HiKV's dual bank: only the recent window accumulates; the scores
+          // of older tokens are frozen (and not rewritten).
+          const bool acc = !a.acc_recent || pn > newest - Wp;
+          ivs[i] = (is_new ? 0.f : ti[i]) + (acc ? p : 0.f);
+          pns[i] = pn;
+          asm volatile("" : "+v"(ivs[i]), "+v"(pns[i]));
+        }
+        // (and the new rows' DMA, issued before the batch, has landed)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int n = base + tid + i * kT2;
           int hbin = kBulkBins;  // the key's histogram bin (a spread bulk cut), or none
           if (n < nb1 && n != dead) {
-            float p = 0.f;
-    #pragma unroll
-            for (int g = 0; g < G; ++g)
-              p += a.acc_logit ? tl[i][g] * scale_nat : fast_exp2(fmaf(tl[i][g], a.scale_log2, -Mg[g])) * ILg[g];
             const bool is_new = n == Lold;
-            const int pn = is_new ? newest : tp[i];
+            const int pn = pns[i];
             const bool recent = pn > newest - Wp;
-            // HiKV's dual bank: only the recent window accumulates; the
-            // scores of older tokens are frozen (and not rewritten).
             const bool acc = !a.acc_recent || recent;
-            const float iv = (is_new ? 0.f : ti[i]) + (acc ? p : 0.f);
+            const float iv = ivs[i];
             if (is_new) s_newimp = iv;
             else if (acc) impw[n] = iv;
             const bool cand = !((pn < S) || recent);
@@ -1433,13 +1473,46 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
             }
           }
         }
+      };
+      if (bulk && !split) {
+        // Bulk in one block: the new token goes to slot Lold, then the unit's L
+        // slots (the dead one included, keyed to go first) are cut to the
+        // budget: select the L - beta lowest keys among the unprotected tokens
+        // and move survivors from above the budget into the evicted slots
+        // below it.  (A path of its own: the steady path after it then waits
+        // for no load of the later batches.)
+        for (int base = nb0; base < nb1; base += CHUNK) {
+          if (base != nb0) load_batch(base);
+          batch(base);
+        }
+        lds_barrier();  // s_newimp
+        const float newimp = s_newimp;
+        if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] =
+              lds_read_u128(lds_addr(&s_nrow[tid]));
+        if (tid == 0) {
+          impw[Lold] = newimp;
+          posw[Lold] = newest;
+          unit_state(a, u)[0] = 0;
+        }
+        __syncthreads();  // every key is stored
+        if constexpr (IB)
+          bulk_compact<kT2, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
+                                a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs,
+                                nullptr);
+        else
+          bulk_cut_unit<RB>(bkeys, L, beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
+                            a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, (lds_u32 *)hist,
+                            (lds_u32 *)whist, (lds_int *)sc, (lds_radix *)&rs);
+        return;
       }
+      batch(nb0);  // the block's tokens: one batch
       if (split) {
         __syncthreads();  // the histogram, s_newimp
         uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
         for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
         if (nb1 == L) {  // the block holding slot Lold appends the new token there
-          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
+          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] =
+              lds_read_u128(lds_addr(&s_nrow[tid]));
           if (tid == 0) {
             impw[Lold] = s_newimp;
             posw[Lold] = newest;
@@ -1451,7 +1524,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         }
         return;
       }
-      if (!bulk) {
+      {
         wave_min_key(best, best_slot);
         if (lane == 0) {
           sk[wave] = best;
@@ -1461,7 +1534,8 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         if (nb1 == L) {
           // The block holding slot Lold places the new token: into the dead
           // slot, or appended at Lold.
-          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)fs * RB)[tid % NR] = nrow;
+          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)fs * RB)[tid % NR] =
+              lds_read_u128(lds_addr(&s_nrow[tid]));
           if (tid == 0) {
             impw[fs] = s_newimp;
             posw[fs] = newest;
@@ -1485,24 +1559,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         } else if (r == 0 && tid == 0) {
           unit_state(a, u)[0] = 0;
         }
-        return;
       }
-      // Bulk: the new token goes to slot Lold, then the unit's L slots (the
-      // dead one included, keyed to go first) are cut to the budget: select
-      // the L - beta lowest keys among the unprotected tokens and move
-      // survivors from above the budget into the evicted slots below it.
-      lds_barrier();  // s_newimp
-      const float newimp = s_newimp;
-      if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] = nrow;
-      if (tid == 0) {
-        impw[Lold] = newimp;
-        posw[Lold] = newest;
-        unit_state(a, u)[0] = 0;
-      }
-      __syncthreads();  // every key is stored
-      bulk_compact<kT2, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
-                            a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs,
-                            nullptr);
     }();
     end_wave();
   }
@@ -1912,8 +1969,9 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
     for (int u = 0; u < a.hp.n; ++u) mx = max(mx, a.hp.L[u]);
     nib = min(nib, (mx + kImpChunk - 1) / kImpChunk);
   }
-  hipLaunchKernelGGL((k_finalize<EL, D, G>), dim3((unsigned)a.n_units, (unsigned)(nib + k2_noc<EL, D, G>())),
-                     dim3(kT2), 0, s, a);
+  const dim3 g2((unsigned)a.n_units, (unsigned)(nib + k2_noc<EL, D, G>()));
+  if (a.bulk_known) hipLaunchKernelGGL((k_finalize<EL, D, G>), g2, dim3(kT2), 0, s, a);
+  else hipLaunchKernelGGL((k_finalize<EL, D, G, false, true>), g2, dim3(kT2), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.bulk_split) {
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
