@@ -221,6 +221,20 @@ __device__ __forceinline__ void stage_sub_by(char *kb, char *vb, const char *kc,
                                              const char *kn, const char *vn, int c0, int nrows,
                                              int t0, int Lold, int wl, int lane) {
   constexpr int RB = 256;
+  if (nrows == 32 && (unsigned)(Lold - c0) >= 32u) {
+    // Every row is a cache row (the usual case): one base per sub-chunk and
+    // per-lane offsets, which do not change from one sub-chunk to the next.
+    const char *kbase = kc + (size_t)c0 * RB, *vbase = vc + (size_t)c0 * RB;
+#pragma unroll
+    for (int i = 0; i < 8 / LW; ++i) {
+      const int piece = i * LW + wl;
+      const int row = piece * 4 + (lane >> 4);
+      const uint32_t o = (uint32_t)(row * RB) + ((((uint32_t)lane & 15u) ^ ((uint32_t)row & 15u)) << 4);
+      __builtin_amdgcn_global_load_lds(kbase + o, kb + (piece << 10), 16, 0, kRowCpol);
+      __builtin_amdgcn_global_load_lds(vbase + o, vb + (piece << 10), 16, 0, kRowCpol);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 8 / LW; ++i) {
     const int piece = i * LW + wl;  // 1 KB piece of the 8 KB sub-chunk: four 256-byte rows

@@ -451,10 +451,15 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
     const f32x4_t S = qk16(rd, qb);
     const int nrows = min(TS, t1 - c0);
     float sv[4];
+    if (nrows == TS && (unsigned)(dead - c0) >= (unsigned)TS) {  // every row live: nothing to mask
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int row = grp * 16 + 4 * qd + r4;
-      sv[r4] = (row < nrows && c0 + row != dead) ? S[r4] : -INFINITY;
+      for (int r4 = 0; r4 < 4; ++r4) sv[r4] = S[r4];
+    } else {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int row = grp * 16 + 4 * qd + r4;
+        sv[r4] = (row < nrows && c0 + row != dead) ? S[r4] : -INFINITY;
+      }
     }
     // The sub-chunk's logits: each half-0 wave gathers its 16 rows x G heads
     // in its own LDS rows and stores them with coalesced write-through stores
