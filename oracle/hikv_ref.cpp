@@ -15,6 +15,9 @@
 //     position asc), so among equal scores the newer token goes first.
 //  R5 sinks are absolute positions 0..S-1; the recent window is the W'
 //     newest positions including the new token, W' = min(W, budget - S).
+//  R7 block-granular eviction: a block is the P consecutive positions
+//     [P b, P b + P); its score is the fp64 sum of its live tokens'
+//     importance; a block with any protected token is never evicted.
 //  R6 Stage II: per q-head, channels E = top-r |q_d| (ties: lower d);
 //     approximate logits over E; importance from their softmax over all live
 //     tokens; output = exact full-D softmax restricted to the k_T tokens with
@@ -111,9 +114,51 @@ bool budget_ok(const Dims &d, const hikv_ref_policy *pol, int beta) {
   return beta >= pol->n_sink && beta <= d.cap;
 }
 
+// Block-granular selection (R7): which slots survive when whole blocks of P
+// positions are evicted, lowest summed importance first (equal sums: higher
+// block id first), until at most beta tokens are live.
+void select_blocks(const Unit &x, int L, int beta, int P, const std::vector<uint8_t> &prot,
+                   std::vector<uint8_t> &keep) {
+  struct Blk {
+    int64_t id;
+    double score;
+    int count;
+    bool prot;
+  };
+  std::vector<Blk> blk;
+  std::vector<int> of(L);  // slot -> index in blk
+  for (int n = 0; n < L; ++n) {
+    const int64_t p = x.pos[n];
+    const int64_t id = p >= 0 ? p / P : -((-p + P - 1) / P);  // floor(pos / P)
+    int k = 0;
+    while (k < (int)blk.size() && blk[k].id != id) ++k;
+    if (k == (int)blk.size()) blk.push_back({id, 0.0, 0, false});
+    blk[k].score += (double)x.imp[n];
+    blk[k].count += 1;
+    blk[k].prot = blk[k].prot || prot[n];
+    of[n] = k;
+  }
+  std::vector<int> order;
+  for (int k = 0; k < (int)blk.size(); ++k)
+    if (!blk[k].prot) order.push_back(k);
+  std::sort(order.begin(), order.end(), [&](int a, int b) {
+    if (blk[a].score != blk[b].score) return blk[a].score < blk[b].score;
+    return blk[a].id > blk[b].id;
+  });
+  std::vector<uint8_t> gone(blk.size(), 0);
+  int live = L;
+  for (int k : order) {
+    if (live <= beta) break;
+    gone[k] = 1;
+    live -= blk[k].count;
+  }
+  for (int n = 0; n < L; ++n) keep[n] = !gone[of[n]];
+}
+
 // Eviction of one unit down to budget beta (H2O with protected sinks and
-// window).  kept[] (pre-eviction slot order) is filled when non-null.  The
-// survivors are compacted stably into slots [0, beta).
+// window; whole blocks of positions with pol->block_tokens >= 2).  kept[]
+// (pre-eviction slot order) is filled when non-null.  The survivors are
+// compacted stably into slots [0, len).
 void evict_unit(const Dims &d, const Unit &x, const hikv_ref_policy *pol, int beta,
                 int32_t newest, uint8_t *kept_out) {
   const int L = *x.len;
@@ -131,14 +176,18 @@ void evict_unit(const Dims &d, const Unit &x, const hikv_ref_policy *pol, int be
       else
         cand.push_back(n);
     }
-    // Rank candidates: higher importance first, then lower position.
-    std::sort(cand.begin(), cand.end(), [&](int a, int b) {
-      if (x.imp[a] != x.imp[b]) return x.imp[a] > x.imp[b];
-      return x.pos[a] < x.pos[b];
-    });
-    int keep_n = std::max(0, beta - n_prot);
-    for (int n = 0; n < L; ++n) keep[n] = prot[n];
-    for (int i = 0; i < (int)cand.size() && i < keep_n; ++i) keep[cand[i]] = 1;
+    if (pol->block_tokens >= 2) {
+      select_blocks(x, L, beta, pol->block_tokens, prot, keep);
+    } else {
+      // Rank candidates: higher importance first, then lower position.
+      std::sort(cand.begin(), cand.end(), [&](int a, int b) {
+        if (x.imp[a] != x.imp[b]) return x.imp[a] > x.imp[b];
+        return x.pos[a] < x.pos[b];
+      });
+      int keep_n = std::max(0, beta - n_prot);
+      for (int n = 0; n < L; ++n) keep[n] = prot[n];
+      for (int i = 0; i < (int)cand.size() && i < keep_n; ++i) keep[cand[i]] = 1;
+    }
     // Stable in-place compaction of the survivors.
     const size_t row = (size_t)d.D * d.el;
     int w = 0;
@@ -167,6 +216,7 @@ bool policy_ok(const Dims &d, const hikv_ref_policy *pol) {
   if (pol->stage2_v != HIKV_REF_S2V_TOPK && pol->stage2_v != HIKV_REF_S2V_CHUNK) return false;
   if (pol->stage2_channels > 0 && pol->stage2_v == HIKV_REF_S2V_TOPK && pol->stage2_tokens < 1)
     return false;
+  if (pol->block_tokens < 0 || pol->block_tokens > HIKV_REF_MAX_BLOCK) return false;
   return true;
 }
 

@@ -96,7 +96,18 @@ typedef struct {
   int32_t stage2_tokens;   /* tokens kept for the exact softmax (k_T) */
   int32_t accumulate;      /* HIKV_REF_ACC_ALL | HIKV_REF_ACC_RECENT | HIKV_REF_ACC_LOGIT */
   int32_t stage2_v;        /* HIKV_REF_S2V_TOPK | HIKV_REF_S2V_CHUNK (used when r > 0) */
+  /* Eviction granularity ("KV Cache Compression and Dynamic Pruning in
+   * Production Serving", Sec. 5, PagedAttention block fragmentation): 0 or 1,
+   * single tokens; P >= 2 (at most HIKV_REF_MAX_BLOCK), whole blocks of P
+   * consecutive positions (block id = pos / P).  A block holding a protected
+   * token is kept whole; the other blocks are ranked by the sum of their
+   * tokens' importance and evicted lowest first (equal sums: the higher
+   * block id first) while more than the budget's tokens are live, so a unit
+   * may end below its budget, or above it when protected blocks hold more. */
+  int32_t block_tokens;
 } hikv_ref_policy;
+
+#define HIKV_REF_MAX_BLOCK 1024
 
 /* Optional per-step debug outputs; any pointer may be NULL. */
 typedef struct {

@@ -35,7 +35,8 @@ class Cache(C.Structure):
 class Policy(C.Structure):
     _fields_ = [("budget", C.c_void_p), ("budget_all", C.c_int32), ("n_sink", C.c_int32),
                 ("n_recent", C.c_int32), ("stage2_channels", C.c_int32),
-                ("stage2_tokens", C.c_int32), ("accumulate", C.c_int32), ("stage2_v", C.c_int32)]
+                ("stage2_tokens", C.c_int32), ("accumulate", C.c_int32), ("stage2_v", C.c_int32),
+                ("block_tokens", C.c_int32)]
 
 
 ACC_ALL, ACC_RECENT, ACC_LOGIT = 0, 1, 2
@@ -98,12 +99,12 @@ def cache_of(state) -> Cache:
 
 
 def policy_of(budget=None, budget_all=0, n_sink=0, n_recent=0, stage2_channels=0,
-              stage2_tokens=0, accumulate=ACC_ALL, stage2_v=S2V_TOPK):
+              stage2_tokens=0, accumulate=ACC_ALL, stage2_v=S2V_TOPK, block_tokens=0):
     keep = None
     if budget is not None:
         keep = np.ascontiguousarray(budget, dtype=np.int32)
     pol = Policy(_ptr(keep), int(budget_all), int(n_sink), int(n_recent), int(stage2_channels),
-                 int(stage2_tokens), int(accumulate), int(stage2_v))
+                 int(stage2_tokens), int(accumulate), int(stage2_v), int(block_tokens))
     return pol, keep
 
 
@@ -113,13 +114,13 @@ def copy_state(state):
 
 def decode_step(state, n_q_heads, q, k_new, v_new, new_pos, *, budget=None, budget_all=0,
                 n_sink=0, n_recent=0, stage2_channels=0, stage2_tokens=0, scale=0.0,
-                debug=True, accumulate=ACC_ALL, stage2_v=S2V_TOPK):
+                debug=True, accumulate=ACC_ALL, stage2_v=S2V_TOPK, block_tokens=0):
     """One oracle decode step; mutates ``state``.  Returns (status, out, dbg)."""
     L = lib()
     sh = shape_of(state, n_q_heads, scale)
     B, Hkv, cap = sh.batch, sh.n_kv_heads, sh.capacity
     pol, _keep = policy_of(budget, budget_all, n_sink, n_recent, stage2_channels, stage2_tokens,
-                           accumulate, stage2_v)
+                           accumulate, stage2_v, block_tokens)
     out = np.zeros((B, n_q_heads, sh.head_dim), dtype=np.float32)
     q = np.ascontiguousarray(q)
     k_new = np.ascontiguousarray(k_new)
@@ -148,11 +149,11 @@ def decode_step(state, n_q_heads, q, k_new, v_new, new_pos, *, budget=None, budg
 
 
 def evict(state, n_q_heads, newest_pos, *, budget=None, budget_all=0, n_sink=0, n_recent=0,
-          debug=True):
+          debug=True, block_tokens=0):
     L = lib()
     sh = shape_of(state, n_q_heads)
     B, Hkv, cap = sh.batch, sh.n_kv_heads, sh.capacity
-    pol, _keep = policy_of(budget, budget_all, n_sink, n_recent)
+    pol, _keep = policy_of(budget, budget_all, n_sink, n_recent, block_tokens=block_tokens)
     newest_pos = np.ascontiguousarray(newest_pos, dtype=np.int32)
     dbg = None
     dbg_c = None

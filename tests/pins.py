@@ -751,10 +751,123 @@ def snapkv_pooling_matches_library(seed=67):
             assert np.abs(got - pooled).max() < 1e-5, (gaps, j)
 
 
+
+# ---------------------------------------------------------------------------
+# Block-granular eviction ("KV Cache Compression and Dynamic Pruning in
+# Production Serving", Sec. 5, PagedAttention block fragmentation).
+# ---------------------------------------------------------------------------
+def _evict_state(pos, imp, cap):
+    L = len(pos)
+    st = dict(k=np.zeros((1, 1, cap, 4), np.float32), v=np.zeros((1, 1, cap, 4), np.float32),
+              pos=np.full((1, 1, cap), -1, np.int32), imp=np.zeros((1, 1, cap), np.float32),
+              len=np.array([[L]], np.int32))
+    st["pos"][0, 0, :L] = pos
+    st["imp"][0, 0, :L] = imp
+    return st
+
+
+def paged_block_golden():
+    """The page's block-allocation figure and two variants worked by hand
+    (tests/golden/paged_blocks.txt)."""
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, "paged_blocks.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, rest = line.partition(" ")
+        if key == "case":
+            cur = dict(name=rest)
+            cases.append(cur)
+        elif key == "fill":
+            cur["fill"] = {int(b): float(v) for b, v in (t.split(":") for t in rest.split())}
+        elif key == "kept_blocks":
+            cur["kept_blocks"] = [int(x) for x in rest.split()]
+        else:
+            cur[key] = int(rest)
+    assert len(cases) == 3
+    for c in cases:
+        P = c["block"]
+        pos = np.arange(c["newest"] + 1, dtype=np.int32)
+        imp = np.array([c["fill"][int(p) // P] for p in pos], np.float32)
+        st = _evict_state(pos, imp, len(pos) + 1)
+        code, _ = ref.evict(st, 1, [c["newest"]], budget_all=c["budget"], n_sink=c["sink"],
+                            n_recent=c["recent"], block_tokens=P)
+        assert code == 0, c["name"]
+        got = list(ref.live_positions(st, 0, 0))
+        want = [p for b in c["kept_blocks"] for p in range(b * P, b * P + P)]
+        assert got == want, (c["name"], got[:40], want[:40])
+
+
+def blocks_of_one_token_match_token_eviction(seed=71, trials=60):
+    """Positions P apart put one token in each block: block sums are the
+    tokens' importances, the tie rules agree (higher block id = higher
+    position goes first), and a block is protected exactly when its token is,
+    so block-granular eviction must keep the token-granular set."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for t in range(trials):
+        P = int(rng.choice([2, 3, 8, 16]))
+        L = int(rng.integers(4, 40))
+        slots = rng.permutation(L)
+        pos = (slots * P + rng.integers(0, P, L)).astype(np.int32)
+        imp = rng.integers(0, 6, L).astype(np.float32) * 0.25  # exact ties
+        S = int(rng.integers(0, 3))
+        beta = int(rng.integers(S, L + 2))
+        R = int(rng.integers(0, 4))
+        newest = int(pos.max())
+        a, b = _evict_state(pos, imp, L + 1), _evict_state(pos, imp, L + 1)
+        ca, _ = ref.evict(a, 1, [newest], budget_all=beta, n_sink=S, n_recent=R)
+        cb, _ = ref.evict(b, 1, [newest], budget_all=beta, n_sink=S, n_recent=R, block_tokens=P)
+        assert ca == 0 and cb == 0
+        assert list(ref.live_positions(a, 0, 0)) == list(ref.live_positions(b, 0, 0)), (t, P)
+
+
+def block_eviction_brute_force(seed=73, trials=120):
+    """Every set of whole unprotected blocks is tried; exactly one satisfies
+    the rule's defining properties -- the unit fits (or no unprotected block
+    is left), every evicted block ranks below every kept unprotected block
+    (lower sum, equal sums: higher id), and without its best-ranked evicted
+    block the unit would not fit -- and it is the one the oracle evicts."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for t in range(trials):
+        P = int(rng.choice([2, 3, 4, 8]))
+        L = int(rng.integers(3, min(28, 10 * P) + 1))
+        pos = rng.choice(np.arange(0, 10 * P), L, replace=False).astype(np.int32)  # <= 10 blocks
+        imp = rng.integers(0, 5, L).astype(np.float32) * 0.5
+        S = int(rng.integers(0, 3))
+        R = int(rng.integers(0, 5))
+        beta = int(rng.integers(S, L + 2))
+        newest = int(pos.max())
+        W_ = min(R, beta - S)
+        prot = (pos < S) | (pos > newest - W_)
+        ids = pos // P
+        blocks = sorted(set(ids.tolist()))
+        score = {b: float(np.sum(imp[ids == b].astype(np.float64))) for b in blocks}
+        count = {b: int(np.sum(ids == b)) for b in blocks}
+        bprot = {b: bool(np.any(prot[ids == b])) for b in blocks}
+        free = [b for b in blocks if not bprot[b]]
+        rank = lambda b: (score[b], -b)  # lower ranks go first
+        valid = []
+        for mask in range(1 << len(free)):
+            ev = [free[i] for i in range(len(free)) if mask >> i & 1]
+            kept_free = [b for b in free if b not in ev]
+            live = L - sum(count[b] for b in ev)
+            fits = live <= beta or not kept_free
+            ordered = all(rank(e) < rank(k) for e in ev for k in kept_free)
+            minimal = not ev or live + count[max(ev, key=rank)] > beta
+            if fits and ordered and minimal:
+                valid.append(set(ev))
+        assert len(valid) == 1, (t, valid)
+        st = _evict_state(pos, imp, L + 1)
+        code, _ = ref.evict(st, 1, [newest], budget_all=beta, n_sink=S, n_recent=R, block_tokens=P)
+        assert code == 0
+        want = sorted(int(p) for p in pos if int(p) // P not in valid[0])
+        assert sorted(ref.live_positions(st, 0, 0)) == want, (t, P)
+
 ALL = [attention_matches_library, rows_sum_to_group, streaming_closed_form, eviction_brute_force,
        golden_cases, permutation_invariance, channel_permutation, conservation,
        stage2_reduces_to_stage1, stage2_selection, equal_keys_closed_form, prefill_column_sums,
        errors_leave_unit_unchanged, heap_worked_examples, heap_keeps_the_top_scores,
        dual_bank_matches_its_definition, stage2_chunks_reduce_to_attention,
        stage2_chunks_select_by_probability, logit_accumulation_matches_library,
-       snapkv_pooling_matches_library]
+       snapkv_pooling_matches_library,
+       paged_block_golden, blocks_of_one_token_match_token_eviction, block_eviction_brute_force]

@@ -64,6 +64,14 @@ MUTANTS = [
      "            for (int n = 0; n < L; ++n) {\n              double a2 = 0.0;\n"
      "              for (int c = 0; c < d.D; ++c) a2 += qh[c] * key_elem(d, x, n, c);\n"
      "              st[n] = d.scale * a2;\n            }\n            pt = softmax(st);\n          }"),
+    ("blocks_evict_highest", "if (blk[a].score != blk[b].score) return blk[a].score < blk[b].score;",
+     "if (blk[a].score != blk[b].score) return blk[a].score > blk[b].score;"),
+    ("blocks_tie_evicts_older", "    return blk[a].id > blk[b].id;", "    return blk[a].id < blk[b].id;"),
+    ("blocks_protected_by_last_token_only", "blk[k].prot = blk[k].prot || prot[n];", "blk[k].prot = prot[n];"),
+    ("blocks_evict_one_too_many", "    if (live <= beta) break;", "    if (live < beta) break;"),
+    ("blocks_by_slot", "const int64_t p = x.pos[n];", "const int64_t p = n;"),
+    ("blocks_score_by_max", "blk[k].score += (double)x.imp[n];",
+     "blk[k].score = std::max(blk[k].score, (double)x.imp[n]);"),
 ]
 
 
