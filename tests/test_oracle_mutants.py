@@ -18,8 +18,8 @@ MUTANTS = [
     ("drop_logit_scale", "            s[n] = d.scale * acc;", "            s[n] = acc;"),
     ("new_token_not_attended", "      *x.len = slot + 1;\n      const int L = *x.len;",
      "      *x.len = slot + 1;\n      const int L = *x.len - 1;"),
-    ("tie_keeps_newer", "      return x.pos[a] < x.pos[b];\n    });",
-     "      return x.pos[a] > x.pos[b];\n    });"),
+    ("tie_keeps_newer", "        return x.pos[a] < x.pos[b];\n      });",
+     "        return x.pos[a] > x.pos[b];\n      });"),
     ("window_off_by_one", "(x.pos[n] > newest - W)", "(x.pos[n] >= newest - W)"),
     ("importance_from_logits", "added[n] += by_logit ? s[n] : p[n];", "added[n] += s[n];"),
     ("gqa_group_strided", "        const int h = j * d.G + g;\n        std::vector<double> qh",
