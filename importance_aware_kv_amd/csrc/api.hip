@@ -56,6 +56,7 @@ int check_policy(const hikv_shape *s, const hikv_policy *p) {
   if (p->stage2_channels < 0 || p->stage2_channels > s->head_dim) return HIKV_EINVAL;
   if (p->stage2_v != HIKV_S2V_TOPK && p->stage2_v != HIKV_S2V_CHUNK) return HIKV_EINVAL;
   if (p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_TOPK && p->stage2_tokens < 1) return HIKV_EINVAL;
+  if (p->block_tokens < 0 || p->block_tokens > HIKV_MAX_BLOCK_TOKENS) return HIKV_EINVAL;
   return HIKV_OK;
 }
 
@@ -68,7 +69,8 @@ int check_cache(const hikv_cache *c) {
 WsSizes sizes_for(const hikv_shape *s, const hikv_policy *p) {
   const bool chunks = p && p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_CHUNK;
   const int kT = (p && p->stage2_channels > 0 && !chunks) ? p->stage2_tokens : 0;  // 0: no exact top-k_T pass
-  return ws_sizes(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->capacity, kT, chunks);
+  const bool blocks = p && p->block_tokens >= 2;
+  return ws_sizes(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->capacity, kT, chunks, chunks || blocks);
 }
 
 StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *p, const Ws &ws) {
@@ -100,6 +102,7 @@ StepArgs make_args(const hikv_shape *s, const hikv_cache *c, const hikv_policy *
   a.r = p->stage2_channels;
   a.s2_chunks = p->stage2_channels > 0 && p->stage2_v == HIKV_S2V_CHUNK;
   a.kT = (p->stage2_channels > 0 && !a.s2_chunks) ? p->stage2_tokens : 0;
+  a.block = p->block_tokens >= 2 ? p->block_tokens : 0;
   a.ws = ws;
   return a;
 }
@@ -172,6 +175,8 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
     ev1 = static_cast<hipEvent_t>(debug->attend_stop);
   }
   hipError_t e;
+  // Block-granular eviction runs on the two-launch Stage I sequence only.
+  if (a.block && (a.r > 0 || path == HIKV_PATH_MULTI_LAUNCH)) return HIKV_EUNSUPPORTED;
   if (clear_tickets && (a.r > 0 || path == HIKV_PATH_MULTI_LAUNCH)) {
     hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream),
                        reinterpret_cast<int32_t *>(a.ws.ticket), a.n_units);
@@ -188,6 +193,16 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
         for (int u = 0; u < U; ++u) {
           const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
           const int len = policy->len_hint[u];
+          if (a.block) {
+            // Every eviction is a bulk cut of whole blocks: at most the
+            // excess plus one block (and a dead slot left by a step of
+            // single-token eviction) go, so at most that many rows move.
+            if (len + 1 > beta) {
+              a.bulk_split = 1;
+              a.bulk_rows = max(a.bulk_rows, min(len + 1, len + 2 - beta + a.block));
+            }
+            continue;
+          }
           const int live = len + 1 - (len > beta ? 1 : 0);  // a unit over budget holds a dead slot
           if (live - beta > 1) {
             a.bulk_split = 1;
@@ -196,6 +211,9 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
             a.bulk_rows = max(a.bulk_rows, min(beta, len + 1 - beta));
           }
         }
+      } else if (a.block) {  // any unit may be cut: the cut's launches always run
+        a.bulk_split = 1;
+        a.bulk_rows = a.cap;
       }
       return dev_err(launch_step(a, dt, s, ev0, ev1));
     }
@@ -310,6 +328,7 @@ extern "C" int hikv_evict(const hikv_shape *shape, const hikv_cache *cache,
   if (shape->batch == 0) return HIKV_OK;
   if ((st = check_cache(cache)) != HIKV_OK) return st;
   if (!newest_pos || !ws || !aligned16(ws)) return HIKV_EINVAL;
+  if (policy->block_tokens >= 2) return HIKV_EUNSUPPORTED;  // block-granular eviction: decode steps only
   const WsSizes sz = sizes_for(shape, policy);
   if (ws_bytes < sz.total) return HIKV_EINVAL;
   if ((st = arch_ok()) != HIKV_OK) return st;

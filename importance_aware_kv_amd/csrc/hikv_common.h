@@ -77,7 +77,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline int max_tiles_for(int n_units) { return kMaxGrid + n_units + 8; }
 
-inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chunks) {
+inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chunks, bool order) {
   const size_t U = (size_t)B * Hkv, G = (size_t)(Hq / Hkv), MT = (size_t)max_tiles_for((int)U);
   const size_t NC = chunks ? (size_t)((cap + D - 1) / D) : 0;
   const size_t sz[kWsParts] = {
@@ -102,7 +102,7 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chu
       sizeof(int32_t) * U,             // nmoves
       sizeof(float) * U * NC * G * D,  // chunk_acc
       sizeof(int32_t) * U * NC * G,    // chunk_cnt
-      chunks ? sizeof(int32_t) * U * cap : 0,  // order
+      order ? sizeof(int32_t) * U * cap : 0,   // order (chunked Stage II V side, block eviction)
       sizeof(uint32_t) * U * (size_t)imp_blocks(cap) * kBulkBins,  // bhist
       sizeof(int32_t) * 4 * U,         // bsel
       (kT > 0 && !chunks) ? sizeof(float) * U * cap * G : 0,     // logits2
@@ -182,6 +182,7 @@ struct StepArgs {
   int32_t bulk_split;        // a bulk cut leaves its row moves to a launch of many workgroups per unit
   int32_t bulk_rows;         // with bulk_split: the host's bound on the rows any unit's cut moves
   int32_t bulk_known;        // the host foresaw every bulk cut of the step (lengths and budgets known)
+  int32_t block;             // block-granular eviction: positions per block (>= 2), or 0 (single tokens)
   int32_t s2_two;            // Stage II (exact top-k_T V side) in the two-launch sequence
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;

@@ -37,6 +37,8 @@ bool step_host_plan(StepArgs &a, int dtype, const int32_t *len_hint);
 hipError_t launch_stage2_channels(const StepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_stage2_exact(const StepArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s);
+// The position order of the units a block-granular eviction cuts (ws.order).
+hipError_t launch_pos_rank(const StepArgs &a, hipStream_t s);
 
 // Prefill scores.
 struct PrefillArgs {

@@ -337,8 +337,19 @@ __global__ __launch_bounds__(kRankThreads) void k_pos_rank(StepArgs a) {
   __shared__ int wpre[NW];
   __shared__ int s_lo[NWV], s_hi[NWV], s_wsum[NWV];
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (!unit_has_tiles(a, u)) return;
-  const int L = a.len[u] + 1;  // the new token sits in slot L - 1
+  // Block-granular eviction orders only the units its second launch marked
+  // as cut this step, over the slots the cut considers; the chunked V side
+  // orders every unit with tiles, over its L slots (the new token sits in
+  // slot L - 1).
+  int L;
+  if (a.block) {
+    const int4 bs = reinterpret_cast<const int4 *>(a.ws.bsel)[u];
+    if (bs.w != 1) return;
+    L = bs.z;
+  } else {
+    if (!unit_has_tiles(a, u)) return;
+    L = a.len[u] + 1;
+  }
   const int32_t *pos = a.pos + (size_t)u * a.cap;
   int32_t *order = a.ws.order + (size_t)u * a.cap;
   // The first KR * kRankThreads positions stay in registers.
@@ -605,6 +616,11 @@ static void chunk_pv_g(const StepArgs &a, dim3 grid, hipStream_t s) {
     case 4: hipLaunchKernelGGL((k_chunk_pv<EL, D, 4>), grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((k_chunk_pv<EL, D, 8>), grid, dim3(256), 0, s, a); break;
   }
+}
+
+hipError_t launch_pos_rank(const StepArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_pos_rank, dim3((unsigned)a.n_units), dim3(kRankThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_pv(const StepArgs &a, int dtype, hipStream_t s) {

@@ -1382,19 +1382,25 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       const int n_evict = over ? live - beta : 0;
       // One eviction (the steady state) is spread over the unit's blocks like
       // the importance, and its victim is left pending for the next call;
-      // more than one (a bulk cut) needs every token in one block.
-      const bool bulk = n_evict > 1;
+      // more than one (a bulk cut) needs every token in one block.  Evicting
+      // whole blocks of positions is always a bulk cut.
+      const bool bulk = a.block ? n_evict > 0 : n_evict > 1;
       // With the caller's lengths a bulk cut is spread over the unit's blocks
       // (each leaves its keys and a histogram of them; k_bulk_select finishes
       // the cut); without them one block takes every token.  Stage II always
       // spreads it: its output blocks read V rows, which must not move during
-      // this launch.
-      const bool split = bulk && (a.bulk_split || S2);
+      // this launch.  So does block-granular eviction, whose keys are made by
+      // a launch of their own (k_block_keys).
+      const bool split = bulk && (a.bulk_split || S2 || a.block);
       if (bulk && !split && r > 0) return;
       const int nb1 = (bulk && !split) ? L : min(L, nb0 + CHUNK);
       const int nact = (L + CHUNK - 1) / CHUNK;  // blocks holding tokens of the unit
       const int Wp = min(a.n_recent, beta - S);
-      const int fs = (dead >= 0 && !bulk) ? dead : Lold;  // the new token's slot
+      // The new token's slot: the dead slot of a pending eviction, except in
+      // a bulk cut of single tokens (which keys the dead slot to go first).
+      const int fs = (dead >= 0 && (!bulk || a.block)) ? dead : Lold;
+      const bool tkeys = bulk && !a.block;  // this launch keys the tokens
+      const bool thist = split && !a.block;  // ... and histograms the keys
       // Kelle's pre-softmax score: the logit scale * q.k (raw q.k times scale)
       const float scale_nat = a.scale_log2 * 0.69314718055994531f;
       float Mg[G], ILg[G];
@@ -1407,7 +1413,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       uint64_t *bkeys = a.ws.bkeys + (size_t)u * a.cap;  // bulk: every slot's key
       uint64_t best = ~0ull;
       int best_slot = -1;
-      if (split) {
+      if (thist) {
         for (int i = tid; i < kBulkBins; i += kT2) whist[i] = 0u;
         __syncthreads();
       }
@@ -1457,16 +1463,16 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
                 best_slot = is_new ? fs : n;
               }
             }
-            if (bulk) {
+            if (tkeys) {
               const uint64_t kk = cand ? evict_key(iv, pn) : ~0ull;
               bkeys[n] = kk;
               if (cand) hbin = (int)(kk >> kBulkShift);
             }
-          } else if (bulk && n < nb1) {
+          } else if (tkeys && n < nb1) {
             bkeys[n] = 0;  // the dead slot: the first to go
             hbin = 0;
           }
-          if (split) {
+          if (thist) {
             // Nearby importances share bins: the lanes with the first lane's
             // bin are counted with one atomic.
             const int h0 = __builtin_amdgcn_readfirstlane(hbin);
@@ -1513,19 +1519,22 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       batch(nb0);  // the block's tokens: one batch
       if (split) {
         __syncthreads();  // the histogram, s_newimp
-        uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
-        for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
-        if (nb1 == L) {  // the block holding slot Lold appends the new token there
-          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)Lold * RB)[tid % NR] =
+        if (thist) {
+          uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
+          for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
+        }
+        if (nb1 == L) {  // the block holding slot Lold places the new token
+          if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)fs * RB)[tid % NR] =
               lds_read_u128(lds_addr(&s_nrow[tid]));
           if (tid == 0) {
-            impw[Lold] = s_newimp;
-            posw[Lold] = newest;
+            impw[fs] = s_newimp;
+            posw[fs] = newest;
           }
         }
         if (r == 0 && tid == 0) {
           unit_state(a, u)[0] = 0;
-          reinterpret_cast<int4 *>(a.ws.bsel)[u] = make_int4(n_evict, beta, L, 1);
+          // the slots the cut considers: a dead slot now holds the new token
+          reinterpret_cast<int4 *>(a.ws.bsel)[u] = make_int4(n_evict, beta, fs == Lold ? L : Lold, 1);
         }
         return;
       }
@@ -1615,6 +1624,72 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
 }
 
 // ---------------------------------------------------------------------------
+// Block-granular eviction ("KV Cache Compression and Dynamic Pruning in
+// Production Serving", Sec. 5, PagedAttention block fragmentation): the keys
+// of a unit cut in bulk when whole blocks of P positions go (block id =
+// pos / P).  k_pos_rank has listed the unit's slots in position order
+// (ws.order); workgroup r takes the ranks [r kImpChunk, (r + 1) kImpChunk)
+// and loads them, with the P - 1 after them and the one before, into LDS.  A
+// rank that starts a block (the rank before it lies in another block) sums the
+// block's importance in position order -- fp32, the same order every call --
+// notes whether any of its tokens is protected, and gives every token of the
+// block the block's key: evict_key with the block sum and the block id, so
+// that equal sums send the higher block first, or no key (~0) when protected.
+// The workgroup leaves the histogram of its keys' top bits as the importance
+// blocks do for single tokens; k_bulk_select then takes every key up to the
+// need-th smallest, which is whole blocks since a block's tokens share one key.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int floor_div(int x, int p) { return x >= 0 ? x / p : -((-x + p - 1) / p); }
+
+__global__ __launch_bounds__(kT2) void k_block_keys(StepArgs a) {
+  constexpr int NL = kImpChunk + HIKV_MAX_BLOCK_TOKENS;  // ranks an LDS copy holds
+  __shared__ int s_slot[NL];
+  __shared__ int s_pos[NL];
+  __shared__ float s_imp[NL];
+  __shared__ uint32_t whist[kBulkBins];
+  const int u = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int4 bs = reinterpret_cast<const int4 *>(a.ws.bsel)[u];
+  if (bs.w != 1) return;  // not cut this step
+  const int beta = bs.y, L = bs.z, P = a.block;
+  const int i0 = r * kImpChunk;
+  if (i0 >= L) return;
+  const int iend = min(L, i0 + kImpChunk);  // ranks whose blocks may start here
+  const int lo = max(i0 - 1, 0), hi = min(L, i0 + kImpChunk + P - 1);  // ranks loaded
+  const int32_t *order = a.ws.order + (size_t)u * a.cap;
+  const int32_t *posw = a.pos + (size_t)u * a.cap;
+  const float *impw = a.imp + (size_t)u * a.cap;
+  uint64_t *bkeys = a.ws.bkeys + (size_t)u * a.cap;
+  for (int k = tid; k < hi - lo; k += kT2) {
+    const int sl = min(max(order[lo + k], 0), a.cap - 1);
+    s_slot[k] = sl;
+    s_pos[k] = posw[sl];
+    s_imp[k] = impw[sl];
+  }
+  for (int i = tid; i < kBulkBins; i += kT2) whist[i] = 0u;
+  __syncthreads();
+  const int b = u / a.Hkv;
+  const int S = a.n_sink, newest = a.new_pos[b], Wp = min(a.n_recent, beta - S);
+  for (int i = i0 + tid; i < iend; i += kT2) {
+    const int k = i - lo;
+    const int blk = floor_div(s_pos[k], P);
+    if (i > 0 && floor_div(s_pos[k - 1], P) == blk) continue;  // not the first rank of its block
+    float sum = 0.f;
+    bool prot = false;
+    int m = 0;
+    for (int j = k; j < hi - lo && floor_div(s_pos[j], P) == blk; ++j, ++m) {
+      sum += s_imp[j];
+      prot = prot || s_pos[j] < S || s_pos[j] > newest - Wp;
+    }
+    const uint64_t key = prot ? ~0ull : evict_key(sum, blk);
+    for (int j = k; j < k + m; ++j) bkeys[s_slot[j]] = key;
+    if (!prot) atomicAdd(&whist[(int)(key >> kBulkShift)], (uint32_t)m);
+  }
+  __syncthreads();
+  uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
+  for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
+}
+
+// ---------------------------------------------------------------------------
 // Third launch of a step that cuts units in bulk (when the host can tell),
 // one workgroup per unit.  The importance blocks left every slot's eviction
 // key and a histogram of the keys' top kBulkBits bits each; the n_evict
@@ -1645,12 +1720,15 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   __shared__ int cs[kBulkCand];
   __shared__ uint64_t eb[NMW];
   __shared__ int sc[kNW2];
-  __shared__ int s_bin, s_need, s_cnt, s_nc;
+  __shared__ int s_bin, s_need, s_cnt, s_nc, s_tot;
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int4 bs = reinterpret_cast<const int4 *>(a.ws.bsel)[u];
   if (bs.w != 1) return;  // not cut in bulk
   const int k = bs.x, beta = bs.y, L = bs.z;
   const uint64_t *keys = a.ws.bkeys + (size_t)u * a.cap;
+  // The unit's length after the cut: the budget, or, when whole blocks go
+  // (every key of a block is the same), L less every key up to the threshold.
+  int newlen = beta;
 
   // The bin of a 2 x kT2-bin histogram (bins 2 tid, 2 tid + 1 in c0, c1)
   // holding the need-th smallest counted key.
@@ -1658,6 +1736,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
     if (tid == 0) s_bin = -1;
     int tot;
     const int ex = block_excl_scan<NT>((int)(c0 + c1), sc, &tot);
+    if (tid == 0) s_tot = tot;
     if (ex < need && ex + (int)(c0 + c1) >= need) {
       const bool first = ex + (int)c0 >= need;
       s_bin = first ? 2 * tid : 2 * tid + 1;
@@ -1679,8 +1758,19 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
       c1 += v.y;
     }
     find_bin(c0, c1, k);
+    // Whole blocks: protected blocks can hold more than the budget leaves,
+    // and then every candidate goes (none at all: the unit stays as it is).
+    if (s_bin < 0 && a.block) {
+      const int tot = s_tot;
+      __syncthreads();
+      if (tot == 0) {
+        if (tid == 0) a.len[u] = L;
+        return;
+      }
+      find_bin(c0, c1, tot);
+    }
   }
-  if (s_bin < 0) {  // fewer candidates than tokens to evict: cannot happen
+  if (s_bin < 0) {  // fewer candidates than tokens to evict: cannot happen for single tokens
     if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
     return;
   }
@@ -1809,8 +1899,16 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
   int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
   if (!use_map) {  // a key goes exactly when it is at most T
-    bulk_list<NT, RB>(keys, L, beta, T, 0, kw, vw, a.pos + (size_t)u * a.cap, a.imp + (size_t)u * a.cap, holes,
-                      movers, a.len + u, a.ws.status, reinterpret_cast<uint64_t *>(ck), sc, a.ws.nmoves + u);
+    if (a.block) {
+      int c = 0;
+      for (int n = tid; n < L; n += NT) c += (keys[n] != ~0ull && keys[n] <= T) ? 1 : 0;
+      int tot;
+      block_excl_scan<NT>(c, sc, &tot);
+      newlen = L - tot;
+    }
+    bulk_list<NT, RB>(keys, L, newlen, T, 0, kw, vw, a.pos + (size_t)u * a.cap, a.imp + (size_t)u * a.cap,
+                      holes, movers, a.len + u, a.ws.status, reinterpret_cast<uint64_t *>(ck), sc,
+                      a.ws.nmoves + u);
     return;
   }
   __syncthreads();  // the bitmap is complete
@@ -1819,9 +1917,16 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   const int nw = (L + 63) / 64, wpt = (nw + NT - 1) / NT;
   const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
   auto below = [](int c) -> uint64_t { return c <= 0 ? 0ull : (c >= 64 ? ~0ull : ((1ull << c) - 1ull)); };
+  if (a.block) {
+    int c = 0;
+    for (int w = w0; w < w1; ++w) c += __popcll(eb[w] & below(L - 64 * w));
+    int tot;
+    block_excl_scan<NT>(c, sc, &tot);
+    newlen = L - tot;
+  }
   int nh = 0, nm = 0;
   for (int w = w0; w < w1; ++w) {
-    const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(beta - 64 * w);
+    const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(newlen - 64 * w);
     nh += __popcll(e & valid & low);
     nm += __popcll(~e & valid & ~low);
   }
@@ -1829,7 +1934,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   int ih = block_excl_scan<NT>(nh, sc, &th);
   int im = block_excl_scan<NT>(nm, sc, &tm);
   for (int w = w0; w < w1; ++w) {
-    const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(beta - 64 * w);
+    const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(newlen - 64 * w);
     for (uint64_t x = e & valid & low; x; x &= x - 1ull) holes[ih++] = 64 * w + __builtin_ctzll(x);
     for (uint64_t x = ~e & valid & ~low; x; x &= x - 1ull) movers[im++] = 64 * w + __builtin_ctzll(x);
   }
@@ -1838,7 +1943,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
       set_status(a.ws.status, HIKV_EINVAL);
     } else {
       a.ws.nmoves[u] = tm;
-      a.len[u] = beta;
+      a.len[u] = newlen;
     }
   }
 }
@@ -1979,6 +2084,11 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
   else hipLaunchKernelGGL((k_finalize<EL, D, G, false, true>), g2, dim3(kT2), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.bulk_split) {
+    if (a.block) {  // whole blocks: the position order, then the blocks' keys
+      if ((e = launch_pos_rank(a, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_block_keys, dim3((unsigned)a.n_units, (unsigned)nib), dim3(kT2), 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int per = bulk_moves_per_block<D * EL>();

@@ -44,7 +44,7 @@ class hikv_policy(C.Structure):
     _fields_ = [("budget", C.c_void_p), ("budget_all", C.c_int32), ("n_sink", C.c_int32),
                 ("n_recent", C.c_int32), ("stage2_channels", C.c_int32),
                 ("stage2_tokens", C.c_int32), ("len_hint", C.c_void_p), ("budget_hint", C.c_void_p),
-                ("accumulate", C.c_int32), ("stage2_v", C.c_int32)]
+                ("accumulate", C.c_int32), ("stage2_v", C.c_int32), ("block_tokens", C.c_int32)]
 
 
 class hikv_debug(C.Structure):
@@ -115,12 +115,12 @@ def make_shape(batch, n_q_heads, n_kv_heads, head_dim, capacity, kv_dtype, scale
 
 def make_policy(budget=None, budget_all=0, n_sink=0, n_recent=0, stage2_channels=0,
                 stage2_tokens=0, len_hint=None, budget_hint=None, accumulate=HIKV_ACC_ALL,
-                stage2_v=HIKV_S2V_TOPK) -> hikv_policy:
+                stage2_v=HIKV_S2V_TOPK, block_tokens=0) -> hikv_policy:
     """len_hint, budget_hint: optional host int32 numpy arrays (kept alive by the caller)."""
     hint = None if len_hint is None else len_hint.ctypes.data
     bhint = None if budget_hint is None else budget_hint.ctypes.data
     return hikv_policy(None if budget is None else budget.data_ptr(), budget_all, n_sink, n_recent,
-                       stage2_channels, stage2_tokens, hint, bhint, accumulate, stage2_v)
+                       stage2_channels, stage2_tokens, hint, bhint, accumulate, stage2_v, block_tokens)
 
 
 def status_string(code: int) -> str:

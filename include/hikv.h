@@ -144,7 +144,22 @@ typedef struct hikv_policy {
                               positions: len * ceil(position span / 2^18) work per unit (one
                               pass while the live positions span at most 262144).  Any other
                               value is HIKV_EINVAL. */
+  int32_t block_tokens;    /* eviction granularity ([Blog] Sec. 5, PagedAttention block
+                              fragmentation): 0 or 1, single tokens; P in
+                              2..HIKV_MAX_BLOCK_TOKENS, whole blocks of P consecutive positions
+                              (block id = pos / P; positions >= 0).  A block holding a
+                              protected token is kept whole; the others are ranked by the sum
+                              of their tokens' importance and evicted lowest first (equal sums:
+                              the higher block id first) while more than the budget's tokens
+                              are live, so a unit can end below its budget, or above it when
+                              protected blocks hold more tokens (the capacity must then hold
+                              budget + 2 P).  Every eviction is a bulk cut; none is left
+                              pending.  Stage I with the default launch sequence only
+                              (stage2_channels > 0 or HIKV_PATH_MULTI_LAUNCH: HIKV_EUNSUPPORTED,
+                              as for hikv_evict); other values are HIKV_EINVAL. */
 } hikv_policy;
+
+#define HIKV_MAX_BLOCK_TOKENS 1024
 
 /* Optional outputs of hikv_decode_step for tests, inspection and profiling;
  * every field may be NULL. */
