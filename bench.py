@@ -174,6 +174,13 @@ def main():
             r = run_workload(name, steps=128, warmup=16, layers=args.layers, hint=not args.no_hint, detail=False)
             r.pop("w")
             subs[name] = r
+        # block-granular eviction (blocks of 16 positions) on llama8b's shape
+        r = run_workload("llama8b", steps=128, warmup=16, layers=args.layers, detail=False, block_tokens=16)
+        r.pop("w")
+        r["what"] = ("llama8b with whole blocks of 16 positions evicted (policy block_tokens 16; no length "
+                     "hints: the device's plan); bytes counted with the single-token lengths, within a "
+                     "block of the device's")
+        subs["llama8b_blocks16"] = r
         pts = []
         for b in SWEEP_BUDGETS:
             r = run_workload("llama8b", steps=128, warmup=16, layers=args.layers, hint=not args.no_hint,
@@ -300,7 +307,7 @@ def stream_floor(caches, lens, rb, log, what):
 
 
 def run_workload(name, *, steps, warmup, layers, hint=True, budget_all=None, accumulate=None, prefill=False,
-                 detail=False, keep_data=False):
+                 detail=False, keep_data=False, block_tokens=0):
     """Compression step and cold steady steps of one seeded workload on `layers`
     layer copies (the timed steps: one HIP graph).  With detail: the attention
     launch timed per launch with HIP events, per-step times, warm steps, the
@@ -335,9 +342,15 @@ def run_workload(name, *, steps, warmup, layers, hint=True, budget_all=None, acc
     # other Stage II variants evict in place
     pending_path = (not stage2) or (w.stage2_v == H.HIKV_S2V_TOPK and w.el == 2 and w.head_dim == 128
                                     and w.stage2_tokens <= 2048)
+    if block_tokens:
+        # Whole blocks leave lengths the host cannot foresee (they depend on
+        # the device's importance): no length hints, no pending eviction, and
+        # the host's lengths below (for the byte count) are the single-token
+        # ones, within a block of the device's.
+        hint, pending_path = False, False
     t0 = time.time()
     d = W.generate(w)
-    tag = name if budget_all is None else f"{name}@{budget_all}"
+    tag = (name if budget_all is None else f"{name}@{budget_all}") + (f"/blocks{block_tokens}" if block_tokens else "")
     log(f"[bench] {tag}: inputs generated in {time.time() - t0:.1f}s")
     B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     budget = w.budget_array()
@@ -349,7 +362,7 @@ def run_workload(name, *, steps, warmup, layers, hint=True, budget_all=None, acc
     budget_t = torch.from_numpy(budget).cuda()
     b_arr, b_all = (budget_t, 0) if w.budgets is not None else (None, w.budget_all)
     pol = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
-                        accumulate=w.accumulate, stage2_v=w.stage2_v)
+                        accumulate=w.accumulate, stage2_v=w.stage2_v, block_tokens=block_tokens)
     # One workspace (scratch) serves every layer copy, as it would every layer
     # of a model; each cache carries its own pending-eviction state.
     ws = H.workspace(caches[0].shape, pol)
@@ -382,7 +395,7 @@ def run_workload(name, *, steps, warmup, layers, hint=True, budget_all=None, acc
         if hint:
             p = H.make_policy(b_arr, b_all, w.n_sink, w.n_recent, w.stage2_channels, w.stage2_tokens,
                               budget_hint=budget if b_arr is not None else None,
-                              len_hint=host_len[li], accumulate=w.accumulate, stage2_v=w.stage2_v)
+                              len_hint=host_len[li], accumulate=w.accumulate, stage2_v=w.stage2_v, block_tokens=block_tokens)
         dbg = None
         if events is not None:
             dbg = H.hikv_debug(None, None, None, events[0].cuda_event, events[1].cuda_event)
@@ -422,7 +435,8 @@ def run_workload(name, *, steps, warmup, layers, hint=True, budget_all=None, acc
     comp_us = e0.elapsed_time(e1) * 1e3 / layers
     device_status("device status after compression")
     live_after = np.minimum(w.ctx + 1, budget)
-    assert np.array_equal(caches[0].len.cpu().numpy(), live_after), "compression did not reach the budgets"
+    if not block_tokens:
+        assert np.array_equal(caches[0].len.cpu().numpy(), live_after), "compression did not reach the budgets"
     # (the rows the cut relocates are not counted: the bytes are what any
     # layout must move, every live row read once and the importance updated)
     comp_bytes = BM.decode_step_bytes(B, Hq, Hkv, D, w.el, np.full((B, Hkv), w.ctx + 1), 0)

@@ -231,6 +231,7 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
     a.s2_two = 1;
     if (policy->len_hint) step_host_plan(a, dt, policy->len_hint);
     if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
+      a.bulk_known = 1;
       const int U = shape->batch * shape->n_kv_heads;
       for (int u = 0; u < U; ++u) {
         const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;

@@ -1962,7 +1962,6 @@ __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
   constexpr int CPR = RB / 16, RPP = 256 / CPR;  // threads per row, rows per pass (4 passes)
   const int u = blockIdx.x, tid = threadIdx.x;
   const int ci = tid % CPR, rr = tid / CPR;
-  const int i0 = (int)blockIdx.y * RPP * 4 + rr;  // this group's moves: i0, i0 + RPP, ...
   const int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
   char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
   char *vw = static_cast<char *>(a.v_w) + (size_t)u * a.cap * RB;
@@ -1974,16 +1973,8 @@ __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
   // Four moves per thread group in named registers (arrays of 16-byte
   // vectors are not kept in registers by the compiler).
   const int nm = a.ws.nmoves[u];
-  const int ia = i0, ib = i0 + RPP, ic = i0 + 2 * RPP, id = i0 + 3 * RPP;
   auto ent = [&](const int32_t *l, int i) { return min(max(l[min(i, a.cap - 1)], 0), a.cap - 1); };
-  const int sa = ent(movers, ia), sb = ent(movers, ib), sc = ent(movers, ic), sd = ent(movers, id);
-  const int da = ent(holes, ia), db = ent(holes, ib), dc = ent(holes, ic), dd = ent(holes, id);
-  if ((int)blockIdx.y * RPP * 4 >= nm) return;  // past this unit's moves
   auto row = [&](const char *base, int slot) { return reinterpret_cast<const uint4 *>(base + (size_t)slot * RB)[ci]; };
-  const uint4 ka = row(kw, sa), kb = row(kw, sb), kc = row(kw, sc), kd = row(kw, sd);
-  const uint4 va = row(vw, sa), vb = row(vw, sb), vc = row(vw, sc), vd = row(vw, sd);
-  const int pa = posw[sa], pb = posw[sb], pc = posw[sc], pd = posw[sd];
-  const float xa = impw[sa], xb = impw[sb], xc = impw[sc], xd = impw[sd];
   auto put = [&](int i, int dst, const uint4 &k, const uint4 &v, int p, float x) {
     if (i < nm) {
       reinterpret_cast<uint4 *>(kw + (size_t)dst * RB)[ci] = k;
@@ -1991,14 +1982,36 @@ __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
       if (ci == 0) posw[dst] = p, impw[dst] = x;
     }
   };
-  put(ia, da, ka, va, pa, xa);
-  put(ib, db, kb, vb, pb, xb);
-  put(ic, dc, kc, vc, pc, xc);
-  put(id, dd, kd, vd, pd, xd);
+  // Moves [RPP 4 y, RPP 4 (y + 1)) for y = blockIdx.y, blockIdx.y + gridDim.y,
+  // ... (one y when the host sized the grid to the moves).
+  for (int y = (int)blockIdx.y;; y += (int)gridDim.y) {
+    const int i0 = y * RPP * 4 + rr;  // this group's moves: i0, i0 + RPP, ...
+    const int ia = i0, ib = i0 + RPP, ic = i0 + 2 * RPP, id = i0 + 3 * RPP;
+    const int sa = ent(movers, ia), sb = ent(movers, ib), sc = ent(movers, ic), sd = ent(movers, id);
+    const int da = ent(holes, ia), db = ent(holes, ib), dc = ent(holes, ic), dd = ent(holes, id);
+    if (y * RPP * 4 >= nm) return;  // past this unit's moves
+    const uint4 ka = row(kw, sa), kb = row(kw, sb), kc = row(kw, sc), kd = row(kw, sd);
+    const uint4 va = row(vw, sa), vb = row(vw, sb), vc = row(vw, sc), vd = row(vw, sd);
+    const int pa = posw[sa], pb = posw[sb], pc = posw[sc], pd = posw[sd];
+    const float xa = impw[sa], xb = impw[sb], xc = impw[sc], xd = impw[sd];
+    put(ia, da, ka, va, pa, xa);
+    put(ib, db, kb, vb, pb, xb);
+    put(ic, dc, kc, vc, pc, xc);
+    put(id, dd, kd, vd, pd, xd);
+  }
 }
 
 template <int RB>
 static constexpr int bulk_moves_per_block() { return (256 / (RB / 16)) * 4; }
+// Workgroups per unit of the move launch: one per bulk_moves_per_block moves of
+// the host's bound; a bound that is only the capacity (no caller's lengths)
+// takes at most 8, each looping over its share.
+template <int RB>
+static unsigned moves_grid_y(const StepArgs &a) {
+  const int per = bulk_moves_per_block<RB>();
+  const int gy = max(1, (a.bulk_rows + per - 1) / per);
+  return (unsigned)(a.bulk_known ? gy : min(gy, 8));
+}
 
 // ---------------------------------------------------------------------------
 // Resolution of the pending eviction, one wave per unit: the dead slot (the
@@ -2091,9 +2104,7 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
     }
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int per = bulk_moves_per_block<D * EL>();
-    const unsigned gy = (unsigned)max(1, (a.bulk_rows + per - 1) / per);
-    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, gy), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, moves_grid_y<D * EL>(a)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -2124,9 +2135,7 @@ static hipError_t step_go_s2(const StepArgs &a, hipStream_t s, hipEvent_t ev0, h
   if (a.bulk_split) {
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int per = bulk_moves_per_block<D * EL>();
-    const unsigned gy = (unsigned)max(1, (a.bulk_rows + per - 1) / per);
-    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, gy), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, moves_grid_y<D * EL>(a)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
