@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-hint", action="store_true", help="do not pass host lengths")
+    ap.add_argument("--block-tokens", type=int, default=0,
+                    help="evict whole blocks of this many positions (policy block_tokens; 0: single tokens)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy this many bytes device-to-device 4 times (a plain copy "
                          "kernel of known size, for calibrating memory counters)")
@@ -146,7 +148,7 @@ def main():
                                                 "logit": H.HIKV_ACC_LOGIT}[args.accumulate]
     head = run_workload(args.workload, steps=args.steps, warmup=args.warmup, layers=args.layers,
                         hint=not args.no_hint, accumulate=acc, prefill=args.prefill, detail=True,
-                        keep_data=not args.no_cpu_baseline)
+                        keep_data=not args.no_cpu_baseline, block_tokens=args.block_tokens)
     launch_us = launch_floor_us()
     log(f"[bench] dependent empty launch in a graph: {launch_us:.2f} us")
 
@@ -162,13 +164,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(head["w"], head["data"], args.cpu_seconds)
+        cpu = cpu_baseline(head["w"], head["data"], args.cpu_seconds, args.block_tokens)
         log(f"[bench] cpu oracle: {cpu}")
     head.pop("data", None)
     w = head.pop("w")
 
     subs, sweep = None, None
-    if not args.quick and args.workload == "headkv32k":
+    if not args.quick and args.workload == "headkv32k" and not args.block_tokens:
         subs = {}
         for name in SUB_WORKLOADS:
             r = run_workload(name, steps=128, warmup=16, layers=args.layers, hint=not args.no_hint, detail=False)
@@ -191,7 +193,7 @@ def main():
         sweep = {"workload": "llama8b (batch 8, 32 q / 8 KV heads, D 128, bf16, 8192-token prefill, sinks 4, "
                              "recent 128), one budget for every unit", "points": pts}
 
-    tr = measured_traffic() if args.workload == "headkv32k" else None
+    tr = measured_traffic() if args.workload == "headkv32k" and not args.block_tokens else None
     line = {
         "metric": "decode steps/s and achieved KV HBM GB/s (fraction of 8 TB/s) per budget",
         "value": round(head["steps_per_s"], 1),
@@ -414,7 +416,8 @@ def run_workload(name, *, steps, warmup, layers, hint=True, budget_all=None, acc
             live = old + 1 - pending
             host_len[li] = np.where(live > budget + 1, budget, np.where(pending, old, old + 1)).astype(np.int32)
 
-    res = {"w": w, "text": workload_text(w, budget, full)}
+    res = {"w": w, "text": workload_text(w, budget, full)
+           + (f", whole blocks of {block_tokens} positions evicted" if block_tokens else "")}
     stream = torch.cuda.current_stream()
     if detail and (prefill or w.accumulate == H.HIKV_ACC_RECENT) and not full:
         res["prefill_scores"] = measure_prefill(w, caches[0], budget, log)
@@ -661,7 +664,7 @@ def kernel_text(w):
             "HIP events per launch)")
 
 
-def cpu_baseline(w, d, seconds):
+def cpu_baseline(w, d, seconds, block_tokens=0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     its own compression step, then steady steps until `seconds` have passed."""
     from oracle import ref
@@ -669,7 +672,7 @@ def cpu_baseline(w, d, seconds):
     budget = w.budget_array()
     kw = dict(budget=budget, n_sink=w.n_sink, n_recent=w.n_recent, debug=False,
               stage2_channels=w.stage2_channels, stage2_tokens=w.stage2_tokens,
-              accumulate=w.accumulate, stage2_v=w.stage2_v)
+              accumulate=w.accumulate, stage2_v=w.stage2_v, block_tokens=block_tokens)
     tc = time.perf_counter()
     ref.decode_step(st, w.n_q_heads, d["q"][0], d["k_new"][0], d["v_new"][0], d["new_pos"][0], **kw)
     tc = time.perf_counter() - tc
