@@ -60,7 +60,8 @@ extern "C" {
 /* Status codes. */
 #define HIKV_OK 0
 #define HIKV_EINVAL (-1)       /* null pointer, bad shape/policy, workspace too small */
-#define HIKV_EUNSUPPORTED (-2) /* head_dim not 64/128, group size not 1/2/4/8, too many units, no gfx950 */
+#define HIKV_EUNSUPPORTED (-2) /* head_dim not 64/128, group size not 1/2/4/8, too many units, no gfx950;
+                                  block_tokens >= 2 with Stage II, the multi-launch path or hikv_evict */
 #define HIKV_EDEVICE (-3)      /* a HIP runtime call or kernel launch failed */
 #define HIKV_ECAPACITY (-4)    /* device: len + 1 > capacity for some unit */
 #define HIKV_EBUDGET (-5)      /* device: budget < n_sink or budget > capacity for some unit */
