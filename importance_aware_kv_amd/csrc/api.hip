@@ -145,6 +145,23 @@ int check_decode_args(const hikv_shape *shape, const hikv_cache *cache, const hi
   return HIKV_OK;
 }
 
+// The move launch of a bulk cut from the host's bound on each unit's moves
+// (mvr): one workgroup per bulk_moves_per_wg moves of each unit, listed in
+// a.hp.mvb, when the host plan covers every unit; else one row of workgroups
+// per unit, sized for the largest bound.
+void moves_plan(StepArgs &a, const int32_t *mvr, int dtype) {
+  a.moves_flat = 0;
+  if (!a.bulk_split || a.hp.n != a.n_units || a.n_units > kHostPlanUnits) return;
+  const int per = bulk_moves_per_wg(a.D * (dtype == HIKV_BF16 ? 2 : 4));
+  int base = 0;
+  for (int u = 0; u < a.n_units; ++u) {
+    a.hp.mvb[u] = base;
+    base += (mvr[u] + per - 1) / per;
+  }
+  a.hp.mvb[a.n_units] = base;
+  a.moves_flat = base > 0 ? 1 : 0;
+}
+
 __global__ void k_zero_words(int32_t *p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
@@ -190,6 +207,7 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
       if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
         a.bulk_known = 1;
         const int U = shape->batch * shape->n_kv_heads;
+        int32_t mvr[kHostPlanUnits] = {};  // each unit's bound on its moves
         for (int u = 0; u < U; ++u) {
           const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
           const int len = policy->len_hint[u];
@@ -200,6 +218,7 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
             if (len + 1 > beta) {
               a.bulk_split = 1;
               a.bulk_rows = max(a.bulk_rows, min(len + 1, len + 2 - beta + a.block));
+              if (u < kHostPlanUnits) mvr[u] = min(len + 1, len + 2 - beta + a.block);
             }
             continue;
           }
@@ -209,8 +228,10 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
             // survivors at or above the budget: at most the budget, and at
             // most the len + 1 - beta slots there
             a.bulk_rows = max(a.bulk_rows, min(beta, len + 1 - beta));
+            if (u < kHostPlanUnits) mvr[u] = min(beta, len + 1 - beta);
           }
         }
+        moves_plan(a, mvr, dt);
       } else if (a.block) {  // any unit may be cut: the cut's launches always run
         a.bulk_split = 1;
         a.bulk_rows = a.cap;
@@ -233,6 +254,7 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
     if (policy->len_hint && (!policy->budget || policy->budget_hint)) {
       a.bulk_known = 1;
       const int U = shape->batch * shape->n_kv_heads;
+      int32_t mvr[kHostPlanUnits] = {};
       for (int u = 0; u < U; ++u) {
         const int beta = policy->budget ? policy->budget_hint[u] : policy->budget_all;
         const int len = policy->len_hint[u];
@@ -240,8 +262,10 @@ int run_decode(const hikv_shape *shape, const hikv_cache *cache, const hikv_poli
         if (live - beta > 1) {
           a.bulk_split = 1;
           a.bulk_rows = max(a.bulk_rows, min(beta, len + 1 - beta));
+          if (u < kHostPlanUnits) mvr[u] = min(beta, len + 1 - beta);
         }
       }
+      moves_plan(a, mvr, dt);
     } else {
       a.bulk_split = 1;
       a.bulk_rows = a.cap;

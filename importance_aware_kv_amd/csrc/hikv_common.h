@@ -159,7 +159,14 @@ struct HostPlan {
   int32_t n, T, ntiles;
   int32_t base[kHostPlanUnits + 1];  // first tile of each unit; base[n] = ntiles
   int32_t L[kHostPlanUnits];         // tokens after the append (0: unit not planned)
+  // A bulk cut's row moves, one workgroup per chunk of bulk_moves_per_wg moves
+  // of each unit's bound: the first chunk of each unit; mvb[n] = chunks.
+  int32_t mvb[kHostPlanUnits + 1];
 };
+
+// Row moves one workgroup of the bulk cut's move launch makes (256 threads,
+// 16 bytes of a row per thread, four rows per thread group).
+constexpr int bulk_moves_per_wg(int rb) { return (256 / (rb / 16)) * 4; }
 
 // Everything a decode-step kernel needs, passed by value.
 struct StepArgs {
@@ -184,6 +191,7 @@ struct StepArgs {
   int32_t bulk_known;        // the host foresaw every bulk cut of the step (lengths and budgets known)
   int32_t block;             // block-granular eviction: positions per block (>= 2), or 0 (single tokens)
   int32_t s2_two;            // Stage II (exact top-k_T V side) in the two-launch sequence
+  int32_t moves_flat;        // the move launch runs one workgroup per chunk of hp.mvb
   const void *q, *k_new, *v_new;
   const int32_t *new_pos;
   float *out;

@@ -1960,7 +1960,17 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
 template <int RB>
 __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
   constexpr int CPR = RB / 16, RPP = 256 / CPR;  // threads per row, rows per pass (4 passes)
-  const int u = blockIdx.x, tid = threadIdx.x;
+  static_assert(RPP * 4 == bulk_moves_per_wg(RB), "moves per workgroup");
+  const int tid = threadIdx.x;
+  int u = blockIdx.x, y0 = blockIdx.y;
+  if (a.moves_flat) {
+    // One chunk of one unit's moves: the unit is the number of units whose
+    // chunks end at or before this workgroup's.
+    const int lane = tid & 63;
+    const int end = lane < a.n_units ? a.hp.mvb[lane + 1] : 0x7fffffff;
+    u = (int)__builtin_amdgcn_readfirstlane(__popcll(__ballot(end <= (int)blockIdx.x)));
+    y0 = (int)blockIdx.x - a.hp.mvb[u];
+  }
   const int ci = tid % CPR, rr = tid / CPR;
   const int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
   char *kw = static_cast<char *>(a.k_w) + (size_t)u * a.cap * RB;
@@ -1982,9 +1992,9 @@ __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
       if (ci == 0) posw[dst] = p, impw[dst] = x;
     }
   };
-  // Moves [RPP 4 y, RPP 4 (y + 1)) for y = blockIdx.y, blockIdx.y + gridDim.y,
-  // ... (one y when the host sized the grid to the moves).
-  for (int y = (int)blockIdx.y;; y += (int)gridDim.y) {
+  // Moves [RPP 4 y, RPP 4 (y + 1)) for y = y0, y0 + gridDim.y, ... (one y
+  // when the host sized the grid to the moves).
+  for (int y = y0;; y += (int)gridDim.y) {
     const int i0 = y * RPP * 4 + rr;  // this group's moves: i0, i0 + RPP, ...
     const int ia = i0, ib = i0 + RPP, ic = i0 + 2 * RPP, id = i0 + 3 * RPP;
     const int sa = ent(movers, ia), sb = ent(movers, ib), sc = ent(movers, ic), sd = ent(movers, id);
@@ -1998,19 +2008,20 @@ __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
     put(ib, db, kb, vb, pb, xb);
     put(ic, dc, kc, vc, pc, xc);
     put(id, dd, kd, vd, pd, xd);
+    if (a.moves_flat) return;  // one chunk per workgroup
   }
 }
 
+// The move launch's grid: one workgroup per chunk of the host's per-unit
+// bounds (moves_flat), else per unit one workgroup per bulk_moves_per_wg
+// moves of the largest bound; a bound that is only the capacity (no caller's
+// lengths) takes at most 8 per unit, each looping over its share.
 template <int RB>
-static constexpr int bulk_moves_per_block() { return (256 / (RB / 16)) * 4; }
-// Workgroups per unit of the move launch: one per bulk_moves_per_block moves of
-// the host's bound; a bound that is only the capacity (no caller's lengths)
-// takes at most 8, each looping over its share.
-template <int RB>
-static unsigned moves_grid_y(const StepArgs &a) {
-  const int per = bulk_moves_per_block<RB>();
+static dim3 moves_grid(const StepArgs &a) {
+  if (a.moves_flat) return dim3((unsigned)a.hp.mvb[a.hp.n]);
+  const int per = bulk_moves_per_wg(RB);
   const int gy = max(1, (a.bulk_rows + per - 1) / per);
-  return (unsigned)(a.bulk_known ? gy : min(gy, 8));
+  return dim3((unsigned)a.n_units, (unsigned)(a.bulk_known ? gy : min(gy, 8)));
 }
 
 // ---------------------------------------------------------------------------
@@ -2104,7 +2115,7 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
     }
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, moves_grid_y<D * EL>(a)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), moves_grid<D * EL>(a), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -2135,7 +2146,7 @@ static hipError_t step_go_s2(const StepArgs &a, hipStream_t s, hipEvent_t ev0, h
   if (a.bulk_split) {
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bulk_moves<D * EL>), dim3((unsigned)a.n_units, moves_grid_y<D * EL>(a)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_moves<D * EL>), moves_grid<D * EL>(a), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
