@@ -59,15 +59,24 @@ struct Ws {
   float *chunk_acc;     // [n_units][ceil(cap/D)][G][D] Stage II chunked V side: each chunk's P.V
   int32_t *chunk_cnt;   // [n_units][ceil(cap/D)][G] tokens each chunk kept per q-head
   int32_t *order;       // [n_units][cap] Stage II chunked V side: the live slots in position order
-  uint32_t *bhist;      // [n_units][imp_blocks(cap)][kBulkBins] bulk cut: each block's key histogram
+  uint32_t *uhist;      // [n_units][kBulkHistWords] bulk cut: the unit's key histogram (kBulkBins
+                        //   words), then its record (kBulkRec: candidates, bin, need, count, mode)
   int32_t *bsel;        // [n_units][4] bulk cut: tokens to evict, budget, tokens, flag (1: cut in bulk)
   float *logits2;       // [n_units][cap][G] Stage II in two launches: the exact logits (raw q.k)
   uint64_t *s2keys;     // [n_units][G][cap] Stage II in two launches: selection keys of long units
+  uint64_t *cand;       // [n_units][kBulkCand] bulk cut: the keys of the threshold's bin
+  int32_t *cslot;       // [n_units][kBulkCand] ... and their slots
+  uint64_t *ebits;      // [n_units][ceil(cap / 64)] bulk cut: the slots whose keys lie below the bin
 };
 
-constexpr int kWsParts = 26;
-// Bulk cut: a histogram of the eviction keys' top kBulkBits bits per importance block.
+constexpr int kWsParts = 29;
+// Bulk cut: a histogram of the eviction keys' top kBulkBits bits per unit,
+// and the keys of the bin that holds the threshold, gathered when at most
+// kBulkCand.
 constexpr int kBulkBits = 11, kBulkBins = 1 << kBulkBits, kBulkShift = 64 - kBulkBits;
+constexpr int kBulkCand = 4096;
+constexpr int kBulkRec = kBulkBins;             // the record's first word in a unit's uhist row
+constexpr int kBulkHistWords = kBulkBins + 64;  // a unit's uhist row (16-byte multiple)
 struct WsSizes {
   size_t off[kWsParts];
   size_t total;
@@ -103,10 +112,13 @@ inline WsSizes ws_sizes(int B, int Hq, int Hkv, int D, int cap, int kT, bool chu
       sizeof(float) * U * NC * G * D,  // chunk_acc
       sizeof(int32_t) * U * NC * G,    // chunk_cnt
       order ? sizeof(int32_t) * U * cap : 0,   // order (chunked Stage II V side, block eviction)
-      sizeof(uint32_t) * U * (size_t)imp_blocks(cap) * kBulkBins,  // bhist
+      sizeof(uint32_t) * U * (size_t)kBulkHistWords,  // uhist
       sizeof(int32_t) * 4 * U,         // bsel
       (kT > 0 && !chunks) ? sizeof(float) * U * cap * G : 0,     // logits2
       (kT > 0 && !chunks) ? sizeof(uint64_t) * U * G * cap : 0,  // s2keys
+      sizeof(uint64_t) * U * kBulkCand,  // cand
+      sizeof(int32_t) * U * kBulkCand,   // cslot
+      sizeof(uint64_t) * U * (size_t)((cap + 63) / 64),  // ebits
   };
   WsSizes w;
   size_t o = 0;
@@ -143,10 +155,13 @@ inline Ws ws_carve(void *base, const WsSizes &s) {
   w.chunk_acc = reinterpret_cast<float *>(b + s.off[19]);
   w.chunk_cnt = reinterpret_cast<int32_t *>(b + s.off[20]);
   w.order = reinterpret_cast<int32_t *>(b + s.off[21]);
-  w.bhist = reinterpret_cast<uint32_t *>(b + s.off[22]);
+  w.uhist = reinterpret_cast<uint32_t *>(b + s.off[22]);
   w.bsel = reinterpret_cast<int32_t *>(b + s.off[23]);
   w.logits2 = reinterpret_cast<float *>(b + s.off[24]);
   w.s2keys = reinterpret_cast<uint64_t *>(b + s.off[25]);
+  w.cand = reinterpret_cast<uint64_t *>(b + s.off[26]);
+  w.cslot = reinterpret_cast<int32_t *>(b + s.off[27]);
+  w.ebits = reinterpret_cast<uint64_t *>(b + s.off[28]);
   return w;
 }
 
@@ -205,6 +220,15 @@ struct StepArgs {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
   atomicCAS(status, 0, code);
+}
+
+// A bulk cut's per-unit histograms and records start at zero: the attention
+// launch, which precedes every launch that adds to them, clears them.
+__device__ __forceinline__ void bulk_hist_clear(const StepArgs &a) {
+  const int n = a.n_units * (kBulkHistWords / 4);
+  uint4 *p = reinterpret_cast<uint4 *>(a.ws.uhist);
+  for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += (int)(gridDim.x * blockDim.x))
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 template <int CTRL>

@@ -26,10 +26,11 @@
 //   written into its slot, so no row moves in the steady state.  A unit that
 //   must shed more than one token (the first step after a prefill) is cut in
 //   bulk by a radix select; with the caller's lengths and budgets the cut is
-//   spread over the unit's importance blocks (keys and a key histogram each)
-//   and finished by two more launches (k_bulk_select: the threshold and the
-//   lists of rows to move; k_bulk_moves: the moves).  Output blocks combine
-//   the tiles' partials.
+//   spread over the unit's importance blocks (keys, and a key histogram for
+//   the unit) and finished by three more launches (k_bulk_mark: the bin of
+//   the threshold, the slots below it and the bin's keys; k_bulk_select: the
+//   threshold and the lists of rows to move; k_bulk_moves: the moves).
+//   Output blocks combine the tiles' partials.
 
 #include <hip/hip_ext.h>
 
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   constexpr int RB = LY::RB;
   constexpr int QB = G * D * EL;  // the group's queries, bytes
   static_assert(QB <= 4 * 1024, "one q DMA instruction per wave");
+  if (a.bulk_split) bulk_hist_clear(a);
   // LDS: NSUB sub-chunks, each K then V; the group's queries.
   __shared__ __attribute__((aligned(16))) char smem[NSUB * 2 * SUBB];
   __shared__ __attribute__((aligned(16))) char qs[QB];
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   __shared__ float sm_ml[4][G][2];
   __shared__ __attribute__((aligned(16))) PendLds pd;
   float(*sm_acc)[G][64] = reinterpret_cast<float(*)[G][64]>(smem);  // reused after the loop
+  if (a.bulk_split) bulk_hist_clear(a);
   static_assert(4 * G * 64 * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -599,6 +602,7 @@ template <int G, int NSUB>
 __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
   constexpr int EL = 2, D = 128, RB = D * EL, TS = 64, SUBB = TS * RB, QB = G * D * EL, NC = 2 * G;
   static_assert(NC <= 16 && NSUB <= 3, "exact and reduced columns fit one 16-column tile; ring offsets fit");
+  if (a.bulk_split) bulk_hist_clear(a);
   __shared__ __attribute__((aligned(16))) char smem[NSUB * SUBB];
   __shared__ __attribute__((aligned(16))) char qs[QB];
   __shared__ __attribute__((aligned(16))) float lgs[2][TS][NC];  // a sub-chunk's scores, two buffers
@@ -1519,9 +1523,12 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       batch(nb0);  // the block's tokens: one batch
       if (split) {
         __syncthreads();  // the histogram, s_newimp
-        if (thist) {
-          uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
-          for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
+        if (thist) {  // the block's counts join the unit's histogram
+          uint32_t *dst = a.ws.uhist + (size_t)u * kBulkHistWords;
+          for (int i = tid; i < kBulkBins; i += kT2) {
+            const uint32_t c = whist[i];
+            if (c) atomicAdd(&dst[i], c);
+          }
         }
         if (nb1 == L) {  // the block holding slot Lold places the new token
           if (tid < 2 * NR) reinterpret_cast<uint4 *>((tid < NR ? kw : vw) + (size_t)fs * RB)[tid % NR] =
@@ -1685,100 +1692,302 @@ __global__ __launch_bounds__(kT2) void k_block_keys(StepArgs a) {
     if (!prot) atomicAdd(&whist[(int)(key >> kBulkShift)], (uint32_t)m);
   }
   __syncthreads();
-  uint32_t *dst = a.ws.bhist + ((size_t)u * imp_blocks(a.cap) + r) * kBulkBins;
-  for (int i = tid; i < kBulkBins; i += kT2) dst[i] = whist[i];
+  uint32_t *dst = a.ws.uhist + (size_t)u * kBulkHistWords;
+  for (int i = tid; i < kBulkBins; i += kT2) {
+    const uint32_t c = whist[i];
+    if (c) atomicAdd(&dst[i], c);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Third launch of a step that cuts units in bulk (when the host can tell),
-// one workgroup per unit.  The importance blocks left every slot's eviction
-// key and a histogram of the keys' top kBulkBits bits each; the n_evict
-// smallest keys go:
-//  1. the summed histograms give the bin that holds the n_evict-th smallest
-//     key (need: how many of the bin's keys go; cnt: how many it holds);
-//     while the bin holds more than kBulkCand keys, one pass over the keys
-//     histograms the next kBulkBits bits of those in it (a narrower bin);
-//  2. one pass over the keys marks the slots whose key lies below the bin
-//     (an LDS bitmap, one bit per slot) and gathers the bin's keys and slots;
-//  3. the need-th smallest of those is found in LDS (radix passes of 8 bits
-//     below the bits the bin fixes), and their slots up to it are marked;
-//  4. the holes (marked slots below the budget) and movers (unmarked live
-//     slots at or above it) are listed in ascending order for the moves.
-// Each pass over the keys has up to kBulkKpt of them per thread in flight.
-// Units longer than the bitmap covers list from the keys instead.
+// A bulk cut (when the host can tell, and always for whole blocks) ends in
+// launches of its own.  The importance blocks (or k_block_keys) leave every
+// slot's eviction key (~0: protected) and add a histogram of the keys' top
+// kBulkBits bits to the unit's, which the attention launch cleared.  The
+// n_evict smallest keys go:
+//  - k_bulk_mark, one workgroup per kMarkSlots slots of a unit: the histogram's
+//    prefix gives the bin holding the n_evict-th smallest key (need: how many
+//    of the bin's keys go; cnt: how many it holds).  Each workgroup marks its
+//    slots whose key lies below the bin in a bitmap (one word per 64 slots)
+//    and appends the bin's keys and slots to the unit's candidate list; the
+//    first leaves the bin in the unit's record.  A bin of more than kBulkCand
+//    keys, or a unit longer than the select's LDS bitmap, is left to the select
+//    (kCutSlow).
+//  - k_bulk_select, one workgroup per unit: the need-th smallest candidate
+//    (radix passes in LDS) is the threshold; the candidates up to it join the
+//    bitmap, and the holes (marked slots below the new length) and movers
+//    (unmarked live slots at or above it) are listed in ascending slot order
+//    for k_bulk_moves.  With kCutSlow it finds the bin itself, narrowing it by
+//    passes over the keys until it holds at most kBulkCand keys, and gathers it.
+// Whole blocks: a block's tokens share one key, so the keys up to the threshold
+// are whole blocks and the new length is L less those; when protected blocks
+// leave fewer candidates than the need every candidate goes, and with none the
+// unit stays as it is (kCutKeep).
 // ---------------------------------------------------------------------------
-constexpr int kBulkCand = 4096;        // keys of the threshold's bin gathered in LDS
-constexpr int kBulkMapSlots = 1 << 18;  // slots the LDS bitmap covers (32 KB)
-constexpr int kBulkKpt = 16;            // keys per thread per pass in flight
+constexpr int kBulkMapSlots = 1 << 18;  // slots the select's LDS bitmap covers (32 KB)
+constexpr int kMarkKpt = 8, kMarkSlots = kMarkKpt * kT2;  // k_bulk_mark: keys per thread, per workgroup
+constexpr int kBulkKpt = 16;            // keys per thread per pass in flight (kCutSlow)
+// The record, words kBulkRec.. of a unit's uhist row: candidates appended, bin,
+// need, cnt, mode.
+enum : int { kCutNone = 0, kCutFast = 1, kCutSlow = 2, kCutKeep = 3, kCutError = 4 };
+
+struct BinPick {
+  int bin, need, cnt, tot;
+};
+
+// The bin of a 2 NT-bin histogram (bins 2 tid, 2 tid + 1 in c0, c1) holding
+// the need-th smallest counted key (bin -1: fewer keys), and the count of every
+// key; every thread sees the same *bp on return.
+template <int NT>
+__device__ void pick_bin(uint32_t c0, uint32_t c1, int need, int *sc, BinPick *bp) {
+  const int tid = threadIdx.x;
+  if (tid == 0) bp->bin = -1;
+  int tot;
+  const int ex = block_excl_scan<NT>((int)(c0 + c1), sc, &tot);  // (its barriers order the writes)
+  if (tid == 0) bp->tot = tot;
+  if (ex < need && ex + (int)(c0 + c1) >= need) {
+    const bool first = ex + (int)c0 >= need;
+    bp->bin = first ? 2 * tid : 2 * tid + 1;
+    bp->need = first ? need - ex : need - ex - (int)c0;
+    bp->cnt = first ? (int)c0 : (int)c1;
+  }
+  __syncthreads();
+}
+
+// The cut's bin from the unit's histogram, k keys to go.  Whole blocks: fewer
+// candidates than k all go (none: kCutKeep).  Returns kCutFast or the mode
+// that ends the cut.
+template <int NT>
+__device__ int cut_bin(uint32_t c0, uint32_t c1, int k, bool blocks, int *sc, BinPick *bp) {
+  pick_bin<NT>(c0, c1, k, sc, bp);
+  if (bp->bin < 0 && blocks) {
+    const int tot = bp->tot;
+    __syncthreads();  // every thread has read *bp
+    if (tot == 0) return kCutKeep;
+    pick_bin<NT>(c0, c1, tot, sc, bp);
+  }
+  return bp->bin < 0 ? kCutError : kCutFast;
+}
+
+__global__ __launch_bounds__(kT2) void k_bulk_mark(StepArgs a) {
+  static_assert(kBulkBins == 2 * kT2, "two histogram bins per thread");
+  constexpr int KPT = kMarkKpt;
+  __shared__ int sc[kNW2];
+  __shared__ BinPick bp;
+  __shared__ uint64_t lk[kBulkCand];
+  __shared__ int ls[kBulkCand];
+  __shared__ int s_nc, s_base;
+  const int u = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t *uh = a.ws.uhist + (size_t)u * kBulkHistWords;
+  const uint64_t *keys = a.ws.bkeys + (size_t)u * a.cap;
+  const int i0 = r * kMarkSlots;
+  // Issued together: the cut's parameters, the histogram's two bins, the keys.
+  const int4 bs = reinterpret_cast<const int4 *>(a.ws.bsel)[u];
+  const uint2 hv = reinterpret_cast<const uint2 *>(uh)[tid];
+  uint64_t kk[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) kk[j] = keys[min(i0 + j * kT2 + tid, a.cap - 1)];
+  if (bs.w != 1) return;  // not cut in bulk
+  const int k = bs.x, L = bs.z;
+  if (i0 >= L) return;
+  if (tid == 0) s_nc = 0;
+  int mode = cut_bin<kT2>(hv.x, hv.y, k, a.block != 0, sc, &bp);
+  const int bin = bp.bin, need = bp.need, cnt = bp.cnt;
+  if (mode == kCutFast && (cnt > kBulkCand || L > kBulkMapSlots)) mode = kCutSlow;
+  if (r == 0 && tid == 0) {
+    uh[kBulkRec + 1] = (uint32_t)bin;
+    uh[kBulkRec + 2] = (uint32_t)need;
+    uh[kBulkRec + 3] = (uint32_t)cnt;
+    uh[kBulkRec + 4] = (uint32_t)mode;
+  }
+  if (mode != kCutFast) return;
+  const bool all = need == cnt;  // the whole bin goes
+  uint64_t *ebits = a.ws.ebits + (size_t)u * ((a.cap + 63) / 64);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int n = i0 + j * kT2 + tid;
+    const bool valid = n < L && kk[j] != ~0ull;
+    const int top = (int)(kk[j] >> kBulkShift);
+    const uint64_t m = __ballot(valid && (top < bin || (all && top == bin)));
+    const int s0 = i0 + j * kT2 + wave * 64;  // the wave's first slot
+    if (lane == 0 && s0 < L) ebits[s0 / 64] = m;
+    const bool c = valid && !all && top == bin;
+    const uint64_t mc = __ballot(c);
+    if (mc) {  // one LDS atomic per wave
+      int b0 = 0;
+      if (lane == 0) b0 = atomicAdd(&s_nc, __popcll(mc));
+      b0 = __shfl(b0, 0);
+      const int i = b0 + __popcll(mc & ((1ull << lane) - 1ull));
+      if (c && i < kBulkCand) {
+        lk[i] = kk[j];
+        ls[i] = n;
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = min(s_nc, kBulkCand);
+  if (nc == 0) return;
+  if (tid == 0) s_base = (int)atomicAdd(&uh[kBulkRec], (uint32_t)s_nc);
+  __syncthreads();
+  const int base = s_base;
+  uint64_t *cand = a.ws.cand + (size_t)u * kBulkCand;
+  int32_t *cslot = a.ws.cslot + (size_t)u * kBulkCand;
+  for (int i = tid; i < nc && base + i < kBulkCand; i += kT2) {
+    cand[base + i] = lk[i];
+    cslot[base + i] = ls[i];
+  }
+}
+
+// Exclusive prefix sums of two values over the block, in one exchange; sc
+// holds 2 NT / 64 words.
+template <int NT>
+__device__ void block_excl_scan2(int va, int vb, int *sc, int *ea, int *eb, int *ta, int *tb) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ia = va, ib = vb;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ya = __shfl_up(ia, off), yb = __shfl_up(ib, off);
+    if (lane >= off) ia += ya, ib += yb;
+  }
+  if (lane == 63) sc[wave] = ia, sc[NW + wave] = ib;
+  __syncthreads();
+  int ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int xa = sc[w], xb = sc[NW + w];
+    if (w < wave) ba += xa, bb += xb;
+    sa += xa;
+    sb += xb;
+  }
+  *ta = sa;
+  *tb = sb;
+  *ea = ba + ia - va;
+  *eb = bb + ib - vb;
+  __syncthreads();  // sc is free for the next call
+}
 
 template <int RB>
 __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   static_assert(kBulkBins == 2 * kT2, "two histogram bins per thread");
   constexpr int NT = kT2, KPT = kBulkKpt, NMW = kBulkMapSlots / 64;
+  static_assert(NMW == 4 * NT && kBulkCand == 4 * NT, "four bitmap words and four candidates per thread");
   __shared__ uint32_t h[kBulkBins];
   __shared__ uint64_t ck[kBulkCand];
   __shared__ int cs[kBulkCand];
   __shared__ uint64_t eb[NMW];
-  __shared__ int sc[kNW2];
-  __shared__ int s_bin, s_need, s_cnt, s_nc, s_tot;
+  __shared__ int sc[2 * kNW2];
+  __shared__ BinPick bp;
+  __shared__ int s_bin, s_need, s_cnt, s_nc;
   const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t *uh = a.ws.uhist + (size_t)u * kBulkHistWords;
+  // Issued together (one round trip): the cut's parameters, the record
+  // k_bulk_mark left, and what it gathered -- the bitmap words and the
+  // candidates, from clamped addresses, used only in kCutFast.
   const int4 bs = reinterpret_cast<const int4 *>(a.ws.bsel)[u];
+  const int4 rec = reinterpret_cast<const int4 *>(uh + kBulkRec)[0];  // candidates, bin, need, cnt
+  const int mode = (int)uh[kBulkRec + 4];
+  const int nwc = (a.cap + 63) / 64;
+  uint64_t ev[4], cv[4];
+  int sv[4];
+  {
+    const uint64_t *cand = a.ws.cand + (size_t)u * kBulkCand;
+    const int32_t *cslot = a.ws.cslot + (size_t)u * kBulkCand;
+    const uint64_t *ebits = a.ws.ebits + (size_t)u * nwc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + q * NT;
+      ev[q] = ebits[min(i, nwc - 1)];
+      cv[q] = cand[i];
+      sv[q] = cslot[i];
+    }
+  }
   if (bs.w != 1) return;  // not cut in bulk
-  const int k = bs.x, beta = bs.y, L = bs.z;
+  const int beta = bs.y, L = bs.z;
   const uint64_t *keys = a.ws.bkeys + (size_t)u * a.cap;
   // The unit's length after the cut: the budget, or, when whole blocks go
   // (every key of a block is the same), L less every key up to the threshold.
   int newlen = beta;
-
-  // The bin of a 2 x kT2-bin histogram (bins 2 tid, 2 tid + 1 in c0, c1)
-  // holding the need-th smallest counted key.
-  auto find_bin = [&](uint32_t c0, uint32_t c1, int need) {
-    if (tid == 0) s_bin = -1;
-    int tot;
-    const int ex = block_excl_scan<NT>((int)(c0 + c1), sc, &tot);
-    if (tid == 0) s_tot = tot;
-    if (ex < need && ex + (int)(c0 + c1) >= need) {
-      const bool first = ex + (int)c0 >= need;
-      s_bin = first ? 2 * tid : 2 * tid + 1;
-      s_need = first ? need - ex : need - ex - (int)c0;
-      s_cnt = first ? (int)c0 : (int)c1;
-    }
-    __syncthreads();
-  };
-
-  // 1. The threshold's bin.
-  {
-    const int nbk = (L + kImpChunk - 1) / kImpChunk;
-    const uint32_t *bh = a.ws.bhist + (size_t)u * imp_blocks(a.cap) * kBulkBins + 2 * tid;
-    uint32_t c0 = 0, c1 = 0;
-#pragma unroll 4
-    for (int r = 0; r < nbk; ++r) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(bh + (size_t)r * kBulkBins);
-      c0 += v.x;
-      c1 += v.y;
-    }
-    find_bin(c0, c1, k);
-    // Whole blocks: protected blocks can hold more than the budget leaves,
-    // and then every candidate goes (none at all: the unit stays as it is).
-    if (s_bin < 0 && a.block) {
-      const int tot = s_tot;
-      __syncthreads();
-      if (tot == 0) {
-        if (tid == 0) a.len[u] = L;
-        return;
-      }
-      find_bin(c0, c1, tot);
-    }
+  if (mode == kCutKeep) {
+    if (tid == 0) a.len[u] = L;
+    return;
   }
-  if (s_bin < 0) {  // fewer candidates than tokens to evict: cannot happen for single tokens
+  if (mode != kCutFast && mode != kCutSlow) {  // fewer candidates than tokens to evict: cannot happen
     if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
     return;
   }
-  uint64_t prefix = (uint64_t)s_bin;  // the bin: the keys' top pbits bits
-  int pbits = kBulkBits, need = s_need, cnt = s_cnt;
-  while (cnt > kBulkCand && pbits < 64) {
-    const int nb = min(kBulkBits, 64 - pbits), sh = 64 - pbits - nb;
-    for (int i = tid; i < kBulkBins; i += NT) h[i] = 0u;
+  uint64_t prefix;  // the bin: the keys' top pbits bits
+  int pbits = kBulkBits, need, cnt;
+  const bool use_map = L <= kBulkMapSlots;
+  if (mode == kCutFast) {
+    // The bin, its candidates and the bitmap below it, as k_bulk_mark left
+    // them.
+    prefix = (uint64_t)rec.y;
+    need = rec.z;
+    cnt = rec.w;
+    const int nw = (L + 63) / 64;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + q * NT;
+      if (i < nw) eb[i] = ev[q];
+      if (i < rec.x) {
+        ck[i] = cv[q];
+        cs[i] = min(max(sv[q], 0), L - 1);
+      }
+    }
+    if (rec.x != (need == cnt ? 0 : cnt)) {  // the histogram and the keys disagree: cannot happen
+      if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+      return;
+    }
+    __syncthreads();
+  } else {
+    // The bin from the histogram, narrowed while it holds more than kBulkCand
+    // keys by one pass over the keys per kBulkBits bits; then one pass marks
+    // the slots below it (LDS bitmap) and gathers its keys and slots.
+    const uint2 hv = reinterpret_cast<const uint2 *>(uh)[tid];
+    if (cut_bin<NT>(hv.x, hv.y, bs.x, a.block != 0, sc, &bp) != kCutFast) {  // cannot happen
+      if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+      return;
+    }
+    prefix = (uint64_t)bp.bin;
+    need = bp.need;
+    cnt = bp.cnt;
+    while (cnt > kBulkCand && pbits < 64) {
+      const int nb = min(kBulkBits, 64 - pbits), sh = 64 - pbits - nb;
+      for (int i = tid; i < kBulkBins; i += NT) h[i] = 0u;
+      __syncthreads();
+      for (int n0 = 0; n0 < L; n0 += KPT * NT) {
+        uint64_t kk[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) kk[j] = keys[min(n0 + j * NT + tid, L - 1)];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const bool in = n0 + j * NT + tid < L && kk[j] != ~0ull && (kk[j] >> (64 - pbits)) == prefix;
+          const int d = in ? (int)((kk[j] >> sh) & ((1ull << nb) - 1ull)) : kBulkBins;
+          const int d0 = __builtin_amdgcn_readfirstlane(d);
+          const uint64_t same = __ballot(d == d0);
+          if (d == d0) {
+            if (d0 < kBulkBins && lane == __builtin_ctzll(same)) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+          } else if (d < kBulkBins) {
+            atomicAdd(&h[d], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      pick_bin<NT>(h[2 * tid], h[2 * tid + 1], need, sc, &bp);
+      if (bp.bin < 0) {
+        if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
+        return;
+      }
+      prefix = (prefix << nb) | (uint64_t)bp.bin;
+      pbits += nb;
+      need = bp.need;
+      cnt = bp.cnt;
+      __syncthreads();  // every thread has read bp and h
+    }
+    const int tsh = 64 - pbits;
+    const bool all = need == cnt;
+    if (tid == 0) s_nc = 0;
     __syncthreads();
     for (int n0 = 0; n0 < L; n0 += KPT * NT) {
       uint64_t kk[KPT];
@@ -1786,63 +1995,31 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
       for (int j = 0; j < KPT; ++j) kk[j] = keys[min(n0 + j * NT + tid, L - 1)];
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const bool in = n0 + j * NT + tid < L && kk[j] != ~0ull && (kk[j] >> (64 - pbits)) == prefix;
-        const int d = in ? (int)((kk[j] >> sh) & ((1ull << nb) - 1ull)) : kBulkBins;
-        const int d0 = __builtin_amdgcn_readfirstlane(d);
-        const uint64_t same = __ballot(d == d0);
-        if (d == d0) {
-          if (d0 < kBulkBins && lane == __builtin_ctzll(same)) atomicAdd(&h[d0], (uint32_t)__popcll(same));
-        } else if (d < kBulkBins) {
-          atomicAdd(&h[d], 1u);
+        const int n = n0 + j * NT + tid;
+        const bool valid = n < L && kk[j] != ~0ull;
+        const uint64_t top = tsh >= 64 ? 0ull : (kk[j] >> tsh);
+        const bool ev = valid && (top < prefix || (all && top == prefix));
+        const bool c = valid && !all && top == prefix;
+        if (use_map) {
+          const uint64_t m = __ballot(ev);
+          if (lane == 0 && n0 + j * NT < L) eb[(n0 + j * NT) / 64 + wave] = m;
         }
+        const uint64_t mc = __ballot(c);  // one atomic per wave
+        int b0 = 0;
+        if (lane == 0 && mc) b0 = atomicAdd(&s_nc, __popcll(mc));
+        b0 = __shfl(b0, 0);
+        const int i = b0 + __popcll(mc & ((1ull << lane) - 1ull));
+        if (c && i < kBulkCand) ck[i] = kk[j], cs[i] = n;
       }
     }
     __syncthreads();
-    find_bin(h[2 * tid], h[2 * tid + 1], need);
-    if (s_bin < 0) {
+    if (!all && s_nc != cnt) {  // the histogram and the keys disagree: cannot happen
       if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
       return;
     }
-    prefix = (prefix << nb) | (uint64_t)s_bin;
-    pbits += nb;
-    need = s_need;
-    cnt = s_cnt;
   }
-  const int tsh = 64 - pbits;  // bits below the bin's
+  const int tsh = 64 - pbits;    // bits below the bin's
   const bool all = need == cnt;  // the whole bin goes
-  const bool use_map = L <= kBulkMapSlots;
-
-  // 2. Slots below the bin marked; the bin's keys gathered.
-  if (tid == 0) s_nc = 0;
-  __syncthreads();
-  for (int n0 = 0; n0 < L; n0 += KPT * NT) {
-    uint64_t kk[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) kk[j] = keys[min(n0 + j * NT + tid, L - 1)];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int n = n0 + j * NT + tid;
-      const bool valid = n < L && kk[j] != ~0ull;
-      const uint64_t top = tsh >= 64 ? 0ull : (kk[j] >> tsh);
-      const bool ev = valid && (top < prefix || (all && top == prefix));
-      const bool c = valid && !all && top == prefix;
-      if (use_map) {
-        const uint64_t m = __ballot(ev);
-        if (lane == 0 && n0 + j * NT < L) eb[(n0 + j * NT) / 64 + wave] = m;
-      }
-      const uint64_t mc = __ballot(c);  // one atomic per wave
-      int b0 = 0;
-      if (lane == 0 && mc) b0 = atomicAdd(&s_nc, __popcll(mc));
-      b0 = __shfl(b0, 0);
-      const int i = b0 + __popcll(mc & ((1ull << lane) - 1ull));
-      if (c && i < kBulkCand) ck[i] = kk[j], cs[i] = n;
-    }
-  }
-  __syncthreads();
-  if (!all && s_nc != cnt) {  // the histograms and the keys disagree: cannot happen
-    if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
-    return;
-  }
 
   // 3. The need-th smallest key of the bin: radix passes of 8 bits over the
   // gathered keys, below the bits the bin fixes.  T: the largest key that goes.
@@ -1913,7 +2090,10 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   }
   __syncthreads();  // the bitmap is complete
 
-  // 4. Holes and movers from the bitmap: each thread takes a run of words.
+  // 4. Holes and movers from the bitmap.  Each thread counts a run of words;
+  // the runs' prefix gives every word the list positions of its first hole and
+  // mover (ph, pm: LDS over ck, which is free now), and then each wave lists
+  // whole words, one slot per lane, so that a word's entries go out together.
   const int nw = (L + 63) / 64, wpt = (nw + NT - 1) / NT;
   const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
   auto below = [](int c) -> uint64_t { return c <= 0 ? 0ull : (c >= 64 ? ~0ull : ((1ull << c) - 1ull)); };
@@ -1930,13 +2110,51 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
     nh += __popcll(e & valid & low);
     nm += __popcll(~e & valid & ~low);
   }
-  int th, tm;
-  int ih = block_excl_scan<NT>(nh, sc, &th);
-  int im = block_excl_scan<NT>(nm, sc, &tm);
+  int th, tm, ih, im;
+  block_excl_scan2<NT>(nh, nm, sc, &ih, &im, &th, &tm);
+  int *ph = reinterpret_cast<int *>(ck), *pm = ph + NMW;
   for (int w = w0; w < w1; ++w) {
     const uint64_t e = eb[w], valid = below(L - 64 * w), low = below(newlen - 64 * w);
-    for (uint64_t x = e & valid & low; x; x &= x - 1ull) holes[ih++] = 64 * w + __builtin_ctzll(x);
-    for (uint64_t x = ~e & valid & ~low; x; x &= x - 1ull) movers[im++] = 64 * w + __builtin_ctzll(x);
+    ph[w] = ih;
+    pm[w] = im;
+    ih += __popcll(e & valid & low);
+    im += __popcll(~e & valid & ~low);
+  }
+  __syncthreads();
+  // Four words per wave at a time, their LDS reads issued together; the word
+  // index is the wave's, so the masks are scalar work.  A lane's rank among
+  // a word's listed slots is the count of listed bits below it (mbcnt).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto put = [&](uint64_t m, int first, int slot, int32_t *list) __attribute__((always_inline)) {
+    const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+    const uint32_t mine = (lane < 32 ? lo >> lane : hi >> (lane - 32)) & 1u;
+    if (mine) list[first + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = slot;
+  };
+  for (int wb = wv; wb < nw; wb += 4 * kNW2) {
+    uint64_t e[4];
+    int h0[4], m0[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int w = min(wb + q * kNW2, nw - 1);
+      e[q] = eb[w];
+      h0[q] = ph[w];
+      m0[q] = pm[w];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int w = wb + q * kNW2;
+      if (w >= nw) break;
+      const int slot = 64 * w + lane;
+      if (64 * w + 64 <= newlen) {  // every slot below the new length: holes only
+        put(e[q], h0[q], slot, holes);
+      } else if (64 * w >= newlen && 64 * w + 64 <= L) {  // every slot live, at or above it: movers only
+        put(~e[q], m0[q], slot, movers);
+      } else {
+        const uint64_t valid = below(L - 64 * w), low = below(newlen - 64 * w);
+        put(e[q] & valid & low, h0[q], slot, holes);
+        put(~e[q] & valid & ~low, m0[q], slot, movers);
+      }
+    }
   }
   if (tid == 0) {
     if (th != tm) {  // cannot happen for distinct positions; fail safe
@@ -2113,6 +2331,9 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
       hipLaunchKernelGGL(k_block_keys, dim3((unsigned)a.n_units, (unsigned)nib), dim3(kT2), 0, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    hipLaunchKernelGGL(k_bulk_mark, dim3((unsigned)a.n_units, (unsigned)((nib * kImpChunk + kMarkSlots - 1) / kMarkSlots)),
+                       dim3(kT2), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bulk_moves<D * EL>), moves_grid<D * EL>(a), dim3(256), 0, s, a);
@@ -2144,6 +2365,9 @@ static hipError_t step_go_s2(const StepArgs &a, hipStream_t s, hipEvent_t ev0, h
                      a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.bulk_split) {
+    hipLaunchKernelGGL(k_bulk_mark, dim3((unsigned)a.n_units, (unsigned)((nib * kImpChunk + kMarkSlots - 1) / kMarkSlots)),
+                       dim3(kT2), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bulk_moves<D * EL>), moves_grid<D * EL>(a), dim3(256), 0, s, a);
