@@ -298,12 +298,12 @@ def test_bulk_cut_threshold_bin_edge_cases(pattern, hint):
     """Bulk cuts at the edges of the key-histogram selection.  "equal": every
     K row of a unit is the same, so every token gets the same probability and
     (from zero) the same importance: the threshold's histogram bin holds every
-    candidate (11900 keys: more than the 8192 the selection gathers in LDS;
-    7400 in the second unit: gathered) and positions decide.  "two-level":
-    exactly the tokens to evict have a low importance, so the threshold's bin
-    is taken whole."""
+    candidate (11900 keys: more than the 4096 the selection gathers, so the
+    bin is narrowed by passes over the keys; 3400 in the second unit:
+    gathered whole) and positions decide.  "two-level": exactly the tokens to
+    evict have a low importance, so the threshold's bin is taken whole."""
     B, Hkv, G, D, cap, S, Wn, beta = 1, 2, 4, 128, 12100, 4, 64, 500
-    st = W.random_cache(61, B, G * Hkv, Hkv, D, W.BF16, cap, [[12000, 7500]])
+    st = W.random_cache(61, B, G * Hkv, Hkv, D, W.BF16, cap, [[12000, 3500]])
     newest = st["newest"]
     if pattern == "equal":
         st["k"][:] = st["k"][:, :, :1]
@@ -323,6 +323,20 @@ def test_bulk_cut_threshold_bin_edge_cases(pattern, hint):
     data = {k: v[None] for k, v in data.items()}
     run = GpuRun(st, G * Hkv, budget_all=beta, n_sink=S, n_recent=Wn, hint=hint)
     lockstep(run, data, 1, tag=f"bulk cut {pattern}")
+
+
+@PATHS
+def test_bulk_cut_beyond_the_select_bitmap(hint):
+    """A bulk cut of a unit longer than the select's LDS bitmap (2^18 slots):
+    the split cut finds the threshold by its own passes over the keys and
+    lists the moves from the keys; without the caller's lengths one block
+    takes the whole unit."""
+    B, Hkv, G, D, cap, S, Wn, beta = 1, 1, 2, 64, 270100, 4, 64, 3000
+    st = W.random_cache(64, B, G * Hkv, Hkv, D, W.BF16, cap, [[270000]])
+    data = W.random_step(65, B, G * Hkv, Hkv, D, W.BF16, st["newest"])
+    data = {k: v[None] for k, v in data.items()}
+    run = GpuRun(st, G * Hkv, budget_all=beta, n_sink=S, n_recent=Wn, hint=hint)
+    lockstep(run, data, 1, tag="bulk cut beyond the select bitmap")
 
 
 @PATHS
