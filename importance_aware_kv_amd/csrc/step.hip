@@ -828,11 +828,11 @@ __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
 constexpr int kT2 = 1024;            // threads of a second-launch workgroup
 constexpr int kNW2 = kT2 / kWave;    // its waves
 
-template <int G>
+template <int G, int NT>
 struct K2Lay {
   static constexpr int CHUNK = kImpChunk;    // tokens per importance block
-  static constexpr int NB = CHUNK / kT2;     // tokens per thread per batch
-  static_assert(NB * kT2 == CHUNK, "an importance block takes whole batches");
+  static constexpr int NB = CHUNK / NT;      // tokens per thread per batch
+  static_assert(NB * NT == CHUNK, "an importance block takes whole batches");
 };
 
 template <int EL, int D, int G>
@@ -840,20 +840,20 @@ __host__ __device__ constexpr int k2_noc() { return G * D / 64; }
 
 // Softmax statistics of a unit per head from its tiles' (max, sum) pairs:
 // M = max over tiles, L = sum over tiles of sum * 2^(max - M).  Pair i =
-// tile * G + g; thread t owns pairs t, t + kT2, ... (all of head t % G); v0 is
+// tile * G + g; thread t of NT owns pairs t, t + NT, ... (all of head t % G); v0 is
 // its first pair, already loaded.  Every wave finishes the reduction itself,
 // so lane l leaves with M and L of head l % G (no broadcast barrier).  When
 // sm_m is given, the maxima of head gm are also left there per tile.
-template <int G>
+template <int G, int NT = kT2>
 __device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 v0, float cs, float (*red)[G],
                                            float (*red2)[G], float &Mlane, float &Llane, float *sm_m, int gm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NV = kNW2 * G, KV = (NV + kWave - 1) / kWave;
+  constexpr int NV = NT / kWave * G, KV = (NV + kWave - 1) / kWave;
   float mx = tid < npair ? v0.x : -INFINITY;
-  for (int i = tid + kT2; i < npair; i += kT2) mx = fmaxf(mx, pml[i].x);
+  for (int i = tid + NT; i < npair; i += NT) mx = fmaxf(mx, pml[i].x);
   if (sm_m) {
     if (tid < npair && tid % G == gm) sm_m[tid / G] = v0.x;
-    for (int i = tid + kT2; i < npair; i += kT2)
+    for (int i = tid + NT; i < npair; i += NT)
       if (i % G == gm) sm_m[i / G] = pml[i].x;
   }
   mx = lanes_max<G>(mx);
@@ -868,7 +868,7 @@ __device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 
   M = lanes_max<G>(M);
   const float Ms = (M == -INFINITY) ? 0.f : M;
   float ls = tid < npair ? v0.y * fast_exp2((v0.x - Ms) * cs) : 0.f;
-  for (int i = tid + kT2; i < npair; i += kT2) {
+  for (int i = tid + NT; i < npair; i += NT) {
     const float2 v = pml[i];
     ls += v.y * fast_exp2((v.x - Ms) * cs);
   }
@@ -1237,39 +1237,43 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) int lds_int;
 typedef __attribute__((address_space(3))) RadixState lds_radix;
-template <int RB>
+template <int NT, int RB>
 __device__ __attribute__((noinline)) void bulk_cut_unit(const uint64_t *keys, int L, int beta, char *kw, char *vw,
                                                         int32_t *posw, float *impw, int32_t *holes, int32_t *movers,
                                                         int32_t *len_u, int32_t *status, lds_u32 *hist,
                                                         lds_u32 *whist, lds_int *sc, lds_radix *rs) {
-  bulk_compact<kT2, RB>(keys, L, beta, L - beta, kw, vw, posw, impw, holes, movers, len_u, status,
-                        (uint32_t *)hist, (uint32_t *)whist, (int *)sc, (RadixState *)rs, nullptr);
+  bulk_compact<NT, RB>(keys, L, beta, L - beta, kw, vw, posw, impw, holes, movers, len_u, status,
+                       (uint32_t *)hist, (uint32_t *)whist, (int *)sc, (RadixState *)rs, nullptr);
 }
 
 // IB: the in-block bulk cut inlined (when the host cannot foresee bulk cuts,
 // any unit may be cut in bulk in this block), or called out of line.
 template <int EL, int D, int G, bool S2 = false, bool IB = false>
-__global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k_finalize(StepArgs a) {
+__global__ __launch_bounds__(S2 ? kT2 : kT2 / 2) __attribute__((amdgpu_waves_per_eu(S2 ? 8 : 6))) void k_finalize(StepArgs a) {
+  // Workgroup size: Stage II's output blocks select among up to 2 kT2 keys
+  // held two per thread; Stage I's blocks take half as many threads (two
+  // workgroups' waves per launch round fit where one did).
+  constexpr int NTF = S2 ? kT2 : kT2 / 2, NWF = NTF / kWave;
   constexpr int RB = D * EL, NR = RB / 16, GD = G * D;
-  constexpr int NB = K2Lay<G>::NB, CHUNK = K2Lay<G>::CHUNK;
+  constexpr int NB = K2Lay<G, NTF>::NB, CHUNK = K2Lay<G, NTF>::CHUNK;
   // output blocks per unit: Stage I one per 64 outputs, Stage II one per head
   constexpr int NOC = S2 ? G : k2_noc<EL, D, G>();
-  constexpr int NTW = 8;  // tiles per wave loaded in one batch by an output block
-  __shared__ float red[kNW2][G], red2[kNW2][G];
+  constexpr int NTW = 8 * kNW2 / NWF;  // tiles per wave loaded in one batch by an output block
+  __shared__ float red[NWF][G], red2[NWF][G];
   __shared__ float sm_m[kMaxGrid];           // output blocks: tile maxima of their head
-  __shared__ float red_o[kNW2][kWave];       // output blocks: per-wave partial sums
-  __shared__ uint64_t sk[kNW2];
-  __shared__ int ss[kNW2];
+  __shared__ float red_o[NWF][kWave];       // output blocks: per-wave partial sums
+  __shared__ uint64_t sk[NWF];
+  __shared__ int ss[NWF];
   __shared__ float s_newimp;
   __shared__ int s_last;
   __shared__ __attribute__((aligned(16))) uint4 s_nrow[kWave];  // the new token's K and V rows
   // bulk cut: radix-select scratch (one block per unit), or the block's key
   // histogram (kBulkBins words of whist) when the cut is spread over blocks
   __shared__ uint32_t hist[256];
-  __shared__ __attribute__((aligned(16))) uint32_t whist[kNW2 * 256];
-  __shared__ int sc[kT2];
+  __shared__ __attribute__((aligned(16))) uint32_t whist[NWF * 256];
+  __shared__ int sc[NTF];
   __shared__ RadixState rs;
-  static_assert(kBulkBins <= kNW2 * 256, "the key histogram fits the radix scratch");
+  static_assert(kBulkBins <= NWF * 256, "the key histogram fits the radix scratch");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
@@ -1348,7 +1352,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       auto load_batch = [&](int base) {
     #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int n = min(base + tid + i * kT2, Lold);
+          const int n = min(base + tid + i * NTF, Lold);
           if constexpr (G % 4 == 0) {
     #pragma unroll
             for (int g = 0; g < G; g += 4) {
@@ -1368,7 +1372,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       load_batch(nb0);
       const int beta = a.budget ? beta_ld : a.budget_all;
       float Mlane, Llane;
-      unit_stats<G>(pml, npair, v0, a.scale_log2, red, red2, Mlane, Llane, nullptr, 0);
+      unit_stats<G, NTF>(pml, npair, v0, a.scale_log2, red, red2, Mlane, Llane, nullptr, 0);
       if (a.hp.n) {  // a host plan covers every unit: check it against the device
         const int err = (L > a.cap) ? HIKV_ECAPACITY : ((beta < S || beta > a.cap) ? HIKV_EBUDGET : 0);
         if (r == 0 && tid == 0) {
@@ -1418,7 +1422,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
       uint64_t best = ~0ull;
       int best_slot = -1;
       if (thist) {
-        for (int i = tid; i < kBulkBins; i += kT2) whist[i] = 0u;
+        for (int i = tid; i < kBulkBins; i += NTF) whist[i] = 0u;
         __syncthreads();
       }
       // One batch of the block's tokens: probabilities, importance, the
@@ -1431,7 +1435,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         int pns[NB];
     #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int n = base + tid + i * kT2;
+          const int n = base + tid + i * NTF;
           float p = 0.f;
     #pragma unroll
           for (int g = 0; g < G; ++g)
@@ -1449,7 +1453,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int n = base + tid + i * kT2;
+          const int n = base + tid + i * NTF;
           int hbin = kBulkBins;  // the key's histogram bin (a spread bulk cut), or none
           if (n < nb1 && n != dead) {
             const bool is_new = n == Lold;
@@ -1511,11 +1515,11 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         }
         __syncthreads();  // every key is stored
         if constexpr (IB)
-          bulk_compact<kT2, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
+          bulk_compact<NTF, RB>(bkeys, L, beta, L - beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
                                 a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, hist, whist, sc, &rs,
                                 nullptr);
         else
-          bulk_cut_unit<RB>(bkeys, L, beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
+          bulk_cut_unit<NTF, RB>(bkeys, L, beta, kw, vw, posw, impw, a.ws.holes + (size_t)u * a.cap,
                             a.ws.movers + (size_t)u * a.cap, a.len + u, a.ws.status, (lds_u32 *)hist,
                             (lds_u32 *)whist, (lds_int *)sc, (lds_radix *)&rs);
         return;
@@ -1525,7 +1529,7 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         __syncthreads();  // the histogram, s_newimp
         if (thist) {  // the block's counts join the unit's histogram
           uint32_t *dst = a.ws.uhist + (size_t)u * kBulkHistWords;
-          for (int i = tid; i < kBulkBins; i += kT2) {
+          for (int i = tid; i < kBulkBins; i += NTF) {
             const uint32_t c = whist[i];
             if (c) atomicAdd(&dst[i], c);
           }
@@ -1567,8 +1571,8 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
         if (n_evict == 1) {
           // The eviction stays pending: each block leaves its lowest key.
           if (wave == 0) {
-            uint64_t kk = lane < kNW2 ? sk[lane] : ~0ull;
-            int vs = lane < kNW2 ? ss[lane] : -1;
+            uint64_t kk = lane < NWF ? sk[lane] : ~0ull;
+            int vs = lane < NWF ? ss[lane] : -1;
             wave_min_key(kk, vs);
             if (lane == 0) {
               cand[4 * r] = (int32_t)(uint32_t)kk;
@@ -1599,10 +1603,10 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   const float *pacc = a.ws.part_acc + (size_t)tb * GD + o;
   float pa[NTW];
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) pa[i] = pacc[(size_t)min(wave + kNW2 * i, nt - 1) * GD];
+  for (int i = 0; i < NTW; ++i) pa[i] = pacc[(size_t)min(wave + NWF * i, nt - 1) * GD];
   const int beta = a.budget ? beta_ld : a.budget_all;
   float Mlane, Llane;
-  unit_stats<G>(pml, npair, v0, a.scale_log2, red, red2, Mlane, Llane, sm_m, g);
+  unit_stats<G, NTF>(pml, npair, v0, a.scale_log2, red, red2, Mlane, Llane, sm_m, g);
   const float Mo = lane_value(Mlane, g), Lo = lane_value(Llane, g);
   float *outu = a.out + (size_t)(b * a.Hq + j * G) * D;
   if (a.hp.n && (L > a.cap || beta < S || beta > a.cap)) {  // unit left alone
@@ -1613,16 +1617,16 @@ __global__ __launch_bounds__(kT2) __attribute__((amdgpu_waves_per_eu(8))) void k
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
-    const int t = wave + kNW2 * i;
+    const int t = wave + NWF * i;
     if (t < nt) acc += pa[i] * fast_exp2((sm_m[t] - Ms) * a.scale_log2);
   }
-  for (int t = wave + kNW2 * NTW; t < nt; t += kNW2)
+  for (int t = wave + NWF * NTW; t < nt; t += NWF)
     acc += pacc[(size_t)t * GD] * fast_exp2((sm_m[t] - Ms) * a.scale_log2);
   red_o[wave][lane] = acc;
   lds_barrier();
   if (wave == 0) {
     float sum = 0.f;
-    for (int w = 0; w < kNW2; ++w) sum += red_o[w][lane];
+    for (int w = 0; w < NWF; ++w) sum += red_o[w][lane];
     outu[o] = sum / Lo;
   }
   }
@@ -2322,8 +2326,8 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
     nib = min(nib, (mx + kImpChunk - 1) / kImpChunk);
   }
   const dim3 g2((unsigned)a.n_units, (unsigned)(nib + k2_noc<EL, D, G>()));
-  if (a.bulk_known) hipLaunchKernelGGL((k_finalize<EL, D, G>), g2, dim3(kT2), 0, s, a);
-  else hipLaunchKernelGGL((k_finalize<EL, D, G, false, true>), g2, dim3(kT2), 0, s, a);
+  if (a.bulk_known) hipLaunchKernelGGL((k_finalize<EL, D, G>), g2, dim3(kT2 / 2), 0, s, a);
+  else hipLaunchKernelGGL((k_finalize<EL, D, G, false, true>), g2, dim3(kT2 / 2), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.bulk_split) {
     if (a.block) {  // whole blocks: the position order, then the blocks' keys
