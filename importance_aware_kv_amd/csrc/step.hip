@@ -54,7 +54,6 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   constexpr int RB = LY::RB;
   constexpr int QB = G * D * EL;  // the group's queries, bytes
   static_assert(QB <= 4 * 1024, "one q DMA instruction per wave");
-  if (a.bulk_split) bulk_hist_clear(a);
   // LDS: NSUB sub-chunks, each K then V; the group's queries.
   __shared__ __attribute__((aligned(16))) char smem[NSUB * 2 * SUBB];
   __shared__ __attribute__((aligned(16))) char qs[QB];
@@ -80,6 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   }
 
   if (!pl.valid) {
+    if (a.bulk_split) bulk_hist_clear(a);  // (on every way out: the grid covers it)
     if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
     return;
   }
@@ -316,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
       store_agent_f(a.ws.part_ml + ((size_t)tile * G + g) * 2 + 1, lv);
     }
   }
+  if (a.bulk_split) bulk_hist_clear(a);  // (on every way out: the grid covers it)
   if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
 
@@ -330,7 +331,6 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   __shared__ float sm_ml[4][G][2];
   __shared__ __attribute__((aligned(16))) PendLds pd;
   float(*sm_acc)[G][64] = reinterpret_cast<float(*)[G][64]>(smem);  // reused after the loop
-  if (a.bulk_split) bulk_hist_clear(a);
   static_assert(4 * G * 64 * 4 <= NSUB * 2 * SUBB, "merge scratch must fit in the stage");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -347,6 +347,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
     asm volatile("" ::"v"(hp_bend), "v"(hp_len));
   }
   if (!pl.valid) {
+    if (a.bulk_split) bulk_hist_clear(a);  // (on every way out: the grid covers it)
     if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
     return;
   }
@@ -575,6 +576,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
       store_agent_f(a.ws.part_ml + ((size_t)tile * G + h) * 2 + 1, sm_ml[w0][h][1] * e0 + sm_ml[w1][h][1] * e1);
     }
   }
+  if (a.bulk_split) bulk_hist_clear(a);  // (on every way out: the grid covers it)
   if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
 
@@ -602,7 +604,6 @@ template <int G, int NSUB>
 __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
   constexpr int EL = 2, D = 128, RB = D * EL, TS = 64, SUBB = TS * RB, QB = G * D * EL, NC = 2 * G;
   static_assert(NC <= 16 && NSUB <= 3, "exact and reduced columns fit one 16-column tile; ring offsets fit");
-  if (a.bulk_split) bulk_hist_clear(a);
   __shared__ __attribute__((aligned(16))) char smem[NSUB * SUBB];
   __shared__ __attribute__((aligned(16))) char qs[QB];
   __shared__ __attribute__((aligned(16))) float lgs[2][TS][NC];  // a sub-chunk's scores, two buffers
@@ -621,6 +622,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
     asm volatile("" ::"v"(hp_bend), "v"(hp_len));
   }
   if (!pl.valid) {
+    if (a.bulk_split) bulk_hist_clear(a);  // (on every way out: the grid covers it)
     if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
     return;
   }
@@ -818,6 +820,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
     store_agent_f(a.ws.part_ml + ((size_t)tile * G + tid) * 2, M);
     store_agent_f(a.ws.part_ml + ((size_t)tile * G + tid) * 2 + 1, Ls);
   }
+  if (a.bulk_split) bulk_hist_clear(a);  // (on every way out: the grid covers it)
   if (blockIdx.x == 0 && !a.hp.n) error_sweep<G, D>(a);
 }
 
