@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "hikv.h"
@@ -220,6 +221,38 @@ struct StepArgs {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void set_status(int32_t *status, int32_t code) {
   atomicCAS(status, 0, code);
+}
+
+// The kernel-argument lines a launch's prologue reads, pulled into the scalar
+// cache together.  Left to the code, each scalar load is issued where its
+// value is first needed, and the prologue waits for one cache miss after
+// another (the plan's words, then the flags, then the pointers); touched
+// together they cost one round trip.  Lines: the first 512 bytes of StepArgs
+// (every field before the host plan), the hidden arguments after it, and the
+// host-plan words of unit uh.  Loads and their wait are in one asm block; the
+// registers they fill are scratch, declared clobbered.
+static_assert(offsetof(StepArgs, hp) <= 512, "the fields before the host plan span eight 64-byte lines");
+__device__ __forceinline__ void kernarg_warm(int uh) {
+  const uint64_t kp = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint64_t pa = kp + offsetof(StepArgs, hp) + offsetof(HostPlan, base) + 4 * (uint64_t)uh;
+  const uint64_t pb = kp + offsetof(StepArgs, hp) + offsetof(HostPlan, L) + 4 * (uint64_t)uh;
+  asm volatile(
+      "s_load_dword s40, %0, 0x0\n\t"
+      "s_load_dword s41, %0, 0x40\n\t"
+      "s_load_dword s42, %0, 0x80\n\t"
+      "s_load_dword s43, %0, 0xc0\n\t"
+      "s_load_dword s44, %0, 0x100\n\t"
+      "s_load_dword s45, %0, 0x140\n\t"
+      "s_load_dword s46, %0, 0x180\n\t"
+      "s_load_dword s47, %0, 0x1c0\n\t"
+      "s_load_dword s48, %0, %3\n\t"
+      "s_load_dword s49, %0, %4\n\t"
+      "s_load_dword s50, %1, 0x0\n\t"
+      "s_load_dword s51, %2, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "s"(kp), "s"(pa), "s"(pb), "i"(sizeof(StepArgs)), "i"(sizeof(StepArgs) + 64)
+      : "s40", "s41", "s42", "s43", "s44", "s45", "s46", "s47", "s48", "s49", "s50", "s51", "memory");
 }
 
 // A bulk cut's per-unit histograms and records start at zero: the attention

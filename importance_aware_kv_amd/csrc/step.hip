@@ -70,6 +70,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(StepArgs a) {
   // arguments are always readable); the device plan's path uses them too, after
   // its own loads, so that the compiler issues them ahead of the branch.
   const int hp_bend = a.hp.base[lane + 1], hp_len = a.hp.L[lane];
+  kernarg_warm(0);  // (after the plan's vector loads are issued)
   Plan pl;
   if (a.hp.n) {
     pl = host_plan(a, blockIdx.x, hp_bend, hp_len);
@@ -339,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(StepArgs a) {
   // arguments are always readable); the device plan's path uses them too, after
   // its own loads, so that the compiler issues them ahead of the branch.
   const int hp_bend = a.hp.base[lane + 1], hp_len = a.hp.L[lane];
+  kernarg_warm(0);  // (after the plan's vector loads are issued)
   Plan pl;
   if (a.hp.n) {
     pl = host_plan(a, blockIdx.x, hp_bend, hp_len);
@@ -614,6 +616,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_s2(StepArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = a.n_units;
   const int hp_bend = a.hp.base[lane + 1], hp_len = a.hp.L[lane];
+  kernarg_warm(0);  // (after the plan's vector loads are issued)
   Plan pl;
   if (a.hp.n) {
     pl = host_plan(a, blockIdx.x, hp_bend, hp_len);
@@ -1286,25 +1289,28 @@ __global__ __launch_bounds__(S2 ? kT2 : kT2 / 2) __attribute__((amdgpu_waves_per
   // output block.
   const int nib = (int)gridDim.y - NOC;  // importance blocks per unit
   const int u = blockIdx.x, r = blockIdx.y;
-  // The move launch that may follow reads every unit's count: none unless a
-  // bulk cut below says otherwise (the same thread writes both).
-  if (a.bulk_split && r == 0 && tid == 0) {
-    a.ws.nmoves[u] = 0;
-    a.ws.bsel[4 * u + 3] = 0;
-  }
   // The host plan's words (kernel arguments, clamped to its table) are loaded
   // with the flag that says whether there is one, so that the host plan costs
   // one round trip; the device plan's path uses them too, after its own load,
   // so that the compiler issues them ahead of the branch.
   const int uh = min(u, kHostPlanUnits - 1);
+  kernarg_warm(uh);
   const int hb0 = a.hp.base[uh], hb1 = a.hp.base[uh + 1], hlen = a.hp.L[uh];
+  const int bsplit = a.bulk_split;
+  asm volatile("" ::"s"(hb0), "s"(hb1), "s"(hlen), "s"(bsplit));  // one wait for all four
   int tb, nt, L;
   if (a.hp.n) {
     tb = hb0, nt = hb1 - hb0, L = hlen;
   } else {
     const int4 rec = reinterpret_cast<const int4 *>(a.ws.urec)[u];
     tb = rec.x, nt = rec.y, L = rec.z;
-    asm volatile("" ::"s"(hb0), "s"(hb1), "s"(hlen));
+  }
+  // The move launch that may follow reads every unit's count: none unless a
+  // bulk cut below says otherwise (the same thread writes both).  (After the
+  // plan's loads, so that its flag is loaded with them.)
+  if (bsplit && r == 0 && tid == 0) {
+    a.ws.nmoves[u] = 0;
+    a.ws.bsel[4 * u + 3] = 0;
   }
   if (nt <= 0) return;  // a unit the first launch excluded
   const bool imp_blk = r < nib;
