@@ -1800,6 +1800,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_mark(StepArgs a) {
   uint64_t kk[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) kk[j] = keys[min(i0 + j * kT2 + tid, a.cap - 1)];
+  kernarg_warm(0);
   if (bs.w != 1) return;  // not cut in bulk
   const int k = bs.x, L = bs.z;
   if (i0 >= L) return;
@@ -1915,6 +1916,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
       sv[q] = cslot[i];
     }
   }
+  kernarg_warm(0);
   if (bs.w != 1) return;  // not cut in bulk
   const int beta = bs.y, L = bs.z;
   const uint64_t *keys = a.ws.bkeys + (size_t)u * a.cap;
@@ -2192,15 +2194,18 @@ template <int RB>
 __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
   constexpr int CPR = RB / 16, RPP = 256 / CPR;  // threads per row, rows per pass (4 passes)
   static_assert(RPP * 4 == bulk_moves_per_wg(RB), "moves per workgroup");
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   int u = blockIdx.x, y0 = blockIdx.y;
+  // The chunk table's words (kernel arguments, always readable) are loaded
+  // before the flag that says whether there is one is known.
+  const int mvend = a.hp.mvb[min(lane, kHostPlanUnits - 1) + 1];
+  kernarg_warm(0);
   if (a.moves_flat) {
     // One chunk of one unit's moves: the unit is the number of units whose
     // chunks end at or before this workgroup's.
-    const int lane = tid & 63;
-    const int end = lane < a.n_units ? a.hp.mvb[lane + 1] : 0x7fffffff;
+    const int end = lane < a.n_units ? mvend : 0x7fffffff;
     u = (int)__builtin_amdgcn_readfirstlane(__popcll(__ballot(end <= (int)blockIdx.x)));
-    y0 = (int)blockIdx.x - a.hp.mvb[u];
+    y0 = (int)blockIdx.x - (u > 0 ? __builtin_amdgcn_readlane(end, u - 1) : 0);
   }
   const int ci = tid % CPR, rr = tid / CPR;
   const int32_t *holes = a.ws.holes + (size_t)u * a.cap, *movers = a.ws.movers + (size_t)u * a.cap;
