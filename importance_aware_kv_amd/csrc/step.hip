@@ -964,8 +964,8 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
     // Keys in registers cover the unit (L <= kS2Kr * kT2).  A histogram of
     // their top 11 bits (padded: bin b at word b + b / 32, so that a lane's
     // 32 consecutive bins sit in distinct banks), the bin holding the kT-th
-    // largest (wave 0), that bin's keys gathered (128 at most), and a bitwise
-    // search over their low 53 bits in registers, counted by ballots (wave 0).
+    // largest (wave 0), that bin's keys gathered (128 at most) and ranked
+    // (each counts the larger ones).
     static_assert(kS2Wave <= kS2Kr * kT2, "the keys of a unit fit the registers");
     uint32_t *h2 = reinterpret_cast<uint32_t *>(&s2red[0][0]);          // 2112 words
     uint64_t *cand = reinterpret_cast<uint64_t *>(s_buf);                 // 128 keys
@@ -1027,12 +1027,27 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
       __syncthreads();
       const int nc = s_cnt;
       // the needb-th largest of the bin's keys: the one with needb - 1 larger
-      // (keys are distinct)
-      if (needb < nc && tid < nc) {
-        const uint64_t c = cand[tid];
-        int rank = 0;
-        for (int i = 0; i < nc; ++i) rank += cand[i] > c;
-        if (rank == needb - 1) s_T = c;
+      // (keys are distinct).  Thread t counts, for key t % 128, the larger
+      // ones among keys 16 (t / 128) .. 16 (t / 128) + 15; the eight counts
+      // of each key are then summed (sixteen compares per thread, not 128).
+      static_assert(kT2 == 8 * 128, "eight slices of the 128 gathered keys");
+      if (needb < nc) {
+        int *pr = reinterpret_cast<int *>(&s2red[0][0]);  // [8][128] (the histogram is done with)
+        const int c = tid & 127, sl = tid >> 7;
+        int part = 0;
+        if (c < nc) {
+          const uint64_t kc = cand[c];
+          const int i1 = min(nc, 16 * sl + 16);
+          for (int i = 16 * sl; i < i1; ++i) part += cand[i] > kc;
+        }
+        pr[128 * sl + c] = part;
+        __syncthreads();
+        if (tid < nc) {
+          int rank = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) rank += pr[128 * q + tid];
+          if (rank == needb - 1) s_T = cand[tid];
+        }
       }
       __syncthreads();
       T = s_T;
