@@ -964,19 +964,43 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
     // Keys in registers cover the unit (L <= kS2Kr * kT2).  A histogram of
     // their top 11 bits (padded: bin b at word b + b / 32, so that a lane's
     // 32 consecutive bins sit in distinct banks), the bin holding the kT-th
-    // largest (wave 0), that bin's keys gathered (128 at most) and ranked
-    // (each counts the larger ones).
+    // largest (wave 0), that bin's keys gathered -- narrowed by a second
+    // histogram of the next 11 bits when over 128 -- and ranked (each counts
+    // the larger ones).
     static_assert(kS2Wave <= kS2Kr * kT2, "the keys of a unit fit the registers");
+    static_assert(kS2Wave * 8 <= (int)sizeof(s_buf), "a bin's keys fit the gather buffer");
     uint32_t *h2 = reinterpret_cast<uint32_t *>(&s2red[0][0]);          // 2112 words
-    uint64_t *cand = reinterpret_cast<uint64_t *>(s_buf);                 // 128 keys
+    uint64_t *cand = reinterpret_cast<uint64_t *>(s_buf);                 // a bin's keys
     auto pidx = [](int bin) { return bin + (bin >> 5); };
-    for (int i = tid; i < 2112; i += kT2) h2[i] = 0u;
-    if (tid == 0) s_fall = 0, s_cnt = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kS2Kr; ++i) {
-      const uint64_t key = kr[i];
-      const int d = key ? (int)(key >> 53) : 2048;
+    // The bin of the 2048-bin histogram in h2 holding the need-th largest
+    // counted key (wave 0; lane l takes bins 2047 - 32 l down to 2016 - 32 l,
+    // then the lane whose range holds it takes that range one bin per lane):
+    // s_d (-1: none), the need within it, its count.
+    auto pick = [&](int need) {
+      if (wave == 0) {
+        uint32_t c = 0;
+#pragma unroll 8
+        for (int q = 0; q < 32; ++q) c += h2[pidx(2047 - 32 * lane - q)];
+        const uint32_t incl = wave_incl_scan_dpp(c), excl = incl - c;
+        const uint64_t lm = __ballot(excl < (uint32_t)need && incl >= (uint32_t)need);
+        const int lt = lm ? __builtin_ctzll(lm) : 0;
+        const uint32_t ex_t = __shfl(excl, lt);
+        const uint32_t hb = lane < 32 ? h2[pidx(2047 - 32 * lt - lane)] : 0u;
+        const uint32_t in2 = wave_incl_scan_dpp(hb) + ex_t, ex2 = in2 - hb;
+        const uint64_t qm = __ballot(lane < 32 && ex2 < (uint32_t)need && in2 >= (uint32_t)need);
+        const int qq = qm ? __builtin_ctzll(qm) : 0;
+        const int cntb = (int)__shfl(hb, qq), exq = (int)__shfl(ex2, qq);  // (every lane of the wave)
+        if (lane == 0) {
+          const bool ok = lm && qm;
+          s_d = ok ? 2047 - 32 * lt - qq : -1;
+          s_need = need - exq;
+          s_fall = cntb;
+        }
+      }
+      __syncthreads();
+    };
+    // Wave-aggregated count of digit d (2048: none) into h2.
+    auto count_digit = [&](int d) {
       const int d0 = __builtin_amdgcn_readfirstlane(d);
       const uint64_t same = __ballot(d == d0);
       if (d == d0) {
@@ -984,36 +1008,19 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
       } else if (d < 2048) {
         atomicAdd(&h2[pidx(d)], 1u);
       }
-    }
+    };
+    for (int i = tid; i < 2112; i += kT2) h2[i] = 0u;
+    if (tid == 0) s_cnt = 0;
     __syncthreads();
-    if (wave == 0) {
-      // lane l: bins 2047 - 32 l down to 2016 - 32 l; the lane whose range
-      // holds the kT-th largest, then that range's bins one per lane
-      uint32_t c = 0;
-#pragma unroll 8
-      for (int q = 0; q < 32; ++q) c += h2[pidx(2047 - 32 * lane - q)];
-      const uint32_t incl = wave_incl_scan_dpp(c), excl = incl - c;
-      const uint64_t lm = __ballot(excl < (uint32_t)kT && incl >= (uint32_t)kT);
-      const int lt = lm ? __builtin_ctzll(lm) : 0;
-      const uint32_t ex_t = __shfl(excl, lt);
-      const uint32_t hb = lane < 32 ? h2[pidx(2047 - 32 * lt - lane)] : 0u;
-      const uint32_t in2 = wave_incl_scan_dpp(hb) + ex_t, ex2 = in2 - hb;
-      const uint64_t qm = __ballot(lane < 32 && ex2 < (uint32_t)kT && in2 >= (uint32_t)kT);
-      const int qq = qm ? __builtin_ctzll(qm) : 0;
-      const int cntb = (int)__shfl(hb, qq), exq = (int)__shfl(ex2, qq);  // (every lane of the wave)
-      if (lane == 0) {
-        const bool ok = lm && qm;
-        s_d = ok ? 2047 - 32 * lt - qq : -1;
-        s_need = kT - exq;
-        s_fall = !ok || cntb > 128;
-        s_T = (uint64_t)(ok ? 2047 - 32 * lt - qq : 0) << 53;  // the whole bin, unless refined below
-      }
-    }
+#pragma unroll
+    for (int i = 0; i < kS2Kr; ++i) count_digit(kr[i] ? (int)(kr[i] >> 53) : 2048);
     __syncthreads();
-    const int bin = s_d, needb = s_need;
-    radix = s_fall != 0;
+    pick(kT);
+    const int bin = s_d;
+    int needb = s_need;
+    radix = bin < 0;
     if (!radix) {
-      // the bin's keys, gathered (one atomic per wave)
+      // The bin's keys, gathered (one atomic per wave; at most kS2Wave).
 #pragma unroll
       for (int i = 0; i < kS2Kr; ++i) {
         const uint64_t key = kr[i];
@@ -1025,32 +1032,77 @@ __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, in
         if (in) cand[base + __popcll(mk & ((1ull << lane) - 1ull))] = key;
       }
       __syncthreads();
-      const int nc = s_cnt;
-      // the needb-th largest of the bin's keys: the one with needb - 1 larger
-      // (keys are distinct).  Thread t counts, for key t % 128, the larger
-      // ones among keys 16 (t / 128) .. 16 (t / 128) + 15; the eight counts
-      // of each key are then summed (sixteen compares per thread, not 128).
-      static_assert(kT2 == 8 * 128, "eight slices of the 128 gathered keys");
-      if (needb < nc) {
-        int *pr = reinterpret_cast<int *>(&s2red[0][0]);  // [8][128] (the histogram is done with)
-        const int c = tid & 127, sl = tid >> 7;
-        int part = 0;
-        if (c < nc) {
-          const uint64_t kc = cand[c];
-          const int i1 = min(nc, 16 * sl + 16);
-          for (int i = 16 * sl; i < i1; ++i) part += cand[i] > kc;
-        }
-        pr[128 * sl + c] = part;
+      int nc = s_cnt;
+      uint64_t floor_key = (uint64_t)bin << 53;  // the lowest key of the bin
+      const uint64_t *kc = cand;
+      uint64_t *cand2 = reinterpret_cast<uint64_t *>(&s2red[0][0]) + 512;  // past the rank counts
+      if (needb < nc && nc > 128) {
+        // More than 128: the next 11 bits (52 .. 42) of the bin's keys,
+        // histogrammed, narrow it to a sub-bin, whose keys are gathered.
+        for (int i = tid; i < 2112; i += kT2) h2[i] = 0u;
         __syncthreads();
-        if (tid < nc) {
-          int rank = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) rank += pr[128 * q + tid];
-          if (rank == needb - 1) s_T = cand[tid];
+        for (int i0 = 0; i0 < nc; i0 += kT2) {
+          const int i = i0 + tid;
+          count_digit(i < nc ? (int)((cand[i] >> 42) & 2047ull) : 2048);
+        }
+        __syncthreads();
+        pick(needb);
+        const int sub = s_d;
+        if (sub < 0 || s_fall > 128) {
+          radix = true;  // a sub-bin still over 128 keys: radix passes over the unit
+        } else {
+          needb = s_need;
+          floor_key |= (uint64_t)sub << 42;
+          if (tid == 0) s_cnt = 0;
+          __syncthreads();  // (h2 is done with: cand2 and the rank counts reuse s2red)
+          for (int i0 = 0; i0 < nc; i0 += kT2) {
+            const int i = i0 + tid;
+            const uint64_t key = i < nc ? cand[i] : 0ull;
+            const bool in = i < nc && (int)((key >> 42) & 2047ull) == sub;
+            const uint64_t mk = __ballot(in);
+            int base = 0;
+            if (lane == 0 && mk) base = atomicAdd(&s_cnt, __popcll(mk));
+            base = __builtin_amdgcn_readfirstlane(base);
+            if (in) cand2[base + __popcll(mk & ((1ull << lane) - 1ull))] = key;
+          }
+          __syncthreads();
+          nc = s_cnt;
+          kc = cand2;
         }
       }
-      __syncthreads();
-      T = s_T;
+      if (!radix) {
+        // the needb-th largest of the gathered keys: the one with needb - 1
+        // larger (keys are distinct).  Thread t counts, for key t % 128, the
+        // larger ones among keys 16 (t / 128) .. 16 (t / 128) + 15; the eight
+        // counts of each key are then summed.  needb = nc: the whole (sub)bin.
+        static_assert(kT2 == 8 * 128, "eight slices of at most 128 gathered keys");
+        if (tid == 0) s_T = floor_key;
+        if (needb < nc) {
+          int *pr = reinterpret_cast<int *>(&s2red[0][0]);  // [8][128] (the histogram is done with)
+          const int c = tid & 127, sl = tid >> 7;
+          // (the slice's sixteen keys read together: a loop of dependent LDS
+          // reads took most of a microsecond; reads past nc stay inside the
+          // gather buffer and are not counted)
+          const uint64_t key = kc[c];
+          uint64_t kv[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) kv[q] = kc[16 * sl + q];
+          int part = 0;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) part += (16 * sl + q < nc && kv[q] > key) ? 1 : 0;
+          if (c >= nc) part = 0;
+          pr[128 * sl + c] = part;
+          __syncthreads();
+          if (tid < nc) {
+            int rank = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) rank += pr[128 * q + tid];
+            if (rank == needb - 1) s_T = kc[tid];
+          }
+        }
+        __syncthreads();
+        T = s_T;
+      }
     }
   }
   if (radix) {
