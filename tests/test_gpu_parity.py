@@ -350,6 +350,26 @@ def test_longctx_g8_lockstep_and_full_attention(hint):
     lockstep(_run(wf, df, hint=hint), df, wf.steps, tag="longctx-small-full")
 
 
+@pytest.mark.parametrize("pattern", ["crowded", "equal"])
+def test_stage2_selection_crowded_bins(pattern):
+    """Stage II's top-k_T selection when the reduced logits crowd one bin of
+    its first histogram.  "crowded": K rows within 2 % of one row, so every
+    key shares its top 11 bits and the second histogram (the next 11 bits)
+    narrows the bin.  "equal": identical K rows, so only positions tell the
+    keys apart and the radix passes over the unit decide."""
+    B, Hkv, G, D, cap = 1, 2, 4, 128, 1100
+    st = W.random_cache(66, B, G * Hkv, Hkv, D, W.BF16, cap, [[1000, 700]])
+    rng = np.random.Generator(np.random.PCG64(67))
+    base = rng.standard_normal(D).astype(np.float32)
+    spread = 0.02 if pattern == "crowded" else 0.0
+    kf = base + spread * rng.standard_normal((B, Hkv, cap, D)).astype(np.float32)
+    st["k"] = W._pack(kf, W.BF16)
+    data = W.random_step(68, B, G * Hkv, Hkv, D, W.BF16, st["newest"])
+    data = {k: v[None] for k, v in data.items()}
+    run = GpuRun(st, G * Hkv, budget_all=900, n_sink=4, n_recent=32, r=32, kT=256)
+    lockstep(run, data, 1, tag=f"stage2 selection {pattern}")
+
+
 def test_twostage_lockstep():
     w = W.workload("twostage", ctx=900, steps=3, batch=2)
     w.budget_all, w.n_recent, w.stage2_tokens = 300, 32, 64
