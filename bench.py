@@ -652,13 +652,13 @@ def workload_text(w, budget, full):
 
 def kernel_text(w):
     if w.stage2_channels and w.stage2_v == 0 and w.el == 2 and w.head_dim == 128:
-        return (f"k_attend_s2<{w.group},3> (Stage II: exact and reduced-channel logits of every live K row on "
+        return (f"k_attend_s2<{w.group},2> (Stage II: exact and reduced-channel logits of every live K row on "
                 "matrix cores, K only; HIP events per launch)")
     if w.stage2_channels:
         return (f"k_attn_tiles<2,{w.head_dim},{w.group},false,true> (Stage II reduced-channel logits over "
                 "every live K row; HIP events per launch)")
     if w.el == 2 and w.head_dim == 128:
-        return (f"k_attend_mfma<{w.group},3> (split-K attention over the live K/V rows on matrix cores; "
+        return (f"k_attend_mfma<{w.group},2> (split-K attention over the live K/V rows on matrix cores; "
                 "HIP events per launch)")
     return (f"k_attend<{w.el},{w.head_dim},{w.group}> (split-K attention over the live K/V rows; "
             "HIP events per launch)")

@@ -2358,8 +2358,8 @@ template <int EL, int D, int G>
 static constexpr bool use_mfma() { return EL == 2 && D == 128; }
 template <int EL, int D, int G, bool S2 = false>
 static void (*attend_kernel())(StepArgs) {
-  if constexpr (S2) return k_attend_s2<G, 3>;
-  else if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G, 3>;
+  if constexpr (S2) return k_attend_s2<G, 2>;
+  else if constexpr (use_mfma<EL, D, G>()) return k_attend_mfma<G, 2>;
   else return k_attend<EL, D, G>;
 }
 
