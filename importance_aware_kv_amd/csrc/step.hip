@@ -1793,11 +1793,12 @@ __global__ __launch_bounds__(kT2) void k_block_keys(StepArgs a) {
 //    first leaves the bin in the unit's record.  A bin of more than kBulkCand
 //    keys, or a unit longer than the select's LDS bitmap, is left to the select
 //    (kCutSlow).
-//  - k_bulk_select, one workgroup per unit: the need-th smallest candidate
+//  - k_bulk_select, a few workgroups per unit: the need-th smallest candidate
 //    (radix passes in LDS) is the threshold; the candidates up to it join the
 //    bitmap, and the holes (marked slots below the new length) and movers
 //    (unmarked live slots at or above it) are listed in ascending slot order
-//    for k_bulk_moves.  With kCutSlow it finds the bin itself, narrowing it by
+//    for k_bulk_moves, each workgroup listing its share of the bitmap's words.
+//    With kCutSlow one workgroup finds the bin itself, narrowing it by
 //    passes over the keys until it holds at most kBulkCand keys, and gathers it.
 // Whole blocks: a block's tokens share one key, so the keys up to the threshold
 // are whole blocks and the new length is L less those; when protected blocks
@@ -1960,7 +1961,10 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   __shared__ int sc[2 * kNW2];
   __shared__ BinPick bp;
   __shared__ int s_bin, s_need, s_cnt, s_nc;
-  const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Workgroup y of a unit lists its share of the bitmap's words (kCutFast; the
+  // rest of the select, which every workgroup of the unit repeats, gives each
+  // the same bitmap and prefixes); kCutSlow is workgroup 0's alone.
+  const int u = blockIdx.x, sl = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t *uh = a.ws.uhist + (size_t)u * kBulkHistWords;
   // Issued together (one round trip): the cut's parameters, the record
   // k_bulk_mark left, and what it gathered -- the bitmap words and the
@@ -1991,13 +1995,14 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   // (every key of a block is the same), L less every key up to the threshold.
   int newlen = beta;
   if (mode == kCutKeep) {
-    if (tid == 0) a.len[u] = L;
+    if (tid == 0 && sl == 0) a.len[u] = L;
     return;
   }
   if (mode != kCutFast && mode != kCutSlow) {  // fewer candidates than tokens to evict: cannot happen
     if (tid == 0) set_status(a.ws.status, HIKV_EINVAL);
     return;
   }
+  if (mode == kCutSlow && sl != 0) return;
   uint64_t prefix;  // the bin: the keys' top pbits bits
   int pbits = kBulkBits, need, cnt;
   const bool use_map = L <= kBulkMapSlots;
@@ -2207,17 +2212,19 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
   // index is the wave's, so the masks are scalar work.  A lane's rank among
   // a word's listed slots is the count of listed bits below it (mbcnt).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int per = mode == kCutFast ? (nw + (int)gridDim.y - 1) / (int)gridDim.y : nw;
+  const int lw0 = mode == kCutFast ? sl * per : 0, lw1 = min(lw0 + per, nw);  // this workgroup's words
   auto put = [&](uint64_t m, int first, int slot, int32_t *list) __attribute__((always_inline)) {
     const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
     const uint32_t mine = (lane < 32 ? lo >> lane : hi >> (lane - 32)) & 1u;
     if (mine) list[first + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = slot;
   };
-  for (int wb = wv; wb < nw; wb += 4 * kNW2) {
+  for (int wb = lw0 + wv; wb < lw1; wb += 4 * kNW2) {
     uint64_t e[4];
     int h0[4], m0[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int w = min(wb + q * kNW2, nw - 1);
+      const int w = min(wb + q * kNW2, lw1 - 1);
       e[q] = eb[w];
       h0[q] = ph[w];
       m0[q] = pm[w];
@@ -2225,7 +2232,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int w = wb + q * kNW2;
-      if (w >= nw) break;
+      if (w >= lw1) break;
       const int slot = 64 * w + lane;
       if (64 * w + 64 <= newlen) {  // every slot below the new length: holes only
         put(e[q], h0[q], slot, holes);
@@ -2238,7 +2245,7 @@ __global__ __launch_bounds__(kT2) void k_bulk_select(StepArgs a) {
       }
     }
   }
-  if (tid == 0) {
+  if (tid == 0 && sl == 0) {
     if (th != tm) {  // cannot happen for distinct positions; fail safe
       set_status(a.ws.status, HIKV_EINVAL);
     } else {
@@ -2319,6 +2326,19 @@ __global__ __launch_bounds__(256) void k_bulk_moves(StepArgs a) {
 // bounds (moves_flat), else per unit one workgroup per bulk_moves_per_wg
 // moves of the largest bound; a bound that is only the capacity (no caller's
 // lengths) takes at most 8 per unit, each looping over its share.
+// The select's grid: per unit, one workgroup per 4096 slots of the longest
+// unit, each listing its share of the bitmap's words, with at most one
+// workgroup per CU in all (the select's LDS).
+static dim3 select_grid(const StepArgs &a) {
+  int mx = a.cap;
+  if (a.hp.n == a.n_units) {
+    mx = 1;
+    for (int u = 0; u < a.hp.n; ++u) mx = max(mx, a.hp.L[u] + 1);
+  }
+  const int sl = (min(mx, kBulkMapSlots) + 4095) / 4096;
+  return dim3((unsigned)a.n_units, (unsigned)max(1, min(sl, 256 / max(1, a.n_units))));
+}
+
 template <int RB>
 static dim3 moves_grid(const StepArgs &a) {
   if (a.moves_flat) return dim3((unsigned)a.hp.mvb[a.hp.n]);
@@ -2419,7 +2439,7 @@ static hipError_t step_go(const StepArgs &a, hipStream_t s, hipEvent_t ev0, hipE
     hipLaunchKernelGGL(k_bulk_mark, dim3((unsigned)a.n_units, (unsigned)((nib * kImpChunk + kMarkSlots - 1) / kMarkSlots)),
                        dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_select<D * EL>), select_grid(a), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bulk_moves<D * EL>), moves_grid<D * EL>(a), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -2453,7 +2473,7 @@ static hipError_t step_go_s2(const StepArgs &a, hipStream_t s, hipEvent_t ev0, h
     hipLaunchKernelGGL(k_bulk_mark, dim3((unsigned)a.n_units, (unsigned)((nib * kImpChunk + kMarkSlots - 1) / kMarkSlots)),
                        dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bulk_select<D * EL>), dim3((unsigned)a.n_units), dim3(kT2), 0, s, a);
+    hipLaunchKernelGGL((k_bulk_select<D * EL>), select_grid(a), dim3(kT2), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_bulk_moves<D * EL>), moves_grid<D * EL>(a), dim3(256), 0, s, a);
     return hipGetLastError();

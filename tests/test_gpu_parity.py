@@ -340,6 +340,25 @@ def test_bulk_cut_beyond_the_select_bitmap(hint):
 
 
 @PATHS
+def test_bulk_cut_listed_by_many_workgroups(hint):
+    """A bulk cut of a few long units under the select's bitmap limit: with the
+    caller's lengths the holes and movers of each unit are listed by up to 49
+    workgroups, each taking its share of the bitmap's words, and the lists
+    pair up across their boundaries.  Importance spread over 100 binades keeps
+    every threshold bin small enough to be gathered whole (the fast cut)."""
+    B, Hkv, G, D, cap, S, Wn, beta = 1, 2, 2, 64, 200100, 4, 64, 60000
+    st = W.random_cache(66, B, G * Hkv, Hkv, D, W.BF16, cap, [[200000, 90000]])
+    rng = np.random.Generator(np.random.PCG64(67))
+    for j in range(Hkv):
+        n = int(st["len"][0, j])
+        st["imp"][0, j, :n] = np.exp2(rng.uniform(0.0, 100.0, size=n)).astype(np.float32)
+    data = W.random_step(68, B, G * Hkv, Hkv, D, W.BF16, st["newest"])
+    data = {k: v[None] for k, v in data.items()}
+    run = GpuRun(st, G * Hkv, budget_all=beta, n_sink=S, n_recent=Wn, hint=hint)
+    lockstep(run, data, 1, tag="bulk cut listed by many workgroups")
+
+
+@PATHS
 def test_longctx_g8_lockstep_and_full_attention(hint):
     w = W.workload("longctx128k", ctx=3000, steps=4, batch=1)
     w.budget_all, w.n_recent = 256, 64
