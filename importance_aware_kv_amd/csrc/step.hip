@@ -1350,12 +1350,14 @@ __global__ __launch_bounds__(S2 ? kT2 : kT2 / 2) __attribute__((amdgpu_waves_per
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vz = vzero();
-  // Grid: x = the unit, y = the unit's workgroup (nib importance blocks, then
-  // NOC output blocks), so that the unit is known without a load and every
-  // unit's importance blocks, which end the step, are dispatched before any
-  // output block.
+  // Grid: x = the unit, y = the unit's workgroup, so that the unit is known
+  // without a load.  r: nib importance blocks, then NOC output blocks.  The
+  // blocks that end the step are dispatched first: every unit's importance
+  // blocks in Stage I, its output blocks (the selection, the exact softmax and
+  // the gathered V rows) in Stage II.
   const int nib = (int)gridDim.y - NOC;  // importance blocks per unit
-  const int u = blockIdx.x, r = blockIdx.y;
+  const int u = blockIdx.x,
+            r = S2 ? ((int)blockIdx.y < NOC ? (int)blockIdx.y + nib : (int)blockIdx.y - NOC) : (int)blockIdx.y;
   // The host plan's words (kernel arguments, clamped to its table) are loaded
   // with the flag that says whether there is one, so that the host plan costs
   // one round trip; the device plan's path uses them too, after its own load,
