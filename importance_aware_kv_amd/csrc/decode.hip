@@ -108,14 +108,22 @@ __device__ TileInfo plan_locate(const StepArgs &a, int tile, bool store, PlanSha
   return ti;
 }
 
-// Unit owning a tile, from the stored plan (binary search over tile bases).
+// The unit of a tile: the last unit whose first tile is at or before it
+// (a unit without tiles shares its successor's first tile).  Called by whole
+// waves with a uniform tile: every lane loads its share of the table at once
+// (from clamped addresses) and the wave counts, one round trip for up to 256
+// units instead of a dependent load per step of a binary search.
 __device__ __forceinline__ int plan_unit(const int32_t *plan, int U, int tile) {
-  int lo = 0, hi = U - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (plan[mid] <= tile) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int i0 = 0; i0 < U; i0 += 256) {
+    int v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = plan[min(i0 + 64 * q + lane, U - 1)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += __popcll(__ballot(i0 + 64 * q + lane < U && v[q] <= tile));
   }
-  return lo;
+  return cnt - 1;  // plan[0] = 0: at least one
 }
 __device__ __forceinline__ int plan_ntiles(const int32_t *plan, int U, int u) {
   return plan[u + 1 < U ? u + 1 : U] - plan[u];
