@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--accumulate", choices=["all", "recent", "logit"], default=None,
                     help="override the workload's importance accumulation (H2O probabilities, HiKV's "
                          "recent window only, Kelle's pre-softmax logits)")
+    ap.add_argument("--budget", type=int, default=None,
+                    help="one budget for every unit in place of the workload's own (a measurement at another size)")
     ap.add_argument("--quick", action="store_true", help="the headline workload only (no sub-workloads, no sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -148,7 +150,7 @@ def main():
                                                 "logit": H.HIKV_ACC_LOGIT}[args.accumulate]
     head = run_workload(args.workload, steps=args.steps, warmup=args.warmup, layers=args.layers,
                         hint=not args.no_hint, accumulate=acc, prefill=args.prefill, detail=True,
-                        keep_data=not args.no_cpu_baseline, block_tokens=args.block_tokens)
+                        keep_data=not args.no_cpu_baseline, block_tokens=args.block_tokens, budget_all=args.budget)
     launch_us = launch_floor_us()
     log(f"[bench] dependent empty launch in a graph: {launch_us:.2f} us")
 
@@ -170,7 +172,7 @@ def main():
     w = head.pop("w")
 
     subs, sweep = None, None
-    if not args.quick and args.workload == "headkv32k" and not args.block_tokens:
+    if not args.quick and args.workload == "headkv32k" and not args.block_tokens and args.budget is None:
         subs = {}
         for name in SUB_WORKLOADS:
             r = run_workload(name, steps=128, warmup=16, layers=args.layers, hint=not args.no_hint, detail=False)
@@ -193,7 +195,7 @@ def main():
         sweep = {"workload": "llama8b (batch 8, 32 q / 8 KV heads, D 128, bf16, 8192-token prefill, sinks 4, "
                              "recent 128), one budget for every unit", "points": pts}
 
-    tr = measured_traffic() if args.workload == "headkv32k" and not args.block_tokens else None
+    tr = measured_traffic() if args.workload == "headkv32k" and not args.block_tokens and args.budget is None else None
     line = {
         "metric": "decode steps/s and achieved KV HBM GB/s (fraction of 8 TB/s) per budget",
         "value": round(head["steps_per_s"], 1),

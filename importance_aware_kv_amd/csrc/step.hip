@@ -900,27 +900,27 @@ __device__ __forceinline__ void unit_stats(const float2 *pml, int npair, float2 
 // has position new_pos[b] and its V row in v_new (the importance blocks of
 // the same launch write it into the cache).
 //
-// Selection.  Units of up to kS2Wave tokens (the steady state): every key
-// goes to LDS and wave 0 alone finds the threshold -- a histogram of the
-// keys' top 11 bits, the bin holding the k_T-th largest, and a bitwise
-// search over the low 53 bits of that bin's keys (gathered in LDS, 1024 at
-// most) -- with no workgroup barrier in between.  Longer units, or a bin
-// with more keys: radix passes of 8 bits from the top over the workgroup.
-// Keys of the first kS2Kr * kT2 tokens stay in registers; longer units
-// recompute the rest from the logits each pass.
+// Selection.  Units of up to KR * kT2 tokens (the steady state), every key
+// in registers: a histogram of the keys' top 11 bits gives the bin holding
+// the k_T-th largest; the bin's keys are gathered in LDS (narrowed by a
+// histogram of the next 11 bits when over 128) and ranked.  Longer units, or
+// a crowded sub-bin: radix passes of 8 bits from the top over the workgroup,
+// the keys beyond the registers' recomputed from the logits each pass.
+// KR = 2, or 4 when some unit of the step is longer than 2048 tokens (more
+// registers and a larger key buffer, which cost the short units' steps
+// time).
 // ---------------------------------------------------------------------------
-constexpr int kS2Kr = 2;
 constexpr int kS2List = kS2TwoMaxTokens;  // selected tokens listed in LDS
-constexpr int kS2Wave = kS2Kr * kT2;      // units up to this many tokens: the histogram selection
-static_assert(kS2List * 8 <= 16384 && kS2Wave * 8 <= 16384, "the list and the keys share a 16 KB buffer");
+static_assert(kS2List * 8 <= 2 * kT2 * 8, "the list fits the key buffer");
 
-template <int G>
+template <int G, int KR>
 __device__ __forceinline__ void s2_out_block(const StepArgs &a, int u, int g, int L, int dead, int newest,
                                              bool skip) {
   constexpr int D = 128, RB = 256, NW = kNW2;
   __shared__ uint32_t h[256];
   __shared__ __attribute__((aligned(16))) float s2red[NW][D + 8];  // P.V partials; the selection's histogram before
-  __shared__ __attribute__((aligned(16))) char s_buf[16384];   // the keys, then the list of selected tokens
+  constexpr int kS2Kr = KR, kS2Wave = KR * kT2;  // units up to kS2Wave tokens: the histogram selection
+  __shared__ __attribute__((aligned(16))) char s_buf[kS2Wave * 8];  // the keys, then the list of selected tokens
   __shared__ float s_pm[NW], s_ps[NW];
   __shared__ uint64_t s_T;
   __shared__ int s_d, s_need, s_cnt, s_fall;
@@ -1321,7 +1321,7 @@ __device__ __attribute__((noinline)) void bulk_cut_unit(const uint64_t *keys, in
 
 // IB: the in-block bulk cut inlined (when the host cannot foresee bulk cuts,
 // any unit may be cut in bulk in this block), or called out of line.
-template <int EL, int D, int G, bool S2 = false, bool IB = false>
+template <int EL, int D, int G, bool S2 = false, bool IB = false, int KR = 2>
 __global__ __launch_bounds__(S2 ? kT2 : kT2 / 2) __attribute__((amdgpu_waves_per_eu(S2 ? 8 : 6))) void k_finalize(StepArgs a) {
   // Workgroup size: Stage II's output blocks select among up to 2 kT2 keys
   // held two per thread; Stage I's blocks take half as many threads (two
@@ -1671,7 +1671,7 @@ __global__ __launch_bounds__(S2 ? kT2 : kT2 / 2) __attribute__((amdgpu_waves_per
     const int beta = a.budget ? ld_vec(a.budget + u, vz) : a.budget_all;
     const int dead = ld_vec(unit_state(a, u) + 1, vz);
     const int newest = ld_vec(a.new_pos + b, vz);
-    s2_out_block<G>(a, u, r - nib, L, dead, newest, a.hp.n && (L > a.cap || beta < S || beta > a.cap));
+    s2_out_block<G, KR>(a, u, r - nib, L, dead, newest, a.hp.n && (L > a.cap || beta < S || beta > a.cap));
   } else {
   // ---------------- output block: chunk c of the unit's G*D outputs ----
   const int beta_ld = ld_opaque(a.budget ? a.budget + u : a.new_pos + b, vz);
@@ -2468,8 +2468,19 @@ static hipError_t step_go_s2(const StepArgs &a, hipStream_t s, hipEvent_t ev0, h
     for (int u = 0; u < a.hp.n; ++u) mx = max(mx, a.hp.L[u]);
     nib = min(nib, (mx + kImpChunk - 1) / kImpChunk);
   }
-  hipLaunchKernelGGL((k_finalize<EL, D, G, true>), dim3((unsigned)a.n_units, (unsigned)(nib + G)), dim3(kT2), 0, s,
-                     a);
+  // Four keys per thread in the output blocks when some unit is longer than
+  // two (the new token included).
+  int mxl = a.cap + 1;
+  if (a.hp.n == a.n_units) {
+    mxl = 1;
+    for (int u = 0; u < a.hp.n; ++u) mxl = max(mxl, a.hp.L[u]);
+  }
+  if (mxl > 2 * kT2)
+    hipLaunchKernelGGL((k_finalize<EL, D, G, true, false, 4>), dim3((unsigned)a.n_units, (unsigned)(nib + G)),
+                       dim3(kT2), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_finalize<EL, D, G, true>), dim3((unsigned)a.n_units, (unsigned)(nib + G)), dim3(kT2), 0, s,
+                       a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.bulk_split) {
     hipLaunchKernelGGL(k_bulk_mark, dim3((unsigned)a.n_units, (unsigned)((nib * kImpChunk + kMarkSlots - 1) / kMarkSlots)),

@@ -845,6 +845,20 @@ def test_stage2_exact_over_more_than_one_slot_chunk():
     lockstep(_run(w, d), d, w.steps, tag="stage2 k_T 1500")
 
 
+@PATHS
+@pytest.mark.parametrize("ctx,budget", [(3500, 3000), (4100, 4095)], ids=["3000", "4095"])
+def test_stage2_units_beyond_2048_tokens(ctx, budget, hint):
+    """Stage II's two-launch step with units longer than 2048 tokens: the
+    output blocks keep four keys per thread and select by histogram up to
+    4096 tokens (4096 exactly in the steady steps of budget 4095); the
+    compression step of the 4100-token prompt (4101 with the new token)
+    takes the radix passes."""
+    w = W.workload("twostage", ctx=ctx, steps=3, batch=1)
+    w.budget_all, w.n_recent = budget, 32
+    d = W.generate(w)
+    lockstep(_run(w, d, hint=hint), d, w.steps, tag=f"stage2 units of {budget}")
+
+
 @pytest.mark.parametrize("L", [16384, 40000])
 def test_prefill_scores_conserve_mass_at_size(L):
     """At prompt sizes the oracle cannot finish: every query's softmax row
