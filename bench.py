@@ -22,7 +22,7 @@ Besides the headline the JSON line carries:
              steady steps (64 steps in all for headkv32k);
   workloads  the same measurement on the other seeded workloads (llama8b,
              longctx128k budgeted and full attention, twostage);
-  budget_sweep  llama8b at budgets 128 ... 2048;
+  budget_sweep  llama8b at budgets 128 ... 4096, and Stage II (twostage) at 1024 ... 4096;
   cpu_baseline  the CPU oracle on a bounded sample of the headline workload.
 
 --workload selects another headline workload with the same protocol:
@@ -55,7 +55,8 @@ FP32_PEAK_TFLOPS = 157.3         # fp32 vector peak
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_headkv32k.md")
 KERNEL_SOURCES = ("importance_aware_kv_amd/csrc/step.hip", "importance_aware_kv_amd/csrc/hikv_common.h",
                   "importance_aware_kv_amd/csrc/hikv_dev.h", "importance_aware_kv_amd/csrc/hikv_block.h")
-SWEEP_BUDGETS = (128, 256, 512, 1024, 2048)
+SWEEP_BUDGETS = (128, 256, 512, 1024, 2048, 3072, 4096)
+STAGE2_BUDGETS = (1024, 2048, 3072, 4096)
 SUB_WORKLOADS = ("llama8b", "longctx128k", "longctx128k_full", "twostage")
 
 
@@ -194,6 +195,16 @@ def main():
                                                         "bytes_per_step", "compression_step_us")}})
         sweep = {"workload": "llama8b (batch 8, 32 q / 8 KV heads, D 128, bf16, 8192-token prefill, sinks 4, "
                              "recent 128), one budget for every unit", "points": pts}
+        # Stage II (r = 32, k_T = 256) on the same shape at the larger budgets
+        pts2 = []
+        for b in STAGE2_BUDGETS:
+            r = run_workload("twostage", steps=128, warmup=16, layers=args.layers, hint=not args.no_hint,
+                             budget_all=b, detail=False)
+            r.pop("w")
+            pts2.append({"budget": b, **{k: r[k] for k in ("us_per_step", "steps_per_s", "bytes_per_step",
+                                                         "compression_step_us")}})
+        sweep["stage2"] = {"workload": "twostage (the same shape; Stage II, r = 32 channels, k_T = 256 tokens)",
+                           "bytes": "Stage I's algorithmic bytes of the same budget", "points": pts2}
 
     tr = measured_traffic() if args.workload == "headkv32k" and not args.block_tokens and args.budget is None else None
     line = {
